@@ -1,0 +1,77 @@
+"""Work and traffic counts for the attention path (host-side arithmetic used
+by the benchmark; no GPU work).
+
+Flops: 4*L*C for the forward and 2.5 times that for the backward, where
+L = B*R*H*N^2 is the number of logits of a call (each logit costs C
+multiply-adds for Q.K and C for P.V; masked keys are counted).
+
+Memory: the dense logits a naive implementation would store are N^3*H
+elements per triangle attention (one [H, N, N] block per row, N rows), and
+the pair representation is N^2*c_z elements ("Evoformer: the memory wall ZeRO
+cannot move", section "Where the memory goes" and the table in "The two
+tensors").
+"""
+
+MI355X_BF16_DENSE_TFLOPS = 2500.0   # dense MFMA, bf16
+MI355X_FP32_MFMA_TFLOPS = 157.3
+MI355X_HBM_GBS = 8000.0
+
+
+def n_logits(B, R, N, H):
+    return B * R * H * N * N
+
+
+def fwd_flops(B, R, N, H, C):
+    return 4.0 * n_logits(B, R, N, H) * C
+
+
+def bwd_flops(B, R, N, H, C):
+    return 2.5 * fwd_flops(B, R, N, H, C)
+
+
+def project_flops(N, CZ, H, C):
+    """LayerNorm'd pair rep times the four [CZ, H*C] projections and the
+    [CZ, H] bias projection."""
+    return 2.0 * N * N * CZ * (4 * H * C + H)
+
+
+def out_project_flops(N, CZ, H, C):
+    return 2.0 * N * N * H * C * CZ
+
+
+def triangle_logit_bytes(N, H, elem_bytes):
+    return N ** 3 * H * elem_bytes
+
+
+def pair_rep_bytes(N, CZ, elem_bytes):
+    return N ** 2 * CZ * elem_bytes
+
+
+def fwd_min_bytes(B, R, N, H, C, elem_bytes, gate=True, bias=True,
+                  lse=False, mask_rows=0):
+    """Algorithmic HBM bytes of one forward call: Q, K, V (and the gate) read
+    once, Out written once, the bias read once per batch, the key mask read
+    once, LSE written once when requested."""
+    t = B * R * N * H * C * elem_bytes
+    n = (3 + (1 if gate else 0) + 1) * t
+    if bias:
+        n += B * H * N * N * elem_bytes
+    if lse:
+        n += B * R * H * N * 4
+    n += B * mask_rows * N
+    return n
+
+
+def bwd_min_bytes(B, R, N, H, C, elem_bytes, gate=True, bias=True,
+                  mask_rows=0):
+    """Algorithmic HBM bytes of one backward call: Q, K, V, gate, Out, dOut
+    read once; dQ, dK, dV, dGate written once; LSE read once; the bias read
+    once per batch and the fp32 dBias written once."""
+    t = B * R * N * H * C * elem_bytes
+    n_in = 4 + (1 if gate else 0) + 1       # q k v out dout (+gate)
+    n_out = 3 + (1 if gate else 0)          # dq dk dv (+dgate)
+    n = (n_in + n_out) * t + B * R * H * N * 4
+    if bias:
+        n += B * H * N * N * elem_bytes + B * H * N * N * 4
+    n += B * mask_rows * N
+    return n

@@ -1,0 +1,349 @@
+"""Plain fp64 CPU oracle for the Evoformer's biased, gated attention.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only the test suite, the smoke check of the entry script
+and the CPU-baseline leg of the benchmark use it.  It shares no code with the
+HIP library and imports nothing from it; both sides receive the same seeded
+arrays from a generator module that holds none of the method's arithmetic.
+
+Sources (web pages; cited by title and section):
+  [COURSE]  "Evoformer: the memory wall ZeRO cannot move" (DeepSpeed course),
+            sections "Where the memory goes" (display equation: logits are
+            O(N_res^3 * n_heads)), "The three operations" (triangle attention
+            picks the third residue k by attention instead of a uniform sum)
+            and "Two properties the tests assert".
+  [MEGAFOLD] "MegaFold: Efficient Training of Next-Generation 3D Attention
+            Protein Models on Cross-Platform GPUs", section "Methodologie",
+            item 1 "EvoFlash-3D": online, numerically stable softmax in the
+            forward and backward passes, exact results, and an additively
+            broadcast pair bias.
+
+What is computed (the plain reading; the pages never print the formula):
+for every attention line (batch b, row r), head h, query q and key k
+
+    s[q,k]  = <Q[q], K[k]> / sqrt(C) + bias[b,h,q,k] + (keep[k] ? 0 : -inf)
+    P[q,:]  = softmax_k(s[q,:])
+    O[q]    = sum_k P[q,k] V[k]
+    Out[q]  = sigmoid(G[q]) * O[q]                  (identity when no gate)
+    LSE[q]  = log sum_k exp(s[q,k])                  (natural log)
+
+A line whose keys are all masked has Out = 0, LSE = -inf and zero gradients
+(a reading: the pages are silent).  The bias is shared by every row of a
+batch ("additively broadcast" in [MEGAFOLD]), so its gradient is the sum over
+rows of dS.
+
+Every array is float64; callers pass the exact values the GPU sees (for bf16
+runs, the bf16-rounded inputs upcast to float64).  No blocking, fusion or
+reordering beyond the definition: each logit block of one (line, head) is
+materialised in full before the value product, which is exactly what the GPU
+path must avoid doing in HBM.
+"""
+import numpy as np
+
+__all__ = [
+    "sigmoid", "attention_line_probs", "attention_line_forward",
+    "attention_forward", "attention_line_backward", "attention_backward",
+    "dbias_query_rows", "layer_norm", "tri_project", "tri_out_project",
+    "tri_module_forward", "tri_module_lines",
+]
+
+
+def sigmoid(x):
+    """Logistic function 1 / (1 + e^-x), evaluated without overflow."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.empty_like(x)
+    pos = x >= 0
+    out[pos] = 1.0 / (1.0 + np.exp(-x[pos]))
+    ex = np.exp(x[~pos])
+    out[~pos] = ex / (1.0 + ex)
+    return out
+
+
+def _line_logits(q, k, bias, keep, h):
+    """Logits s[q, k] of one (line, head): scaled dot products plus pair bias
+    plus the key mask.  q, k: [N, H, C]; bias: [H, N, N] or None; keep: [N]
+    bool or None."""
+    C = q.shape[-1]
+    s = (q[:, h, :] @ k[:, h, :].T) / np.sqrt(C)
+    if bias is not None:
+        s = s + bias[h]
+    if keep is not None:
+        s = np.where(keep[None, :], s, -np.inf)
+    return s
+
+
+def attention_line_probs(q, k, bias=None, keep=None):
+    """Softmax probabilities P[h, q, k] of one attention line.
+
+    A query whose keys are all masked gets an all-zero row (the reading for a
+    fully masked line)."""
+    N, H, _ = q.shape
+    P = np.zeros((H, N, N))
+    for h in range(H):
+        s = _line_logits(q, k, bias, keep, h)
+        m = s.max(axis=1, keepdims=True)
+        live = np.isfinite(m[:, 0])
+        e = np.zeros_like(s)
+        e[live] = np.exp(s[live] - m[live])
+        l = e.sum(axis=1, keepdims=True)
+        P[h][live] = e[live] / l[live]
+    return P
+
+
+def attention_line_forward(q, k, v, gate=None, bias=None, keep=None):
+    """Forward pass of one attention line (one batch entry b and row r).
+
+    q, k, v, gate: [N, H, C]; bias: [H, N, N]; keep: [N] bool.
+    Returns out [N, H, C] and lse [H, N] (natural log; -inf when every key is
+    masked)."""
+    q = np.asarray(q, np.float64)
+    N, H, C = q.shape
+    out = np.zeros((N, H, C))
+    lse = np.empty((H, N))
+    for h in range(H):
+        s = _line_logits(q, k, bias, keep, h)
+        m = s.max(axis=1)
+        live = np.isfinite(m)
+        e = np.zeros_like(s)
+        e[live] = np.exp(s[live] - m[live, None])
+        l = e.sum(axis=1)
+        lse[h] = np.where(live, m + np.log(np.where(live, l, 1.0)), -np.inf)
+        P = np.zeros_like(s)
+        P[live] = e[live] / l[live, None]
+        o = P @ v[:, h, :]
+        if gate is not None:
+            o = o * sigmoid(gate[:, h, :])
+        out[:, h, :] = o
+    return out, lse
+
+
+def _line_inputs(b, r, gate, key_mask, bias):
+    g = None if gate is None else gate[b, r]
+    keep = None
+    if key_mask is not None:
+        mr = key_mask.shape[1]
+        keep = key_mask[b, 0 if mr == 1 else r] != 0
+    bb = None if bias is None else bias[b]
+    return g, keep, bb
+
+
+def attention_forward(q, k, v, gate=None, key_mask=None, bias=None):
+    """Biased gated attention over every line.
+
+    q, k, v, gate: [B, R, N, H, C]; key_mask: [B, MR, N] with MR in {1, R}
+    (nonzero = keep); bias: [B, H, N, N] shared by the R rows of a batch.
+    Returns out [B, R, N, H, C] and lse [B, R, H, N]."""
+    B, R, N, H, C = q.shape
+    out = np.zeros((B, R, N, H, C))
+    lse = np.zeros((B, R, H, N))
+    for b in range(B):
+        for r in range(R):
+            g, keep, bb = _line_inputs(b, r, gate, key_mask, bias)
+            out[b, r], lse[b, r] = attention_line_forward(
+                q[b, r], k[b, r], v[b, r], g, bb, keep)
+    return out, lse
+
+
+def attention_line_backward(q, k, v, gate, bias, keep, dout):
+    """Gradients of one attention line with respect to Q, K, V, the
+    pre-sigmoid gate and this line's contribution to the pair-bias gradient.
+
+    Chain rule through Out = sigmoid(G) * O, O = P V, P = softmax(s):
+      dO    = dOut * sigmoid(G)
+      dG    = dOut * O * sigmoid(G) * (1 - sigmoid(G))
+      dV    = P^T dO,   dP = dO V^T
+      dS    = P * (dP - rowsum(P * dP))
+      dQ    = dS K / sqrt(C),   dK = dS^T Q / sqrt(C),   dBias = dS
+    Returns dq, dk, dv, dg (None when there is no gate) and dbias [H, N, N]."""
+    N, H, C = q.shape
+    dq = np.zeros((N, H, C))
+    dk = np.zeros((N, H, C))
+    dv = np.zeros((N, H, C))
+    dg = None if gate is None else np.zeros((N, H, C))
+    dbias = np.zeros((H, N, N))
+    P_all = attention_line_probs(q, k, bias, keep)
+    for h in range(H):
+        P = P_all[h]
+        o = P @ v[:, h, :]
+        do_h = dout[:, h, :]
+        if gate is not None:
+            sg = sigmoid(gate[:, h, :])
+            dg[:, h, :] = do_h * o * sg * (1.0 - sg)
+            do_h = do_h * sg
+        dv[:, h, :] = P.T @ do_h
+        dP = do_h @ v[:, h, :].T
+        D = (P * dP).sum(axis=1, keepdims=True)
+        dS = P * (dP - D)
+        dq[:, h, :] = dS @ k[:, h, :] / np.sqrt(C)
+        dk[:, h, :] = dS.T @ q[:, h, :] / np.sqrt(C)
+        dbias[h] = dS
+    return dq, dk, dv, dg, dbias
+
+
+def attention_backward(q, k, v, gate, key_mask, bias, dout):
+    """Backward of attention_forward for every line.
+
+    Returns dq, dk, dv, dgate (None without a gate) shaped like q, and dbias
+    [B, H, N, N]: the sum over the R rows of each batch of dS (zeros are
+    returned even when no bias was given, since dS does not depend on it)."""
+    B, R, N, H, C = q.shape
+    dq = np.zeros_like(q, dtype=np.float64)
+    dk = np.zeros_like(dq)
+    dv = np.zeros_like(dq)
+    dg = None if gate is None else np.zeros_like(dq)
+    dbias = np.zeros((B, H, N, N))
+    for b in range(B):
+        for r in range(R):
+            g, keep, bb = _line_inputs(b, r, gate, key_mask, bias)
+            lq, lk, lv, lg, lb = attention_line_backward(
+                q[b, r], k[b, r], v[b, r], g, bb, keep, dout[b, r])
+            dq[b, r], dk[b, r], dv[b, r] = lq, lk, lv
+            if dg is not None:
+                dg[b, r] = lg
+            dbias[b] += lb
+    return dq, dk, dv, dg, dbias
+
+
+def dbias_query_rows(q, k, v, gate, key_mask, bias, dout, b, picks):
+    """dBias[b, h, qi, :] for the (h, qi) pairs in `picks`, summed over every
+    row of batch b.  Only the listed query's logits are formed for each row,
+    so a few entries of a large problem stay cheap.  Returns [len(picks), N]."""
+    _, R, N, H, C = q.shape
+    res = np.zeros((len(picks), N))
+    for r in range(R):
+        g, keep, bb = _line_inputs(b, r, gate, key_mask, bias)
+        for t, (h, qi) in enumerate(picks):
+            s = (k[b, r, :, h, :] @ q[b, r, qi, h, :]) / np.sqrt(C)
+            if bb is not None:
+                s = s + bb[h, qi]
+            if keep is not None:
+                s = np.where(keep, s, -np.inf)
+            m = s.max()
+            if not np.isfinite(m):
+                continue
+            e = np.exp(s - m)
+            P = e / e.sum()
+            do_q = dout[b, r, qi, h, :]
+            if g is not None:
+                do_q = do_q * sigmoid(g[qi, h, :])
+            dP = v[b, r, :, h, :] @ do_q
+            D = (P * dP).sum()
+            res[t] += P * (dP - D)
+    return res
+
+
+# ----------------------------------------------------------------------------
+# Triangle attention module: LayerNorm, projections, core, output projection.
+#
+# [COURSE] "The three operations": triangle attention updates edge (i, j)
+# through third residues k chosen by attention.  [MEGAFOLD] item 3
+# "EvoFusion": layer normalisation is followed by linear projections (the
+# fusion avoids writing the normalised N x N tensor).  Readings (the pages are
+# silent): LayerNorm over c_z with population variance and eps; Q, K, V, gate
+# and the per-head pair bias are projections of the same normalised pair
+# representation; the gate projection and the output projection carry a
+# bias vector, the others do not; the module returns the update only.
+#
+# Starting node: line i, query j, key k:
+#     s_h(i,j,k) = <q_ij, k_ik>/sqrt(C) + b_jk[h],  out_ij = g_ij * sum_k a v_ik
+# Ending node: line j (a column of z), query i, key k:
+#     s_h(j,i,k) = <q_ij, k_kj>/sqrt(C) + b_ki[h],  out_ij = g_ij * sum_k a v_kj
+# The residue mask removes key k from every line.
+# ----------------------------------------------------------------------------
+
+def layer_norm(x, w, b, eps):
+    """LayerNorm over the last axis with population variance."""
+    x = np.asarray(x, np.float64)
+    mu = x.mean(axis=-1, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
+    return (x - mu) / np.sqrt(var + eps) * w + b
+
+
+def _pair_bias(z, ln_w, ln_b, eps, w_bias):
+    """b[j, k, h] = LN(z)[j, k] . w_bias[:, h], computed one z row at a time
+    to keep memory at O(N^2 * H)."""
+    N = z.shape[0]
+    H = w_bias.shape[1]
+    out = np.empty((N, N, H))
+    for j in range(N):
+        out[j] = layer_norm(z[j], ln_w, ln_b, eps) @ w_bias
+    return out
+
+
+def _proj(x, w, H, C, bias_vec=None):
+    y = x @ w
+    if bias_vec is not None:
+        y = y + bias_vec
+    return y.reshape(x.shape[:-1] + (H, C))
+
+
+def tri_project(z, ln_w, ln_b, eps, w_q, w_k, w_v, w_g, b_g, w_bias, H, C,
+                ending):
+    """First half of the module, in the layout the core attention consumes.
+
+    Returns q, k, v, g as [1, N, N, H, C] (row = attention line, then the
+    position along the line) and bias as [1, H, N, N] (bias[h, query, key]).
+    Starting node: line i holds z[i, :]; bias[h, j, k] = b_jk[h].
+    Ending node: line j holds z[:, j]; bias[h, i, k] = b_ki[h]."""
+    z = np.asarray(z, np.float64)
+    N = z.shape[0]
+    x = layer_norm(z, ln_w, ln_b, eps)
+    q = _proj(x, w_q, H, C)
+    k = _proj(x, w_k, H, C)
+    v = _proj(x, w_v, H, C)
+    g = _proj(x, w_g, H, C, b_g)
+    bpair = x @ w_bias                      # [N, N, H], b_jk[h]
+    if ending:
+        # position (i, j) of z sits in line j at place i
+        q, k, v, g = (t.transpose(1, 0, 2, 3) for t in (q, k, v, g))
+        bias = bpair.transpose(2, 1, 0)     # bias[h, i, k] = b_ki[h]
+    else:
+        bias = bpair.transpose(2, 0, 1)     # bias[h, j, k] = b_jk[h]
+    return (q[None], k[None], v[None], g[None], bias[None])
+
+
+def tri_out_project(o, w_o, b_o, ending):
+    """Output projection: o [1, N, N, H, C] in line layout -> [N, N, CZ] in z
+    layout (lines are columns of z for the ending node)."""
+    _, N, _, H, C = o.shape
+    y = o[0].reshape(N, N, H * C) @ w_o + b_o
+    return y.transpose(1, 0, 2) if ending else y
+
+
+def tri_module_lines(z, residue_mask, ln_w, ln_b, eps, w_q, w_k, w_v, w_g,
+                     b_g, w_bias, w_o, b_o, H, C, ending, lines):
+    """Module output for selected attention lines, written straight from the
+    line-wise definition (not through tri_project).
+
+    Starting node: returns out[i, :, :] for each i in `lines`.
+    Ending node:   returns out[:, j, :] for each j in `lines`.
+    Result: [len(lines), N, CZ]."""
+    z = np.asarray(z, np.float64)
+    N = z.shape[0]
+    bpair = _pair_bias(z, ln_w, ln_b, eps, w_bias)   # [N, N, H]
+    keep = None if residue_mask is None else (np.asarray(residue_mask) != 0)
+    res = []
+    for t in lines:
+        if ending:
+            xl = layer_norm(z[:, t], ln_w, ln_b, eps)    # positions (i, t)
+            bias = bpair.transpose(2, 1, 0)               # [h, i, k] = b_ki
+        else:
+            xl = layer_norm(z[t], ln_w, ln_b, eps)        # positions (t, j)
+            bias = bpair.transpose(2, 0, 1)               # [h, j, k] = b_jk
+        q = _proj(xl, w_q, H, C)
+        k = _proj(xl, w_k, H, C)
+        v = _proj(xl, w_v, H, C)
+        g = _proj(xl, w_g, H, C, b_g)
+        o, _ = attention_line_forward(q, k, v, g, bias, keep)
+        res.append(o.reshape(N, H * C) @ w_o + b_o)
+    return np.stack(res)
+
+
+def tri_module_forward(z, residue_mask, ln_w, ln_b, eps, w_q, w_k, w_v, w_g,
+                       b_g, w_bias, w_o, b_o, H, C, ending):
+    """Whole module output [N, N, CZ] (the update; no residual add)."""
+    N = z.shape[0]
+    lines = tri_module_lines(z, residue_mask, ln_w, ln_b, eps, w_q, w_k, w_v,
+                             w_g, b_g, w_bias, w_o, b_o, H, C, ending,
+                             list(range(N)))
+    return lines.transpose(1, 0, 2) if ending else lines

@@ -1,0 +1,485 @@
+"""Pins for the fp64 oracle: each check ties it to something other than
+itself (a library routine, a closed form, an invariant, brute force), and the
+mutation tests at the end show that a planted mistake in the oracle fails at
+least one of them.  CPU only."""
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+from scipy.special import expit
+
+import oracle.evo_oracle as O
+
+
+def rnd(seed, *shape):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def core_case(seed, B=2, R=3, N=9, H=2, C=4, mask=True, gate=True, bias=True,
+              mask_rows=1):
+    rng = np.random.default_rng(seed)
+    d = dict(q=rng.standard_normal((B, R, N, H, C)),
+             k=rng.standard_normal((B, R, N, H, C)),
+             v=rng.standard_normal((B, R, N, H, C)))
+    d["gate"] = rng.standard_normal((B, R, N, H, C)) if gate else None
+    d["bias"] = rng.standard_normal((B, H, N, N)) if bias else None
+    if mask:
+        m = (rng.random((B, mask_rows, N)) < 0.7).astype(np.uint8)
+        m[..., 0] = 1  # at least one live key per line
+        d["key_mask"] = m
+    else:
+        d["key_mask"] = None
+    return d
+
+
+def fwd(d):
+    return O.attention_forward(d["q"], d["k"], d["v"], d["gate"],
+                               d["key_mask"], d["bias"])
+
+
+# ----------------------------------------------------------------- forward
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_probs_rows_sum_to_one_and_masked_keys_zero(seed):
+    d = core_case(seed)
+    keep = d["key_mask"][0, 0] != 0
+    P = O.attention_line_probs(d["q"][0, 0], d["k"][0, 0], d["bias"][0], keep)
+    np.testing.assert_allclose(P.sum(-1), 1.0, rtol=0, atol=1e-13)
+    assert np.all(P[:, :, ~keep] == 0)
+    assert np.all(P >= 0)
+
+
+def test_values_all_one_give_output_one():
+    d = core_case(3, gate=False)
+    d["v"] = np.ones_like(d["v"])
+    out, _ = fwd(d)
+    np.testing.assert_allclose(out, 1.0, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("with_bias,with_mask", [(False, False), (True, False),
+                                                 (True, True), (False, True)])
+def test_matches_torch_sdpa(with_bias, with_mask):
+    """Library routine: torch's scaled_dot_product_attention (fp64, CPU)
+    adds a float attn_mask [query, key] to QK^T/sqrt(C) before the softmax."""
+    d = core_case(4, B=2, R=2, N=11, H=3, C=8, gate=False, bias=with_bias,
+                  mask=with_mask, mask_rows=2)
+    out, _ = fwd(d)
+    B, R, N, H, C = d["q"].shape
+    for b in range(B):
+        for r in range(R):
+            q = torch.tensor(d["q"][b, r]).permute(1, 0, 2)  # [H, N, C]
+            k = torch.tensor(d["k"][b, r]).permute(1, 0, 2)
+            v = torch.tensor(d["v"][b, r]).permute(1, 0, 2)
+            am = torch.zeros(H, N, N, dtype=torch.float64)
+            if with_bias:
+                am = am + torch.tensor(d["bias"][b])
+            if with_mask:
+                keep = torch.tensor(d["key_mask"][b, r] != 0)
+                am = am.masked_fill(~keep[None, None, :], float("-inf"))
+            ref = F.scaled_dot_product_attention(q, k, v, attn_mask=am)
+            np.testing.assert_allclose(out[b, r], ref.permute(1, 0, 2).numpy(),
+                                       rtol=1e-12, atol=1e-12)
+
+
+def test_zero_query_log_weight_bias_closed_form():
+    """Q = 0 and bias[h,q,k] = ln w_k  =>  O = sum_k w_k V_k / sum_k w_k and
+    LSE = ln sum_k w_k."""
+    d = core_case(5, gate=False, mask=False)
+    B, R, N, H, C = d["q"].shape
+    d["q"] = np.zeros_like(d["q"])
+    w = np.random.default_rng(5).uniform(0.1, 3.0, (B, H, N))
+    d["bias"] = np.broadcast_to(np.log(w)[:, :, None, :], (B, H, N, N)).copy()
+    out, lse = fwd(d)
+    for b in range(B):
+        for h in range(H):
+            expect = (w[b, h][None, :, None] * d["v"][b, :, :, h, :]
+                      ).sum(1) / w[b, h].sum()               # [R, C]
+            np.testing.assert_allclose(out[b, :, :, h, :],
+                                       np.broadcast_to(expect[:, None, :],
+                                                       (R, N, C)),
+                                       rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(lse[b, :, h, :], np.log(w[b, h].sum()),
+                                       rtol=1e-13)
+
+
+def test_zero_query_zero_bias_is_masked_mean():
+    d = core_case(6, gate=False, bias=False, mask=True, mask_rows=3)
+    d["q"] = np.zeros_like(d["q"])
+    out, lse = fwd(d)
+    B, R, N, H, C = d["q"].shape
+    for b in range(B):
+        for r in range(R):
+            keep = d["key_mask"][b, r] != 0
+            mean = d["v"][b, r][keep].mean(axis=0)            # [H, C]
+            np.testing.assert_allclose(out[b, r], np.broadcast_to(mean, (N, H, C)),
+                                       rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(lse[b, r], np.log(keep.sum()), rtol=1e-13)
+
+
+def test_single_live_key_returns_its_value_gated():
+    d = core_case(7)
+    B, R, N, H, C = d["q"].shape
+    m = np.zeros((B, 1, N), np.uint8)
+    m[0, 0, 4] = 1
+    m[1, 0, 7] = 1
+    d["key_mask"] = m
+    out, _ = fwd(d)
+    for b, kk in ((0, 4), (1, 7)):
+        expect = expit(d["gate"][b]) * d["v"][b][:, kk][:, None, :, :]
+        np.testing.assert_allclose(out[b], expect, rtol=1e-12, atol=1e-12)
+
+
+def test_fully_masked_line_is_zero_with_neg_inf_lse():
+    d = core_case(8, mask_rows=3)
+    d["key_mask"][1, 2, :] = 0
+    out, lse = fwd(d)
+    assert np.all(out[1, 2] == 0)
+    assert np.all(np.isneginf(lse[1, 2]))
+    assert np.all(np.isfinite(lse[0]))
+
+
+def test_key_permutation_with_bias_columns_is_invariant():
+    d = core_case(9, mask_rows=3)
+    out, lse = fwd(d)
+    perm = np.random.default_rng(9).permutation(d["q"].shape[2])
+    e = dict(d)
+    e["k"] = d["k"][:, :, perm]
+    e["v"] = d["v"][:, :, perm]
+    e["bias"] = d["bias"][..., perm]
+    e["key_mask"] = d["key_mask"][..., perm]
+    out2, lse2 = fwd(e)
+    np.testing.assert_allclose(out2, out, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse2, lse, rtol=1e-12, atol=1e-12)
+
+
+def test_query_permutation_with_bias_rows_permutes_output():
+    d = core_case(10)
+    out, lse = fwd(d)
+    perm = np.random.default_rng(10).permutation(d["q"].shape[2])
+    e = dict(d)
+    e["q"] = d["q"][:, :, perm]
+    e["gate"] = d["gate"][:, :, perm]
+    e["bias"] = d["bias"][:, :, perm, :]
+    out2, lse2 = fwd(e)
+    np.testing.assert_allclose(out2, out[:, :, perm], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse2, lse[..., perm], rtol=1e-12, atol=1e-12)
+
+
+def test_row_permutation_permutes_output():
+    """The order of the rows (MSA sequences / pair rows) carries nothing:
+    permuting them permutes the output ("Two properties the tests assert")."""
+    d = core_case(11, R=4, mask_rows=4)
+    out, _ = fwd(d)
+    perm = np.array([2, 0, 3, 1])
+    e = {k: (None if v is None else v[:, perm] if k != "bias" else v)
+         for k, v in d.items()}
+    out2, _ = fwd(e)
+    np.testing.assert_allclose(out2, out[:, perm], rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("shift", [3.5, 1e4, -1e4])
+def test_softmax_shift_invariance(shift):
+    d = core_case(12)
+    out, lse = fwd(d)
+    e = dict(d)
+    sh = shift * (1 + np.random.default_rng(12).random(d["bias"].shape[:3]))
+    e["bias"] = d["bias"] + sh[..., None]
+    out2, lse2 = fwd(e)
+    np.testing.assert_allclose(out2, out, rtol=1e-9, atol=1e-9)
+    np.testing.assert_allclose(lse2 - sh.transpose(0, 1, 2)[:, None],
+                               lse, rtol=1e-9, atol=1e-7 * abs(shift))
+
+
+def test_gate_is_elementwise_sigmoid():
+    d = core_case(13)
+    out, _ = fwd(d)
+    e = dict(d)
+    e["gate"] = None
+    out_ng, _ = fwd(e)
+    np.testing.assert_allclose(out, expit(d["gate"]) * out_ng, rtol=1e-13,
+                               atol=1e-14)
+    np.testing.assert_allclose(O.sigmoid(np.array([-800.0, 0.0, 800.0])),
+                               [0.0, 0.5, 1.0])
+
+
+# ---------------------------------------------------------------- backward
+
+def loss_and_grads(d, dout):
+    out, _ = fwd(d)
+    return float((out * dout).sum())
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_backward_matches_central_finite_differences(seed):
+    """Brute force: every gradient entry against a central difference of the
+    scalar <dOut, Out> (fp64, step 1e-6) on a tiny problem."""
+    d = core_case(100 + seed, B=1, R=2, N=5, H=2, C=3, mask_rows=2)
+    dout = rnd(200 + seed, *d["q"].shape)
+    dq, dk, dv, dg, dbias = O.attention_backward(
+        d["q"], d["k"], d["v"], d["gate"], d["key_mask"], d["bias"], dout)
+    grads = dict(q=dq, k=dk, v=dv, gate=dg, bias=dbias)
+    eps = 1e-6
+    for name, g in grads.items():
+        base = d[name]
+        num = np.zeros_like(base)
+        it = np.nditer(base, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            e = dict(d)
+            plus = base.copy(); plus[idx] += eps
+            minus = base.copy(); minus[idx] -= eps
+            e[name] = plus
+            lp = loss_and_grads(e, dout)
+            e[name] = minus
+            lm = loss_and_grads(e, dout)
+            num[idx] = (lp - lm) / (2 * eps)
+        np.testing.assert_allclose(g, num, rtol=1e-6, atol=1e-8,
+                                   err_msg=f"gradient of {name}")
+
+
+def test_backward_matches_torch_autograd():
+    """Library routine: torch.autograd through softmax/sigmoid (fp64, CPU)."""
+    d = core_case(14, B=2, R=3, N=13, H=3, C=8, mask_rows=3)
+    dout = rnd(15, *d["q"].shape)
+    dq, dk, dv, dg, dbias = O.attention_backward(
+        d["q"], d["k"], d["v"], d["gate"], d["key_mask"], d["bias"], dout)
+    t = {k: torch.tensor(d[k], requires_grad=True)
+         for k in ("q", "k", "v", "gate", "bias")}
+    C = d["q"].shape[-1]
+    s = torch.einsum("brqhc,brkhc->brhqk", t["q"], t["k"]) / C ** 0.5
+    s = s + t["bias"][:, None]
+    keep = torch.tensor(d["key_mask"] != 0)[:, :, None, None, :]
+    s = s.masked_fill(~keep, float("-inf"))
+    p = torch.softmax(s, dim=-1)
+    o = torch.einsum("brhqk,brkhc->brqhc", p, t["v"]) * torch.sigmoid(t["gate"])
+    (o * torch.tensor(dout)).sum().backward()
+    for name, g in dict(q=dq, k=dk, v=dv, gate=dg, bias=dbias).items():
+        np.testing.assert_allclose(g, t[name].grad.numpy(), rtol=1e-10,
+                                   atol=1e-12, err_msg=name)
+
+
+def test_backward_closed_forms():
+    """Sum_k dBias[h,q,k] = 0 (softmax Jacobian annihilates constants),
+    Sum_k dK[k] = 0 (adding a constant vector to every key shifts each
+    query's logits uniformly), Sum_k dV[k] = Sum_q dO_pre[q] (rows of P sum
+    to one)."""
+    d = core_case(16, B=1, R=4, N=10, H=2, C=4)
+    dout = rnd(17, *d["q"].shape)
+    dq, dk, dv, dg, dbias = O.attention_backward(
+        d["q"], d["k"], d["v"], d["gate"], d["key_mask"], d["bias"], dout)
+    np.testing.assert_allclose(dbias.sum(-1), 0, atol=1e-12)
+    np.testing.assert_allclose(dk.sum(2), 0, atol=1e-12)
+    do_pre = dout * expit(d["gate"])
+    np.testing.assert_allclose(dv.sum(2), do_pre.sum(2), rtol=1e-12, atol=1e-12)
+
+
+def test_dbias_query_rows_matches_full_backward():
+    d = core_case(18, B=2, R=3, N=8, H=2, C=4, mask_rows=3)
+    dout = rnd(19, *d["q"].shape)
+    _, _, _, _, dbias = O.attention_backward(
+        d["q"], d["k"], d["v"], d["gate"], d["key_mask"], d["bias"], dout)
+    picks = [(0, 0), (1, 5), (0, 7)]
+    for b in range(2):
+        got = O.dbias_query_rows(d["q"], d["k"], d["v"], d["gate"],
+                                 d["key_mask"], d["bias"], dout, b, picks)
+        for t, (h, qi) in enumerate(picks):
+            np.testing.assert_allclose(got[t], dbias[b, h, qi], rtol=1e-12,
+                                       atol=1e-13)
+
+
+# ------------------------------------------------------------------ module
+
+def module_case(seed, N=7, CZ=12, H=2, C=3, mask=True):
+    rng = np.random.default_rng(seed)
+    HC = H * C
+    d = dict(z=rng.standard_normal((N, N, CZ)),
+             ln_w=1 + 0.2 * rng.standard_normal(CZ),
+             ln_b=0.2 * rng.standard_normal(CZ), eps=1e-5,
+             w_q=rng.standard_normal((CZ, HC)) / CZ ** 0.5,
+             w_k=rng.standard_normal((CZ, HC)) / CZ ** 0.5,
+             w_v=rng.standard_normal((CZ, HC)) / CZ ** 0.5,
+             w_g=rng.standard_normal((CZ, HC)) / CZ ** 0.5,
+             b_g=0.3 * rng.standard_normal(HC),
+             w_bias=rng.standard_normal((CZ, H)) / CZ ** 0.5,
+             w_o=rng.standard_normal((HC, CZ)) / HC ** 0.5,
+             b_o=0.3 * rng.standard_normal(CZ), H=H, C=C)
+    if mask:
+        m = (rng.random(N) < 0.7).astype(np.uint8)
+        m[0] = 1
+        d["residue_mask"] = m
+    else:
+        d["residue_mask"] = None
+    return d
+
+
+def module(d, ending, z=None, mask="same"):
+    args = dict(d)
+    if z is not None:
+        args["z"] = z
+    if not (isinstance(mask, str) and mask == "same"):
+        args["residue_mask"] = mask
+    return O.tri_module_forward(ending=ending, **args)
+
+
+def test_layer_norm_matches_torch():
+    x = rnd(20, 5, 6, 17)
+    w, b = rnd(21, 17), rnd(22, 17)
+    ref = F.layer_norm(torch.tensor(x), (17,), torch.tensor(w), torch.tensor(b),
+                       1e-5).numpy()
+    np.testing.assert_allclose(O.layer_norm(x, w, b, 1e-5), ref, rtol=1e-12,
+                               atol=1e-12)
+
+
+@pytest.mark.parametrize("masked", [False, True])
+def test_ending_node_is_transposed_starting_node(masked):
+    """Column-wise reading (line = column j, bias b_ki) agrees with the
+    transposition reading: end(z) = T(start(T(z)))."""
+    d = module_case(23, mask=masked)
+    end = module(d, True)
+    zt = d["z"].transpose(1, 0, 2)
+    start_t = module(d, False, z=zt)
+    np.testing.assert_allclose(end, start_t.transpose(1, 0, 2), rtol=1e-12,
+                               atol=1e-12)
+
+
+@pytest.mark.parametrize("ending", [False, True])
+def test_residue_permutation_equivariance(ending):
+    """Relabelling residues permutes the output identically, f(P z P^T) =
+    P f(z) P^T, with the residue mask permuted alike ("Two properties the
+    tests assert": residue-permutation equivariance)."""
+    d = module_case(24)
+    out = module(d, ending)
+    perm = np.random.default_rng(24).permutation(d["z"].shape[0])
+    zp = d["z"][perm][:, perm]
+    outp = module(d, ending, z=zp, mask=d["residue_mask"][perm])
+    np.testing.assert_allclose(outp, out[perm][:, perm], rtol=1e-11,
+                               atol=1e-12)
+
+
+@pytest.mark.parametrize("ending", [False, True])
+def test_module_equals_project_core_outproject(ending):
+    d = module_case(25)
+    H, C = d["H"], d["C"]
+    q, k, v, g, bias = O.tri_project(d["z"], d["ln_w"], d["ln_b"], d["eps"],
+                                     d["w_q"], d["w_k"], d["w_v"], d["w_g"],
+                                     d["b_g"], d["w_bias"], H, C, ending)
+    N = d["z"].shape[0]
+    km = d["residue_mask"][None, None, :]
+    o, _ = O.attention_forward(q, k, v, g, km, bias)
+    out = O.tri_out_project(o, d["w_o"], d["b_o"], ending)
+    np.testing.assert_allclose(out, module(d, ending), rtol=1e-12, atol=1e-12)
+    # and the project layout itself against plain per-position matmuls
+    x = O.layer_norm(d["z"], d["ln_w"], d["ln_b"], d["eps"])
+    i, j = 2, 5
+    qi = (x[i, j] @ d["w_q"]).reshape(H, C)
+    line, pos = (j, i) if ending else (i, j)
+    np.testing.assert_allclose(q[0, line, pos], qi, rtol=1e-12, atol=1e-13)
+    bij = x[i, j] @ d["w_bias"]
+    # starting: bias[h, j', k'] = b_{j'k'} ; ending: bias[h, i', k'] = b_{k'i'}
+    if ending:
+        np.testing.assert_allclose(bias[0, :, j, i], bij, rtol=1e-12)
+    else:
+        np.testing.assert_allclose(bias[0, :, i, j], bij, rtol=1e-12)
+    assert N == q.shape[1]
+
+
+def test_module_lines_subset():
+    d = module_case(26)
+    full = module(d, True)
+    sub = O.tri_module_lines(lines=[1, 4], ending=True, **d)
+    np.testing.assert_allclose(sub[0], full[:, 1], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(sub[1], full[:, 4], rtol=1e-13, atol=1e-13)
+
+
+# -------------------------------------------------------- planted mistakes
+
+def _sdpa_pin(monkeypatch=None):
+    try:
+        test_matches_torch_sdpa(True, True)
+        return True
+    except AssertionError:
+        return False
+
+
+def test_mutant_scale_omitted_is_caught(monkeypatch):
+    orig = O._line_logits
+
+    def no_scale(q, k, bias, keep, h):
+        return orig(q * np.sqrt(q.shape[-1]), k, bias, keep, h)
+    monkeypatch.setattr(O, "_line_logits", no_scale)
+    assert not _sdpa_pin()
+
+
+def test_mutant_bias_transposed_is_caught(monkeypatch):
+    orig = O._line_logits
+
+    def bias_t(q, k, bias, keep, h):
+        return orig(q, k, None if bias is None else bias.transpose(0, 2, 1),
+                    keep, h)
+    monkeypatch.setattr(O, "_line_logits", bias_t)
+    assert not _sdpa_pin()
+    with pytest.raises(AssertionError):
+        test_key_permutation_with_bias_columns_is_invariant()
+
+
+def test_mutant_mask_ignored_is_caught(monkeypatch):
+    orig = O._line_logits
+    monkeypatch.setattr(O, "_line_logits",
+                        lambda q, k, bias, keep, h: orig(q, k, bias, None, h))
+    with pytest.raises(AssertionError):
+        test_single_live_key_returns_its_value_gated()
+
+
+def test_mutant_gate_not_squashed_is_caught(monkeypatch):
+    monkeypatch.setattr(O, "sigmoid", lambda x: np.asarray(x, np.float64))
+    with pytest.raises(AssertionError):
+        test_single_live_key_returns_its_value_gated()
+
+
+def test_mutant_softmax_over_queries_is_caught(monkeypatch):
+    orig = O._line_logits
+    monkeypatch.setattr(O, "_line_logits",
+                        lambda q, k, bias, keep, h: orig(q, k, bias, keep, h).T)
+    assert not _sdpa_pin()
+
+
+def test_mutant_dbias_one_row_is_caught(monkeypatch):
+    orig = O.attention_line_backward
+    state = {"n": 0}
+
+    def one_row(*a):
+        res = list(orig(*a))
+        state["n"] += 1
+        if state["n"] > 1:
+            res[4] = np.zeros_like(res[4])
+        return tuple(res)
+    monkeypatch.setattr(O, "attention_line_backward", one_row)
+    with pytest.raises(AssertionError):
+        test_backward_matches_torch_autograd()
+
+
+def test_mutant_ending_bias_untransposed_is_caught(monkeypatch):
+    orig = O._pair_bias
+
+    def sym(z, ln_w, ln_b, eps, w_bias):
+        b = orig(z, ln_w, ln_b, eps, w_bias)
+        return b.transpose(1, 0, 2)
+    monkeypatch.setattr(O, "_pair_bias", sym)
+    with pytest.raises(AssertionError):
+        test_module_lines_subset_against_project()
+
+
+def test_module_lines_subset_against_project():
+    """Line-wise module (own bias path) against project + core + out-proj."""
+    for ending in (False, True):
+        d = module_case(27)
+        q, k, v, g, bias = O.tri_project(d["z"], d["ln_w"], d["ln_b"],
+                                         d["eps"], d["w_q"], d["w_k"],
+                                         d["w_v"], d["w_g"], d["b_g"],
+                                         d["w_bias"], d["H"], d["C"], ending)
+        km = d["residue_mask"][None, None, :]
+        o, _ = O.attention_forward(q, k, v, g, km, bias)
+        out = O.tri_out_project(o, d["w_o"], d["b_o"], ending)
+        sub = O.tri_module_lines(lines=[3], ending=ending, **d)[0]
+        ref = out[:, 3] if ending else out[3]
+        np.testing.assert_allclose(sub, ref, rtol=1e-12, atol=1e-12)
