@@ -1,0 +1,354 @@
+// C ABI of libevoattn.so (declared in include/evo_attn.h): argument
+// validation, error reporting and dispatch to the kernel launchers.
+// Every check runs before the first HIP call, so an invalid call enqueues
+// nothing and touches no device state.
+#include "evo_attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "evo_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+evo_status_t fail(evo_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+evo_status_t ok() {
+  g_last_error.clear();
+  return EVO_OK;
+}
+
+// Test hook: EVO_FAULT_INJECT=launch makes every entry point report a HIP
+// launch failure after validation, without touching the device.
+bool fault_injected() {
+  const char* e = std::getenv("EVO_FAULT_INJECT");
+  return e && std::strcmp(e, "launch") == 0;
+}
+
+evo_status_t from_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(EVO_EHIP, "%s: HIP error %d (%s)", what, (int)e,
+              hipGetErrorString(e));
+}
+
+size_t elem_size(evo_dtype_t dt) { return dt == EVO_BF16 ? 2 : 4; }
+
+bool aligned16(const void* p) {
+  return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+// Largest element count any single tensor may have (kernel offsets are
+// 64-bit, work-item counts 32-bit).
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+
+evo_status_t check_dtype(evo_dtype_t dt) {
+  if (dt != EVO_FP32 && dt != EVO_BF16)
+    return fail(EVO_ENOTSUP, "dtype %d is not supported (EVO_FP32=0, "
+                "EVO_BF16=1)", (int)dt);
+  return EVO_OK;
+}
+
+evo_status_t check_core_sizes(evo_dtype_t dt, int64_t B, int64_t R, int64_t N,
+                              int64_t H, int64_t C) {
+  evo_status_t st = check_dtype(dt);
+  if (st != EVO_OK) return st;
+  if (B <= 0 || R <= 0 || N <= 0 || H <= 0 || C <= 0)
+    return fail(EVO_EINVAL, "sizes must be positive (B=%lld R=%lld N=%lld "
+                "H=%lld C=%lld)", (long long)B, (long long)R, (long long)N,
+                (long long)H, (long long)C);
+  if (C != evo::kHeadDim)
+    return fail(EVO_ENOTSUP, "head dimension C=%lld is not supported (only "
+                "C=32)", (long long)C);
+  if (N > (int64_t(1) << 20) || H > 4096 || R > (int64_t(1) << 24) ||
+      B > (int64_t(1) << 24))
+    return fail(EVO_ENOTSUP, "problem too large (N<=2^20, H<=4096, R,B<=2^24)");
+  if (B * R * N * H * C > kMaxElems || B * H * N * N > kMaxElems)
+    return fail(EVO_ENOTSUP, "problem too large: tensors above 2^40 elements");
+  return EVO_OK;
+}
+
+#define REQUIRE_PTR(p)                                                   \
+  do {                                                                   \
+    if (!(p)) return fail(EVO_EINVAL, "argument '%s' is NULL", #p);      \
+    if (!aligned16(p))                                                   \
+      return fail(EVO_ENOTSUP, "argument '%s' is not 16-byte aligned", #p); \
+  } while (0)
+
+#define OPTIONAL_PTR(p)                                                  \
+  do {                                                                   \
+    if ((p) && !aligned16(p))                                            \
+      return fail(EVO_ENOTSUP, "argument '%s' is not 16-byte aligned", #p); \
+  } while (0)
+
+evo_status_t check_mask(const uint8_t* key_mask, int64_t mask_rows,
+                        int64_t R) {
+  if (!key_mask) return EVO_OK;
+  if (mask_rows != 1 && mask_rows != R)
+    return fail(EVO_EINVAL, "mask_rows=%lld must be 1 or R=%lld",
+                (long long)mask_rows, (long long)R);
+  return EVO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int evo_abi_version(void) { return 1; }
+
+const char* evo_last_error(void) { return g_last_error.c_str(); }
+
+evo_status_t evo_attn_fwd(evo_dtype_t dtype, int64_t B, int64_t R, int64_t N,
+                          int64_t H, int64_t C, const void* q, const void* k,
+                          const void* v, const void* gate,
+                          const uint8_t* key_mask, int64_t mask_rows,
+                          const void* bias, void* out, float* lse,
+                          void* stream) {
+  try {
+    evo_status_t st = check_core_sizes(dtype, B, R, N, H, C);
+    if (st != EVO_OK) return st;
+    REQUIRE_PTR(q);
+    REQUIRE_PTR(k);
+    REQUIRE_PTR(v);
+    REQUIRE_PTR(out);
+    OPTIONAL_PTR(gate);
+    OPTIONAL_PTR(bias);
+    OPTIONAL_PTR(lse);
+    OPTIONAL_PTR(key_mask);
+    if ((st = check_mask(key_mask, mask_rows, R)) != EVO_OK) return st;
+    if (fault_injected()) return fail(EVO_EHIP, "evo_attn_fwd: injected launch failure");
+    evo::AttnFwdArgs a{(int)dtype, B, R, N, H, q, k, v, gate, key_mask,
+                       mask_rows, bias, out, lse};
+    return from_hip(evo::launch_attn_fwd(a, (hipStream_t)stream),
+                    "evo_attn_fwd");
+  } catch (...) {
+    return fail(EVO_EINTERNAL, "evo_attn_fwd: internal error");
+  }
+}
+
+size_t evo_attn_bwd_workspace_bytes(evo_dtype_t dtype, int64_t B, int64_t R,
+                                    int64_t N, int64_t H, int64_t C) {
+  const std::string saved = g_last_error;
+  const evo_status_t st = check_core_sizes(dtype, B, R, N, H, C);
+  g_last_error = saved;
+  if (st != EVO_OK) return 0;
+  return evo::attn_bwd_workspace((int)dtype, B, R, N, H);
+}
+
+evo_status_t evo_attn_bwd(evo_dtype_t dtype, int64_t B, int64_t R, int64_t N,
+                          int64_t H, int64_t C, const void* q, const void* k,
+                          const void* v, const void* gate,
+                          const uint8_t* key_mask, int64_t mask_rows,
+                          const void* bias, const void* out, const float* lse,
+                          const void* dout, void* dq, void* dk, void* dv,
+                          void* dgate, float* dbias, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  try {
+    evo_status_t st = check_core_sizes(dtype, B, R, N, H, C);
+    if (st != EVO_OK) return st;
+    REQUIRE_PTR(q);
+    REQUIRE_PTR(k);
+    REQUIRE_PTR(v);
+    REQUIRE_PTR(out);
+    REQUIRE_PTR(lse);
+    REQUIRE_PTR(dout);
+    REQUIRE_PTR(dq);
+    REQUIRE_PTR(dk);
+    REQUIRE_PTR(dv);
+    OPTIONAL_PTR(gate);
+    OPTIONAL_PTR(dgate);
+    OPTIONAL_PTR(bias);
+    OPTIONAL_PTR(dbias);
+    if ((gate == nullptr) != (dgate == nullptr))
+      return fail(EVO_EINVAL, "dgate must be given exactly when gate is");
+    OPTIONAL_PTR(key_mask);
+    if ((st = check_mask(key_mask, mask_rows, R)) != EVO_OK) return st;
+    const size_t need = evo::attn_bwd_workspace((int)dtype, B, R, N, H);
+    if (need == 0)
+      return fail(EVO_ENOTSUP, "evo_attn_bwd supports N <= 1024 (N=%lld)",
+                  (long long)N);
+    if (!workspace || workspace_bytes < need)
+      return fail(EVO_EWORKSPACE, "workspace of %zu bytes needed, %zu given",
+                  need, workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace))
+      return fail(EVO_ENOTSUP, "argument 'workspace' is not 16-byte aligned");
+    if (fault_injected()) return fail(EVO_EHIP, "evo_attn_bwd: injected launch failure");
+    evo::AttnBwdArgs a{(int)dtype, B, R, N, H, q, k, v, gate, key_mask,
+                       mask_rows, bias, out, lse, dout, dq, dk, dv, dgate,
+                       dbias, workspace};
+    return from_hip(evo::launch_attn_bwd(a, (hipStream_t)stream),
+                    "evo_attn_bwd");
+  } catch (...) {
+    return fail(EVO_EINTERNAL, "evo_attn_bwd: internal error");
+  }
+}
+
+static evo_status_t check_module_sizes(evo_dtype_t dtype, int64_t N,
+                                       int64_t CZ, int64_t H, int64_t C) {
+  evo_status_t st = check_core_sizes(dtype, 1, N, N, H, C);
+  if (st != EVO_OK) return st;
+  if (CZ <= 0) return fail(EVO_EINVAL, "CZ=%lld must be positive", (long long)CZ);
+  if (CZ % 32 != 0 || CZ > 256)
+    return fail(EVO_ENOTSUP, "CZ=%lld is not supported (multiple of 32, at "
+                "most 256)", (long long)CZ);
+  if (H * C > 256)
+    return fail(EVO_ENOTSUP, "H*C=%lld is not supported (at most 256)",
+                (long long)(H * C));
+  return EVO_OK;
+}
+
+evo_status_t tri_attn_project(evo_dtype_t dtype, int64_t N, int64_t CZ,
+                              int64_t H, int64_t C, int ending, const void* z,
+                              const void* ln_w, const void* ln_b, float ln_eps,
+                              const void* w_q, const void* w_k,
+                              const void* w_v, const void* w_g,
+                              const void* b_g, const void* w_bias, void* q,
+                              void* k, void* v, void* g, void* bias,
+                              void* stream) {
+  try {
+    evo_status_t st = check_module_sizes(dtype, N, CZ, H, C);
+    if (st != EVO_OK) return st;
+    if (ending != 0 && ending != 1)
+      return fail(EVO_EINVAL, "ending=%d must be 0 or 1", ending);
+    if (!(ln_eps > 0.f)) return fail(EVO_EINVAL, "ln_eps must be > 0");
+    REQUIRE_PTR(z);
+    REQUIRE_PTR(ln_w);
+    REQUIRE_PTR(ln_b);
+    REQUIRE_PTR(w_q);
+    REQUIRE_PTR(w_k);
+    REQUIRE_PTR(w_v);
+    REQUIRE_PTR(w_g);
+    REQUIRE_PTR(w_bias);
+    REQUIRE_PTR(q);
+    REQUIRE_PTR(k);
+    REQUIRE_PTR(v);
+    REQUIRE_PTR(g);
+    REQUIRE_PTR(bias);
+    OPTIONAL_PTR(b_g);
+    if (fault_injected()) return fail(EVO_EHIP, "tri_attn_project: injected launch failure");
+    evo::ProjectArgs a{(int)dtype, N, CZ, H, ending, z, ln_w, ln_b, ln_eps,
+                       w_q, w_k, w_v, w_g, b_g, w_bias, q, k, v, g, bias};
+    return from_hip(evo::launch_project(a, (hipStream_t)stream),
+                    "tri_attn_project");
+  } catch (...) {
+    return fail(EVO_EINTERNAL, "tri_attn_project: internal error");
+  }
+}
+
+evo_status_t tri_attn_out_project(evo_dtype_t dtype, int64_t N, int64_t CZ,
+                                  int64_t H, int64_t C, int ending,
+                                  const void* o, const void* w_o,
+                                  const void* b_o, void* out, void* stream) {
+  try {
+    evo_status_t st = check_module_sizes(dtype, N, CZ, H, C);
+    if (st != EVO_OK) return st;
+    if (ending != 0 && ending != 1)
+      return fail(EVO_EINVAL, "ending=%d must be 0 or 1", ending);
+    REQUIRE_PTR(o);
+    REQUIRE_PTR(w_o);
+    REQUIRE_PTR(out);
+    OPTIONAL_PTR(b_o);
+    if (fault_injected()) return fail(EVO_EHIP, "tri_attn_out_project: injected launch failure");
+    evo::OutProjectArgs a{(int)dtype, N, CZ, H, ending, o, w_o, b_o, out};
+    return from_hip(evo::launch_out_project(a, (hipStream_t)stream),
+                    "tri_attn_out_project");
+  } catch (...) {
+    return fail(EVO_EINTERNAL, "tri_attn_out_project: internal error");
+  }
+}
+
+// Workspace layout of tri_attn_module_fwd: q | k | v | g | o (each
+// N*N*H*C elements) | bias (H*N*N elements), each region 256-byte aligned.
+static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+size_t tri_attn_workspace_bytes(evo_dtype_t dtype, int64_t N, int64_t CZ,
+                                int64_t H, int64_t C) {
+  const std::string saved = g_last_error;
+  const evo_status_t st = check_module_sizes(dtype, N, CZ, H, C);
+  g_last_error = saved;
+  if (st != EVO_OK) return 0;
+  const size_t es = elem_size(dtype);
+  const size_t t = align256((size_t)N * N * H * C * es);
+  const size_t b = align256((size_t)H * N * N * es);
+  return 5 * t + b;
+}
+
+evo_status_t tri_attn_module_fwd(evo_dtype_t dtype, int64_t N, int64_t CZ,
+                                 int64_t H, int64_t C, int ending,
+                                 const void* z, const uint8_t* residue_mask,
+                                 const void* ln_w, const void* ln_b,
+                                 float ln_eps, const void* w_q,
+                                 const void* w_k, const void* w_v,
+                                 const void* w_g, const void* b_g,
+                                 const void* w_bias, const void* w_o,
+                                 const void* b_o, void* out, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  try {
+    evo_status_t st = check_module_sizes(dtype, N, CZ, H, C);
+    if (st != EVO_OK) return st;
+    if (ending != 0 && ending != 1)
+      return fail(EVO_EINVAL, "ending=%d must be 0 or 1", ending);
+    if (!(ln_eps > 0.f)) return fail(EVO_EINVAL, "ln_eps must be > 0");
+    REQUIRE_PTR(z);
+    REQUIRE_PTR(ln_w);
+    REQUIRE_PTR(ln_b);
+    REQUIRE_PTR(w_q);
+    REQUIRE_PTR(w_k);
+    REQUIRE_PTR(w_v);
+    REQUIRE_PTR(w_g);
+    REQUIRE_PTR(w_bias);
+    REQUIRE_PTR(w_o);
+    REQUIRE_PTR(out);
+    OPTIONAL_PTR(b_g);
+    OPTIONAL_PTR(b_o);
+    OPTIONAL_PTR(residue_mask);
+    const size_t need = tri_attn_workspace_bytes(dtype, N, CZ, H, C);
+    if (!workspace || workspace_bytes < need)
+      return fail(EVO_EWORKSPACE, "workspace of %zu bytes needed, %zu given",
+                  need, workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace))
+      return fail(EVO_ENOTSUP, "argument 'workspace' is not 16-byte aligned");
+    if (fault_injected()) return fail(EVO_EHIP, "tri_attn_module_fwd: injected launch failure");
+
+    const size_t es = elem_size(dtype);
+    const size_t t = align256((size_t)N * N * H * C * es);
+    char* ws = static_cast<char*>(workspace);
+    void* q = ws;
+    void* k = ws + t;
+    void* v = ws + 2 * t;
+    void* g = ws + 3 * t;
+    void* o = ws + 4 * t;
+    void* bias = ws + 5 * t;
+    hipStream_t s = (hipStream_t)stream;
+
+    evo::ProjectArgs pa{(int)dtype, N, CZ, H, ending, z, ln_w, ln_b, ln_eps,
+                        w_q, w_k, w_v, w_g, b_g, w_bias, q, k, v, g, bias};
+    st = from_hip(evo::launch_project(pa, s), "tri_attn_module_fwd/project");
+    if (st != EVO_OK) return st;
+    evo::AttnFwdArgs fa{(int)dtype, 1, N, N, H, q, k, v, g, residue_mask, 1,
+                        bias, o, nullptr};
+    st = from_hip(evo::launch_attn_fwd(fa, s), "tri_attn_module_fwd/attention");
+    if (st != EVO_OK) return st;
+    evo::OutProjectArgs oa{(int)dtype, N, CZ, H, ending, o, w_o, b_o, out};
+    return from_hip(evo::launch_out_project(oa, s),
+                    "tri_attn_module_fwd/out_project");
+  } catch (...) {
+    return fail(EVO_EINTERNAL, "tri_attn_module_fwd: internal error");
+  }
+}
+
+}  // extern "C"

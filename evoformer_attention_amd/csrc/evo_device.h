@@ -1,0 +1,115 @@
+// Device-side building blocks for the gfx950 (CDNA4) kernels: operand
+// fragments, MFMA wrappers, conversions and the workgroup -> XCD mapping.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace evo {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t bf16_t;  // bfloat16 storage in HBM
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kNumXcd = 8;  // MI355X: 8 accelerator complex dies, 32 CUs each
+
+// Element traits.  An MFMA operand fragment holds, per lane, 8 values that
+// are consecutive along the contraction index.
+template <typename T> struct Tr;
+template <> struct Tr<bf16_t> {
+  using Op = bf16x8;
+  static __device__ __forceinline__ float to_f(bf16_t x) {
+    return __uint_as_float(uint32_t(x) << 16);
+  }
+  static __device__ __forceinline__ bf16_t from_f(float x) {
+    __bf16 b = (__bf16)x;  // v_cvt_pk_bf16_f32: round to nearest even
+    return __builtin_bit_cast(bf16_t, b);
+  }
+};
+template <> struct Tr<float> {
+  using Op = f32x8;
+  static __device__ __forceinline__ float to_f(float x) { return x; }
+  static __device__ __forceinline__ float from_f(float x) { return x; }
+};
+
+// 16x16 output tile, contraction depth 32.  Lane l holds A[l%16][8*(l/16)+j]
+// and B[8*(l/16)+j][l%16] for j < 8, and C/D[4*(l/16)+i][l%16] for i < 4.
+__device__ __forceinline__ f32x4 mma32(const bf16x8& a, const bf16x8& b,
+                                       f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// fp32 version: eight 16x16x4 steps.  Step j contracts over the values each
+// lane holds at position j, i.e. over the depth indices {8g + j : g < 4};
+// the eight steps together cover the same 32 indices as the bf16 form, so
+// both share one fragment layout.
+__device__ __forceinline__ f32x4 mma32(const f32x8& a, const f32x8& b,
+                                       f32x4 c) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], c, 0, 0, 0);
+  return c;
+}
+
+__device__ __forceinline__ float exp2_fast(float x) {
+  return __builtin_amdgcn_exp2f(x);  // v_exp_f32; exp2(-inf) = 0
+}
+__device__ __forceinline__ float log2_fast(float x) {
+  return __builtin_amdgcn_logf(x);  // v_log_f32 (base 2)
+}
+__device__ __forceinline__ float rcp_fast(float x) {
+  return __builtin_amdgcn_rcpf(x);
+}
+__device__ __forceinline__ float sigmoid_f(float x) {
+  return rcp_fast(1.0f + exp2_fast(-x * kLog2e));
+}
+
+__device__ __forceinline__ float shfl_xor(float v, int mask) {
+  return __shfl_xor(v, mask, 64);
+}
+
+// Pack 8 fp32 values into an operand fragment of type Op.
+__device__ __forceinline__ bf16x8 pack8(const f32x4& a, const f32x4& b,
+                                        bf16x8*) {
+  bf16x8 r;
+  r[0] = (__bf16)a[0]; r[1] = (__bf16)a[1]; r[2] = (__bf16)a[2];
+  r[3] = (__bf16)a[3]; r[4] = (__bf16)b[0]; r[5] = (__bf16)b[1];
+  r[6] = (__bf16)b[2]; r[7] = (__bf16)b[3];
+  return r;
+}
+__device__ __forceinline__ f32x8 pack8(const f32x4& a, const f32x4& b,
+                                       f32x8*) {
+  f32x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+  r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
+  return r;
+}
+
+// Scale every element of a fragment (in fp32, rounded back to the type).
+__device__ __forceinline__ bf16x8 scale8(const bf16x8& v, float s) {
+  bf16x8 r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = (__bf16)((float)v[j] * s);
+  return r;
+}
+__device__ __forceinline__ f32x8 scale8(const f32x8& v, float s) {
+  return v * s;
+}
+
+// Workgroups are dispatched round-robin over the XCDs (workgroup i runs on
+// XCD i % 8).  Remap so that XCD x receives the contiguous work range
+// [x * per, (x + 1) * per): neighbouring work items, which share inputs,
+// then run together on one XCD and meet in its L2.  `total` is the real
+// number of work items; the grid has per * 8 workgroups and the function
+// returns -1 for the padding ones.
+__device__ __forceinline__ int xcd_work_index(int total) {
+  const int per = (total + kNumXcd - 1) / kNumXcd;
+  const int i = blockIdx.x;
+  const int w = (i % kNumXcd) * per + i / kNumXcd;
+  return w < total ? w : -1;
+}
+
+}  // namespace evo

@@ -1,0 +1,86 @@
+// Internal interface between the C-ABI layer (evo_api.cpp) and the kernel
+// translation units.  Arguments reaching these functions are validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace evo {
+
+struct AttnFwdArgs {
+  int dtype;  // 0 fp32, 1 bf16
+  int64_t B, R, N, H;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* gate;       // may be null
+  const uint8_t* mask;    // may be null
+  int64_t mask_rows;      // 1 or R
+  const void* bias;       // may be null
+  void* out;
+  float* lse;             // may be null
+};
+
+struct AttnBwdArgs {
+  int dtype;
+  int64_t B, R, N, H;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* gate;
+  const uint8_t* mask;
+  int64_t mask_rows;
+  const void* bias;
+  const void* out;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  void* dgate;
+  float* dbias;
+  void* workspace;
+};
+
+struct ProjectArgs {
+  int dtype;
+  int64_t N, CZ, H;
+  int ending;
+  const void* z;
+  const void* ln_w;
+  const void* ln_b;
+  float eps;
+  const void* w_q;
+  const void* w_k;
+  const void* w_v;
+  const void* w_g;
+  const void* b_g;  // may be null
+  const void* w_bias;
+  void* q;
+  void* k;
+  void* v;
+  void* g;
+  void* bias;
+};
+
+struct OutProjectArgs {
+  int dtype;
+  int64_t N, CZ, H;
+  int ending;
+  const void* o;
+  const void* w_o;
+  const void* b_o;  // may be null
+  void* out;
+};
+
+constexpr int kHeadDim = 32;
+
+hipError_t launch_attn_fwd(const AttnFwdArgs& a, hipStream_t s);
+size_t attn_bwd_workspace(int dtype, int64_t B, int64_t R, int64_t N,
+                          int64_t H);
+hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t s);
+hipError_t launch_project(const ProjectArgs& a, hipStream_t s);
+hipError_t launch_out_project(const OutProjectArgs& a, hipStream_t s);
+
+}  // namespace evo

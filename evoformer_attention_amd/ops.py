@@ -1,0 +1,259 @@
+"""Thin torch-tensor binding over libevoattn.so (include/evo_attn.h).
+
+Each function has the name of the C entry point it calls and does argument
+marshalling only: shape/dtype/device checks, output allocation through
+torch, the data pointers and torch's current HIP stream.  Every step of the
+computation runs in the library's kernels.  A missing library is an error
+(there is no fallback), and a non-OK status raises EvoAttnError with the
+library's message.
+"""
+import ctypes
+import os
+
+import torch
+
+__all__ = ["EvoAttnError", "lib", "evo_abi_version", "evo_attn_fwd",
+           "evo_attn_bwd", "evo_attn_bwd_workspace_bytes", "tri_attn_project",
+           "tri_attn_out_project", "tri_attn_module_fwd",
+           "tri_attn_workspace_bytes", "LIB_PATH", "EXPORTS"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                        "libevoattn.so")
+
+EVO_OK, EVO_EINVAL, EVO_ENOTSUP, EVO_EWORKSPACE, EVO_EHIP, EVO_EINTERNAL = range(6)
+EVO_FP32, EVO_BF16 = 0, 1
+STATUS_NAMES = {0: "EVO_OK", 1: "EVO_EINVAL", 2: "EVO_ENOTSUP",
+                3: "EVO_EWORKSPACE", 4: "EVO_EHIP", 5: "EVO_EINTERNAL"}
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I = ctypes.c_int
+_F = ctypes.c_float
+_SZ = ctypes.c_size_t
+
+# Name -> (restype, argtypes), mirroring include/evo_attn.h.
+EXPORTS = {
+    "evo_abi_version": (_I, []),
+    "evo_last_error": (ctypes.c_char_p, []),
+    "evo_attn_fwd": (_I, [_I, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P,
+                          _P, _I64, _P, _P, _P, _P]),
+    "evo_attn_bwd_workspace_bytes": (_SZ, [_I, _I64, _I64, _I64, _I64, _I64]),
+    "evo_attn_bwd": (_I, [_I, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P,
+                          _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                          _SZ, _P]),
+    "tri_attn_project": (_I, [_I, _I64, _I64, _I64, _I64, _I, _P, _P, _P, _F,
+                              _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                              _P]),
+    "tri_attn_out_project": (_I, [_I, _I64, _I64, _I64, _I64, _I, _P, _P, _P,
+                                  _P, _P]),
+    "tri_attn_workspace_bytes": (_SZ, [_I, _I64, _I64, _I64, _I64]),
+    "tri_attn_module_fwd": (_I, [_I, _I64, _I64, _I64, _I64, _I, _P, _P, _P,
+                                 _P, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                 _P, _SZ, _P]),
+}
+
+
+class EvoAttnError(RuntimeError):
+    def __init__(self, fn, status, message):
+        self.status = status
+        super().__init__(f"{fn}: {STATUS_NAMES.get(status, status)}: {message}")
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library (ctypes.CDLL) with prototypes set."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m evoformer_attention_amd.build` (hipcc, gfx950)")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in EXPORTS.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _check(fn, status):
+    if status != EVO_OK:
+        msg = lib().evo_last_error().decode(errors="replace")
+        raise EvoAttnError(fn, status, msg)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return EVO_BF16
+    if t.dtype == torch.float32:
+        return EVO_FP32
+    raise EvoAttnError("binding", EVO_ENOTSUP, f"dtype {t.dtype} not supported")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dev_tensor(name, t, dtype=None, shape=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise EvoAttnError("binding", EVO_EINVAL, f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise EvoAttnError("binding", EVO_EINVAL, f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise EvoAttnError("binding", EVO_EINVAL,
+                           f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise EvoAttnError("binding", EVO_EINVAL,
+                           f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def evo_abi_version():
+    return lib().evo_abi_version()
+
+
+def evo_attn_fwd(q, k, v, gate=None, key_mask=None, bias=None, out=None,
+                 want_lse=False):
+    """Forward of biased gated attention.  q, k, v, gate: [B,R,N,H,C];
+    key_mask: uint8 [B,1,N] or [B,R,N]; bias: [B,H,N,N].  Returns out, or
+    (out, lse) with lse [B,R,H,N] fp32 when want_lse."""
+    _dev_tensor("q", q)
+    B, R, N, H, C = q.shape
+    dt = q.dtype
+    _dev_tensor("k", k, dt, q.shape)
+    _dev_tensor("v", v, dt, q.shape)
+    _dev_tensor("gate", gate, dt, q.shape)
+    _dev_tensor("bias", bias, dt, (B, H, N, N))
+    mask_rows = 0
+    if key_mask is not None:
+        _dev_tensor("key_mask", key_mask, torch.uint8)
+        if key_mask.dim() != 3 or key_mask.shape[0] != B or key_mask.shape[2] != N:
+            raise EvoAttnError("binding", EVO_EINVAL,
+                               f"key_mask has shape {tuple(key_mask.shape)}")
+        mask_rows = key_mask.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    _dev_tensor("out", out, dt, q.shape)
+    lse = torch.empty((B, R, H, N), dtype=torch.float32, device=q.device) if want_lse else None
+    st = lib().evo_attn_fwd(_dtype_code(q), B, R, N, H, C, _ptr(q), _ptr(k),
+                            _ptr(v), _ptr(gate), _ptr(key_mask), mask_rows,
+                            _ptr(bias), _ptr(out), _ptr(lse), _stream(q.device))
+    _check("evo_attn_fwd", st)
+    return (out, lse) if want_lse else out
+
+
+def evo_attn_bwd_workspace_bytes(dtype, B, R, N, H, C):
+    code = EVO_BF16 if dtype == torch.bfloat16 else EVO_FP32
+    return lib().evo_attn_bwd_workspace_bytes(code, B, R, N, H, C)
+
+
+def evo_attn_bwd(q, k, v, gate, key_mask, bias, out, lse, dout,
+                 want_dbias=True, workspace=None):
+    """Backward of evo_attn_fwd.  Returns dq, dk, dv, dgate (None without a
+    gate) and dbias ([B,H,N,N] fp32, summed over rows; None unless
+    want_dbias)."""
+    _dev_tensor("q", q)
+    B, R, N, H, C = q.shape
+    dt = q.dtype
+    for name, t in (("k", k), ("v", v), ("out", out), ("dout", dout)):
+        _dev_tensor(name, t, dt, q.shape)
+    _dev_tensor("gate", gate, dt, q.shape)
+    _dev_tensor("bias", bias, dt, (B, H, N, N))
+    _dev_tensor("lse", lse, torch.float32, (B, R, H, N))
+    mask_rows = 0
+    if key_mask is not None:
+        _dev_tensor("key_mask", key_mask, torch.uint8)
+        mask_rows = key_mask.shape[1]
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    dg = torch.empty_like(q) if gate is not None else None
+    db = (torch.empty((B, H, N, N), dtype=torch.float32, device=q.device)
+          if want_dbias else None)
+    need = evo_attn_bwd_workspace_bytes(dt, B, R, N, H, C)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = lib().evo_attn_bwd(_dtype_code(q), B, R, N, H, C, _ptr(q), _ptr(k),
+                            _ptr(v), _ptr(gate), _ptr(key_mask), mask_rows,
+                            _ptr(bias), _ptr(out), _ptr(lse), _ptr(dout),
+                            _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(db),
+                            _ptr(workspace), workspace.numel(),
+                            _stream(q.device))
+    _check("evo_attn_bwd", st)
+    return dq, dk, dv, dg, db
+
+
+def tri_attn_project(z, ln_w, ln_b, eps, w_q, w_k, w_v, w_g, b_g, w_bias, H,
+                     C, ending):
+    """LayerNorm + projections.  Returns q, k, v, g [1,N,N,H,C] and bias
+    [1,H,N,N] in line layout."""
+    _dev_tensor("z", z)
+    N, _, CZ = z.shape
+    dt = z.dtype
+    for name, t in (("ln_w", ln_w), ("ln_b", ln_b), ("w_q", w_q), ("w_k", w_k),
+                    ("w_v", w_v), ("w_g", w_g), ("w_bias", w_bias), ("b_g", b_g)):
+        _dev_tensor(name, t, dt)
+    q = torch.empty((1, N, N, H, C), dtype=dt, device=z.device)
+    k, v, g = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    bias = torch.empty((1, H, N, N), dtype=dt, device=z.device)
+    st = lib().tri_attn_project(_dtype_code(z), N, CZ, H, C, int(ending),
+                                _ptr(z), _ptr(ln_w), _ptr(ln_b), float(eps),
+                                _ptr(w_q), _ptr(w_k), _ptr(w_v), _ptr(w_g),
+                                _ptr(b_g), _ptr(w_bias), _ptr(q), _ptr(k),
+                                _ptr(v), _ptr(g), _ptr(bias), _stream(z.device))
+    _check("tri_attn_project", st)
+    return q, k, v, g, bias
+
+
+def tri_attn_out_project(o, w_o, b_o, CZ, ending):
+    """Output projection of o [1,N,N,H,C] (line layout) -> [N,N,CZ]."""
+    _dev_tensor("o", o)
+    _, N, _, H, C = o.shape
+    _dev_tensor("w_o", w_o, o.dtype)
+    _dev_tensor("b_o", b_o, o.dtype)
+    out = torch.empty((N, N, CZ), dtype=o.dtype, device=o.device)
+    st = lib().tri_attn_out_project(_dtype_code(o), N, CZ, H, C, int(ending),
+                                    _ptr(o), _ptr(w_o), _ptr(b_o), _ptr(out),
+                                    _stream(o.device))
+    _check("tri_attn_out_project", st)
+    return out
+
+
+def tri_attn_workspace_bytes(dtype, N, CZ, H, C):
+    code = EVO_BF16 if dtype == torch.bfloat16 else EVO_FP32
+    return lib().tri_attn_workspace_bytes(code, N, CZ, H, C)
+
+
+def tri_attn_module_fwd(z, residue_mask, ln_w, ln_b, eps, w_q, w_k, w_v, w_g,
+                        b_g, w_bias, w_o, b_o, H, C, ending, workspace=None,
+                        out=None):
+    """Whole triangle-attention module forward -> [N,N,CZ] update."""
+    _dev_tensor("z", z)
+    N, _, CZ = z.shape
+    dt = z.dtype
+    for name, t in (("ln_w", ln_w), ("ln_b", ln_b), ("w_q", w_q), ("w_k", w_k),
+                    ("w_v", w_v), ("w_g", w_g), ("w_bias", w_bias),
+                    ("w_o", w_o), ("b_g", b_g), ("b_o", b_o)):
+        _dev_tensor(name, t, dt)
+    _dev_tensor("residue_mask", residue_mask, torch.uint8)
+    need = tri_attn_workspace_bytes(dt, N, CZ, H, C)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=z.device)
+    if out is None:
+        out = torch.empty((N, N, CZ), dtype=dt, device=z.device)
+    st = lib().tri_attn_module_fwd(_dtype_code(z), N, CZ, H, C, int(ending),
+                                   _ptr(z), _ptr(residue_mask), _ptr(ln_w),
+                                   _ptr(ln_b), float(eps), _ptr(w_q),
+                                   _ptr(w_k), _ptr(w_v), _ptr(w_g), _ptr(b_g),
+                                   _ptr(w_bias), _ptr(w_o), _ptr(b_o),
+                                   _ptr(out), _ptr(workspace),
+                                   workspace.numel(), _stream(z.device))
+    _check("tri_attn_module_fwd", st)
+    return out

@@ -1,0 +1,205 @@
+/*
+ * evo_attn.h -- C ABI of libevoattn.so: the Evoformer's biased, gated
+ * attention on AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes.  For every attention line (batch b, row r),
+ * head h, query q and key k:
+ *
+ *     s[q,k] = <Q[q], K[k]> / sqrt(C) + bias[b,h,q,k] + (keep[k] ? 0 : -inf)
+ *     Out[q] = sigmoid(G[q]) * sum_k softmax_k(s[q,:])[k] * V[k]
+ *
+ * This is triangle attention as described in "Evoformer: the memory wall ZeRO
+ * cannot move" (DeepSpeed course), section "The three operations" (the third
+ * residue k of the triangle is chosen by attention; the logits are
+ * O(N_res^3 * n_heads), section "Where the memory goes"), and the MSA row
+ * attention with pair bias of the same trunk.  The forward and backward never
+ * store the logits: they are tiled through on-chip memory with an online
+ * softmax, the approach of EvoFlash-3D in "MegaFold: Efficient Training of
+ * Next-Generation 3D Attention Protein Models on Cross-Platform GPUs",
+ * section "Methodologie", item 1, including its additively broadcast pair
+ * bias (one [H, N, N] bias shared by every row of a batch).
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers are device memory owned by the caller (except where stated).
+ *    The library never allocates, frees or keeps a pointer after returning.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *    the call returns at once.  Inputs must stay valid and unchanged, and
+ *    outputs untouched, until the stream has passed the work.
+ *  - Tensors are dense, row-major (C order), with 16-byte aligned bases.
+ *    "[B,R,N,H,C]" means element (b,r,n,h,c) sits at
+ *    ((((b*R + r)*N + n)*H + h)*C + c).
+ *  - dtype EVO_BF16: activations, weights, bias and outputs are bfloat16;
+ *    products accumulate in fp32.  EVO_FP32: everything fp32.
+ *  - Every argument is validated before any work is enqueued.  On error the
+ *    call returns a non-zero evo_status_t, enqueues nothing, leaves outputs
+ *    untouched and records a message readable with evo_last_error() on the
+ *    calling thread.  No entry point prints, aborts or throws.
+ *  - Supported head dimension: C = 32.  N, R, B and H are arbitrary (N >= 1);
+ *    ragged tiles are handled in the kernels.
+ *  - Calls on one stream are ordered; calls on different streams that share
+ *    output buffers race (the library takes no locks).
+ */
+#ifndef EVO_ATTN_H
+#define EVO_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  EVO_OK = 0,
+  EVO_EINVAL = 1,      /* bad argument: NULL, size <= 0, inconsistent option */
+  EVO_ENOTSUP = 2,     /* valid but unsupported: head dim, dtype, alignment  */
+  EVO_EWORKSPACE = 3,  /* workspace missing or smaller than required         */
+  EVO_EHIP = 4,        /* the HIP runtime reported an error on launch        */
+  EVO_EINTERNAL = 5
+} evo_status_t;
+
+typedef enum { EVO_FP32 = 0, EVO_BF16 = 1 } evo_dtype_t;
+
+/* Version of this header's ABI (incremented on incompatible change). */
+int evo_abi_version(void);
+
+/* Message for the last non-OK status returned on the calling thread ("" if
+ * none).  The pointer stays valid until the next call on that thread. */
+const char* evo_last_error(void);
+
+/*
+ * evo_attn_fwd -- forward of biased gated attention.
+ *
+ *   q, k, v   [B,R,N,H,C] dtype.  Rows r are independent attention lines
+ *             (MSA sequences, or rows/columns of the pair representation).
+ *   gate      [B,R,N,H,C] dtype, pre-sigmoid g; NULL = no gating.
+ *   key_mask  [B,mask_rows,N] uint8, nonzero = keep the key, 0 = the key's
+ *             logit is -inf in every query; mask_rows is 1 (shared by all rows
+ *             of a batch) or R (one mask per row).  NULL = no mask
+ *             (mask_rows ignored).
+ *   bias      [B,H,N,N] dtype, bias[b,h,q,k] added to the logits of every row
+ *             of batch b; NULL = no bias.
+ *   out       [B,R,N,H,C] dtype.
+ *   lse       [B,R,H,N] fp32, natural-log log-sum-exp of each query's logits
+ *             (needed by evo_attn_bwd); NULL = not written.
+ *
+ * A query whose keys are all masked gets Out = 0 and lse = -inf.
+ */
+evo_status_t evo_attn_fwd(evo_dtype_t dtype, int64_t B, int64_t R, int64_t N,
+                          int64_t H, int64_t C, const void* q, const void* k,
+                          const void* v, const void* gate,
+                          const uint8_t* key_mask, int64_t mask_rows,
+                          const void* bias, void* out, float* lse,
+                          void* stream);
+
+/* Bytes of device workspace evo_attn_bwd needs for this problem (0 on a
+ * problem evo_attn_bwd would reject). */
+size_t evo_attn_bwd_workspace_bytes(evo_dtype_t dtype, int64_t B, int64_t R,
+                                    int64_t N, int64_t H, int64_t C);
+
+/*
+ * evo_attn_bwd -- backward of evo_attn_fwd (same q, k, v, gate, key_mask,
+ * mask_rows, bias), recomputing the logits tile by tile from `lse`.
+ *
+ *   out       [B,R,N,H,C] dtype, the forward output.
+ *   lse       [B,R,H,N] fp32 from evo_attn_fwd.
+ *   dout      [B,R,N,H,C] dtype, gradient of the loss with respect to out.
+ *   dq,dk,dv  [B,R,N,H,C] dtype, written (not accumulated).
+ *   dgate     [B,R,N,H,C] dtype, gradient w.r.t. the pre-sigmoid gate;
+ *             must be NULL iff gate is NULL.
+ *   dbias     [B,H,N,N] fp32: the sum over the R rows of each batch of the
+ *             logit gradients, written (not accumulated); NULL = skipped.
+ *   workspace device scratch of evo_attn_bwd_workspace_bytes(...) bytes,
+ *             16-byte aligned, owned by the caller; its contents on entry are
+ *             ignored and on return are unspecified.
+ *
+ * Memory beyond inputs and outputs is O(R*H*N*C + H*N^2): the [N,N] logit
+ * blocks of each row are never stored.
+ */
+evo_status_t evo_attn_bwd(evo_dtype_t dtype, int64_t B, int64_t R, int64_t N,
+                          int64_t H, int64_t C, const void* q, const void* k,
+                          const void* v, const void* gate,
+                          const uint8_t* key_mask, int64_t mask_rows,
+                          const void* bias, const void* out, const float* lse,
+                          const void* dout, void* dq, void* dk, void* dv,
+                          void* dgate, float* dbias, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
+ * tri_attn_project -- first half of a triangle-attention module: LayerNorm
+ * of the pair representation fused with the Q, K, V, gate and pair-bias
+ * projections (the normalised N x N tensor is never written; the fusion of
+ * "MegaFold...", section "Methodologie", item 3 "EvoFusion").
+ *
+ *   z          [N,N,CZ] dtype, the pair representation.
+ *   ln_w,ln_b  [CZ] dtype, LayerNorm weight and bias; ln_eps > 0.
+ *              LayerNorm uses the population variance, statistics in fp32.
+ *   w_q,w_k,w_v,w_g  [CZ, H*C] dtype, y = x . W (row-major, x a row vector).
+ *   b_g        [H*C] dtype, gate bias; NULL = zero.
+ *   w_bias     [CZ, H] dtype, pair-bias projection.
+ *   ending     0 = starting node: line i holds z[i,:], so q[0,i,j] is the
+ *              projection of z[i,j] and bias[0,h,j,k] comes from z[j,k].
+ *              1 = ending node: line j holds column z[:,j], so q[0,j,i] is
+ *              the projection of z[i,j] and bias[0,h,i,k] comes from z[k,i].
+ *   q,k,v,g    [1,N,N,H,C] dtype outputs (B = 1, R = N lines).
+ *   bias       [1,H,N,N] dtype output.
+ */
+evo_status_t tri_attn_project(evo_dtype_t dtype, int64_t N, int64_t CZ,
+                              int64_t H, int64_t C, int ending, const void* z,
+                              const void* ln_w, const void* ln_b, float ln_eps,
+                              const void* w_q, const void* w_k,
+                              const void* w_v, const void* w_g,
+                              const void* b_g, const void* w_bias, void* q,
+                              void* k, void* v, void* g, void* bias,
+                              void* stream);
+
+/*
+ * tri_attn_out_project -- last step of the module: out = O . w_o + b_o,
+ * written back in z layout.
+ *
+ *   o     [1,N,N,H,C] dtype (line layout, as produced by evo_attn_fwd on the
+ *         tensors of tri_attn_project).
+ *   w_o   [H*C, CZ] dtype;  b_o [CZ] dtype or NULL = zero.
+ *   out   [N,N,CZ] dtype; for the ending node, line j / place i is written to
+ *         out[i,j].
+ */
+evo_status_t tri_attn_out_project(evo_dtype_t dtype, int64_t N, int64_t CZ,
+                                  int64_t H, int64_t C, int ending,
+                                  const void* o, const void* w_o,
+                                  const void* b_o, void* out, void* stream);
+
+/* Bytes of device workspace tri_attn_module_fwd needs (0 if it would
+ * reject the sizes). */
+size_t tri_attn_workspace_bytes(evo_dtype_t dtype, int64_t N, int64_t CZ,
+                                int64_t H, int64_t C);
+
+/*
+ * tri_attn_module_fwd -- whole triangle-attention module forward:
+ * tri_attn_project, evo_attn_fwd over the N lines with the projected pair
+ * bias and the residue mask applied to keys, then tri_attn_out_project.
+ *
+ *   residue_mask  [N] uint8, nonzero = keep residue k as a key in every
+ *                 line; NULL = no mask.  Masked residues still get outputs as
+ *                 queries.
+ *   out           [N,N,CZ] dtype, the module's update (no residual add).
+ *   workspace     caller-owned device scratch of tri_attn_workspace_bytes(...)
+ *                 bytes (holds the projected Q, K, V, gate, bias and the
+ *                 attention output; O(N^2 * H * C)).
+ * Other arguments as in tri_attn_project / tri_attn_out_project.
+ */
+evo_status_t tri_attn_module_fwd(evo_dtype_t dtype, int64_t N, int64_t CZ,
+                                 int64_t H, int64_t C, int ending,
+                                 const void* z, const uint8_t* residue_mask,
+                                 const void* ln_w, const void* ln_b,
+                                 float ln_eps, const void* w_q,
+                                 const void* w_k, const void* w_v,
+                                 const void* w_g, const void* b_g,
+                                 const void* w_bias, const void* w_o,
+                                 const void* b_o, void* out, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EVO_ATTN_H */

@@ -1,0 +1,160 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry
+point the header declares, and rejects bad arguments with the documented
+status codes before touching the device.  Pointers passed here are never
+dereferenced: every call below fails validation (or takes the injected
+launch failure) before any HIP call."""
+import ctypes
+import os
+import re
+import threading
+
+import pytest
+import torch
+
+from evoformer_attention_amd import ops
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "evo_attn.h")
+FAKE = 0x10000          # aligned, never dereferenced
+MISALIGNED = 0x10004
+L = None
+
+
+@pytest.fixture(autouse=True)
+def lib():
+    global L
+    L = ops.lib()
+    yield L
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) -
+                  {"if", "defined"})
+
+
+def test_header_functions_are_exported():
+    names = declared_functions()
+    assert set(names) == set(ops.EXPORTS), names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_abi_version():
+    assert L.evo_abi_version() == 1
+
+
+def err():
+    return L.evo_last_error().decode()
+
+
+def fwd(**kw):
+    a = dict(dt=1, B=1, R=2, N=8, H=2, C=32, q=FAKE, k=FAKE, v=FAKE, g=None,
+             m=None, mr=1, bias=None, out=FAKE, lse=None)
+    a.update(kw)
+    return L.evo_attn_fwd(a["dt"], a["B"], a["R"], a["N"], a["H"], a["C"],
+                          a["q"], a["k"], a["v"], a["g"], a["m"], a["mr"],
+                          a["bias"], a["out"], a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(C=16), ops.EVO_ENOTSUP, "head dimension"),
+    (dict(C=64), ops.EVO_ENOTSUP, "head dimension"),
+    (dict(N=0), ops.EVO_EINVAL, "positive"),
+    (dict(B=-1), ops.EVO_EINVAL, "positive"),
+    (dict(q=None), ops.EVO_EINVAL, "'q' is NULL"),
+    (dict(out=None), ops.EVO_EINVAL, "'out' is NULL"),
+    (dict(k=MISALIGNED), ops.EVO_ENOTSUP, "'k' is not 16-byte aligned"),
+    (dict(m=FAKE, mr=3), ops.EVO_EINVAL, "mask_rows"),
+    (dict(dt=7), ops.EVO_ENOTSUP, "dtype"),
+])
+def test_fwd_validation(kw, status, needle):
+    assert fwd(**kw) == status
+    assert needle in err()
+
+
+def test_fault_injection_reports_hip_error(monkeypatch):
+    monkeypatch.setenv("EVO_FAULT_INJECT", "launch")
+    assert fwd() == ops.EVO_EHIP
+    assert "injected" in err()
+
+
+def test_last_error_is_thread_local():
+    assert fwd(C=16) == ops.EVO_ENOTSUP
+    seen = {}
+
+    def other():
+        seen["msg"] = L.evo_last_error().decode()
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen["msg"] == ""
+    assert "head dimension" in err()
+
+
+def test_workspace_queries():
+    n = L.evo_attn_bwd_workspace_bytes(1, 1, 512, 512, 4, 32)
+    assert n > 4 * 512 * 512 * 128 * 2  # the transposed slabs alone
+    assert L.evo_attn_bwd_workspace_bytes(1, 1, 512, 512, 4, 16) == 0
+    assert L.evo_attn_bwd_workspace_bytes(1, 1, 4, 2048, 4, 32) == 0
+    t = L.tri_attn_workspace_bytes(1, 768, 128, 4, 32)
+    assert t >= 5 * 768 * 768 * 128 * 2 + 4 * 768 * 768 * 2
+    assert L.tri_attn_workspace_bytes(1, 768, 100, 4, 32) == 0
+
+
+def bwd(**kw):
+    a = dict(dt=1, B=1, R=2, N=8, H=2, C=32, q=FAKE, k=FAKE, v=FAKE, g=None,
+             m=None, mr=1, bias=None, out=FAKE, lse=FAKE, dout=FAKE, dq=FAKE,
+             dk=FAKE, dv=FAKE, dg=None, db=None, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return L.evo_attn_bwd(a["dt"], a["B"], a["R"], a["N"], a["H"], a["C"],
+                          a["q"], a["k"], a["v"], a["g"], a["m"], a["mr"],
+                          a["bias"], a["out"], a["lse"], a["dout"], a["dq"],
+                          a["dk"], a["dv"], a["dg"], a["db"], a["ws"],
+                          a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(g=FAKE), ops.EVO_EINVAL, "dgate"),
+    (dict(dg=FAKE), ops.EVO_EINVAL, "dgate"),
+    (dict(lse=None), ops.EVO_EINVAL, "'lse' is NULL"),
+    (dict(ws=None), ops.EVO_EWORKSPACE, "workspace"),
+    (dict(wsb=16), ops.EVO_EWORKSPACE, "workspace"),
+    (dict(N=2048), ops.EVO_ENOTSUP, "N <= 1024"),
+])
+def test_bwd_validation(kw, status, needle):
+    assert bwd(**kw) == status
+    assert needle in err()
+
+
+def test_module_validation():
+    args = [1, 64, 128, 4, 32, 2] + [FAKE] * 2 + [FAKE, FAKE, 1e-5] + \
+        [FAKE] * 4 + [None, FAKE, FAKE, None, FAKE, FAKE, 1 << 40, None]
+    assert L.tri_attn_module_fwd(*args) == ops.EVO_EINVAL  # ending = 2
+    assert "ending" in err()
+    args[5] = 1
+    args[21] = 10
+    assert L.tri_attn_module_fwd(*args) == ops.EVO_EWORKSPACE
+    args[2] = 100
+    assert L.tri_attn_module_fwd(*args) == ops.EVO_ENOTSUP
+    assert "CZ" in err()
+    assert L.tri_attn_project(1, 64, 128, 4, 32, 0, FAKE, FAKE, FAKE, -1.0,
+                              FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE,
+                              FAKE, FAKE, FAKE, None) == ops.EVO_EINVAL
+    assert "ln_eps" in err()
+    assert L.tri_attn_out_project(1, 64, 128, 4, 32, 0, None, FAKE, None,
+                                  FAKE, None) == ops.EVO_EINVAL
+
+
+def test_binding_rejects_host_tensors_and_raises():
+    x = torch.zeros(1, 1, 4, 1, 32)
+    with pytest.raises(ops.EvoAttnError, match="GPU tensor"):
+        ops.evo_attn_fwd(x, x, x)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(ops, "LIB_PATH", str(tmp_path / "nope.so"))
+    monkeypatch.setattr(ops, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        ops.lib()
