@@ -1,0 +1,221 @@
+"""Benchmark of the Evoformer biased-attention hot path on one MI355X.
+
+One step = the whole hot path over one synthetic batch, through the C ABI:
+  tri_attn_project   LayerNorm + Q/K/V/gate/pair-bias projections
+  evo_attn_fwd       biased gated attention forward (with LSE)
+  tri_attn_out_project
+  evo_attn_bwd       dQ, dK, dV, dGate and dBias (summed over rows)
+on the triangle-attention ending-node workload N_res = 768, c_z = 128,
+4 heads of 32, 38 residues masked, bf16 (default --workload tri_end_768).
+
+value = attention flops per step / step time, counting 4*L*C for the
+forward and 2.5x that for the backward (L = rows * heads * N^2 logits); the
+projections' time is inside the step but their flops are not counted.
+
+Prints one JSON line.  Options: --steps K --warmup W --gpus 1
+--workload NAME --no-cpu-baseline.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+WORKLOADS_BENCH = ("tri_end_768", "tri_start_384", "tri_start_512_bwd")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="tri_end_768", choices=WORKLOADS_BENCH)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-lines", type=int, default=24,
+                    help="attention lines in the oracle's timed sample")
+    return ap.parse_args()
+
+
+def kernel_sources_digest():
+    """Digest of the HIP sources; stored traffic counters are reported only
+    while it matches the digest they were taken with."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "evoformer_attention_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = data.get(workload, {}).get(kernel)
+    if not ent or ent.get("sources_digest") != kernel_sources_digest():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(d, w, n_lines):
+    """The fp64 oracle on a bounded sample of the same workload: module
+    forward and core backward of `n_lines` attention lines (the oracle's own
+    line-wise definitions), timed on this host's cores."""
+    import numpy as np
+    import torch
+    import oracle.evo_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        cores = 1
+
+    def np64(t):
+        return None if t is None else t.to(torch.float64).numpy()
+
+    N, H, C, ending = w["N"], w["H"], w["C"], w["ending"]
+    args = dict(z=np64(d["z"]), residue_mask=None if d["mask"] is None else d["mask"].numpy(),
+                ln_w=np64(d["ln_w"]), ln_b=np64(d["ln_b"]), eps=d["eps"],
+                w_q=np64(d["w_q"]), w_k=np64(d["w_k"]), w_v=np64(d["w_v"]),
+                w_g=np64(d["w_g"]), b_g=np64(d["b_g"]), w_bias=np64(d["w_bias"]),
+                w_o=np64(d["w_o"]), b_o=np64(d["b_o"]), H=H, C=C)
+    lines = list(range(0, N, max(1, N // n_lines)))[:n_lines]
+    rng = np.random.default_rng(0)
+    t0 = time.perf_counter()
+    O.tri_module_lines(lines=lines, ending=ending, **args)
+    q, k, v, g, bias = O.tri_project(args["z"], args["ln_w"], args["ln_b"],
+                                     args["eps"], args["w_q"], args["w_k"],
+                                     args["w_v"], args["w_g"], args["b_g"],
+                                     args["w_bias"], H, C, ending, lines=lines)
+    t1 = time.perf_counter()
+    keep = None if args["residue_mask"] is None else args["residue_mask"] != 0
+    for t in range(len(lines)):
+        dout = rng.standard_normal((N, H, C))
+        O.attention_line_backward(q[0, t], k[0, t], v[0, t], g[0, t],
+                                  bias[0], keep, dout)
+    t2 = time.perf_counter()
+    flops = len(lines) * 14.0 * H * N * N * C
+    return {"value": flops / (t2 - t0) / 1e12, "unit": "TFLOP/s",
+            "cores": int(cores), "kind": "oracle",
+            "sample": (f"{len(lines)} of {N} attention lines of {w['name']}: "
+                       f"line-wise module forward + core backward "
+                       f"({t2 - t0:.1f} s wall, of which {t1 - t0:.1f} s forward "
+                       f"including the pair bias of the whole z)")}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {a.gpus}); the "
+              "multi-GPU sharding of this path is described in DESIGN.md but "
+              "not built.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from evoformer_attention_amd import metrics as M
+    from evoformer_attention_amd import ops, synth
+
+    w = dict(synth.WORKLOADS[a.workload])
+    w["name"] = a.workload
+    N, CZ, H, C, ending = w["N"], w["CZ"], w["H"], w["C"], w["ending"]
+    d = synth.module_inputs(a.workload)
+    if d["dout"] is None:
+        gen = torch.Generator().manual_seed(1)
+        d["dout"] = synth.round_to(torch.randn((1, N, N, H, C), generator=gen), w["dtype"])
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    g = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    key_mask = g["mask"].view(1, 1, N) if g["mask"] is not None else None
+    ws_bwd = torch.empty(ops.evo_attn_bwd_workspace_bytes(torch.bfloat16, 1, N, N, H, C),
+                         dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        q, k, v, gt, bias = ops.tri_attn_project(
+            g["z"], g["ln_w"], g["ln_b"], g["eps"], g["w_q"], g["w_k"], g["w_v"],
+            g["w_g"], g["b_g"], g["w_bias"], H, C, ending)
+        if ev:
+            ev[1].record(stream)
+        o, lse = ops.evo_attn_fwd(q, k, v, gt, key_mask, bias, want_lse=True)
+        if ev:
+            ev[2].record(stream)
+        out = ops.tri_attn_out_project(o, g["w_o"], g["b_o"], CZ, ending)
+        if ev:
+            ev[3].record(stream)
+        grads = ops.evo_attn_bwd(q, k, v, gt, key_mask, bias, o, lse, g["dout"],
+                                 workspace=ws_bwd)
+        if ev:
+            ev[4].record(stream)
+        return out, grads
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)]
+           for _ in range(a.steps)]
+    torch.cuda.reset_peak_memory_stats()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(a.steps):
+        step(evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms = total_ms / a.steps
+    parts = {"project": 0.0, "attn_fwd": 0.0, "out_project": 0.0, "attn_bwd": 0.0}
+    for e in evs:
+        for j, name in enumerate(parts):
+            parts[name] += e[j].elapsed_time(e[j + 1]) / a.steps
+    peak_mem = torch.cuda.max_memory_allocated()
+
+    R = N
+    fwd_fl = M.fwd_flops(1, R, N, H, C)
+    bwd_fl = M.bwd_flops(1, R, N, H, C)
+    value = (fwd_fl + bwd_fl) / (ms * 1e-3) / 1e12
+    fwd_tf = fwd_fl / (parts["attn_fwd"] * 1e-3) / 1e12
+    bwd_tf = bwd_fl / (parts["attn_bwd"] * 1e-3) / 1e12
+    # Dominant kernel of the step: the attention forward (one kernel per
+    # call, so its event pair brackets exactly one launch).
+    traffic = stored_traffic("attn_fwd", a.workload)
+    roof = {"bound": "mfma", "kernel": "attn_fwd_kernel", "achieved": round(fwd_tf, 2),
+            "peak": M.MI355X_BF16_DENSE_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(fwd_tf / M.MI355X_BF16_DENSE_TFLOPS, 4),
+            "traffic": traffic}
+    res = {
+        "metric": "EvoAttention fwd/bwd TFLOP/s (bf16) and % MFMA peak, tri-attn N_res=768",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": a.workload, "N_res": N, "c_z": CZ, "heads": H,
+                   "head_dim": C, "node": "ending" if ending else "starting",
+                   "masked_residues": int((d["mask"] == 0).sum()) if d["mask"] is not None else 0,
+                   "step": "project + attn fwd + out project + attn bwd (dQ,dK,dV,dGate,dBias)"},
+        "roofline": roof,
+        "breakdown_ms": {k: round(v, 4) for k, v in parts.items()},
+        "attn_fwd_tflops": round(fwd_tf, 2), "attn_bwd_tflops": round(bwd_tf, 2),
+        "attn_fwd_mfma_frac": round(fwd_tf / M.MI355X_BF16_DENSE_TFLOPS, 4),
+        "peak_mem_gb": round(peak_mem / 1e9, 3),
+        "logits_avoided_gb": round(M.triangle_logit_bytes(N, H, 2) / 1e9, 3),
+    }
+    if not a.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(d, w, a.cpu_lines)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

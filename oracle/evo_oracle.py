@@ -278,28 +278,33 @@ def _proj(x, w, H, C, bias_vec=None):
 
 
 def tri_project(z, ln_w, ln_b, eps, w_q, w_k, w_v, w_g, b_g, w_bias, H, C,
-                ending):
+                ending, lines=None):
     """First half of the module, in the layout the core attention consumes.
 
     Returns q, k, v, g as [1, N, N, H, C] (row = attention line, then the
     position along the line) and bias as [1, H, N, N] (bias[h, query, key]).
     Starting node: line i holds z[i, :]; bias[h, j, k] = b_jk[h].
-    Ending node: line j holds z[:, j]; bias[h, i, k] = b_ki[h]."""
+    Ending node: line j holds z[:, j]; bias[h, i, k] = b_ki[h].
+    With `lines` given, q, k, v, g hold only those lines ([1, len(lines), N,
+    H, C], in the order given); the bias is always complete."""
     z = np.asarray(z, np.float64)
     N = z.shape[0]
-    x = layer_norm(z, ln_w, ln_b, eps)
-    q = _proj(x, w_q, H, C)
-    k = _proj(x, w_k, H, C)
-    v = _proj(x, w_v, H, C)
-    g = _proj(x, w_g, H, C, b_g)
-    bpair = x @ w_bias                      # [N, N, H], b_jk[h]
+    bpair = _pair_bias(z, ln_w, ln_b, eps, w_bias)   # [N, N, H], b_jk[h]
     if ending:
-        # position (i, j) of z sits in line j at place i
-        q, k, v, g = (t.transpose(1, 0, 2, 3) for t in (q, k, v, g))
         bias = bpair.transpose(2, 1, 0)     # bias[h, i, k] = b_ki[h]
     else:
         bias = bpair.transpose(2, 0, 1)     # bias[h, j, k] = b_jk[h]
-    return (q[None], k[None], v[None], g[None], bias[None])
+    sel = range(N) if lines is None else lines
+    outs = {name: [] for name in ("q", "k", "v", "g")}
+    for t in sel:
+        # line t: positions (t, j) of z (starting) or (i, t) (ending)
+        xl = layer_norm(z[:, t] if ending else z[t], ln_w, ln_b, eps)
+        outs["q"].append(_proj(xl, w_q, H, C))
+        outs["k"].append(_proj(xl, w_k, H, C))
+        outs["v"].append(_proj(xl, w_v, H, C))
+        outs["g"].append(_proj(xl, w_g, H, C, b_g))
+    q, k, v, g = (np.stack(outs[n])[None] for n in ("q", "k", "v", "g"))
+    return q, k, v, g, bias[None]
 
 
 def tri_out_project(o, w_o, b_o, ending):

@@ -466,7 +466,9 @@ def test_mutant_ending_bias_untransposed_is_caught(monkeypatch):
         return b.transpose(1, 0, 2)
     monkeypatch.setattr(O, "_pair_bias", sym)
     with pytest.raises(AssertionError):
-        test_module_lines_subset_against_project()
+        test_module_equals_project_core_outproject(True)
+    with pytest.raises(AssertionError):
+        test_module_equals_project_core_outproject(False)
 
 
 def test_module_lines_subset_against_project():
