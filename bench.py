@@ -138,6 +138,8 @@ def main():
     key_mask = g["mask"].view(1, 1, N) if g["mask"] is not None else None
     ws_bwd = torch.empty(ops.evo_attn_bwd_workspace_bytes(torch.bfloat16, 1, N, N, H, C),
                          dtype=torch.uint8, device=dev)
+    ws_fwd = torch.empty(ops.evo_attn_fwd_workspace_bytes(torch.bfloat16, 1, N, N, H, C),
+                         dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def step(ev=None):
@@ -148,7 +150,8 @@ def main():
             g["w_g"], g["b_g"], g["w_bias"], H, C, ending)
         if ev:
             ev[1].record(stream)
-        o, lse = ops.evo_attn_fwd(q, k, v, gt, key_mask, bias, want_lse=True)
+        o, lse = ops.evo_attn_fwd(q, k, v, gt, key_mask, bias, want_lse=True,
+                                  workspace=ws_fwd)
         if ev:
             ev[2].record(stream)
         out = ops.tri_attn_out_project(o, g["w_o"], g["b_o"], CZ, ending)

@@ -3,8 +3,10 @@
     python -m evoformer_attention_amd.build
 
 Every HIP source is compiled with packed-fp32 instruction selection turned
-off (-Xclang -target-feature -Xclang -packed-fp32-ops); hipcc's host pass
-warns that it does not know that feature, which is harmless."""
+off (-Xclang -target-feature -Xclang -packed-fp32-ops; hipcc's host pass
+warns that it does not know that feature, which is harmless) and with MFMA
+accumulators in ordinary VGPRs (-mllvm -amdgpu-mfma-vgpr-form), which spares
+the accumulator-register copies around every softmax element."""
 import os
 import shutil
 import subprocess
@@ -32,6 +34,8 @@ def hipcc():
 def flags():
     return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # keep matrix-core accumulators in VGPRs (no AGPR copies)
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function",
             "-Wno-unused-variable", "-Wno-unused-but-set-variable"]
 

@@ -10,22 +10,40 @@
 // Attention Protein Models on Cross-Platform GPUs", section "Methodologie",
 // item 1).
 //
-// Work decomposition.  A workgroup (4 waves) owns 128 queries of one head
-// and ROWS lines of one batch entry; each wave owns 32 queries.  Keys stream
-// in tiles of 64.  The pair bias is the same for every line of a batch, so a
-// bias tile is loaded once (converted to fp32, scaled to base 2, masked) and
-// used for all ROWS lines of the workgroup.
+// Kernels.
+//   bias_prep  writes the pair bias once per call as fp32 [B, H, Nq, Nk]
+//              (Nq, Nk padded to the tile sizes) with the shared key mask and
+//              the padding keys folded in as -inf, so the main loop loads it
+//              straight into the matrix-core accumulator operand.
+//   attn_fwd   a workgroup (4 waves) owns 128 queries of one head and ROWS
+//              lines of one batch entry; each wave owns 32 queries.  Keys
+//              stream in tiles of 64 through double-buffered LDS, the next
+//              tile's K, V and bias being fetched into registers while the
+//              current one is computed (one barrier per tile).  The bias tile
+//              is loaded once per workgroup and used for all ROWS lines.
 //
 // Matrix-core mapping (v_mfma_f32_16x16x32_bf16, fp32 accumulate):
-//   S^T = K . Q^T + bias^T   A = 16 keys x 32 dims (LDS), B = Q^T held in
-//                            registers for the whole line, C = bias tile.
+//   S^T = K . (Q/sqrt(C))^T + bias^T   A = 16 keys x 32 dims (LDS), B = Q^T
+//                            held in registers for the whole line, C = bias.
 //   O^T += V^T . P^T         A = V^T from LDS, B = P^T taken straight from
 //                            the S^T accumulators (no LDS round trip).
 // In the accumulator layout a lane holds one query and 4 keys per 16-key
-// block; the key order inside a tile is permuted so that each lane's 8
-// keys of a 32-key half are consecutive, which makes the P^T operand
-// exactly the registers the lane already holds, the bias/mask loads 16-byte
-// vectors, and the V^T operand one 16-byte LDS read.
+// block; the key order inside a tile is permuted so that each lane's 8 keys
+// of a 32-key half are consecutive: the P^T operand is then exactly the
+// registers the lane holds, bias loads are 16-byte vectors and the V^T
+// operand is one 16-byte LDS read.
+//
+// Softmax with a lazy reference.  p = exp2(S*log2(e) - m) uses a per-query
+// reference m (base 2) that is only raised when needed: the first tile (and
+// any tile while a query has seen no live key) computes the true maximum; a
+// later tile is recomputed with a raised reference only if a lane's sum of p
+// over the tile exceeds 2^8.  So every p <= 2^8 (no overflow in fp32 or
+// bf16), m never exceeds the true maximum (no underflow of the result), and
+// the common tile costs one FMA, one exp and one add per logit with no
+// cross-lane reduction.  The result is exact up to rounding for any m, since
+// O and l are scaled by the same exp2(-m).
+#include <algorithm>
+
 #include "evo_device.h"
 #include "evo_kernels.h"
 
@@ -37,7 +55,7 @@ constexpr int BK = 64;            // keys per tile
 constexpr int BQW = 32;           // queries per wave
 constexpr int WAVES = 4;
 constexpr int BQ = BQW * WAVES;   // queries per workgroup
-constexpr int kRowsShared = 2;    // lines per workgroup when masks are shared
+constexpr float kHeadroom = 256.f;  // 2^8: largest tile sum of p per lane
 
 template <typename T> struct FwdLds;
 // Row strides (elements) of the LDS K tile [64 keys][32 dims] and V^T tile
@@ -50,14 +68,14 @@ struct FwdParams {
   const void* k;
   const void* v;
   const void* gate;
-  const uint8_t* mask;
-  const void* bias;
+  const uint8_t* mask;   // per-line masks only (shared masks are in biasp)
+  const float* biasp;    // [B, H, Nq, Nk] fp32, or null (no bias, no mask)
   void* out;
   float* lse;
   int B, R, N, H, mask_rows;
+  int Nq, Nk;            // padded bias dims
   int n_qt, n_rg, total;
-  float qscale;   // log2(e) / sqrt(C): logits are kept in base 2
-  int vec_ok;     // N % 8 == 0: bias and mask rows allow 8-element vectors
+  float qscale;          // 1 / sqrt(C)
 };
 
 // LDS row of physical key p (0..63) of a tile: A-operand lane m of block
@@ -69,7 +87,70 @@ __device__ __forceinline__ int k_lds_row(int p) {
   return half * 32 + kb * 16 + gg * 4 + i;
 }
 
-// 16-byte-granular copies (fragments of 8 elements).
+// ---- raw tile data one thread fetches for one line: 8 K elements of one
+// key and 4 V elements of two keys.
+template <typename T> struct KVRaw;
+template <> struct KVRaw<bf16_t> { uint4 k; uint2 va, vb; };
+template <> struct KVRaw<float> { uint4 k0, k1; float4 va, vb; };
+
+template <typename T>
+__device__ __forceinline__ void fetch_kv(KVRaw<T>& raw, const T* kline,
+                                         const T* vline, int k0, int N,
+                                         int pos_stride) {
+  const int t = threadIdx.x;
+  const int kk = k0 + (t >> 2), ch = t & 3;       // K: key, 8-dim chunk
+  const int p = t & 31, vc = t >> 5;              // V: key pair, 4-dim chunk
+  const int ka = k0 + 2 * p, kb = ka + 1;
+  if constexpr (sizeof(T) == 2) {
+    raw.k = kk < N ? *reinterpret_cast<const uint4*>(kline + (int64_t)kk * pos_stride + ch * 8)
+                   : make_uint4(0, 0, 0, 0);
+    raw.va = ka < N ? *reinterpret_cast<const uint2*>(vline + (int64_t)ka * pos_stride + vc * 4)
+                    : make_uint2(0, 0);
+    raw.vb = kb < N ? *reinterpret_cast<const uint2*>(vline + (int64_t)kb * pos_stride + vc * 4)
+                    : make_uint2(0, 0);
+  } else {
+    if (kk < N) {
+      const uint4* s = reinterpret_cast<const uint4*>(kline + (int64_t)kk * pos_stride + ch * 8);
+      raw.k0 = s[0];
+      raw.k1 = s[1];
+    } else {
+      raw.k0 = make_uint4(0, 0, 0, 0);
+      raw.k1 = raw.k0;
+    }
+    raw.va = ka < N ? *reinterpret_cast<const float4*>(vline + (int64_t)ka * pos_stride + vc * 4)
+                    : make_float4(0, 0, 0, 0);
+    raw.vb = kb < N ? *reinterpret_cast<const float4*>(vline + (int64_t)kb * pos_stride + vc * 4)
+                    : make_float4(0, 0, 0, 0);
+  }
+}
+
+// Write one line's raw tile into LDS: K rows key-permuted, V transposed.
+template <typename T>
+__device__ __forceinline__ void store_kv(const KVRaw<T>& raw, T* sK, T* sV) {
+  constexpr int KST = FwdLds<T>::KST, VST = FwdLds<T>::VST;
+  const int t = threadIdx.x;
+  const int kk = t >> 2, ch = t & 3;
+  const int p = t & 31, vc = t >> 5;
+  if constexpr (sizeof(T) == 2) {
+    *reinterpret_cast<uint4*>(sK + k_lds_row(kk) * KST + ch * 8) = raw.k;
+    uint32_t* d = reinterpret_cast<uint32_t*>(sV);
+    const int base = ((vc * 4) * VST + 2 * p) >> 1;
+    const int rs = VST >> 1;
+    d[base + 0 * rs] = (raw.va.x & 0xffffu) | (raw.vb.x << 16);
+    d[base + 1 * rs] = (raw.va.x >> 16) | (raw.vb.x & 0xffff0000u);
+    d[base + 2 * rs] = (raw.va.y & 0xffffu) | (raw.vb.y << 16);
+    d[base + 3 * rs] = (raw.va.y >> 16) | (raw.vb.y & 0xffff0000u);
+  } else {
+    uint4* dk = reinterpret_cast<uint4*>(sK + k_lds_row(kk) * KST + ch * 8);
+    dk[0] = raw.k0;
+    dk[1] = raw.k1;
+    *reinterpret_cast<float2*>(sV + (vc * 4 + 0) * VST + 2 * p) = make_float2(raw.va.x, raw.vb.x);
+    *reinterpret_cast<float2*>(sV + (vc * 4 + 1) * VST + 2 * p) = make_float2(raw.va.y, raw.vb.y);
+    *reinterpret_cast<float2*>(sV + (vc * 4 + 2) * VST + 2 * p) = make_float2(raw.va.z, raw.vb.z);
+    *reinterpret_cast<float2*>(sV + (vc * 4 + 3) * VST + 2 * p) = make_float2(raw.va.w, raw.vb.w);
+  }
+}
+
 __device__ __forceinline__ bf16x8 ld8(const bf16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
 }
@@ -83,149 +164,64 @@ __device__ __forceinline__ f32x8 ld8(const float* p) {
   r[6] = __uint_as_float(b.z); r[7] = __uint_as_float(b.w);
   return r;
 }
-__device__ __forceinline__ void copy8(bf16_t* dst, const bf16_t* src) {
-  *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
-}
-__device__ __forceinline__ void copy8(float* dst, const float* src) {
-  reinterpret_cast<uint4*>(dst)[0] = reinterpret_cast<const uint4*>(src)[0];
-  reinterpret_cast<uint4*>(dst)[1] = reinterpret_cast<const uint4*>(src)[1];
-}
-__device__ __forceinline__ void zero8(bf16_t* dst) {
-  *reinterpret_cast<uint4*>(dst) = make_uint4(0, 0, 0, 0);
-}
-__device__ __forceinline__ void zero8(float* dst) {
-  reinterpret_cast<uint4*>(dst)[0] = make_uint4(0, 0, 0, 0);
-  reinterpret_cast<uint4*>(dst)[1] = make_uint4(0, 0, 0, 0);
+__device__ __forceinline__ f32x4 ldf4(const float* p) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  return f32x4{a.x, a.y, a.z, a.w};
 }
 
-// Four consecutive elements -> fp32.
+// Four consecutive elements <-> fp32.
 __device__ __forceinline__ f32x4 ld4f(const bf16_t* p) {
   const uint2 u = *reinterpret_cast<const uint2*>(p);
-  f32x4 r;
-  r[0] = __uint_as_float(u.x << 16);
-  r[1] = __uint_as_float(u.x & 0xffff0000u);
-  r[2] = __uint_as_float(u.y << 16);
-  r[3] = __uint_as_float(u.y & 0xffff0000u);
-  return r;
+  return f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+               __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
 }
-__device__ __forceinline__ f32x4 ld4f(const float* p) {
-  const float4 u = *reinterpret_cast<const float4*>(p);
-  f32x4 r;
-  r[0] = u.x; r[1] = u.y; r[2] = u.z; r[3] = u.w;
-  return r;
-}
+__device__ __forceinline__ f32x4 ld4f(const float* p) { return ldf4(p); }
 __device__ __forceinline__ void st4f(bf16_t* p, const f32x4& v) {
   uint2 u;
-  u.x = uint32_t(Tr<bf16_t>::from_f(v[0])) |
-        (uint32_t(Tr<bf16_t>::from_f(v[1])) << 16);
-  u.y = uint32_t(Tr<bf16_t>::from_f(v[2])) |
-        (uint32_t(Tr<bf16_t>::from_f(v[3])) << 16);
+  u.x = uint32_t(Tr<bf16_t>::from_f(v[0])) | (uint32_t(Tr<bf16_t>::from_f(v[1])) << 16);
+  u.y = uint32_t(Tr<bf16_t>::from_f(v[2])) | (uint32_t(Tr<bf16_t>::from_f(v[3])) << 16);
   *reinterpret_cast<uint2*>(p) = u;
 }
 __device__ __forceinline__ void st4f(float* p, const f32x4& v) {
   *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
 }
 
-// Stage the K tile (key-permuted rows) and the V^T tile of one line.
+// Bias prep: biasp[b,h,q,k] = bias (natural units) or 0, -inf for keys
+// masked by a shared mask or beyond N; q < Nq, k < Nk.
 template <typename T>
-__device__ __forceinline__ void stage_kv(T* sK, T* sV, const T* kline,
-                                         const T* vline, int k0, int N,
-                                         int pos_stride) {
-  constexpr int KST = FwdLds<T>::KST, VST = FwdLds<T>::VST;
-  const int t = threadIdx.x;
-  {  // K: thread -> (key, 8-dim chunk)
-    const int kk = t >> 2, ch = t & 3;
-    T* dst = sK + k_lds_row(kk) * KST + ch * 8;
-    if (k0 + kk < N)
-      copy8(dst, kline + (int64_t)(k0 + kk) * pos_stride + ch * 8);
-    else
-      zero8(dst);
-  }
-  {  // V: thread -> (key pair, 4-dim chunk), written transposed
-    const int p = t & 31, ch = t >> 5;
-    const int ka = k0 + 2 * p, kb = ka + 1;
-    if constexpr (sizeof(T) == 2) {
-      uint2 a = make_uint2(0, 0), b = make_uint2(0, 0);
-      if (ka < N)
-        a = *reinterpret_cast<const uint2*>(vline + (int64_t)ka * pos_stride + ch * 4);
-      if (kb < N)
-        b = *reinterpret_cast<const uint2*>(vline + (int64_t)kb * pos_stride + ch * 4);
-      uint32_t* d = reinterpret_cast<uint32_t*>(sV);
-      const int base = ((ch * 4) * VST + 2 * p) >> 1;
-      const int rs = VST >> 1;
-      d[base + 0 * rs] = (a.x & 0xffffu) | (b.x << 16);
-      d[base + 1 * rs] = (a.x >> 16) | (b.x & 0xffff0000u);
-      d[base + 2 * rs] = (a.y & 0xffffu) | (b.y << 16);
-      d[base + 3 * rs] = (a.y >> 16) | (b.y & 0xffff0000u);
-    } else {
-      float4 a = make_float4(0, 0, 0, 0), b = make_float4(0, 0, 0, 0);
-      if (ka < N)
-        a = *reinterpret_cast<const float4*>(vline + (int64_t)ka * pos_stride + ch * 4);
-      if (kb < N)
-        b = *reinterpret_cast<const float4*>(vline + (int64_t)kb * pos_stride + ch * 4);
-      float2* d0 = reinterpret_cast<float2*>(sV + (ch * 4 + 0) * VST + 2 * p);
-      float2* d1 = reinterpret_cast<float2*>(sV + (ch * 4 + 1) * VST + 2 * p);
-      float2* d2 = reinterpret_cast<float2*>(sV + (ch * 4 + 2) * VST + 2 * p);
-      float2* d3 = reinterpret_cast<float2*>(sV + (ch * 4 + 3) * VST + 2 * p);
-      *d0 = make_float2(a.x, b.x);
-      *d1 = make_float2(a.y, b.y);
-      *d2 = make_float2(a.z, b.z);
-      *d3 = make_float2(a.w, b.w);
-    }
-  }
-}
-
-// Base-2, masked bias for 8 consecutive keys [kbase, kbase+8) of query q:
-// returned as two accumulator quads (keys kbase..+3, kbase+4..+7).
-template <typename T>
-__device__ __forceinline__ void bias8(const FwdParams& p, const T* brow,
-                                      const uint8_t* mrow, int kbase,
-                                      f32x4& lo, f32x4& hi) {
-  float x[8];
-  const int N = p.N;
-  if (p.vec_ok && kbase + 8 <= N) {
-    if (brow) {
-      const f32x4 a = ld4f(brow + kbase), b = ld4f(brow + kbase + 4);
+__global__ void __launch_bounds__(256) fwd_bias_prep_kernel(
+    const T* bias, const uint8_t* mask, int shared_mask, float* biasp, int B,
+    int H, int N, int Nq, int Nk) {
+  const int64_t total = (int64_t)B * H * Nq * (Nk / 4);
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * 256) {
+    const int k4 = (int)(e % (Nk / 4)) * 4;
+    const int64_t row = e / (Nk / 4);       // (b*H + h)*Nq + q
+    const int q = (int)(row % Nq);
+    const int64_t bh = row / Nq;
+    const int b = (int)(bh / H);
+    float v[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        x[j] = a[j] * kLog2e;
-        x[4 + j] = b[j] * kLog2e;
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = 0.f;
-    }
-    if (mrow) {
-      const uint2 m = *reinterpret_cast<const uint2*>(mrow + kbase);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (((m.x >> (8 * j)) & 0xffu) == 0) x[j] = -INFINITY;
-        if (((m.y >> (8 * j)) & 0xffu) == 0) x[4 + j] = -INFINITY;
-      }
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int kk = kbase + j;
-      float b = -INFINITY;
+    for (int j = 0; j < 4; ++j) {
+      const int kk = k4 + j;
+      float x = -INFINITY;
       if (kk < N) {
-        b = brow ? Tr<T>::to_f(brow[kk]) * kLog2e : 0.f;
-        if (mrow && mrow[kk] == 0) b = -INFINITY;
+        x = (bias && q < N) ? Tr<T>::to_f(bias[(bh * N + q) * N + kk]) : 0.f;
+        if (shared_mask && mask[(int64_t)b * N + kk] == 0) x = -INFINITY;
       }
-      x[j] = b;
+      v[j] = x;
     }
+    *reinterpret_cast<float4*>(biasp + row * Nk + k4) = make_float4(v[0], v[1], v[2], v[3]);
   }
-  lo[0] = x[0]; lo[1] = x[1]; lo[2] = x[2]; lo[3] = x[3];
-  hi[0] = x[4]; hi[1] = x[5]; hi[2] = x[6]; hi[3] = x[7];
 }
 
-template <typename T, int ROWS>
+template <typename T, int ROWS, bool ROW_MASK, bool HAS_BIAS>
 __global__ void __launch_bounds__(256)
 attn_fwd_kernel(FwdParams p) {
   using Op = typename Tr<T>::Op;
   constexpr int KST = FwdLds<T>::KST, VST = FwdLds<T>::VST;
-  __shared__ __attribute__((aligned(16))) T sK[ROWS][BK * KST];
-  __shared__ __attribute__((aligned(16))) T sV[ROWS][C * VST];
+  __shared__ __attribute__((aligned(16))) T sK[2][ROWS][BK * KST];
+  __shared__ __attribute__((aligned(16))) T sV[2][ROWS][C * VST];
 
   const int w = xcd_work_index(p.total);
   if (w < 0) return;
@@ -241,13 +237,24 @@ attn_fwd_kernel(FwdParams p) {
   const int l16 = lane & 15, g = lane >> 4;
   const int r0 = rg * ROWS;
   const int qw0 = qt * BQ + wave * BQW;
-  const int pos_stride = H * C;                       // between positions n
-  const int64_t line_stride = (int64_t)N * pos_stride;  // between lines r
+  const int pos_stride = H * C;
+  const int64_t line_stride = (int64_t)N * pos_stride;
 
   const T* Q = static_cast<const T*>(p.q);
   const T* K = static_cast<const T*>(p.k);
   const T* V = static_cast<const T*>(p.v);
-  const T* Bias = static_cast<const T*>(p.bias);
+
+  const T* kline[ROWS];
+  const T* vline[ROWS];
+  bool live[ROWS];
+#pragma unroll
+  for (int rr = 0; rr < ROWS; ++rr) {
+    const int r = min(r0 + rr, R - 1);
+    live[rr] = r0 + rr < R;
+    const int64_t lo = ((int64_t)b * R + r) * line_stride + h * C;
+    kline[rr] = K + lo;
+    vline[rr] = V + lo;
+  }
 
   // Per-line state.
   Op qf[ROWS][2];
@@ -255,11 +262,11 @@ attn_fwd_kernel(FwdParams p) {
   float m[ROWS][2], l[ROWS][2];
 #pragma unroll
   for (int rr = 0; rr < ROWS; ++rr) {
-    const int r = r0 + rr;
+    const int r = min(r0 + rr, R - 1);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const int q = qw0 + qb * 16 + l16;
-      if (r < R && q < N) {
+      if (q < N) {
         const T* src = Q + ((int64_t)b * R + r) * line_stride +
                        (int64_t)q * pos_stride + h * C + 8 * g;
         qf[rr][qb] = scale8(ld8(src), p.qscale);
@@ -273,47 +280,72 @@ attn_fwd_kernel(FwdParams p) {
     }
   }
 
-  // Bias rows of this wave's queries (null when there is no bias); the
-  // mask row is shared by all lines here (per-line masks use ROWS == 1).
-  const T* brow[2];
+  // Bias rows of this wave's queries: lane reads keys k0 + half*32 + 8g..+7.
+  const float* brow[2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int q = qw0 + qb * 16 + l16;
-    brow[qb] = (Bias && q < N) ? Bias + (((int64_t)b * H + h) * N + q) * N
-                               : nullptr;
+    brow[qb] = HAS_BIAS ? p.biasp + (((int64_t)b * H + h) * p.Nq + q) * p.Nk + 8 * g
+                        : nullptr;
   }
-  const uint8_t* mrow = nullptr;
-  if (p.mask) {
-    const int mr = (p.mask_rows == 1) ? 0 : r0;
-    mrow = p.mask + ((int64_t)b * p.mask_rows + mr) * N;
+  const uint8_t* mrow[ROWS];
+  if constexpr (ROW_MASK) {
+#pragma unroll
+    for (int rr = 0; rr < ROWS; ++rr)
+      mrow[rr] = p.mask + ((int64_t)b * p.mask_rows + min(r0 + rr, R - 1)) * N;
   }
 
-  for (int k0 = 0; k0 < N; k0 += BK) {
-    __syncthreads();  // previous tile fully consumed
+  KVRaw<T> raw[ROWS];
+  f32x4 bnext[2][2][2];  // [qb][half][kb]
+  auto fetch_bias = [&](int k0) {
 #pragma unroll
-    for (int rr = 0; rr < ROWS; ++rr) {
-      const int r = r0 + rr;
-      if (r < R) {
-        const int64_t lo = ((int64_t)b * R + r) * line_stride + h * C;
-        stage_kv<T>(sK[rr], sV[rr], K + lo, V + lo, k0, N, pos_stride);
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        if constexpr (HAS_BIAS) {
+          bnext[qb][half][0] = ldf4(brow[qb] + k0 + half * 32);
+          bnext[qb][half][1] = ldf4(brow[qb] + k0 + half * 32 + 4);
+        } else {
+          // no bias and no shared mask: 0, padding keys -inf
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              bnext[qb][half][kb][i] =
+                  (k0 + half * 32 + 8 * g + 4 * kb + i < N) ? 0.f : -INFINITY;
+        }
       }
-    }
-    // Bias tile in accumulator layout: bt[qb][half][kb].
+  };
+#pragma unroll
+  for (int rr = 0; rr < ROWS; ++rr) fetch_kv<T>(raw[rr], kline[rr], vline[rr], 0, N, pos_stride);
+  fetch_bias(0);
+
+  const int ntiles = (N + BK - 1) / BK;
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int k0 = tile * BK;
+    const int buf = tile & 1;
+#pragma unroll
+    for (int rr = 0; rr < ROWS; ++rr) store_kv<T>(raw[rr], sK[buf][rr], sV[buf][rr]);
     f32x4 bt[2][2][2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
       for (int half = 0; half < 2; ++half)
-        bias8<T>(p, brow[qb], mrow, k0 + half * 32 + 8 * g, bt[qb][half][0],
-                 bt[qb][half][1]);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) bt[qb][half][kb] = bnext[qb][half][kb];
     __syncthreads();
+    if (tile + 1 < ntiles) {
+#pragma unroll
+      for (int rr = 0; rr < ROWS; ++rr)
+        fetch_kv<T>(raw[rr], kline[rr], vline[rr], k0 + BK, N, pos_stride);
+      fetch_bias(k0 + BK);
+    }
 
 #pragma unroll
     for (int rr = 0; rr < ROWS; ++rr) {
-      if (r0 + rr >= R) continue;
-      const T* kt = sK[rr];
-      const T* vt = sV[rr];
-      f32x4 s[2][2][2];  // [qb][half][kb]
+      const T* kt = sK[buf][rr];
+      const T* vt = sV[buf][rr];
+      f32x4 s[2][2][2];  // [qb][half][kb] natural-unit logits
 #pragma unroll
       for (int half = 0; half < 2; ++half)
 #pragma unroll
@@ -323,37 +355,80 @@ attn_fwd_kernel(FwdParams p) {
           for (int qb = 0; qb < 2; ++qb)
             s[qb][half][kb] = mma32(kf, qf[rr][qb], bt[qb][half][kb]);
         }
+      if constexpr (ROW_MASK) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int kbase = k0 + half * 32 + 8 * g;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const bool dead = kbase + j < N && mrow[rr][kbase + j] == 0;
+            if (dead) {
+              s[0][half][j >> 2][j & 3] = -INFINITY;
+              s[1][half][j >> 2][j & 3] = -INFINITY;
+            }
+          }
+        }
+      }
 
+      // Fast path: p = exp2(s*log2e - m) with the current reference.
+      f32x4 pv[2][2][2];
+      float psum[2];
+      bool redo = false;
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int half = 0; half < 2; ++half)
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[qb][half][kb][i]);
-        mx = fmaxf(mx, shfl_xor(mx, 16));
-        mx = fmaxf(mx, shfl_xor(mx, 32));
-        const float mnew = fmaxf(m[rr][qb], mx);
-        const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-        const float alpha = exp2_fast(m[rr][qb] - muse);
-        m[rr][qb] = mnew;
-        float ls = 0.f;
+        const float nm = -m[rr][qb];
+        float acc = 0.f;
 #pragma unroll
         for (int half = 0; half < 2; ++half)
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const float e = exp2_fast(s[qb][half][kb][i] - muse);
-              s[qb][half][kb][i] = e;
-              ls += e;
+              const float e = exp2_fast(__builtin_fmaf(s[qb][half][kb][i], kLog2e, nm));
+              pv[qb][half][kb][i] = e;
+              acc += e;
             }
-        l[rr][qb] = l[rr][qb] * alpha + ls;
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb) o[rr][qb][cb] *= alpha;
+        psum[qb] = acc;
+        // not yet anchored (m = -inf gives e = inf or NaN), or too large
+        redo |= !(acc <= kHeadroom);
       }
+      if (__builtin_amdgcn_ballot_w64(redo) != 0) {
+        // Slow path: raise the reference to the tile maximum where needed.
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          float mx = -INFINITY;
+#pragma unroll
+          for (int half = 0; half < 2; ++half)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[qb][half][kb][i]);
+          mx = fmaxf(mx, shfl_xor(mx, 16));
+          mx = fmaxf(mx, shfl_xor(mx, 32));
+          const float mold = m[rr][qb];
+          const float mnew = fmaxf(mold, mx * kLog2e);
+          const float muse = (mnew == -INFINITY) ? 0.f : mnew;
+          const float alpha = (mold == -INFINITY) ? 0.f : exp2_fast(mold - muse);
+          m[rr][qb] = (mnew == -INFINITY) ? -INFINITY : muse;
+          l[rr][qb] *= alpha;
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb) o[rr][qb][cb] *= alpha;
+          float acc = 0.f;
+#pragma unroll
+          for (int half = 0; half < 2; ++half)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const float e = exp2_fast(__builtin_fmaf(s[qb][half][kb][i], kLog2e, -muse));
+                pv[qb][half][kb][i] = e;
+                acc += e;
+              }
+          psum[qb] = acc;
+        }
+      }
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) l[rr][qb] += psum[qb];
 
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
@@ -363,7 +438,7 @@ attn_fwd_kernel(FwdParams p) {
           vf[cb] = ld8(vt + (cb * 16 + l16) * VST + half * 32 + 8 * g);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-          const Op pf = pack8(s[qb][half][0], s[qb][half][1], (Op*)nullptr);
+          const Op pf = pack8(pv[qb][half][0], pv[qb][half][1], (Op*)nullptr);
 #pragma unroll
           for (int cb = 0; cb < 2; ++cb)
             o[rr][qb][cb] = mma32(vf[cb], pf, o[rr][qb][cb]);
@@ -377,8 +452,8 @@ attn_fwd_kernel(FwdParams p) {
   T* Out = static_cast<T*>(p.out);
 #pragma unroll
   for (int rr = 0; rr < ROWS; ++rr) {
+    if (!live[rr]) continue;
     const int r = r0 + rr;
-    if (r >= R) continue;
     const int64_t lo = ((int64_t)b * R + r) * line_stride + h * C;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -408,38 +483,68 @@ attn_fwd_kernel(FwdParams p) {
   }
 }
 
-template <typename T, int ROWS>
+template <typename T, int ROWS, bool ROW_MASK>
 hipError_t launch_t(const FwdParams& p, hipStream_t s) {
   const int grid = ((p.total + kNumXcd - 1) / kNumXcd) * kNumXcd;
-  hipLaunchKernelGGL((attn_fwd_kernel<T, ROWS>), dim3(grid), dim3(256), 0, s,
-                     p);
+  if (p.biasp)
+    hipLaunchKernelGGL((attn_fwd_kernel<T, ROWS, ROW_MASK, true>), dim3(grid), dim3(256), 0,
+                       s, p);
+  else
+    hipLaunchKernelGGL((attn_fwd_kernel<T, ROWS, ROW_MASK, false>), dim3(grid), dim3(256), 0,
+                       s, p);
   return hipGetLastError();
 }
 
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
 }  // namespace
 
+size_t attn_fwd_workspace(int64_t B, int64_t N, int64_t H) {
+  return (size_t)(B * H * round_up(N, BQ) * round_up(N, BK) * 4);
+}
+
 hipError_t launch_attn_fwd(const AttnFwdArgs& a, hipStream_t s) {
-  FwdParams p;
+  FwdParams p{};
   p.q = a.q; p.k = a.k; p.v = a.v; p.gate = a.gate;
-  p.mask = a.mask; p.bias = a.bias; p.out = a.out; p.lse = a.lse;
+  p.out = a.out; p.lse = a.lse;
   p.B = (int)a.B; p.R = (int)a.R; p.N = (int)a.N; p.H = (int)a.H;
   p.mask_rows = a.mask ? (int)a.mask_rows : 1;
-  p.qscale = kLog2e / sqrtf((float)C);
-  p.vec_ok = (a.N % 8 == 0);
-  // Lines share the bias tile; a per-line mask is folded into it, so then
-  // each workgroup takes one line.
-  const bool per_line_mask = a.mask && a.mask_rows > 1;
-  const int rows = per_line_mask ? 1 : (a.dtype == 1 ? kRowsShared : 1);
+  p.qscale = 1.f / sqrtf((float)C);
+  p.Nq = (int)round_up(a.N, BQ);
+  p.Nk = (int)round_up(a.N, BK);
+  const bool row_mask = a.mask && a.mask_rows > 1;
+  const bool shared_mask = a.mask && !row_mask;
+  p.mask = row_mask ? a.mask : nullptr;
+  p.biasp = nullptr;
+  if (a.bias || shared_mask) {
+    float* bp = static_cast<float*>(a.workspace);
+    const int64_t work = a.B * a.H * p.Nq * (p.Nk / 4);
+    const int grid = (int)std::min<int64_t>((work + 255) / 256, 8192);
+    if (a.dtype == 1)
+      hipLaunchKernelGGL(fwd_bias_prep_kernel<bf16_t>, dim3(grid), dim3(256), 0, s,
+                         static_cast<const bf16_t*>(a.bias), a.mask, (int)shared_mask, bp,
+                         p.B, p.H, p.N, p.Nq, p.Nk);
+    else
+      hipLaunchKernelGGL(fwd_bias_prep_kernel<float>, dim3(grid), dim3(256), 0, s,
+                         static_cast<const float*>(a.bias), a.mask, (int)shared_mask, bp,
+                         p.B, p.H, p.N, p.Nq, p.Nk);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    p.biasp = bp;
+  }
+  // Lines of a workgroup share the bias tile.
+  const int rows = (a.dtype == 1 && a.R > 1) ? 2 : 1;
   p.n_qt = (int)((a.N + BQ - 1) / BQ);
   p.n_rg = (int)((a.R + rows - 1) / rows);
   const int64_t total = a.B * a.H * (int64_t)p.n_rg * p.n_qt;
   if (total > (int64_t)INT32_MAX - 8) return hipErrorInvalidValue;
   p.total = (int)total;
   if (a.dtype == 1) {
-    return rows == 1 ? launch_t<bf16_t, 1>(p, s)
-                     : launch_t<bf16_t, kRowsShared>(p, s);
+    if (rows == 2)
+      return row_mask ? launch_t<bf16_t, 2, true>(p, s) : launch_t<bf16_t, 2, false>(p, s);
+    return row_mask ? launch_t<bf16_t, 1, true>(p, s) : launch_t<bf16_t, 1, false>(p, s);
   }
-  return launch_t<float, 1>(p, s);
+  return row_mask ? launch_t<float, 1, true>(p, s) : launch_t<float, 1, false>(p, s);
 }
 
 }  // namespace evo

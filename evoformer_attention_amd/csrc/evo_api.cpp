@@ -117,6 +117,7 @@ evo_status_t evo_attn_fwd(evo_dtype_t dtype, int64_t B, int64_t R, int64_t N,
                           const void* v, const void* gate,
                           const uint8_t* key_mask, int64_t mask_rows,
                           const void* bias, void* out, float* lse,
+                          void* workspace, size_t workspace_bytes,
                           void* stream) {
   try {
     evo_status_t st = check_core_sizes(dtype, B, R, N, H, C);
@@ -130,14 +131,31 @@ evo_status_t evo_attn_fwd(evo_dtype_t dtype, int64_t B, int64_t R, int64_t N,
     OPTIONAL_PTR(lse);
     OPTIONAL_PTR(key_mask);
     if ((st = check_mask(key_mask, mask_rows, R)) != EVO_OK) return st;
+    if (bias || key_mask) {
+      const size_t need = evo::attn_fwd_workspace(B, N, H);
+      if (!workspace || workspace_bytes < need)
+        return fail(EVO_EWORKSPACE, "workspace of %zu bytes needed, %zu given",
+                    need, workspace ? workspace_bytes : (size_t)0);
+      if (!aligned16(workspace))
+        return fail(EVO_ENOTSUP, "argument 'workspace' is not 16-byte aligned");
+    }
     if (fault_injected()) return fail(EVO_EHIP, "evo_attn_fwd: injected launch failure");
     evo::AttnFwdArgs a{(int)dtype, B, R, N, H, q, k, v, gate, key_mask,
-                       mask_rows, bias, out, lse};
+                       mask_rows, bias, out, lse, workspace};
     return from_hip(evo::launch_attn_fwd(a, (hipStream_t)stream),
                     "evo_attn_fwd");
   } catch (...) {
     return fail(EVO_EINTERNAL, "evo_attn_fwd: internal error");
   }
+}
+
+size_t evo_attn_fwd_workspace_bytes(evo_dtype_t dtype, int64_t B, int64_t R,
+                                    int64_t N, int64_t H, int64_t C) {
+  const std::string saved = g_last_error;
+  const evo_status_t st = check_core_sizes(dtype, B, R, N, H, C);
+  g_last_error = saved;
+  if (st != EVO_OK) return 0;
+  return evo::attn_fwd_workspace(B, N, H);
 }
 
 size_t evo_attn_bwd_workspace_bytes(evo_dtype_t dtype, int64_t B, int64_t R,
@@ -272,7 +290,8 @@ evo_status_t tri_attn_out_project(evo_dtype_t dtype, int64_t N, int64_t CZ,
 }
 
 // Workspace layout of tri_attn_module_fwd: q | k | v | g | o (each
-// N*N*H*C elements) | bias (H*N*N elements), each region 256-byte aligned.
+// N*N*H*C elements) | bias (H*N*N elements) | the forward's fp32 bias,
+// each region 256-byte aligned.
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 size_t tri_attn_workspace_bytes(evo_dtype_t dtype, int64_t N, int64_t CZ,
@@ -284,7 +303,7 @@ size_t tri_attn_workspace_bytes(evo_dtype_t dtype, int64_t N, int64_t CZ,
   const size_t es = elem_size(dtype);
   const size_t t = align256((size_t)N * N * H * C * es);
   const size_t b = align256((size_t)H * N * N * es);
-  return 5 * t + b;
+  return 5 * t + b + align256(evo::attn_fwd_workspace(1, N, H));
 }
 
 evo_status_t tri_attn_module_fwd(evo_dtype_t dtype, int64_t N, int64_t CZ,
@@ -333,6 +352,7 @@ evo_status_t tri_attn_module_fwd(evo_dtype_t dtype, int64_t N, int64_t CZ,
     void* g = ws + 3 * t;
     void* o = ws + 4 * t;
     void* bias = ws + 5 * t;
+    void* fwd_ws = ws + 5 * t + align256((size_t)H * N * N * es);
     hipStream_t s = (hipStream_t)stream;
 
     evo::ProjectArgs pa{(int)dtype, N, CZ, H, ending, z, ln_w, ln_b, ln_eps,
@@ -340,7 +360,7 @@ evo_status_t tri_attn_module_fwd(evo_dtype_t dtype, int64_t N, int64_t CZ,
     st = from_hip(evo::launch_project(pa, s), "tri_attn_module_fwd/project");
     if (st != EVO_OK) return st;
     evo::AttnFwdArgs fa{(int)dtype, 1, N, N, H, q, k, v, g, residue_mask, 1,
-                        bias, o, nullptr};
+                        bias, o, nullptr, fwd_ws};
     st = from_hip(evo::launch_attn_fwd(fa, s), "tri_attn_module_fwd/attention");
     if (st != EVO_OK) return st;
     evo::OutProjectArgs oa{(int)dtype, N, CZ, H, ending, o, w_o, b_o, out};

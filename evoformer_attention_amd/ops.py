@@ -13,7 +13,8 @@ import os
 import torch
 
 __all__ = ["EvoAttnError", "lib", "evo_abi_version", "evo_attn_fwd",
-           "evo_attn_bwd", "evo_attn_bwd_workspace_bytes", "tri_attn_project",
+           "evo_attn_bwd", "evo_attn_bwd_workspace_bytes",
+           "evo_attn_fwd_workspace_bytes", "tri_attn_project",
            "tri_attn_out_project", "tri_attn_module_fwd",
            "tri_attn_workspace_bytes", "LIB_PATH", "EXPORTS"]
 
@@ -36,7 +37,8 @@ EXPORTS = {
     "evo_abi_version": (_I, []),
     "evo_last_error": (ctypes.c_char_p, []),
     "evo_attn_fwd": (_I, [_I, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P,
-                          _P, _I64, _P, _P, _P, _P]),
+                          _P, _I64, _P, _P, _P, _P, _SZ, _P]),
+    "evo_attn_fwd_workspace_bytes": (_SZ, [_I, _I64, _I64, _I64, _I64, _I64]),
     "evo_attn_bwd_workspace_bytes": (_SZ, [_I, _I64, _I64, _I64, _I64, _I64]),
     "evo_attn_bwd": (_I, [_I, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P,
                           _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
@@ -121,11 +123,17 @@ def evo_abi_version():
     return lib().evo_abi_version()
 
 
+def evo_attn_fwd_workspace_bytes(dtype, B, R, N, H, C):
+    code = EVO_BF16 if dtype == torch.bfloat16 else EVO_FP32
+    return lib().evo_attn_fwd_workspace_bytes(code, B, R, N, H, C)
+
+
 def evo_attn_fwd(q, k, v, gate=None, key_mask=None, bias=None, out=None,
-                 want_lse=False):
+                 want_lse=False, workspace=None):
     """Forward of biased gated attention.  q, k, v, gate: [B,R,N,H,C];
     key_mask: uint8 [B,1,N] or [B,R,N]; bias: [B,H,N,N].  Returns out, or
-    (out, lse) with lse [B,R,H,N] fp32 when want_lse."""
+    (out, lse) with lse [B,R,H,N] fp32 when want_lse.  `workspace` (uint8
+    device tensor) is allocated here when not given."""
     _dev_tensor("q", q)
     B, R, N, H, C = q.shape
     dt = q.dtype
@@ -144,9 +152,14 @@ def evo_attn_fwd(q, k, v, gate=None, key_mask=None, bias=None, out=None,
         out = torch.empty_like(q)
     _dev_tensor("out", out, dt, q.shape)
     lse = torch.empty((B, R, H, N), dtype=torch.float32, device=q.device) if want_lse else None
+    if workspace is None and (bias is not None or key_mask is not None):
+        need = evo_attn_fwd_workspace_bytes(dt, B, R, N, H, C)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel()
     st = lib().evo_attn_fwd(_dtype_code(q), B, R, N, H, C, _ptr(q), _ptr(k),
                             _ptr(v), _ptr(gate), _ptr(key_mask), mask_rows,
-                            _ptr(bias), _ptr(out), _ptr(lse), _stream(q.device))
+                            _ptr(bias), _ptr(out), _ptr(lse), _ptr(workspace),
+                            ws_bytes, _stream(q.device))
     _check("evo_attn_fwd", st)
     return (out, lse) if want_lse else out
 

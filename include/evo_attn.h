@@ -82,6 +82,10 @@ const char* evo_last_error(void);
  *   out       [B,R,N,H,C] dtype.
  *   lse       [B,R,H,N] fp32, natural-log log-sum-exp of each query's logits
  *             (needed by evo_attn_bwd); NULL = not written.
+ *   workspace device scratch of evo_attn_fwd_workspace_bytes(...) bytes,
+ *             16-byte aligned, owned by the caller; required when bias or
+ *             key_mask is given (it holds the bias as fp32 with the mask
+ *             folded in), ignored otherwise.  Contents on entry are ignored.
  *
  * A query whose keys are all masked gets Out = 0 and lse = -inf.
  */
@@ -90,7 +94,13 @@ evo_status_t evo_attn_fwd(evo_dtype_t dtype, int64_t B, int64_t R, int64_t N,
                           const void* v, const void* gate,
                           const uint8_t* key_mask, int64_t mask_rows,
                           const void* bias, void* out, float* lse,
+                          void* workspace, size_t workspace_bytes,
                           void* stream);
+
+/* Bytes of device workspace evo_attn_fwd needs when a bias or mask is given
+ * (O(B * H * N^2); 0 on a problem evo_attn_fwd would reject). */
+size_t evo_attn_fwd_workspace_bytes(evo_dtype_t dtype, int64_t B, int64_t R,
+                                    int64_t N, int64_t H, int64_t C);
 
 /* Bytes of device workspace evo_attn_bwd needs for this problem (0 on a
  * problem evo_attn_bwd would reject). */
@@ -183,8 +193,9 @@ size_t tri_attn_workspace_bytes(evo_dtype_t dtype, int64_t N, int64_t CZ,
  *                 queries.
  *   out           [N,N,CZ] dtype, the module's update (no residual add).
  *   workspace     caller-owned device scratch of tri_attn_workspace_bytes(...)
- *                 bytes (holds the projected Q, K, V, gate, bias and the
- *                 attention output; O(N^2 * H * C)).
+ *                 bytes (holds the projected Q, K, V, gate, bias, the
+ *                 attention output and the forward's fp32 bias;
+ *                 O(N^2 * H * C)).
  * Other arguments as in tri_attn_project / tri_attn_out_project.
  */
 evo_status_t tri_attn_module_fwd(evo_dtype_t dtype, int64_t N, int64_t CZ,

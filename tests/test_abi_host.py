@@ -51,11 +51,12 @@ def err():
 
 def fwd(**kw):
     a = dict(dt=1, B=1, R=2, N=8, H=2, C=32, q=FAKE, k=FAKE, v=FAKE, g=None,
-             m=None, mr=1, bias=None, out=FAKE, lse=None)
+             m=None, mr=1, bias=None, out=FAKE, lse=None, ws=None, wsb=0)
     a.update(kw)
     return L.evo_attn_fwd(a["dt"], a["B"], a["R"], a["N"], a["H"], a["C"],
                           a["q"], a["k"], a["v"], a["g"], a["m"], a["mr"],
-                          a["bias"], a["out"], a["lse"], None)
+                          a["bias"], a["out"], a["lse"], a["ws"], a["wsb"],
+                          None)
 
 
 @pytest.mark.parametrize("kw,status,needle", [
@@ -67,6 +68,8 @@ def fwd(**kw):
     (dict(out=None), ops.EVO_EINVAL, "'out' is NULL"),
     (dict(k=MISALIGNED), ops.EVO_ENOTSUP, "'k' is not 16-byte aligned"),
     (dict(m=FAKE, mr=3), ops.EVO_EINVAL, "mask_rows"),
+    (dict(bias=FAKE), ops.EVO_EWORKSPACE, "workspace"),
+    (dict(m=FAKE, ws=FAKE, wsb=8), ops.EVO_EWORKSPACE, "workspace"),
     (dict(dt=7), ops.EVO_ENOTSUP, "dtype"),
 ])
 def test_fwd_validation(kw, status, needle):
@@ -94,6 +97,8 @@ def test_last_error_is_thread_local():
 
 
 def test_workspace_queries():
+    assert L.evo_attn_fwd_workspace_bytes(1, 1, 768, 768, 4, 32) == 4 * 768 * 768 * 4
+    assert L.evo_attn_fwd_workspace_bytes(1, 1, 2, 8, 2, 16) == 0
     n = L.evo_attn_bwd_workspace_bytes(1, 1, 512, 512, 4, 32)
     assert n > 4 * 512 * 512 * 128 * 2  # the transposed slabs alone
     assert L.evo_attn_bwd_workspace_bytes(1, 1, 512, 512, 4, 16) == 0
