@@ -18,17 +18,23 @@
 // Kernels:
 //   prep      dO, dG, D, base-2 LSE, and transposed copies Q^T, dO^T, K^T
 //             (one [C, N] slab per line and head) so that every MFMA operand
-//             below is a contiguous 16-byte load; the base-2, mask-folded
-//             pair bias in both orientations.
+//             below is a contiguous 16-byte load.
+//   bias      the base-2, mask-folded pair bias in both orientations.
 //   dkdv      one line, one head, 128 keys per workgroup (32 per wave);
-//             loops over queries.  Lane = key in the accumulator layout:
-//             S = Q K^T, dP = dO V^T, dV^T += dO^T P, dK^T += Q^T dS.
-//   dq_dbias  32 queries of one head for a group of rows; the 4 waves split
-//             the keys (64-key tiles, interleaved) and hold their part of
-//             dBias in registers across the rows.  Lane = query:
-//             S^T = K Q^T + bias, dP^T = V dO^T, dQ^T += K^T dS^T, with a
-//             cross-wave LDS sum of dQ per row.
-//   reduce    dBias = sum of the row-group partials.
+//             loops over 32-query steps staged through double-buffered LDS
+//             (next step prefetched into registers).  Lane = key in the
+//             accumulator layout: S = Q K^T + bias, dP = dO V^T,
+//             dV^T += dO^T P, dK^T += Q^T dS.
+//   dq        one line, one head, 128 queries; loops over 64-key tiles in
+//             double-buffered LDS.  Lane = query: S^T = K Q^T + bias,
+//             dP^T = V dO^T, dQ^T += K^T dS^T.
+//   dbias     one head, a 128-query x 64-key tile, for a group of rows: the
+//             bias tile and the dBias accumulator stay in registers while
+//             the rows stream by (rows innermost), so the sum over rows
+//             never leaves the chip until the group is done.
+//   reduce    dBias = sum of the row-group partials (deterministic order).
+#include <algorithm>
+
 #include "evo_device.h"
 #include "evo_kernels.h"
 
@@ -36,9 +42,8 @@ namespace evo {
 namespace {
 
 constexpr int C = kHeadDim;
-constexpr int kMaxTilesPerWave = 4;         // dq_dbias: keys <= 4 * 4 * 64
-constexpr int kMaxKeysBwd = 4 * kMaxTilesPerWave * 64;
-constexpr int kTargetGroups = 1024;         // dq_dbias workgroups wanted
+constexpr int kMaxKeysBwd = 1 << 16;
+constexpr int kTargetGroups = 1024;         // dbias workgroups wanted
 
 int64_t pad64(int64_t n) { return (n + 63) / 64 * 64; }
 
@@ -54,8 +59,8 @@ BwdLayout bwd_layout(int dtype, int64_t B, int64_t R, int64_t N, int64_t H) {
   BwdLayout L{};
   const size_t es = dtype == 1 ? 2 : 4;
   L.Np = pad64(N);
-  const int64_t nq = L.Np / 32;
-  int64_t want = (kTargetGroups + B * H * nq - 1) / (B * H * nq);
+  const int64_t tiles = B * H * ((N + 127) / 128) * (L.Np / 64);  // dbias tiles
+  int64_t want = (kTargetGroups + tiles - 1) / tiles;
   if (want < 1) want = 1;
   if (want > R) want = R;
   L.rows_per_group = (R + want - 1) / want;
@@ -105,6 +110,23 @@ __device__ __forceinline__ f32x4 ld4(const float* p) {
   return f32x4{a.x, a.y, a.z, a.w};
 }
 
+// Four consecutive elements <-> fp32.
+__device__ __forceinline__ f32x4 ld4e(const bf16_t* p) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  return f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+               __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
+}
+__device__ __forceinline__ f32x4 ld4e(const float* p) { return ld4(p); }
+__device__ __forceinline__ void st4e(bf16_t* p, const f32x4& v) {
+  uint2 u;
+  u.x = uint32_t(Tr<bf16_t>::from_f(v[0])) | (uint32_t(Tr<bf16_t>::from_f(v[1])) << 16);
+  u.y = uint32_t(Tr<bf16_t>::from_f(v[2])) | (uint32_t(Tr<bf16_t>::from_f(v[3])) << 16);
+  *reinterpret_cast<uint2*>(p) = u;
+}
+__device__ __forceinline__ void st4e(float* p, const f32x4& v) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+
 struct BwdParams {
   const void* q; const void* k; const void* v; const void* gate;
   const uint8_t* mask; const void* bias; const void* out; const float* lse;
@@ -132,29 +154,28 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdParams p) {
   const int N = p.N, H = p.H;
   const int pos = nb * 32 + n;
   const int64_t e0 = ((int64_t)line * N + pos) * H * C + h * C + c4;
-  const T* Q = static_cast<const T*>(p.q);
-  const T* K = static_cast<const T*>(p.k);
-  const T* Out = static_cast<const T*>(p.out);
-  const T* dOut = static_cast<const T*>(p.dout);
-  const T* G = static_cast<const T*>(p.gate);
   float dsum = 0.f;
-  float qv[4] = {0, 0, 0, 0}, kv[4] = {0, 0, 0, 0}, dov[4] = {0, 0, 0, 0};
+  f32x4 qv{0.f, 0.f, 0.f, 0.f}, kv = qv, dov = qv;
   if (pos < N) {
+    qv = ld4e(static_cast<const T*>(p.q) + e0);
+    kv = ld4e(static_cast<const T*>(p.k) + e0);
+    const f32x4 o = ld4e(static_cast<const T*>(p.out) + e0);
+    const f32x4 d = ld4e(static_cast<const T*>(p.dout) + e0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      qv[i] = Tr<T>::to_f(Q[e0 + i]);
-      kv[i] = Tr<T>::to_f(K[e0 + i]);
-      const float o = Tr<T>::to_f(Out[e0 + i]);
-      const float d = Tr<T>::to_f(dOut[e0 + i]);
-      dsum += d * o;
-      if (G) {
-        const float sg = sigmoid_f(Tr<T>::to_f(G[e0 + i]));
-        dov[i] = d * sg;
-        static_cast<T*>(p.dgate)[e0 + i] = Tr<T>::from_f(d * o * (1.f - sg));
-        static_cast<T*>(p.dopre)[e0 + i] = Tr<T>::from_f(dov[i]);
-      } else {
-        dov[i] = d;
+    for (int i = 0; i < 4; ++i) dsum += d[i] * o[i];
+    if (p.gate) {
+      const f32x4 gv = ld4e(static_cast<const T*>(p.gate) + e0);
+      f32x4 dg;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float sg = sigmoid_f(gv[i]);
+        dov[i] = d[i] * sg;
+        dg[i] = d[i] * o[i] * (1.f - sg);
       }
+      st4e(static_cast<T*>(p.dgate) + e0, dg);
+      st4e(static_cast<T*>(p.dopre) + e0, dov);
+    } else {
+      dov = d;
     }
   }
   dsum += __shfl_xor(dsum, 1, 64);
@@ -179,16 +200,18 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdParams p) {
   __syncthreads();
   // Transposed slabs: thread -> dim c = t/8, slots 4*(t%8)..+3.
   const int c = t >> 3, s0 = (t & 7) * 4;
-  T* Qt = static_cast<T*>(p.qt) + (lh * C + c) * p.Np + nb * 32 + s0;
-  T* Dt = static_cast<T*>(p.dot) + (lh * C + c) * p.Np + nb * 32 + s0;
-  T* Kt = static_cast<T*>(p.kt) + (lh * C + c) * p.Np + nb * 32 + s0;
+  const int64_t to = (lh * C + c) * p.Np + nb * 32 + s0;
+  f32x4 a, b2, k2;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int qq = slot_query(s0 + i);
-    Qt[i] = Tr<T>::from_f(sQ[qq][c]);
-    Dt[i] = Tr<T>::from_f(sO[qq][c]);
-    Kt[i] = Tr<T>::from_f(sK[s0 + i][c]);
+    a[i] = sQ[qq][c];
+    b2[i] = sO[qq][c];
+    k2[i] = sK[s0 + i][c];
   }
+  st4e(static_cast<T*>(p.qt) + to, a);
+  st4e(static_cast<T*>(p.dot) + to, b2);
+  st4e(static_cast<T*>(p.kt) + to, k2);
 }
 
 // Base-2 pair bias with the shared key mask folded in, both orientations.
@@ -225,15 +248,19 @@ __global__ void __launch_bounds__(256) bwd_bias_kernel(BwdParams p) {
 }
 
 // ----------------------------------------------------------------- dK, dV
+// Staged per 32-query step: Q rows, dO rows (row-major) and the slot-ordered
+// Q^T and dO^T slabs, each [32][32] (+pad); base-2 LSE and D.
+template <typename T> struct StageRaw;
+template <> struct StageRaw<bf16_t> { uint4 a, b; float l; };
+template <> struct StageRaw<float> { uint4 a0, a1, b0, b1; float l; };
+
 template <typename T>
 __global__ void __launch_bounds__(256) bwd_dkdv_kernel(BwdParams p) {
   using Op = typename Tr<T>::Op;
-  // LDS per 32-query step: Q rows, dO rows (row-major, +pad) and the
-  // slot-ordered Q^T and dO^T slabs; base-2 LSE and D.
-  constexpr int RS = 40;  // elements per row (32 + pad) keeps 16-byte reads spread
-  __shared__ __attribute__((aligned(32))) T sQ[32 * RS], sDO[32 * RS],
-      sQt[32 * RS], sDOt[32 * RS];
-  __shared__ float sL[32], sD[32];
+  constexpr int RS = 40;  // row stride (elements): 16-byte reads spread over banks
+  constexpr int E16 = 16 / sizeof(T);
+  __shared__ __attribute__((aligned(32))) T sT[2][4][32 * RS];  // [buf][Q,dO,Qt,dOt]
+  __shared__ float sL[2][2][32];                                 // [buf][lse2, D]
 
   const int nkt = (p.N + 127) / 128;
   int w = blockIdx.x;
@@ -263,9 +290,11 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(BwdParams p) {
   const int kbase = kt * 128 + wave * 32;
   Op kf[2], vf[2];
   bool kdead[2];
+  int krow[2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     const int key = kbase + kb * 16 + l16;
+    krow[kb] = min(key, Np - 1);
     if (key < N) {
       kf[kb] = scale8(ldop<T>(K + lbase + (int64_t)key * pos_stride + 8 * g), p.qscale);
       vf[kb] = ldop<T>(V + lbase + (int64_t)key * pos_stride + 8 * g);
@@ -284,62 +313,96 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(BwdParams p) {
       dv[cb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-  for (int q0 = 0; q0 < N; q0 += 32) {
-    __syncthreads();
-    {  // stage: thread -> (row, 8-element chunk) of each of the 4 tiles
-      const int row = (tid >> 2) & 31, ch = tid & 3, which = tid >> 7;  // 2 tiles per half
-      for (int rep = 0; rep < 2; ++rep) {
-        const int tile = which * 2 + rep;  // 0 Q, 1 dO, 2 Q^T, 3 dO^T
-        T* dst;
-        const T* src = nullptr;
-        if (tile == 0) {
-          dst = sQ + row * RS + ch * 8;
-          if (q0 + row < N) src = Q + lbase + (int64_t)(q0 + row) * pos_stride + ch * 8;
-        } else if (tile == 1) {
-          dst = sDO + row * RS + ch * 8;
-          if (q0 + row < N) src = DO + lbase + (int64_t)(q0 + row) * pos_stride + ch * 8;
-        } else if (tile == 2) {
-          dst = sQt + row * RS + ch * 8;
-          src = QT + (int64_t)row * Np + q0 + ch * 8;
-        } else {
-          dst = sDOt + row * RS + ch * 8;
-          src = DT + (int64_t)row * Np + q0 + ch * 8;
-        }
-        if (src) {
-          *reinterpret_cast<Op*>(dst) = ldop<T>(src);
-        } else {
-          *reinterpret_cast<Op*>(dst) = Op{};
-        }
-      }
-      if (tid < 32) {
-        sL[tid] = p.lse2[lh * Np + q0 + tid];
-        sD[tid] = p.dd[lh * Np + q0 + tid];
-      }
+  // Staging map: thread -> (tile pair, row, 8-element chunk).
+  const int srow = (tid >> 2) & 31, sch = tid & 3, spair = tid >> 7;  // pair 0: Q,dO  1: Qt,dOt
+  auto fetch = [&](StageRaw<T>& raw, int q0) {
+    const T* s0;
+    const T* s1;
+    bool ok = true;
+    if (spair == 0) {
+      ok = q0 + srow < N;
+      s0 = Q + lbase + (int64_t)min(q0 + srow, N - 1) * pos_stride + sch * 8;
+      s1 = DO + lbase + (int64_t)min(q0 + srow, N - 1) * pos_stride + sch * 8;
+    } else {
+      s0 = QT + (int64_t)srow * Np + q0 + sch * 8;
+      s1 = DT + (int64_t)srow * Np + q0 + sch * 8;
     }
-    __syncthreads();
-
-    // S[qb][kb]: lane holds queries qb*16 + 4g + i for key kbase + kb*16 + l16.
-    f32x4 s[2][2], dp[2][2];
-    Op qa[2], da[2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      qa[qb] = *reinterpret_cast<const Op*>(sQ + (qb * 16 + l16) * RS + 8 * g);
-      da[qb] = *reinterpret_cast<const Op*>(sDO + (qb * 16 + l16) * RS + 8 * g);
+    if constexpr (sizeof(T) == 2) {
+      raw.a = *reinterpret_cast<const uint4*>(s0);
+      raw.b = *reinterpret_cast<const uint4*>(s1);
+      if (!ok) { raw.a = make_uint4(0, 0, 0, 0); raw.b = raw.a; }
+    } else {
+      raw.a0 = reinterpret_cast<const uint4*>(s0)[0];
+      raw.a1 = reinterpret_cast<const uint4*>(s0)[1];
+      raw.b0 = reinterpret_cast<const uint4*>(s1)[0];
+      raw.b1 = reinterpret_cast<const uint4*>(s1)[1];
+      if (!ok) { raw.a0 = make_uint4(0, 0, 0, 0); raw.a1 = raw.a0; raw.b0 = raw.a0; raw.b1 = raw.a0; }
     }
+    raw.l = (tid < 64) ? (tid < 32 ? p.lse2[lh * Np + q0 + tid] : p.dd[lh * Np + q0 + tid - 32])
+                       : 0.f;
+  };
+  auto store = [&](const StageRaw<T>& raw, int buf) {
+    T* d0 = sT[buf][2 * spair] + srow * RS + sch * 8;
+    T* d1 = sT[buf][2 * spair + 1] + srow * RS + sch * 8;
+    if constexpr (sizeof(T) == 2) {
+      *reinterpret_cast<uint4*>(d0) = raw.a;
+      *reinterpret_cast<uint4*>(d1) = raw.b;
+    } else {
+      reinterpret_cast<uint4*>(d0)[0] = raw.a0;
+      reinterpret_cast<uint4*>(d0)[1] = raw.a1;
+      reinterpret_cast<uint4*>(d1)[0] = raw.b0;
+      reinterpret_cast<uint4*>(d1)[1] = raw.b1;
+    }
+    if (tid < 64) sL[buf][tid >> 5][tid & 31] = raw.l;
+  };
+  f32x4 cbn[2][2];  // next step's bias^T C operands [qb][kb]
+  auto fetch_bias = [&](int q0) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int key = kbase + kb * 16 + l16;
-        const f32x4 cbias = ld4(BPT + (int64_t)min(key, Np - 1) * Np + q0 + qb * 16 + 4 * g);
-        s[qb][kb] = mma32(qa[qb], kf[kb], cbias);
-        dp[qb][kb] = mma32(da[qb], vf[kb], f32x4{0.f, 0.f, 0.f, 0.f});
-      }
-    // P and dS (natural-log units for dS).
+      for (int kb = 0; kb < 2; ++kb)
+        cbn[qb][kb] = ld4(BPT + (int64_t)krow[kb] * Np + q0 + qb * 16 + 4 * g);
+  };
+  (void)E16;
+
+  StageRaw<T> raw;
+  fetch(raw, 0);
+  fetch_bias(0);
+  const int nsteps = (N + 31) / 32;
+  for (int st = 0; st < nsteps; ++st) {
+    const int q0 = st * 32, buf = st & 1;
+    store(raw, buf);
+    f32x4 cbias[2][2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) cbias[qb][kb] = cbn[qb][kb];
+    __syncthreads();
+    if (st + 1 < nsteps) {
+      fetch(raw, q0 + 32);
+      fetch_bias(q0 + 32);
+    }
+    const T* sQ = sT[buf][0];
+    const T* sDO = sT[buf][1];
+    const T* sQt = sT[buf][2];
+    const T* sDOt = sT[buf][3];
+
+    // S[qb][kb]: lane holds queries qb*16 + 4g + i for key kbase + kb*16 + l16.
+    f32x4 s[2][2], dp[2][2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      const f32x4 l2 = *reinterpret_cast<const f32x4*>(&sL[qb * 16 + 4 * g]);
-      const f32x4 dd = *reinterpret_cast<const f32x4*>(&sD[qb * 16 + 4 * g]);
+      const Op qa = *reinterpret_cast<const Op*>(sQ + (qb * 16 + l16) * RS + 8 * g);
+      const Op da = *reinterpret_cast<const Op*>(sDO + (qb * 16 + l16) * RS + 8 * g);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[qb][kb] = mma32(qa, kf[kb], cbias[qb][kb]);
+        dp[qb][kb] = mma32(da, vf[kb], f32x4{0.f, 0.f, 0.f, 0.f});
+      }
+    }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const f32x4 l2 = *reinterpret_cast<const f32x4*>(&sL[buf][0][qb * 16 + 4 * g]);
+      const f32x4 dd = *reinterpret_cast<const f32x4*>(&sL[buf][1][qb * 16 + 4 * g]);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -351,13 +414,13 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(BwdParams p) {
     }
     // dV^T += dO^T P,  dK^T += Q^T dS  (contraction over the 32 query slots)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const Op pf = pack8(s[0][kb], s[1][kb], (Op*)nullptr);
-      const Op sf = pack8(dp[0][kb], dp[1][kb], (Op*)nullptr);
+    for (int cb = 0; cb < 2; ++cb) {
+      const Op dot = *reinterpret_cast<const Op*>(sDOt + (cb * 16 + l16) * RS + 8 * g);
+      const Op qtf = *reinterpret_cast<const Op*>(sQt + (cb * 16 + l16) * RS + 8 * g);
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        const Op dot = *reinterpret_cast<const Op*>(sDOt + (cb * 16 + l16) * RS + 8 * g);
-        const Op qtf = *reinterpret_cast<const Op*>(sQt + (cb * 16 + l16) * RS + 8 * g);
+      for (int kb = 0; kb < 2; ++kb) {
+        const Op pf = pack8(s[0][kb], s[1][kb], (Op*)nullptr);
+        const Op sf = pack8(dp[0][kb], dp[1][kb], (Op*)nullptr);
         dv[cb][kb] = mma32(dot, pf, dv[cb][kb]);
         dk[cb][kb] = mma32(qtf, sf, dk[cb][kb]);
       }
@@ -375,30 +438,205 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
       const int64_t off = lbase + (int64_t)key * pos_stride + cb * 16 + 4 * g;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        DK[off + i] = Tr<T>::from_f(dk[cb][kb][i] * ks);
-        DV[off + i] = Tr<T>::from_f(dv[cb][kb][i]);
-      }
+      st4e(DK + off, dk[cb][kb] * ks);
+      st4e(DV + off, dv[cb][kb]);
     }
   }
 }
 
 // ------------------------------------------------------------- dQ, dBias
-// LDS row of physical key p within a 64-key tile (see attn_fwd.hip): the
-// A-operand lane m of block (half, kb) holds key half*32 + 8*(m/4) + 4*kb + m%4.
-__device__ __forceinline__ int perm_key(int half, int kb, int m) {
-  return half * 32 + 8 * (m >> 2) + 4 * kb + (m & 3);
+// Key of A-operand lane m in block (half, kb) of a 64-key tile: the
+// accumulator layout then gives lane group g the 8 consecutive keys
+// half*32 + 8g .. +7 (the same permutation as the forward kernel).
+__device__ __forceinline__ int k_lds_row(int p) {
+  const int half = p >> 5, pp = p & 31;
+  const int gg = pp >> 3, kb = (pp >> 2) & 1, i = pp & 3;
+  return half * 32 + kb * 16 + gg * 4 + i;
 }
 
-template <typename T, int TPW>
-__global__ void __launch_bounds__(256) bwd_dq_dbias_kernel(BwdParams p) {
-  using Op = typename Tr<T>::Op;
-  __shared__ __attribute__((aligned(16))) float sRed[4][2][2][64][4];  // [wave][qb][cb][lane][i]
+template <typename T> struct KRaw;   // one thread's share of a 64-key tile
+template <> struct KRaw<bf16_t> { uint4 k, v, kt; };
+template <> struct KRaw<float> { uint4 k0, k1, v0, v1, kt0, kt1; };
 
-  const int nqt = p.Np / 32;
-  int w = xcd_work_index(p.B * p.H * nqt * p.n_rg);
+// Thread t stages key t/4 (dims 8*(t%4)..+7) of K and V, and row t/8 of the
+// K^T slab (keys 8*(t%8)..+7).
+template <typename T>
+__device__ __forceinline__ void fetch_k(KRaw<T>& raw, const T* kline, const T* vline,
+                                        const T* ktslab, int k0, int N, int Np,
+                                        int pos_stride) {
+  const int t = threadIdx.x;
+  const int kk = min(k0 + (t >> 2), N - 1), ch = t & 3;
+  const T* ks = kline + (int64_t)kk * pos_stride + ch * 8;
+  const T* vs = vline + (int64_t)kk * pos_stride + ch * 8;
+  const T* ts = ktslab + (int64_t)(t >> 3) * Np + k0 + (t & 7) * 8;
+  if constexpr (sizeof(T) == 2) {
+    raw.k = *reinterpret_cast<const uint4*>(ks);
+    raw.v = *reinterpret_cast<const uint4*>(vs);
+    raw.kt = *reinterpret_cast<const uint4*>(ts);
+  } else {
+    raw.k0 = reinterpret_cast<const uint4*>(ks)[0];
+    raw.k1 = reinterpret_cast<const uint4*>(ks)[1];
+    raw.v0 = reinterpret_cast<const uint4*>(vs)[0];
+    raw.v1 = reinterpret_cast<const uint4*>(vs)[1];
+    raw.kt0 = reinterpret_cast<const uint4*>(ts)[0];
+    raw.kt1 = reinterpret_cast<const uint4*>(ts)[1];
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void store_k(const KRaw<T>& raw, T* sK, T* sV, T* sKt, int ks_,
+                                        int kts) {
+  const int t = threadIdx.x;
+  const int row = k_lds_row(t >> 2), ch = t & 3;
+  T* dk = sK + row * ks_ + ch * 8;
+  T* dv = sV + row * ks_ + ch * 8;
+  T* dt = sKt + (t >> 3) * kts + (t & 7) * 8;
+  if constexpr (sizeof(T) == 2) {
+    *reinterpret_cast<uint4*>(dk) = raw.k;
+    *reinterpret_cast<uint4*>(dv) = raw.v;
+    *reinterpret_cast<uint4*>(dt) = raw.kt;
+  } else {
+    reinterpret_cast<uint4*>(dk)[0] = raw.k0;
+    reinterpret_cast<uint4*>(dk)[1] = raw.k1;
+    reinterpret_cast<uint4*>(dv)[0] = raw.v0;
+    reinterpret_cast<uint4*>(dv)[1] = raw.v1;
+    reinterpret_cast<uint4*>(dt)[0] = raw.kt0;
+    reinterpret_cast<uint4*>(dt)[1] = raw.kt1;
+  }
+}
+
+template <typename T> struct BLds;
+template <> struct BLds<bf16_t> { static constexpr int KS = 40, TS = 72; };
+template <> struct BLds<float> { static constexpr int KS = 36, TS = 68; };
+
+// dQ: workgroup = one line, one head, 128 queries (32 per wave); loops over
+// 64-key tiles (K, V rows key-permuted, K^T slab) through double-buffered
+// LDS.  Lane = query: S^T = K Q^T + bias, P = exp2(S - LSE), dP^T = V dO^T,
+// dS = P (dP - D), dQ^T += K^T dS^T.
+template <typename T, bool ROW_MASK>
+__global__ void __launch_bounds__(256) bwd_dq_kernel(BwdParams p) {
+  using Op = typename Tr<T>::Op;
+  constexpr int KS = BLds<T>::KS, TS = BLds<T>::TS;
+  __shared__ __attribute__((aligned(32))) T sK[2][64 * KS], sV[2][64 * KS], sKt[2][32 * TS];
+
+  const int nqt = (p.N + 127) / 128;
+  int w = xcd_work_index(p.B * p.R * p.H * nqt);
   if (w < 0) return;
+  const int qt = w % nqt; w /= nqt;
+  const int h = w % p.H;
+  const int line = w / p.H;
+  const int b = line / p.R, r = line - b * p.R;
+  const int N = p.N, H = p.H, Np = p.Np;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int pos_stride = H * C;
+  const int64_t lbase = (int64_t)line * N * pos_stride + h * C;
+  const int64_t lh = (int64_t)line * H + h;
+  const int qw0 = qt * 128 + wave * 32;
+  const T* K = static_cast<const T*>(p.k) + lbase;
+  const T* V = static_cast<const T*>(p.v) + lbase;
+  const T* KT = static_cast<const T*>(p.kt) + lh * C * Np;
+  const uint8_t* mrow = ROW_MASK ? p.mask + ((int64_t)b * p.mask_rows + r) * N : nullptr;
+
+  Op qf[2], df[2];
+  float l2[2], dd[2];
+  const float* brow[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int q = qw0 + qb * 16 + l16;
+    const int qc = min(q, N - 1);
+    qf[qb] = scale8(ldop<T>(static_cast<const T*>(p.q) + lbase + (int64_t)qc * pos_stride + 8 * g),
+                    p.qscale);
+    df[qb] = ldop<T>(static_cast<const T*>(p.dopre) + lbase + (int64_t)qc * pos_stride + 8 * g);
+    const int qp = min(q, Np - 1);
+    l2[qb] = q < N ? p.lse2[lh * Np + q] : INFINITY;
+    dd[qb] = q < N ? p.dd[lh * Np + q] : 0.f;
+    brow[qb] = p.bp + ((int64_t)(b * H + h) * Np + qp) * Np + 8 * g;
+  }
+  f32x4 dq[2][2];  // [qb][cb]
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) dq[qb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  KRaw<T> raw;
+  fetch_k<T>(raw, K, V, KT, 0, N, Np, pos_stride);
+  const int ntiles = (N + 63) / 64;
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int k0 = tile * 64, buf = tile & 1;
+    store_k<T>(raw, sK[buf], sV[buf], sKt[buf], KS, TS);
+    __syncthreads();
+    if (tile + 1 < ntiles) fetch_k<T>(raw, K, V, KT, k0 + 64, N, Np, pos_stride);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      f32x4 s[2][2], dp[2][2];  // [qb][kb]
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const Op vf = *reinterpret_cast<const Op*>(sV[buf] + (half * 32 + kb * 16 + l16) * KS + 8 * g);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          dp[qb][kb] = mma32(vf, df[qb], f32x4{0.f, 0.f, 0.f, 0.f});
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const Op kf = *reinterpret_cast<const Op*>(sK[buf] + (half * 32 + kb * 16 + l16) * KS + 8 * g);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          s[qb][kb] = mma32(kf, qf[qb], ld4(brow[qb] + k0 + half * 32 + 4 * kb));
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        bool dead[4] = {false, false, false, false};
+        if constexpr (ROW_MASK) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = k0 + half * 32 + 8 * g + 4 * kb + i;
+            dead[i] = key < N && mrow[key] == 0;
+          }
+        }
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float pv = dead[i] ? 0.f : exp2_fast(s[qb][kb][i] - l2[qb]);
+            dp[qb][kb][i] = pv * (dp[qb][kb][i] - dd[qb]);
+          }
+      }
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const Op ktf = *reinterpret_cast<const Op*>(sKt[buf] + (cb * 16 + l16) * TS + half * 32 + 8 * g);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          dq[qb][cb] = mma32(ktf, pack8(dp[qb][0], dp[qb][1], (Op*)nullptr), dq[qb][cb]);
+      }
+    }
+  }
+  const float ks = 1.f / sqrtf((float)C);
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int q = qw0 + qb * 16 + l16;
+    if (q >= N) continue;
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+      st4e(static_cast<T*>(p.dq) + lbase + (int64_t)q * pos_stride + cb * 16 + 4 * g,
+           dq[qb][cb] * ks);
+  }
+}
+
+// dBias: workgroup = one head, 128 queries (32 per wave) x 64 keys, for a
+// group of rows; the bias tile (MFMA accumulator operand) and the dBias
+// accumulator stay in registers while the rows stream by, their K and V
+// tiles shared by the 4 waves through double-buffered LDS.
+template <typename T, bool ROW_MASK>
+__global__ void __launch_bounds__(256) bwd_dbias_kernel(BwdParams p) {
+  using Op = typename Tr<T>::Op;
+  constexpr int KS = BLds<T>::KS;
+  __shared__ __attribute__((aligned(32))) T sK[2][64 * KS], sV[2][64 * KS];
+
+  const int nqt = (p.N + 127) / 128, nkt = p.Np / 64;
+  int w = xcd_work_index(p.B * p.H * nqt * nkt * p.n_rg);
+  if (w < 0) return;
+  const int kt = w % nkt; w /= nkt;
   const int qt = w % nqt; w /= nqt;
   const int rg = w % p.n_rg; w /= p.n_rg;
   const int h = w % p.H;
@@ -407,159 +645,141 @@ __global__ void __launch_bounds__(256) bwd_dq_dbias_kernel(BwdParams p) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, g = lane >> 4;
   const int pos_stride = H * C;
-  const int q0 = qt * 32;
   const int bh = b * H + h;
-  const T* Q = static_cast<const T*>(p.q);
-  const T* K = static_cast<const T*>(p.k);
-  const T* V = static_cast<const T*>(p.v);
-  const T* DO = static_cast<const T*>(p.dopre);
-  const T* KT = static_cast<const T*>(p.kt);
-  const float* BP = p.bp + (int64_t)bh * Np * Np;
+  const int k0 = kt * 64;
+  const int qw0 = qt * 128 + wave * 32;
 
-  f32x4 db[TPW][2][2][2];  // [tile][qb][half][kb]
+  f32x4 cbias[2][2][2], db[2][2][2];  // [half][qb][kb]
 #pragma unroll
-  for (int t = 0; t < TPW; ++t)
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qp = min(qw0 + qb * 16 + l16, Np - 1);
+    const float* brow = p.bp + ((int64_t)bh * Np + qp) * Np + k0 + 8 * g;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int half = 0; half < 2; ++half)
 #pragma unroll
-      for (int half = 0; half < 2; ++half)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) db[t][qb][half][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
+      for (int kb = 0; kb < 2; ++kb) {
+        cbias[half][qb][kb] = ld4(brow + half * 32 + 4 * kb);
+        db[half][qb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+  }
   const int r_begin = rg * p.rows_per_group;
   const int r_end = min(R, r_begin + p.rows_per_group);
-  for (int r = r_begin; r < r_end; ++r) {
+  // thread t stages key t/4 (dims 8*(t%4)..+7) of K and V for one row
+  const int kk = min(k0 + (tid >> 2), N - 1), ch = tid & 3;
+  auto fetch = [&](int r, uint4 (&kr)[2], uint4 (&vr)[2]) {
+    const int64_t lbase = ((int64_t)b * R + r) * N * pos_stride + h * C;
+    const T* ks = static_cast<const T*>(p.k) + lbase + (int64_t)kk * pos_stride + ch * 8;
+    const T* vs = static_cast<const T*>(p.v) + lbase + (int64_t)kk * pos_stride + ch * 8;
+    kr[0] = reinterpret_cast<const uint4*>(ks)[0];
+    vr[0] = reinterpret_cast<const uint4*>(vs)[0];
+    if constexpr (sizeof(T) == 4) {
+      kr[1] = reinterpret_cast<const uint4*>(ks)[1];
+      vr[1] = reinterpret_cast<const uint4*>(vs)[1];
+    }
+  };
+  // query-side operands of a row: Q (scaled), dO, base-2 LSE, D
+  auto fetch_q = [&](int r, Op (&qf)[2], Op (&df)[2], float (&l2)[2], float (&dd)[2]) {
     const int64_t line = (int64_t)b * R + r;
     const int64_t lbase = line * N * pos_stride + h * C;
     const int64_t lh = line * H + h;
-    const uint8_t* mrow = (p.mask && p.row_mask) ? p.mask + ((int64_t)b * p.mask_rows + r) * N
-                                                 : nullptr;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int q = qw0 + qb * 16 + l16;
+      const int qc = min(q, N - 1);
+      qf[qb] = ldop<T>(static_cast<const T*>(p.q) + lbase + (int64_t)qc * pos_stride + 8 * g);
+      df[qb] = ldop<T>(static_cast<const T*>(p.dopre) + lbase + (int64_t)qc * pos_stride + 8 * g);
+      l2[qb] = q < N ? p.lse2[lh * Np + q] : INFINITY;
+      dd[qb] = q < N ? p.dd[lh * Np + q] : 0.f;
+    }
+  };
+  uint4 kr[2], vr[2];
+  Op qn[2], dn[2];
+  float l2n[2], ddn[2];
+  if (r_begin < r_end) {
+    fetch(r_begin, kr, vr);
+    fetch_q(r_begin, qn, dn, l2n, ddn);
+  }
+  for (int r = r_begin; r < r_end; ++r) {
+    const int buf = (r - r_begin) & 1;
+    {
+      const int row = k_lds_row(tid >> 2);
+      T* dk = sK[buf] + row * KS + ch * 8;
+      T* dv = sV[buf] + row * KS + ch * 8;
+      reinterpret_cast<uint4*>(dk)[0] = kr[0];
+      reinterpret_cast<uint4*>(dv)[0] = vr[0];
+      if constexpr (sizeof(T) == 4) {
+        reinterpret_cast<uint4*>(dk)[1] = kr[1];
+        reinterpret_cast<uint4*>(dv)[1] = vr[1];
+      }
+    }
     Op qf[2], df[2];
     float l2[2], dd[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      const int q = q0 + qb * 16 + l16;
-      if (q < N) {
-        qf[qb] = scale8(ldop<T>(Q + lbase + (int64_t)q * pos_stride + 8 * g), p.qscale);
-        df[qb] = ldop<T>(DO + lbase + (int64_t)q * pos_stride + 8 * g);
-      } else {
-        qf[qb] = Op{};
-        df[qb] = Op{};
-      }
-      l2[qb] = p.lse2[lh * Np + q];
-      dd[qb] = p.dd[lh * Np + q];
-    }
-    f32x4 dq[2][2];  // [qb][cb]
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb) dq[qb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-      const int k0 = (wave + 4 * t) * 64;
-      if (k0 >= N) continue;
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        f32x4 s[2][2], dp[2][2];  // [qb][kb]
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const int key = k0 + perm_key(half, kb, l16);
-          Op kf = Op{}, vf = Op{};
-          if (key < N) {
-            kf = ldop<T>(K + lbase + (int64_t)key * pos_stride + 8 * g);
-            vf = ldop<T>(V + lbase + (int64_t)key * pos_stride + 8 * g);
-          }
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb) {
-            const int q = q0 + qb * 16 + l16;
-            const float* bsrc = BP + (int64_t)q * Np + k0 + half * 32 + 8 * g + 4 * kb;
-            s[qb][kb] = mma32(kf, qf[qb], ld4(bsrc));
-            dp[qb][kb] = mma32(vf, df[qb], f32x4{0.f, 0.f, 0.f, 0.f});
-          }
-        }
-        // P and dS; keys of this lane: k0 + half*32 + 8g + 4kb + i.
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          bool dead[4] = {false, false, false, false};
-          if (mrow) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int key = k0 + half * 32 + 8 * g + 4 * kb + i;
-              dead[i] = key < N && mrow[key] == 0;
-            }
-          }
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float pv = dead[i] ? 0.f : exp2_fast(s[qb][kb][i] - l2[qb]);
-              const float ds = pv * (dp[qb][kb][i] - dd[qb]);
-              dp[qb][kb][i] = ds;
-              db[t][qb][half][kb][i] += ds;
-            }
-        }
-        // dQ^T += K^T dS^T over this half's 32 keys.
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-          const T* ksrc = KT + (lh * C + cb * 16 + l16) * Np + k0 + half * 32 + 8 * g;
-          const Op ktf = ldop<T>(ksrc);
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb) {
-            const Op sf = pack8(dp[qb][0], dp[qb][1], (Op*)nullptr);
-            dq[qb][cb] = mma32(ktf, sf, dq[qb][cb]);
-          }
-        }
-      }
-    }
-    // Sum the four waves' partial dQ and store.
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
-        *reinterpret_cast<f32x4*>(&sRed[wave][qb][cb][lane][0]) = dq[qb][cb];
-    __syncthreads();
-    {
-      // thread -> (qb, cb, lane): 2*2*64 = 256 outputs of 4 values
-      const int qb = tid >> 7, cb = (tid >> 6) & 1, ln = tid & 63;
-      f32x4 acc = *reinterpret_cast<const f32x4*>(&sRed[0][qb][cb][ln][0]);
-#pragma unroll
-      for (int ww = 1; ww < 4; ++ww) acc += *reinterpret_cast<const f32x4*>(&sRed[ww][qb][cb][ln][0]);
-      const int q = q0 + qb * 16 + (ln & 15);
-      if (q < N) {
-        const float ks = 1.f / sqrtf((float)C);
-        T* dst = static_cast<T*>(p.dq) + lbase + (int64_t)q * pos_stride + cb * 16 + 4 * (ln >> 4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dst[i] = Tr<T>::from_f(acc[i] * ks);
-      }
+      qf[qb] = scale8(qn[qb], p.qscale);
+      df[qb] = dn[qb];
+      l2[qb] = l2n[qb];
+      dd[qb] = ddn[qb];
     }
     __syncthreads();
+    if (r + 1 < r_end) {
+      fetch(r + 1, kr, vr);
+      fetch_q(r + 1, qn, dn, l2n, ddn);
+    }
+    const uint8_t* mrow = ROW_MASK ? p.mask + ((int64_t)b * p.mask_rows + r) * N : nullptr;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      f32x4 s[2][2], dp[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const Op kf = *reinterpret_cast<const Op*>(sK[buf] + (half * 32 + kb * 16 + l16) * KS + 8 * g);
+        const Op vf = *reinterpret_cast<const Op*>(sV[buf] + (half * 32 + kb * 16 + l16) * KS + 8 * g);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          s[qb][kb] = mma32(kf, qf[qb], cbias[half][qb][kb]);
+          dp[qb][kb] = mma32(vf, df[qb], f32x4{0.f, 0.f, 0.f, 0.f});
+        }
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        bool dead[4] = {false, false, false, false};
+        if constexpr (ROW_MASK) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = k0 + half * 32 + 8 * g + 4 * kb + i;
+            dead[i] = key < N && mrow[key] == 0;
+          }
+        }
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float pv = dead[i] ? 0.f : exp2_fast(s[qb][kb][i] - l2[qb]);
+            db[half][qb][kb][i] += pv * (dp[qb][kb][i] - dd[qb]);
+          }
+      }
+    }
   }
 
-  // dBias partial of this row group (or the final value with one group).
   if (!p.dbias) return;
   float* dst = (p.n_rg == 1) ? nullptr : p.dbpart + ((int64_t)rg * p.B * H + bh) * Np * Np;
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    const int k0 = (wave + 4 * t) * 64;
-    if (k0 >= N) continue;
+  for (int qb = 0; qb < 2; ++qb) {
+    const int q = qw0 + qb * 16 + l16;
+    if (q >= N) continue;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const int q = q0 + qb * 16 + l16;
+    for (int half = 0; half < 2; ++half)
 #pragma unroll
-      for (int half = 0; half < 2; ++half)
+      for (int kb = 0; kb < 2; ++kb) {
+        const int kk2 = k0 + half * 32 + 8 * g + 4 * kb;
+        if (dst) {
+          *reinterpret_cast<f32x4*>(dst + (int64_t)q * Np + kk2) = db[half][qb][kb];
+        } else {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const int kk = k0 + half * 32 + 8 * g + 4 * kb;
-          if (dst) {
-            *reinterpret_cast<f32x4*>(dst + (int64_t)q * Np + kk) = db[t][qb][half][kb];
-          } else if (q < N) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (kk + i < N) p.dbias[((int64_t)bh * N + q) * N + kk + i] = db[t][qb][half][kb][i];
-          }
+          for (int i = 0; i < 4; ++i)
+            if (kk2 + i < N) p.dbias[((int64_t)bh * N + q) * N + kk2 + i] = db[half][qb][kb][i];
         }
-    }
+      }
   }
 }
 
@@ -595,17 +815,24 @@ hipError_t launch_t(BwdParams& p, hipStream_t s) {
   hipLaunchKernelGGL(bwd_dkdv_kernel<T>, dim3((unsigned)(lines * p.H * nkt)), dim3(256), 0, s,
                      p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int total = p.B * p.H * (p.Np / 32) * p.n_rg;
-  const int grid = (total + kNumXcd - 1) / kNumXcd * kNumXcd;
-  const int tiles = (int)((p.N + 63) / 64);
-  const int tpw = (tiles + 3) / 4;
-  switch (tpw) {
-    case 1: hipLaunchKernelGGL((bwd_dq_dbias_kernel<T, 1>), dim3(grid), dim3(256), 0, s, p); break;
-    case 2: hipLaunchKernelGGL((bwd_dq_dbias_kernel<T, 2>), dim3(grid), dim3(256), 0, s, p); break;
-    case 3: hipLaunchKernelGGL((bwd_dq_dbias_kernel<T, 3>), dim3(grid), dim3(256), 0, s, p); break;
-    default: hipLaunchKernelGGL((bwd_dq_dbias_kernel<T, 4>), dim3(grid), dim3(256), 0, s, p); break;
+  {
+    const int total = p.B * p.R * p.H * ((p.N + 127) / 128);
+    const int grid = (total + kNumXcd - 1) / kNumXcd * kNumXcd;
+    if (p.row_mask)
+      hipLaunchKernelGGL((bwd_dq_kernel<T, true>), dim3(grid), dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<T, false>), dim3(grid), dim3(256), 0, s, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (p.dbias) {
+    const int total = p.B * p.H * ((p.N + 127) / 128) * (p.Np / 64) * p.n_rg;
+    const int grid = (total + kNumXcd - 1) / kNumXcd * kNumXcd;
+    if (p.row_mask)
+      hipLaunchKernelGGL((bwd_dbias_kernel<T, true>), dim3(grid), dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL((bwd_dbias_kernel<T, false>), dim3(grid), dim3(256), 0, s, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if (p.n_rg > 1 && p.dbias) {
     hipLaunchKernelGGL(bwd_dbias_reduce_kernel, dim3(2048), dim3(256), 0, s, p);
     e = hipGetLastError();

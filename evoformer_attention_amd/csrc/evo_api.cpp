@@ -197,7 +197,7 @@ evo_status_t evo_attn_bwd(evo_dtype_t dtype, int64_t B, int64_t R, int64_t N,
     if ((st = check_mask(key_mask, mask_rows, R)) != EVO_OK) return st;
     const size_t need = evo::attn_bwd_workspace((int)dtype, B, R, N, H);
     if (need == 0)
-      return fail(EVO_ENOTSUP, "evo_attn_bwd supports N <= 1024 (N=%lld)",
+      return fail(EVO_ENOTSUP, "evo_attn_bwd supports N <= 65536 (N=%lld)",
                   (long long)N);
     if (!workspace || workspace_bytes < need)
       return fail(EVO_EWORKSPACE, "workspace of %zu bytes needed, %zu given",

@@ -8,173 +8,209 @@
 // tri_attn_out_project: the output projection back to CZ channels, written
 // in z layout.
 //
-// Both are a row GEMM  Y[pos, :] = f(X[pos, :]) . W  over the N*N positions
-// of a line-layout tile: a workgroup takes TP consecutive positions, builds
-// f(X) for them in LDS once, then streams the weight matrix through LDS in
-// chunks of 64 output columns (transposed on the way in, so both MFMA
-// operands are contiguous 16-byte LDS reads).  Outputs are produced as
-// Y^T = W^T . f(X)^T so each lane holds 4 consecutive output channels of one
-// position, written as one 8- or 16-byte store.
+// Both are a row GEMM  Y[pos, :] = f(X[pos, :]) . W^T  over the N*N positions
+// (W in [out, in] layout).  Kernel structure:
+//   - persistent workgroups of 8 waves; each loads W^T (all output columns of
+//     one pass, padded rows) into LDS once and then walks 256-position tiles;
+//   - a wave owns 32 positions: it loads their rows straight into the MFMA
+//     B-operand layout (lane = position, 8 consecutive input channels per
+//     contraction step), computes LayerNorm there (cross-lane sums over the
+//     4 lane groups of a position) and keeps the normalised rows as bf16
+//     fragments in registers - f(X) never touches LDS or HBM;
+//   - for each block of 16 output columns: Y^T = W^T . f(X)^T on
+//     v_mfma_f32_16x16x32 (A = W^T rows from LDS), so each lane ends up with
+//     4 consecutive output channels of one position, stored as one 8- or
+//     16-byte write.
 //
 // Orientation: position (line a, place n) of the line layout is z[a, n] for
 // the starting node and z[n, a] for the ending node (line = a column of z).
 // The pair bias of position (a, n) goes to bias[h][a*N + n] in both cases.
+#include <algorithm>
+
 #include "evo_device.h"
 #include "evo_kernels.h"
 
 namespace evo {
 namespace {
 
-constexpr int COLS = 64;   // output columns per weight chunk
-constexpr int PAD = 8;     // LDS row padding (elements)
-
-template <typename T> struct GemmCfg;
-template <> struct GemmCfg<bf16_t> { static constexpr int PB = 2; };  // 128 positions
-template <> struct GemmCfg<float> { static constexpr int PB = 1; };   // 64 positions
+constexpr int PW = 32;              // positions per wave
+constexpr int WAVES = 8;
+constexpr int TP = PW * WAVES;      // positions per tile
+constexpr int PAD = 8;              // LDS row padding (elements)
+constexpr int kMaxK = 256;
+constexpr size_t kLdsBudget = 150 * 1024;
 
 struct GemmParams {
-  int mode;        // 0 = project (LayerNorm + 5 outputs), 1 = out projection
-  int N, K, HC, H, ending, ncols, total_tiles;
+  int mode;        // 0 = project (LayerNorm + q,k,v,g,bias), 1 = out projection
+  int N, K, HC, H, ending, ncols;   // ncols: all output columns
+  int col0, pass_cols;              // this launch's column range (multiple of 16)
   int64_t npos;
+  int ntiles;
   const void* x;   // z [N,N,K] (project) or O [N*N, K] (out projection)
   const void* ln_w;
   const void* ln_b;
   float eps;
-  const void* w[5];     // project: w_q, w_k, w_v, w_g [K,HC], w_bias [K,H]
-                        // out projection: w_o [K, ncols]
+  const void* w[5];     // [out, in]: project w_q, w_k, w_v, w_g [HC,K], w_bias [H,K];
+                        // out projection: w_o [ncols, K]
   const void* colbias;  // project: b_g [HC] (gate columns); out: b_o [ncols]
   void* y[5];           // project: q, k, v, g [npos, HC], bias [H, npos]
                         // out projection: out [npos, ncols] in z layout
 };
 
-// Source/destination row of z for line-layout position pidx.
+// z row (or output row) of line-layout position pidx.
 __device__ __forceinline__ int64_t z_row(int64_t pidx, int N, int ending) {
   if (!ending) return pidx;
   const int64_t a = pidx / N, n = pidx - a * N;
   return n * N + a;
 }
 
-// Weight element W(k, col) of the concatenated column space.
+// Source row (K contiguous elements) of output column c, or null for padding.
 template <typename T>
-__device__ __forceinline__ T w_elem(const GemmParams& p, int k, int col) {
-  if (col >= p.ncols) return T(0);
-  if (p.mode == 1) return static_cast<const T*>(p.w[0])[(int64_t)k * p.ncols + col];
-  const int m = col / p.HC;
-  if (m < 4) return static_cast<const T*>(p.w[m])[(int64_t)k * p.HC + (col - m * p.HC)];
-  return static_cast<const T*>(p.w[4])[(int64_t)k * p.H + (col - 4 * p.HC)];
+__device__ __forceinline__ const T* w_row(const GemmParams& p, int c) {
+  if (c >= p.ncols) return nullptr;
+  if (p.mode == 1) return static_cast<const T*>(p.w[0]) + (int64_t)c * p.K;
+  const int m = c / p.HC;
+  if (m < 4) return static_cast<const T*>(p.w[m]) + (int64_t)(c - m * p.HC) * p.K;
+  return static_cast<const T*>(p.w[4]) + (int64_t)(c - 4 * p.HC) * p.K;
+}
+
+__device__ __forceinline__ void ld16(void* dst, const void* src) {
+  *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
 }
 
 template <typename T>
-__global__ void __launch_bounds__(256)
+__device__ __forceinline__ void st4(T* p, const f32x4& v);
+template <>
+__device__ __forceinline__ void st4<bf16_t>(bf16_t* p, const f32x4& v) {
+  uint2 u;
+  u.x = uint32_t(Tr<bf16_t>::from_f(v[0])) | (uint32_t(Tr<bf16_t>::from_f(v[1])) << 16);
+  u.y = uint32_t(Tr<bf16_t>::from_f(v[2])) | (uint32_t(Tr<bf16_t>::from_f(v[3])) << 16);
+  *reinterpret_cast<uint2*>(p) = u;
+}
+template <>
+__device__ __forceinline__ void st4<float>(float* p, const f32x4& v) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+
+template <typename T, int KSTEPS>
+__global__ void __launch_bounds__(512)
 rowgemm_kernel(GemmParams p) {
   using Op = typename Tr<T>::Op;
-  constexpr int PB = GemmCfg<T>::PB;
-  constexpr int TP = 4 * 16 * PB;
+  constexpr int E16 = 16 / sizeof(T);      // elements per 16 bytes
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const int K = p.K, KS = K + PAD;
-  T* sX = reinterpret_cast<T*>(smem);        // [TP][KS]
-  T* sW = sX + TP * KS;                      // [COLS][KS]  (W^T chunk)
+  const int K = KSTEPS * 32;
+  const int KS = K + PAD;
+  T* sW = reinterpret_cast<T*>(smem);                        // [pass_cols][KS]
+  float* sLn = reinterpret_cast<float*>(sW + p.pass_cols * KS);  // ln_w | ln_b
 
-  const int tile = xcd_work_index(p.total_tiles);
-  if (tile < 0) return;
-  const int64_t pos0 = (int64_t)tile * TP;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, g = lane >> 4;
-  const T* X = static_cast<const T*>(p.x);
 
-  // ---- f(X) tile: 16 lanes per position, K/16 consecutive elements each.
+  // ---- W^T rows of this pass into LDS (16-byte copies), LayerNorm affine.
   {
-    const int span = K / 16;
-    const int sub = lane >> 4;              // position within the quad
-    for (int pp = wave * 4 + sub; pp < TP; pp += 16) {
-      const int64_t pidx = pos0 + pp;
-      float vals[16];
-      const bool live = pidx < p.npos;
-      const int64_t row = live ? (p.mode == 0 ? z_row(pidx, p.N, p.ending) : pidx) : 0;
-      const T* src = X + row * K + l16 * span;
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        vals[j] = (j < span && live) ? Tr<T>::to_f(src[j]) : 0.f;
-      if (p.mode == 0) {
-        float s = 0.f;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) s += vals[j];
-        s += __shfl_xor(s, 1, 64); s += __shfl_xor(s, 2, 64);
-        s += __shfl_xor(s, 4, 64); s += __shfl_xor(s, 8, 64);
-        const float mu = s / K;
-        float v = 0.f;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const float d = (j < span) ? vals[j] - mu : 0.f;
-          v += d * d;
-        }
-        v += __shfl_xor(v, 1, 64); v += __shfl_xor(v, 2, 64);
-        v += __shfl_xor(v, 4, 64); v += __shfl_xor(v, 8, 64);
-        const float rstd = rsqrtf(v / K + p.eps);
-        const T* lw = static_cast<const T*>(p.ln_w) + l16 * span;
-        const T* lb = static_cast<const T*>(p.ln_b) + l16 * span;
-#pragma unroll
-        for (int j = 0; j < 16; ++j)
-          if (j < span)
-            vals[j] = live ? (vals[j] - mu) * rstd * Tr<T>::to_f(lw[j]) +
-                                 Tr<T>::to_f(lb[j])
-                           : 0.f;
+    const int chunks = K / E16;
+    for (int e = tid; e < p.pass_cols * chunks; e += blockDim.x) {
+      const int cl = e / chunks, ch = e - cl * chunks;
+      const T* src = w_row<T>(p, p.col0 + cl);
+      T* dst = sW + cl * KS + ch * E16;
+      if (src) ld16(dst, src + ch * E16);
+      else *reinterpret_cast<uint4*>(dst) = make_uint4(0, 0, 0, 0);
+    }
+    if (p.mode == 0)
+      for (int k = tid; k < K; k += blockDim.x) {
+        sLn[k] = Tr<T>::to_f(static_cast<const T*>(p.ln_w)[k]);
+        sLn[kMaxK + k] = Tr<T>::to_f(static_cast<const T*>(p.ln_b)[k]);
       }
-      T* dst = sX + pp * KS + l16 * span;
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        if (j < span) dst[j] = Tr<T>::from_f(vals[j]);
-    }
   }
+  __syncthreads();
 
-  for (int c0 = 0; c0 < p.ncols; c0 += COLS) {
-    __syncthreads();  // sX ready / previous chunk consumed
-    // ---- W^T chunk: sW[col][k] = W(k, c0 + col)
-    for (int e = tid; e < COLS * K; e += 256) {
-      const int col = e / K, k = e - col * K;
-      sW[col * KS + k] = w_elem<T>(p, k, c0 + col);
+  const T* X = static_cast<const T*>(p.x);
+  for (int tile = blockIdx.x; tile < p.ntiles; tile += gridDim.x) {
+    // ---- this wave's 32 rows, in B-operand layout: xf[pb][s] holds
+    // channels 32s + 8g .. +7 of position base + pb*16 + l16.
+    Op xf[2][KSTEPS];
+    int64_t pidx[2];
+#pragma unroll
+    for (int pb = 0; pb < 2; ++pb) {
+      pidx[pb] = (int64_t)tile * TP + wave * PW + pb * 16 + l16;
+      const bool live = pidx[pb] < p.npos;
+      const int64_t row = live ? (p.mode == 0 ? z_row(pidx[pb], p.N, p.ending) : pidx[pb]) : 0;
+      const T* src = X + row * K + 8 * g;
+      float v[KSTEPS][8];
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) {
+        if (live) {
+          const Op f = *reinterpret_cast<const Op*>(src + 32 * s);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[s][j] = (float)f[j];
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[s][j] = 0.f;
+        }
+      }
+      if (p.mode == 0) {
+        float sum = 0.f;
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) sum += v[s][j];
+        sum += shfl_xor(sum, 16);
+        sum += shfl_xor(sum, 32);
+        const float mu = sum / K;
+        float var = 0.f;
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float d = v[s][j] - mu;
+            var += d * d;
+          }
+        var += shfl_xor(var, 16);
+        var += shfl_xor(var, 32);
+        const float rstd = rsqrtf(var / K + p.eps);
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int k = 32 * s + 8 * g + j;
+            v[s][j] = (v[s][j] - mu) * rstd * sLn[k] + sLn[kMaxK + k];
+          }
+      }
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) {
+        Op f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          if constexpr (sizeof(T) == 2) f[j] = (__bf16)v[s][j];
+          else f[j] = v[s][j];
+        }
+        xf[pb][s] = f;
+      }
     }
-    __syncthreads();
 
-    f32x4 acc[4][PB];
+    // ---- Y^T blocks of 16 output columns.
+    for (int cb = 0; cb < p.pass_cols / 16; ++cb) {
+      f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      const T* wr = sW + (cb * 16 + l16) * KS + 8 * g;
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
+      for (int s = 0; s < KSTEPS; ++s) {
+        const Op a = *reinterpret_cast<const Op*>(wr + 32 * s);
+        acc[0] = mma32(a, xf[0][s], acc[0]);
+        acc[1] = mma32(a, xf[1][s], acc[1]);
+      }
+      const int col = p.col0 + cb * 16 + 4 * g;   // this lane's 4 channels
+      if (col >= p.ncols) continue;
 #pragma unroll
-      for (int pb = 0; pb < PB; ++pb) acc[cb][pb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const T* xw = sX + (wave * 16 * PB) * KS;
-    for (int k0 = 0; k0 < K; k0 += 32) {
-      Op a[4], bx[PB];
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
-        a[cb] = *reinterpret_cast<const Op*>(sW + (cb * 16 + l16) * KS + k0 + 8 * g);
-#pragma unroll
-      for (int pb = 0; pb < PB; ++pb)
-        bx[pb] = *reinterpret_cast<const Op*>(xw + (pb * 16 + l16) * KS + k0 + 8 * g);
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-        for (int pb = 0; pb < PB; ++pb) acc[cb][pb] = mma32(a[cb], bx[pb], acc[cb][pb]);
-    }
-
-    // ---- epilogue: lane holds channels col..col+3 of position pidx
-#pragma unroll
-    for (int pb = 0; pb < PB; ++pb) {
-      const int64_t pidx = pos0 + wave * 16 * PB + pb * 16 + l16;
-      if (pidx >= p.npos) continue;
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        const int col = c0 + cb * 16 + 4 * g;
-        if (col >= p.ncols) continue;
-        f32x4 val = acc[cb][pb];
+      for (int pb = 0; pb < 2; ++pb) {
+        if (pidx[pb] >= p.npos) continue;
+        f32x4 val = acc[pb];
         if (p.mode == 1) {
           if (p.colbias) {
             const T* cbp = static_cast<const T*>(p.colbias) + col;
 #pragma unroll
             for (int i = 0; i < 4; ++i) val[i] += Tr<T>::to_f(cbp[i]);
           }
-          T* dst = static_cast<T*>(p.y[0]) + z_row(pidx, p.N, p.ending) * p.ncols + col;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) dst[i] = Tr<T>::from_f(val[i]);
+          st4<T>(static_cast<T*>(p.y[0]) + z_row(pidx[pb], p.N, p.ending) * p.ncols + col, val);
         } else {
           const int m = col / p.HC;
           if (m < 4) {
@@ -184,15 +220,13 @@ rowgemm_kernel(GemmParams p) {
 #pragma unroll
               for (int i = 0; i < 4; ++i) val[i] += Tr<T>::to_f(cbp[i]);
             }
-            T* dst = static_cast<T*>(p.y[m]) + pidx * p.HC + cc;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) dst[i] = Tr<T>::from_f(val[i]);
+            st4<T>(static_cast<T*>(p.y[m]) + pidx[pb] * p.HC + cc, val);
           } else {
             T* bias = static_cast<T*>(p.y[4]);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int hh = col - 4 * p.HC + i;
-              if (hh < p.H) bias[(int64_t)hh * p.npos + pidx] = Tr<T>::from_f(val[i]);
+              if (hh < p.H) bias[(int64_t)hh * p.npos + pidx[pb]] = Tr<T>::from_f(val[i]);
             }
           }
         }
@@ -201,20 +235,46 @@ rowgemm_kernel(GemmParams p) {
   }
 }
 
-template <typename T>
-hipError_t launch_gemm(GemmParams& p, hipStream_t s) {
-  constexpr int TP = 4 * 16 * GemmCfg<T>::PB;
-  const int64_t tiles = (p.npos + TP - 1) / TP;
-  if (tiles > (int64_t)INT32_MAX - 8) return hipErrorInvalidValue;
-  p.total_tiles = (int)tiles;
-  const int grid = ((p.total_tiles + kNumXcd - 1) / kNumXcd) * kNumXcd;
-  const size_t lds = (size_t)(TP + COLS) * (p.K + PAD) * sizeof(T);
+template <typename T, int KSTEPS>
+hipError_t launch_pass(GemmParams& p, size_t lds, int grid, hipStream_t s) {
   hipError_t e = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&rowgemm_kernel<T>),
+      reinterpret_cast<const void*>(&rowgemm_kernel<T, KSTEPS>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(rowgemm_kernel<T>, dim3(grid), dim3(256), lds, s, p);
+  hipLaunchKernelGGL((rowgemm_kernel<T, KSTEPS>), dim3(grid), dim3(512), lds, s, p);
   return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_gemm(GemmParams& p, hipStream_t s) {
+  const int64_t tiles = (p.npos + TP - 1) / TP;
+  if (tiles > (int64_t)INT32_MAX) return hipErrorInvalidValue;
+  p.ntiles = (int)tiles;
+  const int grid = (int)std::min<int64_t>(tiles, 256);
+  const size_t row_bytes = (size_t)(p.K + PAD) * sizeof(T);
+  const size_t ln_bytes = 2 * kMaxK * sizeof(float);
+  int per_pass = (int)((kLdsBudget - ln_bytes) / row_bytes) / 16 * 16;
+  const int ncols_pad = (p.ncols + 15) / 16 * 16;
+  per_pass = std::min(per_pass, ncols_pad);
+  for (int c0 = 0; c0 < p.ncols; c0 += per_pass) {
+    p.col0 = c0;
+    p.pass_cols = std::min(per_pass, ncols_pad - c0);
+    const size_t lds = (size_t)p.pass_cols * row_bytes + ln_bytes;
+    hipError_t e;
+    switch (p.K / 32) {
+      case 1: e = launch_pass<T, 1>(p, lds, grid, s); break;
+      case 2: e = launch_pass<T, 2>(p, lds, grid, s); break;
+      case 3: e = launch_pass<T, 3>(p, lds, grid, s); break;
+      case 4: e = launch_pass<T, 4>(p, lds, grid, s); break;
+      case 5: e = launch_pass<T, 5>(p, lds, grid, s); break;
+      case 6: e = launch_pass<T, 6>(p, lds, grid, s); break;
+      case 7: e = launch_pass<T, 7>(p, lds, grid, s); break;
+      case 8: e = launch_pass<T, 8>(p, lds, grid, s); break;
+      default: return hipErrorInvalidValue;
+    }
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t dispatch(int dtype, GemmParams& p, hipStream_t s) {

@@ -91,10 +91,10 @@ def rand_module(N, CZ, H, C, dtype, seed=0, mask=None, dout=False,
                 ln_affine=False, gate_bias=False, out_bias=False):
     """Module inputs: z ~ N(0,1) [N,N,CZ]; every projection weight
     ~ N(0, 1/fan_in) (standard deviation fan_in^-1/2, fan_in = CZ for the
-    input projections and H*C for the output projection); LayerNorm weight 1
-    and bias 0 unless ln_affine; gate/output bias vectors 0 unless requested.
-    Draw order: z, w_q, w_k, w_v, w_g, w_bias, w_o, mask, dout, then the
-    optional affine/bias draws."""
+    input projections and H*C for the output projection), stored [out, in]
+    as torch.nn.Linear does; LayerNorm weight 1 and bias 0 unless ln_affine;
+    gate/output bias vectors 0 unless requested.  Draw order: z, w_q, w_k,
+    w_v, w_g, w_bias, w_o, mask, dout, then the optional affine/bias draws."""
     gen = torch.Generator().manual_seed(seed)
     HC = H * C
 
@@ -104,9 +104,9 @@ def rand_module(N, CZ, H, C, dtype, seed=0, mask=None, dout=False,
     d = {"z": draw((N, N, CZ))}
     s_in = CZ ** -0.5
     for name in ("w_q", "w_k", "w_v", "w_g"):
-        d[name] = draw((CZ, HC), s_in)
-    d["w_bias"] = draw((CZ, H), s_in)
-    d["w_o"] = draw((HC, CZ), HC ** -0.5)
+        d[name] = draw((HC, CZ), s_in)
+    d["w_bias"] = draw((H, CZ), s_in)
+    d["w_o"] = draw((CZ, HC), HC ** -0.5)
     d["mask"] = _key_mask(mask, N, gen) if isinstance(mask, str) else mask
     d["dout"] = draw((1, N, N, H, C)) if dout else None
     d["ln_w"] = draw((CZ,), 0.2) + 1 if ln_affine else round_to(torch.ones(CZ), dtype)

@@ -144,9 +144,10 @@ evo_status_t evo_attn_bwd(evo_dtype_t dtype, int64_t B, int64_t R, int64_t N,
  *   z          [N,N,CZ] dtype, the pair representation.
  *   ln_w,ln_b  [CZ] dtype, LayerNorm weight and bias; ln_eps > 0.
  *              LayerNorm uses the population variance, statistics in fp32.
- *   w_q,w_k,w_v,w_g  [CZ, H*C] dtype, y = x . W (row-major, x a row vector).
+ *   w_q,w_k,w_v,w_g  [H*C, CZ] dtype in [out, in] layout (as
+ *              torch.nn.Linear.weight): y = x . W^T, x a row vector.
  *   b_g        [H*C] dtype, gate bias; NULL = zero.
- *   w_bias     [CZ, H] dtype, pair-bias projection.
+ *   w_bias     [H, CZ] dtype, pair-bias projection ([out, in]).
  *   ending     0 = starting node: line i holds z[i,:], so q[0,i,j] is the
  *              projection of z[i,j] and bias[0,h,j,k] comes from z[j,k].
  *              1 = ending node: line j holds column z[:,j], so q[0,j,i] is
@@ -169,7 +170,8 @@ evo_status_t tri_attn_project(evo_dtype_t dtype, int64_t N, int64_t CZ,
  *
  *   o     [1,N,N,H,C] dtype (line layout, as produced by evo_attn_fwd on the
  *         tensors of tri_attn_project).
- *   w_o   [H*C, CZ] dtype;  b_o [CZ] dtype or NULL = zero.
+ *   w_o   [CZ, H*C] dtype in [out, in] layout: out = O . w_o^T + b_o;
+ *         b_o [CZ] dtype or NULL = zero.
  *   out   [N,N,CZ] dtype; for the ending node, line j / place i is written to
  *         out[i,j].
  */

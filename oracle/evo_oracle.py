@@ -244,6 +244,9 @@ def dbias_query_rows(q, k, v, gate, key_mask, bias, dout, b, picks):
 # representation; the gate projection and the output projection carry a
 # bias vector, the others do not; the module returns the update only.
 #
+# Weights follow the torch.nn.Linear convention: W has shape [out, in] and
+# y = x . W^T (+ bias vector).
+#
 # Starting node: line i, query j, key k:
 #     s_h(i,j,k) = <q_ij, k_ik>/sqrt(C) + b_jk[h],  out_ij = g_ij * sum_k a v_ik
 # Ending node: line j (a column of z), query i, key k:
@@ -260,18 +263,18 @@ def layer_norm(x, w, b, eps):
 
 
 def _pair_bias(z, ln_w, ln_b, eps, w_bias):
-    """b[j, k, h] = LN(z)[j, k] . w_bias[:, h], computed one z row at a time
+    """b[j, k, h] = LN(z)[j, k] . w_bias[h, :], computed one z row at a time
     to keep memory at O(N^2 * H)."""
     N = z.shape[0]
-    H = w_bias.shape[1]
+    H = w_bias.shape[0]
     out = np.empty((N, N, H))
     for j in range(N):
-        out[j] = layer_norm(z[j], ln_w, ln_b, eps) @ w_bias
+        out[j] = layer_norm(z[j], ln_w, ln_b, eps) @ w_bias.T
     return out
 
 
 def _proj(x, w, H, C, bias_vec=None):
-    y = x @ w
+    y = x @ w.T
     if bias_vec is not None:
         y = y + bias_vec
     return y.reshape(x.shape[:-1] + (H, C))
@@ -309,9 +312,9 @@ def tri_project(z, ln_w, ln_b, eps, w_q, w_k, w_v, w_g, b_g, w_bias, H, C,
 
 def tri_out_project(o, w_o, b_o, ending):
     """Output projection: o [1, N, N, H, C] in line layout -> [N, N, CZ] in z
-    layout (lines are columns of z for the ending node)."""
+    layout (lines are columns of z for the ending node); w_o is [CZ, H*C]."""
     _, N, _, H, C = o.shape
-    y = o[0].reshape(N, N, H * C) @ w_o + b_o
+    y = o[0].reshape(N, N, H * C) @ w_o.T + b_o
     return y.transpose(1, 0, 2) if ending else y
 
 
@@ -340,7 +343,7 @@ def tri_module_lines(z, residue_mask, ln_w, ln_b, eps, w_q, w_k, w_v, w_g,
         v = _proj(xl, w_v, H, C)
         g = _proj(xl, w_g, H, C, b_g)
         o, _ = attention_line_forward(q, k, v, g, bias, keep)
-        res.append(o.reshape(N, H * C) @ w_o + b_o)
+        res.append(o.reshape(N, H * C) @ w_o.T + b_o)
     return np.stack(res)
 
 

@@ -2,8 +2,12 @@
 
 Tolerances of the parity bar (written here, used by every GPU parity test):
   fp32 inputs:  max |gpu - oracle| <= 1e-4
-  bf16 inputs (fp32 accumulation): max |gpu - oracle| <= 2e-2 and
-                ||gpu - oracle||_2 / ||oracle||_2 <= 1e-2
+  bf16 inputs (fp32 accumulation): |gpu - oracle| <= 2e-2 + 2^-8 |oracle|
+                elementwise, and ||gpu - oracle||_2 / ||oracle||_2 <= 1e-2.
+The 2^-8 |oracle| term is the rounding of the stored bf16 output itself
+(unit roundoff of an 8-bit significand): a value of magnitude 5 cannot be
+stored closer than ~0.02, so the 2e-2 absolute bound is applied beyond the
+output's own representation error.
 """
 import sys
 
@@ -13,6 +17,7 @@ import torch
 FP32_MAX_ABS = 1e-4
 BF16_MAX_ABS = 2e-2
 BF16_REL_L2 = 1e-2
+BF16_UNIT_ROUNDOFF = 2.0 ** -8
 
 
 def log(msg):
@@ -56,6 +61,9 @@ def compare(name, got, ref, dtype, scale=1.0):
         assert np.array_equal(got[~fin], ref[~fin]), f"{name}: infinities differ"
     d = np.abs(got[fin] - ref[fin])
     max_abs = float(d.max()) if d.size else 0.0
+    # excess over the output-rounding allowance (bf16 only)
+    rep = BF16_UNIT_ROUNDOFF * np.abs(ref[fin]) if dtype == "bf16" else 0.0
+    excess = float((d - rep).max()) if d.size else 0.0
     nrm = float(np.linalg.norm(ref[fin]))
     rel = float(np.linalg.norm(got[fin] - ref[fin]) / nrm) if nrm > 0 else max_abs
     peak = float(np.abs(ref[fin]).max()) if d.size else 0.0
@@ -63,6 +71,6 @@ def compare(name, got, ref, dtype, scale=1.0):
     if dtype == "fp32":
         assert max_abs <= FP32_MAX_ABS * scale, f"{name}: max_abs {max_abs:.3e}"
     else:
-        assert max_abs <= BF16_MAX_ABS * scale, f"{name}: max_abs {max_abs:.3e}"
+        assert excess <= BF16_MAX_ABS * scale, f"{name}: max_abs {max_abs:.3e} (excess {excess:.3e})"
         assert rel <= BF16_REL_L2, f"{name}: rel_l2 {rel:.3e}"
     return max_abs, rel

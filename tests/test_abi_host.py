@@ -102,7 +102,7 @@ def test_workspace_queries():
     n = L.evo_attn_bwd_workspace_bytes(1, 1, 512, 512, 4, 32)
     assert n > 4 * 512 * 512 * 128 * 2  # the transposed slabs alone
     assert L.evo_attn_bwd_workspace_bytes(1, 1, 512, 512, 4, 16) == 0
-    assert L.evo_attn_bwd_workspace_bytes(1, 1, 4, 2048, 4, 32) == 0
+    assert L.evo_attn_bwd_workspace_bytes(1, 1, 1, 70000, 1, 32) == 0
     t = L.tri_attn_workspace_bytes(1, 768, 128, 4, 32)
     assert t >= 5 * 768 * 768 * 128 * 2 + 4 * 768 * 768 * 2
     assert L.tri_attn_workspace_bytes(1, 768, 100, 4, 32) == 0
@@ -126,7 +126,7 @@ def bwd(**kw):
     (dict(lse=None), ops.EVO_EINVAL, "'lse' is NULL"),
     (dict(ws=None), ops.EVO_EWORKSPACE, "workspace"),
     (dict(wsb=16), ops.EVO_EWORKSPACE, "workspace"),
-    (dict(N=2048), ops.EVO_ENOTSUP, "N <= 1024"),
+    (dict(N=70000, R=1, H=1), ops.EVO_ENOTSUP, "N <= 65536"),
 ])
 def test_bwd_validation(kw, status, needle):
     assert bwd(**kw) == status

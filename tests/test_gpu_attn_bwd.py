@@ -28,7 +28,7 @@ def oracle_bwd(d):
 
 SHAPES = [  # B, R, N, H
     (1, 1, 1, 1), (1, 3, 17, 2), (2, 2, 64, 1), (1, 4, 100, 2), (1, 2, 130, 3),
-    (1, 5, 256, 1),
+    (1, 5, 256, 1), (1, 2, 300, 1),
 ]
 
 

@@ -57,7 +57,7 @@ def test_out_project_parity(dtype, ending):
     log(f"case out_project {dtype} ending={ending}")
     gen = torch.Generator().manual_seed(4)
     o = synth.round_to(torch.randn((1, N, N, H, 32), generator=gen), dtype)
-    w_o = synth.round_to(torch.randn((H * 32, CZ), generator=gen) / 10, dtype)
+    w_o = synth.round_to(torch.randn((CZ, H * 32), generator=gen) / 10, dtype)
     b_o = synth.round_to(torch.randn((CZ,), generator=gen), dtype)
     out = ops.tri_attn_out_project(dev(o), dev(w_o), dev(b_o), CZ, ending)
     torch.cuda.synchronize()

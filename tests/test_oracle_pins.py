@@ -295,13 +295,13 @@ def module_case(seed, N=7, CZ=12, H=2, C=3, mask=True):
     d = dict(z=rng.standard_normal((N, N, CZ)),
              ln_w=1 + 0.2 * rng.standard_normal(CZ),
              ln_b=0.2 * rng.standard_normal(CZ), eps=1e-5,
-             w_q=rng.standard_normal((CZ, HC)) / CZ ** 0.5,
-             w_k=rng.standard_normal((CZ, HC)) / CZ ** 0.5,
-             w_v=rng.standard_normal((CZ, HC)) / CZ ** 0.5,
-             w_g=rng.standard_normal((CZ, HC)) / CZ ** 0.5,
+             w_q=rng.standard_normal((HC, CZ)) / CZ ** 0.5,
+             w_k=rng.standard_normal((HC, CZ)) / CZ ** 0.5,
+             w_v=rng.standard_normal((HC, CZ)) / CZ ** 0.5,
+             w_g=rng.standard_normal((HC, CZ)) / CZ ** 0.5,
              b_g=0.3 * rng.standard_normal(HC),
-             w_bias=rng.standard_normal((CZ, H)) / CZ ** 0.5,
-             w_o=rng.standard_normal((HC, CZ)) / HC ** 0.5,
+             w_bias=rng.standard_normal((H, CZ)) / CZ ** 0.5,
+             w_o=rng.standard_normal((CZ, HC)) / HC ** 0.5,
              b_o=0.3 * rng.standard_normal(CZ), H=H, C=C)
     if mask:
         m = (rng.random(N) < 0.7).astype(np.uint8)
@@ -371,16 +371,41 @@ def test_module_equals_project_core_outproject(ending):
     # and the project layout itself against plain per-position matmuls
     x = O.layer_norm(d["z"], d["ln_w"], d["ln_b"], d["eps"])
     i, j = 2, 5
-    qi = (x[i, j] @ d["w_q"]).reshape(H, C)
+    qi = (x[i, j] @ d["w_q"].T).reshape(H, C)
     line, pos = (j, i) if ending else (i, j)
     np.testing.assert_allclose(q[0, line, pos], qi, rtol=1e-12, atol=1e-13)
-    bij = x[i, j] @ d["w_bias"]
+    bij = x[i, j] @ d["w_bias"].T
     # starting: bias[h, j', k'] = b_{j'k'} ; ending: bias[h, i', k'] = b_{k'i'}
     if ending:
         np.testing.assert_allclose(bias[0, :, j, i], bij, rtol=1e-12)
     else:
         np.testing.assert_allclose(bias[0, :, i, j], bij, rtol=1e-12)
     assert N == q.shape[1]
+
+
+def test_projection_matches_torch_linear():
+    """Library routine: torch.nn.functional.layer_norm + linear (fp64)."""
+    d = module_case(28)
+    H, C = d["H"], d["C"]
+    q, k, v, g, bias = O.tri_project(d["z"], d["ln_w"], d["ln_b"], d["eps"],
+                                     d["w_q"], d["w_k"], d["w_v"], d["w_g"],
+                                     d["b_g"], d["w_bias"], H, C, False)
+    z = torch.tensor(d["z"])
+    x = F.layer_norm(z, (z.shape[-1],), torch.tensor(d["ln_w"]),
+                     torch.tensor(d["ln_b"]), d["eps"])
+    N = z.shape[0]
+    for got, w, bvec in ((q, "w_q", None), (g, "w_g", "b_g")):
+        ref = F.linear(x, torch.tensor(d[w]),
+                       None if bvec is None else torch.tensor(d[bvec]))
+        np.testing.assert_allclose(got[0].reshape(N, N, H * C), ref.numpy(),
+                                   rtol=1e-12, atol=1e-12)
+    refb = F.linear(x, torch.tensor(d["w_bias"])).permute(2, 0, 1).numpy()
+    np.testing.assert_allclose(bias[0], refb, rtol=1e-12, atol=1e-12)
+    o = np.random.default_rng(29).standard_normal((1, N, N, H, C))
+    ref = F.linear(torch.tensor(o[0]).reshape(N, N, H * C),
+                   torch.tensor(d["w_o"]), torch.tensor(d["b_o"])).numpy()
+    np.testing.assert_allclose(O.tri_out_project(o, d["w_o"], d["b_o"], False),
+                               ref, rtol=1e-12, atol=1e-12)
 
 
 def test_module_lines_subset():
