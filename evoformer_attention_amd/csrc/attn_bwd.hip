@@ -454,56 +454,29 @@ __device__ __forceinline__ int k_lds_row(int p) {
   return half * 32 + kb * 16 + gg * 4 + i;
 }
 
-template <typename T> struct KRaw;   // one thread's share of a 64-key tile
-template <> struct KRaw<bf16_t> { uint4 k, v, kt; };
-template <> struct KRaw<float> { uint4 k0, k1, v0, v1, kt0, kt1; };
+// One thread's share of a 64-key tile, held in plain locals (16-byte
+// chunks; fp32 needs two per tensor): key t/4, dims 8*(t%4)..+7 of K and V,
+// and row t/8, keys 8*(t%8)..+7 of the K^T slab.
+#define EVO_FETCH_K(T, K_, V_, KT_, k0_)                                          \
+  do {                                                                        \
+    const int t_ = threadIdx.x;                                               \
+    const int kk_ = min((k0_) + (t_ >> 2), N - 1), ch_ = t_ & 3;              \
+    const uint4* ks_ = reinterpret_cast<const uint4*>((K_) + (int64_t)kk_ * pos_stride + ch_ * 8); \
+    const uint4* vs_ = reinterpret_cast<const uint4*>((V_) + (int64_t)kk_ * pos_stride + ch_ * 8); \
+    const uint4* ts_ = reinterpret_cast<const uint4*>((KT_) + (int64_t)(t_ >> 3) * Np + (k0_) + (t_ & 7) * 8); \
+    rk0 = ks_[0]; rv0 = vs_[0]; rt0 = ts_[0];                                  \
+    if constexpr (sizeof(T) == 4) { rk1 = ks_[1]; rv1 = vs_[1]; rt1 = ts_[1]; } \
+  } while (0)
 
-// Thread t stages key t/4 (dims 8*(t%4)..+7) of K and V, and row t/8 of the
-// K^T slab (keys 8*(t%8)..+7).
-template <typename T>
-__device__ __forceinline__ void fetch_k(KRaw<T>& raw, const T* kline, const T* vline,
-                                        const T* ktslab, int k0, int N, int Np,
-                                        int pos_stride) {
-  const int t = threadIdx.x;
-  const int kk = min(k0 + (t >> 2), N - 1), ch = t & 3;
-  const T* ks = kline + (int64_t)kk * pos_stride + ch * 8;
-  const T* vs = vline + (int64_t)kk * pos_stride + ch * 8;
-  const T* ts = ktslab + (int64_t)(t >> 3) * Np + k0 + (t & 7) * 8;
-  if constexpr (sizeof(T) == 2) {
-    raw.k = *reinterpret_cast<const uint4*>(ks);
-    raw.v = *reinterpret_cast<const uint4*>(vs);
-    raw.kt = *reinterpret_cast<const uint4*>(ts);
-  } else {
-    raw.k0 = reinterpret_cast<const uint4*>(ks)[0];
-    raw.k1 = reinterpret_cast<const uint4*>(ks)[1];
-    raw.v0 = reinterpret_cast<const uint4*>(vs)[0];
-    raw.v1 = reinterpret_cast<const uint4*>(vs)[1];
-    raw.kt0 = reinterpret_cast<const uint4*>(ts)[0];
-    raw.kt1 = reinterpret_cast<const uint4*>(ts)[1];
-  }
-}
-
-template <typename T>
-__device__ __forceinline__ void store_k(const KRaw<T>& raw, T* sK, T* sV, T* sKt, int ks_,
-                                        int kts) {
-  const int t = threadIdx.x;
-  const int row = k_lds_row(t >> 2), ch = t & 3;
-  T* dk = sK + row * ks_ + ch * 8;
-  T* dv = sV + row * ks_ + ch * 8;
-  T* dt = sKt + (t >> 3) * kts + (t & 7) * 8;
-  if constexpr (sizeof(T) == 2) {
-    *reinterpret_cast<uint4*>(dk) = raw.k;
-    *reinterpret_cast<uint4*>(dv) = raw.v;
-    *reinterpret_cast<uint4*>(dt) = raw.kt;
-  } else {
-    reinterpret_cast<uint4*>(dk)[0] = raw.k0;
-    reinterpret_cast<uint4*>(dk)[1] = raw.k1;
-    reinterpret_cast<uint4*>(dv)[0] = raw.v0;
-    reinterpret_cast<uint4*>(dv)[1] = raw.v1;
-    reinterpret_cast<uint4*>(dt)[0] = raw.kt0;
-    reinterpret_cast<uint4*>(dt)[1] = raw.kt1;
-  }
-}
+#define EVO_STORE_K(T, sK_, sV_, sKt_, KS_, TS_)                                  \
+  do {                                                                        \
+    const int t_ = threadIdx.x;                                               \
+    uint4* dk_ = reinterpret_cast<uint4*>((sK_) + k_lds_row(t_ >> 2) * (KS_) + (t_ & 3) * 8); \
+    uint4* dv_ = reinterpret_cast<uint4*>((sV_) + k_lds_row(t_ >> 2) * (KS_) + (t_ & 3) * 8); \
+    uint4* dt_ = reinterpret_cast<uint4*>((sKt_) + (t_ >> 3) * (TS_) + (t_ & 7) * 8); \
+    dk_[0] = rk0; dv_[0] = rv0; dt_[0] = rt0;                                  \
+    if constexpr (sizeof(T) == 4) { dk_[1] = rk1; dv_[1] = rv1; dt_[1] = rt1; } \
+  } while (0)
 
 template <typename T> struct BLds;
 template <> struct BLds<bf16_t> { static constexpr int KS = 40, TS = 72; };
@@ -559,14 +532,16 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) dq[qb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  KRaw<T> raw;
-  fetch_k<T>(raw, K, V, KT, 0, N, Np, pos_stride);
+  uint4 rk0, rk1, rv0, rv1, rt0, rt1;
+  rk1 = rv1 = rt1 = make_uint4(0, 0, 0, 0);
+  EVO_FETCH_K(T, K, V, KT, 0);
   const int ntiles = (N + 63) / 64;
   for (int tile = 0; tile < ntiles; ++tile) {
     const int k0 = tile * 64, buf = tile & 1;
-    store_k<T>(raw, sK[buf], sV[buf], sKt[buf], KS, TS);
+    EVO_STORE_K(T, sK[buf], sV[buf], sKt[buf], KS, TS);
     __syncthreads();
-    if (tile + 1 < ntiles) fetch_k<T>(raw, K, V, KT, k0 + 64, N, Np, pos_stride);
+    // next tile (the last iteration re-fetches its own tile, unused)
+    EVO_FETCH_K(T, K, V, KT, min(k0 + 64, (ntiles - 1) * 64));
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       f32x4 s[2][2], dp[2][2];  // [qb][kb]
@@ -623,6 +598,9 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdParams p) {
   }
 }
 
+#undef EVO_FETCH_K
+#undef EVO_STORE_K
+
 // dBias: workgroup = one head, 128 queries (32 per wave) x 64 keys, for a
 // group of rows; the bias tile (MFMA accumulator operand) and the dBias
 // accumulator stay in registers while the rows stream by, their K and V
@@ -664,68 +642,55 @@ __global__ void __launch_bounds__(256) bwd_dbias_kernel(BwdParams p) {
   }
   const int r_begin = rg * p.rows_per_group;
   const int r_end = min(R, r_begin + p.rows_per_group);
-  // thread t stages key t/4 (dims 8*(t%4)..+7) of K and V for one row
+  // thread t stages key t/4 (dims 8*(t%4)..+7) of K and V for one row;
+  // the next row's tiles and query-side operands are prefetched into plain
+  // locals (the last iteration re-fetches its own row, unused).
   const int kk = min(k0 + (tid >> 2), N - 1), ch = tid & 3;
-  auto fetch = [&](int r, uint4 (&kr)[2], uint4 (&vr)[2]) {
-    const int64_t lbase = ((int64_t)b * R + r) * N * pos_stride + h * C;
-    const T* ks = static_cast<const T*>(p.k) + lbase + (int64_t)kk * pos_stride + ch * 8;
-    const T* vs = static_cast<const T*>(p.v) + lbase + (int64_t)kk * pos_stride + ch * 8;
-    kr[0] = reinterpret_cast<const uint4*>(ks)[0];
-    vr[0] = reinterpret_cast<const uint4*>(vs)[0];
-    if constexpr (sizeof(T) == 4) {
-      kr[1] = reinterpret_cast<const uint4*>(ks)[1];
-      vr[1] = reinterpret_cast<const uint4*>(vs)[1];
-    }
-  };
-  // query-side operands of a row: Q (scaled), dO, base-2 LSE, D
-  auto fetch_q = [&](int r, Op (&qf)[2], Op (&df)[2], float (&l2)[2], float (&dd)[2]) {
-    const int64_t line = (int64_t)b * R + r;
-    const int64_t lbase = line * N * pos_stride + h * C;
-    const int64_t lh = line * H + h;
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const int q = qw0 + qb * 16 + l16;
-      const int qc = min(q, N - 1);
-      qf[qb] = ldop<T>(static_cast<const T*>(p.q) + lbase + (int64_t)qc * pos_stride + 8 * g);
-      df[qb] = ldop<T>(static_cast<const T*>(p.dopre) + lbase + (int64_t)qc * pos_stride + 8 * g);
-      l2[qb] = q < N ? p.lse2[lh * Np + q] : INFINITY;
-      dd[qb] = q < N ? p.dd[lh * Np + q] : 0.f;
-    }
-  };
-  uint4 kr[2], vr[2];
-  Op qn[2], dn[2];
-  float l2n[2], ddn[2];
-  if (r_begin < r_end) {
-    fetch(r_begin, kr, vr);
-    fetch_q(r_begin, qn, dn, l2n, ddn);
-  }
+  uint4 rk0, rk1, rv0, rv1;
+  rk1 = rv1 = make_uint4(0, 0, 0, 0);
+  Op qn0, qn1, dn0, dn1;
+  float l2n0, l2n1, ddn0, ddn1;
+#define EVO_FETCH_ROW(r_)                                                          \
+  do {                                                                         \
+    const int64_t line_ = (int64_t)b * R + (r_);                               \
+    const int64_t lb_ = line_ * N * pos_stride + h * C;                        \
+    const int64_t lh_ = line_ * H + h;                                         \
+    const uint4* ks_ = reinterpret_cast<const uint4*>(                         \
+        static_cast<const T*>(p.k) + lb_ + (int64_t)kk * pos_stride + ch * 8); \
+    const uint4* vs_ = reinterpret_cast<const uint4*>(                         \
+        static_cast<const T*>(p.v) + lb_ + (int64_t)kk * pos_stride + ch * 8); \
+    rk0 = ks_[0]; rv0 = vs_[0];                                                \
+    if constexpr (sizeof(T) == 4) { rk1 = ks_[1]; rv1 = vs_[1]; }              \
+    const int qa_ = qw0 + l16, qb_ = qw0 + 16 + l16;                           \
+    qn0 = ldop<T>(static_cast<const T*>(p.q) + lb_ + (int64_t)min(qa_, N - 1) * pos_stride + 8 * g); \
+    qn1 = ldop<T>(static_cast<const T*>(p.q) + lb_ + (int64_t)min(qb_, N - 1) * pos_stride + 8 * g); \
+    dn0 = ldop<T>(static_cast<const T*>(p.dopre) + lb_ + (int64_t)min(qa_, N - 1) * pos_stride + 8 * g); \
+    dn1 = ldop<T>(static_cast<const T*>(p.dopre) + lb_ + (int64_t)min(qb_, N - 1) * pos_stride + 8 * g); \
+    l2n0 = qa_ < N ? p.lse2[lh_ * Np + qa_] : INFINITY;                        \
+    l2n1 = qb_ < N ? p.lse2[lh_ * Np + qb_] : INFINITY;                        \
+    ddn0 = qa_ < N ? p.dd[lh_ * Np + qa_] : 0.f;                               \
+    ddn1 = qb_ < N ? p.dd[lh_ * Np + qb_] : 0.f;                               \
+  } while (0)
+  if (r_begin < r_end) EVO_FETCH_ROW(r_begin);
   for (int r = r_begin; r < r_end; ++r) {
     const int buf = (r - r_begin) & 1;
     {
       const int row = k_lds_row(tid >> 2);
-      T* dk = sK[buf] + row * KS + ch * 8;
-      T* dv = sV[buf] + row * KS + ch * 8;
-      reinterpret_cast<uint4*>(dk)[0] = kr[0];
-      reinterpret_cast<uint4*>(dv)[0] = vr[0];
+      uint4* dk = reinterpret_cast<uint4*>(sK[buf] + row * KS + ch * 8);
+      uint4* dv = reinterpret_cast<uint4*>(sV[buf] + row * KS + ch * 8);
+      dk[0] = rk0;
+      dv[0] = rv0;
       if constexpr (sizeof(T) == 4) {
-        reinterpret_cast<uint4*>(dk)[1] = kr[1];
-        reinterpret_cast<uint4*>(dv)[1] = vr[1];
+        dk[1] = rk1;
+        dv[1] = rv1;
       }
     }
-    Op qf[2], df[2];
-    float l2[2], dd[2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      qf[qb] = scale8(qn[qb], p.qscale);
-      df[qb] = dn[qb];
-      l2[qb] = l2n[qb];
-      dd[qb] = ddn[qb];
-    }
+    const Op qf[2] = {scale8(qn0, p.qscale), scale8(qn1, p.qscale)};
+    const Op df[2] = {dn0, dn1};
+    const float l2[2] = {l2n0, l2n1};
+    const float dd[2] = {ddn0, ddn1};
     __syncthreads();
-    if (r + 1 < r_end) {
-      fetch(r + 1, kr, vr);
-      fetch_q(r + 1, qn, dn, l2n, ddn);
-    }
+    EVO_FETCH_ROW(min(r + 1, r_end - 1));
     const uint8_t* mrow = ROW_MASK ? p.mask + ((int64_t)b * p.mask_rows + r) * N : nullptr;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -761,6 +726,7 @@ __global__ void __launch_bounds__(256) bwd_dbias_kernel(BwdParams p) {
     }
   }
 
+#undef EVO_FETCH_ROW
   if (!p.dbias) return;
   float* dst = (p.n_rg == 1) ? nullptr : p.dbpart + ((int64_t)rg * p.B * H + bh) * Np * Np;
 #pragma unroll
