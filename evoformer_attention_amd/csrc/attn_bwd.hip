@@ -19,7 +19,8 @@
 //   prep      dO, dG, D, base-2 LSE, and transposed copies Q^T, dO^T, K^T
 //             (one [C, N] slab per line and head) so that every MFMA operand
 //             below is a contiguous 16-byte load.
-//   bias      the base-2, mask-folded pair bias in both orientations.
+//   bias      the mask-folded pair bias in both orientations (working dtype;
+//             the exp argument s*log2(e) - LSE*log2(e) is one FMA).
 //   dkdv      one line, one head, 128 keys per workgroup (32 per wave);
 //             loops over 32-query steps staged through double-buffered LDS
 //             (next step prefetched into registers).  Lane = key in the
@@ -73,8 +74,8 @@ BwdLayout bwd_layout(int dtype, int64_t B, int64_t R, int64_t N, int64_t H) {
   L.off_kt = o;    o += a256(lines * C * L.Np * es);
   L.off_lse2 = o;  o += a256(lines * L.Np * 4);
   L.off_d = o;     o += a256(lines * L.Np * 4);
-  L.off_bp = o;    o += a256((size_t)B * H * L.Np * L.Np * 4);
-  L.off_bpt = o;   o += a256((size_t)B * H * L.Np * L.Np * 4);
+  L.off_bp = o;    o += a256((size_t)B * H * L.Np * L.Np * es);
+  L.off_bpt = o;   o += a256((size_t)B * H * L.Np * L.Np * es);
   L.off_dbpart = o;
   if (L.n_rg > 1) o += a256((size_t)L.n_rg * B * H * L.Np * L.Np * 4);
   L.total = o;
@@ -134,9 +135,10 @@ struct BwdParams {
   void* dq; void* dk; void* dv; void* dgate; float* dbias;
   void* dopre;   // dO (= dout when there is no gate)
   void* qt; void* dot; void* kt;
-  float* lse2; float* dd; float* bp; float* bpt; float* dbpart;
+  float* lse2; float* dd; float* dbpart;
+  void* bp; void* bpt;  // pair bias, natural units, masked, working dtype
   int B, R, N, H, Np, mask_rows, n_rg, rows_per_group, row_mask;
-  float qscale;  // log2(e) / sqrt(C)
+  float qscale;  // 1 / sqrt(C)
 };
 
 // ----------------------------------------------------------------- prep
@@ -214,8 +216,9 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdParams p) {
   st4e(static_cast<T*>(p.kt) + to, k2);
 }
 
-// Base-2 pair bias with the shared key mask folded in, both orientations.
-// bp[b,h,q,k] (q < Np, k < Np), bpt[b,h,k,q]; keys >= N are -inf.
+// Pair bias (natural units, working dtype) with the shared key mask folded
+// in, both orientations: bp[b,h,q,k] (q < Np, k < Np), bpt[b,h,k,q]; keys
+// >= N are -inf.  Every stored value is exact (a bias value, 0 or -inf).
 template <typename T>
 __global__ void __launch_bounds__(256) bwd_bias_kernel(BwdParams p) {
   __shared__ float tile[32][33];
@@ -233,17 +236,17 @@ __global__ void __launch_bounds__(256) bwd_bias_kernel(BwdParams p) {
     float v = -INFINITY;
     if (k < N) {
       v = 0.f;
-      if (Bias && q < N) v = Tr<T>::to_f(Bias[((int64_t)bh * N + q) * N + k]) * kLog2e;
+      if (Bias && q < N) v = Tr<T>::to_f(Bias[((int64_t)bh * N + q) * N + k]);
       if (p.mask && !p.row_mask && p.mask[(int64_t)b * p.mask_rows * N + k] == 0)
         v = -INFINITY;
     }
-    p.bp[((int64_t)bh * p.Np + q) * p.Np + k] = v;
+    static_cast<T*>(p.bp)[((int64_t)bh * p.Np + q) * p.Np + k] = Tr<T>::from_f(v);
     tile[yy][tx] = v;
   }
   __syncthreads();
   for (int yy = ty; yy < 32; yy += 8) {
     const int k = kb * 32 + yy, q = qb * 32 + tx;
-    p.bpt[((int64_t)bh * p.Np + k) * p.Np + q] = tile[tx][yy];
+    static_cast<T*>(p.bpt)[((int64_t)bh * p.Np + k) * p.Np + q] = Tr<T>::from_f(tile[tx][yy]);
   }
 }
 
@@ -281,7 +284,7 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(BwdParams p) {
   const T* DO = static_cast<const T*>(p.dopre);
   const T* QT = static_cast<const T*>(p.qt) + lh * C * Np;
   const T* DT = static_cast<const T*>(p.dot) + lh * C * Np;
-  const float* BPT = p.bpt + (int64_t)(b * H + h) * Np * Np;
+  const T* BPT = static_cast<const T*>(p.bpt) + (int64_t)(b * H + h) * Np * Np;
   const uint8_t* mrow = (p.mask && p.row_mask)
                             ? p.mask + ((int64_t)b * p.mask_rows + r) * N
                             : nullptr;
@@ -361,7 +364,7 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(BwdParams p) {
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
-        cbn[qb][kb] = ld4(BPT + (int64_t)krow[kb] * Np + q0 + qb * 16 + 4 * g);
+        cbn[qb][kb] = ld4e(BPT + (int64_t)krow[kb] * Np + q0 + qb * 16 + 4 * g);
   };
   (void)E16;
 
@@ -407,7 +410,7 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(BwdParams p) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float pv = kdead[kb] ? 0.f : exp2_fast(s[qb][kb][i] - l2[i]);
+          const float pv = kdead[kb] ? 0.f : exp2_fast(__builtin_fmaf(s[qb][kb][i], kLog2e, -l2[i]));
           s[qb][kb][i] = pv;
           dp[qb][kb][i] = pv * (dp[qb][kb][i] - dd[i]);
         }
@@ -513,7 +516,7 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdParams p) {
 
   Op qf[2], df[2];
   float l2[2], dd[2];
-  const float* brow[2];
+  const T* brow[2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int q = qw0 + qb * 16 + l16;
@@ -524,7 +527,7 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdParams p) {
     const int qp = min(q, Np - 1);
     l2[qb] = q < N ? p.lse2[lh * Np + q] : INFINITY;
     dd[qb] = q < N ? p.dd[lh * Np + q] : 0.f;
-    brow[qb] = p.bp + ((int64_t)(b * H + h) * Np + qp) * Np + 8 * g;
+    brow[qb] = static_cast<const T*>(p.bp) + ((int64_t)(b * H + h) * Np + qp) * Np + 8 * g;
   }
   f32x4 dq[2][2];  // [qb][cb]
 #pragma unroll
@@ -557,7 +560,7 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdParams p) {
         const Op kf = *reinterpret_cast<const Op*>(sK[buf] + (half * 32 + kb * 16 + l16) * KS + 8 * g);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
-          s[qb][kb] = mma32(kf, qf[qb], ld4(brow[qb] + k0 + half * 32 + 4 * kb));
+          s[qb][kb] = mma32(kf, qf[qb], ld4e(brow[qb] + k0 + half * 32 + 4 * kb));
       }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -573,7 +576,8 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdParams p) {
         for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float pv = dead[i] ? 0.f : exp2_fast(s[qb][kb][i] - l2[qb]);
+            const float pv =
+                dead[i] ? 0.f : exp2_fast(__builtin_fmaf(s[qb][kb][i], kLog2e, -l2[qb]));
             dp[qb][kb][i] = pv * (dp[qb][kb][i] - dd[qb]);
           }
       }
@@ -631,12 +635,12 @@ __global__ void __launch_bounds__(256) bwd_dbias_kernel(BwdParams p) {
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int qp = min(qw0 + qb * 16 + l16, Np - 1);
-    const float* brow = p.bp + ((int64_t)bh * Np + qp) * Np + k0 + 8 * g;
+    const T* brow = static_cast<const T*>(p.bp) + ((int64_t)bh * Np + qp) * Np + k0 + 8 * g;
 #pragma unroll
     for (int half = 0; half < 2; ++half)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        cbias[half][qb][kb] = ld4(brow + half * 32 + 4 * kb);
+        cbias[half][qb][kb] = ld4e(brow + half * 32 + 4 * kb);
         db[half][qb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
   }
@@ -719,7 +723,8 @@ __global__ void __launch_bounds__(256) bwd_dbias_kernel(BwdParams p) {
         for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float pv = dead[i] ? 0.f : exp2_fast(s[qb][kb][i] - l2[qb]);
+            const float pv =
+                dead[i] ? 0.f : exp2_fast(__builtin_fmaf(s[qb][kb][i], kLog2e, -l2[qb]));
             db[half][qb][kb][i] += pv * (dp[qb][kb][i] - dd[qb]);
           }
       }
@@ -828,8 +833,8 @@ hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t s) {
   p.kt = ws + L.off_kt;
   p.lse2 = reinterpret_cast<float*>(ws + L.off_lse2);
   p.dd = reinterpret_cast<float*>(ws + L.off_d);
-  p.bp = reinterpret_cast<float*>(ws + L.off_bp);
-  p.bpt = reinterpret_cast<float*>(ws + L.off_bpt);
+  p.bp = ws + L.off_bp;
+  p.bpt = ws + L.off_bpt;
   p.dbpart = reinterpret_cast<float*>(ws + L.off_dbpart);
   p.B = (int)a.B; p.R = (int)a.R; p.N = (int)a.N; p.H = (int)a.H;
   p.Np = (int)L.Np;
@@ -837,7 +842,7 @@ hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t s) {
   p.row_mask = a.mask && a.mask_rows > 1;
   p.n_rg = (int)L.n_rg;
   p.rows_per_group = (int)L.rows_per_group;
-  p.qscale = kLog2e / sqrtf((float)C);
+  p.qscale = 1.f / sqrtf((float)C);
   return a.dtype == 1 ? launch_t<bf16_t>(p, s) : launch_t<float>(p, s);
 }
 

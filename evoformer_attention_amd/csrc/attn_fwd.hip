@@ -11,10 +11,14 @@
 // item 1).
 //
 // Kernels.
-//   bias_prep  writes the pair bias once per call as fp32 [B, H, Nq, Nk]
-//              (Nq, Nk padded to the tile sizes) with the shared key mask and
-//              the padding keys folded in as -inf, so the main loop loads it
-//              straight into the matrix-core accumulator operand.
+//   bias_prep  writes the pair bias once per call, in the working dtype, as
+//              [B, H, Nq, Nk] (Nq, Nk padded to the tile sizes) with the
+//              shared key mask and the padding keys folded in as -inf, so the
+//              main loop needs no bounds or mask logic: each lane widens its
+//              8 consecutive keys straight into the matrix-core accumulator
+//              operand.  (Kept in bf16 for bf16 inputs: the bias tile is
+//              re-read by every group of lines, and at 2 bytes per element a
+//              head's bias stays resident in one XCD's L2.)
 //   attn_fwd   a workgroup (4 waves) owns 128 queries of one head and ROWS
 //              lines of one batch entry; each wave owns 32 queries.  Keys
 //              stream in tiles of 64 through double-buffered LDS, the next
@@ -69,7 +73,7 @@ struct FwdParams {
   const void* v;
   const void* gate;
   const uint8_t* mask;   // per-line masks only (shared masks are in biasp)
-  const float* biasp;    // [B, H, Nq, Nk] fp32, or null (no bias, no mask)
+  const void* biasp;     // [B, H, Nq, Nk] working dtype, or null (no bias, no mask)
   void* out;
   float* lse;
   int B, R, N, H, mask_rows;
@@ -190,7 +194,7 @@ __device__ __forceinline__ void st4f(float* p, const f32x4& v) {
 // masked by a shared mask or beyond N; q < Nq, k < Nk.
 template <typename T>
 __global__ void __launch_bounds__(256) fwd_bias_prep_kernel(
-    const T* bias, const uint8_t* mask, int shared_mask, float* biasp, int B,
+    const T* bias, const uint8_t* mask, int shared_mask, T* biasp, int B,
     int H, int N, int Nq, int Nk) {
   const int64_t total = (int64_t)B * H * Nq * (Nk / 4);
   for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total;
@@ -200,7 +204,7 @@ __global__ void __launch_bounds__(256) fwd_bias_prep_kernel(
     const int q = (int)(row % Nq);
     const int64_t bh = row / Nq;
     const int b = (int)(bh / H);
-    float v[4];
+    f32x4 v;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int kk = k4 + j;
@@ -211,9 +215,33 @@ __global__ void __launch_bounds__(256) fwd_bias_prep_kernel(
       }
       v[j] = x;
     }
-    *reinterpret_cast<float4*>(biasp + row * Nk + k4) = make_float4(v[0], v[1], v[2], v[3]);
+    st4f(biasp + row * Nk + k4, v);   // exact: x is a value of type T or -inf
   }
 }
+
+#define EVO_FWD_QK()                                                             \
+  do {                                                                           \
+    for (int rr = 0; rr < ROWS; ++rr)                                            \
+      for (int half = 0; half < 2; ++half)                                       \
+        for (int kb = 0; kb < 2; ++kb) {                                         \
+          const Op kf = ld8(sK[buf][rr] + (half * 32 + kb * 16 + l16) * KST + 8 * g); \
+          for (int qb = 0; qb < 2; ++qb)                                         \
+            s[rr][qb][half][kb] = mma32(kf, qf[rr][qb], bt[qb][half][kb]);       \
+        }                                                                        \
+    if constexpr (ROW_MASK) {                                                    \
+      for (int rr = 0; rr < ROWS; ++rr)                                          \
+        for (int half = 0; half < 2; ++half) {                                   \
+          const int kbase = k0 + half * 32 + 8 * g;                              \
+          for (int j = 0; j < 8; ++j) {                                          \
+            const bool dead = kbase + j < N && mrow[rr][kbase + j] == 0;         \
+            if (dead) {                                                          \
+              s[rr][0][half][j >> 2][j & 3] = -INFINITY;                         \
+              s[rr][1][half][j >> 2][j & 3] = -INFINITY;                         \
+            }                                                                    \
+          }                                                                      \
+        }                                                                        \
+    }                                                                            \
+  } while (0)
 
 template <typename T, int ROWS, bool ROW_MASK, bool HAS_BIAS>
 __global__ void __launch_bounds__(256)
@@ -281,11 +309,12 @@ attn_fwd_kernel(FwdParams p) {
   }
 
   // Bias rows of this wave's queries: lane reads keys k0 + half*32 + 8g..+7.
-  const float* brow[2];
+  const T* brow[2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int q = qw0 + qb * 16 + l16;
-    brow[qb] = HAS_BIAS ? p.biasp + (((int64_t)b * H + h) * p.Nq + q) * p.Nk + 8 * g
+    brow[qb] = HAS_BIAS ? static_cast<const T*>(p.biasp) +
+                              (((int64_t)b * H + h) * p.Nq + q) * p.Nk + 8 * g
                         : nullptr;
   }
   const uint8_t* mrow[ROWS];
@@ -296,22 +325,22 @@ attn_fwd_kernel(FwdParams p) {
   }
 
   KVRaw<T> raw[ROWS];
-  f32x4 bnext[2][2][2];  // [qb][half][kb]
+  f32x4 bt[2][2][2];  // bias tile in accumulator layout: [qb][half][kb]
   auto fetch_bias = [&](int k0) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         if constexpr (HAS_BIAS) {
-          bnext[qb][half][0] = ldf4(brow[qb] + k0 + half * 32);
-          bnext[qb][half][1] = ldf4(brow[qb] + k0 + half * 32 + 4);
+          bt[qb][half][0] = ld4f(brow[qb] + k0 + half * 32);
+          bt[qb][half][1] = ld4f(brow[qb] + k0 + half * 32 + 4);
         } else {
           // no bias and no shared mask: 0, padding keys -inf
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-              bnext[qb][half][kb][i] =
+              bt[qb][half][kb][i] =
                   (k0 + half * 32 + 8 * g + 4 * kb + i < N) ? 0.f : -INFINITY;
         }
       }
@@ -326,54 +355,24 @@ attn_fwd_kernel(FwdParams p) {
     const int buf = tile & 1;
 #pragma unroll
     for (int rr = 0; rr < ROWS; ++rr) store_kv<T>(raw[rr], sK[buf][rr], sV[buf][rr]);
-    f32x4 bt[2][2][2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int half = 0; half < 2; ++half)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) bt[qb][half][kb] = bnext[qb][half][kb];
     __syncthreads();
     if (tile + 1 < ntiles) {
 #pragma unroll
       for (int rr = 0; rr < ROWS; ++rr)
         fetch_kv<T>(raw[rr], kline[rr], vline[rr], k0 + BK, N, pos_stride);
-      fetch_bias(k0 + BK);
     }
 
-#pragma unroll
-    for (int rr = 0; rr < ROWS; ++rr) {
-      const T* kt = sK[buf][rr];
-      const T* vt = sV[buf][rr];
-      f32x4 s[2][2][2];  // [qb][half][kb] natural-unit logits
-#pragma unroll
-      for (int half = 0; half < 2; ++half)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const Op kf = ld8(kt + (half * 32 + kb * 16 + l16) * KST + 8 * g);
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-            s[qb][half][kb] = mma32(kf, qf[rr][qb], bt[qb][half][kb]);
-        }
-      if constexpr (ROW_MASK) {
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int kbase = k0 + half * 32 + 8 * g;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const bool dead = kbase + j < N && mrow[rr][kbase + j] == 0;
-            if (dead) {
-              s[0][half][j >> 2][j & 3] = -INFINITY;
-              s[1][half][j >> 2][j & 3] = -INFINITY;
-            }
-          }
-        }
-      }
+    // All lines of the group go through each phase together (one basic
+    // block per phase), so the matrix-core work of one line overlaps the
+    // softmax of the other.
+    f32x4 s[ROWS][2][2][2];  // [rr][qb][half][kb]: logits, then p in place
+    EVO_FWD_QK();
 
-      // Fast path: p = exp2(s*log2e - m) with the current reference.
-      f32x4 pv[2][2][2];
-      float psum[2];
-      bool redo = false;
+    // Fast path: p = exp2(s*log2e - m) with the current reference.
+    float psum[ROWS][2];
+    bool redo = false;
+#pragma unroll
+    for (int rr = 0; rr < ROWS; ++rr)
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         const float nm = -m[rr][qb];
@@ -384,16 +383,20 @@ attn_fwd_kernel(FwdParams p) {
           for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const float e = exp2_fast(__builtin_fmaf(s[qb][half][kb][i], kLog2e, nm));
-              pv[qb][half][kb][i] = e;
+              const float e = exp2_fast(__builtin_fmaf(s[rr][qb][half][kb][i], kLog2e, nm));
+              s[rr][qb][half][kb][i] = e;
               acc += e;
             }
-        psum[qb] = acc;
+        psum[rr][qb] = acc;
         // not yet anchored (m = -inf gives e = inf or NaN), or too large
         redo |= !(acc <= kHeadroom);
       }
-      if (__builtin_amdgcn_ballot_w64(redo) != 0) {
-        // Slow path: raise the reference to the tile maximum where needed.
+    if (__builtin_amdgcn_ballot_w64(redo) != 0) {
+      // Slow path: recompute the logits and raise the reference to the tile
+      // maximum where needed.
+      EVO_FWD_QK();
+#pragma unroll
+      for (int rr = 0; rr < ROWS; ++rr)
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
           float mx = -INFINITY;
@@ -402,7 +405,7 @@ attn_fwd_kernel(FwdParams p) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-              for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[qb][half][kb][i]);
+              for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[rr][qb][half][kb][i]);
           mx = fmaxf(mx, shfl_xor(mx, 16));
           mx = fmaxf(mx, shfl_xor(mx, 32));
           const float mold = m[rr][qb];
@@ -420,31 +423,36 @@ attn_fwd_kernel(FwdParams p) {
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
-                const float e = exp2_fast(__builtin_fmaf(s[qb][half][kb][i], kLog2e, -muse));
-                pv[qb][half][kb][i] = e;
+                const float e = exp2_fast(__builtin_fmaf(s[rr][qb][half][kb][i], kLog2e, -muse));
+                s[rr][qb][half][kb][i] = e;
                 acc += e;
               }
-          psum[qb] = acc;
+          psum[rr][qb] = acc;
         }
-      }
+    }
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) l[rr][qb] += psum[qb];
+    for (int rr = 0; rr < ROWS; ++rr)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) l[rr][qb] += psum[rr][qb];
 
+#pragma unroll
+    for (int rr = 0; rr < ROWS; ++rr)
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         Op vf[2];
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb)
-          vf[cb] = ld8(vt + (cb * 16 + l16) * VST + half * 32 + 8 * g);
+          vf[cb] = ld8(sV[buf][rr] + (cb * 16 + l16) * VST + half * 32 + 8 * g);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-          const Op pf = pack8(pv[qb][half][0], pv[qb][half][1], (Op*)nullptr);
+          const Op pf = pack8(s[rr][qb][half][0], s[rr][qb][half][1], (Op*)nullptr);
 #pragma unroll
           for (int cb = 0; cb < 2; ++cb)
             o[rr][qb][cb] = mma32(vf[cb], pf, o[rr][qb][cb]);
         }
       }
-    }
+    // next tile's bias operands (the logit registers are free again)
+    if (tile + 1 < ntiles) fetch_bias(k0 + BK);
   }
 
   // Epilogue: normalise, gate, store; LSE in natural log.
@@ -499,8 +507,8 @@ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 }  // namespace
 
-size_t attn_fwd_workspace(int64_t B, int64_t N, int64_t H) {
-  return (size_t)(B * H * round_up(N, BQ) * round_up(N, BK) * 4);
+size_t attn_fwd_workspace(int dtype, int64_t B, int64_t N, int64_t H) {
+  return (size_t)(B * H * round_up(N, BQ) * round_up(N, BK) * (dtype == 1 ? 2 : 4));
 }
 
 hipError_t launch_attn_fwd(const AttnFwdArgs& a, hipStream_t s) {
@@ -517,17 +525,17 @@ hipError_t launch_attn_fwd(const AttnFwdArgs& a, hipStream_t s) {
   p.mask = row_mask ? a.mask : nullptr;
   p.biasp = nullptr;
   if (a.bias || shared_mask) {
-    float* bp = static_cast<float*>(a.workspace);
+    void* bp = a.workspace;
     const int64_t work = a.B * a.H * p.Nq * (p.Nk / 4);
     const int grid = (int)std::min<int64_t>((work + 255) / 256, 8192);
     if (a.dtype == 1)
       hipLaunchKernelGGL(fwd_bias_prep_kernel<bf16_t>, dim3(grid), dim3(256), 0, s,
-                         static_cast<const bf16_t*>(a.bias), a.mask, (int)shared_mask, bp,
-                         p.B, p.H, p.N, p.Nq, p.Nk);
+                         static_cast<const bf16_t*>(a.bias), a.mask, (int)shared_mask,
+                         static_cast<bf16_t*>(bp), p.B, p.H, p.N, p.Nq, p.Nk);
     else
       hipLaunchKernelGGL(fwd_bias_prep_kernel<float>, dim3(grid), dim3(256), 0, s,
-                         static_cast<const float*>(a.bias), a.mask, (int)shared_mask, bp,
-                         p.B, p.H, p.N, p.Nq, p.Nk);
+                         static_cast<const float*>(a.bias), a.mask, (int)shared_mask,
+                         static_cast<float*>(bp), p.B, p.H, p.N, p.Nq, p.Nk);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     p.biasp = bp;

@@ -132,7 +132,7 @@ evo_status_t evo_attn_fwd(evo_dtype_t dtype, int64_t B, int64_t R, int64_t N,
     OPTIONAL_PTR(key_mask);
     if ((st = check_mask(key_mask, mask_rows, R)) != EVO_OK) return st;
     if (bias || key_mask) {
-      const size_t need = evo::attn_fwd_workspace(B, N, H);
+      const size_t need = evo::attn_fwd_workspace((int)dtype, B, N, H);
       if (!workspace || workspace_bytes < need)
         return fail(EVO_EWORKSPACE, "workspace of %zu bytes needed, %zu given",
                     need, workspace ? workspace_bytes : (size_t)0);
@@ -155,7 +155,7 @@ size_t evo_attn_fwd_workspace_bytes(evo_dtype_t dtype, int64_t B, int64_t R,
   const evo_status_t st = check_core_sizes(dtype, B, R, N, H, C);
   g_last_error = saved;
   if (st != EVO_OK) return 0;
-  return evo::attn_fwd_workspace(B, N, H);
+  return evo::attn_fwd_workspace((int)dtype, B, N, H);
 }
 
 size_t evo_attn_bwd_workspace_bytes(evo_dtype_t dtype, int64_t B, int64_t R,
@@ -303,7 +303,7 @@ size_t tri_attn_workspace_bytes(evo_dtype_t dtype, int64_t N, int64_t CZ,
   const size_t es = elem_size(dtype);
   const size_t t = align256((size_t)N * N * H * C * es);
   const size_t b = align256((size_t)H * N * N * es);
-  return 5 * t + b + align256(evo::attn_fwd_workspace(1, N, H));
+  return 5 * t + b + align256(evo::attn_fwd_workspace((int)dtype, 1, N, H));
 }
 
 evo_status_t tri_attn_module_fwd(evo_dtype_t dtype, int64_t N, int64_t CZ,

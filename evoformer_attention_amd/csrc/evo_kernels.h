@@ -77,7 +77,7 @@ struct OutProjectArgs {
 
 constexpr int kHeadDim = 32;
 
-size_t attn_fwd_workspace(int64_t B, int64_t N, int64_t H);
+size_t attn_fwd_workspace(int dtype, int64_t B, int64_t N, int64_t H);
 hipError_t launch_attn_fwd(const AttnFwdArgs& a, hipStream_t s);
 size_t attn_bwd_workspace(int dtype, int64_t B, int64_t R, int64_t N,
                           int64_t H);

@@ -97,7 +97,8 @@ def test_last_error_is_thread_local():
 
 
 def test_workspace_queries():
-    assert L.evo_attn_fwd_workspace_bytes(1, 1, 768, 768, 4, 32) == 4 * 768 * 768 * 4
+    assert L.evo_attn_fwd_workspace_bytes(1, 1, 768, 768, 4, 32) == 4 * 768 * 768 * 2
+    assert L.evo_attn_fwd_workspace_bytes(0, 1, 768, 768, 4, 32) == 4 * 768 * 768 * 4
     assert L.evo_attn_fwd_workspace_bytes(1, 1, 2, 8, 2, 16) == 0
     n = L.evo_attn_bwd_workspace_bytes(1, 1, 512, 512, 4, 32)
     assert n > 4 * 512 * 512 * 128 * 2  # the transposed slabs alone
