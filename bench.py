@@ -13,7 +13,8 @@ forward and 2.5x that for the backward (L = rows * heads * N^2 logits); the
 projections' time is inside the step but their flops are not counted.
 
 Prints one JSON line.  Options: --steps K --warmup W --gpus 1
---workload NAME --no-cpu-baseline.
+--workload NAME --no-cpu-baseline --cpu-lines L --calibrate-copy
+--write-traffic FETCH_CSV WRITE_CSV.
 """
 import argparse
 import hashlib
@@ -35,9 +36,24 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="tri_end_768", choices=WORKLOADS_BENCH)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-lines", type=int, default=24,
+    ap.add_argument("--cpu-lines", type=int, default=192,
                     help="attention lines in the oracle's timed sample")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after the timed steps, run a plain elementwise copy "
+                         "of COPY_BYTES (read) + COPY_BYTES (write), for scaling "
+                         "the FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU work: turn two rocprofv3 --pmc counter files "
+                         "(FETCH_SIZE run, WRITE_SIZE run) of a --calibrate-copy "
+                         "bench into profiles/traffic.json")
     return ap.parse_args()
+
+
+COPY_BYTES = 1 << 29          # 512 MiB read and 512 MiB written by the copy
+TRAFFIC_KERNELS = {"attn_fwd": "attn_fwd_kernel", "bwd_dkdv": "bwd_dkdv_kernel",
+                   "bwd_dq": "bwd_dq_kernel", "bwd_dbias": "bwd_dbias_kernel",
+                   "rowgemm": "rowgemm_kernel", "bwd_prep": "bwd_prep_kernel"}
+COPY_KERNEL = "neg_kernel"    # torch.neg(out=): a plain streaming copy
 
 
 def kernel_sources_digest():
@@ -65,6 +81,65 @@ def stored_traffic(kernel, workload):
     if not ent or ent.get("sources_digest") != kernel_sources_digest():
         return None
     return ent.get("bytes_per_launch")
+
+
+def _counter_means(path, counter):
+    """Mean counter value per dispatch, by kernel short name."""
+    import csv
+    sums = {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] != counter:
+                continue
+            name = row["Kernel_Name"]
+            for short, pat in list(TRAFFIC_KERNELS.items()) + [("copy", COPY_KERNEL)]:
+                if pat in name:
+                    break
+            else:
+                continue
+            key = (short, row["Dispatch_Id"])
+            sums[key] = sums.get(key, 0.0) + float(row["Counter_Value"])
+    per = {}
+    for (short, _), v in sums.items():
+        per.setdefault(short, []).append(v)
+    return {k: sum(v) / len(v) for k, v in per.items()}
+
+
+def write_traffic(fetch_csv, write_csv, workload):
+    """profiles/traffic.json from the two counter runs.  Each counter (KiB
+    per dispatch) is scaled by known bytes / counter bytes of the copy kernel
+    measured in the same run."""
+    fetch = _counter_means(fetch_csv, "FETCH_SIZE")
+    write = _counter_means(write_csv, "WRITE_SIZE")
+    if "copy" not in fetch or "copy" not in write:
+        raise SystemExit("no copy-calibration dispatch in the counter files "
+                         "(run the bench with --calibrate-copy)")
+    f_scale = COPY_BYTES / (fetch["copy"] * 1024.0)
+    w_scale = COPY_BYTES / (write["copy"] * 1024.0)
+    out = {"_method": ("FETCH_SIZE and WRITE_SIZE (KiB per dispatch, mean over "
+                       "dispatches) from two rocprofv3 --pmc runs of "
+                       "'bench.py --steps 2 --warmup 1 --no-cpu-baseline "
+                       "--calibrate-copy'; each scaled by the factor that maps "
+                       "the same counter of a plain %d-byte elementwise copy to "
+                       "its known size" % COPY_BYTES),
+           "copy_calibration": {"fetch_kib": fetch["copy"], "write_kib": write["copy"],
+                                "known_bytes": COPY_BYTES,
+                                "fetch_scale": f_scale, "write_scale": w_scale}}
+    ent = {}
+    digest = kernel_sources_digest()
+    for short in TRAFFIC_KERNELS:
+        if short in fetch and short in write:
+            fb = fetch[short] * 1024.0 * f_scale
+            wb = write[short] * 1024.0 * w_scale
+            ent[short] = {"fetch_kib": fetch[short], "write_kib": write[short],
+                          "fetch_bytes": fb, "write_bytes": wb,
+                          "bytes_per_launch": fb + wb, "sources_digest": digest}
+    out[workload] = ent
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
 
 
 def cpu_baseline(d, w, n_lines):
@@ -115,10 +190,13 @@ def cpu_baseline(d, w, n_lines):
 
 def main():
     a = parse()
+    if a.write_traffic:
+        write_traffic(a.write_traffic[0], a.write_traffic[1], a.workload)
+        return
     if a.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {a.gpus}); the "
-              "multi-GPU sharding of this path is described in DESIGN.md but "
-              "not built.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (got --gpus {a.gpus}): this "
+              "library has no multi-GPU path (no sharding, no collectives).",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -184,6 +262,13 @@ def main():
         for j, name in enumerate(parts):
             parts[name] += e[j].elapsed_time(e[j + 1]) / a.steps
     peak_mem = torch.cuda.max_memory_allocated()
+    if a.calibrate_copy:
+        src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     R = N
     fwd_fl = M.fwd_flops(1, R, N, H, C)
