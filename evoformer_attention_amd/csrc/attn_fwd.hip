@@ -251,14 +251,19 @@ attn_fwd_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(16))) T sK[2][ROWS][BK * KST];
   __shared__ __attribute__((aligned(16))) T sV[2][ROWS][C * VST];
 
+  // Work order (fastest first): query tile, head within a head pair, row
+  // group, head pair, batch.  The heads of a position are interleaved at
+  // 64-byte granularity, so heads 2j and 2j+1 share every 128-byte line of
+  // Q, K, V and G: running them back to back on one XCD lets the second
+  // find the lines in L2 instead of fetching them again from HBM.
   const int w = xcd_work_index(p.total);
   if (w < 0) return;
   const int qt = w % p.n_qt;
   int t = w / p.n_qt;
-  const int rg = t % p.n_rg;
-  t /= p.n_rg;
-  const int h = t % p.H;
-  const int b = t / p.H;
+  const int h = 2 * ((t >> 1) / p.n_rg % ((p.H + 1) >> 1)) + (t & 1);
+  const int rg = (t >> 1) % p.n_rg;
+  const int b = (t >> 1) / p.n_rg / ((p.H + 1) >> 1);
+  if (h >= p.H) return;  // odd H: the missing partner of the last pair
 
   const int N = p.N, H = p.H, R = p.R;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -368,33 +373,42 @@ attn_fwd_kernel(FwdParams p) {
     f32x4 s[ROWS][2][2][2];  // [rr][qb][half][kb]: logits, then p in place
     EVO_FWD_QK();
 
-    // Fast path: p = exp2(s*log2e - m) with the current reference.
+    // p = exp2(s*log2e - m), rounded to the operand type at once: P^T is
+    // kept as matrix-core operands (half the registers of fp32 logits) and
+    // the row sums are taken over exactly the rounded values the PV product
+    // uses.  Fast path: the current reference.  The first tile always takes
+    // the exact maximum.
+    Op pf[ROWS][2][2];  // [rr][qb][half]
     float psum[ROWS][2];
-    bool redo = false;
+    bool slow = tile == 0;
+    if (!slow) {
+      bool redo = false;
 #pragma unroll
-    for (int rr = 0; rr < ROWS; ++rr)
+      for (int rr = 0; rr < ROWS; ++rr)
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const float nm = -m[rr][qb];
-        float acc = 0.f;
+        for (int qb = 0; qb < 2; ++qb) {
+          const float nm = -m[rr][qb];
+          float acc = 0.f;
 #pragma unroll
-        for (int half = 0; half < 2; ++half)
+          for (int half = 0; half < 2; ++half) {
+            f32x4 e[2];
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float e = exp2_fast(__builtin_fmaf(s[rr][qb][half][kb][i], kLog2e, nm));
-              s[rr][qb][half][kb][i] = e;
-              acc += e;
-            }
-        psum[rr][qb] = acc;
-        // not yet anchored (m = -inf gives e = inf or NaN), or too large
-        redo |= !(acc <= kHeadroom);
-      }
-    if (__builtin_amdgcn_ballot_w64(redo) != 0) {
-      // Slow path: recompute the logits and raise the reference to the tile
-      // maximum where needed.
-      EVO_FWD_QK();
+              for (int i = 0; i < 4; ++i)
+                e[kb][i] = exp2_fast(__builtin_fmaf(s[rr][qb][half][kb][i], kLog2e, nm));
+            pf[rr][qb][half] = pack8(e[0], e[1], (Op*)nullptr);
+            acc = sum8(pf[rr][qb][half], acc);
+          }
+          psum[rr][qb] = acc;
+          // not yet anchored (m = -inf gives inf or NaN), or too large
+          redo |= !(acc <= kHeadroom);
+        }
+      slow = __builtin_amdgcn_ballot_w64(redo) != 0;
+      if (slow) EVO_FWD_QK();  // the logits again, for the exact path
+    }
+    if (slow) {
+      // Raise the reference to the tile maximum where needed.
 #pragma unroll
       for (int rr = 0; rr < ROWS; ++rr)
 #pragma unroll
@@ -418,15 +432,16 @@ attn_fwd_kernel(FwdParams p) {
           for (int cb = 0; cb < 2; ++cb) o[rr][qb][cb] *= alpha;
           float acc = 0.f;
 #pragma unroll
-          for (int half = 0; half < 2; ++half)
+          for (int half = 0; half < 2; ++half) {
+            f32x4 e[2];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const float e = exp2_fast(__builtin_fmaf(s[rr][qb][half][kb][i], kLog2e, -muse));
-                s[rr][qb][half][kb][i] = e;
-                acc += e;
-              }
+              for (int i = 0; i < 4; ++i)
+                e[kb][i] = exp2_fast(__builtin_fmaf(s[rr][qb][half][kb][i], kLog2e, -muse));
+            pf[rr][qb][half] = pack8(e[0], e[1], (Op*)nullptr);
+            acc = sum8(pf[rr][qb][half], acc);
+          }
           psum[rr][qb] = acc;
         }
     }
@@ -444,12 +459,10 @@ attn_fwd_kernel(FwdParams p) {
         for (int cb = 0; cb < 2; ++cb)
           vf[cb] = ld8(sV[buf][rr] + (cb * 16 + l16) * VST + half * 32 + 8 * g);
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          const Op pf = pack8(s[rr][qb][half][0], s[rr][qb][half][1], (Op*)nullptr);
+        for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
           for (int cb = 0; cb < 2; ++cb)
-            o[rr][qb][cb] = mma32(vf[cb], pf, o[rr][qb][cb]);
-        }
+            o[rr][qb][cb] = mma32(vf[cb], pf[rr][qb][half], o[rr][qb][cb]);
       }
     // next tile's bias operands (the logit registers are free again)
     if (tile + 1 < ntiles) fetch_bias(k0 + BK);
@@ -544,7 +557,7 @@ hipError_t launch_attn_fwd(const AttnFwdArgs& a, hipStream_t s) {
   const int rows = (a.dtype == 1 && a.R > 1) ? 2 : 1;
   p.n_qt = (int)((a.N + BQ - 1) / BQ);
   p.n_rg = (int)((a.R + rows - 1) / rows);
-  const int64_t total = a.B * a.H * (int64_t)p.n_rg * p.n_qt;
+  const int64_t total = a.B * ((a.H + 1) / 2) * 2 * (int64_t)p.n_rg * p.n_qt;
   if (total > (int64_t)INT32_MAX - 8) return hipErrorInvalidValue;
   p.total = (int)total;
   if (a.dtype == 1) {

@@ -88,6 +88,24 @@ __device__ __forceinline__ f32x8 pack8(const f32x4& a, const f32x4& b,
   return r;
 }
 
+// acc + the sum of the 8 values of a fragment (bf16: v_dot2 with ones,
+// fp32 accumulate; exact products, so only the additions round).
+__device__ __forceinline__ float sum8(const bf16x8& v, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const bf16x2 pr = {v[2 * j], v[2 * j + 1]};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(pr, one, acc, false);
+  }
+  return acc;
+}
+__device__ __forceinline__ float sum8(const f32x8& v, float acc) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc += v[j];
+  return acc;
+}
+
 // Scale every element of a fragment (in fp32, rounded back to the type).
 __device__ __forceinline__ bf16x8 scale8(const bf16x8& v, float s) {
   bf16x8 r;
