@@ -91,10 +91,18 @@ __device__ __forceinline__ int k_lds_row(int p) {
   return half * 32 + kb * 16 + gg * 4 + i;
 }
 
+// Column of key chunk c (a multiple of 8) in row `row` of the transposed V
+// tile.  bf16 tiles are swizzled by 16 * (row / 8 mod 4) (see store_kv);
+// fp32 tiles are stored plainly.
+template <typename T>
+__device__ __forceinline__ int v_col_t(int row, int c) {
+  return sizeof(T) == 2 ? (c ^ (16 * ((row >> 3) & 3))) : c;
+}
+
 // ---- raw tile data one thread fetches for one line: 8 K elements of one
 // key and 4 V elements of two keys.
 template <typename T> struct KVRaw;
-template <> struct KVRaw<bf16_t> { uint4 k; uint2 va, vb; };
+template <> struct KVRaw<bf16_t> { uint4 k, v; };
 template <> struct KVRaw<float> { uint4 k0, k1; float4 va, vb; };
 
 template <typename T>
@@ -106,12 +114,12 @@ __device__ __forceinline__ void fetch_kv(KVRaw<T>& raw, const T* kline,
   const int p = t & 31, vc = t >> 5;              // V: key pair, 4-dim chunk
   const int ka = k0 + 2 * p, kb = ka + 1;
   if constexpr (sizeof(T) == 2) {
-    raw.k = kk < N ? *reinterpret_cast<const uint4*>(kline + (int64_t)kk * pos_stride + ch * 8)
-                   : make_uint4(0, 0, 0, 0);
-    raw.va = ka < N ? *reinterpret_cast<const uint2*>(vline + (int64_t)ka * pos_stride + vc * 4)
-                    : make_uint2(0, 0);
-    raw.vb = kb < N ? *reinterpret_cast<const uint2*>(vline + (int64_t)kb * pos_stride + vc * 4)
-                    : make_uint2(0, 0);
+    // K and V alike: one 16-byte chunk (8 dims of one key) per thread, so a
+    // wave's load touches 16 keys x 64 bytes.
+    (void)ka; (void)kb; (void)vc;
+    const int64_t off = (int64_t)kk * pos_stride + ch * 8;
+    raw.k = kk < N ? *reinterpret_cast<const uint4*>(kline + off) : make_uint4(0, 0, 0, 0);
+    raw.v = kk < N ? *reinterpret_cast<const uint4*>(vline + off) : make_uint4(0, 0, 0, 0);
   } else {
     if (kk < N) {
       const uint4* s = reinterpret_cast<const uint4*>(kline + (int64_t)kk * pos_stride + ch * 8);
@@ -136,14 +144,20 @@ __device__ __forceinline__ void store_kv(const KVRaw<T>& raw, T* sK, T* sV) {
   const int kk = t >> 2, ch = t & 3;
   const int p = t & 31, vc = t >> 5;
   if constexpr (sizeof(T) == 2) {
+    (void)p; (void)vc;
     *reinterpret_cast<uint4*>(sK + k_lds_row(kk) * KST + ch * 8) = raw.k;
-    uint32_t* d = reinterpret_cast<uint32_t*>(sV);
-    const int base = ((vc * 4) * VST + 2 * p) >> 1;
-    const int rs = VST >> 1;
-    d[base + 0 * rs] = (raw.va.x & 0xffffu) | (raw.vb.x << 16);
-    d[base + 1 * rs] = (raw.va.x >> 16) | (raw.vb.x & 0xffff0000u);
-    d[base + 2 * rs] = (raw.va.y & 0xffffu) | (raw.vb.y << 16);
-    d[base + 3 * rs] = (raw.va.y >> 16) | (raw.vb.y & 0xffff0000u);
+    // V transposed: dim 8*ch + j of key kk goes to row 8*ch + j, column
+    // kk ^ (16*ch) (16-bit stores of the low and high halves of each loaded
+    // dword).  The swizzle spreads the four dim groups of a key over
+    // different banks; it moves whole 8-key chunks, so a lane's 8 keys stay
+    // one 16-byte read (v_col_t).
+    uint16_t* d = reinterpret_cast<uint16_t*>(sV) + (ch * 8) * VST + (kk ^ (16 * ch));
+    const uint32_t w[4] = {raw.v.x, raw.v.y, raw.v.z, raw.v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      d[(2 * j) * VST] = (uint16_t)(w[j] & 0xffffu);
+      d[(2 * j + 1) * VST] = (uint16_t)(w[j] >> 16);
+    }
   } else {
     uint4* dk = reinterpret_cast<uint4*>(sK + k_lds_row(kk) * KST + ch * 8);
     dk[0] = raw.k0;
@@ -190,32 +204,47 @@ __device__ __forceinline__ void st4f(float* p, const f32x4& v) {
   *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
 }
 
-// Bias prep: biasp[b,h,q,k] = bias (natural units) or 0, -inf for keys
-// masked by a shared mask or beyond N; q < Nq, k < Nk.
+// Bias prep.  The prepared bias holds, for every (b, h, query q < Nq, key
+// k < Nk), the bias in natural units (0 without a bias), or -inf for keys
+// masked by a shared mask or beyond N.  It is stored in the order the main
+// kernel reads it, so that each wave's bias load is one contiguous 1 KB
+// block: per (b, h) a grid of [Nq/128][Nk/64] tiles, each tile
+// [wave 4][qb 2][half 2][lane 64][8 keys], where lane (l16, g) of wave w
+// holds query 128*qt + 32*w + 16*qb + l16 and keys 64*kt + 32*half + 8*g
+// .. +7 (the accumulator-operand layout of the logit tile).
 template <typename T>
 __global__ void __launch_bounds__(256) fwd_bias_prep_kernel(
     const T* bias, const uint8_t* mask, int shared_mask, T* biasp, int B,
     int H, int N, int Nq, int Nk) {
-  const int64_t total = (int64_t)B * H * Nq * (Nk / 4);
+  const int nqt = Nq / BQ, nkt = Nk / BK;
+  const int64_t total = (int64_t)B * H * Nq * (Nk / 8);
   for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total;
        e += (int64_t)gridDim.x * 256) {
-    const int k4 = (int)(e % (Nk / 4)) * 4;
-    const int64_t row = e / (Nk / 4);       // (b*H + h)*Nq + q
-    const int q = (int)(row % Nq);
-    const int64_t bh = row / Nq;
+    const int lane = (int)(e & 63);
+    int64_t t = e >> 6;
+    const int half = (int)(t & 1); t >>= 1;
+    const int qb = (int)(t & 1); t >>= 1;
+    const int wv = (int)(t & 3); t >>= 2;
+    const int kt = (int)(t % nkt); t /= nkt;
+    const int qt = (int)(t % nqt);
+    const int64_t bh = t / nqt;
     const int b = (int)(bh / H);
-    f32x4 v;
+    const int q = qt * BQ + wv * BQW + qb * 16 + (lane & 15);
+    const int k0 = kt * BK + half * 32 + 8 * (lane >> 4);
+    f32x4 v[2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int kk = k4 + j;
+    for (int j = 0; j < 8; ++j) {
+      const int kk = k0 + j;
       float x = -INFINITY;
       if (kk < N) {
         x = (bias && q < N) ? Tr<T>::to_f(bias[(bh * N + q) * N + kk]) : 0.f;
         if (shared_mask && mask[(int64_t)b * N + kk] == 0) x = -INFINITY;
       }
-      v[j] = x;
+      v[j >> 2][j & 3] = x;
     }
-    st4f(biasp + row * Nk + k4, v);   // exact: x is a value of type T or -inf
+    // exact: every x is a value of type T, 0 or -inf
+    st4f(biasp + e * 8, v[0]);
+    st4f(biasp + e * 8 + 4, v[1]);
   }
 }
 
@@ -313,15 +342,13 @@ attn_fwd_kernel(FwdParams p) {
     }
   }
 
-  // Bias rows of this wave's queries: lane reads keys k0 + half*32 + 8g..+7.
-  const T* brow[2];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int q = qw0 + qb * 16 + l16;
-    brow[qb] = HAS_BIAS ? static_cast<const T*>(p.biasp) +
-                              (((int64_t)b * H + h) * p.Nq + q) * p.Nk + 8 * g
-                        : nullptr;
-  }
+  // This lane's 8 bias values of (qb, half) in key tile `tile` sit at
+  // bbase + tile * BQ*BK + (qb*2 + half) * 512 (prepared tile order).
+  const T* bbase = HAS_BIAS ? static_cast<const T*>(p.biasp) +
+                                  ((((int64_t)b * H + h) * (p.Nq / BQ) + qt) *
+                                       (p.Nk / BK) * (BQ * BK) +
+                                   wave * 2048 + lane * 8)
+                            : nullptr;
   const uint8_t* mrow[ROWS];
   if constexpr (ROW_MASK) {
 #pragma unroll
@@ -337,8 +364,9 @@ attn_fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         if constexpr (HAS_BIAS) {
-          bt[qb][half][0] = ld4f(brow[qb] + k0 + half * 32);
-          bt[qb][half][1] = ld4f(brow[qb] + k0 + half * 32 + 4);
+          const T* src = bbase + (int64_t)(k0 / BK) * (BQ * BK) + (qb * 2 + half) * 512;
+          bt[qb][half][0] = ld4f(src);
+          bt[qb][half][1] = ld4f(src + 4);
         } else {
           // no bias and no shared mask: 0, padding keys -inf
 #pragma unroll
@@ -457,7 +485,7 @@ attn_fwd_kernel(FwdParams p) {
         Op vf[2];
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb)
-          vf[cb] = ld8(sV[buf][rr] + (cb * 16 + l16) * VST + half * 32 + 8 * g);
+          vf[cb] = ld8(sV[buf][rr] + (cb * 16 + l16) * VST + v_col_t<T>(cb * 16 + l16, half * 32 + 8 * g));
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
@@ -539,7 +567,7 @@ hipError_t launch_attn_fwd(const AttnFwdArgs& a, hipStream_t s) {
   p.biasp = nullptr;
   if (a.bias || shared_mask) {
     void* bp = a.workspace;
-    const int64_t work = a.B * a.H * p.Nq * (p.Nk / 4);
+    const int64_t work = a.B * a.H * p.Nq * (p.Nk / 8);
     const int grid = (int)std::min<int64_t>((work + 255) / 256, 8192);
     if (a.dtype == 1)
       hipLaunchKernelGGL(fwd_bias_prep_kernel<bf16_t>, dim3(grid), dim3(256), 0, s,
