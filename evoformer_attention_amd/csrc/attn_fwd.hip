@@ -101,38 +101,39 @@ __device__ __forceinline__ int v_col_t(int row, int c) {
 
 // ---- raw tile data one thread fetches for one line: 8 K elements of one
 // key and 4 V elements of two keys.
+// (native vector types: HIP's uint4 struct is copied as an aggregate, which
+// can leave the tile in scratch memory)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 template <typename T> struct KVRaw;
-template <> struct KVRaw<bf16_t> { uint4 k, v; };
-template <> struct KVRaw<float> { uint4 k0, k1; float4 va, vb; };
+template <> struct KVRaw<bf16_t> { u32x4 k, v; };
+template <> struct KVRaw<float> { u32x4 k0, k1, va, vb; };
 
+// Keys at or beyond N have -inf logits on every path (the bias operand
+// carries -inf for padding keys), so K and V there only need to be finite:
+// bf16 loads zeros, fp32 reads key N-1 again (a clamped address instead of a
+// guarded load, which the compiler would route through scratch memory).
 template <typename T>
 __device__ __forceinline__ void fetch_kv(KVRaw<T>& raw, const T* kline,
                                          const T* vline, int k0, int N,
                                          int pos_stride) {
   const int t = threadIdx.x;
-  const int kk = k0 + (t >> 2), ch = t & 3;       // K: key, 8-dim chunk
-  const int p = t & 31, vc = t >> 5;              // V: key pair, 4-dim chunk
-  const int ka = k0 + 2 * p, kb = ka + 1;
+  const int ch = t & 3;
   if constexpr (sizeof(T) == 2) {
     // K and V alike: one 16-byte chunk (8 dims of one key) per thread, so a
     // wave's load touches 16 keys x 64 bytes.
-    (void)ka; (void)kb; (void)vc;
+    const int kk = k0 + (t >> 2);
     const int64_t off = (int64_t)kk * pos_stride + ch * 8;
-    raw.k = kk < N ? *reinterpret_cast<const uint4*>(kline + off) : make_uint4(0, 0, 0, 0);
-    raw.v = kk < N ? *reinterpret_cast<const uint4*>(vline + off) : make_uint4(0, 0, 0, 0);
+    raw.k = kk < N ? *reinterpret_cast<const u32x4*>(kline + off) : u32x4{0, 0, 0, 0};
+    raw.v = kk < N ? *reinterpret_cast<const u32x4*>(vline + off) : u32x4{0, 0, 0, 0};
   } else {
-    if (kk < N) {
-      const uint4* s = reinterpret_cast<const uint4*>(kline + (int64_t)kk * pos_stride + ch * 8);
-      raw.k0 = s[0];
-      raw.k1 = s[1];
-    } else {
-      raw.k0 = make_uint4(0, 0, 0, 0);
-      raw.k1 = raw.k0;
-    }
-    raw.va = ka < N ? *reinterpret_cast<const float4*>(vline + (int64_t)ka * pos_stride + vc * 4)
-                    : make_float4(0, 0, 0, 0);
-    raw.vb = kb < N ? *reinterpret_cast<const float4*>(vline + (int64_t)kb * pos_stride + vc * 4)
-                    : make_float4(0, 0, 0, 0);
+    const int kk = min(k0 + (t >> 2), N - 1);
+    const int p = t & 31, vc = t >> 5;               // V: key pair, 4-dim chunk
+    const int ka = min(k0 + 2 * p, N - 1), kb = min(k0 + 2 * p + 1, N - 1);
+    const u32x4* s = reinterpret_cast<const u32x4*>(kline + (int64_t)kk * pos_stride + ch * 8);
+    raw.k0 = s[0];
+    raw.k1 = s[1];
+    raw.va = *reinterpret_cast<const u32x4*>(vline + (int64_t)ka * pos_stride + vc * 4);
+    raw.vb = *reinterpret_cast<const u32x4*>(vline + (int64_t)kb * pos_stride + vc * 4);
   }
 }
 
@@ -145,7 +146,7 @@ __device__ __forceinline__ void store_kv(const KVRaw<T>& raw, T* sK, T* sV) {
   const int p = t & 31, vc = t >> 5;
   if constexpr (sizeof(T) == 2) {
     (void)p; (void)vc;
-    *reinterpret_cast<uint4*>(sK + k_lds_row(kk) * KST + ch * 8) = raw.k;
+    *reinterpret_cast<u32x4*>(sK + k_lds_row(kk) * KST + ch * 8) = raw.k;
     // V transposed: dim 8*ch + j of key kk goes to row 8*ch + j, column
     // kk ^ (16*ch) (16-bit stores of the low and high halves of each loaded
     // dword).  The swizzle spreads the four dim groups of a key over
@@ -159,13 +160,15 @@ __device__ __forceinline__ void store_kv(const KVRaw<T>& raw, T* sK, T* sV) {
       d[(2 * j + 1) * VST] = (uint16_t)(w[j] >> 16);
     }
   } else {
-    uint4* dk = reinterpret_cast<uint4*>(sK + k_lds_row(kk) * KST + ch * 8);
+    u32x4* dk = reinterpret_cast<u32x4*>(sK + k_lds_row(kk) * KST + ch * 8);
     dk[0] = raw.k0;
     dk[1] = raw.k1;
-    *reinterpret_cast<float2*>(sV + (vc * 4 + 0) * VST + 2 * p) = make_float2(raw.va.x, raw.vb.x);
-    *reinterpret_cast<float2*>(sV + (vc * 4 + 1) * VST + 2 * p) = make_float2(raw.va.y, raw.vb.y);
-    *reinterpret_cast<float2*>(sV + (vc * 4 + 2) * VST + 2 * p) = make_float2(raw.va.z, raw.vb.z);
-    *reinterpret_cast<float2*>(sV + (vc * 4 + 3) * VST + 2 * p) = make_float2(raw.va.w, raw.vb.w);
+    uint2* dv = reinterpret_cast<uint2*>(sV + (vc * 4) * VST + 2 * p);
+    const int rs = VST / 2;  // row stride in uint2
+    dv[0 * rs] = make_uint2(raw.va.x, raw.vb.x);
+    dv[1 * rs] = make_uint2(raw.va.y, raw.vb.y);
+    dv[2 * rs] = make_uint2(raw.va.z, raw.vb.z);
+    dv[3 * rs] = make_uint2(raw.va.w, raw.vb.w);
   }
 }
 
@@ -202,6 +205,32 @@ __device__ __forceinline__ void st4f(bf16_t* p, const f32x4& v) {
 }
 __device__ __forceinline__ void st4f(float* p, const f32x4& v) {
   *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+
+// Eight consecutive bias values of one query, as loaded (16 or 32 bytes).
+template <typename T> struct BiasRaw;
+template <> struct BiasRaw<bf16_t> { uint4 u; };
+template <> struct BiasRaw<float> { uint4 a, b; };
+
+__device__ __forceinline__ void fetch_bias_raw(BiasRaw<bf16_t>& r, const bf16_t* p) {
+  r.u = *reinterpret_cast<const uint4*>(p);
+}
+__device__ __forceinline__ void fetch_bias_raw(BiasRaw<float>& r, const float* p) {
+  r.a = reinterpret_cast<const uint4*>(p)[0];
+  r.b = reinterpret_cast<const uint4*>(p)[1];
+}
+// Widen to fp32 accumulator operands: x = keys 0..3, y = keys 4..7.
+__device__ __forceinline__ void widen_bias(const BiasRaw<bf16_t>& r, f32x4& x, f32x4& y) {
+  x = f32x4{__uint_as_float(r.u.x << 16), __uint_as_float(r.u.x & 0xffff0000u),
+            __uint_as_float(r.u.y << 16), __uint_as_float(r.u.y & 0xffff0000u)};
+  y = f32x4{__uint_as_float(r.u.z << 16), __uint_as_float(r.u.z & 0xffff0000u),
+            __uint_as_float(r.u.w << 16), __uint_as_float(r.u.w & 0xffff0000u)};
+}
+__device__ __forceinline__ void widen_bias(const BiasRaw<float>& r, f32x4& x, f32x4& y) {
+  x = f32x4{__uint_as_float(r.a.x), __uint_as_float(r.a.y), __uint_as_float(r.a.z),
+            __uint_as_float(r.a.w)};
+  y = f32x4{__uint_as_float(r.b.x), __uint_as_float(r.b.y), __uint_as_float(r.b.z),
+            __uint_as_float(r.b.w)};
 }
 
 // Bias prep.  The prepared bias holds, for every (b, h, query q < Nq, key
@@ -357,16 +386,38 @@ attn_fwd_kernel(FwdParams p) {
   }
 
   KVRaw<T> raw[ROWS];
-  f32x4 bt[2][2][2];  // bias tile in accumulator layout: [qb][half][kb]
-  auto fetch_bias = [&](int k0) {
+  // Bias operands of the next tile as loaded (raw), widened to fp32 only
+  // after the next barrier: the loads stay in flight across the K/V tile
+  // store instead of being waited for at the end of the tile.
+  BiasRaw<T> braw[2][2];  // [qb][half]
+#define EVO_FETCH_BIAS(k0_)                                                        \
+  do {                                                                         \
+    if constexpr (HAS_BIAS) {                                                  \
+      for (int qb = 0; qb < 2; ++qb)                                           \
+        for (int half = 0; half < 2; ++half)                                   \
+          fetch_bias_raw(braw[qb][half],                                       \
+                         bbase + (int64_t)((k0_) / BK) * (BQ * BK) + (qb * 2 + half) * 512); \
+    }                                                                          \
+  } while (0)
+#pragma unroll
+  for (int rr = 0; rr < ROWS; ++rr) fetch_kv<T>(raw[rr], kline[rr], vline[rr], 0, N, pos_stride);
+  EVO_FETCH_BIAS(0);
+
+  const int ntiles = (N + BK - 1) / BK;
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int k0 = tile * BK;
+    const int buf = tile & 1;
+#pragma unroll
+    for (int rr = 0; rr < ROWS; ++rr) store_kv<T>(raw[rr], sK[buf][rr], sV[buf][rr]);
+    __syncthreads();
+    // This tile's bias operands in accumulator layout: [qb][half][kb].
+    f32x4 bt[2][2][2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         if constexpr (HAS_BIAS) {
-          const T* src = bbase + (int64_t)(k0 / BK) * (BQ * BK) + (qb * 2 + half) * 512;
-          bt[qb][half][0] = ld4f(src);
-          bt[qb][half][1] = ld4f(src + 4);
+          widen_bias(braw[qb][half], bt[qb][half][0], bt[qb][half][1]);
         } else {
           // no bias and no shared mask: 0, padding keys -inf
 #pragma unroll
@@ -377,18 +428,6 @@ attn_fwd_kernel(FwdParams p) {
                   (k0 + half * 32 + 8 * g + 4 * kb + i < N) ? 0.f : -INFINITY;
         }
       }
-  };
-#pragma unroll
-  for (int rr = 0; rr < ROWS; ++rr) fetch_kv<T>(raw[rr], kline[rr], vline[rr], 0, N, pos_stride);
-  fetch_bias(0);
-
-  const int ntiles = (N + BK - 1) / BK;
-  for (int tile = 0; tile < ntiles; ++tile) {
-    const int k0 = tile * BK;
-    const int buf = tile & 1;
-#pragma unroll
-    for (int rr = 0; rr < ROWS; ++rr) store_kv<T>(raw[rr], sK[buf][rr], sV[buf][rr]);
-    __syncthreads();
     if (tile + 1 < ntiles) {
 #pragma unroll
       for (int rr = 0; rr < ROWS; ++rr)
@@ -493,7 +532,7 @@ attn_fwd_kernel(FwdParams p) {
             o[rr][qb][cb] = mma32(vf[cb], pf[rr][qb][half], o[rr][qb][cb]);
       }
     // next tile's bias operands (the logit registers are free again)
-    if (tile + 1 < ntiles) fetch_bias(k0 + BK);
+    if (tile + 1 < ntiles) EVO_FETCH_BIAS(k0 + BK);
   }
 
   // Epilogue: normalise, gate, store; LSE in natural log.
@@ -531,6 +570,8 @@ attn_fwd_kernel(FwdParams p) {
     }
   }
 }
+
+#undef EVO_FETCH_BIAS
 
 template <typename T, int ROWS, bool ROW_MASK>
 hipError_t launch_t(const FwdParams& p, hipStream_t s) {
@@ -581,16 +622,16 @@ hipError_t launch_attn_fwd(const AttnFwdArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     p.biasp = bp;
   }
-  // Lines of a workgroup share the bias tile.
-  const int rows = (a.dtype == 1 && a.R > 1) ? 2 : 1;
+  // Lines of a workgroup share the bias tile (bf16; with one mask per line
+  // the two-line variant would not fit two waves per SIMD in registers).
+  const int rows = (a.dtype == 1 && a.R > 1 && !row_mask) ? 2 : 1;
   p.n_qt = (int)((a.N + BQ - 1) / BQ);
   p.n_rg = (int)((a.R + rows - 1) / rows);
   const int64_t total = a.B * ((a.H + 1) / 2) * 2 * (int64_t)p.n_rg * p.n_qt;
   if (total > (int64_t)INT32_MAX - 8) return hipErrorInvalidValue;
   p.total = (int)total;
   if (a.dtype == 1) {
-    if (rows == 2)
-      return row_mask ? launch_t<bf16_t, 2, true>(p, s) : launch_t<bf16_t, 2, false>(p, s);
+    if (rows == 2) return launch_t<bf16_t, 2, false>(p, s);
     return row_mask ? launch_t<bf16_t, 1, true>(p, s) : launch_t<bf16_t, 1, false>(p, s);
   }
   return row_mask ? launch_t<float, 1, true>(p, s) : launch_t<float, 1, false>(p, s);
