@@ -47,6 +47,7 @@ constexpr int kMaxKeysBwd = 1 << 16;
 constexpr int kTargetGroups = 1024;         // dbias workgroups wanted
 
 int64_t pad64(int64_t n) { return (n + 63) / 64 * 64; }
+int64_t pad128(int64_t n) { return (n + 127) / 128 * 128; }
 
 struct BwdLayout {
   int64_t Np, n_rg, rows_per_group;
@@ -74,8 +75,8 @@ BwdLayout bwd_layout(int dtype, int64_t B, int64_t R, int64_t N, int64_t H) {
   L.off_kt = o;    o += a256(lines * C * L.Np * es);
   L.off_lse2 = o;  o += a256(lines * L.Np * 4);
   L.off_d = o;     o += a256(lines * L.Np * 4);
-  L.off_bp = o;    o += a256((size_t)B * H * L.Np * L.Np * es);
-  L.off_bpt = o;   o += a256((size_t)B * H * L.Np * L.Np * es);
+  L.off_bp = o;    o += a256((size_t)B * H * pad128(N) * L.Np * es);
+  L.off_bpt = o;   o += a256((size_t)B * H * pad128(N) * L.Np * es);
   L.off_dbpart = o;
   if (L.n_rg > 1) o += a256((size_t)L.n_rg * B * H * L.Np * L.Np * 4);
   L.total = o;
@@ -191,7 +192,7 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdParams p) {
       if (lse != -INFINITY) l2 = lse * kLog2e;
     }
     p.lse2[lh * p.Np + pos] = l2;
-    p.dd[lh * p.Np + pos] = pos < N ? dsum : 0.f;
+    p.dd[lh * p.Np + pos] = pos < N ? -dsum : 0.f;  // -D: the dP accumulator's start
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -216,37 +217,71 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdParams p) {
   st4e(static_cast<T*>(p.kt) + to, k2);
 }
 
-// Pair bias (natural units, working dtype) with the shared key mask folded
-// in, both orientations: bp[b,h,q,k] (q < Np, k < Np), bpt[b,h,k,q]; keys
-// >= N are -inf.  Every stored value is exact (a bias value, 0 or -inf).
+// Pair bias (natural units, working dtype) with the shared key mask and the
+// padding folded in: -inf for masked keys and keys >= N, 0 without a bias,
+// any finite value for queries >= N.  Every stored value is exact.  Two
+// copies, each in the order one kernel reads it, so that every bias load is
+// a contiguous block per wave:
+//   bp  (dQ and dBias kernels; the forward's order): per (b, h) a grid of
+//       [Nq128/128][Np/64] tiles, each [wave 4][qb 2][half 2][lane 64][8]:
+//       lane (l16, g) of wave w holds query 128*qt + 32*w + 16*qb + l16,
+//       keys 64*kt + 32*half + 8*g .. +7.
+//   bpt (dK/dV kernel): per (b, h) a grid of [Nk128/128][Np/32] blocks (key
+//       tile, 32-query step), each [wave 4][lane 64][qb 2][kb 2][i 4]: lane
+//       (l16, g) of wave w holds key 128*kt + 32*w + 16*kb + l16 and
+//       queries 32*st + 16*qb + 4*g + i.
+template <typename T>
+__device__ __forceinline__ float bias_value(const BwdParams& p, int bh, int q, int k) {
+  if (k >= p.N) return -INFINITY;
+  const int b = bh / p.H;
+  if (p.mask && !p.row_mask && p.mask[(int64_t)b * p.mask_rows * p.N + k] == 0) return -INFINITY;
+  const T* Bias = static_cast<const T*>(p.bias);
+  return (Bias && q < p.N) ? Tr<T>::to_f(Bias[((int64_t)bh * p.N + q) * p.N + k]) : 0.f;
+}
+
 template <typename T>
 __global__ void __launch_bounds__(256) bwd_bias_kernel(BwdParams p) {
-  __shared__ float tile[32][33];
-  const int nblk = p.Np / 32;
-  int w = blockIdx.x;
-  const int kb = w % nblk; w /= nblk;
-  const int qb = w % nblk; w /= nblk;
-  const int bh = w;  // b * H + h
-  const int b = bh / p.H;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
-  const T* Bias = static_cast<const T*>(p.bias);
-  const int N = p.N;
-  for (int yy = ty; yy < 32; yy += 8) {
-    const int q = qb * 32 + yy, k = kb * 32 + tx;
-    float v = -INFINITY;
-    if (k < N) {
-      v = 0.f;
-      if (Bias && q < N) v = Tr<T>::to_f(Bias[((int64_t)bh * N + q) * N + k]);
-      if (p.mask && !p.row_mask && p.mask[(int64_t)b * p.mask_rows * N + k] == 0)
-        v = -INFINITY;
+  const int Np = p.Np, nq128 = (p.N + 127) / 128, nk64 = Np / 64, nst = Np / 32;
+  const int64_t chunks = (int64_t)p.B * p.H * nq128 * 128 * Np / 8;  // per copy
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < 2 * chunks;
+       e += (int64_t)gridDim.x * 256) {
+    f32x4 v[2];
+    if (e < chunks) {  // bp chunk e: 8 keys of one query
+      const int lane = (int)(e & 63);
+      int64_t t = e >> 6;
+      const int half = (int)(t & 1); t >>= 1;
+      const int qb = (int)(t & 1); t >>= 1;
+      const int wv = (int)(t & 3); t >>= 2;
+      const int kt = (int)(t % nk64); t /= nk64;
+      const int qt = (int)(t % nq128);
+      const int bh = (int)(t / nq128);
+      const int q = qt * 128 + wv * 32 + qb * 16 + (lane & 15);
+      const int k0 = kt * 64 + half * 32 + 8 * (lane >> 4);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j >> 2][j & 3] = bias_value<T>(p, bh, q, k0 + j);
+      T* dst = static_cast<T*>(p.bp) + e * 8;
+      st4e(dst, v[0]);
+      st4e(dst + 4, v[1]);
+    } else {  // bpt chunk: (qb) half of a lane's 16 values, 4 queries x 2 keys
+      const int64_t f = e - chunks;
+      const int qb = (int)(f & 1);
+      const int lane = (int)((f >> 1) & 63);
+      int64_t t = f >> 7;
+      const int wv = (int)(t & 3); t >>= 2;
+      const int st = (int)(t % nst); t /= nst;
+      const int kt = (int)(t % nq128);
+      const int bh = (int)(t / nq128);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int k = kt * 128 + wv * 32 + kb * 16 + (lane & 15);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          v[kb][i] = bias_value<T>(p, bh, st * 32 + qb * 16 + 4 * (lane >> 4) + i, k);
+      }
+      T* dst = static_cast<T*>(p.bpt) + f * 8;
+      st4e(dst, v[0]);
+      st4e(dst + 4, v[1]);
     }
-    static_cast<T*>(p.bp)[((int64_t)bh * p.Np + q) * p.Np + k] = Tr<T>::from_f(v);
-    tile[yy][tx] = v;
-  }
-  __syncthreads();
-  for (int yy = ty; yy < 32; yy += 8) {
-    const int k = kb * 32 + yy, q = qb * 32 + tx;
-    static_cast<T*>(p.bpt)[((int64_t)bh * p.Np + k) * p.Np + q] = Tr<T>::from_f(tile[tx][yy]);
   }
 }
 
@@ -257,7 +292,7 @@ template <typename T> struct StageRaw;
 template <> struct StageRaw<bf16_t> { uint4 a, b; float l; };
 template <> struct StageRaw<float> { uint4 a0, a1, b0, b1; float l; };
 
-template <typename T>
+template <typename T, bool ROW_MASK>
 __global__ void __launch_bounds__(256) bwd_dkdv_kernel(BwdParams p) {
   using Op = typename Tr<T>::Op;
   constexpr int RS = 40;  // row stride (elements): 16-byte reads spread over banks
@@ -265,11 +300,20 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(32))) T sT[2][4][32 * RS];  // [buf][Q,dO,Qt,dOt]
   __shared__ float sL[2][2][32];                                 // [buf][lse2, D]
 
+  // Work order (fastest first): key tile, head within a head pair, line,
+  // head pair.  The key tiles of one line read the same query-side data and
+  // the two heads of a pair share every 128-byte line of it (heads are
+  // interleaved at 64 bytes), so all of them run back to back on one XCD
+  // and meet in its L2; a pair's bias^T (2 x N^2 elements) stays there too.
   const int nkt = (p.N + 127) / 128;
-  int w = blockIdx.x;
+  const int HP = (p.H + 1) >> 1;
+  int w = xcd_work_index(p.B * p.R * HP * 2 * nkt);
+  if (w < 0) return;
   const int kt = w % nkt; w /= nkt;
-  const int h = w % p.H;
-  const int line = w / p.H;   // b * R + r
+  const int hi = w & 1; w >>= 1;
+  const int line = w % (p.B * p.R);   // b * R + r
+  const int h = 2 * (w / (p.B * p.R)) + hi;
+  if (h >= p.H) return;  // odd H: the missing partner of the last pair
   const int b = line / p.R, r = line - b * p.R;
   const int N = p.N, H = p.H, Np = p.Np;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -284,20 +328,19 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(BwdParams p) {
   const T* DO = static_cast<const T*>(p.dopre);
   const T* QT = static_cast<const T*>(p.qt) + lh * C * Np;
   const T* DT = static_cast<const T*>(p.dot) + lh * C * Np;
-  const T* BPT = static_cast<const T*>(p.bpt) + (int64_t)(b * H + h) * Np * Np;
-  const uint8_t* mrow = (p.mask && p.row_mask)
-                            ? p.mask + ((int64_t)b * p.mask_rows + r) * N
-                            : nullptr;
+  // This lane's bias^T operands of step st: 16 values at BPT + st * 4096
+  // (prepared block order: [qb][kb][i]).
+  const T* BPT = static_cast<const T*>(p.bpt) +
+                 ((int64_t)(b * H + h) * nkt + kt) * (Np / 32) * 4096 + wave * 1024 + lane * 16;
+  const uint8_t* mrow = ROW_MASK ? p.mask + ((int64_t)b * p.mask_rows + r) * N : nullptr;
 
   // This wave's keys: kbase + kb*16 + l16 (kb = 0, 1).
   const int kbase = kt * 128 + wave * 32;
   Op kf[2], vf[2];
-  bool kdead[2];
-  int krow[2];
+  bool kdead[2];  // keys of a per-line mask (padding and shared masks are in the bias)
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     const int key = kbase + kb * 16 + l16;
-    krow[kb] = min(key, Np - 1);
     if (key < N) {
       kf[kb] = scale8(ldop<T>(K + lbase + (int64_t)key * pos_stride + 8 * g), p.qscale);
       vf[kb] = ldop<T>(V + lbase + (int64_t)key * pos_stride + 8 * g);
@@ -305,7 +348,7 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(BwdParams p) {
       kf[kb] = Op{};
       vf[kb] = Op{};
     }
-    kdead[kb] = key >= N || (mrow && mrow[key] == 0);
+    kdead[kb] = ROW_MASK && key < N && mrow[key] == 0;
   }
   f32x4 dk[2][2], dv[2][2];  // [cb][kb]
 #pragma unroll
@@ -358,32 +401,26 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(BwdParams p) {
     }
     if (tid < 64) sL[buf][tid >> 5][tid & 31] = raw.l;
   };
-  f32x4 cbn[2][2];  // next step's bias^T C operands [qb][kb]
-  auto fetch_bias = [&](int q0) {
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        cbn[qb][kb] = ld4e(BPT + (int64_t)krow[kb] * Np + q0 + qb * 16 + 4 * g);
-  };
   (void)E16;
+  // next step's bias^T operands, raw until the step's barrier has passed
+  Raw8<T> bn[2];  // [qb]
 
   StageRaw<T> raw;
   fetch(raw, 0);
-  fetch_bias(0);
+  ld_raw8(bn[0], BPT);
+  ld_raw8(bn[1], BPT + 8);
   const int nsteps = (N + 31) / 32;
   for (int st = 0; st < nsteps; ++st) {
     const int q0 = st * 32, buf = st & 1;
     store(raw, buf);
-    f32x4 cbias[2][2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) cbias[qb][kb] = cbn[qb][kb];
     __syncthreads();
+    f32x4 cbias[2][2];  // [qb][kb]
+    widen8(bn[0], cbias[0][0], cbias[0][1]);
+    widen8(bn[1], cbias[1][0], cbias[1][1]);
     if (st + 1 < nsteps) {
       fetch(raw, q0 + 32);
-      fetch_bias(q0 + 32);
+      ld_raw8(bn[0], BPT + (int64_t)(st + 1) * 4096);
+      ld_raw8(bn[1], BPT + (int64_t)(st + 1) * 4096 + 8);
     }
     const T* sQ = sT[buf][0];
     const T* sDO = sT[buf][1];
@@ -391,28 +428,30 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(BwdParams p) {
     const T* sDOt = sT[buf][3];
 
     // S[qb][kb]: lane holds queries qb*16 + 4g + i for key kbase + kb*16 + l16.
+    // dP starts from -D, so the accumulator ends at dP - D.
     f32x4 s[2][2], dp[2][2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const Op qa = *reinterpret_cast<const Op*>(sQ + (qb * 16 + l16) * RS + 8 * g);
       const Op da = *reinterpret_cast<const Op*>(sDO + (qb * 16 + l16) * RS + 8 * g);
+      const f32x4 negd = *reinterpret_cast<const f32x4*>(&sL[buf][1][qb * 16 + 4 * g]);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         s[qb][kb] = mma32(qa, kf[kb], cbias[qb][kb]);
-        dp[qb][kb] = mma32(da, vf[kb], f32x4{0.f, 0.f, 0.f, 0.f});
+        dp[qb][kb] = mma32(da, vf[kb], negd);
       }
     }
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const f32x4 l2 = *reinterpret_cast<const f32x4*>(&sL[buf][0][qb * 16 + 4 * g]);
-      const f32x4 dd = *reinterpret_cast<const f32x4*>(&sL[buf][1][qb * 16 + 4 * g]);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float pv = kdead[kb] ? 0.f : exp2_fast(__builtin_fmaf(s[qb][kb][i], kLog2e, -l2[i]));
+          float pv = exp2_fast(__builtin_fmaf(s[qb][kb][i], kLog2e, -l2[i]));
+          if constexpr (ROW_MASK) pv = kdead[kb] ? 0.f : pv;
           s[qb][kb][i] = pv;
-          dp[qb][kb][i] = pv * (dp[qb][kb][i] - dd[i]);
+          dp[qb][kb][i] = pv * dp[qb][kb][i];
         }
     }
     // dV^T += dO^T P,  dK^T += Q^T dS  (contraction over the 32 query slots)
@@ -495,12 +534,17 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdParams p) {
   constexpr int KS = BLds<T>::KS, TS = BLds<T>::TS;
   __shared__ __attribute__((aligned(32))) T sK[2][64 * KS], sV[2][64 * KS], sKt[2][32 * TS];
 
+  // Work order: query tile, head within a pair, line, head pair (as in the
+  // dK/dV kernel): the pair's bias rows and shared K/V lines stay in L2.
   const int nqt = (p.N + 127) / 128;
-  int w = xcd_work_index(p.B * p.R * p.H * nqt);
+  const int HP = (p.H + 1) >> 1;
+  int w = xcd_work_index(p.B * p.R * HP * 2 * nqt);
   if (w < 0) return;
   const int qt = w % nqt; w /= nqt;
-  const int h = w % p.H;
-  const int line = w / p.H;
+  const int hi = w & 1; w >>= 1;
+  const int line = w % (p.B * p.R);
+  const int h = 2 * (w / (p.B * p.R)) + hi;
+  if (h >= p.H) return;
   const int b = line / p.R, r = line - b * p.R;
   const int N = p.N, H = p.H, Np = p.Np;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -515,8 +559,7 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdParams p) {
   const uint8_t* mrow = ROW_MASK ? p.mask + ((int64_t)b * p.mask_rows + r) * N : nullptr;
 
   Op qf[2], df[2];
-  float l2[2], dd[2];
-  const T* brow[2];
+  float l2[2], dd[2];  // dd = -D
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int q = qw0 + qb * 16 + l16;
@@ -524,11 +567,14 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdParams p) {
     qf[qb] = scale8(ldop<T>(static_cast<const T*>(p.q) + lbase + (int64_t)qc * pos_stride + 8 * g),
                     p.qscale);
     df[qb] = ldop<T>(static_cast<const T*>(p.dopre) + lbase + (int64_t)qc * pos_stride + 8 * g);
-    const int qp = min(q, Np - 1);
     l2[qb] = q < N ? p.lse2[lh * Np + q] : INFINITY;
     dd[qb] = q < N ? p.dd[lh * Np + q] : 0.f;
-    brow[qb] = static_cast<const T*>(p.bp) + ((int64_t)(b * H + h) * Np + qp) * Np + 8 * g;
   }
+  // This lane's 8 bias values of (qb, half) in key tile `tile` sit at
+  // BP + tile * 8192 + (qb*2 + half) * 512 (prepared tile order).
+  const T* BP = static_cast<const T*>(p.bp) +
+                (((int64_t)(b * H + h) * nqt + qt) * (Np / 64)) * 8192 + wave * 2048 + lane * 8;
+  Raw8<T> bn[2][2];  // next tile's bias operands [qb][half], raw
   f32x4 dq[2][2];  // [qb][cb]
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb)
@@ -538,29 +584,46 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdParams p) {
   uint4 rk0, rk1, rv0, rv1, rt0, rt1;
   rk1 = rv1 = rt1 = make_uint4(0, 0, 0, 0);
   EVO_FETCH_K(T, K, V, KT, 0);
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int half = 0; half < 2; ++half) ld_raw8(bn[qb][half], BP + (qb * 2 + half) * 512);
   const int ntiles = (N + 63) / 64;
   for (int tile = 0; tile < ntiles; ++tile) {
     const int k0 = tile * 64, buf = tile & 1;
     EVO_STORE_K(T, sK[buf], sV[buf], sKt[buf], KS, TS);
     __syncthreads();
+    f32x4 cb_[2][2][2];  // this tile's bias operands [qb][half][kb]
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) widen8(bn[qb][half], cb_[qb][half][0], cb_[qb][half][1]);
     // next tile (the last iteration re-fetches its own tile, unused)
     EVO_FETCH_K(T, K, V, KT, min(k0 + 64, (ntiles - 1) * 64));
+    {
+      const int nt = min(tile + 1, ntiles - 1);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+          ld_raw8(bn[qb][half], BP + (int64_t)nt * 8192 + (qb * 2 + half) * 512);
+    }
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      f32x4 s[2][2], dp[2][2];  // [qb][kb]
+      f32x4 s[2][2], dp[2][2];  // [qb][kb]; dP starts from -D
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const Op vf = *reinterpret_cast<const Op*>(sV[buf] + (half * 32 + kb * 16 + l16) * KS + 8 * g);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
-          dp[qb][kb] = mma32(vf, df[qb], f32x4{0.f, 0.f, 0.f, 0.f});
+          dp[qb][kb] = mma32(vf, df[qb], f32x4{dd[qb], dd[qb], dd[qb], dd[qb]});
       }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const Op kf = *reinterpret_cast<const Op*>(sK[buf] + (half * 32 + kb * 16 + l16) * KS + 8 * g);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
-          s[qb][kb] = mma32(kf, qf[qb], ld4e(brow[qb] + k0 + half * 32 + 4 * kb));
+          s[qb][kb] = mma32(kf, qf[qb], cb_[qb][half][kb]);
       }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -578,7 +641,7 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdParams p) {
           for (int i = 0; i < 4; ++i) {
             const float pv =
                 dead[i] ? 0.f : exp2_fast(__builtin_fmaf(s[qb][kb][i], kLog2e, -l2[qb]));
-            dp[qb][kb][i] = pv * (dp[qb][kb][i] - dd[qb]);
+            dp[qb][kb][i] = pv * dp[qb][kb][i];
           }
       }
 #pragma unroll
@@ -615,14 +678,20 @@ __global__ void __launch_bounds__(256) bwd_dbias_kernel(BwdParams p) {
   constexpr int KS = BLds<T>::KS;
   __shared__ __attribute__((aligned(32))) T sK[2][64 * KS], sV[2][64 * KS];
 
+  // Work order: head within a pair, key tile, query tile, row group, head
+  // pair, batch.  The two heads of a pair walk the same rows in lockstep and
+  // share every 128-byte line of Q, dO, K and V.
   const int nqt = (p.N + 127) / 128, nkt = p.Np / 64;
-  int w = xcd_work_index(p.B * p.H * nqt * nkt * p.n_rg);
+  const int HP = (p.H + 1) >> 1;
+  int w = xcd_work_index(p.B * HP * 2 * nqt * nkt * p.n_rg);
   if (w < 0) return;
+  const int hi = w & 1; w >>= 1;
   const int kt = w % nkt; w /= nkt;
   const int qt = w % nqt; w /= nqt;
   const int rg = w % p.n_rg; w /= p.n_rg;
-  const int h = w % p.H;
-  const int b = w / p.H;
+  const int h = 2 * (w % HP) + hi;
+  const int b = w / HP;
+  if (h >= p.H) return;
   const int N = p.N, H = p.H, R = p.R, Np = p.Np;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, g = lane >> 4;
@@ -632,16 +701,19 @@ __global__ void __launch_bounds__(256) bwd_dbias_kernel(BwdParams p) {
   const int qw0 = qt * 128 + wave * 32;
 
   f32x4 cbias[2][2][2], db[2][2][2];  // [half][qb][kb]
+  {
+    // prepared tile order: this lane's 8 values of (qb, half) are contiguous
+    const T* bt = static_cast<const T*>(p.bp) + (((int64_t)bh * nqt + qt) * nkt + kt) * 8192 +
+                  wave * 2048 + lane * 8;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int qp = min(qw0 + qb * 16 + l16, Np - 1);
-    const T* brow = static_cast<const T*>(p.bp) + ((int64_t)bh * Np + qp) * Np + k0 + 8 * g;
+    for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-    for (int half = 0; half < 2; ++half)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        cbias[half][qb][kb] = ld4e(brow + half * 32 + 4 * kb);
-        db[half][qb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int half = 0; half < 2; ++half) {
+        Raw8<T> r;
+        ld_raw8(r, bt + (qb * 2 + half) * 512);
+        widen8(r, cbias[half][qb][0], cbias[half][qb][1]);
+        db[half][qb][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+        db[half][qb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
   }
   const int r_begin = rg * p.rows_per_group;
@@ -706,7 +778,7 @@ __global__ void __launch_bounds__(256) bwd_dbias_kernel(BwdParams p) {
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
           s[qb][kb] = mma32(kf, qf[qb], cbias[half][qb][kb]);
-          dp[qb][kb] = mma32(vf, df[qb], f32x4{0.f, 0.f, 0.f, 0.f});
+          dp[qb][kb] = mma32(vf, df[qb], f32x4{dd[qb], dd[qb], dd[qb], dd[qb]});  // from -D
         }
       }
 #pragma unroll
@@ -725,7 +797,7 @@ __global__ void __launch_bounds__(256) bwd_dbias_kernel(BwdParams p) {
           for (int i = 0; i < 4; ++i) {
             const float pv =
                 dead[i] ? 0.f : exp2_fast(__builtin_fmaf(s[qb][kb][i], kLog2e, -l2[qb]));
-            db[half][qb][kb][i] += pv * (dp[qb][kb][i] - dd[qb]);
+            db[half][qb][kb][i] += pv * dp[qb][kb][i];
           }
       }
     }
@@ -779,15 +851,24 @@ hipError_t launch_t(BwdParams& p, hipStream_t s) {
                      s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_bias_kernel<T>, dim3((unsigned)(p.B * p.H * nblk * nblk)), dim3(256),
-                     0, s, p);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int nkt = (p.N + 127) / 128;
-  hipLaunchKernelGGL(bwd_dkdv_kernel<T>, dim3((unsigned)(lines * p.H * nkt)), dim3(256), 0, s,
-                     p);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   {
-    const int total = p.B * p.R * p.H * ((p.N + 127) / 128);
+    const int64_t work = 2 * (int64_t)p.B * p.H * ((p.N + 127) / 128) * 128 * p.Np / 8;
+    hipLaunchKernelGGL(bwd_bias_kernel<T>, dim3((unsigned)std::min<int64_t>((work + 255) / 256, 8192)),
+                       dim3(256), 0, s, p);
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int HP2 = (p.H + 1) / 2 * 2;  // heads rounded up to whole pairs
+  {
+    const int total = (int)(lines * HP2 * ((p.N + 127) / 128));
+    const int grid = (total + kNumXcd - 1) / kNumXcd * kNumXcd;
+    if (p.row_mask)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<T, true>), dim3(grid), dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<T, false>), dim3(grid), dim3(256), 0, s, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  {
+    const int total = (int)(lines * HP2 * ((p.N + 127) / 128));
     const int grid = (total + kNumXcd - 1) / kNumXcd * kNumXcd;
     if (p.row_mask)
       hipLaunchKernelGGL((bwd_dq_kernel<T, true>), dim3(grid), dim3(256), 0, s, p);
@@ -796,7 +877,7 @@ hipError_t launch_t(BwdParams& p, hipStream_t s) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (p.dbias) {
-    const int total = p.B * p.H * ((p.N + 127) / 128) * (p.Np / 64) * p.n_rg;
+    const int total = p.B * HP2 * ((p.N + 127) / 128) * (p.Np / 64) * p.n_rg;
     const int grid = (total + kNumXcd - 1) / kNumXcd * kNumXcd;
     if (p.row_mask)
       hipLaunchKernelGGL((bwd_dbias_kernel<T, true>), dim3(grid), dim3(256), 0, s, p);

@@ -103,7 +103,6 @@ __device__ __forceinline__ int v_col_t(int row, int c) {
 // key and 4 V elements of two keys.
 // (native vector types: HIP's uint4 struct is copied as an aggregate, which
 // can leave the tile in scratch memory)
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 template <typename T> struct KVRaw;
 template <> struct KVRaw<bf16_t> { u32x4 k, v; };
 template <> struct KVRaw<float> { u32x4 k0, k1, va, vb; };
@@ -205,32 +204,6 @@ __device__ __forceinline__ void st4f(bf16_t* p, const f32x4& v) {
 }
 __device__ __forceinline__ void st4f(float* p, const f32x4& v) {
   *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
-}
-
-// Eight consecutive bias values of one query, as loaded (16 or 32 bytes).
-template <typename T> struct BiasRaw;
-template <> struct BiasRaw<bf16_t> { uint4 u; };
-template <> struct BiasRaw<float> { uint4 a, b; };
-
-__device__ __forceinline__ void fetch_bias_raw(BiasRaw<bf16_t>& r, const bf16_t* p) {
-  r.u = *reinterpret_cast<const uint4*>(p);
-}
-__device__ __forceinline__ void fetch_bias_raw(BiasRaw<float>& r, const float* p) {
-  r.a = reinterpret_cast<const uint4*>(p)[0];
-  r.b = reinterpret_cast<const uint4*>(p)[1];
-}
-// Widen to fp32 accumulator operands: x = keys 0..3, y = keys 4..7.
-__device__ __forceinline__ void widen_bias(const BiasRaw<bf16_t>& r, f32x4& x, f32x4& y) {
-  x = f32x4{__uint_as_float(r.u.x << 16), __uint_as_float(r.u.x & 0xffff0000u),
-            __uint_as_float(r.u.y << 16), __uint_as_float(r.u.y & 0xffff0000u)};
-  y = f32x4{__uint_as_float(r.u.z << 16), __uint_as_float(r.u.z & 0xffff0000u),
-            __uint_as_float(r.u.w << 16), __uint_as_float(r.u.w & 0xffff0000u)};
-}
-__device__ __forceinline__ void widen_bias(const BiasRaw<float>& r, f32x4& x, f32x4& y) {
-  x = f32x4{__uint_as_float(r.a.x), __uint_as_float(r.a.y), __uint_as_float(r.a.z),
-            __uint_as_float(r.a.w)};
-  y = f32x4{__uint_as_float(r.b.x), __uint_as_float(r.b.y), __uint_as_float(r.b.z),
-            __uint_as_float(r.b.w)};
 }
 
 // Bias prep.  The prepared bias holds, for every (b, h, query q < Nq, key
@@ -389,13 +362,13 @@ attn_fwd_kernel(FwdParams p) {
   // Bias operands of the next tile as loaded (raw), widened to fp32 only
   // after the next barrier: the loads stay in flight across the K/V tile
   // store instead of being waited for at the end of the tile.
-  BiasRaw<T> braw[2][2];  // [qb][half]
+  Raw8<T> braw[2][2];  // [qb][half]
 #define EVO_FETCH_BIAS(k0_)                                                        \
   do {                                                                         \
     if constexpr (HAS_BIAS) {                                                  \
       for (int qb = 0; qb < 2; ++qb)                                           \
         for (int half = 0; half < 2; ++half)                                   \
-          fetch_bias_raw(braw[qb][half],                                       \
+          ld_raw8(braw[qb][half],                                              \
                          bbase + (int64_t)((k0_) / BK) * (BQ * BK) + (qb * 2 + half) * 512); \
     }                                                                          \
   } while (0)
@@ -417,7 +390,7 @@ attn_fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         if constexpr (HAS_BIAS) {
-          widen_bias(braw[qb][half], bt[qb][half][0], bt[qb][half][1]);
+          widen8(braw[qb][half], bt[qb][half][0], bt[qb][half][1]);
         } else {
           // no bias and no shared mask: 0, padding keys -inf
 #pragma unroll

@@ -11,6 +11,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t bf16_t;  // bfloat16 storage in HBM
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -115,6 +116,34 @@ __device__ __forceinline__ bf16x8 scale8(const bf16x8& v, float s) {
 }
 __device__ __forceinline__ f32x8 scale8(const f32x8& v, float s) {
   return v * s;
+}
+
+// Eight consecutive elements as loaded (16 bytes bf16, 32 bytes fp32), kept
+// raw while a prefetch is in flight and widened to two fp32 accumulator
+// operands (elements 0..3 and 4..7) only where they are used.  Native vector
+// types, so the data never round-trips through scratch memory.
+template <typename T> struct Raw8;
+template <> struct Raw8<bf16_t> { u32x4 a; };
+template <> struct Raw8<float> { u32x4 a, b; };
+
+__device__ __forceinline__ void ld_raw8(Raw8<bf16_t>& r, const bf16_t* p) {
+  r.a = *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void ld_raw8(Raw8<float>& r, const float* p) {
+  r.a = reinterpret_cast<const u32x4*>(p)[0];
+  r.b = reinterpret_cast<const u32x4*>(p)[1];
+}
+__device__ __forceinline__ void widen8(const Raw8<bf16_t>& r, f32x4& x, f32x4& y) {
+  x = f32x4{__uint_as_float(r.a.x << 16), __uint_as_float(r.a.x & 0xffff0000u),
+            __uint_as_float(r.a.y << 16), __uint_as_float(r.a.y & 0xffff0000u)};
+  y = f32x4{__uint_as_float(r.a.z << 16), __uint_as_float(r.a.z & 0xffff0000u),
+            __uint_as_float(r.a.w << 16), __uint_as_float(r.a.w & 0xffff0000u)};
+}
+__device__ __forceinline__ void widen8(const Raw8<float>& r, f32x4& x, f32x4& y) {
+  x = f32x4{__uint_as_float(r.a.x), __uint_as_float(r.a.y), __uint_as_float(r.a.z),
+            __uint_as_float(r.a.w)};
+  y = f32x4{__uint_as_float(r.b.x), __uint_as_float(r.b.y), __uint_as_float(r.b.z),
+            __uint_as_float(r.b.w)};
 }
 
 // Workgroups are dispatched round-robin over the XCDs (workgroup i runs on
