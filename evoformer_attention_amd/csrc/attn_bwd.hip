@@ -768,21 +768,21 @@ __global__ void __launch_bounds__(256) bwd_dbias_kernel(BwdParams p) {
     __syncthreads();
     EVO_FETCH_ROW(min(r + 1, r_end - 1));
     const uint8_t* mrow = ROW_MASK ? p.mask + ((int64_t)b * p.mask_rows + r) * N : nullptr;
+    // one 16-key block at a time (short live ranges: this kernel's budget is
+    // three waves per SIMD); dP starts from -D
+    const f32x4 negd[2] = {f32x4{dd[0], dd[0], dd[0], dd[0]}, f32x4{dd[1], dd[1], dd[1], dd[1]}};
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      f32x4 s[2][2], dp[2][2];
+    for (int half = 0; half < 2; ++half)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const Op kf = *reinterpret_cast<const Op*>(sK[buf] + (half * 32 + kb * 16 + l16) * KS + 8 * g);
         const Op vf = *reinterpret_cast<const Op*>(sV[buf] + (half * 32 + kb * 16 + l16) * KS + 8 * g);
+        f32x4 s[2], dp[2];
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-          s[qb][kb] = mma32(kf, qf[qb], cbias[half][qb][kb]);
-          dp[qb][kb] = mma32(vf, df[qb], f32x4{dd[qb], dd[qb], dd[qb], dd[qb]});  // from -D
+          s[qb] = mma32(kf, qf[qb], cbias[half][qb][kb]);
+          dp[qb] = mma32(vf, df[qb], negd[qb]);
         }
-      }
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
         bool dead[4] = {false, false, false, false};
         if constexpr (ROW_MASK) {
 #pragma unroll
@@ -796,11 +796,10 @@ __global__ void __launch_bounds__(256) bwd_dbias_kernel(BwdParams p) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const float pv =
-                dead[i] ? 0.f : exp2_fast(__builtin_fmaf(s[qb][kb][i], kLog2e, -l2[qb]));
-            db[half][qb][kb][i] += pv * dp[qb][kb][i];
+                dead[i] ? 0.f : exp2_fast(__builtin_fmaf(s[qb][i], kLog2e, -l2[qb]));
+            db[half][qb][kb][i] += pv * dp[qb][i];
           }
       }
-    }
   }
 
 #undef EVO_FETCH_ROW
