@@ -34,8 +34,10 @@ namespace evo {
 namespace {
 
 constexpr int PW = 32;              // positions per wave
-constexpr int WAVES = 8;
-constexpr int TP = PW * WAVES;      // positions per tile
+// Waves per workgroup: one workgroup per CU (W^T fills the LDS), so its wave
+// count is the CU's occupancy.  16 waves (4 per SIMD) fit the register file
+// up to K = 128 input channels; wider inputs use 8.
+template <int KSTEPS> constexpr int waves_for() { return KSTEPS <= 4 ? 16 : 8; }
 constexpr int PAD = 8;              // LDS row padding (elements)
 constexpr int kMaxK = 256;
 constexpr size_t kLdsBudget = 150 * 1024;
@@ -92,9 +94,10 @@ __device__ __forceinline__ void st4<float>(float* p, const f32x4& v) {
   *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
 }
 
-template <typename T, int KSTEPS>
-__global__ void __launch_bounds__(512)
+template <typename T, int KSTEPS, int WAVES = waves_for<KSTEPS>()>
+__global__ void __launch_bounds__(WAVES * 64)
 rowgemm_kernel(GemmParams p) {
+  constexpr int TP = PW * WAVES;  // positions per tile
   using Op = typename Tr<T>::Op;
   constexpr int E16 = 16 / sizeof(T);      // elements per 16 bytes
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -236,21 +239,22 @@ rowgemm_kernel(GemmParams p) {
 }
 
 template <typename T, int KSTEPS>
-hipError_t launch_pass(GemmParams& p, size_t lds, int grid, hipStream_t s) {
+hipError_t launch_pass(GemmParams& p, size_t lds, hipStream_t s) {
+  constexpr int WAVES = waves_for<KSTEPS>();
+  const int64_t tiles = (p.npos + PW * WAVES - 1) / (PW * WAVES);
+  if (tiles > (int64_t)INT32_MAX) return hipErrorInvalidValue;
+  p.ntiles = (int)tiles;
+  const int grid = (int)std::min<int64_t>(tiles, 256);  // persistent: one per CU
   hipError_t e = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&rowgemm_kernel<T, KSTEPS>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((rowgemm_kernel<T, KSTEPS>), dim3(grid), dim3(512), lds, s, p);
+  hipLaunchKernelGGL((rowgemm_kernel<T, KSTEPS>), dim3(grid), dim3(WAVES * 64), lds, s, p);
   return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_gemm(GemmParams& p, hipStream_t s) {
-  const int64_t tiles = (p.npos + TP - 1) / TP;
-  if (tiles > (int64_t)INT32_MAX) return hipErrorInvalidValue;
-  p.ntiles = (int)tiles;
-  const int grid = (int)std::min<int64_t>(tiles, 256);
   const size_t row_bytes = (size_t)(p.K + PAD) * sizeof(T);
   const size_t ln_bytes = 2 * kMaxK * sizeof(float);
   int per_pass = (int)((kLdsBudget - ln_bytes) / row_bytes) / 16 * 16;
@@ -262,14 +266,14 @@ hipError_t launch_gemm(GemmParams& p, hipStream_t s) {
     const size_t lds = (size_t)p.pass_cols * row_bytes + ln_bytes;
     hipError_t e;
     switch (p.K / 32) {
-      case 1: e = launch_pass<T, 1>(p, lds, grid, s); break;
-      case 2: e = launch_pass<T, 2>(p, lds, grid, s); break;
-      case 3: e = launch_pass<T, 3>(p, lds, grid, s); break;
-      case 4: e = launch_pass<T, 4>(p, lds, grid, s); break;
-      case 5: e = launch_pass<T, 5>(p, lds, grid, s); break;
-      case 6: e = launch_pass<T, 6>(p, lds, grid, s); break;
-      case 7: e = launch_pass<T, 7>(p, lds, grid, s); break;
-      case 8: e = launch_pass<T, 8>(p, lds, grid, s); break;
+      case 1: e = launch_pass<T, 1>(p, lds, s); break;
+      case 2: e = launch_pass<T, 2>(p, lds, s); break;
+      case 3: e = launch_pass<T, 3>(p, lds, s); break;
+      case 4: e = launch_pass<T, 4>(p, lds, s); break;
+      case 5: e = launch_pass<T, 5>(p, lds, s); break;
+      case 6: e = launch_pass<T, 6>(p, lds, s); break;
+      case 7: e = launch_pass<T, 7>(p, lds, s); break;
+      case 8: e = launch_pass<T, 8>(p, lds, s); break;
       default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess) return e;
