@@ -39,7 +39,6 @@ constexpr int PW = 32;              // positions per wave
 // up to K = 128 input channels; wider inputs use 8.
 template <int KSTEPS> constexpr int waves_for() { return KSTEPS <= 4 ? 16 : 8; }
 constexpr int PAD = 8;              // LDS row padding (elements)
-constexpr int kMaxK = 256;
 constexpr size_t kLdsBudget = 150 * 1024;
 
 struct GemmParams {
@@ -76,10 +75,6 @@ __device__ __forceinline__ const T* w_row(const GemmParams& p, int c) {
   return static_cast<const T*>(p.w[4]) + (int64_t)(c - 4 * p.HC) * p.K;
 }
 
-__device__ __forceinline__ void ld16(void* dst, const void* src) {
-  *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
-}
-
 template <typename T>
 __device__ __forceinline__ void st4(T* p, const f32x4& v);
 template <>
@@ -99,64 +94,104 @@ __global__ void __launch_bounds__(WAVES * 64)
 rowgemm_kernel(GemmParams p) {
   constexpr int TP = PW * WAVES;  // positions per tile
   using Op = typename Tr<T>::Op;
-  constexpr int E16 = 16 / sizeof(T);      // elements per 16 bytes
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int K = KSTEPS * 32;
   const int KS = K + PAD;
-  T* sW = reinterpret_cast<T*>(smem);                        // [pass_cols][KS]
-  float* sLn = reinterpret_cast<float*>(sW + p.pass_cols * KS);  // ln_w | ln_b
+  T* sW = reinterpret_cast<T*>(smem);                           // [pass_cols][KS]
+  float* sC = reinterpret_cast<float*>(sW + p.pass_cols * KS);  // [pass_cols]
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, g = lane >> 4;
 
-  // ---- W^T rows of this pass into LDS (16-byte copies), LayerNorm affine.
+  // ---- This pass's weights into LDS, with the LayerNorm affine folded in:
+  // LN(x) . W^T = xhat . (W diag(gamma))^T + beta . W^T, xhat = (x - mu) *
+  // rstd.  sW holds W diag(gamma) (rounded to the working dtype), sC the
+  // per-column constant beta . W^T plus the column bias (gate or output).
+  const T* lnw = static_cast<const T*>(p.ln_w);
+  const T* lnb = static_cast<const T*>(p.ln_b);
   {
-    const int chunks = K / E16;
+    const int chunks = K / 8;
     for (int e = tid; e < p.pass_cols * chunks; e += blockDim.x) {
-      const int cl = e / chunks, ch = e - cl * chunks;
+      const int cl = e / chunks, k0 = (e - cl * chunks) * 8;
       const T* src = w_row<T>(p, p.col0 + cl);
-      T* dst = sW + cl * KS + ch * E16;
-      if (src) ld16(dst, src + ch * E16);
-      else *reinterpret_cast<uint4*>(dst) = make_uint4(0, 0, 0, 0);
-    }
-    if (p.mode == 0)
-      for (int k = tid; k < K; k += blockDim.x) {
-        sLn[k] = Tr<T>::to_f(static_cast<const T*>(p.ln_w)[k]);
-        sLn[kMaxK + k] = Tr<T>::to_f(static_cast<const T*>(p.ln_b)[k]);
+      T* dst = sW + cl * KS + k0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float wv = src ? Tr<T>::to_f(src[k0 + j]) : 0.f;
+        if (p.mode == 0) wv *= Tr<T>::to_f(lnw[k0 + j]);
+        dst[j] = Tr<T>::from_f(wv);
       }
+    }
+    // one column per wave: lanes split the K products, then a fixed-order
+    // butterfly sum (deterministic)
+    for (int cl = wave; cl < p.pass_cols; cl += WAVES) {
+      const int c = p.col0 + cl;
+      const T* src = w_row<T>(p, c);
+      float acc = 0.f;
+      if (src && p.mode == 0)
+        for (int k = lane; k < K; k += 64) acc += Tr<T>::to_f(lnb[k]) * Tr<T>::to_f(src[k]);
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) acc += shfl_xor(acc, o);
+      if (src && p.colbias) {
+        if (p.mode == 1) acc += Tr<T>::to_f(static_cast<const T*>(p.colbias)[c]);
+        else if (c >= 3 * p.HC && c < 4 * p.HC)
+          acc += Tr<T>::to_f(static_cast<const T*>(p.colbias)[c - 3 * p.HC]);
+      }
+      if (lane == 0) sC[cl] = acc;
+    }
   }
   __syncthreads();
 
   const T* X = static_cast<const T*>(p.x);
+  // Rows of position `pi` as loaded: channels 32s + 8g .. +7 in nx[s].
+  // Positions past the end read row 0 (finite; never stored).
+  auto load_rows = [&](Op (&nx)[2][KSTEPS], int tile) {
+#pragma unroll
+    for (int pb = 0; pb < 2; ++pb) {
+      const int64_t pi = (int64_t)tile * TP + wave * PW + pb * 16 + l16;
+      const int64_t row =
+          pi < p.npos ? (p.mode == 0 ? z_row(pi, p.N, p.ending) : pi) : 0;
+      const T* src = X + row * K + 8 * g;
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) nx[pb][s] = *reinterpret_cast<const Op*>(src + 32 * s);
+    }
+  };
+  // bf16: the next tile's rows are in flight during this tile (fp32 rows
+  // would not fit the register budget and are loaded at the tile's start)
+  constexpr bool PREFETCH = sizeof(T) == 2;
+  Op nx[2][KSTEPS];
+  if (PREFETCH && blockIdx.x < p.ntiles) load_rows(nx, blockIdx.x);
   for (int tile = blockIdx.x; tile < p.ntiles; tile += gridDim.x) {
+    if (!PREFETCH) load_rows(nx, tile);
     // ---- this wave's 32 rows, in B-operand layout: xf[pb][s] holds
     // channels 32s + 8g .. +7 of position base + pb*16 + l16.
     Op xf[2][KSTEPS];
-    int64_t pidx[2];
+    int64_t pidx[2], orow[2];
 #pragma unroll
     for (int pb = 0; pb < 2; ++pb) {
       pidx[pb] = (int64_t)tile * TP + wave * PW + pb * 16 + l16;
       const bool live = pidx[pb] < p.npos;
-      const int64_t row = live ? (p.mode == 0 ? z_row(pidx[pb], p.N, p.ending) : pidx[pb]) : 0;
-      const T* src = X + row * K + 8 * g;
-      float v[KSTEPS][8];
+      const int64_t zr = live ? z_row(pidx[pb], p.N, p.ending) : 0;
+      // output row offset: line layout (project) or z layout (out projection)
+      orow[pb] = p.mode == 0 ? pidx[pb] * p.HC : zr * p.ncols;
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) {
-        if (live) {
-          const Op f = *reinterpret_cast<const Op*>(src + 32 * s);
+      for (int s = 0; s < KSTEPS; ++s) xf[pb][s] = nx[pb][s];  // raw rows
+    }
+    if (PREFETCH && tile + (int)gridDim.x < p.ntiles) load_rows(nx, tile + gridDim.x);
 #pragma unroll
-          for (int j = 0; j < 8; ++j) v[s][j] = (float)f[j];
-        } else {
+    for (int pb = 0; pb < 2; ++pb) {
+      float v[1][KSTEPS][8];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) v[s][j] = 0.f;
-        }
-      }
+      for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[0][s][j] = (float)xf[pb][s][j];
       if (p.mode == 0) {
+        // two-pass statistics in fp32 (population variance), centred in place
         float sum = 0.f;
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s)
 #pragma unroll
-          for (int j = 0; j < 8; ++j) sum += v[s][j];
+          for (int j = 0; j < 8; ++j) sum += v[0][s][j];
         sum += shfl_xor(sum, 16);
         sum += shfl_xor(sum, 32);
         const float mu = sum / K;
@@ -165,8 +200,8 @@ rowgemm_kernel(GemmParams p) {
         for (int s = 0; s < KSTEPS; ++s)
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
-            const float d = v[s][j] - mu;
-            var += d * d;
+            v[0][s][j] -= mu;
+            var = __builtin_fmaf(v[0][s][j], v[0][s][j], var);
           }
         var += shfl_xor(var, 16);
         var += shfl_xor(var, 32);
@@ -174,18 +209,15 @@ rowgemm_kernel(GemmParams p) {
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s)
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int k = 32 * s + 8 * g + j;
-            v[s][j] = (v[s][j] - mu) * rstd * sLn[k] + sLn[kMaxK + k];
-          }
+          for (int j = 0; j < 8; ++j) v[0][s][j] *= rstd;
       }
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) {
         Op f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          if constexpr (sizeof(T) == 2) f[j] = (__bf16)v[s][j];
-          else f[j] = v[s][j];
+          if constexpr (sizeof(T) == 2) f[j] = (__bf16)v[0][s][j];
+          else f[j] = v[0][s][j];
         }
         xf[pb][s] = f;
       }
@@ -193,6 +225,10 @@ rowgemm_kernel(GemmParams p) {
 
     // ---- Y^T blocks of 16 output columns.
     for (int cb = 0; cb < p.pass_cols / 16; ++cb) {
+      // first column of the block: wave-uniform (output matrices are
+      // multiples of 16 columns wide, so a block never straddles two)
+      const int cblk = __builtin_amdgcn_readfirstlane(p.col0 + cb * 16);
+      if (cblk >= p.ncols) break;
       f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
       const T* wr = sW + (cb * 16 + l16) * KS + 8 * g;
 #pragma unroll
@@ -201,37 +237,22 @@ rowgemm_kernel(GemmParams p) {
         acc[0] = mma32(a, xf[0][s], acc[0]);
         acc[1] = mma32(a, xf[1][s], acc[1]);
       }
-      const int col = p.col0 + cb * 16 + 4 * g;   // this lane's 4 channels
-      if (col >= p.ncols) continue;
+      const f32x4 cc4 = *reinterpret_cast<const f32x4*>(sC + cb * 16 + 4 * g);
+      const int m = p.mode == 0 ? cblk / p.HC : 0;   // scalar
+      const int c = cblk - m * p.HC + 4 * g;        // column within output m
 #pragma unroll
       for (int pb = 0; pb < 2; ++pb) {
         if (pidx[pb] >= p.npos) continue;
-        f32x4 val = acc[pb];
+        const f32x4 val = acc[pb] + cc4;
         if (p.mode == 1) {
-          if (p.colbias) {
-            const T* cbp = static_cast<const T*>(p.colbias) + col;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) val[i] += Tr<T>::to_f(cbp[i]);
-          }
-          st4<T>(static_cast<T*>(p.y[0]) + z_row(pidx[pb], p.N, p.ending) * p.ncols + col, val);
+          st4<T>(static_cast<T*>(p.y[0]) + orow[pb] + c, val);
+        } else if (m < 4) {
+          st4<T>(static_cast<T*>(p.y[m]) + orow[pb] + c, val);
         } else {
-          const int m = col / p.HC;
-          if (m < 4) {
-            const int cc = col - m * p.HC;
-            if (m == 3 && p.colbias) {
-              const T* cbp = static_cast<const T*>(p.colbias) + cc;
+          T* bias = static_cast<T*>(p.y[4]);
 #pragma unroll
-              for (int i = 0; i < 4; ++i) val[i] += Tr<T>::to_f(cbp[i]);
-            }
-            st4<T>(static_cast<T*>(p.y[m]) + pidx[pb] * p.HC + cc, val);
-          } else {
-            T* bias = static_cast<T*>(p.y[4]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int hh = col - 4 * p.HC + i;
-              if (hh < p.H) bias[(int64_t)hh * p.npos + pidx[pb]] = Tr<T>::from_f(val[i]);
-            }
-          }
+          for (int i = 0; i < 4; ++i)
+            if (c + i < p.H) bias[(int64_t)(c + i) * p.npos + pidx[pb]] = Tr<T>::from_f(val[i]);
         }
       }
     }
@@ -255,15 +276,15 @@ hipError_t launch_pass(GemmParams& p, size_t lds, hipStream_t s) {
 
 template <typename T>
 hipError_t launch_gemm(GemmParams& p, hipStream_t s) {
-  const size_t row_bytes = (size_t)(p.K + PAD) * sizeof(T);
-  const size_t ln_bytes = 2 * kMaxK * sizeof(float);
-  int per_pass = (int)((kLdsBudget - ln_bytes) / row_bytes) / 16 * 16;
+  // LDS per output column: its weight row and its constant
+  const size_t row_bytes = (size_t)(p.K + PAD) * sizeof(T) + sizeof(float);
+  int per_pass = (int)(kLdsBudget / row_bytes) / 16 * 16;
   const int ncols_pad = (p.ncols + 15) / 16 * 16;
   per_pass = std::min(per_pass, ncols_pad);
   for (int c0 = 0; c0 < p.ncols; c0 += per_pass) {
     p.col0 = c0;
     p.pass_cols = std::min(per_pass, ncols_pad - c0);
-    const size_t lds = (size_t)p.pass_cols * row_bytes + ln_bytes;
+    const size_t lds = (size_t)p.pass_cols * row_bytes;
     hipError_t e;
     switch (p.K / 32) {
       case 1: e = launch_pass<T, 1>(p, lds, s); break;
