@@ -89,6 +89,45 @@ __device__ __forceinline__ void st4<float>(float* p, const f32x4& v) {
   *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
 }
 
+// Store two adjacent 16-column blocks A (columns 0..15) and B (16..31) of
+// one position row.  A lane of group g holds columns 4g..4g+3 of each; lanes
+// of groups g and g^1 (lanes l and l^16) swap halves so that an even-g lane
+// stores columns 4g..4g+7 of A and an odd-g lane columns 4(g-1)..4g+3 of B,
+// one contiguous 8-element chunk each: a wave's store then covers 16
+// positions x 64 contiguous bytes (bf16) instead of 16 x 32.  Every lane
+// takes part in the swap; `live` only gates the store.
+template <typename T>
+__device__ __forceinline__ void store_pair(T* row, const f32x4& a, const f32x4& b, int g,
+                                           bool live);
+template <>
+__device__ __forceinline__ void store_pair<bf16_t>(bf16_t* row, const f32x4& a, const f32x4& b,
+                                                   int g, bool live) {
+  auto pk = [](float x, float y) {
+    return uint32_t(Tr<bf16_t>::from_f(x)) | (uint32_t(Tr<bf16_t>::from_f(y)) << 16);
+  };
+  const uint32_t a0 = pk(a[0], a[1]), a1 = pk(a[2], a[3]);
+  const uint32_t b0 = pk(b[0], b[1]), b1 = pk(b[2], b[3]);
+  const bool odd = g & 1;
+  const uint32_t r0 = (uint32_t)__shfl_xor((int)(odd ? a0 : b0), 16, 64);
+  const uint32_t r1 = (uint32_t)__shfl_xor((int)(odd ? a1 : b1), 16, 64);
+  const u32x4 chunk = odd ? u32x4{r0, r1, b0, b1} : u32x4{a0, a1, r0, r1};
+  if (live) *reinterpret_cast<u32x4*>(row + (odd ? 16 + 4 * (g - 1) : 4 * g)) = chunk;
+}
+template <>
+__device__ __forceinline__ void store_pair<float>(float* row, const f32x4& a, const f32x4& b,
+                                                  int g, bool live) {
+  const bool odd = g & 1;
+  f32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = __shfl_xor(odd ? a[i] : b[i], 16, 64);
+  const f32x4 lo = odd ? r : a, hi = odd ? b : r;
+  if (live) {
+    float* dst = row + (odd ? 16 + 4 * (g - 1) : 4 * g);
+    *reinterpret_cast<f32x4*>(dst) = lo;
+    *reinterpret_cast<f32x4*>(dst + 4) = hi;
+  }
+}
+
 template <typename T, int KSTEPS, int WAVES = waves_for<KSTEPS>()>
 __global__ void __launch_bounds__(WAVES * 64)
 rowgemm_kernel(GemmParams p) {
@@ -223,38 +262,56 @@ rowgemm_kernel(GemmParams p) {
       }
     }
 
-    // ---- Y^T blocks of 16 output columns.
-    for (int cb = 0; cb < p.pass_cols / 16; ++cb) {
+    // ---- Y^T blocks of 16 output columns, two at a time where both belong
+    // to one output matrix (see store_pair).
+    const int nblk = p.pass_cols / 16;
+    for (int cb = 0; cb < nblk;) {
       // first column of the block: wave-uniform (output matrices are
       // multiples of 16 columns wide, so a block never straddles two)
       const int cblk = __builtin_amdgcn_readfirstlane(p.col0 + cb * 16);
       if (cblk >= p.ncols) break;
-      f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-      const T* wr = sW + (cb * 16 + l16) * KS + 8 * g;
+      const int m = p.mode == 0 ? cblk / p.HC : 0;  // scalar
+      const bool pair = cb + 1 < nblk && cblk + 16 < p.ncols &&
+                        (p.mode == 1 || (m < 4 && (cblk + 16) / p.HC == m));
+      f32x4 acc[2][2];  // [block][pb]
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) {
-        const Op a = *reinterpret_cast<const Op*>(wr + 32 * s);
-        acc[0] = mma32(a, xf[0][s], acc[0]);
-        acc[1] = mma32(a, xf[1][s], acc[1]);
+      for (int j = 0; j < 2; ++j) {
+        if (j == 1 && !pair) break;
+        acc[j][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+        acc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const T* wr = sW + ((cb + j) * 16 + l16) * KS + 8 * g;
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) {
+          const Op a = *reinterpret_cast<const Op*>(wr + 32 * s);
+          acc[j][0] = mma32(a, xf[0][s], acc[j][0]);
+          acc[j][1] = mma32(a, xf[1][s], acc[j][1]);
+        }
+        const f32x4 cc4 = *reinterpret_cast<const f32x4*>(sC + (cb + j) * 16 + 4 * g);
+        acc[j][0] += cc4;
+        acc[j][1] += cc4;
       }
-      const f32x4 cc4 = *reinterpret_cast<const f32x4*>(sC + cb * 16 + 4 * g);
-      const int m = p.mode == 0 ? cblk / p.HC : 0;   // scalar
-      const int c = cblk - m * p.HC + 4 * g;        // column within output m
+      const int cbase = cblk - m * p.HC;  // first column within output m
+      T* out = static_cast<T*>(p.y[p.mode == 1 ? 0 : (m < 4 ? m : 4)]);
+      if (pair) {
+#pragma unroll
+        for (int pb = 0; pb < 2; ++pb)
+          store_pair<T>(out + orow[pb] + cbase, acc[0][pb], acc[1][pb], g, pidx[pb] < p.npos);
+        cb += 2;
+        continue;
+      }
 #pragma unroll
       for (int pb = 0; pb < 2; ++pb) {
         if (pidx[pb] >= p.npos) continue;
-        const f32x4 val = acc[pb] + cc4;
-        if (p.mode == 1) {
-          st4<T>(static_cast<T*>(p.y[0]) + orow[pb] + c, val);
-        } else if (m < 4) {
-          st4<T>(static_cast<T*>(p.y[m]) + orow[pb] + c, val);
+        const int c = cbase + 4 * g;
+        if (p.mode == 1 || m < 4) {
+          st4<T>(out + orow[pb] + c, acc[0][pb]);
         } else {
-          T* bias = static_cast<T*>(p.y[4]);
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (c + i < p.H) bias[(int64_t)(c + i) * p.npos + pidx[pb]] = Tr<T>::from_f(val[i]);
+            if (c + i < p.H) out[(int64_t)(c + i) * p.npos + pidx[pb]] = Tr<T>::from_f(acc[0][pb][i]);
         }
       }
+      cb += 1;
     }
   }
 }
@@ -278,7 +335,7 @@ template <typename T>
 hipError_t launch_gemm(GemmParams& p, hipStream_t s) {
   // LDS per output column: its weight row and its constant
   const size_t row_bytes = (size_t)(p.K + PAD) * sizeof(T) + sizeof(float);
-  int per_pass = (int)(kLdsBudget / row_bytes) / 16 * 16;
+  int per_pass = (int)(kLdsBudget / row_bytes) / 32 * 32;  // whole block pairs
   const int ncols_pad = (p.ncols + 15) / 16 * 16;
   per_pass = std::min(per_pass, ncols_pad);
   for (int c0 = 0; c0 < p.ncols; c0 += per_pass) {
