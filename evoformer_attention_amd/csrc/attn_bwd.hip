@@ -43,6 +43,8 @@ namespace evo {
 namespace {
 
 constexpr int C = kHeadDim;
+constexpr float kSqrtC = 5.656854249492380f;  // sqrt(C)
+static_assert(C == 32, "kSqrtC is sqrt(32)");
 constexpr int kMaxKeysBwd = 1 << 16;
 constexpr int kTargetGroups = 1024;         // dbias workgroups wanted
 
@@ -51,7 +53,7 @@ int64_t pad128(int64_t n) { return (n + 127) / 128 * 128; }
 
 struct BwdLayout {
   int64_t Np, n_rg, rows_per_group;
-  size_t off_dopre, off_qt, off_dot, off_kt, off_lse2, off_d, off_bp, off_bpt,
+  size_t off_dopre, off_lse2, off_d, off_bp, off_bpt,
       off_dbpart, total;
 };
 
@@ -70,9 +72,6 @@ BwdLayout bwd_layout(int dtype, int64_t B, int64_t R, int64_t N, int64_t H) {
   const size_t lines = (size_t)B * R * H;
   size_t o = 0;
   L.off_dopre = o; o += a256((size_t)B * R * N * H * C * es);
-  L.off_qt = o;    o += a256(lines * C * L.Np * es);
-  L.off_dot = o;   o += a256(lines * C * L.Np * es);
-  L.off_kt = o;    o += a256(lines * C * L.Np * es);
   L.off_lse2 = o;  o += a256(lines * L.Np * 4);
   L.off_d = o;     o += a256(lines * L.Np * 4);
   L.off_bp = o;    o += a256((size_t)B * H * pad128(N) * L.Np * es);
@@ -83,12 +82,12 @@ BwdLayout bwd_layout(int dtype, int64_t B, int64_t R, int64_t N, int64_t H) {
   return L;
 }
 
-// Query held at slot s (0..31) of a 32-query step in the dK/dV kernel: the
+// Slot (0..31) of query q in a 32-query step of the dK/dV kernel: the
 // accumulator layout gives lane group g the queries 4g..4g+3 of each of the
-// two 16-query blocks, which become the 8 contraction slots 8g..8g+7.
-__device__ __forceinline__ int slot_query(int s) {
-  const int gg = s >> 3, j = s & 7;
-  return j < 4 ? 4 * gg + j : 16 + 4 * gg + (j - 4);
+// two 16-query blocks, which become the 8 contraction slots 8g..8g+7, so
+// query 4g + i sits at slot 8g + i and query 16 + 4g + i at slot 8g + 4 + i.
+__device__ __forceinline__ int query_slot(int q) {
+  return q < 16 ? 8 * (q >> 2) + (q & 3) : 8 * ((q - 16) >> 2) + 4 + (q & 3);
 }
 
 template <typename T>
@@ -135,7 +134,6 @@ struct BwdParams {
   const void* dout;
   void* dq; void* dk; void* dv; void* dgate; float* dbias;
   void* dopre;   // dO (= dout when there is no gate)
-  void* qt; void* dot; void* kt;
   float* lse2; float* dd; float* dbpart;
   void* bp; void* bpt;  // pair bias, natural units, masked, working dtype
   int B, R, N, H, Np, mask_rows, n_rg, rows_per_group, row_mask;
@@ -146,75 +144,90 @@ struct BwdParams {
 // Workgroup: one line (b, r), one head, 32 positions.  Thread: position
 // t/8, dims 4*(t%8)..+3.
 template <typename T>
+__device__ __forceinline__ void ld_chunk(const T* p, float (&v)[16 / sizeof(T)]) {
+  const u32x4 u = *reinterpret_cast<const u32x4*>(p);
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(u[i] << 16);
+      v[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(u[i]);
+  }
+}
+template <typename T>
+__device__ __forceinline__ void st_chunk(T* p, const float (&v)[16 / sizeof(T)]) {
+  u32x4 u;
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      u[i] = uint32_t(Tr<bf16_t>::from_f(v[2 * i])) |
+             (uint32_t(Tr<bf16_t>::from_f(v[2 * i + 1])) << 16);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u[i] = __float_as_uint(v[i]);
+  }
+  *reinterpret_cast<u32x4*>(p) = u;
+}
+
+// Elementwise pass over [B, R, N, H, C], one 16-byte chunk per thread (whole
+// position rows per wave, so every access is contiguous): dO = dOut*sigmoid(G),
+// dG = dOut*Out*(1 - sigmoid(G)), and per (line, head, position) the
+// base-2 LSE and -D, D = sum_c dOut*Out (a butterfly over the head's lanes).
+template <typename T>
 __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdParams p) {
-  __shared__ float sQ[32][33], sK[32][33], sO[32][33];
-  const int nblk = p.Np / 32;
-  int w = blockIdx.x;
-  const int nb = w % nblk; w /= nblk;
-  const int h = w % p.H;
-  const int line = w / p.H;  // b * R + r
-  const int t = threadIdx.x, n = t >> 3, c4 = (t & 7) * 4;
-  const int N = p.N, H = p.H;
-  const int pos = nb * 32 + n;
-  const int64_t e0 = ((int64_t)line * N + pos) * H * C + h * C + c4;
+  constexpr int E = 16 / sizeof(T);  // elements per chunk
+  constexpr int CPH = C / E;         // chunks per head
+  const int cpp = p.H * CPH;         // chunks per position
+  const int64_t total = (int64_t)p.B * p.R * p.N * cpp;
+  const int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const bool live = gi < total;
+  const int64_t pos = gi / cpp;      // (b*R + r)*N + n
+  const int ci = (int)(gi - pos * cpp);
+  const int64_t e0 = gi * E;         // chunks are contiguous in [.., H, C]
   float dsum = 0.f;
-  f32x4 qv{0.f, 0.f, 0.f, 0.f}, kv = qv, dov = qv;
-  if (pos < N) {
-    qv = ld4e(static_cast<const T*>(p.q) + e0);
-    kv = ld4e(static_cast<const T*>(p.k) + e0);
-    const f32x4 o = ld4e(static_cast<const T*>(p.out) + e0);
-    const f32x4 d = ld4e(static_cast<const T*>(p.dout) + e0);
+  if (live) {
+    float o[E], d[E];
+    ld_chunk<T>(static_cast<const T*>(p.out) + e0, o);
+    ld_chunk<T>(static_cast<const T*>(p.dout) + e0, d);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dsum += d[i] * o[i];
+    for (int i = 0; i < E; ++i) dsum += d[i] * o[i];
     if (p.gate) {
-      const f32x4 gv = ld4e(static_cast<const T*>(p.gate) + e0);
-      f32x4 dg;
+      float gv[E], dov[E], dg[E];
+      ld_chunk<T>(static_cast<const T*>(p.gate) + e0, gv);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < E; ++i) {
         const float sg = sigmoid_f(gv[i]);
         dov[i] = d[i] * sg;
         dg[i] = d[i] * o[i] * (1.f - sg);
       }
-      st4e(static_cast<T*>(p.dgate) + e0, dg);
-      st4e(static_cast<T*>(p.dopre) + e0, dov);
-    } else {
-      dov = d;
+      st_chunk<T>(static_cast<T*>(p.dgate) + e0, dg);
+      st_chunk<T>(static_cast<T*>(p.dopre) + e0, dov);
     }
   }
-  dsum += __shfl_xor(dsum, 1, 64);
-  dsum += __shfl_xor(dsum, 2, 64);
-  dsum += __shfl_xor(dsum, 4, 64);
-  const int64_t lh = (int64_t)line * H + h;  // line-head index
-  if ((t & 7) == 0) {
-    float l2 = INFINITY;  // padded or fully masked: P = exp2(-inf) = 0
-    if (pos < N) {
-      const float lse = p.lse[lh * N + pos];
-      if (lse != -INFINITY) l2 = lse * kLog2e;
-    }
-    p.lse2[lh * p.Np + pos] = l2;
-    p.dd[lh * p.Np + pos] = pos < N ? -dsum : 0.f;  // -D: the dP accumulator's start
-  }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    sQ[n][c4 + i] = qv[i];
-    sK[n][c4 + i] = kv[i];
-    sO[n][c4 + i] = dov[i];
+  for (int m = 1; m < CPH; m <<= 1) dsum += __shfl_xor(dsum, m, 64);
+  if (live && ci % CPH == 0) {
+    const int h = ci / CPH;
+    const int64_t line = pos / p.N;
+    const int n = (int)(pos - line * p.N);
+    const int64_t lh = line * p.H + h;  // line-head index
+    const float lse = p.lse[lh * p.N + n];
+    // fully masked query: P = exp2(-inf) = 0 everywhere
+    p.lse2[lh * p.Np + n] = lse == -INFINITY ? INFINITY : lse * kLog2e;
+    p.dd[lh * p.Np + n] = -dsum;  // -D: the dP accumulator's start
   }
-  __syncthreads();
-  // Transposed slabs: thread -> dim c = t/8, slots 4*(t%8)..+3.
-  const int c = t >> 3, s0 = (t & 7) * 4;
-  const int64_t to = (lh * C + c) * p.Np + nb * 32 + s0;
-  f32x4 a, b2, k2;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int qq = slot_query(s0 + i);
-    a[i] = sQ[qq][c];
-    b2[i] = sO[qq][c];
-    k2[i] = sK[s0 + i][c];
+  // padding queries n in [N, Np): P = 0, D = 0
+  const int npad = p.Np - p.N;
+  const int64_t pad_total = (int64_t)p.B * p.R * p.H * npad;
+  for (int64_t e = gi; e < pad_total; e += (int64_t)gridDim.x * 256) {
+    const int64_t lh = e / npad;
+    const int n = p.N + (int)(e - lh * npad);
+    p.lse2[lh * p.Np + n] = INFINITY;
+    p.dd[lh * p.Np + n] = 0.f;
   }
-  st4e(static_cast<T*>(p.qt) + to, a);
-  st4e(static_cast<T*>(p.dot) + to, b2);
-  st4e(static_cast<T*>(p.kt) + to, k2);
 }
 
 // Pair bias (natural units, working dtype) with the shared key mask and the
@@ -288,9 +301,9 @@ __global__ void __launch_bounds__(256) bwd_bias_kernel(BwdParams p) {
 // ----------------------------------------------------------------- dK, dV
 // Staged per 32-query step: Q rows, dO rows (row-major) and the slot-ordered
 // Q^T and dO^T slabs, each [32][32] (+pad); base-2 LSE and D.
-template <typename T> struct StageRaw;
-template <> struct StageRaw<bf16_t> { uint4 a, b; float l; };
-template <> struct StageRaw<float> { uint4 a0, a1, b0, b1; float l; };
+template <typename T> struct StageRaw;  // one 16-byte chunk (fp32: two)
+template <> struct StageRaw<bf16_t> { u32x4 a; float l; };
+template <> struct StageRaw<float> { u32x4 a, b; float l; };
 
 template <typename T, bool ROW_MASK>
 __global__ void __launch_bounds__(256) bwd_dkdv_kernel(BwdParams p) {
@@ -326,8 +339,6 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(BwdParams p) {
   const T* V = static_cast<const T*>(p.v);
   const T* Q = static_cast<const T*>(p.q);
   const T* DO = static_cast<const T*>(p.dopre);
-  const T* QT = static_cast<const T*>(p.qt) + lh * C * Np;
-  const T* DT = static_cast<const T*>(p.dot) + lh * C * Np;
   // This lane's bias^T operands of step st: 16 values at BPT + st * 4096
   // (prepared block order: [qb][kb][i]).
   const T* BPT = static_cast<const T*>(p.bpt) +
@@ -359,45 +370,41 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(BwdParams p) {
       dv[cb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-  // Staging map: thread -> (tile pair, row, 8-element chunk).
-  const int srow = (tid >> 2) & 31, sch = tid & 3, spair = tid >> 7;  // pair 0: Q,dO  1: Qt,dOt
+  // Staging: thread -> (tensor: Q or dO, query row, 8-dim chunk).  Each
+  // 32-query step is stored twice in LDS from the same registers: row-major
+  // (the S and dP operands) and transposed with the queries in slot order
+  // (the dV and dK operands).  Queries past N read query N-1 (finite; their
+  // P and dS are 0).
+  const int srow = (tid >> 2) & 31, sch = tid & 3, sten = tid >> 7;
+  const T* ssrc = (sten == 0 ? Q : DO) + lbase + sch * 8;
+  const int sslot = query_slot(srow);
   auto fetch = [&](StageRaw<T>& raw, int q0) {
-    const T* s0;
-    const T* s1;
-    bool ok = true;
-    if (spair == 0) {
-      ok = q0 + srow < N;
-      s0 = Q + lbase + (int64_t)min(q0 + srow, N - 1) * pos_stride + sch * 8;
-      s1 = DO + lbase + (int64_t)min(q0 + srow, N - 1) * pos_stride + sch * 8;
-    } else {
-      s0 = QT + (int64_t)srow * Np + q0 + sch * 8;
-      s1 = DT + (int64_t)srow * Np + q0 + sch * 8;
-    }
-    if constexpr (sizeof(T) == 2) {
-      raw.a = *reinterpret_cast<const uint4*>(s0);
-      raw.b = *reinterpret_cast<const uint4*>(s1);
-      if (!ok) { raw.a = make_uint4(0, 0, 0, 0); raw.b = raw.a; }
-    } else {
-      raw.a0 = reinterpret_cast<const uint4*>(s0)[0];
-      raw.a1 = reinterpret_cast<const uint4*>(s0)[1];
-      raw.b0 = reinterpret_cast<const uint4*>(s1)[0];
-      raw.b1 = reinterpret_cast<const uint4*>(s1)[1];
-      if (!ok) { raw.a0 = make_uint4(0, 0, 0, 0); raw.a1 = raw.a0; raw.b0 = raw.a0; raw.b1 = raw.a0; }
-    }
+    const T* src = ssrc + (int64_t)min(q0 + srow, N - 1) * pos_stride;
+    raw.a = reinterpret_cast<const u32x4*>(src)[0];
+    if constexpr (sizeof(T) == 4) raw.b = reinterpret_cast<const u32x4*>(src)[1];
     raw.l = (tid < 64) ? (tid < 32 ? p.lse2[lh * Np + q0 + tid] : p.dd[lh * Np + q0 + tid - 32])
                        : 0.f;
   };
   auto store = [&](const StageRaw<T>& raw, int buf) {
-    T* d0 = sT[buf][2 * spair] + srow * RS + sch * 8;
-    T* d1 = sT[buf][2 * spair + 1] + srow * RS + sch * 8;
+    T* drow = sT[buf][sten] + srow * RS + sch * 8;
+    T* dcol = sT[buf][2 + sten] + (sch * 8) * RS + sslot;
     if constexpr (sizeof(T) == 2) {
-      *reinterpret_cast<uint4*>(d0) = raw.a;
-      *reinterpret_cast<uint4*>(d1) = raw.b;
+      *reinterpret_cast<u32x4*>(drow) = raw.a;
+      uint16_t* d16 = reinterpret_cast<uint16_t*>(dcol);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        d16[(2 * j) * RS] = (uint16_t)(raw.a[j] & 0xffffu);
+        d16[(2 * j + 1) * RS] = (uint16_t)(raw.a[j] >> 16);
+      }
     } else {
-      reinterpret_cast<uint4*>(d0)[0] = raw.a0;
-      reinterpret_cast<uint4*>(d0)[1] = raw.a1;
-      reinterpret_cast<uint4*>(d1)[0] = raw.b0;
-      reinterpret_cast<uint4*>(d1)[1] = raw.b1;
+      reinterpret_cast<u32x4*>(drow)[0] = raw.a;
+      reinterpret_cast<u32x4*>(drow)[1] = raw.b;
+      uint32_t* d32 = reinterpret_cast<uint32_t*>(dcol);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        d32[j * RS] = raw.a[j];
+        d32[(4 + j) * RS] = raw.b[j];
+      }
     }
     if (tid < 64) sL[buf][tid >> 5][tid & 31] = raw.l;
   };
@@ -497,28 +504,50 @@ __device__ __forceinline__ int k_lds_row(int p) {
 }
 
 // One thread's share of a 64-key tile, held in plain locals (16-byte
-// chunks; fp32 needs two per tensor): key t/4, dims 8*(t%4)..+7 of K and V,
-// and row t/8, keys 8*(t%8)..+7 of the K^T slab.
-#define EVO_FETCH_K(T, K_, V_, KT_, k0_)                                          \
+// chunks; fp32 needs two per tensor): key t/4, dims 8*(t%4)..+7 of K and V.
+// Keys past N read key N-1 (finite; their dS is 0).
+#define EVO_FETCH_K(T, K_, V_, k0_)                                               \
   do {                                                                        \
     const int t_ = threadIdx.x;                                               \
     const int kk_ = min((k0_) + (t_ >> 2), N - 1), ch_ = t_ & 3;              \
-    const uint4* ks_ = reinterpret_cast<const uint4*>((K_) + (int64_t)kk_ * pos_stride + ch_ * 8); \
-    const uint4* vs_ = reinterpret_cast<const uint4*>((V_) + (int64_t)kk_ * pos_stride + ch_ * 8); \
-    const uint4* ts_ = reinterpret_cast<const uint4*>((KT_) + (int64_t)(t_ >> 3) * Np + (k0_) + (t_ & 7) * 8); \
-    rk0 = ks_[0]; rv0 = vs_[0]; rt0 = ts_[0];                                  \
-    if constexpr (sizeof(T) == 4) { rk1 = ks_[1]; rv1 = vs_[1]; rt1 = ts_[1]; } \
+    const u32x4* ks_ = reinterpret_cast<const u32x4*>((K_) + (int64_t)kk_ * pos_stride + ch_ * 8); \
+    const u32x4* vs_ = reinterpret_cast<const u32x4*>((V_) + (int64_t)kk_ * pos_stride + ch_ * 8); \
+    rk0 = ks_[0]; rv0 = vs_[0];                                               \
+    if constexpr (sizeof(T) == 4) { rk1 = ks_[1]; rv1 = vs_[1]; }             \
   } while (0)
 
+// K and V rows key-permuted (the S and dP operands) and K transposed, keys
+// in physical order (the dQ operand); bf16 columns swizzled by kt_col.
 #define EVO_STORE_K(T, sK_, sV_, sKt_, KS_, TS_)                                  \
   do {                                                                        \
-    const int t_ = threadIdx.x;                                               \
-    uint4* dk_ = reinterpret_cast<uint4*>((sK_) + k_lds_row(t_ >> 2) * (KS_) + (t_ & 3) * 8); \
-    uint4* dv_ = reinterpret_cast<uint4*>((sV_) + k_lds_row(t_ >> 2) * (KS_) + (t_ & 3) * 8); \
-    uint4* dt_ = reinterpret_cast<uint4*>((sKt_) + (t_ >> 3) * (TS_) + (t_ & 7) * 8); \
-    dk_[0] = rk0; dv_[0] = rv0; dt_[0] = rt0;                                  \
-    if constexpr (sizeof(T) == 4) { dk_[1] = rk1; dv_[1] = rv1; dt_[1] = rt1; } \
+    const int t_ = threadIdx.x, kk_ = t_ >> 2, ch_ = t_ & 3;                  \
+    u32x4* dk_ = reinterpret_cast<u32x4*>((sK_) + k_lds_row(kk_) * (KS_) + ch_ * 8); \
+    u32x4* dv_ = reinterpret_cast<u32x4*>((sV_) + k_lds_row(kk_) * (KS_) + ch_ * 8); \
+    dk_[0] = rk0; dv_[0] = rv0;                                               \
+    if constexpr (sizeof(T) == 4) {                                           \
+      dk_[1] = rk1; dv_[1] = rv1;                                             \
+      uint32_t* dt_ = reinterpret_cast<uint32_t*>(sKt_) + (ch_ * 8) * (TS_) + kk_; \
+      for (int j_ = 0; j_ < 4; ++j_) {                                        \
+        dt_[j_ * (TS_)] = rk0[j_];                                            \
+        dt_[(4 + j_) * (TS_)] = rk1[j_];                                      \
+      }                                                                       \
+    } else {                                                                  \
+      uint16_t* dt_ = reinterpret_cast<uint16_t*>(sKt_) + (ch_ * 8) * (TS_) + (kk_ ^ (16 * ch_)); \
+      for (int j_ = 0; j_ < 4; ++j_) {                                        \
+        dt_[(2 * j_) * (TS_)] = (uint16_t)(rk0[j_] & 0xffffu);                \
+        dt_[(2 * j_ + 1) * (TS_)] = (uint16_t)(rk0[j_] >> 16);                \
+      }                                                                       \
+    }                                                                         \
   } while (0)
+
+// Column of key chunk c (a multiple of 8) in row `row` of the transposed K
+// tile: bf16 rows are swizzled by 16 * (row / 8 mod 4), which spreads the
+// transposed 16-bit stores of the four dim groups of a key over different
+// banks while keeping every 8-key chunk one 16-byte read.
+template <typename T>
+__device__ __forceinline__ int kt_col(int row, int c) {
+  return sizeof(T) == 2 ? (c ^ (16 * ((row >> 3) & 3))) : c;
+}
 
 template <typename T> struct BLds;
 template <> struct BLds<bf16_t> { static constexpr int KS = 40, TS = 72; };
@@ -555,7 +584,6 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdParams p) {
   const int qw0 = qt * 128 + wave * 32;
   const T* K = static_cast<const T*>(p.k) + lbase;
   const T* V = static_cast<const T*>(p.v) + lbase;
-  const T* KT = static_cast<const T*>(p.kt) + lh * C * Np;
   const uint8_t* mrow = ROW_MASK ? p.mask + ((int64_t)b * p.mask_rows + r) * N : nullptr;
 
   Op qf[2], df[2];
@@ -581,9 +609,9 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) dq[qb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  uint4 rk0, rk1, rv0, rv1, rt0, rt1;
-  rk1 = rv1 = rt1 = make_uint4(0, 0, 0, 0);
-  EVO_FETCH_K(T, K, V, KT, 0);
+  u32x4 rk0, rk1, rv0, rv1;
+  rk1 = rv1 = u32x4{0, 0, 0, 0};
+  EVO_FETCH_K(T, K, V, 0);
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
@@ -599,7 +627,7 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int half = 0; half < 2; ++half) widen8(bn[qb][half], cb_[qb][half][0], cb_[qb][half][1]);
     // next tile (the last iteration re-fetches its own tile, unused)
-    EVO_FETCH_K(T, K, V, KT, min(k0 + 64, (ntiles - 1) * 64));
+    EVO_FETCH_K(T, K, V, min(k0 + 64, (ntiles - 1) * 64));
     {
       const int nt = min(tile + 1, ntiles - 1);
 #pragma unroll
@@ -646,7 +674,8 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdParams p) {
       }
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
-        const Op ktf = *reinterpret_cast<const Op*>(sKt[buf] + (cb * 16 + l16) * TS + half * 32 + 8 * g);
+        const Op ktf = *reinterpret_cast<const Op*>(
+            sKt[buf] + (cb * 16 + l16) * TS + kt_col<T>(cb * 16 + l16, half * 32 + 8 * g));
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
           dq[qb][cb] = mma32(ktf, pack8(dp[qb][0], dp[qb][1], (Op*)nullptr), dq[qb][cb]);
@@ -712,10 +741,15 @@ __global__ void __launch_bounds__(256) bwd_dbias_kernel(BwdParams p) {
         Raw8<T> r;
         ld_raw8(r, bt + (qb * 2 + half) * 512);
         widen8(r, cbias[half][qb][0], cbias[half][qb][1]);
+        // the logit accumulators hold <Q,K> + bias*sqrt(C) (unscaled Q);
+        // 1/sqrt(C) is applied in the exponent
+        cbias[half][qb][0] *= kSqrtC;
+        cbias[half][qb][1] *= kSqrtC;
         db[half][qb][0] = f32x4{0.f, 0.f, 0.f, 0.f};
         db[half][qb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
   }
+  const float sc = p.qscale * kLog2e;
   const int r_begin = rg * p.rows_per_group;
   const int r_end = min(R, r_begin + p.rows_per_group);
   // thread t stages key t/4 (dims 8*(t%4)..+7) of K and V for one row;
@@ -726,26 +760,36 @@ __global__ void __launch_bounds__(256) bwd_dbias_kernel(BwdParams p) {
   rk1 = rv1 = make_uint4(0, 0, 0, 0);
   Op qn0, qn1, dn0, dn1;
   float l2n0, l2n1, ddn0, ddn1;
+  // Per-lane addresses in row r_begin; row r is `r - r_begin` line strides on.
+  const int64_t lstride = (int64_t)N * pos_stride;       // one line of [.., N, H, C]
+  const int64_t l0 = ((int64_t)b * R + r_begin) * lstride + h * C;
+  const int qa = qw0 + l16, qbq = qw0 + 16 + l16;
+  const T* kp = static_cast<const T*>(p.k) + l0 + (int64_t)kk * pos_stride + ch * 8;
+  const T* vp = static_cast<const T*>(p.v) + l0 + (int64_t)kk * pos_stride + ch * 8;
+  const T* qp0 = static_cast<const T*>(p.q) + l0 + (int64_t)min(qa, N - 1) * pos_stride + 8 * g;
+  const T* qp1 = static_cast<const T*>(p.q) + l0 + (int64_t)min(qbq, N - 1) * pos_stride + 8 * g;
+  const T* op0 = static_cast<const T*>(p.dopre) + l0 + (int64_t)min(qa, N - 1) * pos_stride + 8 * g;
+  const T* op1 = static_cast<const T*>(p.dopre) + l0 + (int64_t)min(qbq, N - 1) * pos_stride + 8 * g;
+  const int64_t lh0 = ((int64_t)b * R + r_begin) * H + h;
+  const float* lp = p.lse2 + lh0 * Np;
+  const float* dq_ = p.dd + lh0 * Np;
+  const int64_t hstride = (int64_t)H * Np;                // one line of [.., H, Np]
 #define EVO_FETCH_ROW(r_)                                                          \
   do {                                                                         \
-    const int64_t line_ = (int64_t)b * R + (r_);                               \
-    const int64_t lb_ = line_ * N * pos_stride + h * C;                        \
-    const int64_t lh_ = line_ * H + h;                                         \
-    const uint4* ks_ = reinterpret_cast<const uint4*>(                         \
-        static_cast<const T*>(p.k) + lb_ + (int64_t)kk * pos_stride + ch * 8); \
-    const uint4* vs_ = reinterpret_cast<const uint4*>(                         \
-        static_cast<const T*>(p.v) + lb_ + (int64_t)kk * pos_stride + ch * 8); \
+    const int64_t ro_ = (int64_t)((r_) - r_begin);                             \
+    const int64_t lo_ = ro_ * lstride, ho_ = ro_ * hstride;                     \
+    const uint4* ks_ = reinterpret_cast<const uint4*>(kp + lo_);               \
+    const uint4* vs_ = reinterpret_cast<const uint4*>(vp + lo_);               \
     rk0 = ks_[0]; rv0 = vs_[0];                                                \
     if constexpr (sizeof(T) == 4) { rk1 = ks_[1]; rv1 = vs_[1]; }              \
-    const int qa_ = qw0 + l16, qb_ = qw0 + 16 + l16;                           \
-    qn0 = ldop<T>(static_cast<const T*>(p.q) + lb_ + (int64_t)min(qa_, N - 1) * pos_stride + 8 * g); \
-    qn1 = ldop<T>(static_cast<const T*>(p.q) + lb_ + (int64_t)min(qb_, N - 1) * pos_stride + 8 * g); \
-    dn0 = ldop<T>(static_cast<const T*>(p.dopre) + lb_ + (int64_t)min(qa_, N - 1) * pos_stride + 8 * g); \
-    dn1 = ldop<T>(static_cast<const T*>(p.dopre) + lb_ + (int64_t)min(qb_, N - 1) * pos_stride + 8 * g); \
-    l2n0 = qa_ < N ? p.lse2[lh_ * Np + qa_] : INFINITY;                        \
-    l2n1 = qb_ < N ? p.lse2[lh_ * Np + qb_] : INFINITY;                        \
-    ddn0 = qa_ < N ? p.dd[lh_ * Np + qa_] : 0.f;                               \
-    ddn1 = qb_ < N ? p.dd[lh_ * Np + qb_] : 0.f;                               \
+    qn0 = ldop<T>(qp0 + lo_);                                                  \
+    qn1 = ldop<T>(qp1 + lo_);                                                  \
+    dn0 = ldop<T>(op0 + lo_);                                                  \
+    dn1 = ldop<T>(op1 + lo_);                                                  \
+    l2n0 = qa < N ? lp[ho_ + qa] : INFINITY;                                   \
+    l2n1 = qbq < N ? lp[ho_ + qbq] : INFINITY;                                 \
+    ddn0 = qa < N ? dq_[ho_ + qa] : 0.f;                                       \
+    ddn1 = qbq < N ? dq_[ho_ + qbq] : 0.f;                                     \
   } while (0)
   if (r_begin < r_end) EVO_FETCH_ROW(r_begin);
   for (int r = r_begin; r < r_end; ++r) {
@@ -761,7 +805,7 @@ __global__ void __launch_bounds__(256) bwd_dbias_kernel(BwdParams p) {
         dv[1] = rv1;
       }
     }
-    const Op qf[2] = {scale8(qn0, p.qscale), scale8(qn1, p.qscale)};
+    const Op qf[2] = {qn0, qn1};
     const Op df[2] = {dn0, dn1};
     const float l2[2] = {l2n0, l2n1};
     const float dd[2] = {ddn0, ddn1};
@@ -796,7 +840,7 @@ __global__ void __launch_bounds__(256) bwd_dbias_kernel(BwdParams p) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const float pv =
-                dead[i] ? 0.f : exp2_fast(__builtin_fmaf(s[qb][i], kLog2e, -l2[qb]));
+                dead[i] ? 0.f : exp2_fast(__builtin_fmaf(s[qb][i], sc, -l2[qb]));
             db[half][qb][kb][i] += pv * dp[qb][i];
           }
       }
@@ -845,9 +889,11 @@ __global__ void __launch_bounds__(256) bwd_dbias_reduce_kernel(BwdParams p) {
 template <typename T>
 hipError_t launch_t(BwdParams& p, hipStream_t s) {
   const int64_t lines = (int64_t)p.B * p.R;
-  const int nblk = p.Np / 32;
-  hipLaunchKernelGGL(bwd_prep_kernel<T>, dim3((unsigned)(lines * p.H * nblk)), dim3(256), 0,
-                     s, p);
+  {
+    const int64_t chunks = lines * p.N * p.H * (C * (int64_t)sizeof(T) / 16);
+    hipLaunchKernelGGL(bwd_prep_kernel<T>, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0,
+                       s, p);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   {
@@ -908,9 +954,6 @@ hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t s) {
   p.bias = a.bias; p.out = a.out; p.lse = a.lse; p.dout = a.dout;
   p.dq = a.dq; p.dk = a.dk; p.dv = a.dv; p.dgate = a.dgate; p.dbias = a.dbias;
   p.dopre = a.gate ? (void*)(ws + L.off_dopre) : const_cast<void*>(a.dout);
-  p.qt = ws + L.off_qt;
-  p.dot = ws + L.off_dot;
-  p.kt = ws + L.off_kt;
   p.lse2 = reinterpret_cast<float*>(ws + L.off_lse2);
   p.dd = reinterpret_cast<float*>(ws + L.off_d);
   p.bp = ws + L.off_bp;
