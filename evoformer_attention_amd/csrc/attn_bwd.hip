@@ -46,7 +46,7 @@ constexpr int C = kHeadDim;
 constexpr float kSqrtC = 5.656854249492380f;  // sqrt(C)
 static_assert(C == 32, "kSqrtC is sqrt(32)");
 constexpr int kMaxKeysBwd = 1 << 16;
-constexpr int kTargetGroups = 1024;         // dbias workgroups wanted
+constexpr int kTargetGroups = 2048;         // dbias workgroups wanted
 
 int64_t pad64(int64_t n) { return (n + 63) / 64 * 64; }
 int64_t pad128(int64_t n) { return (n + 127) / 128 * 128; }
