@@ -11,20 +11,20 @@
 // item 1).
 //
 // Kernels.
-//   bias_prep  writes the pair bias once per call, in the working dtype, as
-//              [B, H, Nq, Nk] (Nq, Nk padded to the tile sizes) with the
-//              shared key mask and the padding keys folded in as -inf, so the
-//              main loop needs no bounds or mask logic: each lane widens its
-//              8 consecutive keys straight into the matrix-core accumulator
-//              operand.  (Kept in bf16 for bf16 inputs: the bias tile is
-//              re-read by every group of lines, and at 2 bytes per element a
-//              head's bias stays resident in one XCD's L2.)
-//   attn_fwd   a workgroup (4 waves) owns 128 queries of one head and ROWS
-//              lines of one batch entry; each wave owns 32 queries.  Keys
-//              stream in tiles of 64 through double-buffered LDS, the next
-//              tile's K, V and bias being fetched into registers while the
-//              current one is computed (one barrier per tile).  The bias tile
-//              is loaded once per workgroup and used for all ROWS lines.
+//   bias_prep  writes the pair bias once per call, in the working dtype,
+//              with the shared key mask and the padding keys folded in as
+//              -inf, so the main loop needs no bounds or mask logic.  It is
+//              stored in the main kernel's fragment order (see the prep
+//              kernel): each wave's bias load is one contiguous 1 KB block,
+//              which each lane widens into matrix-core accumulator operands.
+//   attn_fwd   a workgroup (4 waves) owns 128 queries of one head and one
+//              line (ROWS = 1; the kernel is written for ROWS lines sharing
+//              the bias tile); each wave owns 32 queries.  Keys stream in
+//              tiles of 64 through double-buffered LDS, the next tile's K, V
+//              and bias being fetched into registers while the current one is
+//              computed (one barrier per tile); each tile is processed as two
+//              32-key halves (logits, softmax, PV), which keeps the kernel at
+//              ~120 registers per lane: four waves per SIMD.
 //
 // Matrix-core mapping (v_mfma_f32_16x16x32_bf16, fp32 accumulate):
 //   S^T = K . (Q/sqrt(C))^T + bias^T   A = 16 keys x 32 dims (LDS), B = Q^T
@@ -38,14 +38,15 @@
 // operand is one 16-byte LDS read.
 //
 // Softmax with a lazy reference.  p = exp2(S*log2(e) - m) uses a per-query
-// reference m (base 2) that is only raised when needed: the first tile (and
-// any tile while a query has seen no live key) computes the true maximum; a
-// later tile is recomputed with a raised reference only if a lane's sum of p
-// over the tile exceeds 2^8.  So every p <= 2^8 (no overflow in fp32 or
-// bf16), m never exceeds the true maximum (no underflow of the result), and
-// the common tile costs one FMA, one exp and one add per logit with no
-// cross-lane reduction.  The result is exact up to rounding for any m, since
-// O and l are scaled by the same exp2(-m).
+// reference m (base 2) that is only raised when needed: the first half-tile
+// (and any half while a query has seen no live key) computes the true
+// maximum; a later half is recomputed with a raised reference only if a
+// lane's sum of p over it exceeds 2^8.  So every p <= 2^8 (no overflow in
+// fp32 or bf16), m never exceeds the true maximum (no underflow of the
+// result), and the common half costs one FMA and one exp per logit plus a
+// dot2 per two for the row sum, with no cross-lane reduction.  The result is
+// exact up to rounding for any m, since O and l are scaled by the same
+// exp2(-m).
 #include <algorithm>
 
 #include "evo_device.h"
@@ -250,27 +251,27 @@ __global__ void __launch_bounds__(256) fwd_bias_prep_kernel(
   }
 }
 
-#define EVO_FWD_QK()                                                             \
+// Logits of one 32-key half `hf_` of the tile, all lines of the group:
+// s[rr][qb][kb] = K . (Q/sqrt(C))^T + bias^T.
+#define EVO_FWD_QK(hf_)                                                          \
   do {                                                                           \
     for (int rr = 0; rr < ROWS; ++rr)                                            \
-      for (int half = 0; half < 2; ++half)                                       \
-        for (int kb = 0; kb < 2; ++kb) {                                         \
-          const Op kf = ld8(sK[buf][rr] + (half * 32 + kb * 16 + l16) * KST + 8 * g); \
-          for (int qb = 0; qb < 2; ++qb)                                         \
-            s[rr][qb][half][kb] = mma32(kf, qf[rr][qb], bt[qb][half][kb]);       \
-        }                                                                        \
+      for (int kb = 0; kb < 2; ++kb) {                                           \
+        const Op kf = ld8(sK[buf][rr] + ((hf_) * 32 + kb * 16 + l16) * KST + 8 * g); \
+        for (int qb = 0; qb < 2; ++qb)                                           \
+          s[rr][qb][kb] = mma32(kf, qf[rr][qb], bt[qb][kb]);                     \
+      }                                                                          \
     if constexpr (ROW_MASK) {                                                    \
-      for (int rr = 0; rr < ROWS; ++rr)                                          \
-        for (int half = 0; half < 2; ++half) {                                   \
-          const int kbase = k0 + half * 32 + 8 * g;                              \
-          for (int j = 0; j < 8; ++j) {                                          \
-            const bool dead = kbase + j < N && mrow[rr][kbase + j] == 0;         \
-            if (dead) {                                                          \
-              s[rr][0][half][j >> 2][j & 3] = -INFINITY;                         \
-              s[rr][1][half][j >> 2][j & 3] = -INFINITY;                         \
-            }                                                                    \
+      for (int rr = 0; rr < ROWS; ++rr) {                                        \
+        const int kbase = k0 + (hf_) * 32 + 8 * g;                               \
+        for (int j = 0; j < 8; ++j) {                                            \
+          const bool dead = kbase + j < N && mrow[rr][kbase + j] == 0;           \
+          if (dead) {                                                            \
+            s[rr][0][j >> 2][j & 3] = -INFINITY;                                 \
+            s[rr][1][j >> 2][j & 3] = -INFINITY;                                 \
           }                                                                      \
         }                                                                        \
+      }                                                                          \
     }                                                                            \
   } while (0)
 
@@ -383,127 +384,114 @@ attn_fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int rr = 0; rr < ROWS; ++rr) store_kv<T>(raw[rr], sK[buf][rr], sV[buf][rr]);
     __syncthreads();
-    // This tile's bias operands in accumulator layout: [qb][half][kb].
-    f32x4 bt[2][2][2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        if constexpr (HAS_BIAS) {
-          widen8(braw[qb][half], bt[qb][half][0], bt[qb][half][1]);
-        } else {
-          // no bias and no shared mask: 0, padding keys -inf
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              bt[qb][half][kb][i] =
-                  (k0 + half * 32 + 8 * g + 4 * kb + i < N) ? 0.f : -INFINITY;
-        }
-      }
     if (tile + 1 < ntiles) {
 #pragma unroll
       for (int rr = 0; rr < ROWS; ++rr)
         fetch_kv<T>(raw[rr], kline[rr], vline[rr], k0 + BK, N, pos_stride);
     }
 
-    // All lines of the group go through each phase together (one basic
-    // block per phase), so the matrix-core work of one line overlaps the
-    // softmax of the other.
-    f32x4 s[ROWS][2][2][2];  // [rr][qb][half][kb]: logits, then p in place
-    EVO_FWD_QK();
+    // The tile in two 32-key halves: logits, softmax and PV of one half
+    // before the next (half the logit and P registers of a whole tile).  All
+    // lines of the group go through each phase together, so the matrix-core
+    // work of one line overlaps the softmax of the other.
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      // this half's bias operands in accumulator layout: [qb][kb]
+      f32x4 bt[2][2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        if constexpr (HAS_BIAS) {
+          widen8(braw[qb][hf], bt[qb][0], bt[qb][1]);
+        } else {
+          // no bias and no shared mask: 0, padding keys -inf
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              bt[qb][kb][i] = (k0 + hf * 32 + 8 * g + 4 * kb + i < N) ? 0.f : -INFINITY;
+        }
+      }
+      f32x4 s[ROWS][2][2];  // [rr][qb][kb]
+      EVO_FWD_QK(hf);
 
-    // p = exp2(s*log2e - m), rounded to the operand type at once: P^T is
-    // kept as matrix-core operands (half the registers of fp32 logits) and
-    // the row sums are taken over exactly the rounded values the PV product
-    // uses.  Fast path: the current reference.  The first tile always takes
-    // the exact maximum.
-    Op pf[ROWS][2][2];  // [rr][qb][half]
-    float psum[ROWS][2];
-    bool slow = tile == 0;
-    if (!slow) {
-      bool redo = false;
+      // p = exp2(s*log2e - m), rounded to the operand type at once: P^T is
+      // kept as matrix-core operands and the row sums are taken over
+      // exactly the rounded values the PV product uses.  Fast path: the
+      // current reference; the first half of the first tile always takes
+      // the exact maximum.
+      Op pf[ROWS][2];  // [rr][qb]
+      float psum[ROWS][2];
+      bool slow = tile == 0 && hf == 0;
+      if (!slow) {
+        bool redo = false;
 #pragma unroll
-      for (int rr = 0; rr < ROWS; ++rr)
+        for (int rr = 0; rr < ROWS; ++rr)
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          const float nm = -m[rr][qb];
-          float acc = 0.f;
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
+          for (int qb = 0; qb < 2; ++qb) {
+            const float nm = -m[rr][qb];
             f32x4 e[2];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
               for (int i = 0; i < 4; ++i)
-                e[kb][i] = exp2_fast(__builtin_fmaf(s[rr][qb][half][kb][i], kLog2e, nm));
-            pf[rr][qb][half] = pack8(e[0], e[1], (Op*)nullptr);
-            acc = sum8(pf[rr][qb][half], acc);
+                e[kb][i] = exp2_fast(__builtin_fmaf(s[rr][qb][kb][i], kLog2e, nm));
+            pf[rr][qb] = pack8(e[0], e[1], (Op*)nullptr);
+            psum[rr][qb] = sum8(pf[rr][qb], 0.f);
+            // not yet anchored (m = -inf gives inf or NaN), or too large
+            redo |= !(psum[rr][qb] <= kHeadroom);
           }
-          psum[rr][qb] = acc;
-          // not yet anchored (m = -inf gives inf or NaN), or too large
-          redo |= !(acc <= kHeadroom);
-        }
-      slow = __builtin_amdgcn_ballot_w64(redo) != 0;
-      if (slow) EVO_FWD_QK();  // the logits again, for the exact path
-    }
-    if (slow) {
-      // Raise the reference to the tile maximum where needed.
+        slow = __builtin_amdgcn_ballot_w64(redo) != 0;
+        if (slow) EVO_FWD_QK(hf);  // the logits again, for the exact path
+      }
+      if (slow) {
+        // Raise the reference to the half's maximum where needed.
 #pragma unroll
-      for (int rr = 0; rr < ROWS; ++rr)
+        for (int rr = 0; rr < ROWS; ++rr)
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          float mx = -INFINITY;
-#pragma unroll
-          for (int half = 0; half < 2; ++half)
+          for (int qb = 0; qb < 2; ++qb) {
+            float mx = -INFINITY;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-              for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[rr][qb][half][kb][i]);
-          mx = fmaxf(mx, shfl_xor(mx, 16));
-          mx = fmaxf(mx, shfl_xor(mx, 32));
-          const float mold = m[rr][qb];
-          const float mnew = fmaxf(mold, mx * kLog2e);
-          const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-          const float alpha = (mold == -INFINITY) ? 0.f : exp2_fast(mold - muse);
-          m[rr][qb] = (mnew == -INFINITY) ? -INFINITY : muse;
-          l[rr][qb] *= alpha;
+              for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[rr][qb][kb][i]);
+            mx = fmaxf(mx, shfl_xor(mx, 16));
+            mx = fmaxf(mx, shfl_xor(mx, 32));
+            const float mold = m[rr][qb];
+            const float mnew = fmaxf(mold, mx * kLog2e);
+            const float muse = (mnew == -INFINITY) ? 0.f : mnew;
+            const float alpha = (mold == -INFINITY) ? 0.f : exp2_fast(mold - muse);
+            m[rr][qb] = (mnew == -INFINITY) ? -INFINITY : muse;
+            l[rr][qb] *= alpha;
 #pragma unroll
-          for (int cb = 0; cb < 2; ++cb) o[rr][qb][cb] *= alpha;
-          float acc = 0.f;
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
+            for (int cb = 0; cb < 2; ++cb) o[rr][qb][cb] *= alpha;
             f32x4 e[2];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
               for (int i = 0; i < 4; ++i)
-                e[kb][i] = exp2_fast(__builtin_fmaf(s[rr][qb][half][kb][i], kLog2e, -muse));
-            pf[rr][qb][half] = pack8(e[0], e[1], (Op*)nullptr);
-            acc = sum8(pf[rr][qb][half], acc);
+                e[kb][i] = exp2_fast(__builtin_fmaf(s[rr][qb][kb][i], kLog2e, -muse));
+            pf[rr][qb] = pack8(e[0], e[1], (Op*)nullptr);
+            psum[rr][qb] = sum8(pf[rr][qb], 0.f);
           }
-          psum[rr][qb] = acc;
-        }
-    }
+      }
 #pragma unroll
-    for (int rr = 0; rr < ROWS; ++rr)
+      for (int rr = 0; rr < ROWS; ++rr)
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) l[rr][qb] += psum[rr][qb];
+        for (int qb = 0; qb < 2; ++qb) l[rr][qb] += psum[rr][qb];
 
 #pragma unroll
-    for (int rr = 0; rr < ROWS; ++rr)
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
+      for (int rr = 0; rr < ROWS; ++rr) {
         Op vf[2];
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb)
-          vf[cb] = ld8(sV[buf][rr] + (cb * 16 + l16) * VST + v_col_t<T>(cb * 16 + l16, half * 32 + 8 * g));
+          vf[cb] = ld8(sV[buf][rr] + (cb * 16 + l16) * VST + v_col_t<T>(cb * 16 + l16, hf * 32 + 8 * g));
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
           for (int cb = 0; cb < 2; ++cb)
-            o[rr][qb][cb] = mma32(vf[cb], pf[rr][qb][half], o[rr][qb][cb]);
+            o[rr][qb][cb] = mma32(vf[cb], pf[rr][qb], o[rr][qb][cb]);
       }
+    }
     // next tile's bias operands (the logit registers are free again)
     if (tile + 1 < ntiles) EVO_FETCH_BIAS(k0 + BK);
   }
@@ -595,18 +583,17 @@ hipError_t launch_attn_fwd(const AttnFwdArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     p.biasp = bp;
   }
-  // Lines of a workgroup share the bias tile (bf16; with one mask per line
-  // the two-line variant would not fit two waves per SIMD in registers).
-  const int rows = (a.dtype == 1 && a.R > 1 && !row_mask) ? 2 : 1;
+  // One line per workgroup.  (A two-line variant, sharing each bias tile
+  // between two lines, needs ~210 registers per lane, hence two waves per
+  // SIMD against four for one line; measured slower at N_res = 768.)
+  const int rows = 1;
   p.n_qt = (int)((a.N + BQ - 1) / BQ);
   p.n_rg = (int)((a.R + rows - 1) / rows);
   const int64_t total = a.B * ((a.H + 1) / 2) * 2 * (int64_t)p.n_rg * p.n_qt;
   if (total > (int64_t)INT32_MAX - 8) return hipErrorInvalidValue;
   p.total = (int)total;
-  if (a.dtype == 1) {
-    if (rows == 2) return launch_t<bf16_t, 2, false>(p, s);
+  if (a.dtype == 1)
     return row_mask ? launch_t<bf16_t, 1, true>(p, s) : launch_t<bf16_t, 1, false>(p, s);
-  }
   return row_mask ? launch_t<float, 1, true>(p, s) : launch_t<float, 1, false>(p, s);
 }
 
