@@ -306,7 +306,10 @@ template <> struct StageRaw<bf16_t> { u32x4 a; float l; };
 template <> struct StageRaw<float> { u32x4 a, b; float l; };
 
 template <typename T, bool ROW_MASK>
-__global__ void __launch_bounds__(256) bwd_dkdv_kernel(BwdParams p) {
+// Four waves per SIMD: the register cap costs a 12-byte spill of values
+// used only after the query loop.
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
+bwd_dkdv_kernel(BwdParams p) {
   using Op = typename Tr<T>::Op;
   constexpr int RS = 40;  // row stride (elements): 16-byte reads spread over banks
   constexpr int E16 = 16 / sizeof(T);
