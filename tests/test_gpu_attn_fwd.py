@@ -101,6 +101,43 @@ def test_fully_masked_line_and_single_key(dtype):
     check(d, dtype)
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_neg_inf_bias_entries_act_as_masks(dtype):
+    """-inf pair-bias entries remove single (query, key) pairs, and a query
+    whose bias row is all -inf gets out 0 and lse -inf, as with a mask (the
+    bf16 path stores them as the lowest finite bf16 and must still give
+    p = 0 exactly)."""
+    log(f"case fwd -inf bias {dtype}")
+    d = synth.rand_core(1, 3, 70, 2, 32, dtype, seed=21, mask="random")
+    gen = torch.Generator().manual_seed(3)
+    holes = torch.rand(d["bias"].shape, generator=gen) < 0.2
+    b = d["bias"].clone()
+    b[holes] = float("-inf")
+    b[0, 1, 9, :] = float("-inf")   # head 1, query 9: nothing left
+    d["bias"] = b
+    out, lse = run_gpu(d)
+    assert torch.isfinite(out).all()
+    assert torch.all(out[:, :, 9, 1] == 0)
+    assert torch.all(torch.isneginf(lse[:, :, 1, 9]))
+    check(d, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_fully_masked_batch_shared_mask(dtype):
+    """A shared key mask (one per batch entry, folded into the prepared
+    bias) that removes every key of batch entry 1: its lines give out 0 and
+    lse -inf; batch entry 0 is unaffected."""
+    log(f"case fwd shared mask empty {dtype}")
+    d = synth.rand_core(2, 3, 45, 2, 32, dtype, seed=8, mask="random")
+    m = d["mask"].clone()
+    m[1] = 0
+    d["mask"] = m
+    out, lse = run_gpu(d)
+    assert torch.all(out[1] == 0)
+    assert torch.all(torch.isneginf(lse[1]))
+    check(d, dtype)
+
+
 @pytest.mark.parametrize("shift", [1e4, -1e4])
 def test_large_bias_shift(shift):
     """Bias entries near +-1e4: no overflow or NaN (the online softmax
