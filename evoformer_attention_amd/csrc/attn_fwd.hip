@@ -63,10 +63,13 @@ constexpr int BQ = BQW * WAVES;   // queries per workgroup
 constexpr float kHeadroom = 256.f;  // 2^8: largest tile sum of p per lane
 
 template <typename T> struct FwdLds;
-// Row strides (elements) of the LDS K tile [64 keys][32 dims] and V^T tile
-// [32 dims][64 keys]; the padding spreads 16-byte reads over all banks.
-template <> struct FwdLds<bf16_t> { static constexpr int KST = 40, VST = 72; };
-template <> struct FwdLds<float> { static constexpr int KST = 36, VST = 68; };
+// Row strides (elements) of the LDS K tile [64 keys][32 dims] and V tile;
+// the padding spreads the reads over all banks.
+// bf16: V is stored row-major like K ([64 keys][VST]) and read transposed
+// (lds_read_tr16); a row stride of 48 makes those reads conflict-free.
+// fp32: V is stored transposed ([32 dims][VST]).
+template <> struct FwdLds<bf16_t> { static constexpr int KST = 40, VST = 48, VROWS = BK; };
+template <> struct FwdLds<float> { static constexpr int KST = 36, VST = 68, VROWS = C; };
 
 struct FwdParams {
   const void* q;
@@ -92,16 +95,8 @@ __device__ __forceinline__ int k_lds_row(int p) {
   return half * 32 + kb * 16 + gg * 4 + i;
 }
 
-// Column of key chunk c (a multiple of 8) in row `row` of the transposed V
-// tile.  bf16 tiles are swizzled by 16 * (row / 8 mod 4) (see store_kv);
-// fp32 tiles are stored plainly.
-template <typename T>
-__device__ __forceinline__ int v_col_t(int row, int c) {
-  return sizeof(T) == 2 ? (c ^ (16 * ((row >> 3) & 3))) : c;
-}
-
-// ---- raw tile data one thread fetches for one line: 8 K elements of one
-// key and 4 V elements of two keys.
+// ---- raw tile data one thread fetches for one line: 8 K and 8 V elements
+// of one key (fp32: 8 K elements of one key, 4 V elements of two keys).
 // (native vector types: HIP's uint4 struct is copied as an aggregate, which
 // can leave the tile in scratch memory)
 template <typename T> struct KVRaw;
@@ -147,18 +142,8 @@ __device__ __forceinline__ void store_kv(const KVRaw<T>& raw, T* sK, T* sV) {
   if constexpr (sizeof(T) == 2) {
     (void)p; (void)vc;
     *reinterpret_cast<u32x4*>(sK + k_lds_row(kk) * KST + ch * 8) = raw.k;
-    // V transposed: dim 8*ch + j of key kk goes to row 8*ch + j, column
-    // kk ^ (16*ch) (16-bit stores of the low and high halves of each loaded
-    // dword).  The swizzle spreads the four dim groups of a key over
-    // different banks; it moves whole 8-key chunks, so a lane's 8 keys stay
-    // one 16-byte read (v_col_t).
-    uint16_t* d = reinterpret_cast<uint16_t*>(sV) + (ch * 8) * VST + (kk ^ (16 * ch));
-    const uint32_t w[4] = {raw.v.x, raw.v.y, raw.v.z, raw.v.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      d[(2 * j) * VST] = (uint16_t)(w[j] & 0xffffu);
-      d[(2 * j + 1) * VST] = (uint16_t)(w[j] >> 16);
-    }
+    // V row-major (physical key order), read transposed
+    *reinterpret_cast<u32x4*>(sV + kk * VST + ch * 8) = raw.v;
   } else {
     u32x4* dk = reinterpret_cast<u32x4*>(sK + k_lds_row(kk) * KST + ch * 8);
     dk[0] = raw.k0;
@@ -281,7 +266,7 @@ attn_fwd_kernel(FwdParams p) {
   using Op = typename Tr<T>::Op;
   constexpr int KST = FwdLds<T>::KST, VST = FwdLds<T>::VST;
   __shared__ __attribute__((aligned(16))) T sK[2][ROWS][BK * KST];
-  __shared__ __attribute__((aligned(16))) T sV[2][ROWS][C * VST];
+  __shared__ __attribute__((aligned(16))) T sV[2][ROWS][FwdLds<T>::VROWS * VST];
 
   // Work order (fastest first): query tile, head within a head pair, row
   // group, head pair, batch.  The heads of a position are interleaved at
@@ -483,8 +468,15 @@ attn_fwd_kernel(FwdParams p) {
       for (int rr = 0; rr < ROWS; ++rr) {
         Op vf[2];
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
-          vf[cb] = ld8(sV[buf][rr] + (cb * 16 + l16) * VST + v_col_t<T>(cb * 16 + l16, hf * 32 + 8 * g));
+        for (int cb = 0; cb < 2; ++cb) {
+          if constexpr (sizeof(T) == 2) {
+            // V^T fragment: keys hf*32 + 8g .. +7 of dim cb*16 + l16
+            const T* v0 = sV[buf][rr] + (hf * 32 + 8 * g + (l16 >> 2)) * VST + cb * 16 + 4 * (l16 & 3);
+            vf[cb] = lds_read_tr_op(v0, v0 + 4 * VST);
+          } else {
+            vf[cb] = ld8(sV[buf][rr] + (cb * 16 + l16) * VST + hf * 32 + 8 * g);
+          }
+        }
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
 #pragma unroll

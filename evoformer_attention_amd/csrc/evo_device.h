@@ -146,6 +146,33 @@ __device__ __forceinline__ void widen8(const Raw8<float>& r, f32x4& x, f32x4& y)
             __uint_as_float(r.b.w)};
 }
 
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane r addresses a chunk of 4 consecutive 16-bit elements; lane i
+// receives element i % 4 of the chunks addressed by lanes i / 4 + 4j,
+// j = 0..3 (the mapping measured on gfx950).  So if lane r of group g points
+// at row 8g + r/4 (+4 for a second read), columns c0 + 4(r % 4) .. +3, of a
+// row-major tile, lane i gets column c0 + i of rows 8g .. 8g + 3 (+4): the
+// 8 consecutive-row values of one column that an MFMA operand needs, read
+// from a tile stored without transposition.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i16x4 lds_read_tr16(const void* lds_ptr) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)lds_ptr);
+#else
+  (void)lds_ptr;
+  return i16x4{};
+#endif
+}
+// Two transposing reads (rows 8g..+3 at p0, 8g+4..+7 at p1) as one bf16
+// operand fragment.
+__device__ __forceinline__ bf16x8 lds_read_tr_op(const void* p0, const void* p1) {
+  const i16x4 lo = lds_read_tr16(p0), hi = lds_read_tr16(p1);
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 // Workgroups are dispatched round-robin over the XCDs (workgroup i runs on
 // XCD i % 8).  Remap so that XCD x receives the contiguous work range
 // [x * per, (x + 1) * per): neighbouring work items, which share inputs,
