@@ -16,19 +16,20 @@
 //   dQ = dS K / sqrt(C),  dBias = sum over rows of dS.
 //
 // Kernels:
-//   prep      dO, dG, D, base-2 LSE, and transposed copies Q^T, dO^T, K^T
-//             (one [C, N] slab per line and head) so that every MFMA operand
-//             below is a contiguous 16-byte load.
-//   bias      the mask-folded pair bias in both orientations (working dtype;
-//             the exp argument s*log2(e) - LSE*log2(e) is one FMA).
+//   prep      an elementwise pass: dO, dG, -D and the base-2 LSE.
+//   bias      the mask-folded pair bias, in the fragment orders of the dQ /
+//             dBias kernels and (transposed) of the dK/dV kernel (working
+//             dtype; the exp argument s*log2(e) - LSE*log2(e) is one FMA).
 //   dkdv      one line, one head, 128 keys per workgroup (32 per wave);
 //             loops over 32-query steps staged through double-buffered LDS
 //             (next step prefetched into registers).  Lane = key in the
 //             accumulator layout: S = Q K^T + bias, dP = dO V^T,
-//             dV^T += dO^T P, dK^T += Q^T dS.
+//             dV^T += dO^T P, dK^T += Q^T dS; the transposed operands dO^T
+//             and Q^T are read from the row-major tiles with transposing LDS
+//             reads (bf16).
 //   dq        one line, one head, 128 queries; loops over 64-key tiles in
 //             double-buffered LDS.  Lane = query: S^T = K Q^T + bias,
-//             dP^T = V dO^T, dQ^T += K^T dS^T.
+//             dP^T = V dO^T, dQ^T += K^T dS^T (K^T likewise read transposed).
 //   dbias     one head, a 128-query x 64-key tile, for a group of rows: the
 //             bias tile and the dBias accumulator stay in registers while
 //             the rows stream by (rows innermost), so the sum over rows
@@ -313,7 +314,9 @@ bwd_dkdv_kernel(BwdParams p) {
   using Op = typename Tr<T>::Op;
   constexpr int RS = 40;  // row stride (elements): 16-byte reads spread over banks
   constexpr int E16 = 16 / sizeof(T);
-  __shared__ __attribute__((aligned(32))) T sT[2][4][32 * RS];  // [buf][Q,dO,Qt,dOt]
+  // [buf][Q, dO, Q^T, dO^T]; bf16 reads the transposed operands straight
+  // from the row-major tiles (lds_read_tr16), so only fp32 stores Q^T, dO^T
+  __shared__ __attribute__((aligned(32))) T sT[2][sizeof(T) == 2 ? 2 : 4][32 * RS];
   __shared__ float sL[2][2][32];                                 // [buf][lse2, D]
 
   // Work order (fastest first): key tile, head within a head pair, line,
@@ -390,16 +393,11 @@ bwd_dkdv_kernel(BwdParams p) {
   };
   auto store = [&](const StageRaw<T>& raw, int buf) {
     T* drow = sT[buf][sten] + srow * RS + sch * 8;
-    T* dcol = sT[buf][2 + sten] + (sch * 8) * RS + sslot;
     if constexpr (sizeof(T) == 2) {
+      (void)sslot;
       *reinterpret_cast<u32x4*>(drow) = raw.a;
-      uint16_t* d16 = reinterpret_cast<uint16_t*>(dcol);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        d16[(2 * j) * RS] = (uint16_t)(raw.a[j] & 0xffffu);
-        d16[(2 * j + 1) * RS] = (uint16_t)(raw.a[j] >> 16);
-      }
     } else {
+      T* dcol = sT[buf][2 + sten] + (sch * 8) * RS + sslot;
       reinterpret_cast<u32x4*>(drow)[0] = raw.a;
       reinterpret_cast<u32x4*>(drow)[1] = raw.b;
       uint32_t* d32 = reinterpret_cast<uint32_t*>(dcol);
@@ -434,8 +432,6 @@ bwd_dkdv_kernel(BwdParams p) {
     }
     const T* sQ = sT[buf][0];
     const T* sDO = sT[buf][1];
-    const T* sQt = sT[buf][2];
-    const T* sDOt = sT[buf][3];
 
     // S[qb][kb]: lane holds queries qb*16 + 4g + i for key kbase + kb*16 + l16.
     // dP starts from -D, so the accumulator ends at dP - D.
@@ -467,8 +463,17 @@ bwd_dkdv_kernel(BwdParams p) {
     // dV^T += dO^T P,  dK^T += Q^T dS  (contraction over the 32 query slots)
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
-      const Op dot = *reinterpret_cast<const Op*>(sDOt + (cb * 16 + l16) * RS + 8 * g);
-      const Op qtf = *reinterpret_cast<const Op*>(sQt + (cb * 16 + l16) * RS + 8 * g);
+      Op dot, qtf;  // dO^T, Q^T: dims cb*16 + l16, query slots 8g .. +7
+      if constexpr (sizeof(T) == 2) {
+        // slots 8g + i and 8g + 4 + i hold queries 4g + i and 16 + 4g + i
+        const int c0 = cb * 16 + 4 * (l16 & 3);
+        const int r0 = (4 * g + (l16 >> 2)) * RS + c0, r1 = r0 + 16 * RS;
+        dot = lds_read_tr_op(sDO + r0, sDO + r1);
+        qtf = lds_read_tr_op(sQ + r0, sQ + r1);
+      } else {
+        dot = *reinterpret_cast<const Op*>(sT[buf][3] + (cb * 16 + l16) * RS + 8 * g);
+        qtf = *reinterpret_cast<const Op*>(sT[buf][2] + (cb * 16 + l16) * RS + 8 * g);
+      }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const Op pf = pack8(s[0][kb], s[1][kb], (Op*)nullptr);
@@ -519,8 +524,9 @@ __device__ __forceinline__ int k_lds_row(int p) {
     if constexpr (sizeof(T) == 4) { rk1 = ks_[1]; rv1 = vs_[1]; }             \
   } while (0)
 
-// K and V rows key-permuted (the S and dP operands) and K transposed, keys
-// in physical order (the dQ operand); bf16 columns swizzled by kt_col.
+// K and V rows key-permuted (the S and dP operands); fp32 also stores K
+// transposed, keys in physical order (the dQ operand; bf16 reads it with a
+// transposing LDS read instead).
 #define EVO_STORE_K(T, sK_, sV_, sKt_, KS_, TS_)                                  \
   do {                                                                        \
     const int t_ = threadIdx.x, kk_ = t_ >> 2, ch_ = t_ & 3;                  \
@@ -534,37 +540,24 @@ __device__ __forceinline__ int k_lds_row(int p) {
         dt_[j_ * (TS_)] = rk0[j_];                                            \
         dt_[(4 + j_) * (TS_)] = rk1[j_];                                      \
       }                                                                       \
-    } else {                                                                  \
-      uint16_t* dt_ = reinterpret_cast<uint16_t*>(sKt_) + (ch_ * 8) * (TS_) + (kk_ ^ (16 * ch_)); \
-      for (int j_ = 0; j_ < 4; ++j_) {                                        \
-        dt_[(2 * j_) * (TS_)] = (uint16_t)(rk0[j_] & 0xffffu);                \
-        dt_[(2 * j_ + 1) * (TS_)] = (uint16_t)(rk0[j_] >> 16);                \
-      }                                                                       \
     }                                                                         \
   } while (0)
-
-// Column of key chunk c (a multiple of 8) in row `row` of the transposed K
-// tile: bf16 rows are swizzled by 16 * (row / 8 mod 4), which spreads the
-// transposed 16-bit stores of the four dim groups of a key over different
-// banks while keeping every 8-key chunk one 16-byte read.
-template <typename T>
-__device__ __forceinline__ int kt_col(int row, int c) {
-  return sizeof(T) == 2 ? (c ^ (16 * ((row >> 3) & 3))) : c;
-}
 
 template <typename T> struct BLds;
 template <> struct BLds<bf16_t> { static constexpr int KS = 40, TS = 72; };
 template <> struct BLds<float> { static constexpr int KS = 36, TS = 68; };
 
 // dQ: workgroup = one line, one head, 128 queries (32 per wave); loops over
-// 64-key tiles (K, V rows key-permuted, K^T slab) through double-buffered
-// LDS.  Lane = query: S^T = K Q^T + bias, P = exp2(S - LSE), dP^T = V dO^T,
+// 64-key tiles (K, V rows key-permuted) through double-buffered LDS.  Lane = query: S^T = K Q^T + bias, P = exp2(S - LSE), dP^T = V dO^T,
 // dS = P (dP - D), dQ^T += K^T dS^T.
 template <typename T, bool ROW_MASK>
 __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdParams p) {
   using Op = typename Tr<T>::Op;
   constexpr int KS = BLds<T>::KS, TS = BLds<T>::TS;
-  __shared__ __attribute__((aligned(32))) T sK[2][64 * KS], sV[2][64 * KS], sKt[2][32 * TS];
+  // bf16 reads K^T straight from the key-permuted K tile (lds_read_tr16);
+  // only fp32 stores a transposed copy
+  __shared__ __attribute__((aligned(32))) T sK[2][64 * KS], sV[2][64 * KS],
+      sKt[2][sizeof(T) == 2 ? 1 : 32 * TS];
 
   // Work order: query tile, head within a pair, line, head pair (as in the
   // dK/dV kernel): the pair's bias rows and shared K/V lines stay in L2.
@@ -677,8 +670,14 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdParams p) {
       }
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
-        const Op ktf = *reinterpret_cast<const Op*>(
-            sKt[buf] + (cb * 16 + l16) * TS + kt_col<T>(cb * 16 + l16, half * 32 + 8 * g));
+        Op ktf;  // K^T: dims cb*16 + l16, keys half*32 + 8g .. +7
+        if constexpr (sizeof(T) == 2) {
+          // physical key half*32 + 8g + 4h + i sits in row half*32 + 16h + 4g + i
+          const T* k0p = sK[buf] + (half * 32 + 4 * g + (l16 >> 2)) * KS + cb * 16 + 4 * (l16 & 3);
+          ktf = lds_read_tr_op(k0p, k0p + 16 * KS);
+        } else {
+          ktf = *reinterpret_cast<const Op*>(sKt[buf] + (cb * 16 + l16) * TS + half * 32 + 8 * g);
+        }
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
           dq[qb][cb] = mma32(ktf, pack8(dp[qb][0], dp[qb][1], (Op*)nullptr), dq[qb][cb]);
