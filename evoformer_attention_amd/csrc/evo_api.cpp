@@ -220,6 +220,8 @@ static evo_status_t check_module_sizes(evo_dtype_t dtype, int64_t N,
   evo_status_t st = check_core_sizes(dtype, 1, N, N, H, C);
   if (st != EVO_OK) return st;
   if (CZ <= 0) return fail(EVO_EINVAL, "CZ=%lld must be positive", (long long)CZ);
+  if (N > 46340)  // N*N positions are indexed in 32 bits
+    return fail(EVO_ENOTSUP, "N=%lld is not supported (at most 46340)", (long long)N);
   if (CZ % 32 != 0 || CZ > 256)
     return fail(EVO_ENOTSUP, "CZ=%lld is not supported (multiple of 32, at "
                 "most 256)", (long long)CZ);

@@ -10,8 +10,9 @@
 //
 // Both are a row GEMM  Y[pos, :] = f(X[pos, :]) . W^T  over the N*N positions
 // (W in [out, in] layout).  Kernel structure:
-//   - persistent workgroups of 8 waves; each loads W^T (all output columns of
-//     one pass, padded rows) into LDS once and then walks 256-position tiles;
+//   - persistent workgroups, one per CU (16 waves up to 128 input channels,
+//     else 8); each loads W^T (all output columns of one pass, padded rows)
+//     into LDS once and then walks tiles of 32 positions per wave;
 //   - a wave owns 32 positions: it loads their rows straight into the MFMA
 //     B-operand layout (lane = position, 8 consecutive input channels per
 //     contraction step), computes LayerNorm there (cross-lane sums over the
@@ -58,14 +59,24 @@ struct GemmParams {
                         // out projection: out [npos, ncols] in z layout
 };
 
-// z row (or output row) of line-layout position pidx.
-__device__ __forceinline__ int64_t z_row(int64_t pidx, int N, int ending) {
+// z row (or output row) of line-layout position pidx (N*N < 2^31, so 32-bit
+// index arithmetic).
+__device__ __forceinline__ uint32_t z_row(uint32_t pidx, uint32_t N, int ending) {
   if (!ending) return pidx;
-  const int64_t a = pidx / N, n = pidx - a * N;
+  const uint32_t a = pidx / N, n = pidx - a * N;
   return n * N + a;
 }
 
-// Source row (K contiguous elements) of output column c, or null for padding.
+// Line-layout position of element j (0..31) of wave `wave` in tile `tile`
+// (WAVES*32 consecutive positions per tile); `live` is false past the end.
+template <int WAVES>
+__device__ __forceinline__ uint32_t tile_pos(const GemmParams& p, int tile, int wave, int j,
+                                             bool& live) {
+  const uint32_t pi = ((uint32_t)tile * WAVES + wave) * PW + j;
+  live = pi < (uint32_t)p.npos;
+  return pi;
+}
+
 template <typename T>
 __device__ __forceinline__ const T* w_row(const GemmParams& p, int c) {
   if (c >= p.ncols) return nullptr;
@@ -90,12 +101,19 @@ __device__ __forceinline__ void st4<float>(float* p, const f32x4& v) {
 }
 
 // Store two adjacent 16-column blocks A (columns 0..15) and B (16..31) of
-// one position row.  A lane of group g holds columns 4g..4g+3 of each; lanes
-// of groups g and g^1 (lanes l and l^16) swap halves so that an even-g lane
-// stores columns 4g..4g+7 of A and an odd-g lane columns 4(g-1)..4g+3 of B,
-// one contiguous 8-element chunk each: a wave's store then covers 16
-// positions x 64 contiguous bytes (bf16) instead of 16 x 32.  Every lane
-// takes part in the swap; `live` only gates the store.
+// one position row.  A lane of row group g (lanes 16g..16g+15) holds
+// columns 4g..4g+3 of each.  v_permlane16_swap(x, y) exchanges the odd row
+// groups of x with the even row groups of y (measured on gfx950: x becomes
+// [x.r0, y.r0, x.r2, y.r2] and y [x.r1, y.r1, x.r3, y.r3]); with x = A and
+// y = B, an even-g lane then holds columns 4g..4g+7 of A and an odd-g lane
+// columns 4(g-1)..4g+3 of B, one contiguous 8-element chunk each, and a
+// wave's store covers 16 positions x 64 contiguous bytes (bf16) instead of
+// 16 x 32.  Every lane takes part in the swap; `live` only gates the store.
+__device__ __forceinline__ void swap_rows16(uint32_t& x, uint32_t& y) {
+  const auto r = __builtin_amdgcn_permlane16_swap(x, y, false, false);
+  x = r[0];
+  y = r[1];
+}
 template <typename T>
 __device__ __forceinline__ void store_pair(T* row, const f32x4& a, const f32x4& b, int g,
                                            bool live);
@@ -105,33 +123,34 @@ __device__ __forceinline__ void store_pair<bf16_t>(bf16_t* row, const f32x4& a, 
   auto pk = [](float x, float y) {
     return uint32_t(Tr<bf16_t>::from_f(x)) | (uint32_t(Tr<bf16_t>::from_f(y)) << 16);
   };
-  const uint32_t a0 = pk(a[0], a[1]), a1 = pk(a[2], a[3]);
-  const uint32_t b0 = pk(b[0], b[1]), b1 = pk(b[2], b[3]);
-  const bool odd = g & 1;
-  const uint32_t r0 = (uint32_t)__shfl_xor((int)(odd ? a0 : b0), 16, 64);
-  const uint32_t r1 = (uint32_t)__shfl_xor((int)(odd ? a1 : b1), 16, 64);
-  const u32x4 chunk = odd ? u32x4{r0, r1, b0, b1} : u32x4{a0, a1, r0, r1};
-  if (live) *reinterpret_cast<u32x4*>(row + (odd ? 16 + 4 * (g - 1) : 4 * g)) = chunk;
+  uint32_t x0 = pk(a[0], a[1]), x1 = pk(a[2], a[3]);
+  uint32_t y0 = pk(b[0], b[1]), y1 = pk(b[2], b[3]);
+  swap_rows16(x0, y0);
+  swap_rows16(x1, y1);
+  if (live)
+    *reinterpret_cast<u32x4*>(row + ((g & 1) ? 16 + 4 * (g - 1) : 4 * g)) = u32x4{x0, x1, y0, y1};
 }
 template <>
 __device__ __forceinline__ void store_pair<float>(float* row, const f32x4& a, const f32x4& b,
                                                   int g, bool live) {
-  const bool odd = g & 1;
-  f32x4 r;
+  u32x4 x, y;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = __shfl_xor(odd ? a[i] : b[i], 16, 64);
-  const f32x4 lo = odd ? r : a, hi = odd ? b : r;
+  for (int i = 0; i < 4; ++i) {
+    uint32_t xi = __float_as_uint(a[i]), yi = __float_as_uint(b[i]);
+    swap_rows16(xi, yi);
+    x[i] = xi;
+    y[i] = yi;
+  }
   if (live) {
-    float* dst = row + (odd ? 16 + 4 * (g - 1) : 4 * g);
-    *reinterpret_cast<f32x4*>(dst) = lo;
-    *reinterpret_cast<f32x4*>(dst + 4) = hi;
+    u32x4* dst = reinterpret_cast<u32x4*>(row + ((g & 1) ? 16 + 4 * (g - 1) : 4 * g));
+    dst[0] = x;
+    dst[1] = y;
   }
 }
 
 template <typename T, int KSTEPS, int WAVES = waves_for<KSTEPS>()>
 __global__ void __launch_bounds__(WAVES * 64)
 rowgemm_kernel(GemmParams p) {
-  constexpr int TP = PW * WAVES;  // positions per tile
   using Op = typename Tr<T>::Op;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int K = KSTEPS * 32;
@@ -142,6 +161,27 @@ rowgemm_kernel(GemmParams p) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, g = lane >> 4;
 
+  const T* X = static_cast<const T*>(p.x);
+  // Rows of position `pi` as loaded: channels 32s + 8g .. +7 in nx[s].
+  // Positions past the end read row 0 (finite; never stored).
+  auto load_rows = [&](Op (&nx)[2][KSTEPS], int tile) {
+#pragma unroll
+    for (int pb = 0; pb < 2; ++pb) {
+      bool live;
+      const uint32_t pi = tile_pos<WAVES>(p, tile, wave, pb * 16 + l16, live);
+      const uint32_t row = live ? (p.mode == 0 ? z_row(pi, p.N, p.ending) : pi) : 0;
+      const T* src = X + (int64_t)row * K + 8 * g;
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) nx[pb][s] = *reinterpret_cast<const Op*>(src + 32 * s);
+    }
+  };
+  // bf16: the next tile's rows are in flight during this tile, the first
+  // tile's during the weight set-up (fp32 rows would not fit the register
+  // budget and are loaded at the tile's start)
+  constexpr bool PREFETCH = sizeof(T) == 2;
+  Op nx[2][KSTEPS];
+  if (PREFETCH && blockIdx.x < p.ntiles) load_rows(nx, blockIdx.x);
+
   // ---- This pass's weights into LDS, with the LayerNorm affine folded in:
   // LN(x) . W^T = xhat . (W diag(gamma))^T + beta . W^T, xhat = (x - mu) *
   // rstd.  sW holds W diag(gamma) (rounded to the working dtype), sC the
@@ -149,70 +189,95 @@ rowgemm_kernel(GemmParams p) {
   const T* lnw = static_cast<const T*>(p.ln_w);
   const T* lnb = static_cast<const T*>(p.ln_b);
   {
+    // One chunk = 8 input channels of one column: a vector load of W and one
+    // of gamma; four chunks per thread are in flight before any is used.
     const int chunks = K / 8;
-    for (int e = tid; e < p.pass_cols * chunks; e += blockDim.x) {
-      const int cl = e / chunks, k0 = (e - cl * chunks) * 8;
-      const T* src = w_row<T>(p, p.col0 + cl);
-      T* dst = sW + cl * KS + k0;
+    const int total = p.pass_cols * chunks;
+    const int nthr = WAVES * 64;
+    for (int e0 = tid; e0 < total; e0 += 4 * nthr) {
+      Raw8<T> wr[4], gr[4];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float wv = src ? Tr<T>::to_f(src[k0 + j]) : 0.f;
-        if (p.mode == 0) wv *= Tr<T>::to_f(lnw[k0 + j]);
-        dst[j] = Tr<T>::from_f(wv);
+      for (int u = 0; u < 4; ++u) {
+        const int e = e0 + u * nthr;
+        const int cl = e / chunks, k0 = (e - cl * chunks) * 8;
+        const T* src = e < total ? w_row<T>(p, p.col0 + cl) : nullptr;
+        if (src) {
+          ld_raw8(wr[u], src + k0);
+          if (p.mode == 0) ld_raw8(gr[u], lnw + k0);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = e0 + u * nthr;
+        if (e >= total) break;
+        const int cl = e / chunks, k0 = (e - cl * chunks) * 8;
+        f32x4 w0 = {0.f, 0.f, 0.f, 0.f}, w1 = w0;
+        if (w_row<T>(p, p.col0 + cl)) {
+          widen8(wr[u], w0, w1);
+          if (p.mode == 0) {
+            f32x4 g0, g1;
+            widen8(gr[u], g0, g1);
+            w0 *= g0;
+            w1 *= g1;
+          }
+        }
+        T* dst = sW + cl * KS + k0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          dst[j] = Tr<T>::from_f(w0[j]);
+          dst[4 + j] = Tr<T>::from_f(w1[j]);
+        }
       }
     }
-    // one column per wave: lanes split the K products, then a fixed-order
-    // butterfly sum (deterministic)
-    for (int cl = wave; cl < p.pass_cols; cl += WAVES) {
+    // Column constants, one thread per column: beta . W^T summed in channel
+    // order (fixed order, deterministic), plus the column bias.
+    for (int cl = tid; cl < p.pass_cols; cl += nthr) {
       const int c = p.col0 + cl;
       const T* src = w_row<T>(p, c);
       float acc = 0.f;
-      if (src && p.mode == 0)
-        for (int k = lane; k < K; k += 64) acc += Tr<T>::to_f(lnb[k]) * Tr<T>::to_f(src[k]);
+      if (src && p.mode == 0) {
+#pragma unroll 4
+        for (int k0 = 0; k0 < K; k0 += 8) {
+          Raw8<T> wr, br;
+          ld_raw8(wr, src + k0);
+          ld_raw8(br, lnb + k0);
+          f32x4 w0, w1, b0, b1;
+          widen8(wr, w0, w1);
+          widen8(br, b0, b1);
 #pragma unroll
-      for (int o = 1; o < 64; o <<= 1) acc += shfl_xor(acc, o);
+          for (int j = 0; j < 4; ++j) acc = __builtin_fmaf(b0[j], w0[j], acc);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc = __builtin_fmaf(b1[j], w1[j], acc);
+        }
+      }
       if (src && p.colbias) {
         if (p.mode == 1) acc += Tr<T>::to_f(static_cast<const T*>(p.colbias)[c]);
         else if (c >= 3 * p.HC && c < 4 * p.HC)
           acc += Tr<T>::to_f(static_cast<const T*>(p.colbias)[c - 3 * p.HC]);
       }
-      if (lane == 0) sC[cl] = acc;
+      sC[cl] = acc;
     }
   }
   __syncthreads();
 
-  const T* X = static_cast<const T*>(p.x);
-  // Rows of position `pi` as loaded: channels 32s + 8g .. +7 in nx[s].
-  // Positions past the end read row 0 (finite; never stored).
-  auto load_rows = [&](Op (&nx)[2][KSTEPS], int tile) {
-#pragma unroll
-    for (int pb = 0; pb < 2; ++pb) {
-      const int64_t pi = (int64_t)tile * TP + wave * PW + pb * 16 + l16;
-      const int64_t row =
-          pi < p.npos ? (p.mode == 0 ? z_row(pi, p.N, p.ending) : pi) : 0;
-      const T* src = X + row * K + 8 * g;
-#pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) nx[pb][s] = *reinterpret_cast<const Op*>(src + 32 * s);
-    }
-  };
-  // bf16: the next tile's rows are in flight during this tile (fp32 rows
-  // would not fit the register budget and are loaded at the tile's start)
-  constexpr bool PREFETCH = sizeof(T) == 2;
-  Op nx[2][KSTEPS];
-  if (PREFETCH && blockIdx.x < p.ntiles) load_rows(nx, blockIdx.x);
+  // output matrix and column within it where this pass starts (passes start
+  // at multiples of 32 columns, so never inside a block pair)
+  const int m0 = p.mode == 0 ? min(p.col0 / p.HC, 4) : 0;
+  const int cbase0 = p.col0 - m0 * p.HC;
   for (int tile = blockIdx.x; tile < p.ntiles; tile += gridDim.x) {
     if (!PREFETCH) load_rows(nx, tile);
     // ---- this wave's 32 rows, in B-operand layout: xf[pb][s] holds
     // channels 32s + 8g .. +7 of position base + pb*16 + l16.
     Op xf[2][KSTEPS];
-    int64_t pidx[2], orow[2];
+    uint32_t pidx[2];
+    int64_t orow[2];
+    bool live[2];
 #pragma unroll
     for (int pb = 0; pb < 2; ++pb) {
-      pidx[pb] = (int64_t)tile * TP + wave * PW + pb * 16 + l16;
-      const bool live = pidx[pb] < p.npos;
-      const int64_t zr = live ? z_row(pidx[pb], p.N, p.ending) : 0;
+      pidx[pb] = tile_pos<WAVES>(p, tile, wave, pb * 16 + l16, live[pb]);
       // output row offset: line layout (project) or z layout (out projection)
-      orow[pb] = p.mode == 0 ? pidx[pb] * p.HC : zr * p.ncols;
+      orow[pb] = p.mode == 0 ? (int64_t)pidx[pb] * p.HC
+                             : (int64_t)(live[pb] ? z_row(pidx[pb], p.N, p.ending) : 0) * p.ncols;
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) xf[pb][s] = nx[pb][s];  // raw rows
     }
@@ -262,56 +327,56 @@ rowgemm_kernel(GemmParams p) {
       }
     }
 
-    // ---- Y^T blocks of 16 output columns, two at a time where both belong
-    // to one output matrix (see store_pair).
+    // ---- Y^T in blocks of 16 output columns, output matrix by output
+    // matrix (projection: q, k, v, g, then the pair bias; out projection:
+    // one), two blocks at a time where both belong to one matrix (see
+    // store_pair).  The accumulators start from the column constants.
     const int nblk = p.pass_cols / 16;
-    for (int cb = 0; cb < nblk;) {
-      // first column of the block: wave-uniform (output matrices are
-      // multiples of 16 columns wide, so a block never straddles two)
-      const int cblk = __builtin_amdgcn_readfirstlane(p.col0 + cb * 16);
-      if (cblk >= p.ncols) break;
-      const int m = p.mode == 0 ? cblk / p.HC : 0;  // scalar
-      const bool pair = cb + 1 < nblk && cblk + 16 < p.ncols &&
-                        (p.mode == 1 || (m < 4 && (cblk + 16) / p.HC == m));
-      f32x4 acc[2][2];  // [block][pb]
+    for (int cb = 0, m = m0, cbase = cbase0; cb < nblk; ++m, cbase = 0) {
+      const bool bias_out = p.mode == 0 && m == 4;
+      const int width = p.mode == 1 ? p.ncols : (bias_out ? p.H : p.HC);
+      T* out = static_cast<T*>(p.y[p.mode == 1 ? 0 : m]);
+      while (cb < nblk && cbase < width) {
+        const bool pair = !bias_out && cb + 1 < nblk && cbase + 32 <= width;
+        f32x4 acc[2][2];  // [block][pb]
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        if (j == 1 && !pair) break;
-        acc[j][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-        acc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const T* wr = sW + ((cb + j) * 16 + l16) * KS + 8 * g;
+        for (int j = 0; j < 2; ++j) {
+          if (j == 1 && !pair) break;
+          const f32x4 cc4 = *reinterpret_cast<const f32x4*>(sC + (cb + j) * 16 + 4 * g);
+          acc[j][0] = cc4;
+          acc[j][1] = cc4;
+          const T* wr = sW + ((cb + j) * 16 + l16) * KS + 8 * g;
 #pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) {
-          const Op a = *reinterpret_cast<const Op*>(wr + 32 * s);
-          acc[j][0] = mma32(a, xf[0][s], acc[j][0]);
-          acc[j][1] = mma32(a, xf[1][s], acc[j][1]);
+          for (int s = 0; s < KSTEPS; ++s) {
+            const Op a = *reinterpret_cast<const Op*>(wr + 32 * s);
+            acc[j][0] = mma32(a, xf[0][s], acc[j][0]);
+            acc[j][1] = mma32(a, xf[1][s], acc[j][1]);
+          }
         }
-        const f32x4 cc4 = *reinterpret_cast<const f32x4*>(sC + (cb + j) * 16 + 4 * g);
-        acc[j][0] += cc4;
-        acc[j][1] += cc4;
-      }
-      const int cbase = cblk - m * p.HC;  // first column within output m
-      T* out = static_cast<T*>(p.y[p.mode == 1 ? 0 : (m < 4 ? m : 4)]);
-      if (pair) {
+        if (pair) {
 #pragma unroll
-        for (int pb = 0; pb < 2; ++pb)
-          store_pair<T>(out + orow[pb] + cbase, acc[0][pb], acc[1][pb], g, pidx[pb] < p.npos);
-        cb += 2;
-        continue;
-      }
-#pragma unroll
-      for (int pb = 0; pb < 2; ++pb) {
-        if (pidx[pb] >= p.npos) continue;
-        const int c = cbase + 4 * g;
-        if (p.mode == 1 || m < 4) {
-          st4<T>(out + orow[pb] + c, acc[0][pb]);
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (c + i < p.H) out[(int64_t)(c + i) * p.npos + pidx[pb]] = Tr<T>::from_f(acc[0][pb][i]);
+          for (int pb = 0; pb < 2; ++pb)
+            store_pair<T>(out + orow[pb] + cbase, acc[0][pb], acc[1][pb], g, live[pb]);
+          cb += 2;
+          cbase += 32;
+          continue;
         }
+#pragma unroll
+        for (int pb = 0; pb < 2; ++pb) {
+          if (!live[pb]) continue;
+          const int c = cbase + 4 * g;
+          if (!bias_out) {
+            st4<T>(out + orow[pb] + c, acc[0][pb]);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (c + i < p.H) out[(int64_t)(c + i) * p.npos + pidx[pb]] = Tr<T>::from_f(acc[0][pb][i]);
+          }
+        }
+        cb += 1;
+        cbase += 16;
       }
-      cb += 1;
+      if (p.mode == 1 || m == 4) break;
     }
   }
 }

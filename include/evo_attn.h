@@ -141,7 +141,9 @@ evo_status_t evo_attn_bwd(evo_dtype_t dtype, int64_t B, int64_t R, int64_t N,
  * projections (the normalised N x N tensor is never written; the fusion of
  * "MegaFold...", section "Methodologie", item 3 "EvoFusion").
  *
- *   z          [N,N,CZ] dtype, the pair representation.
+ *   z          [N,N,CZ] dtype, the pair representation; CZ a multiple of
+ *              32, at most 256; H*C at most 256; N at most 46340 (N*N
+ *              positions are indexed in 32 bits); otherwise EVO_ENOTSUP.
  *   ln_w,ln_b  [CZ] dtype, LayerNorm weight and bias; ln_eps > 0.
  *              LayerNorm uses the population variance, statistics in fp32.
  *   w_q,w_k,w_v,w_g  [H*C, CZ] dtype in [out, in] layout (as
