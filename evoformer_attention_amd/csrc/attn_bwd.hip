@@ -704,7 +704,10 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdParams p) {
 // accumulator stay in registers while the rows stream by, their K and V
 // tiles shared by the 4 waves through double-buffered LDS.
 template <typename T, bool ROW_MASK>
-__global__ void __launch_bounds__(256) bwd_dbias_kernel(BwdParams p) {
+// bf16 without a per-line mask: three waves per SIMD (168 registers)
+__global__ void __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 && !ROW_MASK ? 3 : 1)))
+bwd_dbias_kernel(BwdParams p) {
   using Op = typename Tr<T>::Op;
   constexpr int KS = BLds<T>::KS;
   __shared__ __attribute__((aligned(32))) T sK[2][64 * KS], sV[2][64 * KS];
@@ -768,10 +771,21 @@ __global__ void __launch_bounds__(256) bwd_dbias_kernel(BwdParams p) {
   const int qa = qw0 + l16, qbq = qw0 + 16 + l16;
   const T* kp = static_cast<const T*>(p.k) + l0 + (int64_t)kk * pos_stride + ch * 8;
   const T* vp = static_cast<const T*>(p.v) + l0 + (int64_t)kk * pos_stride + ch * 8;
-  const T* qp0 = static_cast<const T*>(p.q) + l0 + (int64_t)min(qa, N - 1) * pos_stride + 8 * g;
-  const T* qp1 = static_cast<const T*>(p.q) + l0 + (int64_t)min(qbq, N - 1) * pos_stride + 8 * g;
-  const T* op0 = static_cast<const T*>(p.dopre) + l0 + (int64_t)min(qa, N - 1) * pos_stride + 8 * g;
-  const T* op1 = static_cast<const T*>(p.dopre) + l0 + (int64_t)min(qbq, N - 1) * pos_stride + 8 * g;
+  // Q and dO rows.  bf16 loads them with four consecutive lanes covering one
+  // position's 64 contiguous bytes (lane l: query qw0 + l/4 (+16), dims
+  // 8*(l%4)..+7), which the vector memory path serves about four times
+  // faster than the MFMA operand order (lane l: query l%16, dims 8*(l/16));
+  // each wave then moves its rows into operand order through its own LDS
+  // slots.  fp32 loads the operands directly.
+  constexpr bool QD_LDS = sizeof(T) == 2;
+  const int qr0 = QD_LDS ? qw0 + (lane >> 2) : qa, qr1 = QD_LDS ? qw0 + 16 + (lane >> 2) : qbq;
+  const int qch = QD_LDS ? (lane & 3) * 8 : 8 * g;
+  const T* qp0 = static_cast<const T*>(p.q) + l0 + (int64_t)min(qr0, N - 1) * pos_stride + qch;
+  const T* qp1 = static_cast<const T*>(p.q) + l0 + (int64_t)min(qr1, N - 1) * pos_stride + qch;
+  const T* op0 = static_cast<const T*>(p.dopre) + l0 + (int64_t)min(qr0, N - 1) * pos_stride + qch;
+  const T* op1 = static_cast<const T*>(p.dopre) + l0 + (int64_t)min(qr1, N - 1) * pos_stride + qch;
+  constexpr int QS = 40;  // LDS row stride (elements) of the per-wave Q / dO slots
+  __shared__ __attribute__((aligned(16))) T sQD[QD_LDS ? 4 : 1][2][QD_LDS ? 32 * QS : 8];
   const int64_t lh0 = ((int64_t)b * R + r_begin) * H + h;
   const float* lp = p.lse2 + lh0 * Np;
   const float* dq_ = p.dd + lh0 * Np;
@@ -807,8 +821,25 @@ __global__ void __launch_bounds__(256) bwd_dbias_kernel(BwdParams p) {
         dv[1] = rv1;
       }
     }
-    const Op qf[2] = {qn0, qn1};
-    const Op df[2] = {dn0, dn1};
+    Op qf[2], df[2];
+    if constexpr (QD_LDS) {
+      // this wave's slots only: no barrier, LDS keeps a wave's accesses in order
+      T* sq = sQD[wave][0];
+      T* sd = sQD[wave][1];
+      const int wr = (lane >> 2) * QS + (lane & 3) * 8;
+      *reinterpret_cast<Op*>(sq + wr) = qn0;
+      *reinterpret_cast<Op*>(sq + wr + 16 * QS) = qn1;
+      *reinterpret_cast<Op*>(sd + wr) = dn0;
+      *reinterpret_cast<Op*>(sd + wr + 16 * QS) = dn1;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        qf[qb] = *reinterpret_cast<const Op*>(sq + (qb * 16 + l16) * QS + 8 * g);
+        df[qb] = *reinterpret_cast<const Op*>(sd + (qb * 16 + l16) * QS + 8 * g);
+      }
+    } else {
+      qf[0] = qn0; qf[1] = qn1;
+      df[0] = dn0; df[1] = dn1;
+    }
     const float l2[2] = {l2n0, l2n1};
     const float dd[2] = {ddn0, ddn1};
     __syncthreads();
