@@ -115,11 +115,14 @@ __device__ __forceinline__ void fetch_kv(KVRaw<T>& raw, const T* kline,
   const int ch = t & 3;
   if constexpr (sizeof(T) == 2) {
     // K and V alike: one 16-byte chunk (8 dims of one key) per thread, so a
-    // wave's load touches 16 keys x 64 bytes.
-    const int kk = k0 + (t >> 2);
-    const int64_t off = (int64_t)kk * pos_stride + ch * 8;
-    raw.k = kk < N ? *reinterpret_cast<const u32x4*>(kline + off) : u32x4{0, 0, 0, 0};
-    raw.v = kk < N ? *reinterpret_cast<const u32x4*>(vline + off) : u32x4{0, 0, 0, 0};
+    // wave's load touches 16 keys x 64 bytes.  Buffer loads: the tile offset
+    // is scalar, the lane's offset fixed, and keys at or past N (past the
+    // range) read zeros.
+    const uint32_t nbytes = (uint32_t)((N - 1) * pos_stride + C) * 2u;
+    const uint32_t voff = (uint32_t)((t >> 2) * pos_stride + ch * 8) * 2u;
+    const uint32_t soff = (uint32_t)(k0 * pos_stride) * 2u;
+    raw.k = buf_ld128(kline, nbytes, voff, soff);
+    raw.v = buf_ld128(vline, nbytes, voff, soff);
   } else {
     const int kk = min(k0 + (t >> 2), N - 1);
     const int p = t & 31, vc = t >> 5;               // V: key pair, 4-dim chunk
@@ -332,11 +335,11 @@ attn_fwd_kernel(FwdParams p) {
 
   // This lane's 8 bias values of (qb, half) in key tile `tile` sit at
   // bbase + tile * BQ*BK + (qb*2 + half) * 512 (prepared tile order).
-  const T* bbase = HAS_BIAS ? static_cast<const T*>(p.biasp) +
-                                  ((((int64_t)b * H + h) * (p.Nq / BQ) + qt) *
-                                       (p.Nk / BK) * (BQ * BK) +
-                                   wave * 2048 + lane * 8)
-                            : nullptr;
+  const T* btile = HAS_BIAS ? static_cast<const T*>(p.biasp) +
+                                  (((int64_t)b * H + h) * (p.Nq / BQ) + qt) *
+                                      (p.Nk / BK) * (BQ * BK)
+                            : nullptr;  // this workgroup's row of tiles
+  const T* bbase = HAS_BIAS ? btile + wave * 2048 + lane * 8 : nullptr;
   const uint8_t* mrow[ROWS];
   if constexpr (ROW_MASK) {
 #pragma unroll
@@ -349,13 +352,22 @@ attn_fwd_kernel(FwdParams p) {
   // after the next barrier: the loads stay in flight across the K/V tile
   // store instead of being waited for at the end of the tile.
   Raw8<T> braw[2][2];  // [qb][half]
+  // (bf16: buffer loads from the workgroup's tile row with the lane's offset
+  // fixed, like the K/V tiles)
+  const uint32_t bvoff = (uint32_t)(wave * 2048 + lane * 8) * (uint32_t)sizeof(T);
+  const uint32_t bbytes = (uint32_t)(p.Nk / BK) * (BQ * BK) * (uint32_t)sizeof(T);  // the row
 #define EVO_FETCH_BIAS(k0_)                                                        \
   do {                                                                         \
     if constexpr (HAS_BIAS) {                                                  \
       for (int qb = 0; qb < 2; ++qb)                                           \
-        for (int half = 0; half < 2; ++half)                                   \
-          ld_raw8(braw[qb][half],                                              \
-                         bbase + (int64_t)((k0_) / BK) * (BQ * BK) + (qb * 2 + half) * 512); \
+        for (int half = 0; half < 2; ++half) {                                 \
+          if constexpr (sizeof(T) == 2)                                        \
+            braw[qb][half].a = buf_ld128(btile, bbytes, bvoff + (qb * 2 + half) * 1024u, \
+                                         (uint32_t)((k0_) / BK) * (BQ * BK * 2u)); \
+          else                                                                 \
+            ld_raw8(braw[qb][half],                                            \
+                    bbase + (int64_t)((k0_) / BK) * (BQ * BK) + (qb * 2 + half) * 512); \
+        }                                                                      \
     }                                                                          \
   } while (0)
 #pragma unroll
@@ -369,11 +381,12 @@ attn_fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int rr = 0; rr < ROWS; ++rr) store_kv<T>(raw[rr], sK[buf][rr], sV[buf][rr]);
     __syncthreads();
-    if (tile + 1 < ntiles) {
+    // The next tile's K/V (after the last tile: keys past N, zeros for bf16,
+    // key N-1 again for fp32; unused).  Unconditional, so that the waits for
+    // these loads are exact.
 #pragma unroll
-      for (int rr = 0; rr < ROWS; ++rr)
-        fetch_kv<T>(raw[rr], kline[rr], vline[rr], k0 + BK, N, pos_stride);
-    }
+    for (int rr = 0; rr < ROWS; ++rr)
+      fetch_kv<T>(raw[rr], kline[rr], vline[rr], k0 + BK, N, pos_stride);
 
     // The tile in two 32-key halves: logits, softmax and PV of one half
     // before the next (half the logit and P registers of a whole tile).  All
@@ -484,8 +497,10 @@ attn_fwd_kernel(FwdParams p) {
             o[rr][qb][cb] = mma32(vf[cb], pf[rr][qb], o[rr][qb][cb]);
       }
     }
-    // next tile's bias operands (the logit registers are free again)
-    if (tile + 1 < ntiles) EVO_FETCH_BIAS(k0 + BK);
+    // next tile's bias operands (the logit registers are free again); bf16
+    // reads past the workgroup's row of tiles as zeros, so it needs no test
+    // and its waits stay exact
+    if (sizeof(T) == 2 || tile + 1 < ntiles) EVO_FETCH_BIAS(k0 + BK);
   }
 
   // Epilogue: normalise, gate, store; LSE in natural log.

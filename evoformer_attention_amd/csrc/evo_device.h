@@ -173,6 +173,24 @@ __device__ __forceinline__ bf16x8 lds_read_tr_op(const void* p0, const void* p1)
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// 16-byte buffer load from base + soff + voff.  `base` and `soff` must be the
+// same across the wave (they go to scalar registers: the buffer resource and
+// the scalar offset); `voff` is the lane's byte offset.  Kept in one
+// register for a whole loop, `voff` leaves no per-load address registers
+// behind, so nothing waits for a load in flight before reusing them.  Bytes
+// at or past `nbytes` read as zero (the buffer range check).
+__device__ __forceinline__ u32x4 buf_ld128(const void* base, uint32_t nbytes, uint32_t voff,
+                                           uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)nbytes, 0x00020000);
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+#else
+  (void)base; (void)nbytes; (void)voff; (void)soff;
+  return u32x4{};
+#endif
+}
+
 // Workgroups are dispatched round-robin over the XCDs (workgroup i runs on
 // XCD i % 8).  Remap so that XCD x receives the contiguous work range
 // [x * per, (x + 1) * per): neighbouring work items, which share inputs,
