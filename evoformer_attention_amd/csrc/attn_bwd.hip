@@ -335,7 +335,8 @@ bwd_dkdv_kernel(BwdParams p) {
   if (h >= p.H) return;  // odd H: the missing partner of the last pair
   const int b = line / p.R, r = line - b * p.R;
   const int N = p.N, H = p.H, Np = p.Np;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar
   const int l16 = lane & 15, g = lane >> 4;
   const int64_t lh = (int64_t)line * H + h;
   const int pos_stride = H * C;
@@ -377,19 +378,33 @@ bwd_dkdv_kernel(BwdParams p) {
     }
 
   // Staging: thread -> (tensor: Q or dO, query row, 8-dim chunk).  Each
-  // 32-query step is stored twice in LDS from the same registers: row-major
-  // (the S and dP operands) and transposed with the queries in slot order
-  // (the dV and dK operands).  Queries past N read query N-1 (finite; their
-  // P and dS are 0).
-  const int srow = (tid >> 2) & 31, sch = tid & 3, sten = tid >> 7;
-  const T* ssrc = (sten == 0 ? Q : DO) + lbase + sch * 8;
+  // 32-query step is stored in LDS row-major (the S and dP operands); bf16
+  // reads the transposed dV and dK operands from there, fp32 also stores
+  // them transposed with the queries in slot order.
+  // Loads: bf16 uses buffer loads, with the wave's row base (waves 0-1 load
+  // Q, 2-3 dO) and the step offset in scalar registers and the lane's offset
+  // fixed, so no address register is rewritten while a prefetch is in
+  // flight; query rows past N read zeros (their P and dS are 0).  fp32
+  // clamps to query N-1.
+  const int srow = (tid >> 2) & 31, sch = tid & 3, sten = wave >> 1;
+  const T* sbase = (sten == 0 ? Q : DO) + lbase;
+  const T* ssrc = sbase + sch * 8;
+  const uint32_t s_nbytes = (uint32_t)((N - 1) * pos_stride + C) * (uint32_t)sizeof(T);
+  const uint32_t s_voff = (uint32_t)(srow * pos_stride + sch * 8) * (uint32_t)sizeof(T);
+  // LSE (lanes 0-31 of each wave) and -D (lanes 32-63).  Every wave loads
+  // and stores them, so that no branch makes the waits for the other loads
+  // conservative.
+  const float* lsrc = ((lane & 32) ? p.dd : p.lse2) + lh * Np;
   const int sslot = query_slot(srow);
   auto fetch = [&](StageRaw<T>& raw, int q0) {
-    const T* src = ssrc + (int64_t)min(q0 + srow, N - 1) * pos_stride;
-    raw.a = reinterpret_cast<const u32x4*>(src)[0];
-    if constexpr (sizeof(T) == 4) raw.b = reinterpret_cast<const u32x4*>(src)[1];
-    raw.l = (tid < 64) ? (tid < 32 ? p.lse2[lh * Np + q0 + tid] : p.dd[lh * Np + q0 + tid - 32])
-                       : 0.f;
+    if constexpr (sizeof(T) == 2) {
+      raw.a = buf_ld128(sbase, s_nbytes, s_voff, (uint32_t)(q0 * pos_stride) * 2u);
+    } else {
+      const T* src = ssrc + (int64_t)min(q0 + srow, N - 1) * pos_stride;
+      raw.a = reinterpret_cast<const u32x4*>(src)[0];
+      raw.b = reinterpret_cast<const u32x4*>(src)[1];
+    }
+    raw.l = lsrc[min(q0 + (lane & 31), Np - 1)];
   };
   auto store = [&](const StageRaw<T>& raw, int buf) {
     T* drow = sT[buf][sten] + srow * RS + sch * 8;
@@ -407,29 +422,46 @@ bwd_dkdv_kernel(BwdParams p) {
         d32[(4 + j) * RS] = raw.b[j];
       }
     }
-    if (tid < 64) sL[buf][tid >> 5][tid & 31] = raw.l;
+    // every wave writes the same values (no branch, see the LSE load)
+    sL[buf][lane >> 5][lane & 31] = raw.l;
   };
   (void)E16;
-  // next step's bias^T operands, raw until the step's barrier has passed
-  Raw8<T> bn[2];  // [qb]
-
-  StageRaw<T> raw;
-  fetch(raw, 0);
-  ld_raw8(bn[0], BPT);
-  ld_raw8(bn[1], BPT + 8);
+  // A step's bias^T operands (bf16: buffer loads; past this workgroup's
+  // blocks they read zeros; fp32: the step index is clamped).
   const int nsteps = (N + 31) / 32;
-  for (int st = 0; st < nsteps; ++st) {
+  const T* bpt_w = static_cast<const T*>(p.bpt) +
+                   ((int64_t)(b * H + h) * nkt + kt) * (Np / 32) * 4096 + wave * 1024;  // the wave's base
+  const uint32_t b_nbytes = (uint32_t)((Np / 32) * 4096 - wave * 1024) * (uint32_t)sizeof(T);
+  auto fetch_bias = [&](Raw8<T> (&bn)[2], int st) {
+    if constexpr (sizeof(T) == 2) {
+      const uint32_t so = (uint32_t)st * 4096u * 2u;
+      bn[0].a = buf_ld128(bpt_w, b_nbytes, (uint32_t)lane * 32u, so);
+      bn[1].a = buf_ld128(bpt_w, b_nbytes, (uint32_t)lane * 32u + 16u, so);
+    } else {
+      const T* src = BPT + (int64_t)min(st, nsteps - 1) * 4096;
+      ld_raw8(bn[0], src);
+      ld_raw8(bn[1], src + 8);
+    }
+  };
+
+  // One 32-query step: stage `cur` (fetched a step earlier), then fetch the
+  // next step into `nxt` while this one computes.  Two register sets used in
+  // turn, so that no prefetch is copied; the fetches are unconditional, so
+  // that every wait for them is exact.
+  auto step = [&](int st, const StageRaw<T>& cur, StageRaw<T>& nxt, const Raw8<T> (&bc)[2],
+                  Raw8<T> (&bx)[2]) {
     const int q0 = st * 32, buf = st & 1;
-    store(raw, buf);
+    // keep the scheduler from hoisting this store (and its wait for the
+    // prefetch) into the previous step
+    __builtin_amdgcn_sched_barrier(0);
+    store(cur, buf);
     __syncthreads();
     f32x4 cbias[2][2];  // [qb][kb]
-    widen8(bn[0], cbias[0][0], cbias[0][1]);
-    widen8(bn[1], cbias[1][0], cbias[1][1]);
-    if (st + 1 < nsteps) {
-      fetch(raw, q0 + 32);
-      ld_raw8(bn[0], BPT + (int64_t)(st + 1) * 4096);
-      ld_raw8(bn[1], BPT + (int64_t)(st + 1) * 4096 + 8);
-    }
+    widen8(bc[0], cbias[0][0], cbias[0][1]);
+    widen8(bc[1], cbias[1][0], cbias[1][1]);
+    fetch(nxt, q0 + 32);
+    fetch_bias(bx, st + 1);
+    __builtin_amdgcn_sched_barrier(0);  // issue the prefetch here, not later
     const T* sQ = sT[buf][0];
     const T* sDO = sT[buf][1];
 
@@ -482,7 +514,17 @@ bwd_dkdv_kernel(BwdParams p) {
         dk[cb][kb] = mma32(qtf, sf, dk[cb][kb]);
       }
     }
+  };
+  StageRaw<T> ra, rb;
+  Raw8<T> ba[2], bb[2];
+  fetch(ra, 0);
+  fetch_bias(ba, 0);
+  int st = 0;
+  for (; st + 1 < nsteps; st += 2) {
+    step(st, ra, rb, ba, bb);
+    step(st + 1, rb, ra, bb, ba);
   }
+  if (st < nsteps) step(st, ra, rb, ba, bb);
 
   // Store: lane holds dims cb*16 + 4g + i of key kbase + kb*16 + l16.
   T* DK = static_cast<T*>(p.dk);
