@@ -593,7 +593,9 @@ template <> struct BLds<float> { static constexpr int KS = 36, TS = 68; };
 // 64-key tiles (K, V rows key-permuted) through double-buffered LDS.  Lane = query: S^T = K Q^T + bias, P = exp2(S - LSE), dP^T = V dO^T,
 // dS = P (dP - D), dQ^T += K^T dS^T.
 template <typename T, bool ROW_MASK>
-__global__ void __launch_bounds__(256) bwd_dq_kernel(BwdParams p) {
+__global__ void __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 && !ROW_MASK ? 4 : 1)))
+bwd_dq_kernel(BwdParams p) {
   using Op = typename Tr<T>::Op;
   constexpr int KS = BLds<T>::KS, TS = BLds<T>::TS;
   // bf16 reads K^T straight from the key-permuted K tile (lds_read_tr16);
@@ -614,7 +616,8 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdParams p) {
   if (h >= p.H) return;
   const int b = line / p.R, r = line - b * p.R;
   const int N = p.N, H = p.H, Np = p.Np;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar
   const int l16 = lane & 15, g = lane >> 4;
   const int pos_stride = H * C;
   const int64_t lbase = (int64_t)line * N * pos_stride + h * C;
@@ -649,11 +652,38 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdParams p) {
 
   u32x4 rk0, rk1, rv0, rv1;
   rk1 = rv1 = u32x4{0, 0, 0, 0};
-  EVO_FETCH_K(T, K, V, 0);
+  // bf16 tile loads are buffer loads: the workgroup's (wave's) base and the
+  // tile offset in scalar registers, the lane's offset fixed for the loop,
+  // so no address registers are rewritten while a prefetch is in flight;
+  // keys past N and tiles past this workgroup's row read zeros.  fp32 uses
+  // clamped addresses.
+  const uint32_t kv_nbytes = (uint32_t)((N - 1) * pos_stride + C) * 2u;
+  const uint32_t kv_voff = (uint32_t)((tid >> 2) * pos_stride + (tid & 3) * 8) * 2u;
+  const T* BPw = static_cast<const T*>(p.bp) +
+                 (((int64_t)(b * H + h) * nqt + qt) * (Np / 64)) * 8192 + wave * 2048;
+  const uint32_t b_nbytes = (uint32_t)((Np / 64) * 8192 - wave * 2048) * 2u;
+  auto fetch_tile = [&](int tile) {
+    if constexpr (sizeof(T) == 2) {
+      const uint32_t so = (uint32_t)(tile * 64 * pos_stride) * 2u;
+      rk0 = buf_ld128(K, kv_nbytes, kv_voff, so);
+      rv0 = buf_ld128(V, kv_nbytes, kv_voff, so);
+      const uint32_t bo = (uint32_t)tile * 8192u * 2u;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
+      for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-    for (int half = 0; half < 2; ++half) ld_raw8(bn[qb][half], BP + (qb * 2 + half) * 512);
+        for (int half = 0; half < 2; ++half)
+          bn[qb][half].a = buf_ld128(BPw, b_nbytes, (uint32_t)lane * 16u + (qb * 2 + half) * 1024u, bo);
+    } else {
+      const int nt = min(tile, (N + 63) / 64 - 1);
+      EVO_FETCH_K(T, K, V, nt * 64);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+          ld_raw8(bn[qb][half], BP + (int64_t)nt * 8192 + (qb * 2 + half) * 512);
+    }
+  };
+  fetch_tile(0);
   const int ntiles = (N + 63) / 64;
   for (int tile = 0; tile < ntiles; ++tile) {
     const int k0 = tile * 64, buf = tile & 1;
@@ -664,16 +694,12 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdParams p) {
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
       for (int half = 0; half < 2; ++half) widen8(bn[qb][half], cb_[qb][half][0], cb_[qb][half][1]);
-    // next tile (the last iteration re-fetches its own tile, unused)
-    EVO_FETCH_K(T, K, V, min(k0 + 64, (ntiles - 1) * 64));
-    {
-      const int nt = min(tile + 1, ntiles - 1);
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int half = 0; half < 2; ++half)
-          ld_raw8(bn[qb][half], BP + (int64_t)nt * 8192 + (qb * 2 + half) * 512);
-    }
+    // next tile (after the last: zeros for bf16, the last tile again for
+    // fp32; unused)
+    fetch_tile(tile + 1);
+    // issue that prefetch here: left to itself, the scheduler sinks it to
+    // the end of the tile, next to the store that waits for it
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       f32x4 s[2][2], dp[2][2];  // [qb][kb]; dP starts from -D
