@@ -300,8 +300,8 @@ __global__ void __launch_bounds__(256) bwd_bias_kernel(BwdParams p) {
 }
 
 // ----------------------------------------------------------------- dK, dV
-// Staged per 32-query step: Q rows, dO rows (row-major) and the slot-ordered
-// Q^T and dO^T slabs, each [32][32] (+pad); base-2 LSE and D.
+// Staged per 32-query step: Q rows and dO rows (row-major; fp32 also the
+// slot-ordered Q^T and dO^T slabs), each [32][32] (+pad); base-2 LSE and -D.
 template <typename T> struct StageRaw;  // one 16-byte chunk (fp32: two)
 template <> struct StageRaw<bf16_t> { u32x4 a; float l; };
 template <> struct StageRaw<float> { u32x4 a, b; float l; };
