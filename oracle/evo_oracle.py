@@ -44,7 +44,9 @@ __all__ = [
     "sigmoid", "attention_line_probs", "attention_line_forward",
     "attention_forward", "attention_line_backward", "attention_backward",
     "dbias_query_rows", "layer_norm", "tri_project", "tri_out_project",
-    "tri_module_forward", "tri_module_lines",
+    "tri_module_forward", "tri_module_lines", "layer_norm_backward",
+    "tri_out_project_backward", "tri_project_backward",
+    "tri_module_backward",
 ]
 
 
@@ -355,3 +357,103 @@ def tri_module_forward(z, residue_mask, ln_w, ln_b, eps, w_q, w_k, w_v, w_g,
                              w_g, b_g, w_bias, w_o, b_o, H, C, ending,
                              list(range(N)))
     return lines.transpose(1, 0, 2) if ending else lines
+
+
+# ----------------------------------------------------------------------------
+# Backward of the triangle attention module.
+#
+# [MEGAFOLD] item 1 trains with the fused kernels in both directions, and
+# item 3 fuses the layer normalisation with the projections that follow it;
+# the pages print no formula for either backward, so the plain chain rule of
+# the forward above is written out here (a reading: the derivative of the
+# definition, nothing else).  Weight gradients are summed over every pair
+# position; the input gradient is returned in z layout.
+# ----------------------------------------------------------------------------
+
+def layer_norm_backward(x, w, eps, dy):
+    """Gradients of y = (x - mean) / sqrt(var + eps) * w + b over the last
+    axis (population variance).  Returns dx (shaped like x) and dw, db
+    summed over every leading axis.  With xhat the normalised input,
+    rstd = 1 / sqrt(var + eps) and dxhat = dy * w:
+        dx = rstd * (dxhat - mean(dxhat) - xhat * mean(dxhat * xhat))."""
+    x = np.asarray(x, np.float64)
+    n = x.shape[-1]
+    mu = x.mean(axis=-1, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
+    rstd = 1.0 / np.sqrt(var + eps)
+    xhat = (x - mu) * rstd
+    dxhat = dy * w
+    dx = rstd * (dxhat - dxhat.mean(axis=-1, keepdims=True)
+                 - xhat * (dxhat * xhat).mean(axis=-1, keepdims=True))
+    dw = (dy * xhat).reshape(-1, n).sum(axis=0)
+    db = dy.reshape(-1, n).sum(axis=0)
+    return dx, dw, db
+
+
+def _to_lines(t, ending):
+    """[N, N, ...] z layout -> line layout (line a, place n): z[a, n] for the
+    starting node, z[n, a] for the ending node.  Its own inverse."""
+    return t.transpose((1, 0) + tuple(range(2, t.ndim))) if ending else t
+
+
+def tri_out_project_backward(o, w_o, dout, ending):
+    """Backward of tri_out_project.  o [1, N, N, H, C] (line layout),
+    w_o [CZ, H*C], dout [N, N, CZ] (z layout).  Returns d_o like o,
+    dw_o [CZ, H*C] and db_o [CZ]."""
+    _, N, _, H, C = o.shape
+    dy = _to_lines(np.asarray(dout, np.float64), ending)   # [line, place, CZ]
+    ol = o[0].reshape(N, N, H * C)
+    d_o = (dy @ w_o).reshape(1, N, N, H, C)
+    CZ = w_o.shape[0]
+    dw_o = dy.reshape(-1, CZ).T @ ol.reshape(-1, H * C)
+    db_o = dy.reshape(-1, CZ).sum(axis=0)
+    return d_o, dw_o, db_o
+
+
+def tri_project_backward(z, ln_w, ln_b, eps, w_q, w_k, w_v, w_g, w_bias,
+                         dq, dk, dv, dg, dbias, ending):
+    """Backward of tri_project.  dq, dk, dv, dg: [1, N, N, H, C] (line
+    layout), dbias: [1, H, N, N] (bias[h, a, n] is the projection of the
+    line-layout position (a, n) in both orientations).  Returns a dict with
+    dz [N, N, CZ], dln_w, dln_b [CZ], dw_q, dw_k, dw_v, dw_g [H*C, CZ],
+    db_g [H*C] and dw_bias [H, CZ]."""
+    z = np.asarray(z, np.float64)
+    N, _, CZ = z.shape
+    H = w_bias.shape[0]
+    HC = w_q.shape[0]
+    xl = _to_lines(layer_norm(z, ln_w, ln_b, eps), ending)   # [line, place, CZ]
+    flat = {n: t[0].reshape(N, N, HC) for n, t in
+            (("q", dq), ("k", dk), ("v", dv), ("g", dg))}
+    db = np.moveaxis(dbias[0], 0, -1)                          # [line, place, H]
+    dxl = (flat["q"] @ w_q + flat["k"] @ w_k + flat["v"] @ w_v
+           + flat["g"] @ w_g + db @ w_bias)
+    X = xl.reshape(-1, CZ)
+    res = {f"dw_{n}": flat[n].reshape(-1, HC).T @ X for n in "qkvg"}
+    res["db_g"] = flat["g"].reshape(-1, HC).sum(axis=0)
+    res["dw_bias"] = db.reshape(-1, H).T @ X
+    dz, res["dln_w"], res["dln_b"] = layer_norm_backward(
+        z, ln_w, eps, _to_lines(dxl, ending))
+    res["dz"] = dz
+    return res
+
+
+def tri_module_backward(z, residue_mask, ln_w, ln_b, eps, w_q, w_k, w_v, w_g,
+                        b_g, w_bias, w_o, b_o, H, C, ending, dout):
+    """Gradients of <dout, tri_module_forward(...)> with respect to z and
+    every parameter: the forward recomputed (projections, attention with the
+    residue mask on keys), then tri_out_project_backward,
+    attention_backward and tri_project_backward.  Returns a dict with the
+    entries of tri_project_backward plus dw_o [CZ, H*C] and db_o [CZ]."""
+    q, k, v, g, bias = tri_project(z, ln_w, ln_b, eps, w_q, w_k, w_v, w_g,
+                                   b_g, w_bias, H, C, ending)
+    N = q.shape[1]
+    key_mask = (None if residue_mask is None else
+                (np.asarray(residue_mask) != 0).astype(np.uint8).reshape(1, 1, N))
+    o, _ = attention_forward(q, k, v, g, key_mask, bias)
+    d_o, dw_o, db_o = tri_out_project_backward(o, w_o, dout, ending)
+    dq, dk, dv, dg, dbias = attention_backward(q, k, v, g, key_mask, bias, d_o)
+    res = tri_project_backward(z, ln_w, ln_b, eps, w_q, w_k, w_v, w_g, w_bias,
+                               dq, dk, dv, dg, dbias, ending)
+    res["dw_o"] = dw_o
+    res["db_o"] = db_o
+    return res

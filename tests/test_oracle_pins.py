@@ -510,3 +510,126 @@ def test_module_lines_subset_against_project():
         sub = O.tri_module_lines(lines=[3], ending=ending, **d)[0]
         ref = out[:, 3] if ending else out[3]
         np.testing.assert_allclose(sub, ref, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------- module backward
+
+MODULE_PARAMS = ("z", "ln_w", "ln_b", "w_q", "w_k", "w_v", "w_g", "b_g",
+                 "w_bias", "w_o", "b_o")
+
+
+def module_grads(d, ending, dout):
+    g = O.tri_module_backward(ending=ending, dout=dout, **d)
+    return {"z": g["dz"], "ln_w": g["dln_w"], "ln_b": g["dln_b"],
+            "w_q": g["dw_q"], "w_k": g["dw_k"], "w_v": g["dw_v"],
+            "w_g": g["dw_g"], "b_g": g["db_g"], "w_bias": g["dw_bias"],
+            "w_o": g["dw_o"], "b_o": g["db_o"]}
+
+
+def _module_fd_pin(ending, seed=40):
+    """Every gradient entry of the module against a central difference of
+    <dout, module(...)> (fp64, step 1e-6), residue mask on."""
+    d = module_case(seed, N=4, CZ=5, H=2, C=2)
+    dout = rnd(seed + 1, 4, 4, 5)
+    grads = module_grads(d, ending, dout)
+    eps = 1e-6
+    for name in MODULE_PARAMS:
+        base = d[name]
+        num = np.zeros_like(base)
+        it = np.nditer(base, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            e = dict(d)
+            plus = base.copy(); plus[idx] += eps
+            minus = base.copy(); minus[idx] -= eps
+            e[name] = plus
+            lp = float((module(e, ending) * dout).sum())
+            e[name] = minus
+            lm = float((module(e, ending) * dout).sum())
+            num[idx] = (lp - lm) / (2 * eps)
+        np.testing.assert_allclose(grads[name], num, rtol=1e-6, atol=1e-8,
+                                   err_msg=f"gradient of {name}")
+
+
+@pytest.mark.parametrize("ending", [False, True])
+def test_module_backward_matches_central_finite_differences(ending):
+    _module_fd_pin(ending)
+
+
+def _torch_module(t, H, C, ending, keep):
+    """The module written with torch library routines (fp64): layer_norm,
+    linear, softmax, sigmoid; line layout by transposing z for the ending
+    node."""
+    z = t["z"]
+    N, _, CZ = z.shape
+    x = F.layer_norm(z, (CZ,), t["ln_w"], t["ln_b"], 1e-5)
+    xl = x.transpose(0, 1) if ending else x
+    q, k, v = (F.linear(xl, t[w]).reshape(N, N, H, C) for w in ("w_q", "w_k", "w_v"))
+    g = F.linear(xl, t["w_g"], t["b_g"]).reshape(N, N, H, C)
+    bias = F.linear(xl, t["w_bias"]).permute(2, 0, 1)          # [h, query, key]
+    s = torch.einsum("lqhc,lkhc->lhqk", q, k) / C ** 0.5 + bias[None]
+    s = s.masked_fill(~keep[None, None, None, :], float("-inf"))
+    o = torch.einsum("lhqk,lkhc->lqhc", torch.softmax(s, dim=-1), v)
+    y = F.linear((o * torch.sigmoid(g)).reshape(N, N, H * C), t["w_o"], t["b_o"])
+    return y.transpose(0, 1) if ending else y
+
+
+@pytest.mark.parametrize("ending", [False, True])
+def test_module_backward_matches_torch_autograd(ending):
+    """Library routine: torch.autograd through the module written with
+    torch.nn.functional (fp64, CPU)."""
+    d = module_case(42, N=9, CZ=12, H=2, C=4)
+    dout = rnd(43, 9, 9, 12)
+    grads = module_grads(d, ending, dout)
+    t = {n: torch.tensor(d[n], requires_grad=True) for n in MODULE_PARAMS}
+    keep = torch.tensor(d["residue_mask"] != 0)
+    y = _torch_module(t, d["H"], d["C"], ending, keep)
+    (y * torch.tensor(dout)).sum().backward()
+    for n in MODULE_PARAMS:
+        np.testing.assert_allclose(grads[n], t[n].grad.numpy(), rtol=1e-9,
+                                   atol=1e-11, err_msg=n)
+
+
+def test_module_backward_closed_forms():
+    """Sum over channels of dz is 0 at every position (LayerNorm is
+    invariant to adding a constant to a position's channels), and db_o is the
+    sum of dout over positions."""
+    d = module_case(44, N=6, CZ=8, H=2, C=3)
+    dout = rnd(45, 6, 6, 8)
+    for ending in (False, True):
+        g = module_grads(d, ending, dout)
+        np.testing.assert_allclose(g["z"].sum(-1), 0, atol=1e-12)
+        np.testing.assert_allclose(g["b_o"], dout.sum((0, 1)), rtol=1e-12)
+
+
+def test_layer_norm_backward_matches_torch():
+    x = rnd(46, 4, 3, 11)
+    w = rnd(47, 11)
+    dy = rnd(48, 4, 3, 11)
+    tx, tw, tb = (torch.tensor(a, requires_grad=True) for a in (x, w, rnd(49, 11)))
+    (F.layer_norm(tx, (11,), tw, tb, 1e-5) * torch.tensor(dy)).sum().backward()
+    dx, dw, db = O.layer_norm_backward(x, w, 1e-5, dy)
+    for got, ref in ((dx, tx.grad), (dw, tw.grad), (db, tb.grad)):
+        np.testing.assert_allclose(got, ref.numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_mutant_layer_norm_backward_without_variance_term_is_caught(monkeypatch):
+    def no_var_term(x, w, eps, dy):
+        x = np.asarray(x, np.float64)
+        n = x.shape[-1]
+        mu = x.mean(axis=-1, keepdims=True)
+        rstd = 1.0 / np.sqrt(((x - mu) ** 2).mean(axis=-1, keepdims=True) + eps)
+        xhat = (x - mu) * rstd
+        dxhat = dy * w
+        dx = rstd * (dxhat - dxhat.mean(axis=-1, keepdims=True))
+        return dx, (dy * xhat).reshape(-1, n).sum(0), dy.reshape(-1, n).sum(0)
+    monkeypatch.setattr(O, "layer_norm_backward", no_var_term)
+    with pytest.raises(AssertionError):
+        _module_fd_pin(False)
+
+
+def test_mutant_ending_gradient_left_in_line_layout_is_caught(monkeypatch):
+    monkeypatch.setattr(O, "_to_lines", lambda t, ending: t)
+    _module_fd_pin(False)  # the starting node does not transpose
+    with pytest.raises(AssertionError):
+        _module_fd_pin(True)
