@@ -19,7 +19,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libevoattn.so")
-SOURCES = ["evo_api.cpp", "attn_fwd.hip", "attn_bwd.hip", "tri_project.hip"]
+SOURCES = ["evo_api.cpp", "attn_fwd.hip", "attn_bwd.hip", "tri_project.hip",
+           "tri_module_bwd.hip"]
 ARCH = "gfx950"
 
 

@@ -373,4 +373,242 @@ evo_status_t tri_attn_module_fwd(evo_dtype_t dtype, int64_t N, int64_t CZ,
   }
 }
 
+
+// ---------------------------------------------------------------- backward
+
+static evo_status_t check_module_bwd_sizes(evo_dtype_t dtype, int64_t N,
+                                           int64_t CZ, int64_t H, int64_t C) {
+  evo_status_t st = check_module_sizes(dtype, N, CZ, H, C);
+  if (st != EVO_OK) return st;
+  if (CZ > 128 || H * C > 128)
+    return fail(EVO_ENOTSUP, "the module backward supports CZ <= 128 and "
+                "H*C <= 128 (CZ=%lld, H*C=%lld)", (long long)CZ,
+                (long long)(H * C));
+  return EVO_OK;
+}
+
+size_t tri_attn_proj_bwd_workspace_bytes(evo_dtype_t dtype, int64_t N,
+                                         int64_t CZ, int64_t H, int64_t C) {
+  const std::string saved = g_last_error;
+  const evo_status_t st = check_module_bwd_sizes(dtype, N, CZ, H, C);
+  g_last_error = saved;
+  if (st != EVO_OK) return 0;
+  return evo::proj_bwd_workspace(N, CZ, H);
+}
+
+// Workspace layout of tri_attn_module_bwd: q | k | v | g | o | do | dq | dk
+// | dv | dg (each N*N*H*C elements) | bias (H*N*N elements) | lse and dbias
+// (fp32) | the attention forward's and backward's workspaces | the
+// projection backward's workspace, each region 256-byte aligned.
+struct ModuleBwdLayout {
+  size_t t, bias, lse, dbias, fwd, bwd, proj, total;
+};
+static ModuleBwdLayout module_bwd_layout(evo_dtype_t dtype, int64_t N,
+                                         int64_t CZ, int64_t H, int64_t C) {
+  const size_t es = elem_size(dtype);
+  ModuleBwdLayout L;
+  L.t = align256((size_t)N * N * H * C * es);
+  L.bias = 10 * L.t;
+  L.lse = L.bias + align256((size_t)H * N * N * es);
+  L.dbias = L.lse + align256((size_t)N * H * N * 4);
+  L.fwd = L.dbias + align256((size_t)H * N * N * 4);
+  L.bwd = L.fwd + align256(evo::attn_fwd_workspace((int)dtype, 1, N, H));
+  L.proj = L.bwd + align256(evo::attn_bwd_workspace((int)dtype, 1, N, N, H));
+  L.total = L.proj + align256(evo::proj_bwd_workspace(N, CZ, H));
+  return L;
+}
+
+size_t tri_attn_bwd_workspace_bytes(evo_dtype_t dtype, int64_t N, int64_t CZ,
+                                    int64_t H, int64_t C) {
+  const std::string saved = g_last_error;
+  const evo_status_t st = check_module_bwd_sizes(dtype, N, CZ, H, C);
+  g_last_error = saved;
+  if (st != EVO_OK) return 0;
+  return module_bwd_layout(dtype, N, CZ, H, C).total;
+}
+
+static evo_status_t check_workspace(const char* fn, void* workspace,
+                                    size_t workspace_bytes, size_t need) {
+  if (!workspace || workspace_bytes < need)
+    return fail(EVO_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given",
+                fn, need, workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace))
+    return fail(EVO_ENOTSUP, "argument 'workspace' is not 16-byte aligned");
+  return EVO_OK;
+}
+
+evo_status_t tri_attn_out_project_bwd(evo_dtype_t dtype, int64_t N,
+                                      int64_t CZ, int64_t H, int64_t C,
+                                      int ending, const void* o,
+                                      const void* w_o, const void* dout,
+                                      void* d_o, float* dw_o, float* db_o,
+                                      void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  try {
+    evo_status_t st = check_module_bwd_sizes(dtype, N, CZ, H, C);
+    if (st != EVO_OK) return st;
+    if (ending != 0 && ending != 1)
+      return fail(EVO_EINVAL, "ending=%d must be 0 or 1", ending);
+    REQUIRE_PTR(o);
+    REQUIRE_PTR(w_o);
+    REQUIRE_PTR(dout);
+    REQUIRE_PTR(d_o);
+    REQUIRE_PTR(dw_o);
+    REQUIRE_PTR(db_o);
+    st = check_workspace("tri_attn_out_project_bwd", workspace, workspace_bytes,
+                         evo::proj_bwd_workspace(N, CZ, H));
+    if (st != EVO_OK) return st;
+    if (fault_injected())
+      return fail(EVO_EHIP, "tri_attn_out_project_bwd: injected launch failure");
+    evo::OutProjectBwdArgs a{(int)dtype, N, CZ, H, ending, o, w_o, dout, d_o,
+                             dw_o, db_o, workspace};
+    return from_hip(evo::launch_out_project_bwd(a, (hipStream_t)stream),
+                    "tri_attn_out_project_bwd");
+  } catch (...) {
+    return fail(EVO_EINTERNAL, "tri_attn_out_project_bwd: internal error");
+  }
+}
+
+evo_status_t tri_attn_project_bwd(
+    evo_dtype_t dtype, int64_t N, int64_t CZ, int64_t H, int64_t C, int ending,
+    const void* z, const void* ln_w, const void* ln_b, float ln_eps,
+    const void* w_q, const void* w_k, const void* w_v, const void* w_g,
+    const void* w_bias, const void* dq, const void* dk, const void* dv,
+    const void* dg, const float* dbias, void* dz, float* dln_w, float* dln_b,
+    float* dw_q, float* dw_k, float* dw_v, float* dw_g, float* db_g,
+    float* dw_bias, void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    evo_status_t st = check_module_bwd_sizes(dtype, N, CZ, H, C);
+    if (st != EVO_OK) return st;
+    if (ending != 0 && ending != 1)
+      return fail(EVO_EINVAL, "ending=%d must be 0 or 1", ending);
+    if (!(ln_eps > 0.f)) return fail(EVO_EINVAL, "ln_eps must be > 0");
+    REQUIRE_PTR(z);
+    REQUIRE_PTR(ln_w);
+    REQUIRE_PTR(ln_b);
+    REQUIRE_PTR(w_q);
+    REQUIRE_PTR(w_k);
+    REQUIRE_PTR(w_v);
+    REQUIRE_PTR(w_g);
+    REQUIRE_PTR(w_bias);
+    REQUIRE_PTR(dq);
+    REQUIRE_PTR(dk);
+    REQUIRE_PTR(dv);
+    REQUIRE_PTR(dg);
+    REQUIRE_PTR(dbias);
+    REQUIRE_PTR(dz);
+    REQUIRE_PTR(dln_w);
+    REQUIRE_PTR(dln_b);
+    REQUIRE_PTR(dw_q);
+    REQUIRE_PTR(dw_k);
+    REQUIRE_PTR(dw_v);
+    REQUIRE_PTR(dw_g);
+    REQUIRE_PTR(db_g);
+    REQUIRE_PTR(dw_bias);
+    st = check_workspace("tri_attn_project_bwd", workspace, workspace_bytes,
+                         evo::proj_bwd_workspace(N, CZ, H));
+    if (st != EVO_OK) return st;
+    if (fault_injected())
+      return fail(EVO_EHIP, "tri_attn_project_bwd: injected launch failure");
+    evo::ProjectBwdArgs a{(int)dtype, N, CZ, H, ending, z, ln_w, ln_b, ln_eps,
+                          w_q, w_k, w_v, w_g, w_bias, dq, dk, dv, dg, dbias,
+                          dz, dln_w, dln_b, dw_q, dw_k, dw_v, dw_g, db_g,
+                          dw_bias, workspace};
+    return from_hip(evo::launch_project_bwd(a, (hipStream_t)stream),
+                    "tri_attn_project_bwd");
+  } catch (...) {
+    return fail(EVO_EINTERNAL, "tri_attn_project_bwd: internal error");
+  }
+}
+
+evo_status_t tri_attn_module_bwd(
+    evo_dtype_t dtype, int64_t N, int64_t CZ, int64_t H, int64_t C, int ending,
+    const void* z, const uint8_t* residue_mask, const void* ln_w,
+    const void* ln_b, float ln_eps, const void* w_q, const void* w_k,
+    const void* w_v, const void* w_g, const void* b_g, const void* w_bias,
+    const void* w_o, const void* dout, void* dz, float* dln_w, float* dln_b,
+    float* dw_q, float* dw_k, float* dw_v, float* dw_g, float* db_g,
+    float* dw_bias, float* dw_o, float* db_o, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  try {
+    evo_status_t st = check_module_bwd_sizes(dtype, N, CZ, H, C);
+    if (st != EVO_OK) return st;
+    if (ending != 0 && ending != 1)
+      return fail(EVO_EINVAL, "ending=%d must be 0 or 1", ending);
+    if (!(ln_eps > 0.f)) return fail(EVO_EINVAL, "ln_eps must be > 0");
+    REQUIRE_PTR(z);
+    REQUIRE_PTR(ln_w);
+    REQUIRE_PTR(ln_b);
+    REQUIRE_PTR(w_q);
+    REQUIRE_PTR(w_k);
+    REQUIRE_PTR(w_v);
+    REQUIRE_PTR(w_g);
+    REQUIRE_PTR(w_bias);
+    REQUIRE_PTR(w_o);
+    REQUIRE_PTR(dout);
+    REQUIRE_PTR(dz);
+    REQUIRE_PTR(dln_w);
+    REQUIRE_PTR(dln_b);
+    REQUIRE_PTR(dw_q);
+    REQUIRE_PTR(dw_k);
+    REQUIRE_PTR(dw_v);
+    REQUIRE_PTR(dw_g);
+    REQUIRE_PTR(db_g);
+    REQUIRE_PTR(dw_bias);
+    REQUIRE_PTR(dw_o);
+    REQUIRE_PTR(db_o);
+    OPTIONAL_PTR(b_g);
+    OPTIONAL_PTR(residue_mask);
+    const ModuleBwdLayout L = module_bwd_layout(dtype, N, CZ, H, C);
+    st = check_workspace("tri_attn_module_bwd", workspace, workspace_bytes, L.total);
+    if (st != EVO_OK) return st;
+    if (fault_injected())
+      return fail(EVO_EHIP, "tri_attn_module_bwd: injected launch failure");
+
+    char* ws = static_cast<char*>(workspace);
+    void* q = ws;
+    void* k = ws + L.t;
+    void* v = ws + 2 * L.t;
+    void* g = ws + 3 * L.t;
+    void* o = ws + 4 * L.t;
+    void* d_o = ws + 5 * L.t;
+    void* dq = ws + 6 * L.t;
+    void* dk = ws + 7 * L.t;
+    void* dv = ws + 8 * L.t;
+    void* dg = ws + 9 * L.t;
+    void* bias = ws + L.bias;
+    float* lse = reinterpret_cast<float*>(ws + L.lse);
+    float* dbias = reinterpret_cast<float*>(ws + L.dbias);
+    hipStream_t s = (hipStream_t)stream;
+
+    // the forward's activations, recomputed from z
+    evo::ProjectArgs pa{(int)dtype, N, CZ, H, ending, z, ln_w, ln_b, ln_eps,
+                        w_q, w_k, w_v, w_g, b_g, w_bias, q, k, v, g, bias};
+    st = from_hip(evo::launch_project(pa, s), "tri_attn_module_bwd/project");
+    if (st != EVO_OK) return st;
+    evo::AttnFwdArgs fa{(int)dtype, 1, N, N, H, q, k, v, g, residue_mask, 1,
+                        bias, o, lse, ws + L.fwd};
+    st = from_hip(evo::launch_attn_fwd(fa, s), "tri_attn_module_bwd/attention");
+    if (st != EVO_OK) return st;
+    // backward, last step first
+    evo::OutProjectBwdArgs ob{(int)dtype, N, CZ, H, ending, o, w_o, dout, d_o,
+                              dw_o, db_o, ws + L.proj};
+    st = from_hip(evo::launch_out_project_bwd(ob, s),
+                  "tri_attn_module_bwd/out_project_bwd");
+    if (st != EVO_OK) return st;
+    evo::AttnBwdArgs ab{(int)dtype, 1, N, N, H, q, k, v, g, residue_mask, 1,
+                        bias, o, lse, d_o, dq, dk, dv, dg, dbias, ws + L.bwd};
+    st = from_hip(evo::launch_attn_bwd(ab, s), "tri_attn_module_bwd/attention_bwd");
+    if (st != EVO_OK) return st;
+    evo::ProjectBwdArgs pb{(int)dtype, N, CZ, H, ending, z, ln_w, ln_b, ln_eps,
+                           w_q, w_k, w_v, w_g, w_bias, dq, dk, dv, dg, dbias,
+                           dz, dln_w, dln_b, dw_q, dw_k, dw_v, dw_g, db_g,
+                           dw_bias, ws + L.proj};
+    return from_hip(evo::launch_project_bwd(pb, s),
+                    "tri_attn_module_bwd/project_bwd");
+  } catch (...) {
+    return fail(EVO_EINTERNAL, "tri_attn_module_bwd: internal error");
+  }
+}
+
 }  // extern "C"

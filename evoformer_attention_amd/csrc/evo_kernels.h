@@ -75,6 +75,49 @@ struct OutProjectArgs {
   void* out;
 };
 
+struct OutProjectBwdArgs {
+  int dtype;
+  int64_t N, CZ, H;
+  int ending;
+  const void* o;
+  const void* w_o;
+  const void* dout;
+  void* d_o;
+  float* dw_o;
+  float* db_o;
+  void* workspace;  // proj_bwd_workspace bytes
+};
+
+struct ProjectBwdArgs {
+  int dtype;
+  int64_t N, CZ, H;
+  int ending;
+  const void* z;
+  const void* ln_w;
+  const void* ln_b;
+  float eps;
+  const void* w_q;
+  const void* w_k;
+  const void* w_v;
+  const void* w_g;
+  const void* w_bias;
+  const void* dq;
+  const void* dk;
+  const void* dv;
+  const void* dg;
+  const float* dbias;
+  void* dz;
+  float* dln_w;
+  float* dln_b;
+  float* dw_q;
+  float* dw_k;
+  float* dw_v;
+  float* dw_g;
+  float* db_g;
+  float* dw_bias;
+  void* workspace;  // proj_bwd_workspace bytes
+};
+
 constexpr int kHeadDim = 32;
 
 size_t attn_fwd_workspace(int dtype, int64_t B, int64_t N, int64_t H);
@@ -84,5 +127,8 @@ size_t attn_bwd_workspace(int dtype, int64_t B, int64_t R, int64_t N,
 hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t s);
 hipError_t launch_project(const ProjectArgs& a, hipStream_t s);
 hipError_t launch_out_project(const OutProjectArgs& a, hipStream_t s);
+size_t proj_bwd_workspace(int64_t N, int64_t CZ, int64_t H);
+hipError_t launch_out_project_bwd(const OutProjectBwdArgs& a, hipStream_t s);
+hipError_t launch_project_bwd(const ProjectBwdArgs& a, hipStream_t s);
 
 }  // namespace evo

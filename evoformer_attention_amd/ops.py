@@ -16,7 +16,10 @@ __all__ = ["EvoAttnError", "lib", "evo_abi_version", "evo_attn_fwd",
            "evo_attn_bwd", "evo_attn_bwd_workspace_bytes",
            "evo_attn_fwd_workspace_bytes", "tri_attn_project",
            "tri_attn_out_project", "tri_attn_module_fwd",
-           "tri_attn_workspace_bytes", "LIB_PATH", "EXPORTS"]
+           "tri_attn_workspace_bytes", "tri_attn_proj_bwd_workspace_bytes",
+           "tri_attn_out_project_bwd", "tri_attn_project_bwd",
+           "tri_attn_bwd_workspace_bytes", "tri_attn_module_bwd",
+           "LIB_PATH", "EXPORTS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
                         "libevoattn.so")
@@ -52,6 +55,18 @@ EXPORTS = {
     "tri_attn_module_fwd": (_I, [_I, _I64, _I64, _I64, _I64, _I, _P, _P, _P,
                                  _P, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                  _P, _SZ, _P]),
+    "tri_attn_proj_bwd_workspace_bytes": (_SZ, [_I, _I64, _I64, _I64, _I64]),
+    "tri_attn_out_project_bwd": (_I, [_I, _I64, _I64, _I64, _I64, _I, _P, _P,
+                                      _P, _P, _P, _P, _P, _SZ, _P]),
+    "tri_attn_project_bwd": (_I, [_I, _I64, _I64, _I64, _I64, _I, _P, _P, _P,
+                                  _F, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                  _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                  _SZ, _P]),
+    "tri_attn_bwd_workspace_bytes": (_SZ, [_I, _I64, _I64, _I64, _I64]),
+    "tri_attn_module_bwd": (_I, [_I, _I64, _I64, _I64, _I64, _I, _P, _P, _P,
+                                 _P, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                 _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                 _SZ, _P]),
 }
 
 
@@ -270,3 +285,110 @@ def tri_attn_module_fwd(z, residue_mask, ln_w, ln_b, eps, w_q, w_k, w_v, w_g,
                                    workspace.numel(), _stream(z.device))
     _check("tri_attn_module_fwd", st)
     return out
+
+
+def _f32(shape, device):
+    return torch.empty(shape, dtype=torch.float32, device=device)
+
+
+def tri_attn_proj_bwd_workspace_bytes(dtype, N, CZ, H, C):
+    code = EVO_BF16 if dtype == torch.bfloat16 else EVO_FP32
+    return lib().tri_attn_proj_bwd_workspace_bytes(code, N, CZ, H, C)
+
+
+def tri_attn_bwd_workspace_bytes(dtype, N, CZ, H, C):
+    code = EVO_BF16 if dtype == torch.bfloat16 else EVO_FP32
+    return lib().tri_attn_bwd_workspace_bytes(code, N, CZ, H, C)
+
+
+def _workspace(need, device, workspace):
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    return workspace
+
+
+def tri_attn_out_project_bwd(o, w_o, dout, ending, workspace=None):
+    """Backward of tri_attn_out_project -> (d_o, dw_o fp32, db_o fp32)."""
+    _dev_tensor("o", o)
+    _, N, _, H, C = o.shape
+    dt = o.dtype
+    _dev_tensor("w_o", w_o, dt)
+    _dev_tensor("dout", dout, dt)
+    CZ = w_o.shape[0]
+    workspace = _workspace(tri_attn_proj_bwd_workspace_bytes(dt, N, CZ, H, C),
+                           o.device, workspace)
+    d_o = torch.empty_like(o)
+    dw_o = _f32((CZ, H * C), o.device)
+    db_o = _f32((CZ,), o.device)
+    st = lib().tri_attn_out_project_bwd(
+        _dtype_code(o), N, CZ, H, C, int(ending), _ptr(o), _ptr(w_o),
+        _ptr(dout), _ptr(d_o), _ptr(dw_o), _ptr(db_o), _ptr(workspace),
+        workspace.numel(), _stream(o.device))
+    _check("tri_attn_out_project_bwd", st)
+    return d_o, dw_o, db_o
+
+
+_PARAM_GRADS = ("dln_w", "dln_b", "dw_q", "dw_k", "dw_v", "dw_g", "db_g",
+                "dw_bias")
+
+
+def _param_grads(CZ, H, C, device):
+    HC = H * C
+    shapes = dict(dln_w=(CZ,), dln_b=(CZ,), dw_q=(HC, CZ), dw_k=(HC, CZ),
+                  dw_v=(HC, CZ), dw_g=(HC, CZ), db_g=(HC,), dw_bias=(H, CZ))
+    return {n: _f32(shapes[n], device) for n in _PARAM_GRADS}
+
+
+def tri_attn_project_bwd(z, ln_w, ln_b, eps, w_q, w_k, w_v, w_g, w_bias, dq,
+                         dk, dv, dg, dbias, H, C, ending, workspace=None):
+    """Backward of tri_attn_project -> dict with dz and the fp32 parameter
+    gradients (dln_w, dln_b, dw_q, dw_k, dw_v, dw_g, db_g, dw_bias)."""
+    _dev_tensor("z", z)
+    N, _, CZ = z.shape
+    dt = z.dtype
+    for name, t in (("ln_w", ln_w), ("ln_b", ln_b), ("w_q", w_q), ("w_k", w_k),
+                    ("w_v", w_v), ("w_g", w_g), ("w_bias", w_bias), ("dq", dq),
+                    ("dk", dk), ("dv", dv), ("dg", dg)):
+        _dev_tensor(name, t, dt)
+    _dev_tensor("dbias", dbias, torch.float32)
+    workspace = _workspace(tri_attn_proj_bwd_workspace_bytes(dt, N, CZ, H, C),
+                           z.device, workspace)
+    res = _param_grads(CZ, H, C, z.device)
+    res["dz"] = torch.empty_like(z)
+    st = lib().tri_attn_project_bwd(
+        _dtype_code(z), N, CZ, H, C, int(ending), _ptr(z), _ptr(ln_w),
+        _ptr(ln_b), float(eps), _ptr(w_q), _ptr(w_k), _ptr(w_v), _ptr(w_g),
+        _ptr(w_bias), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbias),
+        _ptr(res["dz"]), *(_ptr(res[n]) for n in _PARAM_GRADS),
+        _ptr(workspace), workspace.numel(), _stream(z.device))
+    _check("tri_attn_project_bwd", st)
+    return res
+
+
+def tri_attn_module_bwd(z, residue_mask, ln_w, ln_b, eps, w_q, w_k, w_v, w_g,
+                        b_g, w_bias, w_o, dout, H, C, ending, workspace=None):
+    """Gradients of the module forward -> dict with dz and the fp32
+    parameter gradients (those of tri_attn_project_bwd plus dw_o, db_o)."""
+    _dev_tensor("z", z)
+    N, _, CZ = z.shape
+    dt = z.dtype
+    for name, t in (("ln_w", ln_w), ("ln_b", ln_b), ("w_q", w_q), ("w_k", w_k),
+                    ("w_v", w_v), ("w_g", w_g), ("b_g", b_g),
+                    ("w_bias", w_bias), ("w_o", w_o), ("dout", dout)):
+        _dev_tensor(name, t, dt)
+    _dev_tensor("residue_mask", residue_mask, torch.uint8)
+    workspace = _workspace(tri_attn_bwd_workspace_bytes(dt, N, CZ, H, C),
+                           z.device, workspace)
+    res = _param_grads(CZ, H, C, z.device)
+    res["dz"] = torch.empty_like(z)
+    res["dw_o"] = _f32((CZ, H * C), z.device)
+    res["db_o"] = _f32((CZ,), z.device)
+    st = lib().tri_attn_module_bwd(
+        _dtype_code(z), N, CZ, H, C, int(ending), _ptr(z), _ptr(residue_mask),
+        _ptr(ln_w), _ptr(ln_b), float(eps), _ptr(w_q), _ptr(w_k), _ptr(w_v),
+        _ptr(w_g), _ptr(b_g), _ptr(w_bias), _ptr(w_o), _ptr(dout),
+        _ptr(res["dz"]), *(_ptr(res[n]) for n in _PARAM_GRADS),
+        _ptr(res["dw_o"]), _ptr(res["db_o"]), _ptr(workspace),
+        workspace.numel(), _stream(z.device))
+    _check("tri_attn_module_bwd", st)
+    return res

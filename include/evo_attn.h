@@ -213,6 +213,106 @@ evo_status_t tri_attn_module_fwd(evo_dtype_t dtype, int64_t N, int64_t CZ,
                                  const void* b_o, void* out, void* workspace,
                                  size_t workspace_bytes, void* stream);
 
+/*
+ * Backward of the triangle-attention module.
+ *
+ * The pages train with the fused kernels in both directions ("MegaFold:
+ * Efficient Training of Next-Generation 3D Attention Protein Models on
+ * Cross-Platform GPUs", section "Methodologie", items 1 and 3) but print no
+ * formula for the backward; these calls compute the chain rule of the
+ * forward defined by tri_attn_project, evo_attn_fwd and tri_attn_out_project.
+ * Input gradients are in the working dtype; parameter gradients are fp32,
+ * summed over every pair position, and overwrite their buffers.  The results
+ * are deterministic (no atomics; sums in a fixed order).
+ *
+ * Sizes: as for the forward, and in addition CZ <= 128 and H*C <= 128
+ * (otherwise EVO_ENOTSUP).  Pointers: caller-owned device memory, 16-byte
+ * aligned (EVO_ENOTSUP otherwise), NULL only where stated (EVO_EINVAL).
+ * The calls enqueue on `stream` and return at once.
+ */
+
+/* Bytes of device workspace tri_attn_out_project_bwd and
+ * tri_attn_project_bwd need (0 if they would reject the sizes). */
+size_t tri_attn_proj_bwd_workspace_bytes(evo_dtype_t dtype, int64_t N,
+                                         int64_t CZ, int64_t H, int64_t C);
+
+/*
+ * tri_attn_out_project_bwd -- backward of tri_attn_out_project.
+ *
+ *   o      [1,N,N,H,C] dtype, the forward's input (line layout).
+ *   w_o    [CZ, H*C] dtype ([out, in]).
+ *   dout   [N,N,CZ] dtype, gradient of the output (z layout).
+ *   d_o    [1,N,N,H,C] dtype out: dout (line order) . w_o.
+ *   dw_o   [CZ, H*C] fp32 out: sum over positions of dout^T o.
+ *   db_o   [CZ] fp32 out: sum over positions of dout.
+ *   workspace  tri_attn_proj_bwd_workspace_bytes(...) bytes.
+ */
+evo_status_t tri_attn_out_project_bwd(evo_dtype_t dtype, int64_t N,
+                                      int64_t CZ, int64_t H, int64_t C,
+                                      int ending, const void* o,
+                                      const void* w_o, const void* dout,
+                                      void* d_o, float* dw_o, float* db_o,
+                                      void* workspace, size_t workspace_bytes,
+                                      void* stream);
+
+/*
+ * tri_attn_project_bwd -- backward of tri_attn_project (LayerNorm and the
+ * Q, K, V, gate and pair-bias projections), fused like the forward: the
+ * normalised pair representation is recomputed from z and never stored.
+ *
+ *   z, ln_w, ln_b, ln_eps, w_q, w_k, w_v, w_g, w_bias, ending: as given to
+ *              tri_attn_project.
+ *   dq,dk,dv,dg  [1,N,N,H,C] dtype: gradients of q, k, v and of the
+ *              pre-sigmoid gate g (as evo_attn_bwd returns them).
+ *   dbias      [1,H,N,N] fp32: gradient of the projected pair bias.
+ *   dz         [N,N,CZ] dtype out: gradient of z.
+ *   dln_w, dln_b  [CZ] fp32 out.
+ *   dw_q,dw_k,dw_v,dw_g  [H*C, CZ] fp32 out; db_g [H*C] fp32 out (the gate
+ *              bias; its gradient is the sum of dg).
+ *   dw_bias    [H, CZ] fp32 out.
+ *   workspace  tri_attn_proj_bwd_workspace_bytes(...) bytes.
+ */
+evo_status_t tri_attn_project_bwd(
+    evo_dtype_t dtype, int64_t N, int64_t CZ, int64_t H, int64_t C, int ending,
+    const void* z, const void* ln_w, const void* ln_b, float ln_eps,
+    const void* w_q, const void* w_k, const void* w_v, const void* w_g,
+    const void* w_bias, const void* dq, const void* dk, const void* dv,
+    const void* dg, const float* dbias, void* dz, float* dln_w, float* dln_b,
+    float* dw_q, float* dw_k, float* dw_v, float* dw_g, float* db_g,
+    float* dw_bias, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace tri_attn_module_bwd needs (0 if it would reject
+ * the sizes): the recomputed activations and their gradients, O(N^2 * H *
+ * C). */
+size_t tri_attn_bwd_workspace_bytes(evo_dtype_t dtype, int64_t N, int64_t CZ,
+                                    int64_t H, int64_t C);
+
+/*
+ * tri_attn_module_bwd -- gradients of the whole module forward
+ * (tri_attn_module_fwd) with respect to z and every parameter, given the
+ * gradient of its output.  The forward's activations are recomputed from z
+ * (tri_attn_project, evo_attn_fwd with the log-sum-exp), then
+ * tri_attn_out_project_bwd, evo_attn_bwd (residue mask on keys, pair-bias
+ * gradient summed over lines) and tri_attn_project_bwd run in turn.
+ *
+ *   z, residue_mask, ln_w, ln_b, ln_eps, w_q, w_k, w_v, w_g, b_g, w_bias,
+ *   w_o, ending: as given to tri_attn_module_fwd (b_o does not enter the
+ *              gradients).
+ *   dout       [N,N,CZ] dtype: gradient of the module's output.
+ *   dz ... dw_bias: as in tri_attn_project_bwd; dw_o, db_o: as in
+ *              tri_attn_out_project_bwd.
+ *   workspace  tri_attn_bwd_workspace_bytes(...) bytes.
+ */
+evo_status_t tri_attn_module_bwd(
+    evo_dtype_t dtype, int64_t N, int64_t CZ, int64_t H, int64_t C, int ending,
+    const void* z, const uint8_t* residue_mask, const void* ln_w,
+    const void* ln_b, float ln_eps, const void* w_q, const void* w_k,
+    const void* w_v, const void* w_g, const void* b_g, const void* w_bias,
+    const void* w_o, const void* dout, void* dz, float* dln_w, float* dln_b,
+    float* dw_q, float* dw_k, float* dw_v, float* dw_g, float* db_g,
+    float* dw_bias, float* dw_o, float* db_o, void* workspace,
+    size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -165,3 +165,64 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(ops, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         ops.lib()
+
+
+def test_module_bwd_workspace_queries():
+    p = L.tri_attn_proj_bwd_workspace_bytes(1, 768, 128, 4, 32)
+    assert 0 < p < 64 << 20  # chunk partials of the weight gradients only
+    m = L.tri_attn_bwd_workspace_bytes(1, 768, 128, 4, 32)
+    # ten activation-sized tensors (q k v g o and their gradients) and more
+    assert m >= 10 * 768 * 768 * 128 * 2 + p
+    assert m < 12 * 768 * 768 * 128 * 2 + 64 << 20
+    assert L.tri_attn_bwd_workspace_bytes(1, 64, 256, 4, 32) == 0   # CZ > 128
+    assert L.tri_attn_proj_bwd_workspace_bytes(1, 64, 128, 8, 32) == 0  # H*C > 128
+    assert L.tri_attn_bwd_workspace_bytes(1, 64, 96, 2, 16) == 0   # C != 32
+
+
+def module_bwd(**kw):
+    a = dict(dt=1, N=64, CZ=128, H=4, C=32, ending=0, eps=1e-5, ws=FAKE,
+             wsb=1 << 40, mask=None, dz=FAKE)
+    a.update(kw)
+    return L.tri_attn_module_bwd(
+        a["dt"], a["N"], a["CZ"], a["H"], a["C"], a["ending"], FAKE, a["mask"],
+        FAKE, FAKE, a["eps"], FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE,
+        a["dz"], *([FAKE] * 10), a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(ending=2), ops.EVO_EINVAL, "ending"),
+    (dict(eps=0.0), ops.EVO_EINVAL, "ln_eps"),
+    (dict(dz=None), ops.EVO_EINVAL, "'dz' is NULL"),
+    (dict(dz=MISALIGNED), ops.EVO_ENOTSUP, "aligned"),
+    (dict(wsb=10), ops.EVO_EWORKSPACE, "workspace"),
+    (dict(CZ=256), ops.EVO_ENOTSUP, "CZ <= 128"),
+    (dict(H=8), ops.EVO_ENOTSUP, "H*C <= 128"),
+    (dict(dt=7), ops.EVO_ENOTSUP, "dtype"),
+])
+def test_module_bwd_validation(kw, status, needle):
+    assert module_bwd(**kw) == status
+    assert needle in err()
+
+
+def test_project_bwd_validation():
+    args = [1, 64, 128, 4, 32, 1, FAKE, FAKE, FAKE, -1.0] + [FAKE] * 10 + \
+        [FAKE] * 9 + [FAKE, 1 << 40, None]
+    assert L.tri_attn_project_bwd(*args) == ops.EVO_EINVAL
+    assert "ln_eps" in err()
+    args[9] = 1e-5
+    args[19] = None  # dbias
+    assert L.tri_attn_project_bwd(*args) == ops.EVO_EINVAL
+    assert "'dbias' is NULL" in err()
+    args[19] = FAKE
+    args[30] = 100
+    assert L.tri_attn_project_bwd(*args) == ops.EVO_EWORKSPACE
+    assert L.tri_attn_out_project_bwd(1, 64, 128, 4, 32, 0, FAKE, FAKE, FAKE,
+                                      FAKE, None, FAKE, FAKE, 1 << 40,
+                                      None) == ops.EVO_EINVAL
+    assert "'dw_o' is NULL" in err()
+
+
+def test_module_bwd_fault_injection(monkeypatch):
+    monkeypatch.setenv("EVO_FAULT_INJECT", "launch")
+    assert module_bwd() == ops.EVO_EHIP
+    assert "injected" in err()

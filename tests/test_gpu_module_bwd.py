@@ -1,0 +1,158 @@
+"""GPU parity of the module backward entry points against the fp64 oracle:
+tri_attn_out_project_bwd, tri_attn_project_bwd and tri_attn_module_bwd,
+called through the C ABI.  Weight gradients are sums over every pair
+position, so they are compared in units of their largest entry (the "peak"
+scale of helpers.compare), as dBias is."""
+import numpy as np
+import pytest
+import torch
+
+import oracle.evo_oracle as O
+from evoformer_attention_amd import ops, synth
+from helpers import compare, dev, log, np64, npu8
+
+pytestmark = pytest.mark.gpu
+
+PARAM_NAMES = ("dln_w", "dln_b", "dw_q", "dw_k", "dw_v", "dw_g", "db_g",
+               "dw_bias")
+
+
+def _draw(gen, shape, dtype, std=1.0):
+    return synth.round_to(torch.randn(shape, generator=gen) * std, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("ending", [False, True])
+@pytest.mark.parametrize("N,CZ,H", [(45, 96, 3), (8, 32, 1)])
+def test_out_project_bwd_parity(dtype, ending, N, CZ, H):
+    log(f"case out_project_bwd {dtype} N={N} CZ={CZ} H={H} ending={ending}")
+    gen = torch.Generator().manual_seed(N + CZ)
+    o = _draw(gen, (1, N, N, H, 32), dtype)
+    w_o = _draw(gen, (CZ, H * 32), dtype, (H * 32) ** -0.5)
+    dout = _draw(gen, (N, N, CZ), dtype)
+    d_o, dw_o, db_o = ops.tri_attn_out_project_bwd(dev(o), dev(w_o), dev(dout), ending)
+    torch.cuda.synchronize()
+    r_do, r_dw, r_db = O.tri_out_project_backward(np64(o), np64(w_o), np64(dout), ending)
+    compare("d_o", np64(d_o), r_do, dtype)
+    compare("dw_o", np64(dw_o), r_dw, "fp32" if dtype == "fp32" else "bf16", scale="peak")
+    compare("db_o", np64(db_o), r_db, dtype, scale="peak")
+
+
+def _proj_case(N, CZ, H, dtype, seed):
+    d = synth.rand_module(N, CZ, H, 32, dtype, seed=seed, ln_affine=True,
+                          gate_bias=True)
+    gen = torch.Generator().manual_seed(1000 + seed)
+    for name in ("dq", "dk", "dv", "dg"):
+        d[name] = _draw(gen, (1, N, N, H, 32), dtype)
+    d["dbias"] = torch.randn((1, H, N, N), generator=gen) * 4.0  # fp32, row sums
+    return d
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("ending", [False, True])
+@pytest.mark.parametrize("N,CZ,H", [(37, 64, 2), (70, 128, 4), (5, 32, 1), (33, 96, 3)])
+def test_project_bwd_parity(dtype, ending, N, CZ, H):
+    log(f"case project_bwd {dtype} N={N} CZ={CZ} H={H} ending={ending}")
+    d = _proj_case(N, CZ, H, dtype, seed=N + H)
+    got = ops.tri_attn_project_bwd(
+        dev(d["z"]), dev(d["ln_w"]), dev(d["ln_b"]), d["eps"], dev(d["w_q"]),
+        dev(d["w_k"]), dev(d["w_v"]), dev(d["w_g"]), dev(d["w_bias"]),
+        dev(d["dq"]), dev(d["dk"]), dev(d["dv"]), dev(d["dg"]), dev(d["dbias"]),
+        H, 32, ending)
+    torch.cuda.synchronize()
+    ref = O.tri_project_backward(
+        np64(d["z"]), np64(d["ln_w"]), np64(d["ln_b"]), d["eps"],
+        np64(d["w_q"]), np64(d["w_k"]), np64(d["w_v"]), np64(d["w_g"]),
+        np64(d["w_bias"]), np64(d["dq"]), np64(d["dk"]), np64(d["dv"]),
+        np64(d["dg"]), np64(d["dbias"]), ending)
+    compare("dz", np64(got["dz"]), ref["dz"], dtype)
+    for name in PARAM_NAMES:
+        compare(name, np64(got[name]), ref[name], dtype, scale="peak")
+
+
+def _module_case(N, CZ, H, dtype, seed, mask):
+    d = synth.rand_module(N, CZ, H, 32, dtype, seed=seed, mask=mask,
+                          ln_affine=True, gate_bias=True, out_bias=True)
+    gen = torch.Generator().manual_seed(2000 + seed)
+    d["dout"] = _draw(gen, (N, N, CZ), dtype)
+    return d
+
+
+def _gpu_module_bwd(d, H, ending):
+    g = ops.tri_attn_module_bwd(
+        dev(d["z"]), dev(d["mask"]), dev(d["ln_w"]), dev(d["ln_b"]), d["eps"],
+        dev(d["w_q"]), dev(d["w_k"]), dev(d["w_v"]), dev(d["w_g"]),
+        dev(d["b_g"]), dev(d["w_bias"]), dev(d["w_o"]), dev(d["dout"]), H, 32,
+        ending)
+    torch.cuda.synchronize()
+    return g
+
+
+def _oracle_module_bwd(d, H, ending):
+    return O.tri_module_backward(
+        np64(d["z"]), npu8(d["mask"]), np64(d["ln_w"]), np64(d["ln_b"]),
+        d["eps"], np64(d["w_q"]), np64(d["w_k"]), np64(d["w_v"]),
+        np64(d["w_g"]), np64(d["b_g"]), np64(d["w_bias"]), np64(d["w_o"]),
+        np64(d["b_o"]), H, 32, ending, np64(d["dout"]))
+
+
+def _w_ext_gain(d):
+    """max over channels c of ||W_ext[:, c]||_2, W_ext = the Q, K, V, gate and
+    pair-bias weights stacked along their output rows.  In the whole-module
+    backward dz is formed from dX = [dq dk dv dg dbias] . W_ext, whose
+    inputs are themselves bf16 results of the attention backward (each within
+    the bf16 bar), so an error of the bar's size in every input reaches dX
+    multiplied by up to this factor (errors of independent sign add in
+    quadrature); the LayerNorm backward then scales it by rstd * gamma ~ 1."""
+    w = np.concatenate([np64(d[n]) for n in ("w_q", "w_k", "w_v", "w_g", "w_bias")])
+    return max(1.0, float(np.sqrt((w ** 2).sum(0)).max()))
+
+
+def _compare_module(got, ref, dtype, d):
+    compare("dz", np64(got["dz"]), ref["dz"], dtype, scale=_w_ext_gain(d))
+    for name in PARAM_NAMES + ("dw_o", "db_o"):
+        compare(name, np64(got[name]), ref[name], dtype, scale="peak")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("ending", [False, True])
+@pytest.mark.parametrize("masked", [False, True])
+def test_module_bwd_small_parity(dtype, ending, masked):
+    N, CZ, H = 67, 64, 2
+    log(f"case module_bwd {dtype} N={N} ending={ending} masked={masked}")
+    d = _module_case(N, CZ, H, dtype, seed=5 + ending, mask="random5" if masked else None)
+    _compare_module(_gpu_module_bwd(d, H, ending), _oracle_module_bwd(d, H, ending), dtype, d)
+
+
+def test_module_bwd_c128_h4_parity():
+    """c_z = 128, 4 heads (the pages' pair width), ending node, masked
+    residues, bf16: several position tiles, the full contraction of the
+    projection backward (4 x 128 + the pair-bias block) and a ragged tail."""
+    N, CZ, H = 100, 128, 4
+    log(f"case module_bwd bf16 N={N} CZ={CZ} H={H} ending masked")
+    d = _module_case(N, CZ, H, "bf16", seed=11, mask="random5")
+    _compare_module(_gpu_module_bwd(d, H, True), _oracle_module_bwd(d, H, True), "bf16", d)
+
+
+def test_module_bwd_tri_end_768_properties():
+    """Full size (z [768,768,128], ending node, 38 residues masked, bf16):
+    properties that hold at any size.  Every position's dz sums to ~0 over
+    channels (LayerNorm is invariant to a shift of a position's channels);
+    db_o is the sum of dout over positions (computed in fp64 here); two runs
+    agree bit for bit; everything is finite."""
+    log("case module_bwd tri_end_768")
+    w = synth.WORKLOADS["tri_end_768"]
+    N, CZ, H = w["N"], w["CZ"], w["H"]
+    d = synth.module_inputs("tri_end_768")
+    gen = torch.Generator().manual_seed(7)
+    d["dout"] = _draw(gen, (N, N, CZ), "bf16")
+    g1 = _gpu_module_bwd(d, H, True)
+    g2 = _gpu_module_bwd(d, H, True)
+    for name in g1:
+        assert torch.equal(g1[name], g2[name]), f"{name} differs between runs"
+        assert torch.isfinite(g1[name]).all(), name
+    dz = g1["dz"].float()
+    s = dz.sum(-1).abs()
+    bound = 2.0 ** -8 * dz.abs().sum(-1) + 1e-6
+    assert bool((s <= bound).all()), float((s / bound).max())
+    compare("db_o", np64(g1["db_o"]), np64(d["dout"]).sum((0, 1)), "bf16", scale="peak")
