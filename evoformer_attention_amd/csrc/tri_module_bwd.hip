@@ -141,9 +141,14 @@ __device__ __forceinline__ int wrow_of(int c) {
   return 16 * (2 * s + (j >> 2)) + 4 * gg + (j & 3);
 }
 
-template <typename T, int CB, int WAVES>
-__global__ void __launch_bounds__(WAVES * 64) rowgrad_kernel(RowGradParams p) {
+// NSEG = 4 (the module: q, k, v, gate segments, then the pair-bias block,
+// LayerNorm backward) or 1 (the output projection: one z-layout segment, dX
+// written).  Eight waves, 32 positions per wave per tile.
+template <typename T, int CB, int NSEG>
+__global__ void __launch_bounds__(512) rowgrad_kernel(RowGradParams p) {
   using Op = typename Tr<T>::Op;
+  constexpr int WAVES = 8;
+  constexpr bool LN = NSEG == 4;  // the module: pair-bias block and LayerNorm
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   T* sW = reinterpret_cast<T*>(smem);  // [cout][kc + PADE]
   const int KCS = p.kc + PADE;
@@ -151,7 +156,8 @@ __global__ void __launch_bounds__(WAVES * 64) rowgrad_kernel(RowGradParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
   const int cout = p.cout;  // 16 * CB
-  const int segK = p.nseg * p.seg_w;
+  const int segK = NSEG * p.seg_w;
+  const int seg_steps = p.seg_w / 32;  // 1..4
 
   // W_ext columns [k0, k0 + kn) into LDS (channel-permuted rows).
   auto load_w = [&](int k0, int kn) {
@@ -176,97 +182,117 @@ __global__ void __launch_bounds__(WAVES * 64) rowgrad_kernel(RowGradParams p) {
     __syncthreads();
   }
 
-  const int seg_steps = p.seg_w / 32;  // 1..4
-  for (int tile = blockIdx.x; tile < p.ntiles; tile += gridDim.x) {
+  // Positions of a tile (past the end: position 0, finite, never stored).
+  struct Pos {
     uint32_t pc[2], inrow[2];
     bool live[2];
+  };
+  auto pos_of = [&](int tile) {
+    Pos q;
 #pragma unroll
     for (int pb = 0; pb < 2; ++pb) {
       const uint32_t pidx = ((uint32_t)tile * WAVES + wave) * PW + pb * 16 + l16;
-      live[pb] = pidx < (uint32_t)p.npos;
-      pc[pb] = live[pb] ? pidx : 0u;  // past the end: position 0 (finite, not stored)
-      inrow[pb] = p.in_zrow ? zrow_of(pc[pb], p.N, p.ending) : pc[pb];
+      q.live[pb] = pidx < (uint32_t)p.npos;
+      q.pc[pb] = q.live[pb] ? pidx : 0u;
+      q.inrow[pb] = p.in_zrow ? zrow_of(q.pc[pb], p.N, p.ending) : q.pc[pb];
     }
-    f32x4 acc[CB][2];
+    return q;
+  };
+  // Segment s of a tile: the lane's 8 consecutive contraction values
+  // 32u + 8g .. +7 of its two positions, all steps of the segment.
+  auto load_seg = [&](Op (&x)[4][2], int s, const Pos& q) {
+    const T* src0 = static_cast<const T*>(p.seg[s]) + (int64_t)q.inrow[0] * p.seg_w + 8 * g;
+    const T* src1 = static_cast<const T*>(p.seg[s]) + (int64_t)q.inrow[1] * p.seg_w + 8 * g;
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) acc[cb][0] = acc[cb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // K step ks of the LDS-resident columns starting at column kb: acc +=
-    // W_ext[:, kb + 32ks ..] . x^T for both position blocks.
-    auto mma_step = [&](int kb, const Op (&x)[2]) {
-      const T* wr = sW + kb + 8 * g;
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        const Op a = ld_op<T>(wr + (cb * 16 + l16) * KCS);
-        acc[cb][0] = mma32(a, x[0], acc[cb][0]);
-        acc[cb][1] = mma32(a, x[1], acc[cb][1]);
+    for (int u = 0; u < 4; ++u)
+      if (u < seg_steps) {
+        x[u][0] = ld_op<T>(src0 + 32 * u);
+        x[u][1] = ld_op<T>(src1 + 32 * u);
       }
-    };
-    // One segment at a time (an LDS chunk when the weight is not resident):
-    // the lane's 8 consecutive contraction values 32*ks + 8g .. +7 of its
-    // position, all steps of the segment loaded before the first product.
-    for (int s = 0; s < p.nseg; ++s) {
-      if (!p.resident) {
-        __syncthreads();  // every wave is done with the previous chunk
-        load_w(s * p.seg_w, p.seg_w);
-        __syncthreads();
-      }
-      const int kb = p.resident ? s * p.seg_w : 0;
-      const T* src0 = static_cast<const T*>(p.seg[s]) + (int64_t)inrow[0] * p.seg_w + 8 * g;
-      const T* src1 = static_cast<const T*>(p.seg[s]) + (int64_t)inrow[1] * p.seg_w + 8 * g;
-      Op xf[4][2];
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (u < seg_steps) {
-          xf[u][0] = ld_op<T>(src0 + 32 * u);
-          xf[u][1] = ld_op<T>(src1 + 32 * u);
-        }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (u < seg_steps) {
-          mma_step(kb + 32 * u, xf[u]);
-          // one step's weight fragments live at a time (register budget)
-          __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-    if (p.dbias) {
-      // the pair-bias block: slot j' = 8g + j holds the high part of
-      // dBias[j'] (j' < H) or the low part of dBias[j' - H] (j' < 2H)
-      if (!p.resident) {
-        __syncthreads();
-        load_w(segK, 32);
-        __syncthreads();
-      }
-      Op xb[2];
-#pragma unroll
-      for (int pb = 0; pb < 2; ++pb) {
-        float v[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int slot = 8 * g + j;
-          float x = 0.f;
-          if (slot < 2 * p.H) {
-            const float d = p.dbias[(int64_t)(slot % p.H) * p.npos + pc[pb]];
-            if constexpr (sizeof(T) == 2) {
-              const float hi = (float)(__bf16)d;
-              x = slot < p.H ? hi : d - hi;  // d - hi is exact in fp32
-            } else {
-              x = slot < p.H ? d : 0.f;
-            }
-          }
-          v[j] = x;
-        }
-        xb[pb] = to_op(v, (Op*)nullptr);
-      }
-      mma_step(p.resident ? segK : 0, xb);
-    }
+  };
 
-    // Lane (l16, g) holds dX[position pb*16 + l16][32s + 8g + j] in
-    // acc[2s + j/4][pb][j%4].
+  f32x4 acc[CB][2];
+  // acc += W_ext[:, kb .. kb+31] . x^T for both position blocks
+  auto mma_step = [&](int kb, const Op (&x)[2]) {
+    const T* wr = sW + kb + 8 * g;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const Op a = ld_op<T>(wr + (cb * 16 + l16) * KCS);
+      acc[cb][0] = mma32(a, x[0], acc[cb][0]);
+      acc[cb][1] = mma32(a, x[1], acc[cb][1]);
+    }
+  };
+  auto comp_seg = [&](const Op (&x)[4][2], int s) {
+    if (!p.resident) {
+      __syncthreads();  // every wave is done with the previous chunk
+      load_w(s * p.seg_w, p.seg_w);
+      __syncthreads();
+    }
+    const int kb = p.resident ? s * p.seg_w : 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (u < seg_steps) {
+        mma_step(kb + 32 * u, x[u]);
+        // one step's weight fragments live at a time (register budget)
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  };
+  // The pair-bias block: slot j' = 8g + j holds the high part of dBias[j']
+  // (j' < H) or the low part of dBias[j' - H] (j' < 2H); raw fp32 values.
+  auto load_bias = [&](float (&b)[2][8], const Pos& q) {
+#pragma unroll
+    for (int pb = 0; pb < 2; ++pb)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int slot = 8 * g + j;
+        b[pb][j] = slot < 2 * p.H ? p.dbias[(int64_t)(slot % p.H) * p.npos + q.pc[pb]] : 0.f;
+      }
+  };
+  auto comp_bias = [&](const float (&b)[2][8]) {
+    if (!p.resident) {
+      __syncthreads();
+      load_w(segK, 32);
+      __syncthreads();
+    }
+    Op xb[2];
 #pragma unroll
     for (int pb = 0; pb < 2; ++pb) {
-      if (!p.ln) {
-        if (live[pb]) {
-          T* dst = static_cast<T*>(p.y) + (int64_t)pc[pb] * cout + 8 * g;
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int slot = 8 * g + j;
+        const float d = b[pb][j];
+        if constexpr (sizeof(T) == 2) {
+          const float hi = (float)(__bf16)d;
+          v[j] = slot < p.H ? hi : d - hi;  // d - hi is exact in fp32; 0 past 2H
+        } else {
+          v[j] = slot < p.H ? d : 0.f;
+        }
+      }
+      xb[pb] = to_op(v, (Op*)nullptr);
+    }
+    mma_step(p.resident ? segK : 0, xb);
+  };
+  // The z rows of a tile's positions (LayerNorm backward), as loaded.
+  using ZRaw = Raw8<T>;
+  auto load_z = [&](ZRaw (&zr)[2][CB / 2], const Pos& q) {
+#pragma unroll
+    for (int pb = 0; pb < 2; ++pb) {
+      const uint32_t row = zrow_of(q.pc[pb], p.N, p.ending);
+      const T* src = static_cast<const T*>(p.z) + (int64_t)row * cout + 8 * g;
+#pragma unroll
+      for (int s = 0; s < CB / 2; ++s) ld_raw8(zr[pb][s], src + 32 * s);
+    }
+  };
+
+  // Lane (l16, g) ends a tile with dX[position pb*16 + l16][32s + 8g + j] in
+  // acc[2s + j/4][pb][j%4].
+  auto epilogue = [&](const Pos& q, const ZRaw (&zr)[2][CB / 2]) {
+#pragma unroll
+    for (int pb = 0; pb < 2; ++pb) {
+      if constexpr (!LN) {
+        if (q.live[pb]) {
+          T* dst = static_cast<T*>(p.y) + (int64_t)q.pc[pb] * cout + 8 * g;
 #pragma unroll
           for (int s = 0; s < CB / 2; ++s) {
             float v[8];
@@ -278,344 +304,460 @@ __global__ void __launch_bounds__(WAVES * 64) rowgrad_kernel(RowGradParams p) {
             st8f(dst + 32 * s, v);
           }
         }
-        continue;
-      }
-      // LayerNorm backward of this position (statistics recomputed in fp32,
-      // two-pass, population variance; sums over the 4 lane groups).
-      const uint32_t zr = zrow_of(pc[pb], p.N, p.ending);
-      const T* zsrc = static_cast<const T*>(p.z) + (int64_t)zr * cout + 8 * g;
-      const T* gsrc = static_cast<const T*>(p.ln_w) + 8 * g;
-      float xv[CB / 2][8];
-      float sum = 0.f;
-#pragma unroll
-      for (int s = 0; s < CB / 2; ++s) {
-        ld8f(zsrc + 32 * s, xv[s]);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) sum += xv[s][j];
-      }
-      sum += shfl_xor(sum, 16);
-      sum += shfl_xor(sum, 32);
-      const float inv_n = 1.f / (float)cout;
-      const float mu = sum * inv_n;
-      float var = 0.f;
-#pragma unroll
-      for (int s = 0; s < CB / 2; ++s)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          xv[s][j] -= mu;
-          var = __builtin_fmaf(xv[s][j], xv[s][j], var);
-        }
-      var += shfl_xor(var, 16);
-      var += shfl_xor(var, 32);
-      const float rstd = rsqrtf(var * inv_n + p.eps);
-      float a = 0.f, b = 0.f;
-#pragma unroll
-      for (int s = 0; s < CB / 2; ++s) {
-        float gm[8];
-        ld8f(gsrc + 32 * s, gm);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          xv[s][j] *= rstd;  // xhat
-          const float d = acc[2 * s + (j >> 2)][pb][j & 3] * gm[j];
-          acc[2 * s + (j >> 2)][pb][j & 3] = d;  // dxhat, in place
-          a += d;
-          b = __builtin_fmaf(d, xv[s][j], b);
-        }
-      }
-      a += shfl_xor(a, 16);
-      a += shfl_xor(a, 32);
-      b += shfl_xor(b, 16);
-      b += shfl_xor(b, 32);
-      a *= inv_n;
-      b *= inv_n;
-      if (live[pb]) {
-        T* dst = static_cast<T*>(p.y) + (int64_t)zr * cout + 8 * g;
+      } else {
+        // LayerNorm backward of this position: statistics recomputed in
+        // fp32 (two-pass, population variance; sums over the 4 lane groups)
+        float xv[CB / 2][8];
+        float sum = 0.f;
 #pragma unroll
         for (int s = 0; s < CB / 2; ++s) {
-          float v[8];
+          f32x4 lo, hi;
+          widen8(zr[pb][s], lo, hi);
 #pragma unroll
-          for (int j = 0; j < 8; ++j)
-            v[j] = rstd * (acc[2 * s + (j >> 2)][pb][j & 3] - a - xv[s][j] * b);
-          st8f(dst + 32 * s, v);
+          for (int i = 0; i < 4; ++i) {
+            xv[s][i] = lo[i];
+            xv[s][4 + i] = hi[i];
+          }
+#pragma unroll
+          for (int j = 0; j < 8; ++j) sum += xv[s][j];
+        }
+        sum += shfl_xor(sum, 16);
+        sum += shfl_xor(sum, 32);
+        const float inv_n = 1.f / (float)cout;
+        const float mu = sum * inv_n;
+        float var = 0.f;
+#pragma unroll
+        for (int s = 0; s < CB / 2; ++s)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            xv[s][j] -= mu;
+            var = __builtin_fmaf(xv[s][j], xv[s][j], var);
+          }
+        var += shfl_xor(var, 16);
+        var += shfl_xor(var, 32);
+        const float rstd = rsqrtf(var * inv_n + p.eps);
+        const T* gsrc = static_cast<const T*>(p.ln_w) + 8 * g;
+        float a = 0.f, b = 0.f;
+#pragma unroll
+        for (int s = 0; s < CB / 2; ++s) {
+          float gm[8];
+          ld8f(gsrc + 32 * s, gm);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            xv[s][j] *= rstd;  // xhat
+            const float d = acc[2 * s + (j >> 2)][pb][j & 3] * gm[j];
+            acc[2 * s + (j >> 2)][pb][j & 3] = d;  // dxhat, in place
+            a += d;
+            b = __builtin_fmaf(d, xv[s][j], b);
+          }
+        }
+        a += shfl_xor(a, 16);
+        a += shfl_xor(a, 32);
+        b += shfl_xor(b, 16);
+        b += shfl_xor(b, 32);
+        a *= inv_n;
+        b *= inv_n;
+        if (q.live[pb]) {
+          const uint32_t zrow = zrow_of(q.pc[pb], p.N, p.ending);
+          T* dst = static_cast<T*>(p.y) + (int64_t)zrow * cout + 8 * g;
+#pragma unroll
+          for (int s = 0; s < CB / 2; ++s) {
+            float v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+              v[j] = rstd * (acc[2 * s + (j >> 2)][pb][j & 3] - a - xv[s][j] * b);
+            st8f(dst + 32 * s, v);
+          }
         }
       }
     }
+  };
+
+  // Software pipeline: the next segment's (or the next tile's first
+  // segment's) loads are issued before the current segment's products.  Two
+  // operand sets, xa and xb, used in turn; with four segments xa ends each
+  // tile holding the next tile's first segment, so nothing is copied.
+  // (fp32 operands are twice the registers: one set, no prefetch.)
+  constexpr bool PIPE = sizeof(T) == 2;
+  Op xa[4][2], xb[PIPE ? 4 : 1][2];
+  int tile = blockIdx.x;
+  if (tile >= p.ntiles) return;
+  Pos cur = pos_of(tile);
+  if constexpr (PIPE) load_seg(xa, 0, cur);
+  for (; tile < p.ntiles; tile += gridDim.x) {
+    const int nt = tile + (int)gridDim.x < p.ntiles ? tile + (int)gridDim.x : tile;
+    const Pos nxt = pos_of(nt);
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) acc[cb][0] = acc[cb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    ZRaw zr[2][CB / 2];
+    if constexpr (!PIPE) {
+      for (int sg = 0; sg < NSEG; ++sg) {
+        load_seg(xa, sg, cur);
+        comp_seg(xa, sg);
+      }
+      if constexpr (NSEG == 4) {
+        float bx[2][8];
+        load_bias(bx, cur);
+        comp_bias(bx);
+        load_z(zr, cur);
+      }
+    } else if constexpr (NSEG == 4) {
+      float bx[2][8];
+      load_seg(xb, 1, cur);
+      load_z(zr, cur);
+      comp_seg(xa, 0);
+      load_seg(xa, 2, cur);
+      comp_seg(xb, 1);
+      load_seg(xb, 3, cur);
+      comp_seg(xa, 2);
+      load_bias(bx, cur);
+      load_seg(xa, 0, nxt);  // the next tile's first segment
+      comp_seg(xb, 3);
+      comp_bias(bx);
+    } else {
+      load_seg(xb, 0, nxt);
+      comp_seg(xa, 0);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        xa[u][0] = xb[u < (PIPE ? 4 : 1) ? u : 0][0];
+        xa[u][1] = xb[u < (PIPE ? 4 : 1) ? u : 0][1];
+      }
+    }
+    epilogue(cur, zr);
+    cur = nxt;
   }
 }
 
 // -------------------------------------------------------------------- wgrad
 struct WGradParams {
   int N, ending, npos;
-  int nseg, a_w, a_zrow;        // A segments [npos][a_w] (row tile = segment)
+  int nseg, a_w, a_zrow;        // A segments [npos][a_w]
   const void* aseg[kMaxSeg];
-  const float* dbias;           // [H][npos]: one more row tile (16 rows), or null
+  const float* dbias;           // [H][npos] (with nseg 4) or null
   int H;
   int b_w, b_zrow, b_ln;        // B [npos][b_w]; LayerNorm-normalised (no affine)
   const void* b;
   float eps;
-  int ntt, nchunks, chunk_pos;  // row tiles; positions per chunk (multiple of 32)
-  float* part;                  // [nchunks][ntt*128][b_w]
-  float* cpart;                 // [nchunks][ntt*128]
+  int rows_pad;                 // nseg*128 (+16 pair-bias rows): partial rows
+  int nchunks, chunk_pos;       // one workgroup per chunk of positions
+  float* part;                  // [nchunks][rows_pad][b_w]
+  float* cpart;                 // [nchunks][rows_pad]
 };
 
-template <typename T> struct WLds;
-// bf16: row-major [32 positions][128 + 16] (transposing reads); fp32:
-// transposed [128][32 + 4].
-template <> struct WLds<bf16_t> { static constexpr int ELEMS = 32 * 144, RS = 144; };
-template <> struct WLds<float> { static constexpr int ELEMS = 128 * 36, PS = 36; };
-
-template <typename T>
+// LDS tiles of one 32-position step.  bf16: row-major [32 positions][cols]
+// read with transposing reads (a 288-byte row stride spreads a read's four
+// rows over distinct banks), double-buffered; fp32: transposed
+// [cols][32 positions], single-buffered.
+template <typename T> struct WL;
+template <> struct WL<bf16_t> {
+  static constexpr int RS = 144, BRS = 24;  // row strides: 128- and 16-column tiles
+  static constexpr int TILE = 32 * RS, BTILE = 32 * BRS, NBUF = 2;
+};
+template <> struct WL<float> {
+  static constexpr int PS = 36;             // position stride of a transposed tile
+  static constexpr int TILE = 128 * PS, BTILE = 16 * PS, NBUF = 1;
+};
+template <typename T, int NSEG>
 constexpr size_t wgrad_lds() {
-  return 4 * WLds<T>::ELEMS * sizeof(T) + 4 * 128 * sizeof(float);
+  return (size_t)WL<T>::NBUF * ((NSEG + 1) * WL<T>::TILE + WL<T>::BTILE) * sizeof(T) +
+         8 * 144 * sizeof(float);
 }
 
-template <typename T>
-__global__ void __launch_bounds__(256) wgrad_kernel(WGradParams p) {
+// One workgroup (eight waves) per chunk of positions computes every row of
+// M = A^T B for that chunk, so each B row (and its LayerNorm) is formed once.
+// NSEG = 4: the module (A = q, k, v, gate gradients + the pair-bias rows,
+// B = xhat); NSEG = 1: the output projection (A = dout, B = o).  Wave w owns
+// segment w / (8/NSEG) and the column blocks w % (8/NSEG) + (8/NSEG) i,
+// i < NSEG; with NSEG = 4 also the pair-bias rows of column block w.
+template <typename T, int NSEG>
+__global__ void __launch_bounds__(512) wgrad_kernel(WGradParams p) {
   using Op = typename Tr<T>::Op;
-  // A and B tiles, double-buffered, then the column-sum scratch (dynamic:
-  // the fp32 tiles exceed the static limit)
+  constexpr bool BIAS = NSEG == 4;
+  constexpr int WPS = 8 / NSEG;     // waves (and column groups) per segment
+  constexpr int TPS = 512 / NSEG;   // staging threads per segment
+  constexpr int NB = WL<T>::NBUF;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  T (*sA)[WLds<T>::ELEMS] = reinterpret_cast<T (*)[WLds<T>::ELEMS]>(smem);
-  T (*sB)[WLds<T>::ELEMS] = sA + 2;
-  float (*sred)[128] = reinterpret_cast<float (*)[128]>(smem + 4 * WLds<T>::ELEMS * sizeof(T));
+  T* sA = reinterpret_cast<T*>(smem);                   // [NB][NSEG][TILE]
+  T* sB = sA + NB * NSEG * WL<T>::TILE;                  // [NB][TILE]
+  T* sBi = sB + NB * WL<T>::TILE;                        // [NB][BTILE]
+  float (*sred)[144] = reinterpret_cast<float (*)[144]>(sBi + NB * WL<T>::BTILE);
 
-  int w = xcd_work_index(p.ntt * p.nchunks);
-  if (w < 0) return;
-  const int tt = w % p.ntt, chunk = w / p.ntt;  // row tiles of one chunk side by side
+  const int chunk = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
-  const bool btile = tt == p.nseg;  // the pair-bias row tile
-  const int rows_t = btile ? 16 : p.a_w;
-  const int RBn = rows_t / 16, CBn = p.b_w / 16;
-  const int pbeg = chunk * p.chunk_pos;
-  const int pend = min(p.npos, pbeg + p.chunk_pos);
+  const int pbeg = chunk * p.chunk_pos, pend = min(p.npos, pbeg + p.chunk_pos);
   const int nst = (pend - pbeg + PW - 1) / PW;
+  const int RB = p.a_w / 16, CBn = p.b_w / 16;
+  const int wseg = wave / WPS, cw = wave % WPS;
 
-  // Staging roles.  A (segment tile): chunks e = tid + 256u, position e/16,
-  // channels 8*(e%16) .. +7 (the same 8 channels for u = 0, 1).  A (bias
-  // tile): position tid/8, rows 2*(tid%8), +1.  B: position tid/8,
-  // channels 16*(tid%8) .. +15.
-  const T* A = btile ? nullptr : static_cast<const T*>(p.aseg[tt]);
+  // Staging roles.  A: segment tid / TPS, channels 8*(tid%16) .. +7 of
+  // positions (tid%TPS)/16 + (TPS/16) u, u < NSEG (the same channels every
+  // step, so the column sums stay in 8 registers).  B: position tid/16,
+  // channels 8*(tid%16) .. +7.  Pair-bias rows: position tid/16, row tid%16.
+  const int a_seg = tid / TPS, a_c8 = (tid & 15) * 8, a_pos0 = (tid % TPS) >> 4;
+  const T* Aseg = static_cast<const T*>(p.aseg[a_seg]);
   const T* Bsrc = static_cast<const T*>(p.b);
-  float csum[8];
+  const int b_pos = tid >> 4, b_c8 = (tid & 15) * 8, bi_row = tid & 15;
+  float csum[8], csum_b = 0.f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) csum[j] = 0.f;
 
   struct Raw {
-    float a[2][8];   // A values (segment tile: two chunks; bias tile: a[0][0..1] raw dBias)
-    float b[2][8];   // B values
+    Raw8<T> a[NSEG];
+    Raw8<T> b;
+    float bi;
+  };
+  auto zero8 = [](Raw8<T>& r) {
+    r.a = u32x4{0, 0, 0, 0};
+    if constexpr (sizeof(T) == 4) r.b = u32x4{0, 0, 0, 0};
   };
   auto fetch = [&](int st, Raw& r) {
     const int p0 = pbeg + st * PW;
-    if (!btile) {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int e = tid + 256 * u, pos = e >> 4, c8 = (e & 15) * 8;
-        const int pidx = p0 + pos;
-        if (pidx < pend && c8 < p.a_w) {
-          const uint32_t row = p.a_zrow ? zrow_of(pidx, p.N, p.ending) : (uint32_t)pidx;
-          ld8f(A + (int64_t)row * p.a_w + c8, r.a[u]);
-        } else {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) r.a[u][j] = 0.f;
-        }
-      }
-    } else {
-      const int pos = tid >> 3, r2 = (tid & 7) * 2;
-      const int pidx = p0 + pos;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int row = r2 + j;
-        r.a[0][j] = (pidx < pend && row < 2 * p.H)
-                        ? p.dbias[(int64_t)(row % p.H) * p.npos + pidx] : 0.f;
+    for (int u = 0; u < NSEG; ++u) {
+      const int pidx = p0 + a_pos0 + (TPS / 16) * u;
+      if (pidx < pend && a_c8 < p.a_w) {
+        const uint32_t row = p.a_zrow ? zrow_of(pidx, p.N, p.ending) : (uint32_t)pidx;
+        ld_raw8(r.a[u], Aseg + (int64_t)row * p.a_w + a_c8);
+      } else {
+        zero8(r.a[u]);
       }
     }
-    const int pos = tid >> 3, c16 = (tid & 7) * 16;
-    const int pidx = p0 + pos;
-    const bool ok = pidx < pend;
-    const uint32_t row = ok ? (p.b_zrow ? zrow_of(pidx, p.N, p.ending) : (uint32_t)pidx) : 0u;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      if (ok && c16 + 8 * u < p.b_w) {
-        ld8f(Bsrc + (int64_t)row * p.b_w + c16 + 8 * u, r.b[u]);
+    {
+      const int pidx = p0 + b_pos;
+      if (pidx < pend && b_c8 < p.b_w) {
+        const uint32_t row = p.b_zrow ? zrow_of(pidx, p.N, p.ending) : (uint32_t)pidx;
+        ld_raw8(r.b, Bsrc + (int64_t)row * p.b_w + b_c8);
       } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) r.b[u][j] = 0.f;
+        zero8(r.b);
       }
+    }
+    if constexpr (BIAS) {
+      const int pidx = p0 + b_pos;
+      r.bi = (pidx < pend && bi_row < 2 * p.H)
+                 ? p.dbias[(int64_t)(bi_row % p.H) * p.npos + pidx] : 0.f;
     }
   };
-  // Column sums, LayerNorm of B, and the stores into LDS buffer `buf`.
-  auto stage = [&](Raw& r, int buf) {
-    T* a_ = sA[buf];
-    T* b_ = sB[buf];
-    if (!btile) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int e = tid + 256 * u, pos = e >> 4, c8 = (e & 15) * 8;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) csum[j] += r.a[u][j];
-        if (c8 < p.a_w) {
-          if constexpr (sizeof(T) == 2) {
-            st8f(a_ + pos * WLds<T>::RS + c8, r.a[u]);
-          } else {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) a_[(c8 + j) * WLds<T>::PS + pos] = r.a[u][j];
-          }
-        }
-      }
+  // Store 8 values (channels c8 .. c8+7 of position pos) into a tile.
+  auto put8 = [&](T* tile, int pos, int c8, const float (&v)[8]) {
+    if constexpr (sizeof(T) == 2) {
+      st8f(tile + pos * WL<T>::RS + c8, v);
     } else {
-      const int pos = tid >> 3, r2 = (tid & 7) * 2;
-      float v[2];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int row = r2 + j;
-        const float d = r.a[0][j];
-        if (row < p.H) csum[j] += d;
-        if constexpr (sizeof(T) == 2) {
-          const float hi = (float)(__bf16)d;
-          v[j] = row < p.H ? hi : d - hi;
-        } else {
-          v[j] = row < p.H ? d : 0.f;
-        }
-      }
-      if constexpr (sizeof(T) == 2) {
-        const uint32_t u2 = uint32_t(Tr<bf16_t>::from_f(v[0])) |
-                            (uint32_t(Tr<bf16_t>::from_f(v[1])) << 16);
-        *reinterpret_cast<uint32_t*>(a_ + pos * WLds<T>::RS + r2) = u2;
-      } else {
-        a_[r2 * WLds<T>::PS + pos] = v[0];
-        a_[(r2 + 1) * WLds<T>::PS + pos] = v[1];
-      }
+      for (int j = 0; j < 8; ++j) tile[(c8 + j) * WL<T>::PS + pos] = v[j];
     }
-    const int pos = tid >> 3, c16 = (tid & 7) * 16;
-    if (p.b_ln) {
-      // statistics over the 8 lanes of this position (lanes 8k .. 8k+7)
-      const int nv = min(16, max(0, p.b_w - c16));
-      float s = 0.f;
+  };
+  auto stage = [&](Raw& r, int buf) {
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < NSEG; ++u) {
+      float v[8];
+      f32x4 lo, hi;
+      widen8(r.a[u], lo, hi);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) s += r.b[u][j];
-      s += shfl_xor(s, 1);
-      s += shfl_xor(s, 2);
-      s += shfl_xor(s, 4);
-      const float inv_n = 1.f / (float)p.b_w;
-      const float mu = s * inv_n;
-      float var = 0.f;
+      for (int i = 0; i < 4; ++i) {
+        v[i] = lo[i];
+        v[4 + i] = hi[i];
+      }
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+      for (int j = 0; j < 8; ++j) csum[j] += v[j];
+      if (a_c8 < p.a_w)
+        put8(sA + (buf * NSEG + a_seg) * WL<T>::TILE, a_pos0 + (TPS / 16) * u, a_c8, v);
+    }
+    {
+      float v[8];
+      f32x4 lo, hi;
+      widen8(r.b, lo, hi);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[i] = lo[i];
+        v[4 + i] = hi[i];
+      }
+      if (p.b_ln) {
+        // statistics over the 16 lanes of this position
+        const bool in = b_c8 < p.b_w;
+        float sm = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sm += v[j];
+        sm += __shfl_xor(sm, 1, 64);
+        sm += __shfl_xor(sm, 2, 64);
+        sm += __shfl_xor(sm, 4, 64);
+        sm += __shfl_xor(sm, 8, 64);
+        const float inv_n = 1.f / (float)p.b_w;
+        const float mu = sm * inv_n;
+        float var = 0.f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const float d = (8 * u + j < nv) ? r.b[u][j] - mu : 0.f;
-          r.b[u][j] = d;
-          var = __builtin_fmaf(d, d, var);
+          v[j] = in ? v[j] - mu : 0.f;
+          var = __builtin_fmaf(v[j], v[j], var);
         }
-      var += shfl_xor(var, 1);
-      var += shfl_xor(var, 2);
-      var += shfl_xor(var, 4);
-      const float rstd = rsqrtf(var * inv_n + p.eps);
+        var += __shfl_xor(var, 1, 64);
+        var += __shfl_xor(var, 2, 64);
+        var += __shfl_xor(var, 4, 64);
+        var += __shfl_xor(var, 8, 64);
+        const float rstd = rsqrtf(var * inv_n + p.eps);
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) r.b[u][j] *= rstd;
+        for (int j = 0; j < 8; ++j) v[j] *= rstd;
+      }
+      if (b_c8 < p.b_w) put8(sB + buf * WL<T>::TILE, b_pos, b_c8, v);
     }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int c8 = c16 + 8 * u;
-      if (c8 < p.b_w) {
-        if constexpr (sizeof(T) == 2) {
-          st8f(b_ + pos * WLds<T>::RS + c8, r.b[u]);
-        } else {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) b_[(c8 + j) * WLds<T>::PS + pos] = r.b[u][j];
-        }
+    if constexpr (BIAS) {
+      const float d = r.bi;
+      if (bi_row < p.H) csum_b += d;
+      T* t = sBi + buf * WL<T>::BTILE;
+      if constexpr (sizeof(T) == 2) {
+        const float hi = (float)(__bf16)d;
+        t[b_pos * WL<T>::BRS + bi_row] = Tr<T>::from_f(bi_row < p.H ? hi : d - hi);
+      } else {
+        t[bi_row * WL<T>::PS + b_pos] = bi_row < p.H ? d : 0.f;
       }
     }
   };
-  // Operand fragment: column `col` of a [32 positions][cols] tile, positions
-  // 8g .. 8g+7 (bf16: two transposing reads of the row-major tile).
-  auto frag = [&](const T* t, int col0) -> Op {
+  // Operand fragment: column col0 + l16 of a step's tile, positions 8g .. +7.
+  auto frag = [&](const T* t, int col0, int rs) -> Op {
     if constexpr (sizeof(T) == 2) {
-      const T* p0 = t + (8 * g + (l16 >> 2)) * WLds<T>::RS + col0 + 4 * (l16 & 3);
-      return lds_read_tr_op(p0, p0 + 4 * WLds<T>::RS);
+      const T* p0 = t + (8 * g + (l16 >> 2)) * rs + col0 + 4 * (l16 & 3);
+      return lds_read_tr_op(p0, p0 + 4 * rs);
     } else {
-      return ld_op<T>(t + (col0 + l16) * WLds<T>::PS + 8 * g);
+      (void)rs;
+      return ld_op<T>(t + (col0 + l16) * WL<T>::PS + 8 * g);
     }
   };
 
-  f32x4 acc[8][2];  // [row block][column block of this wave]
+  f32x4 acc[8][NSEG], accb = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int rb = 0; rb < 8; ++rb) acc[rb][0] = acc[rb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int rb = 0; rb < 8; ++rb)
+#pragma unroll
+    for (int i = 0; i < NSEG; ++i) acc[rb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int rsA = sizeof(T) == 2 ? WL<bf16_t>::RS : 0, rsB = rsA;
+  const int rsBi = sizeof(T) == 2 ? WL<bf16_t>::BRS : 0;
 
   Raw raw;
   if (nst > 0) fetch(0, raw);
   for (int st = 0; st < nst; ++st) {
-    const int buf = st & 1;
+    const int buf = NB == 2 ? (st & 1) : 0;
+    if (NB == 1 && st > 0) __syncthreads();  // the previous step's reads are done
     stage(raw, buf);
     __syncthreads();
     if (st + 1 < nst) fetch(st + 1, raw);
-    Op bf[2];
+    const T* tA = sA + (buf * NSEG + wseg) * WL<T>::TILE;
+    const T* tB = sB + buf * WL<T>::TILE;
+    if constexpr (sizeof(T) == 2) {
+      Op bf[NSEG];
 #pragma unroll
-    for (int ci = 0; ci < 2; ++ci)
-      if (wave + 4 * ci < CBn) bf[ci] = frag(sB[buf], (wave + 4 * ci) * 16);
+      for (int i = 0; i < NSEG; ++i)
+        if (cw + WPS * i < CBn) bf[i] = frag(tB, (cw + WPS * i) * 16, rsB);
 #pragma unroll
-    for (int rb = 0; rb < 8; ++rb) {
-      if (rb >= RBn) break;
-      const Op af = frag(sA[buf], rb * 16);
+      for (int rb = 0; rb < 8; ++rb) {
+        if (rb >= RB) break;
+        const Op af = frag(tA, rb * 16, rsA);
 #pragma unroll
-      for (int ci = 0; ci < 2; ++ci)
-        if (wave + 4 * ci < CBn) acc[rb][ci] = mma32(af, bf[ci], acc[rb][ci]);
+        for (int i = 0; i < NSEG; ++i)
+          if (cw + WPS * i < CBn) acc[rb][i] = mma32(af, bf[i], acc[rb][i]);
+      }
+    } else {
+      // fp32 fragments are twice the registers: one column block at a time
+#pragma unroll
+      for (int i = 0; i < NSEG; ++i) {
+        if (cw + WPS * i >= CBn) continue;
+        const Op bfi = frag(tB, (cw + WPS * i) * 16, rsB);
+#pragma unroll
+        for (int rb = 0; rb < 8; ++rb) {
+          if (rb >= RB) break;
+          acc[rb][i] = mma32(frag(tA, rb * 16, rsA), bfi, acc[rb][i]);
+        }
+      }
+    }
+    if constexpr (BIAS) {
+      if (wave < CBn) {
+        const Op ab = frag(sBi + buf * WL<T>::BTILE, 0, rsBi);
+        const Op bw = frag(tB, wave * 16, rsB);
+        accb = mma32(ab, bw, accb);
+      }
     }
   }
 
   // Partials: lane (l16, g) holds M[rb*16 + 4g + i][cb*16 + l16].
-  const int rows_pad = p.ntt * 128;
-  float* dst = p.part + ((int64_t)chunk * rows_pad + tt * 128) * p.b_w;
+  float* dst = p.part + (int64_t)chunk * p.rows_pad * p.b_w;
 #pragma unroll
-  for (int ci = 0; ci < 2; ++ci) {
-    const int cb = wave + 4 * ci;
+  for (int i = 0; i < NSEG; ++i) {
+    const int cb = cw + WPS * i;
     if (cb >= CBn) continue;
 #pragma unroll
     for (int rb = 0; rb < 8; ++rb) {
-      if (rb >= RBn) break;
+      if (rb >= RB) break;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        dst[(int64_t)(rb * 16 + 4 * g + i) * p.b_w + cb * 16 + l16] = acc[rb][ci][i];
+      for (int r = 0; r < 4; ++r)
+        dst[(int64_t)(wseg * 128 + rb * 16 + 4 * g + r) * p.b_w + cb * 16 + l16] = acc[rb][i][r];
     }
   }
-  // Column sums of A: reduce the lanes that staged the same rows, then the
-  // four waves.
-  if (!btile) {
+  if constexpr (BIAS) {
+    if (wave < CBn) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      csum[j] += shfl_xor(csum[j], 16);
-      csum[j] += shfl_xor(csum[j], 32);
+      for (int r = 0; r < 4; ++r)
+        dst[(int64_t)(NSEG * 128 + 4 * g + r) * p.b_w + wave * 16 + l16] = accb[r];
     }
-    if (lane < 16) {
+  }
+  // Column sums: lanes with equal tid % 16 of a wave staged the same
+  // channels (and pair-bias row); then the waves of a segment.
 #pragma unroll
-      for (int j = 0; j < 8; ++j) sred[wave][lane * 8 + j] = csum[j];
-    }
-  } else {
+  for (int j = 0; j < 8; ++j) {
+    csum[j] += __shfl_xor(csum[j], 16, 64);
+    csum[j] += __shfl_xor(csum[j], 32, 64);
+  }
+  csum_b += __shfl_xor(csum_b, 16, 64);
+  csum_b += __shfl_xor(csum_b, 32, 64);
+  if (lane < 16) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      csum[j] += shfl_xor(csum[j], 8);
-      csum[j] += shfl_xor(csum[j], 16);
-      csum[j] += shfl_xor(csum[j], 32);
-    }
-    if (lane < 8) {
-      sred[wave][lane * 2] = csum[0];
-      sred[wave][lane * 2 + 1] = csum[1];
-    }
+    for (int j = 0; j < 8; ++j) sred[wave][lane * 8 + j] = csum[j];
+    sred[wave][128 + lane] = csum_b;
   }
   __syncthreads();
-  if (tid < rows_t) {
-    const float s = ((sred[0][tid] + sred[1][tid]) + sred[2][tid]) + sred[3][tid];
-    p.cpart[(int64_t)chunk * rows_pad + tt * 128 + tid] = s;
+  float* cdst = p.cpart + (int64_t)chunk * p.rows_pad;
+  if (tid < NSEG * 128) {
+    const int sg = tid >> 7, ch = tid & 127;
+    if (ch < p.a_w) {
+      float t = 0.f;
+#pragma unroll
+      for (int w = 0; w < WPS; ++w) t += sred[sg * WPS + w][ch];
+      cdst[sg * 128 + ch] = t;
+    }
+  }
+  if constexpr (BIAS) {
+    if (tid < 16) {
+      float t = 0.f;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) t += sred[w][128 + tid];
+      cdst[NSEG * 128 + tid] = t;
+    }
   }
 }
 
 // ------------------------------------------------------------------- finish
+// First stage of the chunk reduction: group gi = blockIdx.y sums chunks
+// 16 gi .. 16 gi + 15 in order (partials, then the column sums).
+constexpr int kGroup = 16;
+__global__ void __launch_bounds__(256) chunk_sum_kernel(const float* part, const float* cpart,
+                                                        int nchunks, int rows_pad, int ncols,
+                                                        float* part2, float* cpart2) {
+  const int gi = blockIdx.y;
+  const int c0 = gi * kGroup, c1 = min(nchunks, c0 + kGroup);
+  const int64_t esize = (int64_t)rows_pad * ncols;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < esize + rows_pad;
+       e += (int64_t)gridDim.x * 256) {
+    float t = 0.f;
+    if (e < esize) {
+      for (int ch = c0; ch < c1; ++ch) t += part[ch * esize + e];
+      part2[gi * esize + e] = t;
+    } else {
+      const int64_t r = e - esize;
+      for (int ch = c0; ch < c1; ++ch) t += cpart[(int64_t)ch * rows_pad + r];
+      cpart2[(int64_t)gi * rows_pad + r] = t;
+    }
+  }
+}
+
+
 struct FinishParams {
   int nchunks, rows_pad, ncols;
   int nseg, a_w, H, has_bias;
@@ -631,35 +773,52 @@ struct FinishParams {
   float* cred;              // [nseg*a_w + H] (ln)
 };
 
+// Sum of 16 lanes' partials (lanes 16a .. 16a+15), complete in the first
+// lane of the group (a fixed butterfly: the same order on every run).
+__device__ __forceinline__ float sum16(float v) {
+  v += __shfl_xor(v, 1, 64);
+  v += __shfl_xor(v, 2, 64);
+  v += __shfl_xor(v, 4, 64);
+  v += __shfl_xor(v, 8, 64);
+  return v;
+}
+
+// One output element per 16 lanes: lane j of the group sums chunks j, j+16,
+// ..., then the group adds the 16 sums.
 template <typename T>
 __global__ void __launch_bounds__(256) wgrad_finish_kernel(FinishParams p) {
   const int nrows = p.nseg * p.a_w + (p.has_bias ? p.H : 0);
   const int64_t total = (int64_t)nrows * p.ncols;
   const int64_t cstride = (int64_t)p.rows_pad * p.ncols;
-  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total;
-       e += (int64_t)gridDim.x * 256) {
-    const int k = (int)(e / p.ncols), c = (int)(e - (int64_t)k * p.ncols);
+  const int j = threadIdx.x & 15;
+  for (int64_t e0 = (int64_t)blockIdx.x * 16; e0 < total; e0 += (int64_t)gridDim.x * 16) {
+    // elements e0 .. e0+15: lane group (threadIdx.x / 16) takes one
+    const int64_t e = e0 + (threadIdx.x >> 4);
+    const bool live = e < total;
+    const int64_t ec = live ? e : total - 1;
+    const int k = (int)(ec / p.ncols), c = (int)(ec - (int64_t)k * p.ncols);
     float m = 0.f, s = 0.f;
     int seg = -1, r = 0;
     if (k < p.nseg * p.a_w) {
       seg = k / p.a_w;
       r = k - seg * p.a_w;
       const int slot = seg * 128 + r;
-      for (int ch = 0; ch < p.nchunks; ++ch) {
+      for (int ch = j; ch < p.nchunks; ch += 16) {
         m += p.part[ch * cstride + (int64_t)slot * p.ncols + c];
         s += p.cpart[(int64_t)ch * p.rows_pad + slot];
       }
     } else {
-      r = k - p.nseg * p.a_w;  // head
+      r = k - p.nseg * p.a_w;  // head: high plus low part of dBias
       const int hi = p.nseg * 128 + r, lo = hi + p.H;
-      float mh = 0.f, ml = 0.f;
-      for (int ch = 0; ch < p.nchunks; ++ch) {
-        mh += p.part[ch * cstride + (int64_t)hi * p.ncols + c];
-        ml += p.part[ch * cstride + (int64_t)lo * p.ncols + c];
+      for (int ch = j; ch < p.nchunks; ch += 16) {
+        m += p.part[ch * cstride + (int64_t)hi * p.ncols + c] +
+             p.part[ch * cstride + (int64_t)lo * p.ncols + c];
         s += p.cpart[(int64_t)ch * p.rows_pad + hi];
       }
-      m = mh + ml;
     }
+    m = sum16(m);
+    s = sum16(s);
+    if (!live || j != 0) continue;
     float out = m;
     if (p.ln) {
       const float gm = Tr<T>::to_f(static_cast<const T*>(p.ln_w)[c]);
@@ -689,13 +848,15 @@ struct LnParamParams {
   float* dln_b;
 };
 
+// One workgroup per column c: thread t takes rows t, t+256, ...; the
+// workgroup then adds the 256 sums in a fixed order.
 template <typename T>
 __global__ void __launch_bounds__(256) lnparam_kernel(LnParamParams p) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  if (c >= p.ncols) return;
+  __shared__ float red[2][4];
+  const int c = blockIdx.x, tid = threadIdx.x;
   float dg = 0.f, db = 0.f;
   const int nrows = p.nseg * p.a_w + p.H;
-  for (int k = 0; k < nrows; ++k) {
+  for (int k = tid; k < nrows; k += 256) {
     const T* wr;
     if (k < p.nseg * p.a_w) {
       const int s = k / p.a_w;
@@ -707,15 +868,25 @@ __global__ void __launch_bounds__(256) lnparam_kernel(LnParamParams p) {
     dg = __builtin_fmaf(wv, p.mred[(int64_t)k * p.ncols + c], dg);
     db = __builtin_fmaf(wv, p.cred[k], db);
   }
-  p.dln_w[c] = dg;
-  p.dln_b[c] = db;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    dg += __shfl_xor(dg, m, 64);
+    db += __shfl_xor(db, m, 64);
+  }
+  if ((tid & 63) == 0) {
+    red[0][tid >> 6] = dg;
+    red[1][tid >> 6] = db;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    p.dln_w[c] = ((red[0][0] + red[0][1]) + red[0][2]) + red[0][3];
+    p.dln_b[c] = ((red[1][0] + red[1][1]) + red[1][2]) + red[1][3];
+  }
 }
 
 // ----------------------------------------------------------------- launches
-template <typename T, int CB>
+template <typename T, int CB, int NSEG>
 hipError_t launch_rowgrad_cb(RowGradParams& p, hipStream_t s) {
-  // eight waves: the LayerNorm epilogue holds a position block's z row
-  // next to both blocks' accumulators
   constexpr int WAVES = 8;
   const size_t wbytes = (size_t)p.cout * (p.Kext + PADE) * sizeof(T);
   p.resident = wbytes <= kLdsBudget;
@@ -724,20 +895,24 @@ hipError_t launch_rowgrad_cb(RowGradParams& p, hipStream_t s) {
   const int64_t tiles = ((int64_t)p.npos + PW * WAVES - 1) / (PW * WAVES);
   p.ntiles = (int)tiles;
   const int grid = (int)std::min<int64_t>(tiles, 256);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&rowgrad_kernel<T, CB, WAVES>),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&rowgrad_kernel<T, CB, NSEG>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((rowgrad_kernel<T, CB, WAVES>), dim3(grid), dim3(WAVES * 64), lds, s, p);
+  hipLaunchKernelGGL((rowgrad_kernel<T, CB, NSEG>), dim3(grid), dim3(WAVES * 64), lds, s, p);
   return hipGetLastError();
 }
 
+// nseg 4 with the pair-bias block and the LayerNorm backward (the module),
+// or 1 without either (the output projection).
 template <typename T>
 hipError_t launch_rowgrad(RowGradParams& p, hipStream_t s) {
+  const bool module = p.nseg == 4;
+  if (module != (p.dbias != nullptr) || module != (p.ln != 0)) return hipErrorInvalidValue;
   switch (p.cout / 16) {
-    case 2: return launch_rowgrad_cb<T, 2>(p, s);
-    case 4: return launch_rowgrad_cb<T, 4>(p, s);
-    case 6: return launch_rowgrad_cb<T, 6>(p, s);
-    case 8: return launch_rowgrad_cb<T, 8>(p, s);
+    case 2: return module ? launch_rowgrad_cb<T, 2, 4>(p, s) : launch_rowgrad_cb<T, 2, 1>(p, s);
+    case 4: return module ? launch_rowgrad_cb<T, 4, 4>(p, s) : launch_rowgrad_cb<T, 4, 1>(p, s);
+    case 6: return module ? launch_rowgrad_cb<T, 6, 4>(p, s) : launch_rowgrad_cb<T, 6, 1>(p, s);
+    case 8: return module ? launch_rowgrad_cb<T, 8, 4>(p, s) : launch_rowgrad_cb<T, 8, 1>(p, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -750,25 +925,41 @@ void chunking(int64_t npos, int target, int& nchunks, int& chunk_pos) {
   chunk_pos = (int)(per * PW);
   nchunks = (int)((npos + chunk_pos - 1) / chunk_pos);
 }
-constexpr int kChunksModule = 128;   // 5 row tiles: ~640 workgroups
-constexpr int kChunksOut = 512;      // 1 row tile
+// One workgroup of the weight-gradient kernel per CU (eight waves, about 100
+// KB of LDS), each over one chunk of positions.
+constexpr int kChunks = 256;
 
 template <typename T>
 hipError_t launch_wgrad(WGradParams& p, hipStream_t s) {
-  const int total = p.ntt * p.nchunks;
-  const int grid = (total + kNumXcd - 1) / kNumXcd * kNumXcd;
-  const size_t lds = wgrad_lds<T>();
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&wgrad_kernel<T>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  const size_t lds = p.nseg == 4 ? wgrad_lds<T, 4>() : wgrad_lds<T, 1>();
+  const void* fn = p.nseg == 4 ? reinterpret_cast<const void*>(&wgrad_kernel<T, 4>)
+                               : reinterpret_cast<const void*>(&wgrad_kernel<T, 1>);
+  if ((p.nseg == 4) != (p.dbias != nullptr)) return hipErrorInvalidValue;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(wgrad_kernel<T>, dim3(grid), dim3(256), lds, s, p);
+  if (p.nseg == 4)
+    hipLaunchKernelGGL((wgrad_kernel<T, 4>), dim3(p.nchunks), dim3(512), lds, s, p);
+  else
+    hipLaunchKernelGGL((wgrad_kernel<T, 1>), dim3(p.nchunks), dim3(512), lds, s, p);
   return hipGetLastError();
 }
 
+// Sums the chunk partials in two fixed-order stages (groups of kGroup chunks
+// into part2/cpart2, then the groups) and writes the gradients.
 template <typename T>
-hipError_t launch_finish(FinishParams& f, hipStream_t s) {
+hipError_t launch_finish(FinishParams& f, float* part2, float* cpart2, hipStream_t s) {
+  const int ngroups = (f.nchunks + kGroup - 1) / kGroup;
+  const int64_t esize = (int64_t)f.rows_pad * f.ncols + f.rows_pad;
+  const int gx = (int)std::min<int64_t>((esize + 255) / 256, 1024);
+  hipLaunchKernelGGL(chunk_sum_kernel, dim3(gx, ngroups), dim3(256), 0, s, f.part, f.cpart,
+                     f.nchunks, f.rows_pad, f.ncols, part2, cpart2);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  f.nchunks = ngroups;
+  f.part = part2;
+  f.cpart = cpart2;
   const int64_t total = (int64_t)(f.nseg * f.a_w + (f.has_bias ? f.H : 0)) * f.ncols;
-  const int grid = (int)std::min<int64_t>((total + 255) / 256, 1024);
+  const int grid = (int)std::min<int64_t>((total + 15) / 16, 16384);
   hipLaunchKernelGGL(wgrad_finish_kernel<T>, dim3(grid), dim3(256), 0, s, f);
   return hipGetLastError();
 }
@@ -776,19 +967,21 @@ hipError_t launch_finish(FinishParams& f, hipStream_t s) {
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct PartLayout {
-  size_t part, cpart, mred, cred, total;
+  size_t part, cpart, part2, cpart2, mred, cred, total;
 };
 PartLayout part_layout(int64_t N, int64_t CZ, int64_t H) {
   const int64_t npos = N * N, HC = H * kHeadDim;
-  int nm, cm, no, co;
-  chunking(npos, kChunksModule, nm, cm);
-  chunking(npos, kChunksOut, no, co);
-  const size_t part_m = (size_t)nm * 5 * 128 * CZ * 4, cpart_m = (size_t)nm * 5 * 128 * 4;
-  const size_t part_o = (size_t)no * 128 * HC * 4, cpart_o = (size_t)no * 128 * 4;
+  int nc, cp;
+  chunking(npos, kChunks, nc, cp);
+  const size_t part_m = (size_t)nc * (4 * 128 + 16) * CZ * 4, cpart_m = (size_t)nc * (4 * 128 + 16) * 4;
+  const size_t part_o = (size_t)nc * 128 * HC * 4, cpart_o = (size_t)nc * 128 * 4;
   PartLayout L;
   L.part = 0;
   L.cpart = align256(std::max(part_m, part_o));
-  L.mred = L.cpart + align256(std::max(cpart_m, cpart_o));
+  const int ng = (nc + kGroup - 1) / kGroup;
+  L.part2 = L.cpart + align256(std::max(cpart_m, cpart_o));
+  L.cpart2 = L.part2 + align256((size_t)ng * (4 * 128 + 16) * std::max(CZ, HC) * 4);
+  L.mred = L.cpart2 + align256((size_t)ng * (4 * 128 + 16) * 4);
   L.cred = L.mred + align256((size_t)(4 * HC + H) * CZ * 4);
   L.total = L.cred + align256((size_t)(4 * HC + H) * 4);
   return L;
@@ -815,18 +1008,19 @@ hipError_t out_project_bwd_t(const OutProjectBwdArgs& a, hipStream_t s) {
   w.nseg = 1; w.a_w = CZ; w.a_zrow = 1; w.aseg[0] = a.dout;
   w.dbias = nullptr; w.H = H;
   w.b_w = HC; w.b_zrow = 0; w.b_ln = 0; w.b = a.o; w.eps = 0.f;
-  w.ntt = 1;
-  chunking(npos, kChunksOut, w.nchunks, w.chunk_pos);
+  w.rows_pad = 128;
+  chunking(npos, kChunks, w.nchunks, w.chunk_pos);
   w.part = reinterpret_cast<float*>(ws + L.part);
   w.cpart = reinterpret_cast<float*>(ws + L.cpart);
   if ((e = launch_wgrad<T>(w, s)) != hipSuccess) return e;
   FinishParams f{};
-  f.nchunks = w.nchunks; f.rows_pad = 128; f.ncols = HC;
+  f.nchunks = w.nchunks; f.rows_pad = w.rows_pad; f.ncols = HC;
   f.nseg = 1; f.a_w = CZ; f.H = H; f.has_bias = 0;
   f.part = w.part; f.cpart = w.cpart;
   f.ln = 0;
   f.dw[0] = a.dw_o; f.dcol[0] = a.db_o;
-  return launch_finish<T>(f, s);
+  return launch_finish<T>(f, reinterpret_cast<float*>(ws + L.part2),
+                          reinterpret_cast<float*>(ws + L.cpart2), s);
 }
 
 template <typename T>
@@ -854,13 +1048,13 @@ hipError_t project_bwd_t(const ProjectBwdArgs& a, hipStream_t s) {
   for (int i = 0; i < 4; ++i) w.aseg[i] = dys[i];
   w.dbias = a.dbias; w.H = H;
   w.b_w = CZ; w.b_zrow = 1; w.b_ln = 1; w.b = a.z; w.eps = a.eps;
-  w.ntt = 5;
-  chunking(npos, kChunksModule, w.nchunks, w.chunk_pos);
+  w.rows_pad = 4 * 128 + 16;
+  chunking(npos, kChunks, w.nchunks, w.chunk_pos);
   w.part = reinterpret_cast<float*>(ws + L.part);
   w.cpart = reinterpret_cast<float*>(ws + L.cpart);
   if ((e = launch_wgrad<T>(w, s)) != hipSuccess) return e;
   FinishParams f{};
-  f.nchunks = w.nchunks; f.rows_pad = 5 * 128; f.ncols = CZ;
+  f.nchunks = w.nchunks; f.rows_pad = w.rows_pad; f.ncols = CZ;
   f.nseg = 4; f.a_w = HC; f.H = H; f.has_bias = 1;
   f.part = w.part; f.cpart = w.cpart;
   f.ln = 1; f.ln_w = a.ln_w; f.ln_b = a.ln_b;
@@ -869,13 +1063,15 @@ hipError_t project_bwd_t(const ProjectBwdArgs& a, hipStream_t s) {
   f.dcol[3] = a.db_g;
   f.mred = reinterpret_cast<float*>(ws + L.mred);
   f.cred = reinterpret_cast<float*>(ws + L.cred);
-  if ((e = launch_finish<T>(f, s)) != hipSuccess) return e;
+  if ((e = launch_finish<T>(f, reinterpret_cast<float*>(ws + L.part2),
+                           reinterpret_cast<float*>(ws + L.cpart2), s)) != hipSuccess)
+    return e;
   LnParamParams l{};
   l.nseg = 4; l.a_w = HC; l.H = H; l.ncols = CZ;
   for (int i = 0; i < 4; ++i) l.wseg[i] = wts[i];
   l.wbias = a.w_bias; l.mred = f.mred; l.cred = f.cred;
   l.dln_w = a.dln_w; l.dln_b = a.dln_b;
-  hipLaunchKernelGGL(lnparam_kernel<T>, dim3((CZ + 255) / 256), dim3(256), 0, s, l);
+  hipLaunchKernelGGL(lnparam_kernel<T>, dim3(CZ), dim3(256), 0, s, l);
   return hipGetLastError();
 }
 
