@@ -14,7 +14,9 @@ projections' time is inside the step but their flops are not counted.
 
 Prints one JSON line.  Options: --steps K --warmup W --gpus 1
 --workload NAME --no-cpu-baseline --cpu-lines L --calibrate-copy
---write-traffic FETCH_CSV WRITE_CSV.
+--write-traffic FETCH_CSV WRITE_CSV, and --module-train (a training step of
+the whole module instead: forward, then the backward with the LayerNorm,
+projection and output-projection gradients).
 """
 import argparse
 import hashlib
@@ -42,6 +44,10 @@ def parse():
                     help="after the timed steps, run a plain elementwise copy "
                          "of COPY_BYTES (read) + COPY_BYTES (write), for scaling "
                          "the FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--module-train", action="store_true",
+                    help="time a training step of the whole module instead: "
+                         "tri_attn_module_fwd + tri_attn_module_bwd (LayerNorm, "
+                         "projection and output-projection gradients included)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU work: turn two rocprofv3 --pmc counter files "
                          "(FETCH_SIZE run, WRITE_SIZE run) of a --calibrate-copy "
@@ -188,8 +194,96 @@ def cpu_baseline(d, w, n_lines):
                        f"including the pair bias of the whole z)")}
 
 
+def module_train(a):
+    """One training step of the triangle-attention module on the workload:
+    the module forward, then the module backward (which recomputes the
+    forward's activations from z, as an activation-checkpointed Evoformer
+    block does).  Prints one JSON line; the roofline entry is the projection
+    backward (tri_attn_project_bwd, HBM-bound), timed on its own."""
+    import torch
+    from evoformer_attention_amd import metrics as M
+    from evoformer_attention_amd import ops, synth
+
+    w = dict(synth.WORKLOADS[a.workload])
+    N, CZ, H, C, ending = w["N"], w["CZ"], w["H"], w["C"], w["ending"]
+    d = synth.module_inputs(a.workload)
+    gen = torch.Generator().manual_seed(7)
+    dout = synth.round_to(torch.randn((N, N, CZ), generator=gen), w["dtype"])
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    g = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    dout = dout.to(dev)
+    dt = g["z"].dtype
+    ws_f = torch.empty(ops.tri_attn_workspace_bytes(dt, N, CZ, H, C), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(ops.tri_attn_bwd_workspace_bytes(dt, N, CZ, H, C), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        out = ops.tri_attn_module_fwd(
+            g["z"], g["mask"], g["ln_w"], g["ln_b"], g["eps"], g["w_q"], g["w_k"],
+            g["w_v"], g["w_g"], g["b_g"], g["w_bias"], g["w_o"], g["b_o"], H, C,
+            ending, workspace=ws_f)
+        grads = ops.tri_attn_module_bwd(
+            g["z"], g["mask"], g["ln_w"], g["ln_b"], g["eps"], g["w_q"], g["w_k"],
+            g["w_v"], g["w_g"], g["b_g"], g["w_bias"], g["w_o"], dout, H, C,
+            ending, workspace=ws_b)
+        return out, grads
+
+    def timed(fn, iters):
+        for _ in range(a.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(iters):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters
+
+    ms = timed(step, a.steps)
+    # the projection backward alone, on gradients of the same shapes
+    gq = [torch.randn((1, N, N, H, C), device=dev).to(dt) for _ in range(4)]
+    gb = torch.randn((1, H, N, N), device=dev)
+    ws_p = torch.empty(ops.tri_attn_proj_bwd_workspace_bytes(dt, N, CZ, H, C),
+                       dtype=torch.uint8, device=dev)
+
+    def pbwd():
+        return ops.tri_attn_project_bwd(
+            g["z"], g["ln_w"], g["ln_b"], g["eps"], g["w_q"], g["w_k"], g["w_v"],
+            g["w_g"], g["w_bias"], *gq, gb, H, C, ending, workspace=ws_p)
+
+    ms_p = timed(pbwd, a.steps)
+    pbytes = M.project_bwd_min_bytes(N, CZ, H, C, 2)
+    gbs = pbytes / (ms_p * 1e-3) / 1e9
+    flops = M.module_step_flops(N, CZ, H, C)
+    res = {
+        "metric": "Triangle-attention module training step (fwd + bwd) TFLOP/s (bf16), tri-attn N_res=768",
+        "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": a.workload, "N_res": N, "c_z": CZ, "heads": H,
+                   "head_dim": C, "node": "ending" if ending else "starting",
+                   "step": "module fwd + module bwd (recomputes the forward; "
+                           "dz and every parameter gradient)"},
+        "roofline": {"bound": "hbm", "kernel": "tri_attn_project_bwd (call)",
+                     "achieved": round(gbs, 1), "peak": M.MI355X_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / M.MI355X_HBM_GBS, 4), "traffic": None},
+        "project_bwd_ms": round(ms_p, 4),
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     a = parse()
+    if a.module_train:
+        if a.gpus != 1:
+            print("bench.py runs on one GPU only", file=sys.stderr)
+            sys.exit(2)
+        module_train(a)
+        return
     if a.write_traffic:
         write_traffic(a.write_traffic[0], a.write_traffic[1], a.workload)
         return

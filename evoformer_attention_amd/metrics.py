@@ -75,3 +75,20 @@ def bwd_min_bytes(B, R, N, H, C, elem_bytes, gate=True, bias=True,
         n += B * H * N * N * elem_bytes + B * H * N * N * 4
     n += B * mask_rows * N
     return n
+
+
+def module_step_flops(N, CZ, H, C):
+    """Counted flops of one training step of the triangle-attention module
+    (forward plus backward, recomputation not counted): the projection and
+    output-projection GEMMs once forward and twice backward (input and weight
+    gradients), the attention 1 + 2.5 times its forward."""
+    gemm = project_flops(N, CZ, H, C) + out_project_flops(N, CZ, H, C)
+    return 3.0 * gemm + fwd_flops(1, N, N, H, C) + bwd_flops(1, N, N, H, C)
+
+
+def project_bwd_min_bytes(N, CZ, H, C, elem_bytes):
+    """Algorithmic HBM bytes of tri_attn_project_bwd: dq, dk, dv, dg read
+    once (working dtype), the fp32 pair-bias gradient read once, z read once
+    and dz written once; the fp32 parameter gradients are negligible."""
+    t = N * N * H * C * elem_bytes
+    return 4 * t + H * N * N * 4 + 2 * pair_rep_bytes(N, CZ, elem_bytes)
