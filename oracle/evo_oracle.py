@@ -46,7 +46,7 @@ __all__ = [
     "dbias_query_rows", "layer_norm", "tri_project", "tri_out_project",
     "tri_module_forward", "tri_module_lines", "layer_norm_backward",
     "tri_out_project_backward", "tri_project_backward",
-    "tri_module_backward",
+    "tri_module_backward", "tri_mul_forward",
 ]
 
 
@@ -457,3 +457,42 @@ def tri_module_backward(z, residue_mask, ln_w, ln_b, eps, w_q, w_k, w_v, w_g,
     res["dw_o"] = dw_o
     res["db_o"] = db_o
     return res
+
+
+# ----------------------------------------------------------------------------
+# Triangular multiplicative update.
+#
+# [COURSE] "The three operations": edge (i, j) is updated from every third
+# residue k as the sum over k of a_ik * b_jk, channel by channel: O(N^3) time,
+# O(N^2) memory.  The pages leave the rest open; the reading taken here is
+# the plainest one the module around it supports: a and b are linear
+# projections (c channels, no bias) of the layer-normalised pair
+# representation, the same normalisation and projection as the
+# triangle-attention module; the update is projected back to c_z with an
+# output bias.  "Outgoing" sums over edges (i, k) and (j, k); "incoming" over
+# (k, i) and (k, j).  A residue mask removes third residues k from the sum.
+# ----------------------------------------------------------------------------
+
+def tri_mul_forward(z, residue_mask, ln_w, ln_b, eps, w_a, w_b, w_o, b_o,
+                    outgoing=True):
+    """z [N, N, CZ]; w_a, w_b [C, CZ]; w_o [CZ, C]; b_o [CZ]; residue_mask
+    [N] (nonzero = keep) or None.  Returns the update [N, N, CZ]:
+        t[i, j, c] = sum_k keep[k] a[i, k, c] b[j, k, c]   (outgoing)
+        t[i, j, c] = sum_k keep[k] a[k, i, c] b[k, j, c]   (incoming)
+        out[i, j]  = t[i, j] . w_o^T + b_o,
+    with a = LN(z) . w_a^T and b = LN(z) . w_b^T."""
+    z = np.asarray(z, np.float64)
+    N = z.shape[0]
+    x = layer_norm(z, ln_w, ln_b, eps)
+    a = x @ w_a.T                        # a[p, q] = projection of edge (p, q)
+    b = x @ w_b.T
+    keep = (np.ones(N) if residue_mask is None
+            else (np.asarray(residue_mask) != 0).astype(np.float64))
+    C = a.shape[-1]
+    t = np.empty((N, N, C))
+    for c in range(C):
+        # edges (i, k) / (j, k) for outgoing, (k, i) / (k, j) for incoming
+        A = a[:, :, c] if outgoing else a[:, :, c].T     # A[i, k]
+        Bm = b[:, :, c] if outgoing else b[:, :, c].T    # Bm[j, k]
+        t[:, :, c] = (A * keep) @ Bm.T
+    return t @ w_o.T + b_o

@@ -633,3 +633,117 @@ def test_mutant_ending_gradient_left_in_line_layout_is_caught(monkeypatch):
     _module_fd_pin(False)  # the starting node does not transpose
     with pytest.raises(AssertionError):
         _module_fd_pin(True)
+
+
+# ------------------------------------------- triangular multiplicative update
+
+def trimul_case(seed, N=6, CZ=8, C=5, mask=True):
+    rng = np.random.default_rng(seed)
+    d = dict(z=rng.standard_normal((N, N, CZ)),
+             ln_w=1 + 0.2 * rng.standard_normal(CZ),
+             ln_b=0.2 * rng.standard_normal(CZ), eps=1e-5,
+             w_a=rng.standard_normal((C, CZ)) / CZ ** 0.5,
+             w_b=rng.standard_normal((C, CZ)) / CZ ** 0.5,
+             w_o=rng.standard_normal((CZ, C)) / C ** 0.5,
+             b_o=0.3 * rng.standard_normal(CZ))
+    m = (rng.random(N) < 0.7).astype(np.uint8)
+    m[0] = 1
+    d["residue_mask"] = m if mask else None
+    return d
+
+
+@pytest.mark.parametrize("outgoing", [True, False])
+def test_trimul_matches_triple_loop(outgoing):
+    """Brute force: the sum over the third residue written as explicit loops
+    over i, j, k and channels (no matrix products)."""
+    d = trimul_case(60)
+    got = O.tri_mul_forward(outgoing=outgoing, **d)
+    z = d["z"]
+    N, _, CZ = z.shape
+    mu = z.mean(-1, keepdims=True)
+    x = (z - mu) / np.sqrt(((z - mu) ** 2).mean(-1, keepdims=True) + d["eps"])
+    x = x * d["ln_w"] + d["ln_b"]
+    C = d["w_a"].shape[0]
+    ref = np.zeros((N, N, CZ))
+    for i in range(N):
+        for j in range(N):
+            t = np.zeros(C)
+            for k in range(N):
+                if not d["residue_mask"][k]:
+                    continue
+                e1, e2 = ((i, k), (j, k)) if outgoing else ((k, i), (k, j))
+                for c in range(C):
+                    ac = sum(x[e1][q] * d["w_a"][c, q] for q in range(CZ))
+                    bc = sum(x[e2][q] * d["w_b"][c, q] for q in range(CZ))
+                    t[c] += ac * bc
+            for o in range(CZ):
+                ref[i, j, o] = sum(t[c] * d["w_o"][o, c] for c in range(C)) + d["b_o"][o]
+    np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-12)
+
+
+def test_trimul_matches_torch_einsum():
+    """Library routines: F.layer_norm, F.linear and torch.einsum (fp64)."""
+    d = trimul_case(61, N=9, CZ=12, C=7)
+    t = {k: torch.tensor(v) for k, v in d.items() if isinstance(v, np.ndarray)}
+    x = F.layer_norm(t["z"], (12,), t["ln_w"], t["ln_b"], 1e-5)
+    a, b = F.linear(x, t["w_a"]), F.linear(x, t["w_b"])
+    keep = t["residue_mask"].double()
+    out = torch.einsum("ikc,jkc,k->ijc", a, b, keep)
+    ref_out = F.linear(out, t["w_o"], t["b_o"]).numpy()
+    np.testing.assert_allclose(O.tri_mul_forward(outgoing=True, **d), ref_out,
+                               rtol=1e-11, atol=1e-12)
+    inc = torch.einsum("kic,kjc,k->ijc", a, b, keep)
+    ref_in = F.linear(inc, t["w_o"], t["b_o"]).numpy()
+    np.testing.assert_allclose(O.tri_mul_forward(outgoing=False, **d), ref_in,
+                               rtol=1e-11, atol=1e-12)
+
+
+def test_trimul_incoming_is_outgoing_of_transpose():
+    """Incoming on z equals outgoing on z with its two residue axes swapped
+    (edges (k, i) of z are edges (i, k) of the transpose)."""
+    d = trimul_case(62)
+    e = dict(d)
+    e["z"] = d["z"].transpose(1, 0, 2).copy()
+    np.testing.assert_allclose(O.tri_mul_forward(outgoing=False, **d),
+                               O.tri_mul_forward(outgoing=True, **e),
+                               rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("outgoing", [True, False])
+def test_trimul_residue_permutation_equivariance(outgoing):
+    """Relabelling residues permutes the update identically ("Two properties
+    the tests assert")."""
+    d = trimul_case(63)
+    out = O.tri_mul_forward(outgoing=outgoing, **d)
+    perm = np.random.default_rng(63).permutation(d["z"].shape[0])
+    e = dict(d)
+    e["z"] = d["z"][perm][:, perm]
+    e["residue_mask"] = d["residue_mask"][perm]
+    np.testing.assert_allclose(O.tri_mul_forward(outgoing=outgoing, **e),
+                               out[perm][:, perm], rtol=1e-11, atol=1e-12)
+
+
+def test_trimul_closure_separates_the_broken_variant():
+    """The course's counterexample: replacing the sum over the third residue
+    by an elementwise product (no k) must give a different answer; the
+    correct update depends on edges (i, k) off the (i, j) edge itself."""
+    d = trimul_case(64, mask=False)
+    out = O.tri_mul_forward(outgoing=True, **d)
+    x = O.layer_norm(d["z"], d["ln_w"], d["ln_b"], d["eps"])
+    broken = ((x @ d["w_a"].T) * (x @ d["w_b"].T)) @ d["w_o"].T + d["b_o"]
+    assert np.abs(out - broken).max() > 0.1
+    # changing an edge (i, k) with k != j moves out[i, j] for every j
+    e = dict(d)
+    e["z"] = d["z"].copy()
+    e["z"][1, 3, 0] += 1.0  # one channel (a shift of all channels is normalised away)
+    moved = np.abs(O.tri_mul_forward(outgoing=True, **e) - out).max(-1)
+    assert (moved[1] > 1e-6).all()
+
+
+def test_mutant_trimul_without_third_index_is_caught(monkeypatch):
+    def broken(z, residue_mask, ln_w, ln_b, eps, w_a, w_b, w_o, b_o, outgoing=True):
+        x = O.layer_norm(z, ln_w, ln_b, eps)
+        return ((x @ w_a.T) * (x @ w_b.T)) @ w_o.T + b_o
+    monkeypatch.setattr(O, "tri_mul_forward", broken)
+    with pytest.raises(AssertionError):
+        test_trimul_matches_torch_einsum()
