@@ -611,4 +611,66 @@ evo_status_t tri_attn_module_bwd(
   }
 }
 
+// ------------------------------------------- triangular multiplicative update
+
+static evo_status_t check_trimul_sizes(evo_dtype_t dtype, int64_t N, int64_t CZ,
+                                       int64_t C) {
+  evo_status_t st = check_dtype(dtype);
+  if (st != EVO_OK) return st;
+  if (N <= 0 || CZ <= 0 || C <= 0)
+    return fail(EVO_EINVAL, "sizes must be positive (N=%lld CZ=%lld C=%lld)",
+                (long long)N, (long long)CZ, (long long)C);
+  if (N > 46340)  // N*N positions are indexed in 32 bits
+    return fail(EVO_ENOTSUP, "N=%lld is not supported (at most 46340)", (long long)N);
+  if (CZ % 32 != 0 || CZ > 128 || C % 32 != 0 || C > 128)
+    return fail(EVO_ENOTSUP, "CZ=%lld and C=%lld must be multiples of 32, at most "
+                "128", (long long)CZ, (long long)C);
+  if (C * N * N > kMaxElems)
+    return fail(EVO_ENOTSUP, "problem too large: tensors above 2^40 elements");
+  return EVO_OK;
+}
+
+size_t tri_mul_workspace_bytes(evo_dtype_t dtype, int64_t N, int64_t CZ,
+                               int64_t C) {
+  const std::string saved = g_last_error;
+  const evo_status_t st = check_trimul_sizes(dtype, N, CZ, C);
+  g_last_error = saved;
+  if (st != EVO_OK) return 0;
+  return evo::trimul_workspace((int)dtype, N, C);
+}
+
+evo_status_t tri_mul_fwd(evo_dtype_t dtype, int64_t N, int64_t CZ, int64_t C,
+                         int outgoing, const void* z,
+                         const uint8_t* residue_mask, const void* ln_w,
+                         const void* ln_b, float ln_eps, const void* w_a,
+                         const void* w_b, const void* w_o, const void* b_o,
+                         void* out, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  try {
+    evo_status_t st = check_trimul_sizes(dtype, N, CZ, C);
+    if (st != EVO_OK) return st;
+    if (outgoing != 0 && outgoing != 1)
+      return fail(EVO_EINVAL, "outgoing=%d must be 0 or 1", outgoing);
+    if (!(ln_eps > 0.f)) return fail(EVO_EINVAL, "ln_eps must be > 0");
+    REQUIRE_PTR(z);
+    REQUIRE_PTR(ln_w);
+    REQUIRE_PTR(ln_b);
+    REQUIRE_PTR(w_a);
+    REQUIRE_PTR(w_b);
+    REQUIRE_PTR(w_o);
+    REQUIRE_PTR(out);
+    OPTIONAL_PTR(b_o);
+    OPTIONAL_PTR(residue_mask);
+    st = check_workspace("tri_mul_fwd", workspace, workspace_bytes,
+                         evo::trimul_workspace((int)dtype, N, C));
+    if (st != EVO_OK) return st;
+    if (fault_injected()) return fail(EVO_EHIP, "tri_mul_fwd: injected launch failure");
+    evo::TriMulArgs a{(int)dtype, N, CZ, C, outgoing, z, residue_mask, ln_w,
+                      ln_b, ln_eps, w_a, w_b, w_o, b_o, out, workspace};
+    return from_hip(evo::launch_trimul(a, (hipStream_t)stream), "tri_mul_fwd");
+  } catch (...) {
+    return fail(EVO_EINTERNAL, "tri_mul_fwd: internal error");
+  }
+}
+
 }  // extern "C"

@@ -118,6 +118,42 @@ struct ProjectBwdArgs {
   void* workspace;  // proj_bwd_workspace bytes
 };
 
+// Triangular multiplicative update: LayerNorm + the a, b projections,
+// stored channel-major with padded rows [C][Np][Kp] (row = line i, column =
+// place k; zero where k is masked), for the per-channel products.
+struct TriMulProjectArgs {
+  int dtype;
+  int64_t N, CZ, C;
+  int outgoing;
+  const void* z;
+  const uint8_t* mask;
+  const void* ln_w;
+  const void* ln_b;
+  float eps;
+  const void* w_a;
+  const void* w_b;
+  void* a;
+  void* b;
+  int64_t Np, Kp;
+};
+
+struct TriMulArgs {
+  int dtype;
+  int64_t N, CZ, C;
+  int outgoing;
+  const void* z;
+  const uint8_t* mask;
+  const void* ln_w;
+  const void* ln_b;
+  float eps;
+  const void* w_a;
+  const void* w_b;
+  const void* w_o;
+  const void* b_o;
+  void* out;
+  void* workspace;  // trimul_workspace bytes
+};
+
 constexpr int kHeadDim = 32;
 
 size_t attn_fwd_workspace(int dtype, int64_t B, int64_t N, int64_t H);
@@ -128,6 +164,9 @@ hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t s);
 hipError_t launch_project(const ProjectArgs& a, hipStream_t s);
 hipError_t launch_out_project(const OutProjectArgs& a, hipStream_t s);
 size_t proj_bwd_workspace(int64_t N, int64_t CZ, int64_t H);
+hipError_t launch_trimul_project(const TriMulProjectArgs& a, hipStream_t s);
+size_t trimul_workspace(int dtype, int64_t N, int64_t C);
+hipError_t launch_trimul(const TriMulArgs& a, hipStream_t s);
 hipError_t launch_out_project_bwd(const OutProjectBwdArgs& a, hipStream_t s);
 hipError_t launch_project_bwd(const ProjectBwdArgs& a, hipStream_t s);
 

@@ -1,0 +1,373 @@
+// Triangular multiplicative update on gfx950.
+//
+// Edge (i, j) of the pair representation is updated from every third residue
+// k as the sum over k of a_ik * b_jk, channel by channel ("Evoformer: the
+// memory wall ZeRO cannot move", section "The three operations": O(N^3)
+// time, O(N^2) memory).  a and b are projections of the layer-normalised
+// pair representation; the update is projected back to c_z:
+//   x = LN(z),  a = x . W_a^T,  b = x . W_b^T                 (c channels)
+//   t[i,j,c] = sum_k keep[k] a[i,k,c] b[j,k,c]              (outgoing)
+//   t[i,j,c] = sum_k keep[k] a[k,i,c] b[k,j,c]              (incoming)
+//   out[i,j] = t[i,j] . W_o^T + b_o
+// Steps:
+//   1. the persistent row GEMM of the triangle-attention module (LayerNorm
+//      fused, the normalised tensor never written) writes a and b
+//      channel-major with padded rows, A_c[i][k] and B_c[j][k] (row = line,
+//      column = place; incoming reads z transposed), zero where k is masked;
+//      a small kernel zeroes the padding columns k >= N;
+//   2. trimul_gemm: for every channel, T_c = A_c . B_c^T, a dense bf16
+//      contraction over k on the matrix cores (fp32 accumulation), 128 x 128
+//      output tiles, K staged through double-buffered LDS;
+//   3. trimul_out: out[p] = W_o . T[:, p] + b_o with T read channel-major,
+//      staged through LDS and read with transposing LDS reads.
+#include <algorithm>
+
+#include "evo_device.h"
+#include "evo_kernels.h"
+
+namespace evo {
+namespace {
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+constexpr int kTile = 128;  // GEMM output tile (rows and columns)
+
+template <typename T> struct MulCfg;
+// K columns per LDS stage; LDS row stride (elements)
+template <> struct MulCfg<bf16_t> { static constexpr int BK = 64, RS = 72; };
+template <> struct MulCfg<float> { static constexpr int BK = 32, RS = 36; };
+
+// Columns [N, Kp) of rows [0, N) of the C channel matrices of a and b: zero.
+template <typename T>
+__global__ void __launch_bounds__(256) trimul_pad_kernel(T* a, T* b, int C, int N, int Np, int Kp) {
+  const int padw = Kp - N;
+  const int64_t total = (int64_t)C * N * padw;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * 256) {
+    const int col = N + (int)(e % padw);
+    const int64_t r = e / padw;  // channel * N + row
+    const int c = (int)(r / N), row = (int)(r - (int64_t)c * N);
+    const int64_t off = ((int64_t)c * Np + row) * Kp + col;
+    a[off] = T(0);
+    b[off] = T(0);
+  }
+}
+
+// ----------------------------------------------------------------- GEMM
+struct MulGemmParams {
+  int C, N, Np, Kp;
+  const void* a;  // [C][Np][Kp]
+  const void* b;  // [C][Np][Kp]
+  void* t;        // [C][N][N]
+  int ntile;      // Np / kTile
+};
+
+template <typename T>
+__device__ __forceinline__ void st4t(T* p, const f32x4& v);
+template <>
+__device__ __forceinline__ void st4t<bf16_t>(bf16_t* p, const f32x4& v) {
+  uint2 u;
+  u.x = uint32_t(Tr<bf16_t>::from_f(v[0])) | (uint32_t(Tr<bf16_t>::from_f(v[1])) << 16);
+  u.y = uint32_t(Tr<bf16_t>::from_f(v[2])) | (uint32_t(Tr<bf16_t>::from_f(v[3])) << 16);
+  *reinterpret_cast<uint2*>(p) = u;
+}
+template <>
+__device__ __forceinline__ void st4t<float>(float* p, const f32x4& v) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+
+// One workgroup (4 waves, 2 x 2) per 128 x 128 tile of one channel; a wave
+// owns 64 x 64 as 4 x 4 blocks of 16 x 16.  The product is formed as
+// T^T = B . A^T so that a lane's accumulators hold 4 consecutive columns j
+// of one row i (one 8- or 16-byte store).  Work order: column tile fastest,
+// then row tile, then channel; the XCD mapping gives each XCD a contiguous
+// range of channels, whose A and B (2 x Np x Kp) stay in its L2.
+template <typename T>
+__global__ void __launch_bounds__(256) trimul_gemm_kernel(MulGemmParams p) {
+  using Op = typename Tr<T>::Op;
+  constexpr int BK = MulCfg<T>::BK, RS = MulCfg<T>::RS;
+  constexpr int E16 = 16 / sizeof(T);            // elements per 16-byte chunk
+  constexpr int CPR = BK / E16;                  // chunks per tile row per stage
+  constexpr int CPT = kTile * CPR / 256;         // chunks per thread per tile
+  __shared__ __attribute__((aligned(16))) T sA[2][kTile * RS];
+  __shared__ __attribute__((aligned(16))) T sB[2][kTile * RS];
+
+  const int w = xcd_work_index(p.C * p.ntile * p.ntile);
+  if (w < 0) return;
+  const int tj = w % p.ntile, ti = (w / p.ntile) % p.ntile, c = w / (p.ntile * p.ntile);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, g = lane >> 4;
+  const int wi = wave >> 1, wj = wave & 1;
+  const int64_t cs = (int64_t)p.Np * p.Kp;
+  const T* A = static_cast<const T*>(p.a) + c * cs + (int64_t)ti * kTile * p.Kp;
+  const T* B = static_cast<const T*>(p.b) + c * cs + (int64_t)tj * kTile * p.Kp;
+
+  // staging: chunk e = tid + 256 u: tile row e / CPR, elements (e % CPR) * E16
+  u32x4 ra[CPT], rb[CPT];
+  auto fetch = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int e = tid + 256 * u, row = e / CPR, col = (e % CPR) * E16;
+      ra[u] = *reinterpret_cast<const u32x4*>(A + (int64_t)row * p.Kp + k0 + col);
+      rb[u] = *reinterpret_cast<const u32x4*>(B + (int64_t)row * p.Kp + k0 + col);
+    }
+  };
+  auto stage = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int e = tid + 256 * u, row = e / CPR, col = (e % CPR) * E16;
+      *reinterpret_cast<u32x4*>(sA[buf] + row * RS + col) = ra[u];
+      *reinterpret_cast<u32x4*>(sB[buf] + row * RS + col) = rb[u];
+    }
+  };
+
+  f32x4 acc[4][4];  // [column block bj][row block bi]
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nstage = p.Kp / BK;
+  fetch(0);
+  for (int st = 0; st < nstage; ++st) {
+    const int buf = st & 1;
+    stage(buf);
+    __syncthreads();
+    if (st + 1 < nstage) fetch((st + 1) * BK);
+#pragma unroll
+    for (int ks = 0; ks < BK / 32; ++ks) {
+      Op af[4], bf[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        af[x] = *reinterpret_cast<const Op*>(sA[buf] + (wi * 64 + x * 16 + l16) * RS + ks * 32 + 8 * g);
+        bf[x] = *reinterpret_cast<const Op*>(sB[buf] + (wj * 64 + x * 16 + l16) * RS + ks * 32 + 8 * g);
+      }
+#pragma unroll
+      for (int bj = 0; bj < 4; ++bj)
+#pragma unroll
+        for (int bi = 0; bi < 4; ++bi) acc[bj][bi] = mma32(bf[bj], af[bi], acc[bj][bi]);
+    }
+  }
+
+  // lane (l16, g) holds T[i = .. + bi*16 + l16][j = .. + bj*16 + 4g + r]
+  T* Tc = static_cast<T*>(p.t) + (int64_t)c * p.N * p.N;
+#pragma unroll
+  for (int bi = 0; bi < 4; ++bi) {
+    const int i = ti * kTile + wi * 64 + bi * 16 + l16;
+    if (i >= p.N) continue;
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) {
+      const int j0 = tj * kTile + wj * 64 + bj * 16 + 4 * g;
+      T* dst = Tc + (int64_t)i * p.N + j0;
+      if (j0 + 3 < p.N && (p.N & 3) == 0) {
+        st4t<T>(dst, acc[bj][bi]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (j0 + r < p.N) dst[r] = Tr<T>::from_f(acc[bj][bi][r]);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------ output projection
+struct MulOutParams {
+  int C, CZ, npos, ntiles;
+  const void* t;     // [C][npos]
+  const void* w_o;   // [CZ][C]
+  const void* b_o;   // [CZ] or null
+  void* out;         // [npos][CZ]
+};
+
+// Positions per workgroup tile (32 per wave).
+constexpr int kOutP = 128;
+
+template <typename T> struct OutLds;
+// bf16: T tile [C][128 + 8] read with transposing reads; fp32: [128][C + 4]
+// (stored transposed).
+template <> struct OutLds<bf16_t> { static constexpr int TS = kOutP + 8; };
+template <> struct OutLds<float> { static constexpr int TS = 128 + 4; };
+
+// Persistent workgroups (4 waves) with W_o resident in LDS; per tile of 128
+// positions: T[:, tile] staged in LDS, then out^T = W_o . T for each wave's
+// 32 positions.
+template <typename T, int CB>  // CB = CZ / 16
+__global__ void __launch_bounds__(256) trimul_out_kernel(MulOutParams p) {
+  using Op = typename Tr<T>::Op;
+  constexpr int TS = OutLds<T>::TS;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int C = p.C, WS = C + 8;
+  T* sW = reinterpret_cast<T*>(smem);        // [CZ][C + 8]
+  T* sT = sW + CB * 16 * WS;                 // bf16 [C][TS]; fp32 [kOutP][TS]
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, g = lane >> 4;
+  const int CZ = CB * 16;
+
+  for (int e = tid; e < CZ * C; e += 256) {
+    const int r = e / C, k = e - r * C;
+    sW[r * WS + k] = static_cast<const T*>(p.w_o)[e];
+  }
+  float bo[CB / 2][8];
+#pragma unroll
+  for (int s = 0; s < CB / 2; ++s)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      // column constant of output channel cb*16 + 4g + r, cb = 2s + j/4, r = j%4
+      const int cz = (2 * s + (j >> 2)) * 16 + 4 * g + (j & 3);
+      bo[s][j] = p.b_o ? Tr<T>::to_f(static_cast<const T*>(p.b_o)[cz]) : 0.f;
+    }
+  const T* Tg = static_cast<const T*>(p.t);
+  const int ksteps = C / 32;
+  for (int tile = blockIdx.x; tile < p.ntiles; tile += gridDim.x) {
+    const int p0 = tile * kOutP;
+    __syncthreads();  // previous tile's reads (and the weights) done
+    // stage T[:, p0 .. p0+127]: chunk e: channel e / (kOutP/8), positions 8*(e % 16)
+    constexpr int E16 = 16 / sizeof(T);
+    constexpr int CPR = kOutP / E16;
+    for (int e = tid; e < C * CPR; e += 256) {
+      const int k = e / CPR, pc = (e % CPR) * E16;
+      const int pos = p0 + pc;
+      u32x4 v = u32x4{0, 0, 0, 0};
+      if (pos + E16 <= p.npos) {
+        v = *reinterpret_cast<const u32x4*>(Tg + (int64_t)k * p.npos + pos);
+      } else {
+#pragma unroll
+        for (int q = 0; q < E16; ++q)
+          if (pos + q < p.npos) {
+            const T x = Tg[(int64_t)k * p.npos + pos + q];
+            if constexpr (sizeof(T) == 2)
+              v[q >> 1] |= uint32_t(x) << (16 * (q & 1));
+            else
+              v[q] = __float_as_uint(x);
+          }
+      }
+      if constexpr (sizeof(T) == 2) {
+        *reinterpret_cast<u32x4*>(sT + k * TS + pc) = v;
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sT[(pc + q) * TS + k] = __uint_as_float(v[q]);
+      }
+    }
+    __syncthreads();
+    f32x4 acc[CB][2];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) acc[cb][0] = acc[cb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ks = 0; ks < ksteps; ++ks) {
+      Op tf[2];
+#pragma unroll
+      for (int pb = 0; pb < 2; ++pb) {
+        const int pl = wave * 32 + pb * 16;  // tile-local position block
+        if constexpr (sizeof(T) == 2) {
+          // rows (channels) ks*32 + 8g .. +7 of column pl + l16
+          const T* q0 = sT + (ks * 32 + 8 * g + (l16 >> 2)) * TS + pl + 4 * (l16 & 3);
+          tf[pb] = lds_read_tr_op(q0, q0 + 4 * TS);
+        } else {
+          const float* q0 = sT + (pl + l16) * TS + ks * 32 + 8 * g;
+          tf[pb] = f32x8{q0[0], q0[1], q0[2], q0[3], q0[4], q0[5], q0[6], q0[7]};
+        }
+      }
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const Op wf = *reinterpret_cast<const Op*>(sW + (cb * 16 + l16) * WS + ks * 32 + 8 * g);
+        acc[cb][0] = mma32(wf, tf[0], acc[cb][0]);
+        acc[cb][1] = mma32(wf, tf[1], acc[cb][1]);
+      }
+    }
+    // lane (l16, g) holds out[position .. + l16][cb*16 + 4g + r]
+#pragma unroll
+    for (int pb = 0; pb < 2; ++pb) {
+      const int pos = p0 + wave * 32 + pb * 16 + l16;
+      if (pos >= p.npos) continue;
+      T* dst = static_cast<T*>(p.out) + (int64_t)pos * CZ + 4 * g;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        f32x4 v = acc[cb][pb];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] += bo[cb >> 1][4 * (cb & 1) + r];
+        st4t<T>(dst + cb * 16, v);
+      }
+    }
+  }
+}
+
+template <typename T, int CB>
+hipError_t launch_out(MulOutParams& o, hipStream_t s) {
+  const size_t lds = (size_t)CB * 16 * (o.C + 8) * sizeof(T) +
+                     (size_t)(sizeof(T) == 2 ? o.C : kOutP) * OutLds<T>::TS * sizeof(T);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&trimul_out_kernel<T, CB>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  const int grid = std::min(o.ntiles, 512);
+  hipLaunchKernelGGL((trimul_out_kernel<T, CB>), dim3(grid), dim3(256), lds, s, o);
+  return hipGetLastError();
+}
+
+struct MulLayout {
+  int64_t Np, Kp;
+  size_t a, b, t, total;
+};
+MulLayout mul_layout(int dtype, int64_t N, int64_t C) {
+  const size_t es = dtype == 1 ? 2 : 4;
+  MulLayout L;
+  L.Np = round_up(N, kTile);
+  L.Kp = round_up(N, 64);
+  const size_t ab = ((size_t)C * L.Np * L.Kp * es + 255) & ~size_t(255);
+  L.a = 0;
+  L.b = ab;
+  L.t = 2 * ab;
+  L.total = L.t + (((size_t)C * N * N * es + 255) & ~size_t(255));
+  return L;
+}
+
+template <typename T>
+hipError_t trimul_t(const TriMulArgs& a, hipStream_t s) {
+  const MulLayout L = mul_layout(a.dtype, a.N, a.C);
+  char* ws = static_cast<char*>(a.workspace);
+  T* A = reinterpret_cast<T*>(ws + L.a);
+  T* B = reinterpret_cast<T*>(ws + L.b);
+  T* Tm = reinterpret_cast<T*>(ws + L.t);
+  const int N = (int)a.N, C = (int)a.C;
+  TriMulProjectArgs pa{a.dtype, a.N, a.CZ, a.C, a.outgoing, a.z, a.mask, a.ln_w, a.ln_b,
+                       a.eps, a.w_a, a.w_b, A, B, L.Np, L.Kp};
+  hipError_t e = launch_trimul_project(pa, s);
+  if (e != hipSuccess) return e;
+  if (L.Kp > N) {
+    const int64_t total = (int64_t)C * N * (L.Kp - N);
+    const int grid = (int)std::min<int64_t>((total + 255) / 256, 4096);
+    hipLaunchKernelGGL(trimul_pad_kernel<T>, dim3(grid), dim3(256), 0, s, A, B, C, N,
+                       (int)L.Np, (int)L.Kp);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  MulGemmParams g{};
+  g.C = C; g.N = N; g.Np = (int)L.Np; g.Kp = (int)L.Kp;
+  g.a = A; g.b = B; g.t = Tm;
+  g.ntile = (int)(L.Np / kTile);
+  const int total = C * g.ntile * g.ntile;
+  const int grid = (total + kNumXcd - 1) / kNumXcd * kNumXcd;
+  hipLaunchKernelGGL(trimul_gemm_kernel<T>, dim3(grid), dim3(256), 0, s, g);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  MulOutParams o{};
+  o.C = C; o.CZ = (int)a.CZ; o.npos = N * N;
+  o.ntiles = (o.npos + kOutP - 1) / kOutP;
+  o.t = Tm; o.w_o = a.w_o; o.b_o = a.b_o; o.out = a.out;
+  switch (o.CZ / 16) {
+    case 2: return launch_out<T, 2>(o, s);
+    case 4: return launch_out<T, 4>(o, s);
+    case 6: return launch_out<T, 6>(o, s);
+    case 8: return launch_out<T, 8>(o, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+size_t trimul_workspace(int dtype, int64_t N, int64_t C) {
+  return mul_layout(dtype, N, C).total;
+}
+
+hipError_t launch_trimul(const TriMulArgs& a, hipStream_t s) {
+  return a.dtype == 1 ? trimul_t<bf16_t>(a, s) : trimul_t<float>(a, s);
+}
+
+}  // namespace evo

@@ -43,7 +43,8 @@ constexpr int PAD = 8;              // LDS row padding (elements)
 constexpr size_t kLdsBudget = 150 * 1024;
 
 struct GemmParams {
-  int mode;        // 0 = project (LayerNorm + q,k,v,g,bias), 1 = out projection
+  int mode;        // 0 = project (LayerNorm + q,k,v,g,bias), 1 = out projection,
+                   // 2 = multiplicative-update operands (LayerNorm + a, b)
   int N, K, HC, H, ending, ncols;   // ncols: all output columns
   int col0, pass_cols;              // this launch's column range (multiple of 16)
   int64_t npos;
@@ -57,6 +58,10 @@ struct GemmParams {
   const void* colbias;  // project: b_g [HC] (gate columns); out: b_o [ncols]
   void* y[5];           // project: q, k, v, g [npos, HC], bias [H, npos]
                         // out projection: out [npos, ncols] in z layout
+                        // operands: a, b [HC][Np][Kp], channel-major, row =
+                        // line, column = place (zero where the place is masked)
+  const uint8_t* mask;  // operands: residue keep flags [N] or null
+  int Np, Kp;           // operands: padded rows and row length
 };
 
 // z row (or output row) of line-layout position pidx (N*N < 2^31, so 32-bit
@@ -148,7 +153,9 @@ __device__ __forceinline__ void store_pair<float>(float* row, const f32x4& a, co
   }
 }
 
-template <typename T, int KSTEPS, int WAVES = waves_for<KSTEPS>()>
+// MUL: the multiplicative-update operand mode (p.mode == 2), a separate
+// instantiation so that the other modes' code is unchanged by it.
+template <typename T, int KSTEPS, int WAVES = waves_for<KSTEPS>(), bool MUL = false>
 __global__ void __launch_bounds__(WAVES * 64)
 rowgemm_kernel(GemmParams p) {
   using Op = typename Tr<T>::Op;
@@ -169,7 +176,7 @@ rowgemm_kernel(GemmParams p) {
     for (int pb = 0; pb < 2; ++pb) {
       bool live;
       const uint32_t pi = tile_pos<WAVES>(p, tile, wave, pb * 16 + l16, live);
-      const uint32_t row = live ? (p.mode == 0 ? z_row(pi, p.N, p.ending) : pi) : 0;
+      const uint32_t row = live ? (p.mode != 1 ? z_row(pi, p.N, p.ending) : pi) : 0;
       const T* src = X + (int64_t)row * K + 8 * g;
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) nx[pb][s] = *reinterpret_cast<const Op*>(src + 32 * s);
@@ -203,7 +210,7 @@ rowgemm_kernel(GemmParams p) {
         const T* src = e < total ? w_row<T>(p, p.col0 + cl) : nullptr;
         if (src) {
           ld_raw8(wr[u], src + k0);
-          if (p.mode == 0) ld_raw8(gr[u], lnw + k0);
+          if (p.mode != 1) ld_raw8(gr[u], lnw + k0);
         }
       }
 #pragma unroll
@@ -214,7 +221,7 @@ rowgemm_kernel(GemmParams p) {
         f32x4 w0 = {0.f, 0.f, 0.f, 0.f}, w1 = w0;
         if (w_row<T>(p, p.col0 + cl)) {
           widen8(wr[u], w0, w1);
-          if (p.mode == 0) {
+          if (p.mode != 1) {
             f32x4 g0, g1;
             widen8(gr[u], g0, g1);
             w0 *= g0;
@@ -235,7 +242,7 @@ rowgemm_kernel(GemmParams p) {
       const int c = p.col0 + cl;
       const T* src = w_row<T>(p, c);
       float acc = 0.f;
-      if (src && p.mode == 0) {
+      if (src && p.mode != 1) {
 #pragma unroll 4
         for (int k0 = 0; k0 < K; k0 += 8) {
           Raw8<T> wr, br;
@@ -250,7 +257,7 @@ rowgemm_kernel(GemmParams p) {
           for (int j = 0; j < 4; ++j) acc = __builtin_fmaf(b1[j], w1[j], acc);
         }
       }
-      if (src && p.colbias) {
+      if (src && p.colbias && p.mode != 2) {
         if (p.mode == 1) acc += Tr<T>::to_f(static_cast<const T*>(p.colbias)[c]);
         else if (c >= 3 * p.HC && c < 4 * p.HC)
           acc += Tr<T>::to_f(static_cast<const T*>(p.colbias)[c - 3 * p.HC]);
@@ -262,7 +269,7 @@ rowgemm_kernel(GemmParams p) {
 
   // output matrix and column within it where this pass starts (passes start
   // at multiples of 32 columns, so never inside a block pair)
-  const int m0 = p.mode == 0 ? min(p.col0 / p.HC, 4) : 0;
+  const int m0 = p.mode == 0 ? min(p.col0 / p.HC, 4) : p.mode == 2 ? p.col0 / p.HC : 0;
   const int cbase0 = p.col0 - m0 * p.HC;
   for (int tile = blockIdx.x; tile < p.ntiles; tile += gridDim.x) {
     if (!PREFETCH) load_rows(nx, tile);
@@ -289,7 +296,7 @@ rowgemm_kernel(GemmParams p) {
       for (int s = 0; s < KSTEPS; ++s)
 #pragma unroll
         for (int j = 0; j < 8; ++j) v[0][s][j] = (float)xf[pb][s][j];
-      if (p.mode == 0) {
+      if (p.mode != 1) {
         // two-pass statistics in fp32 (population variance), centred in place
         float sum = 0.f;
 #pragma unroll
@@ -335,9 +342,9 @@ rowgemm_kernel(GemmParams p) {
     for (int cb = 0, m = m0, cbase = cbase0; cb < nblk; ++m, cbase = 0) {
       const bool bias_out = p.mode == 0 && m == 4;
       const int width = p.mode == 1 ? p.ncols : (bias_out ? p.H : p.HC);
-      T* out = static_cast<T*>(p.y[p.mode == 1 ? 0 : m]);
+      T* out = static_cast<T*>(p.y[p.mode == 1 ? 0 : m]);  // mode 2: a, then b
       while (cb < nblk && cbase < width) {
-        const bool pair = !bias_out && cb + 1 < nblk && cbase + 32 <= width;
+        const bool pair = !MUL && !bias_out && cb + 1 < nblk && cbase + 32 <= width;
         f32x4 acc[2][2];  // [block][pb]
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -365,7 +372,16 @@ rowgemm_kernel(GemmParams p) {
         for (int pb = 0; pb < 2; ++pb) {
           if (!live[pb]) continue;
           const int c = cbase + 4 * g;
-          if (!bias_out) {
+          if constexpr (MUL) {
+            // channel-major [HC][Np][Kp]: element (line, place) of channel c+i
+            const uint32_t line = pidx[pb] / (uint32_t)p.N, place = pidx[pb] - line * (uint32_t)p.N;
+            const bool dead = p.mask && p.mask[place] == 0;
+            T* dst = out + (int64_t)line * p.Kp + place;
+            const int64_t cs = (int64_t)p.Np * p.Kp;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (c + i < p.HC) dst[(c + i) * cs] = Tr<T>::from_f(dead ? 0.f : acc[0][pb][i]);
+          } else if (!bias_out) {
             st4<T>(out + orow[pb] + c, acc[0][pb]);
           } else {
 #pragma unroll
@@ -376,24 +392,31 @@ rowgemm_kernel(GemmParams p) {
         cb += 1;
         cbase += 16;
       }
-      if (p.mode == 1 || m == 4) break;
+      if (p.mode == 1 || m == 4 || (MUL && m == 1)) break;
     }
   }
 }
 
-template <typename T, int KSTEPS>
-hipError_t launch_pass(GemmParams& p, size_t lds, hipStream_t s) {
+template <typename T, int KSTEPS, bool MUL>
+hipError_t launch_pass_m(GemmParams& p, size_t lds, hipStream_t s) {
   constexpr int WAVES = waves_for<KSTEPS>();
   const int64_t tiles = (p.npos + PW * WAVES - 1) / (PW * WAVES);
   if (tiles > (int64_t)INT32_MAX) return hipErrorInvalidValue;
   p.ntiles = (int)tiles;
   const int grid = (int)std::min<int64_t>(tiles, 256);  // persistent: one per CU
   hipError_t e = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&rowgemm_kernel<T, KSTEPS>),
+      reinterpret_cast<const void*>(&rowgemm_kernel<T, KSTEPS, WAVES, MUL>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((rowgemm_kernel<T, KSTEPS>), dim3(grid), dim3(WAVES * 64), lds, s, p);
+  hipLaunchKernelGGL((rowgemm_kernel<T, KSTEPS, WAVES, MUL>), dim3(grid), dim3(WAVES * 64), lds,
+                     s, p);
   return hipGetLastError();
+}
+
+template <typename T, int KSTEPS>
+hipError_t launch_pass(GemmParams& p, size_t lds, hipStream_t s) {
+  return p.mode == 2 ? launch_pass_m<T, KSTEPS, true>(p, lds, s)
+                     : launch_pass_m<T, KSTEPS, false>(p, lds, s);
 }
 
 template <typename T>
@@ -448,6 +471,31 @@ hipError_t launch_project(const ProjectArgs& a, hipStream_t s) {
   p.w[4] = a.w_bias;
   p.colbias = a.b_g;
   p.y[0] = a.q; p.y[1] = a.k; p.y[2] = a.v; p.y[3] = a.g; p.y[4] = a.bias;
+  return dispatch(a.dtype, p, s);
+}
+
+hipError_t launch_trimul_project(const TriMulProjectArgs& a, hipStream_t s) {
+  GemmParams p{};
+  p.mode = 2;
+  p.N = (int)a.N;
+  p.K = (int)a.CZ;
+  p.HC = (int)a.C;
+  p.H = 1;
+  p.ending = a.outgoing ? 0 : 1;  // incoming: line i holds edges (k, i)
+  p.ncols = 2 * p.HC;
+  p.npos = a.N * a.N;
+  p.x = a.z;
+  p.ln_w = a.ln_w;
+  p.ln_b = a.ln_b;
+  p.eps = a.eps;
+  p.w[0] = a.w_a;
+  p.w[1] = a.w_b;
+  p.colbias = nullptr;
+  p.y[0] = a.a;
+  p.y[1] = a.b;
+  p.mask = a.mask;
+  p.Np = (int)a.Np;
+  p.Kp = (int)a.Kp;
   return dispatch(a.dtype, p, s);
 }
 

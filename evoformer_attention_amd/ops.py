@@ -19,7 +19,7 @@ __all__ = ["EvoAttnError", "lib", "evo_abi_version", "evo_attn_fwd",
            "tri_attn_workspace_bytes", "tri_attn_proj_bwd_workspace_bytes",
            "tri_attn_out_project_bwd", "tri_attn_project_bwd",
            "tri_attn_bwd_workspace_bytes", "tri_attn_module_bwd",
-           "LIB_PATH", "EXPORTS"]
+           "tri_mul_workspace_bytes", "tri_mul_fwd", "LIB_PATH", "EXPORTS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
                         "libevoattn.so")
@@ -67,6 +67,9 @@ EXPORTS = {
                                  _P, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                  _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                  _SZ, _P]),
+    "tri_mul_workspace_bytes": (_SZ, [_I, _I64, _I64, _I64]),
+    "tri_mul_fwd": (_I, [_I, _I64, _I64, _I64, _I, _P, _P, _P, _P, _F, _P, _P,
+                         _P, _P, _P, _P, _SZ, _P]),
 }
 
 
@@ -392,3 +395,31 @@ def tri_attn_module_bwd(z, residue_mask, ln_w, ln_b, eps, w_q, w_k, w_v, w_g,
         workspace.numel(), _stream(z.device))
     _check("tri_attn_module_bwd", st)
     return res
+
+
+def tri_mul_workspace_bytes(dtype, N, CZ, C):
+    code = EVO_BF16 if dtype == torch.bfloat16 else EVO_FP32
+    return lib().tri_mul_workspace_bytes(code, N, CZ, C)
+
+
+def tri_mul_fwd(z, residue_mask, ln_w, ln_b, eps, w_a, w_b, w_o, b_o,
+                outgoing=True, workspace=None, out=None):
+    """Triangular multiplicative update -> [N,N,CZ] update."""
+    _dev_tensor("z", z)
+    N, _, CZ = z.shape
+    dt = z.dtype
+    for name, t in (("ln_w", ln_w), ("ln_b", ln_b), ("w_a", w_a), ("w_b", w_b),
+                    ("w_o", w_o), ("b_o", b_o)):
+        _dev_tensor(name, t, dt)
+    _dev_tensor("residue_mask", residue_mask, torch.uint8)
+    C = w_a.shape[0]
+    workspace = _workspace(tri_mul_workspace_bytes(dt, N, CZ, C), z.device, workspace)
+    if out is None:
+        out = torch.empty((N, N, CZ), dtype=dt, device=z.device)
+    st = lib().tri_mul_fwd(_dtype_code(z), N, CZ, C, int(bool(outgoing)),
+                           _ptr(z), _ptr(residue_mask), _ptr(ln_w), _ptr(ln_b),
+                           float(eps), _ptr(w_a), _ptr(w_b), _ptr(w_o),
+                           _ptr(b_o), _ptr(out), _ptr(workspace),
+                           workspace.numel(), _stream(z.device))
+    _check("tri_mul_fwd", st)
+    return out

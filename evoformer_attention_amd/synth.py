@@ -15,12 +15,14 @@ ZeRO cannot move"):
                     masked (5% of 768, rounded down)
   tri_start_512_bwd projection + core forward + core backward, starting node,
                     z [512,512,128], upstream gradient ~ N(0,1)
+  trimul_out_768    triangular multiplicative update, outgoing edges,
+                    z [768,768,128], 128 channels, 38 random residues masked
 """
 import math
 import torch
 
 __all__ = ["WORKLOADS", "core_inputs", "module_inputs", "round_to",
-           "rand_core", "rand_module"]
+           "rand_core", "rand_module", "rand_trimul", "trimul_inputs"]
 
 WORKLOADS = {
     "core_fp32_small": dict(kind="core", B=1, R=32, N=32, H=4, C=32,
@@ -33,6 +35,8 @@ WORKLOADS = {
                         dtype="bf16", ending=True, mask="random5"),
     "tri_start_512_bwd": dict(kind="module_bwd", N=512, CZ=128, H=4, C=32,
                               dtype="bf16", ending=False, mask=None),
+    "trimul_out_768": dict(kind="trimul", N=768, CZ=128, C=128, dtype="bf16",
+                           outgoing=True, mask="random5"),
 }
 
 _TORCH_DT = {"fp32": torch.float32, "bf16": torch.bfloat16}
@@ -129,3 +133,31 @@ def module_inputs(name, seed=0):
     w = WORKLOADS[name]
     return rand_module(w["N"], w["CZ"], w["H"], w["C"], w["dtype"], seed=seed,
                        mask=w["mask"], dout=(w["kind"] == "module_bwd"))
+
+
+def rand_trimul(N, CZ, C, dtype, seed=0, mask=None):
+    """Multiplicative-update inputs: z ~ N(0,1) [N,N,CZ]; w_a, w_b [C, CZ]
+    ~ N(0, 1/CZ); w_o [CZ, C] ~ N(0, 1/C) / sqrt(N) (the update sums N
+    products); LayerNorm weight 1 + N(0, 0.2^2), bias N(0, 0.2^2); b_o
+    N(0, 0.5^2).  Draw order: z, w_a, w_b, w_o, mask, ln_w, ln_b, b_o."""
+    gen = torch.Generator().manual_seed(seed)
+
+    def draw(shape, std=1.0):
+        return round_to(torch.randn(shape, generator=gen) * std, dtype)
+
+    d = {"z": draw((N, N, CZ))}
+    d["w_a"] = draw((C, CZ), CZ ** -0.5)
+    d["w_b"] = draw((C, CZ), CZ ** -0.5)
+    d["w_o"] = draw((CZ, C), (C * N) ** -0.5)
+    d["mask"] = _key_mask(mask, N, gen) if isinstance(mask, str) else mask
+    d["ln_w"] = draw((CZ,), 0.2) + 1
+    d["ln_b"] = draw((CZ,), 0.2)
+    d["b_o"] = draw((CZ,), 0.5)
+    d["eps"] = 1e-5
+    return d
+
+
+def trimul_inputs(name, seed=0):
+    w = WORKLOADS[name]
+    assert w["kind"] == "trimul"
+    return rand_trimul(w["N"], w["CZ"], w["C"], w["dtype"], seed=seed, mask=w["mask"])

@@ -313,6 +313,43 @@ evo_status_t tri_attn_module_bwd(
     float* dw_bias, float* dw_o, float* db_o, void* workspace,
     size_t workspace_bytes, void* stream);
 
+/*
+ * Triangular multiplicative update ("Evoformer: the memory wall ZeRO cannot
+ * move", section "The three operations"): edge (i, j) of the pair
+ * representation is updated from every third residue k as the sum over k of
+ * a_ik * b_jk, channel by channel.  a and b are projections of the
+ * layer-normalised pair representation (the normalisation and projection of
+ * tri_attn_project); the update is projected back to CZ channels:
+ *   x = LN(z),  a = x . w_a^T,  b = x . w_b^T                 (C channels)
+ *   outgoing:  t[i,j,c] = sum_k keep[k] a[i,k,c] b[j,k,c]
+ *   incoming:  t[i,j,c] = sum_k keep[k] a[k,i,c] b[k,j,c]
+ *   out[i,j]   = t[i,j] . w_o^T + b_o
+ * The sum over k is a dense per-channel matrix product (C products of
+ * N x N by N x N) on the matrix cores, fp32 accumulation.
+ *
+ *   z          [N,N,CZ] dtype; N at most 46340; CZ and C multiples of 32, at
+ *              most 128 (EVO_ENOTSUP otherwise).
+ *   residue_mask  [N] uint8, nonzero = keep residue k as a third residue;
+ *              NULL = keep all.
+ *   ln_w, ln_b [CZ] dtype; ln_eps > 0 (population variance, fp32 statistics).
+ *   w_a, w_b   [C, CZ] dtype ([out, in]); w_o [CZ, C] dtype; b_o [CZ] dtype
+ *              or NULL = zero.
+ *   outgoing   1 = outgoing edges (i,k), (j,k); 0 = incoming (k,i), (k,j).
+ *   out        [N,N,CZ] dtype, the update (no residual add).
+ *   workspace  tri_mul_workspace_bytes(...) bytes, caller-owned (a and b
+ *              channel-major with padded rows, and t; O(N^2 * C)).
+ * Pointers: device memory, 16-byte aligned.  Enqueued on `stream`.
+ */
+size_t tri_mul_workspace_bytes(evo_dtype_t dtype, int64_t N, int64_t CZ,
+                               int64_t C);
+evo_status_t tri_mul_fwd(evo_dtype_t dtype, int64_t N, int64_t CZ, int64_t C,
+                         int outgoing, const void* z,
+                         const uint8_t* residue_mask, const void* ln_w,
+                         const void* ln_b, float ln_eps, const void* w_a,
+                         const void* w_b, const void* w_o, const void* b_o,
+                         void* out, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -46,7 +46,7 @@ __all__ = [
     "dbias_query_rows", "layer_norm", "tri_project", "tri_out_project",
     "tri_module_forward", "tri_module_lines", "layer_norm_backward",
     "tri_out_project_backward", "tri_project_backward",
-    "tri_module_backward", "tri_mul_forward",
+    "tri_module_backward", "tri_mul_forward", "tri_mul_entries",
 ]
 
 
@@ -496,3 +496,25 @@ def tri_mul_forward(z, residue_mask, ln_w, ln_b, eps, w_a, w_b, w_o, b_o,
         Bm = b[:, :, c] if outgoing else b[:, :, c].T    # Bm[j, k]
         t[:, :, c] = (A * keep) @ Bm.T
     return t @ w_o.T + b_o
+
+
+def tri_mul_entries(z, residue_mask, ln_w, ln_b, eps, w_a, w_b, w_o, b_o,
+                    picks, outgoing=True):
+    """out[i, j] of tri_mul_forward for the (i, j) pairs in `picks` only: the
+    same definition, with the projections formed for the edges those entries
+    need (rows i and j for outgoing, columns for incoming), so that a few
+    entries of a large problem stay cheap.  Returns [len(picks), CZ]."""
+    z = np.asarray(z, np.float64)
+    N = z.shape[0]
+    keep = (np.ones(N) if residue_mask is None
+            else (np.asarray(residue_mask) != 0).astype(np.float64))
+    res = []
+    for i, j in picks:
+        # edges (i, k) and (j, k), or (k, i) and (k, j)
+        ei = z[i] if outgoing else z[:, i]
+        ej = z[j] if outgoing else z[:, j]
+        a = layer_norm(ei, ln_w, ln_b, eps) @ w_a.T       # [N, C]
+        b = layer_norm(ej, ln_w, ln_b, eps) @ w_b.T
+        t = (keep[:, None] * a * b).sum(axis=0)
+        res.append(t @ w_o.T + b_o)
+    return np.stack(res)

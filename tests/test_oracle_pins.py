@@ -747,3 +747,13 @@ def test_mutant_trimul_without_third_index_is_caught(monkeypatch):
     monkeypatch.setattr(O, "tri_mul_forward", broken)
     with pytest.raises(AssertionError):
         test_trimul_matches_torch_einsum()
+
+
+@pytest.mark.parametrize("outgoing", [True, False])
+def test_trimul_entries_match_full_forward(outgoing):
+    d = trimul_case(65, N=7)
+    full = O.tri_mul_forward(outgoing=outgoing, **d)
+    picks = [(0, 0), (2, 5), (6, 1)]
+    got = O.tri_mul_entries(picks=picks, outgoing=outgoing, **d)
+    for t, (i, j) in enumerate(picks):
+        np.testing.assert_allclose(got[t], full[i, j], rtol=1e-12, atol=1e-12)
