@@ -16,7 +16,8 @@ Prints one JSON line.  Options: --steps K --warmup W --gpus 1
 --workload NAME --no-cpu-baseline --cpu-lines L --calibrate-copy
 --write-traffic FETCH_CSV WRITE_CSV, and --module-train (a training step of
 the whole module instead: forward, then the backward with the LayerNorm,
-projection and output-projection gradients).
+projection and output-projection gradients) and --trimul (the triangular
+multiplicative update instead).
 """
 import argparse
 import hashlib
@@ -48,6 +49,10 @@ def parse():
                     help="time a training step of the whole module instead: "
                          "tri_attn_module_fwd + tri_attn_module_bwd (LayerNorm, "
                          "projection and output-projection gradients included)")
+    ap.add_argument("--trimul", action="store_true",
+                    help="time the triangular multiplicative update instead "
+                         "(tri_mul_fwd, outgoing edges, z [768,768,128], 128 "
+                         "channels, 38 residues masked)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU work: turn two rocprofv3 --pmc counter files "
                          "(FETCH_SIZE run, WRITE_SIZE run) of a --calibrate-copy "
@@ -276,8 +281,65 @@ def module_train(a):
     print(json.dumps(res), flush=True)
 
 
+def trimul_bench(a):
+    """The triangular multiplicative update on trimul_out_768.  Prints one
+    JSON line; the roofline entry is the whole tri_mul_fwd call against the
+    dense bf16 matrix-core peak, its flops dominated by the per-channel
+    products (2 C N^3)."""
+    import torch
+    from evoformer_attention_amd import metrics as M
+    from evoformer_attention_amd import ops, synth
+
+    w = dict(synth.WORKLOADS["trimul_out_768"])
+    N, CZ, C = w["N"], w["CZ"], w["C"]
+    d = synth.trimul_inputs("trimul_out_768")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    g = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    ws = torch.empty(ops.tri_mul_workspace_bytes(g["z"].dtype, N, CZ, C), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty((N, N, CZ), dtype=g["z"].dtype, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        return ops.tri_mul_fwd(g["z"], g["mask"], g["ln_w"], g["ln_b"], g["eps"], g["w_a"],
+                               g["w_b"], g["w_o"], g["b_o"], w["outgoing"], workspace=ws,
+                               out=out)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(a.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / a.steps
+    tf = M.trimul_flops(N, CZ, C) / (ms * 1e-3) / 1e12
+    res = {
+        "metric": "Triangular multiplicative update (outgoing) TFLOP/s (bf16), N_res=768, c=128",
+        "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "trimul_out_768", "N_res": N, "c_z": CZ, "channels": C,
+                   "edges": "outgoing", "masked_residues": int((d["mask"] == 0).sum())},
+        "roofline": {"bound": "mfma", "kernel": "tri_mul_fwd (call)", "achieved": round(tf, 2),
+                     "peak": M.MI355X_BF16_DENSE_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / M.MI355X_BF16_DENSE_TFLOPS, 4), "traffic": None},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     a = parse()
+    if a.trimul:
+        if a.gpus != 1:
+            print("bench.py runs on one GPU only", file=sys.stderr)
+            sys.exit(2)
+        trimul_bench(a)
+        return
     if a.module_train:
         if a.gpus != 1:
             print("bench.py runs on one GPU only", file=sys.stderr)

@@ -92,3 +92,10 @@ def project_bwd_min_bytes(N, CZ, H, C, elem_bytes):
     and dz written once; the fp32 parameter gradients are negligible."""
     t = N * N * H * C * elem_bytes
     return 4 * t + H * N * N * 4 + 2 * pair_rep_bytes(N, CZ, elem_bytes)
+
+
+def trimul_flops(N, CZ, C):
+    """Counted flops of one triangular multiplicative update: the a and b
+    projections (2 x C outputs per position), the per-channel products
+    (C matrices of N x N times N x N) and the output projection."""
+    return 2.0 * N * N * CZ * 2 * C + 2.0 * C * N ** 3 + 2.0 * N * N * C * CZ
