@@ -47,6 +47,7 @@ __all__ = [
     "tri_module_forward", "tri_module_lines", "layer_norm_backward",
     "tri_out_project_backward", "tri_project_backward",
     "tri_module_backward", "tri_mul_forward", "tri_mul_entries",
+    "transition_forward",
 ]
 
 
@@ -518,3 +519,23 @@ def tri_mul_entries(z, residue_mask, ln_w, ln_b, eps, w_a, w_b, w_o, b_o,
         t = (keep[:, None] * a * b).sum(axis=0)
         res.append(t @ w_o.T + b_o)
     return np.stack(res)
+
+
+# ----------------------------------------------------------------------------
+# LayerNorm + linear + SwiGLU transition.
+#
+# [MEGAFOLD] item 3 "EvoFusion" fuses layer normalisation, the linear
+# projections and the SwiGLU activations so that no N x N intermediate is
+# written between them.  The pages do not write the transition out; the
+# reading taken is the plain SwiGLU feed-forward block on the layer-normalised
+# pair representation, without bias vectors:
+#     x = LN(z),  h = silu(x . w_a^T) * (x . w_b^T),  out = h . w_o^T
+# with silu(u) = u * sigmoid(u) and a hidden width of w_a.shape[0].
+# ----------------------------------------------------------------------------
+
+def transition_forward(z, ln_w, ln_b, eps, w_a, w_b, w_o):
+    """z [..., CZ]; w_a, w_b [HID, CZ]; w_o [CZ, HID].  Returns [..., CZ]."""
+    x = layer_norm(z, ln_w, ln_b, eps)
+    u = x @ w_a.T
+    h = u * sigmoid(u) * (x @ w_b.T)
+    return h @ w_o.T

@@ -757,3 +757,76 @@ def test_trimul_entries_match_full_forward(outgoing):
     got = O.tri_mul_entries(picks=picks, outgoing=outgoing, **d)
     for t, (i, j) in enumerate(picks):
         np.testing.assert_allclose(got[t], full[i, j], rtol=1e-12, atol=1e-12)
+
+
+# -------------------------------------------- LayerNorm + SwiGLU transition
+
+def transition_case(seed, N=5, CZ=8, HID=12):
+    rng = np.random.default_rng(seed)
+    return dict(z=rng.standard_normal((N, N, CZ)),
+                ln_w=1 + 0.2 * rng.standard_normal(CZ),
+                ln_b=0.2 * rng.standard_normal(CZ), eps=1e-5,
+                w_a=rng.standard_normal((HID, CZ)) / CZ ** 0.5,
+                w_b=rng.standard_normal((HID, CZ)) / CZ ** 0.5,
+                w_o=rng.standard_normal((CZ, HID)) / HID ** 0.5)
+
+
+def test_transition_matches_torch():
+    """Library routines: F.layer_norm, F.linear, F.silu (fp64)."""
+    d = transition_case(70, N=7, CZ=16, HID=40)
+    t = {k: torch.tensor(v) for k, v in d.items() if isinstance(v, np.ndarray)}
+    x = F.layer_norm(t["z"], (16,), t["ln_w"], t["ln_b"], 1e-5)
+    ref = F.linear(F.silu(F.linear(x, t["w_a"])) * F.linear(x, t["w_b"]), t["w_o"])
+    np.testing.assert_allclose(O.transition_forward(**d), ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_transition_matches_scalar_loops():
+    """Brute force on a tiny case: every sum written as a loop, silu(u) as
+    u / (1 + exp(-u))."""
+    d = transition_case(71, N=2, CZ=4, HID=3)
+    z = d["z"]
+    N, _, CZ = z.shape
+    HID = d["w_a"].shape[0]
+    got = O.transition_forward(**d)
+    for i in range(N):
+        for j in range(N):
+            v = z[i, j]
+            mu = sum(v) / CZ
+            var = sum((q - mu) ** 2 for q in v) / CZ
+            x = [(v[q] - mu) / np.sqrt(var + d["eps"]) * d["ln_w"][q] + d["ln_b"][q]
+                 for q in range(CZ)]
+            h = []
+            for m in range(HID):
+                u = sum(x[q] * d["w_a"][m, q] for q in range(CZ))
+                b = sum(x[q] * d["w_b"][m, q] for q in range(CZ))
+                h.append(u / (1.0 + np.exp(-u)) * b)
+            for o in range(CZ):
+                ref = sum(h[m] * d["w_o"][o, m] for m in range(HID))
+                assert abs(got[i, j, o] - ref) <= 1e-12 * max(1.0, abs(ref))
+
+
+def test_transition_closed_forms():
+    """w_b = 0 or w_a = 0 give 0 (silu(0) = 0); the output is linear in w_o
+    and in w_b; a shift of a position's channels leaves it unchanged
+    (LayerNorm)."""
+    d = transition_case(72)
+    out = O.transition_forward(**d)
+    e = dict(d, w_b=np.zeros_like(d["w_b"]))
+    assert np.abs(O.transition_forward(**e)).max() == 0
+    e = dict(d, w_a=np.zeros_like(d["w_a"]))
+    assert np.abs(O.transition_forward(**e)).max() == 0
+    np.testing.assert_allclose(O.transition_forward(**dict(d, w_o=3 * d["w_o"])), 3 * out,
+                               rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(O.transition_forward(**dict(d, w_b=-2 * d["w_b"])), -2 * out,
+                               rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(O.transition_forward(**dict(d, z=d["z"] + 5.0)), out,
+                               rtol=1e-8, atol=1e-9)
+
+
+def test_mutant_transition_relu_gate_is_caught(monkeypatch):
+    def relu_gate(z, ln_w, ln_b, eps, w_a, w_b, w_o):
+        x = O.layer_norm(z, ln_w, ln_b, eps)
+        return (np.maximum(x @ w_a.T, 0) * (x @ w_b.T)) @ w_o.T
+    monkeypatch.setattr(O, "transition_forward", relu_gate)
+    with pytest.raises(AssertionError):
+        test_transition_matches_torch()
