@@ -673,4 +673,63 @@ evo_status_t tri_mul_fwd(evo_dtype_t dtype, int64_t N, int64_t CZ, int64_t C,
   }
 }
 
+// ---------------------------------------------- LayerNorm + SwiGLU transition
+
+static evo_status_t check_transition_sizes(evo_dtype_t dtype, int64_t N,
+                                           int64_t CZ, int64_t HID) {
+  evo_status_t st = check_dtype(dtype);
+  if (st != EVO_OK) return st;
+  if (N <= 0 || CZ <= 0 || HID <= 0)
+    return fail(EVO_EINVAL, "sizes must be positive (N=%lld CZ=%lld HID=%lld)",
+                (long long)N, (long long)CZ, (long long)HID);
+  if (N > 46340)  // N*N positions are indexed in 32 bits
+    return fail(EVO_ENOTSUP, "N=%lld is not supported (at most 46340)", (long long)N);
+  if (CZ % 32 != 0 || CZ > 128)
+    return fail(EVO_ENOTSUP, "CZ=%lld must be a multiple of 32, at most 128", (long long)CZ);
+  if (HID % 64 != 0 || HID > 4096)
+    return fail(EVO_ENOTSUP, "HID=%lld must be a multiple of 64, at most 4096",
+                (long long)HID);
+  return EVO_OK;
+}
+
+size_t pair_transition_workspace_bytes(evo_dtype_t dtype, int64_t N, int64_t CZ,
+                                       int64_t HID) {
+  const std::string saved = g_last_error;
+  const evo_status_t st = check_transition_sizes(dtype, N, CZ, HID);
+  g_last_error = saved;
+  if (st != EVO_OK) return 0;
+  return evo::transition_workspace((int)dtype, CZ, HID);
+}
+
+evo_status_t pair_transition_fwd(evo_dtype_t dtype, int64_t N, int64_t CZ,
+                                 int64_t HID, const void* z, const void* ln_w,
+                                 const void* ln_b, float ln_eps,
+                                 const void* w_a, const void* w_b,
+                                 const void* w_o, void* out, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  try {
+    evo_status_t st = check_transition_sizes(dtype, N, CZ, HID);
+    if (st != EVO_OK) return st;
+    if (!(ln_eps > 0.f)) return fail(EVO_EINVAL, "ln_eps must be > 0");
+    REQUIRE_PTR(z);
+    REQUIRE_PTR(ln_w);
+    REQUIRE_PTR(ln_b);
+    REQUIRE_PTR(w_a);
+    REQUIRE_PTR(w_b);
+    REQUIRE_PTR(w_o);
+    REQUIRE_PTR(out);
+    st = check_workspace("pair_transition_fwd", workspace, workspace_bytes,
+                         evo::transition_workspace((int)dtype, CZ, HID));
+    if (st != EVO_OK) return st;
+    if (fault_injected())
+      return fail(EVO_EHIP, "pair_transition_fwd: injected launch failure");
+    evo::TransitionArgs a{(int)dtype, N * N, CZ, HID, z, ln_w, ln_b, ln_eps,
+                          w_a, w_b, w_o, out, workspace};
+    return from_hip(evo::launch_transition(a, (hipStream_t)stream),
+                    "pair_transition_fwd");
+  } catch (...) {
+    return fail(EVO_EINTERNAL, "pair_transition_fwd: internal error");
+  }
+}
+
 }  // extern "C"

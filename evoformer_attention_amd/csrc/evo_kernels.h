@@ -154,6 +154,20 @@ struct TriMulArgs {
   void* workspace;  // trimul_workspace bytes
 };
 
+struct TransitionArgs {
+  int dtype;
+  int64_t npos, CZ, HID;
+  const void* z;
+  const void* ln_w;
+  const void* ln_b;
+  float eps;
+  const void* w_a;
+  const void* w_b;
+  const void* w_o;
+  void* out;
+  void* workspace;  // transition_workspace bytes
+};
+
 constexpr int kHeadDim = 32;
 
 size_t attn_fwd_workspace(int dtype, int64_t B, int64_t N, int64_t H);
@@ -167,6 +181,8 @@ size_t proj_bwd_workspace(int64_t N, int64_t CZ, int64_t H);
 hipError_t launch_trimul_project(const TriMulProjectArgs& a, hipStream_t s);
 size_t trimul_workspace(int dtype, int64_t N, int64_t C);
 hipError_t launch_trimul(const TriMulArgs& a, hipStream_t s);
+size_t transition_workspace(int dtype, int64_t CZ, int64_t HID);
+hipError_t launch_transition(const TransitionArgs& a, hipStream_t s);
 hipError_t launch_out_project_bwd(const OutProjectBwdArgs& a, hipStream_t s);
 hipError_t launch_project_bwd(const ProjectBwdArgs& a, hipStream_t s);
 

@@ -19,7 +19,9 @@ __all__ = ["EvoAttnError", "lib", "evo_abi_version", "evo_attn_fwd",
            "tri_attn_workspace_bytes", "tri_attn_proj_bwd_workspace_bytes",
            "tri_attn_out_project_bwd", "tri_attn_project_bwd",
            "tri_attn_bwd_workspace_bytes", "tri_attn_module_bwd",
-           "tri_mul_workspace_bytes", "tri_mul_fwd", "LIB_PATH", "EXPORTS"]
+           "tri_mul_workspace_bytes", "tri_mul_fwd", "pair_transition_fwd",
+           "pair_transition_workspace_bytes",
+           "LIB_PATH", "EXPORTS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
                         "libevoattn.so")
@@ -70,6 +72,9 @@ EXPORTS = {
     "tri_mul_workspace_bytes": (_SZ, [_I, _I64, _I64, _I64]),
     "tri_mul_fwd": (_I, [_I, _I64, _I64, _I64, _I, _P, _P, _P, _P, _F, _P, _P,
                          _P, _P, _P, _P, _SZ, _P]),
+    "pair_transition_workspace_bytes": (_SZ, [_I, _I64, _I64, _I64]),
+    "pair_transition_fwd": (_I, [_I, _I64, _I64, _I64, _P, _P, _P, _F, _P, _P,
+                                 _P, _P, _P, _SZ, _P]),
 }
 
 
@@ -422,4 +427,32 @@ def tri_mul_fwd(z, residue_mask, ln_w, ln_b, eps, w_a, w_b, w_o, b_o,
                            _ptr(b_o), _ptr(out), _ptr(workspace),
                            workspace.numel(), _stream(z.device))
     _check("tri_mul_fwd", st)
+    return out
+
+
+def pair_transition_workspace_bytes(dtype, N, CZ, HID):
+    code = EVO_BF16 if dtype == torch.bfloat16 else EVO_FP32
+    return lib().pair_transition_workspace_bytes(code, N, CZ, HID)
+
+
+def pair_transition_fwd(z, ln_w, ln_b, eps, w_a, w_b, w_o, out=None,
+                        workspace=None):
+    """LayerNorm + SwiGLU transition of the pair representation -> [N,N,CZ]."""
+    _dev_tensor("z", z)
+    N, _, CZ = z.shape
+    dt = z.dtype
+    for name, t in (("ln_w", ln_w), ("ln_b", ln_b), ("w_a", w_a), ("w_b", w_b),
+                    ("w_o", w_o)):
+        _dev_tensor(name, t, dt)
+    HID = w_a.shape[0]
+    workspace = _workspace(pair_transition_workspace_bytes(dt, N, CZ, HID),
+                           z.device, workspace)
+    if out is None:
+        out = torch.empty((N, N, CZ), dtype=dt, device=z.device)
+    st = lib().pair_transition_fwd(_dtype_code(z), N, CZ, HID, _ptr(z),
+                                   _ptr(ln_w), _ptr(ln_b), float(eps),
+                                   _ptr(w_a), _ptr(w_b), _ptr(w_o), _ptr(out),
+                                   _ptr(workspace), workspace.numel(),
+                                   _stream(z.device))
+    _check("pair_transition_fwd", st)
     return out

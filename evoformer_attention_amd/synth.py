@@ -17,12 +17,15 @@ ZeRO cannot move"):
                     z [512,512,128], upstream gradient ~ N(0,1)
   trimul_out_768    triangular multiplicative update, outgoing edges,
                     z [768,768,128], 128 channels, 38 random residues masked
+  transition_768    LayerNorm + SwiGLU transition, z [768,768,128], hidden
+                    width 4 x 128 = 512
 """
 import math
 import torch
 
 __all__ = ["WORKLOADS", "core_inputs", "module_inputs", "round_to",
-           "rand_core", "rand_module", "rand_trimul", "trimul_inputs"]
+           "rand_core", "rand_module", "rand_trimul", "trimul_inputs",
+           "rand_transition", "transition_inputs"]
 
 WORKLOADS = {
     "core_fp32_small": dict(kind="core", B=1, R=32, N=32, H=4, C=32,
@@ -37,6 +40,7 @@ WORKLOADS = {
                               dtype="bf16", ending=False, mask=None),
     "trimul_out_768": dict(kind="trimul", N=768, CZ=128, C=128, dtype="bf16",
                            outgoing=True, mask="random5"),
+    "transition_768": dict(kind="transition", N=768, CZ=128, HID=512, dtype="bf16"),
 }
 
 _TORCH_DT = {"fp32": torch.float32, "bf16": torch.bfloat16}
@@ -161,3 +165,28 @@ def trimul_inputs(name, seed=0):
     w = WORKLOADS[name]
     assert w["kind"] == "trimul"
     return rand_trimul(w["N"], w["CZ"], w["C"], w["dtype"], seed=seed, mask=w["mask"])
+
+
+def rand_transition(N, CZ, HID, dtype, seed=0):
+    """Transition inputs: z ~ N(0,1) [N,N,CZ]; w_a, w_b [HID, CZ] ~ N(0,
+    1/CZ); w_o [CZ, HID] ~ N(0, 1/HID); LayerNorm weight 1 + N(0, 0.2^2),
+    bias N(0, 0.2^2).  Draw order: z, w_a, w_b, w_o, ln_w, ln_b."""
+    gen = torch.Generator().manual_seed(seed)
+
+    def draw(shape, std=1.0):
+        return round_to(torch.randn(shape, generator=gen) * std, dtype)
+
+    d = {"z": draw((N, N, CZ))}
+    d["w_a"] = draw((HID, CZ), CZ ** -0.5)
+    d["w_b"] = draw((HID, CZ), CZ ** -0.5)
+    d["w_o"] = draw((CZ, HID), HID ** -0.5)
+    d["ln_w"] = draw((CZ,), 0.2) + 1
+    d["ln_b"] = draw((CZ,), 0.2)
+    d["eps"] = 1e-5
+    return d
+
+
+def transition_inputs(name, seed=0):
+    w = WORKLOADS[name]
+    assert w["kind"] == "transition"
+    return rand_transition(w["N"], w["CZ"], w["HID"], w["dtype"], seed=seed)

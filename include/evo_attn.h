@@ -350,6 +350,36 @@ evo_status_t tri_mul_fwd(evo_dtype_t dtype, int64_t N, int64_t CZ, int64_t C,
                          void* out, void* workspace, size_t workspace_bytes,
                          void* stream);
 
+/*
+ * pair_transition_fwd -- LayerNorm + linear + SwiGLU transition of the pair
+ * representation, fused (EvoFusion, "MegaFold: Efficient Training of
+ * Next-Generation 3D Attention Protein Models on Cross-Platform GPUs",
+ * section "Methodologie", item 3: no N x N intermediate is written between
+ * the normalisation, the projections and the activation).  Per position:
+ *   x = LN(z),  h = silu(x . w_a^T) * (x . w_b^T),  out = h . w_o^T
+ * with silu(u) = u * sigmoid(u); no bias vectors; fp32 accumulation.
+ *
+ *   z          [N,N,CZ] dtype; N at most 46340; CZ a multiple of 32, at most
+ *              128 (EVO_ENOTSUP otherwise).
+ *   ln_w, ln_b [CZ] dtype; ln_eps > 0 (population variance, fp32 statistics).
+ *   w_a, w_b   [HID, CZ] dtype ([out, in]); HID a multiple of 64, at most
+ *              4096 (EVO_ENOTSUP otherwise).
+ *   w_o        [CZ, HID] dtype.
+ *   out        [N,N,CZ] dtype.
+ *   workspace  pair_transition_workspace_bytes(...) bytes, caller-owned: the
+ *              weights rearranged once per call for the fused kernel
+ *              (O(HID * CZ), independent of N).
+ * Pointers: device memory, 16-byte aligned.  Enqueued on `stream`.
+ */
+size_t pair_transition_workspace_bytes(evo_dtype_t dtype, int64_t N,
+                                       int64_t CZ, int64_t HID);
+evo_status_t pair_transition_fwd(evo_dtype_t dtype, int64_t N, int64_t CZ,
+                                 int64_t HID, const void* z, const void* ln_w,
+                                 const void* ln_b, float ln_eps,
+                                 const void* w_a, const void* w_b,
+                                 const void* w_o, void* out, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
