@@ -16,8 +16,9 @@ Prints one JSON line.  Options: --steps K --warmup W --gpus 1
 --workload NAME --no-cpu-baseline --cpu-lines L --calibrate-copy
 --write-traffic FETCH_CSV WRITE_CSV, and --module-train (a training step of
 the whole module instead: forward, then the backward with the LayerNorm,
-projection and output-projection gradients) and --trimul (the triangular
-multiplicative update instead).
+projection and output-projection gradients), --trimul (the triangular
+multiplicative update instead) and --transition (the fused LayerNorm + SwiGLU
+transition instead).
 """
 import argparse
 import hashlib
@@ -53,6 +54,9 @@ def parse():
                     help="time the triangular multiplicative update instead "
                          "(tri_mul_fwd, outgoing edges, z [768,768,128], 128 "
                          "channels, 38 residues masked)")
+    ap.add_argument("--transition", action="store_true",
+                    help="time the fused LayerNorm + SwiGLU transition instead "
+                         "(pair_transition_fwd, z [768,768,128], hidden 512)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU work: turn two rocprofv3 --pmc counter files "
                          "(FETCH_SIZE run, WRITE_SIZE run) of a --calibrate-copy "
@@ -332,8 +336,63 @@ def trimul_bench(a):
     print(json.dumps(res), flush=True)
 
 
+def transition_bench(a):
+    """The fused transition on transition_768.  Prints one JSON line; the
+    roofline entry is the call (a weight-preparation kernel of ~1% plus the
+    fused kernel) against the dense bf16 matrix-core peak."""
+    import torch
+    from evoformer_attention_amd import metrics as M
+    from evoformer_attention_amd import ops, synth
+
+    w = dict(synth.WORKLOADS["transition_768"])
+    N, CZ, HID = w["N"], w["CZ"], w["HID"]
+    d = synth.transition_inputs("transition_768")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    g = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    ws = torch.empty(ops.pair_transition_workspace_bytes(g["z"].dtype, N, CZ, HID),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty_like(g["z"])
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        return ops.pair_transition_fwd(g["z"], g["ln_w"], g["ln_b"], g["eps"], g["w_a"],
+                                       g["w_b"], g["w_o"], out=out, workspace=ws)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(a.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / a.steps
+    tf = M.transition_flops(N, CZ, HID) / (ms * 1e-3) / 1e12
+    res = {
+        "metric": "Fused LayerNorm + SwiGLU pair transition TFLOP/s (bf16), N_res=768",
+        "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "transition_768", "N_res": N, "c_z": CZ, "hidden": HID},
+        "roofline": {"bound": "mfma", "kernel": "pair_transition_fwd (call)",
+                     "achieved": round(tf, 2), "peak": M.MI355X_BF16_DENSE_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf / M.MI355X_BF16_DENSE_TFLOPS, 4),
+                     "traffic": None},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     a = parse()
+    if a.transition:
+        if a.gpus != 1:
+            print("bench.py runs on one GPU only", file=sys.stderr)
+            sys.exit(2)
+        transition_bench(a)
+        return
     if a.trimul:
         if a.gpus != 1:
             print("bench.py runs on one GPU only", file=sys.stderr)

@@ -99,3 +99,9 @@ def trimul_flops(N, CZ, C):
     projections (2 x C outputs per position), the per-channel products
     (C matrices of N x N times N x N) and the output projection."""
     return 2.0 * N * N * CZ * 2 * C + 2.0 * C * N ** 3 + 2.0 * N * N * C * CZ
+
+
+def transition_flops(N, CZ, HID):
+    """Counted flops of the LayerNorm + SwiGLU transition: two [HID, CZ]
+    projections and the [CZ, HID] output projection per position."""
+    return 2.0 * N * N * (2 * HID * CZ + HID * CZ)

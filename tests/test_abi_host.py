@@ -229,3 +229,28 @@ def test_module_bwd_fault_injection(monkeypatch):
     monkeypatch.setenv("EVO_FAULT_INJECT", "launch")
     assert module_bwd() == ops.EVO_EHIP
     assert "injected" in err()
+
+
+def test_trimul_and_transition_validation():
+    assert L.tri_mul_workspace_bytes(1, 768, 128, 128) >= 3 * 128 * 768 * 768 * 2
+    assert L.tri_mul_workspace_bytes(1, 768, 128, 100) == 0   # C not a multiple of 32
+    args = [1, 64, 128, 128, 1, FAKE, None, FAKE, FAKE, 1e-5, FAKE, FAKE, FAKE,
+            None, FAKE, FAKE, 1 << 40, None]
+    args[4] = 2
+    assert L.tri_mul_fwd(*args) == ops.EVO_EINVAL and "outgoing" in err()
+    args[4] = 1
+    args[16] = 10
+    assert L.tri_mul_fwd(*args) == ops.EVO_EWORKSPACE
+    args[16] = 1 << 40
+    args[3] = 256
+    assert L.tri_mul_fwd(*args) == ops.EVO_ENOTSUP
+    w = L.pair_transition_workspace_bytes(1, 768, 128, 512)
+    assert 0 < w < 1 << 20  # the rearranged weights only, independent of N
+    assert L.pair_transition_workspace_bytes(1, 64, 128, 500) == 0  # HID % 64
+    targs = [1, 64, 128, 512, FAKE, FAKE, FAKE, 1e-5, FAKE, FAKE, FAKE, FAKE,
+             FAKE, 1 << 30, None]
+    targs[11] = None
+    assert L.pair_transition_fwd(*targs) == ops.EVO_EINVAL and "'out' is NULL" in err()
+    targs[11] = FAKE
+    targs[13] = 16
+    assert L.pair_transition_fwd(*targs) == ops.EVO_EWORKSPACE
