@@ -47,7 +47,7 @@ __all__ = [
     "tri_module_forward", "tri_module_lines", "layer_norm_backward",
     "tri_out_project_backward", "tri_project_backward",
     "tri_module_backward", "tri_mul_forward", "tri_mul_entries",
-    "transition_forward",
+    "transition_forward", "outer_product_mean", "outer_product_mean_pairs",
 ]
 
 
@@ -539,3 +539,49 @@ def transition_forward(z, ln_w, ln_b, eps, w_a, w_b, w_o):
     u = x @ w_a.T
     h = u * sigmoid(u) * (x @ w_b.T)
     return h @ w_o.T
+
+
+# ----------------------------------------------------------------------------
+# Outer product mean.
+#
+# [COURSE] "The three operations": the bridge from the MSA to the pair
+# representation averages, over all sequences, the outer product of MSA
+# columns i and j.  Reading (the pages give no formula): the MSA
+# representation m [S, N, c_m] is layer-normalised and projected to two
+# c-channel vectors per (sequence, residue), a = LN(m) . w_a^T and
+# b = LN(m) . w_b^T (no bias); for every residue pair
+#     o[i, j, c, d] = (1/S) sum_s a[s, i, c] b[s, j, d],
+# flattened with d fastest and projected to c_z with an output bias:
+#     out[i, j] = o[i, j].reshape(c*c) . w_o^T + b_o.
+# ----------------------------------------------------------------------------
+
+def outer_product_mean(m, ln_w, ln_b, eps, w_a, w_b, w_o, b_o):
+    """m [S, N, CM]; w_a, w_b [C, CM]; w_o [CZ, C*C]; b_o [CZ].
+    Returns [N, N, CZ]."""
+    m = np.asarray(m, np.float64)
+    S, N, _ = m.shape
+    x = layer_norm(m, ln_w, ln_b, eps)
+    a = x @ w_a.T                                   # [S, N, C]
+    b = x @ w_b.T
+    C = a.shape[-1]
+    # o[i, j, c, d]: one residue i at a time (memory N^2 C^2)
+    out = np.empty((N, N, w_o.shape[0]))
+    for i in range(N):
+        o_i = np.einsum("sc,sjd->jcd", a[:, i, :], b) / S   # [N, C, C]
+        out[i] = o_i.reshape(N, C * C) @ w_o.T + b_o
+    return out
+
+
+def outer_product_mean_pairs(m, ln_w, ln_b, eps, w_a, w_b, w_o, b_o, picks):
+    """out[i, j] of outer_product_mean for the (i, j) pairs in `picks` only,
+    with the projections formed for residues i and j alone.  Returns
+    [len(picks), CZ]."""
+    m = np.asarray(m, np.float64)
+    S = m.shape[0]
+    res = []
+    for i, j in picks:
+        a = layer_norm(m[:, i], ln_w, ln_b, eps) @ w_a.T    # [S, C]
+        b = layer_norm(m[:, j], ln_w, ln_b, eps) @ w_b.T
+        o = a.T @ b / S                                      # [C, C]
+        res.append(o.reshape(-1) @ w_o.T + b_o)
+    return np.stack(res)

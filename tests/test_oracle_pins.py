@@ -830,3 +830,93 @@ def test_mutant_transition_relu_gate_is_caught(monkeypatch):
     monkeypatch.setattr(O, "transition_forward", relu_gate)
     with pytest.raises(AssertionError):
         test_transition_matches_torch()
+
+
+# ------------------------------------------------------- outer product mean
+
+def opm_case(seed, S=4, N=5, CM=6, C=3, CZ=7):
+    rng = np.random.default_rng(seed)
+    return dict(m=rng.standard_normal((S, N, CM)),
+                ln_w=1 + 0.2 * rng.standard_normal(CM),
+                ln_b=0.2 * rng.standard_normal(CM), eps=1e-5,
+                w_a=rng.standard_normal((C, CM)) / CM ** 0.5,
+                w_b=rng.standard_normal((C, CM)) / CM ** 0.5,
+                w_o=rng.standard_normal((CZ, C * C)) / C,
+                b_o=0.3 * rng.standard_normal(CZ))
+
+
+def test_opm_matches_torch_einsum():
+    """Library routines: F.layer_norm, F.linear, torch.einsum (fp64)."""
+    d = opm_case(80, S=6, N=7, CM=10, C=4, CZ=9)
+    t = {k: torch.tensor(v) for k, v in d.items() if isinstance(v, np.ndarray)}
+    x = F.layer_norm(t["m"], (10,), t["ln_w"], t["ln_b"], 1e-5)
+    a, b = F.linear(x, t["w_a"]), F.linear(x, t["w_b"])
+    o = torch.einsum("sic,sjd->ijcd", a, b) / 6
+    ref = F.linear(o.reshape(7, 7, 16), t["w_o"], t["b_o"])
+    np.testing.assert_allclose(O.outer_product_mean(**d), ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_opm_matches_scalar_loops():
+    d = opm_case(81, S=3, N=3, CM=4, C=2, CZ=3)
+    got = O.outer_product_mean(**d)
+    m = d["m"]
+    S, N, CM = m.shape
+    x = np.empty_like(m)
+    for s in range(S):
+        for n in range(N):
+            v = m[s, n]
+            mu = sum(v) / CM
+            var = sum((q - mu) ** 2 for q in v) / CM
+            for q in range(CM):
+                x[s, n, q] = (v[q] - mu) / np.sqrt(var + d["eps"]) * d["ln_w"][q] + d["ln_b"][q]
+    C = d["w_a"].shape[0]
+    for i in range(N):
+        for j in range(N):
+            o = [[sum(sum(x[s, i, q] * d["w_a"][c, q] for q in range(CM)) *
+                      sum(x[s, j, q] * d["w_b"][e, q] for q in range(CM)) for s in range(S)) / S
+                  for e in range(C)] for c in range(C)]
+            for z in range(d["w_o"].shape[0]):
+                ref = sum(o[c][e] * d["w_o"][z, c * C + e] for c in range(C) for e in range(C))
+                assert abs(got[i, j, z] - (ref + d["b_o"][z])) < 1e-12
+
+
+def test_opm_sequence_order_carries_no_information():
+    """Permuting the MSA rows leaves the mean unchanged ("Non-query MSA row
+    invariance"), and permuting residues permutes both pair axes."""
+    d = opm_case(82, S=6, N=5)
+    out = O.outer_product_mean(**d)
+    e = dict(d, m=d["m"][np.random.default_rng(1).permutation(6)])
+    np.testing.assert_allclose(O.outer_product_mean(**e), out, rtol=1e-12, atol=1e-12)
+    perm = np.random.default_rng(2).permutation(5)
+    e = dict(d, m=d["m"][:, perm])
+    np.testing.assert_allclose(O.outer_product_mean(**e), out[perm][:, perm], rtol=1e-12,
+                               atol=1e-12)
+
+
+def test_opm_single_sequence_is_outer_product():
+    d = opm_case(83, S=1, N=4, C=3)
+    x = O.layer_norm(d["m"][0], d["ln_w"], d["ln_b"], d["eps"])
+    a, b = x @ d["w_a"].T, x @ d["w_b"].T
+    i, j = 1, 3
+    ref = np.outer(a[i], b[j]).reshape(-1) @ d["w_o"].T + d["b_o"]
+    np.testing.assert_allclose(O.outer_product_mean(**d)[i, j], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_opm_pairs_match_full():
+    d = opm_case(84, S=5, N=6)
+    full = O.outer_product_mean(**d)
+    picks = [(0, 0), (2, 5), (5, 1)]
+    got = O.outer_product_mean_pairs(picks=picks, **d)
+    for t, (i, j) in enumerate(picks):
+        np.testing.assert_allclose(got[t], full[i, j], rtol=1e-12, atol=1e-12)
+
+
+def test_mutant_opm_sum_instead_of_mean_is_caught(monkeypatch):
+    orig = O.outer_product_mean
+
+    def summed(m, ln_w, ln_b, eps, w_a, w_b, w_o, b_o):
+        S = m.shape[0]
+        return (orig(m, ln_w, ln_b, eps, w_a, w_b, w_o, b_o) - b_o) * S + b_o
+    monkeypatch.setattr(O, "outer_product_mean", summed)
+    with pytest.raises(AssertionError):
+        test_opm_matches_torch_einsum()
