@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libevoattn.so")
 SOURCES = ["evo_api.cpp", "attn_fwd.hip", "attn_bwd.hip", "tri_project.hip",
-           "tri_module_bwd.hip", "tri_mul.hip", "transition.hip"]
+           "tri_module_bwd.hip", "tri_mul.hip", "transition.hip", "opm.hip"]
 ARCH = "gfx950"
 
 

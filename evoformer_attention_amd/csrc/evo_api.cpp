@@ -613,6 +613,26 @@ evo_status_t tri_attn_module_bwd(
 
 // ------------------------------------------- triangular multiplicative update
 
+static evo_status_t check_opm_sizes(evo_dtype_t dtype, int64_t S, int64_t N,
+                                    int64_t CM, int64_t C, int64_t CZ) {
+  evo_status_t st = check_dtype(dtype);
+  if (st != EVO_OK) return st;
+  if (S <= 0 || N <= 0 || CM <= 0 || C <= 0 || CZ <= 0)
+    return fail(EVO_EINVAL, "sizes must be positive (S=%lld N=%lld CM=%lld C=%lld CZ=%lld)",
+                (long long)S, (long long)N, (long long)CM, (long long)C, (long long)CZ);
+  if (S > INT32_MAX / N)  // sequence-residue positions are indexed in 32 bits
+    return fail(EVO_ENOTSUP, "S*N=%lld*%lld is not supported (below 2^31)", (long long)S,
+                (long long)N);
+  if (CM % 32 != 0 || CM > 256)
+    return fail(EVO_ENOTSUP, "CM=%lld must be a multiple of 32, at most 256", (long long)CM);
+  if (CZ % 32 != 0 || CZ > 128 || C % 32 != 0 || C > 128)
+    return fail(EVO_ENOTSUP, "CZ=%lld and C=%lld must be multiples of 32, at most "
+                "128", (long long)CZ, (long long)C);
+  if (N * C > 46340 || (N * C) * (N * C) > kMaxElems)  // product rows indexed in 32 bits
+    return fail(EVO_ENOTSUP, "N*C=%lld is not supported (at most 46340)", (long long)(N * C));
+  return EVO_OK;
+}
+
 static evo_status_t check_trimul_sizes(evo_dtype_t dtype, int64_t N, int64_t CZ,
                                        int64_t C) {
   evo_status_t st = check_dtype(dtype);
@@ -729,6 +749,47 @@ evo_status_t pair_transition_fwd(evo_dtype_t dtype, int64_t N, int64_t CZ,
                     "pair_transition_fwd");
   } catch (...) {
     return fail(EVO_EINTERNAL, "pair_transition_fwd: internal error");
+  }
+}
+
+
+size_t outer_product_mean_workspace_bytes(evo_dtype_t dtype, int64_t S, int64_t N,
+                                          int64_t CM, int64_t C, int64_t CZ) {
+  const std::string saved = g_last_error;
+  const evo_status_t st = check_opm_sizes(dtype, S, N, CM, C, CZ);
+  g_last_error = saved;
+  if (st != EVO_OK) return 0;
+  return evo::opm_workspace((int)dtype, S, N, C);
+}
+
+evo_status_t outer_product_mean_fwd(evo_dtype_t dtype, int64_t S, int64_t N, int64_t CM,
+                                    int64_t C, int64_t CZ, const void* m, const void* ln_w,
+                                    const void* ln_b, float ln_eps, const void* w_a,
+                                    const void* w_b, const void* w_o, const void* b_o,
+                                    void* out, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  try {
+    evo_status_t st = check_opm_sizes(dtype, S, N, CM, C, CZ);
+    if (st != EVO_OK) return st;
+    if (!(ln_eps > 0.f)) return fail(EVO_EINVAL, "ln_eps must be > 0");
+    REQUIRE_PTR(m);
+    REQUIRE_PTR(ln_w);
+    REQUIRE_PTR(ln_b);
+    REQUIRE_PTR(w_a);
+    REQUIRE_PTR(w_b);
+    REQUIRE_PTR(w_o);
+    REQUIRE_PTR(out);
+    OPTIONAL_PTR(b_o);
+    st = check_workspace("outer_product_mean_fwd", workspace, workspace_bytes,
+                         evo::opm_workspace((int)dtype, S, N, C));
+    if (st != EVO_OK) return st;
+    if (fault_injected())
+      return fail(EVO_EHIP, "outer_product_mean_fwd: injected launch failure");
+    evo::OpmArgs a{(int)dtype, S, N, CM, C, CZ, m, ln_w, ln_b, ln_eps,
+                   w_a, w_b, w_o, b_o, out, workspace};
+    return from_hip(evo::launch_opm(a, (hipStream_t)stream), "outer_product_mean_fwd");
+  } catch (...) {
+    return fail(EVO_EINTERNAL, "outer_product_mean_fwd: internal error");
   }
 }
 

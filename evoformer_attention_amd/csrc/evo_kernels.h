@@ -118,15 +118,16 @@ struct ProjectBwdArgs {
   void* workspace;  // proj_bwd_workspace bytes
 };
 
-// Triangular multiplicative update: LayerNorm + the a, b projections,
-// stored channel-major with padded rows [C][Np][Kp] (row = line i, column =
-// place k; zero where k is masked), for the per-channel products.
-struct TriMulProjectArgs {
+// LayerNorm + two projections (a, b) of rows of a [lines x places x CZ]
+// tensor, stored element (channel c, line, place) at c*s_ch + line*s_line +
+// place*s_place, zero where the place is masked.  Row of (line, place):
+// line*P + place, or place*L + line when transposed.
+struct ChannelProjectArgs {
   int dtype;
-  int64_t N, CZ, C;
-  int outgoing;
+  int64_t L, P, CZ, C;
+  int transposed;
   const void* z;
-  const uint8_t* mask;
+  const uint8_t* mask;  // [P] keep flags or null
   const void* ln_w;
   const void* ln_b;
   float eps;
@@ -134,7 +135,7 @@ struct TriMulProjectArgs {
   const void* w_b;
   void* a;
   void* b;
-  int64_t Np, Kp;
+  int64_t s_ch, s_line, s_place;
 };
 
 struct TriMulArgs {
@@ -178,9 +179,31 @@ hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t s);
 hipError_t launch_project(const ProjectArgs& a, hipStream_t s);
 hipError_t launch_out_project(const OutProjectArgs& a, hipStream_t s);
 size_t proj_bwd_workspace(int64_t N, int64_t CZ, int64_t H);
-hipError_t launch_trimul_project(const TriMulProjectArgs& a, hipStream_t s);
+hipError_t launch_channel_project(const ChannelProjectArgs& a, hipStream_t s);
 size_t trimul_workspace(int dtype, int64_t N, int64_t C);
 hipError_t launch_trimul(const TriMulArgs& a, hipStream_t s);
+// T_c = A_c . B_c^T for c < C: A, B [C][Np][Kp] (columns >= K zeroed here),
+// T [C][M][M]; M <= Np, Np a multiple of pair_gemm_row_tile().
+int pair_gemm_row_tile();
+hipError_t launch_pair_gemm(int dtype, int C, int M, int K, int Np, int Kp, void* a, void* b,
+                            void* t, hipStream_t s);
+// Outer product mean: m [S][N][CM] -> out [N][N][CZ].
+struct OpmArgs {
+  int dtype;
+  int64_t S, N, CM, C, CZ;
+  const void* m;
+  const void* ln_w;
+  const void* ln_b;
+  float eps;
+  const void* w_a;  // [C][CM]
+  const void* w_b;  // [C][CM]
+  const void* w_o;  // [CZ][C * C]
+  const void* b_o;  // [CZ] or null
+  void* out;
+  void* workspace;  // opm_workspace bytes
+};
+size_t opm_workspace(int dtype, int64_t S, int64_t N, int64_t C);
+hipError_t launch_opm(const OpmArgs& a, hipStream_t s);
 size_t transition_workspace(int dtype, int64_t CZ, int64_t HID);
 hipError_t launch_transition(const TransitionArgs& a, hipStream_t s);
 hipError_t launch_out_project_bwd(const OutProjectBwdArgs& a, hipStream_t s);

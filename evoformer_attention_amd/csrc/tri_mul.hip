@@ -36,16 +36,16 @@ template <typename T> struct MulCfg;
 template <> struct MulCfg<bf16_t> { static constexpr int BK = 64, RS = 72; };
 template <> struct MulCfg<float> { static constexpr int BK = 32, RS = 36; };
 
-// Columns [N, Kp) of rows [0, N) of the C channel matrices of a and b: zero.
+// Columns [K, Kp) of rows [0, M) of the C matrices [Np][Kp] of a and b: zero.
 template <typename T>
-__global__ void __launch_bounds__(256) trimul_pad_kernel(T* a, T* b, int C, int N, int Np, int Kp) {
-  const int padw = Kp - N;
-  const int64_t total = (int64_t)C * N * padw;
+__global__ void __launch_bounds__(256) pad_cols_kernel(T* a, T* b, int C, int M, int K, int Np, int Kp) {
+  const int padw = Kp - K;
+  const int64_t total = (int64_t)C * M * padw;
   for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total;
        e += (int64_t)gridDim.x * 256) {
-    const int col = N + (int)(e % padw);
-    const int64_t r = e / padw;  // channel * N + row
-    const int c = (int)(r / N), row = (int)(r - (int64_t)c * N);
+    const int col = K + (int)(e % padw);
+    const int64_t r = e / padw;  // matrix * M + row
+    const int c = (int)(r / M), row = (int)(r - (int64_t)c * M);
     const int64_t off = ((int64_t)c * Np + row) * Kp + col;
     a[off] = T(0);
     b[off] = T(0);
@@ -54,12 +54,15 @@ __global__ void __launch_bounds__(256) trimul_pad_kernel(T* a, T* b, int C, int 
 
 // ----------------------------------------------------------------- GEMM
 struct MulGemmParams {
-  int C, N, Np, Kp;
+  int C, N, Np, Kp;  // N: rows of each product (at most Np)
   const void* a;  // [C][Np][Kp]
   const void* b;  // [C][Np][Kp]
   void* t;        // [C][N][N]
   int ntile;      // Np / kTile
 };
+
+// Row tiles per group of the work order.
+constexpr int kGroup = 8;
 
 template <typename T>
 __device__ __forceinline__ void st4t(T* p, const f32x4& v);
@@ -78,9 +81,11 @@ __device__ __forceinline__ void st4t<float>(float* p, const f32x4& v) {
 // One workgroup (4 waves, 2 x 2) per 128 x 128 tile of one channel; a wave
 // owns 64 x 64 as 4 x 4 blocks of 16 x 16.  The product is formed as
 // T^T = B . A^T so that a lane's accumulators hold 4 consecutive columns j
-// of one row i (one 8- or 16-byte store).  Work order: column tile fastest,
-// then row tile, then channel; the XCD mapping gives each XCD a contiguous
-// range of channels, whose A and B (2 x Np x Kp) stay in its L2.
+// of one row i (one 8- or 16-byte store).  Work order: channel slowest;
+// within a channel, groups of kGroup row tiles, and in a group the row tile
+// fastest, so that the tiles an XCD runs at one time (the XCD mapping gives
+// it a contiguous range of the order) share a few row and column tiles of A
+// and B in its L2.
 template <typename T>
 __global__ void __launch_bounds__(256) trimul_gemm_kernel(MulGemmParams p) {
   using Op = typename Tr<T>::Op;
@@ -93,7 +98,12 @@ __global__ void __launch_bounds__(256) trimul_gemm_kernel(MulGemmParams p) {
 
   const int w = xcd_work_index(p.C * p.ntile * p.ntile);
   if (w < 0) return;
-  const int tj = w % p.ntile, ti = (w / p.ntile) % p.ntile, c = w / (p.ntile * p.ntile);
+  const int per_c = p.ntile * p.ntile;
+  const int c = w / per_c, r0 = w - c * per_c;
+  const int first = r0 / (kGroup * p.ntile) * kGroup;
+  const int h = min(kGroup, p.ntile - first);
+  const int r = r0 - first * p.ntile;
+  const int ti = first + r % h, tj = r / h;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
@@ -321,6 +331,25 @@ MulLayout mul_layout(int dtype, int64_t N, int64_t C) {
 }
 
 template <typename T>
+hipError_t pair_gemm_t(int C, int M, int K, int Np, int Kp, T* A, T* B, T* Tm, hipStream_t s) {
+  hipError_t e;
+  if (Kp > K) {
+    const int64_t total = (int64_t)C * M * (Kp - K);
+    const int grid = (int)std::min<int64_t>((total + 255) / 256, 4096);
+    hipLaunchKernelGGL(pad_cols_kernel<T>, dim3(grid), dim3(256), 0, s, A, B, C, M, K, Np, Kp);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  MulGemmParams g{};
+  g.C = C; g.N = M; g.Np = Np; g.Kp = Kp;
+  g.a = A; g.b = B; g.t = Tm;
+  g.ntile = Np / kTile;
+  const int total = C * g.ntile * g.ntile;
+  const int grid = (total + kNumXcd - 1) / kNumXcd * kNumXcd;
+  hipLaunchKernelGGL(trimul_gemm_kernel<T>, dim3(grid), dim3(256), 0, s, g);
+  return hipGetLastError();
+}
+
+template <typename T>
 hipError_t trimul_t(const TriMulArgs& a, hipStream_t s) {
   const MulLayout L = mul_layout(a.dtype, a.N, a.C);
   char* ws = static_cast<char*>(a.workspace);
@@ -328,25 +357,13 @@ hipError_t trimul_t(const TriMulArgs& a, hipStream_t s) {
   T* B = reinterpret_cast<T*>(ws + L.b);
   T* Tm = reinterpret_cast<T*>(ws + L.t);
   const int N = (int)a.N, C = (int)a.C;
-  TriMulProjectArgs pa{a.dtype, a.N, a.CZ, a.C, a.outgoing, a.z, a.mask, a.ln_w, a.ln_b,
-                       a.eps, a.w_a, a.w_b, A, B, L.Np, L.Kp};
-  hipError_t e = launch_trimul_project(pa, s);
+  // A_c[line][place], B_c likewise; incoming lines read z transposed
+  ChannelProjectArgs pa{a.dtype, a.N, a.N, a.CZ, a.C, a.outgoing ? 0 : 1, a.z, a.mask,
+                        a.ln_w, a.ln_b, a.eps, a.w_a, a.w_b, A, B,
+                        L.Np * L.Kp, L.Kp, 1};
+  hipError_t e = launch_channel_project(pa, s);
   if (e != hipSuccess) return e;
-  if (L.Kp > N) {
-    const int64_t total = (int64_t)C * N * (L.Kp - N);
-    const int grid = (int)std::min<int64_t>((total + 255) / 256, 4096);
-    hipLaunchKernelGGL(trimul_pad_kernel<T>, dim3(grid), dim3(256), 0, s, A, B, C, N,
-                       (int)L.Np, (int)L.Kp);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  MulGemmParams g{};
-  g.C = C; g.N = N; g.Np = (int)L.Np; g.Kp = (int)L.Kp;
-  g.a = A; g.b = B; g.t = Tm;
-  g.ntile = (int)(L.Np / kTile);
-  const int total = C * g.ntile * g.ntile;
-  const int grid = (total + kNumXcd - 1) / kNumXcd * kNumXcd;
-  hipLaunchKernelGGL(trimul_gemm_kernel<T>, dim3(grid), dim3(256), 0, s, g);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = pair_gemm_t<T>(C, N, N, (int)L.Np, (int)L.Kp, A, B, Tm, s)) != hipSuccess) return e;
   MulOutParams o{};
   o.C = C; o.CZ = (int)a.CZ; o.npos = N * N;
   o.ntiles = (o.npos + kOutP - 1) / kOutP;
@@ -368,6 +385,19 @@ size_t trimul_workspace(int dtype, int64_t N, int64_t C) {
 
 hipError_t launch_trimul(const TriMulArgs& a, hipStream_t s) {
   return a.dtype == 1 ? trimul_t<bf16_t>(a, s) : trimul_t<float>(a, s);
+}
+
+int pair_gemm_row_tile() { return kTile; }
+
+hipError_t launch_pair_gemm(int dtype, int C, int M, int K, int Np, int Kp, void* a, void* b,
+                            void* t, hipStream_t s) {
+  if (Np % kTile != 0 || M > Np || K > Kp || Kp % MulCfg<float>::BK != 0 ||
+      Kp % MulCfg<bf16_t>::BK != 0)
+    return hipErrorInvalidValue;
+  return dtype == 1 ? pair_gemm_t<bf16_t>(C, M, K, Np, Kp, static_cast<bf16_t*>(a),
+                                          static_cast<bf16_t*>(b), static_cast<bf16_t*>(t), s)
+                    : pair_gemm_t<float>(C, M, K, Np, Kp, static_cast<float*>(a),
+                                         static_cast<float*>(b), static_cast<float*>(t), s);
 }
 
 }  // namespace evo

@@ -58,10 +58,12 @@ struct GemmParams {
   const void* colbias;  // project: b_g [HC] (gate columns); out: b_o [ncols]
   void* y[5];           // project: q, k, v, g [npos, HC], bias [H, npos]
                         // out projection: out [npos, ncols] in z layout
-                        // operands: a, b [HC][Np][Kp], channel-major, row =
-                        // line, column = place (zero where the place is masked)
-  const uint8_t* mask;  // operands: residue keep flags [N] or null
-  int Np, Kp;           // operands: padded rows and row length
+                        // operands: a, b, element (channel c, line, place) at
+                        // c*s_ch + line*s_line + place*s_place (zero where
+                        // the place is masked)
+  const uint8_t* mask;  // operands: keep flags per place, or null
+  int P, L;             // operands: places per line, lines (npos = P * L)
+  int64_t s_ch, s_line, s_place;
 };
 
 // z row (or output row) of line-layout position pidx (N*N < 2^31, so 32-bit
@@ -176,7 +178,16 @@ rowgemm_kernel(GemmParams p) {
     for (int pb = 0; pb < 2; ++pb) {
       bool live;
       const uint32_t pi = tile_pos<WAVES>(p, tile, wave, pb * 16 + l16, live);
-      const uint32_t row = live ? (p.mode != 1 ? z_row(pi, p.N, p.ending) : pi) : 0;
+      uint32_t row = 0;
+      if (live) {
+        if constexpr (MUL) {
+          // operands: line-major positions; transposed rows are place * L + line
+          const uint32_t ln = pi / (uint32_t)p.P, pl = pi - ln * (uint32_t)p.P;
+          row = p.ending ? pl * (uint32_t)p.L + ln : pi;
+        } else {
+          row = p.mode != 1 ? z_row(pi, p.N, p.ending) : pi;
+        }
+      }
       const T* src = X + (int64_t)row * K + 8 * g;
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) nx[pb][s] = *reinterpret_cast<const Op*>(src + 32 * s);
@@ -373,14 +384,13 @@ rowgemm_kernel(GemmParams p) {
           if (!live[pb]) continue;
           const int c = cbase + 4 * g;
           if constexpr (MUL) {
-            // channel-major [HC][Np][Kp]: element (line, place) of channel c+i
-            const uint32_t line = pidx[pb] / (uint32_t)p.N, place = pidx[pb] - line * (uint32_t)p.N;
+            // element (line, place) of channel c+i
+            const uint32_t line = pidx[pb] / (uint32_t)p.P, place = pidx[pb] - line * (uint32_t)p.P;
             const bool dead = p.mask && p.mask[place] == 0;
-            T* dst = out + (int64_t)line * p.Kp + place;
-            const int64_t cs = (int64_t)p.Np * p.Kp;
+            T* dst = out + (int64_t)line * p.s_line + (int64_t)place * p.s_place;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-              if (c + i < p.HC) dst[(c + i) * cs] = Tr<T>::from_f(dead ? 0.f : acc[0][pb][i]);
+              if (c + i < p.HC) dst[(c + i) * p.s_ch] = Tr<T>::from_f(dead ? 0.f : acc[0][pb][i]);
           } else if (!bias_out) {
             st4<T>(out + orow[pb] + c, acc[0][pb]);
           } else {
@@ -474,16 +484,16 @@ hipError_t launch_project(const ProjectArgs& a, hipStream_t s) {
   return dispatch(a.dtype, p, s);
 }
 
-hipError_t launch_trimul_project(const TriMulProjectArgs& a, hipStream_t s) {
+hipError_t launch_channel_project(const ChannelProjectArgs& a, hipStream_t s) {
   GemmParams p{};
   p.mode = 2;
-  p.N = (int)a.N;
+  p.N = (int)a.L;
   p.K = (int)a.CZ;
   p.HC = (int)a.C;
   p.H = 1;
-  p.ending = a.outgoing ? 0 : 1;  // incoming: line i holds edges (k, i)
+  p.ending = a.transposed;
   p.ncols = 2 * p.HC;
-  p.npos = a.N * a.N;
+  p.npos = a.L * a.P;
   p.x = a.z;
   p.ln_w = a.ln_w;
   p.ln_b = a.ln_b;
@@ -494,8 +504,11 @@ hipError_t launch_trimul_project(const TriMulProjectArgs& a, hipStream_t s) {
   p.y[0] = a.a;
   p.y[1] = a.b;
   p.mask = a.mask;
-  p.Np = (int)a.Np;
-  p.Kp = (int)a.Kp;
+  p.P = (int)a.P;
+  p.L = (int)a.L;
+  p.s_ch = a.s_ch;
+  p.s_line = a.s_line;
+  p.s_place = a.s_place;
   return dispatch(a.dtype, p, s);
 }
 

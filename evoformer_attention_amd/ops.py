@@ -21,6 +21,7 @@ __all__ = ["EvoAttnError", "lib", "evo_abi_version", "evo_attn_fwd",
            "tri_attn_bwd_workspace_bytes", "tri_attn_module_bwd",
            "tri_mul_workspace_bytes", "tri_mul_fwd", "pair_transition_fwd",
            "pair_transition_workspace_bytes",
+           "outer_product_mean_workspace_bytes", "outer_product_mean_fwd",
            "LIB_PATH", "EXPORTS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
@@ -75,6 +76,10 @@ EXPORTS = {
     "pair_transition_workspace_bytes": (_SZ, [_I, _I64, _I64, _I64]),
     "pair_transition_fwd": (_I, [_I, _I64, _I64, _I64, _P, _P, _P, _F, _P, _P,
                                  _P, _P, _P, _SZ, _P]),
+    "outer_product_mean_workspace_bytes": (_SZ, [_I, _I64, _I64, _I64, _I64,
+                                                 _I64]),
+    "outer_product_mean_fwd": (_I, [_I, _I64, _I64, _I64, _I64, _I64, _P, _P,
+                                    _P, _F, _P, _P, _P, _P, _P, _P, _SZ, _P]),
 }
 
 
@@ -455,4 +460,32 @@ def pair_transition_fwd(z, ln_w, ln_b, eps, w_a, w_b, w_o, out=None,
                                    _ptr(workspace), workspace.numel(),
                                    _stream(z.device))
     _check("pair_transition_fwd", st)
+    return out
+
+
+def outer_product_mean_workspace_bytes(dtype, S, N, CM, C, CZ):
+    code = EVO_BF16 if dtype == torch.bfloat16 else EVO_FP32
+    return lib().outer_product_mean_workspace_bytes(code, S, N, CM, C, CZ)
+
+
+def outer_product_mean_fwd(m, ln_w, ln_b, eps, w_a, w_b, w_o, b_o, out=None,
+                           workspace=None):
+    """Outer product mean of the MSA representation m [S,N,CM] -> [N,N,CZ]."""
+    _dev_tensor("m", m)
+    S, N, CM = m.shape
+    dt = m.dtype
+    for name, t in (("ln_w", ln_w), ("ln_b", ln_b), ("w_a", w_a), ("w_b", w_b),
+                    ("w_o", w_o), ("b_o", b_o)):
+        _dev_tensor(name, t, dt)
+    C, CZ = w_a.shape[0], w_o.shape[0]
+    workspace = _workspace(outer_product_mean_workspace_bytes(dt, S, N, CM, C, CZ),
+                           m.device, workspace)
+    if out is None:
+        out = torch.empty((N, N, CZ), dtype=dt, device=m.device)
+    st = lib().outer_product_mean_fwd(_dtype_code(m), S, N, CM, C, CZ, _ptr(m),
+                                      _ptr(ln_w), _ptr(ln_b), float(eps),
+                                      _ptr(w_a), _ptr(w_b), _ptr(w_o), _ptr(b_o),
+                                      _ptr(out), _ptr(workspace),
+                                      workspace.numel(), _stream(m.device))
+    _check("outer_product_mean_fwd", st)
     return out

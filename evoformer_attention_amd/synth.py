@@ -19,13 +19,16 @@ ZeRO cannot move"):
                     z [768,768,128], 128 channels, 38 random residues masked
   transition_768    LayerNorm + SwiGLU transition, z [768,768,128], hidden
                     width 4 x 128 = 512
+  opm_1024x768      outer product mean, m [1024,768,256] (MSA depth 1024 as
+                    in the pages' coevolution example, c_m = 8 x 32 as in
+                    msa_row_bf16), 32 channels, out [768,768,128]
 """
 import math
 import torch
 
 __all__ = ["WORKLOADS", "core_inputs", "module_inputs", "round_to",
            "rand_core", "rand_module", "rand_trimul", "trimul_inputs",
-           "rand_transition", "transition_inputs"]
+           "rand_transition", "transition_inputs", "rand_opm", "opm_inputs"]
 
 WORKLOADS = {
     "core_fp32_small": dict(kind="core", B=1, R=32, N=32, H=4, C=32,
@@ -41,6 +44,7 @@ WORKLOADS = {
     "trimul_out_768": dict(kind="trimul", N=768, CZ=128, C=128, dtype="bf16",
                            outgoing=True, mask="random5"),
     "transition_768": dict(kind="transition", N=768, CZ=128, HID=512, dtype="bf16"),
+    "opm_1024x768": dict(kind="opm", S=1024, N=768, CM=256, C=32, CZ=128, dtype="bf16"),
 }
 
 _TORCH_DT = {"fp32": torch.float32, "bf16": torch.bfloat16}
@@ -190,3 +194,32 @@ def transition_inputs(name, seed=0):
     w = WORKLOADS[name]
     assert w["kind"] == "transition"
     return rand_transition(w["N"], w["CZ"], w["HID"], w["dtype"], seed=seed)
+
+
+def rand_opm(S, N, CM, C, CZ, dtype, seed=0):
+    """Outer-product-mean inputs: m ~ N(0,1) [S,N,CM]; w_a, w_b [C, CM] ~
+    N(0, 1/CM); w_o [CZ, C*C] ~ N(0, S/C^2) (a mean of S products of
+    independent unit terms has size 1/sqrt(S), so the projected update is of
+    unit size, like b_o); LayerNorm weight 1 + N(0, 0.2^2), bias N(0,
+    0.2^2); b_o N(0, 0.5^2).  Draw order: m, w_a, w_b, w_o, ln_w, ln_b,
+    b_o."""
+    gen = torch.Generator().manual_seed(seed)
+
+    def draw(shape, std=1.0):
+        return round_to(torch.randn(shape, generator=gen) * std, dtype)
+
+    d = {"m": draw((S, N, CM))}
+    d["w_a"] = draw((C, CM), CM ** -0.5)
+    d["w_b"] = draw((C, CM), CM ** -0.5)
+    d["w_o"] = draw((CZ, C * C), S ** 0.5 / C)
+    d["ln_w"] = draw((CM,), 0.2) + 1
+    d["ln_b"] = draw((CM,), 0.2)
+    d["b_o"] = draw((CZ,), 0.5)
+    d["eps"] = 1e-5
+    return d
+
+
+def opm_inputs(name, seed=0):
+    w = WORKLOADS[name]
+    assert w["kind"] == "opm"
+    return rand_opm(w["S"], w["N"], w["CM"], w["C"], w["CZ"], w["dtype"], seed=seed)

@@ -380,6 +380,43 @@ evo_status_t pair_transition_fwd(evo_dtype_t dtype, int64_t N, int64_t CZ,
                                  const void* w_o, void* out, void* workspace,
                                  size_t workspace_bytes, void* stream);
 
+/*
+ * outer_product_mean_fwd -- the MSA-to-pair bridge ("Evoformer: the memory
+ * wall ZeRO cannot move", section "The three operations": the mean over all
+ * sequences of the outer product of MSA columns i and j).  The pages give no
+ * formula; this entry point computes
+ *   x = LN(m),  a = x . w_a^T,  b = x . w_b^T               (c channels)
+ *   o[i,j,c,d] = (1/S) sum_s a[s,i,c] b[s,j,d]
+ *   out[i,j]   = flatten(o[i,j]) . w_o^T + b_o              (d fastest)
+ * with fp32 accumulation; the product sum_s a b is rounded to dtype once
+ * before the output projection.
+ *
+ *   m          [S,N,CM] dtype (sequence, residue, channel); S >= 1, N >= 1,
+ *              S*N below 2^31; CM a multiple of 32, at most 256.
+ *   ln_w, ln_b [CM] dtype; ln_eps > 0 (population variance, fp32 statistics).
+ *   w_a, w_b   [C, CM] dtype ([out, in]); C a multiple of 32, at most 128.
+ *   w_o        [CZ, C*C] dtype; CZ a multiple of 32, at most 128.
+ *   b_o        [CZ] dtype, or null for no bias.
+ *   out        [N,N,CZ] dtype.
+ *   workspace  outer_product_mean_workspace_bytes(...) bytes, caller-owned:
+ *              the two projections [N*C, S] and the product [N*C, N*C]
+ *              (O(N^2 C^2); 1.2 GB in bf16 at N = 768, C = 32).
+ * Sizes outside these limits: EVO_ENOTSUP; non-positive sizes, null required
+ * pointers or a short workspace: EVO_EINVAL.  Pointers: device memory,
+ * 16-byte aligned.  Enqueued on `stream`.
+ */
+size_t outer_product_mean_workspace_bytes(evo_dtype_t dtype, int64_t S,
+                                          int64_t N, int64_t CM, int64_t C,
+                                          int64_t CZ);
+evo_status_t outer_product_mean_fwd(evo_dtype_t dtype, int64_t S, int64_t N,
+                                    int64_t CM, int64_t C, int64_t CZ,
+                                    const void* m, const void* ln_w,
+                                    const void* ln_b, float ln_eps,
+                                    const void* w_a, const void* w_b,
+                                    const void* w_o, const void* b_o,
+                                    void* out, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

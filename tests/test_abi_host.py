@@ -254,3 +254,34 @@ def test_trimul_and_transition_validation():
     targs[11] = FAKE
     targs[13] = 16
     assert L.pair_transition_fwd(*targs) == ops.EVO_EWORKSPACE
+
+
+def test_opm_validation():
+    w = L.outer_product_mean_workspace_bytes(1, 1024, 768, 256, 32, 128)
+    M = 768 * 32
+    assert w >= M * M * 2 + 2 * M * 1024 * 2  # the product and both projections
+    assert L.outer_product_mean_workspace_bytes(1, 1024, 768, 256, 48, 128) == 0  # C % 32
+    assert L.outer_product_mean_workspace_bytes(1, 1024, 768, 512, 32, 128) == 0  # CM > 256
+    assert L.outer_product_mean_workspace_bytes(1, 8, 2000, 64, 32, 128) == 0  # N*C too big
+    assert L.outer_product_mean_workspace_bytes(1, 0, 8, 64, 32, 128) == 0
+    args = [1, 16, 8, 64, 32, 64, FAKE, FAKE, FAKE, 1e-5, FAKE, FAKE, FAKE, None,
+            FAKE, FAKE, 1 << 30, None]
+    args[14] = None
+    assert L.outer_product_mean_fwd(*args) == ops.EVO_EINVAL and "'out' is NULL" in err()
+    args[14] = FAKE
+    args[16] = 64
+    assert L.outer_product_mean_fwd(*args) == ops.EVO_EWORKSPACE
+    args[16] = 1 << 30
+    args[9] = 0.0
+    assert L.outer_product_mean_fwd(*args) == ops.EVO_EINVAL and "ln_eps" in err()
+    args[9] = 1e-5
+    args[3] = 100
+    assert L.outer_product_mean_fwd(*args) == ops.EVO_ENOTSUP and "CM=100" in err()
+
+
+def test_opm_fault_injection(monkeypatch):
+    monkeypatch.setenv("EVO_FAULT_INJECT", "launch")
+    args = [1, 16, 8, 64, 32, 64, FAKE, FAKE, FAKE, 1e-5, FAKE, FAKE, FAKE, None,
+            FAKE, FAKE, 1 << 30, None]
+    assert L.outer_product_mean_fwd(*args) == ops.EVO_EHIP
+    assert "injected" in err()
