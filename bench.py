@@ -17,8 +17,8 @@ Prints one JSON line.  Options: --steps K --warmup W --gpus 1
 --write-traffic FETCH_CSV WRITE_CSV, and --module-train (a training step of
 the whole module instead: forward, then the backward with the LayerNorm,
 projection and output-projection gradients), --trimul (the triangular
-multiplicative update instead) and --transition (the fused LayerNorm + SwiGLU
-transition instead).
+multiplicative update instead), --transition (the fused LayerNorm + SwiGLU
+transition instead) and --opm (the outer product mean instead).
 """
 import argparse
 import hashlib
@@ -57,6 +57,10 @@ def parse():
     ap.add_argument("--transition", action="store_true",
                     help="time the fused LayerNorm + SwiGLU transition instead "
                          "(pair_transition_fwd, z [768,768,128], hidden 512)")
+    ap.add_argument("--opm", action="store_true",
+                    help="time the outer product mean instead "
+                         "(outer_product_mean_fwd, m [1024,768,256], 32 "
+                         "channels, out [768,768,128])")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU work: turn two rocprofv3 --pmc counter files "
                          "(FETCH_SIZE run, WRITE_SIZE run) of a --calibrate-copy "
@@ -385,8 +389,64 @@ def transition_bench(a):
     print(json.dumps(res), flush=True)
 
 
+def opm_bench(a):
+    """The outer product mean on opm_1024x768.  Prints one JSON line; the
+    roofline entry is the whole call (projections, the product on the matrix
+    cores, the output projection) against the dense bf16 matrix-core peak."""
+    import torch
+    from evoformer_attention_amd import metrics as M
+    from evoformer_attention_amd import ops, synth
+
+    w = dict(synth.WORKLOADS["opm_1024x768"])
+    S, N, CM, C, CZ = w["S"], w["N"], w["CM"], w["C"], w["CZ"]
+    d = synth.opm_inputs("opm_1024x768")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    g = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    ws = torch.empty(ops.outer_product_mean_workspace_bytes(g["m"].dtype, S, N, CM, C, CZ),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty((N, N, CZ), dtype=g["m"].dtype, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        return ops.outer_product_mean_fwd(g["m"], g["ln_w"], g["ln_b"], g["eps"], g["w_a"],
+                                          g["w_b"], g["w_o"], g["b_o"], out=out, workspace=ws)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(a.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / a.steps
+    tf = M.opm_flops(S, N, CM, C, CZ) / (ms * 1e-3) / 1e12
+    res = {
+        "metric": "Outer product mean TFLOP/s (bf16), N_seq=1024, N_res=768",
+        "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "opm_1024x768", "N_seq": S, "N_res": N, "c_m": CM,
+                   "c": C, "c_z": CZ},
+        "roofline": {"bound": "mfma", "kernel": "outer_product_mean_fwd (call)",
+                     "achieved": round(tf, 2), "peak": M.MI355X_BF16_DENSE_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf / M.MI355X_BF16_DENSE_TFLOPS, 4),
+                     "traffic": None},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     a = parse()
+    if a.opm:
+        if a.gpus != 1:
+            print("bench.py runs on one GPU only", file=sys.stderr)
+            sys.exit(2)
+        opm_bench(a)
+        return
     if a.transition:
         if a.gpus != 1:
             print("bench.py runs on one GPU only", file=sys.stderr)

@@ -101,6 +101,14 @@ def trimul_flops(N, CZ, C):
     return 2.0 * N * N * CZ * 2 * C + 2.0 * C * N ** 3 + 2.0 * N * N * C * CZ
 
 
+def opm_flops(S, N, CM, C, CZ):
+    """Counted flops of one outer product mean: the a and b projections (2 x C
+    outputs per sequence-residue position), the product of the [N*C, S] and
+    [S, N*C] operand matrices and the [CZ, C*C] output projection per pair."""
+    return (2.0 * S * N * CM * 2 * C + 2.0 * (N * C) ** 2 * S
+            + 2.0 * N * N * C * C * CZ)
+
+
 def transition_flops(N, CZ, HID):
     """Counted flops of the LayerNorm + SwiGLU transition: two [HID, CZ]
     projections and the [CZ, HID] output projection per position."""
