@@ -15,7 +15,8 @@
 //      B[(j, d)][s] with rows padded to the GEMM tile;
 //   2. the per-channel product kernel of the multiplicative update, with one
 //      channel: P = A . B^T, P[(i, c)][(j, d)] = sum_s a[s,i,c] b[s,j,d],
-//      a dense contraction over s on the matrix cores;
+//      a dense contraction over s on the matrix cores (rows padded to its
+//      256-row tile);
 //   3. opm_out: out[i, j] = W_o . P[(i, :)][(j, :)] / S + b_o.  For a
 //      residue i and 64 consecutive j a wave's B operand for c*C + d0 .. +31
 //      is one contiguous 1 KiB run of row i*C + c of P, loaded straight into

@@ -15,9 +15,11 @@
 //      channel-major with padded rows, A_c[i][k] and B_c[j][k] (row = line,
 //      column = place; incoming reads z transposed), zero where k is masked;
 //      a small kernel zeroes the padding columns k >= N;
-//   2. trimul_gemm: for every channel, T_c = A_c . B_c^T, a dense bf16
+//   2. trimul_gemm: for every channel, T_c = A_c . B_c^T, a dense
 //      contraction over k on the matrix cores (fp32 accumulation), 128 x 128
-//      output tiles, K staged through double-buffered LDS;
+//      output tiles, K staged through double-buffered LDS (a single large
+//      bf16 product, as in the outer product mean, uses pair_gemm_bf16:
+//      256 x 128 tiles, A straight into registers, B through LDS);
 //   3. trimul_out: out[p] = W_o . T[:, p] + b_o with T read channel-major,
 //      staged through LDS and read with transposing LDS reads.
 #include <algorithm>
@@ -29,7 +31,8 @@ namespace evo {
 namespace {
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
-constexpr int kTile = 128;  // GEMM output tile (rows and columns)
+constexpr int kTile = 128;  // fp32 GEMM output tile (rows and columns)
+constexpr int kRowPad = 256;  // operand rows are padded to a multiple of this
 
 template <typename T> struct MulCfg;
 // K columns per LDS stage; LDS row stride (elements)
@@ -180,6 +183,132 @@ __global__ void __launch_bounds__(256) trimul_gemm_kernel(MulGemmParams p) {
   }
 }
 
+// bf16 products: a workgroup of 4*WJ waves owns a 256 x 128*WJ tile (rows i
+// of A, rows j of B); wave (wi, wj) owns rows wi*64 .. +63 and columns
+// wj*128 .. +127 as 4 x 8 accumulator blocks.  Each wave's A rows are its
+// own, so its A operands come straight from global memory into registers
+// (16 rows x 64 contiguous bytes per load), one 64-wide stage ahead; only B
+// goes through double-buffered LDS.  Per 32-wide K step a wave issues 32
+// products against 8 LDS operand reads (a 64 x 64 wave tile with both
+// operands in LDS needs 8 reads for 16), and per 64-wide stage the
+// workgroup moves (256 + 128*WJ) x 128 bytes from L2.
+constexpr int kBigI = 256, kBigJ = 128;
+
+template <int WJ>
+__global__ void __launch_bounds__(256 * WJ) pair_gemm_bf16_kernel(MulGemmParams p) {
+  using T = bf16_t;
+  using Op = bf16x8;
+  constexpr int BK = 64, RS = 72;
+  constexpr int NT = 256 * WJ;                 // threads
+  constexpr int BROWS = kBigJ * WJ;            // B rows per tile
+  constexpr int CPT = BROWS * (BK / 8) / NT;   // 16-byte B chunks per thread per stage
+  __shared__ __attribute__((aligned(16))) T sB[2][BROWS * RS];
+
+  const int nti = p.Np / kBigI, ntj = p.Np / BROWS;
+  const int w = xcd_work_index(p.C * nti * ntj);
+  if (w < 0) return;
+  const int per_c = nti * ntj;
+  const int c = w / per_c, r0 = w - c * per_c;
+  constexpr int G = 4;  // row tiles per group of the work order
+  const int first = r0 / (G * ntj) * G;
+  const int h = min(G, nti - first);
+  const int r = r0 - first * ntj;
+  const int ti = first + r % h, tj = r / h;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, g = lane >> 4;
+  const int wi = wave & 3, wj = wave >> 2;
+  const int64_t cs = (int64_t)p.Np * p.Kp;
+  const T* A = static_cast<const T*>(p.a) + c * cs +
+               ((int64_t)ti * kBigI + wi * 64 + l16) * p.Kp + 8 * g;
+  const T* B = static_cast<const T*>(p.b) + c * cs + (int64_t)tj * BROWS * p.Kp;
+
+  u32x4 rb[CPT];
+  auto fetch_b = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int e = tid + NT * u, row = e >> 3, col = (e & 7) * 8;
+      rb[u] = *reinterpret_cast<const u32x4*>(B + (int64_t)row * p.Kp + k0 + col);
+    }
+  };
+  auto stage_b = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int e = tid + NT * u, row = e >> 3, col = (e & 7) * 8;
+      *reinterpret_cast<u32x4*>(sB[buf] + row * RS + col) = rb[u];
+    }
+  };
+  // A operands of one stage: [k step][row block]
+  Op an[2][4], ac[2][4];
+  auto fetch_a = [&](Op (&v)[2][4], int k0) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi)
+        v[ks][bi] = *reinterpret_cast<const Op*>(A + (int64_t)bi * 16 * p.Kp + k0 + ks * 32);
+  };
+
+  f32x4 acc[8][4];  // [column block bj][row block bi]
+#pragma unroll
+  for (int x = 0; x < 8; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nstage = p.Kp / BK;
+  fetch_b(0);
+  fetch_a(an, 0);
+  for (int st = 0; st < nstage; ++st) {
+    const int buf = st & 1;
+    stage_b(buf);
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi) ac[ks][bi] = an[ks][bi];
+    // next stage (the last one again at the end: in bounds, exact waits)
+    const int nk0 = min(st + 1, nstage - 1) * BK;
+    fetch_b(nk0);
+    fetch_a(an, nk0);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        Op bf[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+          bf[x] = *reinterpret_cast<const Op*>(
+              sB[buf] + (wj * kBigJ + (half * 4 + x) * 16 + l16) * RS + ks * 32 + 8 * g);
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+          for (int bi = 0; bi < 4; ++bi)
+            acc[half * 4 + x][bi] = mma32(bf[x], ac[ks][bi], acc[half * 4 + x][bi]);
+      }
+    }
+  }
+
+  // lane (l16, g) holds T[i = .. + bi*16 + l16][j = .. + bj*16 + 4g + r]
+  T* Tc = static_cast<T*>(p.t) + (int64_t)c * p.N * p.N;
+#pragma unroll
+  for (int bi = 0; bi < 4; ++bi) {
+    const int i = ti * kBigI + wi * 64 + bi * 16 + l16;
+    if (i >= p.N) continue;
+#pragma unroll
+    for (int bj = 0; bj < 8; ++bj) {
+      const int j0 = tj * BROWS + wj * kBigJ + bj * 16 + 4 * g;
+      T* dst = Tc + (int64_t)i * p.N + j0;
+      if (j0 + 3 < p.N && (p.N & 3) == 0) {
+        st4t<T>(dst, acc[bj][bi]);
+      } else {
+#pragma unroll
+        for (int r2 = 0; r2 < 4; ++r2)
+          if (j0 + r2 < p.N) dst[r2] = Tr<T>::from_f(acc[bj][bi][r2]);
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------ output projection
 struct MulOutParams {
   int C, CZ, npos, ntiles;
@@ -320,7 +449,7 @@ struct MulLayout {
 MulLayout mul_layout(int dtype, int64_t N, int64_t C) {
   const size_t es = dtype == 1 ? 2 : 4;
   MulLayout L;
-  L.Np = round_up(N, kTile);
+  L.Np = round_up(N, kRowPad);
   L.Kp = round_up(N, 64);
   const size_t ab = ((size_t)C * L.Np * L.Kp * es + 255) & ~size_t(255);
   L.a = 0;
@@ -343,9 +472,20 @@ hipError_t pair_gemm_t(int C, int M, int K, int Np, int Kp, T* A, T* B, T* Tm, h
   g.C = C; g.N = M; g.Np = Np; g.Kp = Kp;
   g.a = A; g.b = B; g.t = Tm;
   g.ntile = Np / kTile;
-  const int total = C * g.ntile * g.ntile;
-  const int grid = (total + kNumXcd - 1) / kNumXcd * kNumXcd;
-  hipLaunchKernelGGL(trimul_gemm_kernel<T>, dim3(grid), dim3(256), 0, s, g);
+  // bf16: the 256 x 128 kernel for one large product (24576^2 by K = 1024:
+  // 1.78 vs 1.93 ms), the 128 x 128 one for many small ones (128 products of
+  // 768^2 by 768: 206 vs 218 us)
+  if (sizeof(T) == 2 && C == 1) {
+    constexpr int WJ = 1;  // 256 x 256 tiles with 8 waves (WJ = 2) measured slower
+    const int total = C * (Np / kBigI) * (Np / (kBigJ * WJ));
+    const int grid = (total + kNumXcd - 1) / kNumXcd * kNumXcd;
+    if constexpr (sizeof(T) == 2)
+      hipLaunchKernelGGL(pair_gemm_bf16_kernel<WJ>, dim3(grid), dim3(256 * WJ), 0, s, g);
+  } else {
+    const int total = C * g.ntile * g.ntile;
+    const int grid = (total + kNumXcd - 1) / kNumXcd * kNumXcd;
+    hipLaunchKernelGGL(trimul_gemm_kernel<T>, dim3(grid), dim3(256), 0, s, g);
+  }
   return hipGetLastError();
 }
 
@@ -387,11 +527,11 @@ hipError_t launch_trimul(const TriMulArgs& a, hipStream_t s) {
   return a.dtype == 1 ? trimul_t<bf16_t>(a, s) : trimul_t<float>(a, s);
 }
 
-int pair_gemm_row_tile() { return kTile; }
+int pair_gemm_row_tile() { return kRowPad; }
 
 hipError_t launch_pair_gemm(int dtype, int C, int M, int K, int Np, int Kp, void* a, void* b,
                             void* t, hipStream_t s) {
-  if (Np % kTile != 0 || M > Np || K > Kp || Kp % MulCfg<float>::BK != 0 ||
+  if (Np % kRowPad != 0 || M > Np || K > Kp || Kp % MulCfg<float>::BK != 0 ||
       Kp % MulCfg<bf16_t>::BK != 0)
     return hipErrorInvalidValue;
   return dtype == 1 ? pair_gemm_t<bf16_t>(C, M, K, Np, Kp, static_cast<bf16_t*>(a),

@@ -38,7 +38,7 @@ def oracle_args(d):
                                          (64, 260, 128, 32, 128)])
 def test_opm_parity(dtype, S, N, CM, C, CZ):
     """Ragged S (not a multiple of the 64-wide stage, and S = 1), ragged N
-    (N*C spanning several 128-row product tiles and a tail; N above the 256
+    (N*C spanning several 256-row product tiles and a tail; N above the 256
     pairs of an output tile), every supported output width class."""
     log(f"case opm {dtype} S={S} N={N} CM={CM} C={C} CZ={CZ}")
     d = synth.rand_opm(S, N, CM, C, CZ, dtype, seed=S + N)

@@ -35,11 +35,12 @@ def oracle_args(d):
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("outgoing", [True, False])
 @pytest.mark.parametrize("N,CZ,C,mask", [(37, 64, 32, "random5"), (130, 128, 128, None),
-                                         (5, 32, 64, None), (200, 96, 96, "random5")])
+                                         (5, 32, 64, None), (200, 96, 96, "random5"),
+                                         (300, 64, 32, "random5")])
 def test_trimul_parity(dtype, outgoing, N, CZ, C, mask):
-    """Ragged N (several 128 x 128 output tiles and a tail, and K not a
-    multiple of the 64-wide stage), both orientations, with and without a
-    residue mask."""
+    """Ragged N (several output tiles and a tail: 256 x 128 in bf16, 128 x
+    128 in fp32; K not a multiple of the 64-wide stage), both orientations,
+    with and without a residue mask."""
     log(f"case trimul {dtype} N={N} CZ={CZ} C={C} outgoing={outgoing} mask={mask}")
     d = synth.rand_trimul(N, CZ, C, dtype, seed=N + C, mask=mask)
     got = gpu_trimul(d, outgoing)
