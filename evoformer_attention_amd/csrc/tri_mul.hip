@@ -330,12 +330,12 @@ template <> struct OutLds<float> { static constexpr int TS = 128 + 4; };
 // Persistent workgroups (4 waves) with W_o resident in LDS; per tile of 128
 // positions: T[:, tile] staged in LDS, then out^T = W_o . T for each wave's
 // 32 positions.
-template <typename T, int CB>  // CB = CZ / 16
+template <typename T, int CB, int KS>  // CB = CZ / 16, KS = C / 32
 __global__ void __launch_bounds__(256) trimul_out_kernel(MulOutParams p) {
   using Op = typename Tr<T>::Op;
   constexpr int TS = OutLds<T>::TS;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const int C = p.C, WS = C + 8;
+  constexpr int C = 32 * KS, WS = C + 8;
   T* sW = reinterpret_cast<T*>(smem);        // [CZ][C + 8]
   T* sT = sW + CB * 16 * WS;                 // bf16 [C][TS]; fp32 [kOutP][TS]
   const int tid = threadIdx.x, lane = tid & 63;
@@ -358,13 +358,18 @@ __global__ void __launch_bounds__(256) trimul_out_kernel(MulOutParams p) {
     }
   const T* Tg = static_cast<const T*>(p.t);
   const int ksteps = C / 32;
-  for (int tile = blockIdx.x; tile < p.ntiles; tile += gridDim.x) {
+  // T[:, p0 .. p0+127] of a tile: chunk e = tid + 256 u: channel e / CPR,
+  // positions 8*(e % CPR) (bf16; fp32 4).  The next tile's chunks are loaded
+  // into registers while the current tile is computed.
+  constexpr int E16 = 16 / sizeof(T);
+  constexpr int CPR = kOutP / E16;
+  constexpr int NU = C * CPR / 256;  // chunks per thread
+  u32x4 tr[NU];
+  auto fetch_t = [&](int tile) {
     const int p0 = tile * kOutP;
-    __syncthreads();  // previous tile's reads (and the weights) done
-    // stage T[:, p0 .. p0+127]: chunk e: channel e / (kOutP/8), positions 8*(e % 16)
-    constexpr int E16 = 16 / sizeof(T);
-    constexpr int CPR = kOutP / E16;
-    for (int e = tid; e < C * CPR; e += 256) {
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int e = tid + 256 * u;
       const int k = e / CPR, pc = (e % CPR) * E16;
       const int pos = p0 + pc;
       u32x4 v = u32x4{0, 0, 0, 0};
@@ -381,13 +386,26 @@ __global__ void __launch_bounds__(256) trimul_out_kernel(MulOutParams p) {
               v[q] = __float_as_uint(x);
           }
       }
+      tr[u] = v;
+    }
+  };
+  fetch_t(min((int)blockIdx.x, p.ntiles - 1));
+  for (int tile = blockIdx.x; tile < p.ntiles; tile += gridDim.x) {
+    const int p0 = tile * kOutP;
+    __syncthreads();  // previous tile's reads (and the weights) done
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int e = tid + 256 * u;
+      const int k = e / CPR, pc = (e % CPR) * E16;
       if constexpr (sizeof(T) == 2) {
-        *reinterpret_cast<u32x4*>(sT + k * TS + pc) = v;
+        *reinterpret_cast<u32x4*>(sT + k * TS + pc) = tr[u];
       } else {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) sT[(pc + q) * TS + k] = __uint_as_float(v[q]);
+        for (int q = 0; q < 4; ++q) sT[(pc + q) * TS + k] = __uint_as_float(tr[u][q]);
       }
     }
+    // the next tile (the last one again at the end: exact waits)
+    fetch_t(min(tile + (int)gridDim.x, p.ntiles - 1));
     __syncthreads();
     f32x4 acc[CB][2];
 #pragma unroll
@@ -430,16 +448,27 @@ __global__ void __launch_bounds__(256) trimul_out_kernel(MulOutParams p) {
   }
 }
 
-template <typename T, int CB>
-hipError_t launch_out(MulOutParams& o, hipStream_t s) {
+template <typename T, int CB, int KS>
+hipError_t launch_out_k(MulOutParams& o, hipStream_t s) {
   const size_t lds = (size_t)CB * 16 * (o.C + 8) * sizeof(T) +
                      (size_t)(sizeof(T) == 2 ? o.C : kOutP) * OutLds<T>::TS * sizeof(T);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&trimul_out_kernel<T, CB>),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&trimul_out_kernel<T, CB, KS>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const int grid = std::min(o.ntiles, 512);
-  hipLaunchKernelGGL((trimul_out_kernel<T, CB>), dim3(grid), dim3(256), lds, s, o);
+  hipLaunchKernelGGL((trimul_out_kernel<T, CB, KS>), dim3(grid), dim3(256), lds, s, o);
   return hipGetLastError();
+}
+
+template <typename T, int CB>
+hipError_t launch_out(MulOutParams& o, hipStream_t s) {
+  switch (o.C / 32) {
+    case 1: return launch_out_k<T, CB, 1>(o, s);
+    case 2: return launch_out_k<T, CB, 2>(o, s);
+    case 3: return launch_out_k<T, CB, 3>(o, s);
+    case 4: return launch_out_k<T, CB, 4>(o, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 struct MulLayout {

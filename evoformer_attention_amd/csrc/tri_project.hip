@@ -41,6 +41,7 @@ constexpr int PW = 32;              // positions per wave
 template <int KSTEPS> constexpr int waves_for() { return KSTEPS <= 4 ? 16 : 8; }
 constexpr int PAD = 8;              // LDS row padding (elements)
 constexpr size_t kLdsBudget = 150 * 1024;
+constexpr int OS = 24;               // operand mode: staging row stride (elements)
 
 struct GemmParams {
   int mode;        // 0 = project (LayerNorm + q,k,v,g,bias), 1 = out projection,
@@ -169,6 +170,9 @@ rowgemm_kernel(GemmParams p) {
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, g = lane >> 4;
+  // operand mode (bf16): per wave, one 32-position x 16-channel block staged
+  // row by position, read back channel by channel
+  T* sO = reinterpret_cast<T*>(sC + p.pass_cols) + (MUL ? wave * 32 * OS : 0);
 
   const T* X = static_cast<const T*>(p.x);
   // Rows of position `pi` as loaded: channels 32s + 8g .. +7 in nx[s].
@@ -281,6 +285,10 @@ rowgemm_kernel(GemmParams p) {
   // output matrix and column within it where this pass starts (passes start
   // at multiples of 32 columns, so never inside a block pair)
   const int m0 = p.mode == 0 ? min(p.col0 / p.HC, 4) : p.mode == 2 ? p.col0 / p.HC : 0;
+  // operand mode: 8 consecutive positions from a multiple of 8 are 8
+  // consecutive, 16-byte aligned places of one line
+  const bool vec_ok = MUL && p.s_place == 1 && p.P % 8 == 0 && p.s_ch % 8 == 0 &&
+                      p.s_line % 8 == 0;
   const int cbase0 = p.col0 - m0 * p.HC;
   for (int tile = blockIdx.x; tile < p.ntiles; tile += gridDim.x) {
     if (!PREFETCH) load_rows(nx, tile);
@@ -379,11 +387,60 @@ rowgemm_kernel(GemmParams p) {
           cbase += 32;
           continue;
         }
+        if constexpr (MUL && sizeof(T) == 2) {
+          // Through the wave's staging tile: lane (l16, g) then holds channel
+          // cbase + l16 of the 8 consecutive positions 8g .. 8g+7 of the
+          // wave's 32, stored as one 16-byte run where they are consecutive
+          // places of one line.
+#pragma unroll
+          for (int pb = 0; pb < 2; ++pb) {
+            uint2 u;
+            u.x = uint32_t(Tr<T>::from_f(acc[0][pb][0])) | (uint32_t(Tr<T>::from_f(acc[0][pb][1])) << 16);
+            u.y = uint32_t(Tr<T>::from_f(acc[0][pb][2])) | (uint32_t(Tr<T>::from_f(acc[0][pb][3])) << 16);
+            *reinterpret_cast<uint2*>(sO + (pb * 16 + l16) * OS + 4 * g) = u;
+          }
+          __builtin_amdgcn_wave_barrier();
+          const T* q0 = sO + (8 * g + (l16 >> 2)) * OS + 4 * (l16 & 3);
+          u32x4 v = __builtin_bit_cast(u32x4, lds_read_tr_op(q0, q0 + 4 * OS));
+          const int c = cbase + l16;
+          const uint32_t pi0 = ((uint32_t)tile * WAVES + wave) * PW + 8 * g;
+          if (c < p.HC && pi0 < (uint32_t)p.npos) {
+            uint32_t line = pi0 / (uint32_t)p.P, place = pi0 - line * (uint32_t)p.P;
+            T* base = out + (int64_t)c * p.s_ch;
+            if (vec_ok && pi0 + 8 <= (uint32_t)p.npos) {
+              if (p.mask) {  // 8 keep flags, 8-byte aligned: zero the dead places
+                const uint2 mb = *reinterpret_cast<const uint2*>(p.mask + place);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  const uint32_t w = (i < 2 ? mb.x : mb.y) >> (16 * (i & 1));
+                  v[i] &= ((w & 0xffu) ? 0xffffu : 0u) | ((w & 0xff00u) ? 0xffff0000u : 0u);
+                }
+              }
+              *reinterpret_cast<u32x4*>(base + (int64_t)line * p.s_line + place) = v;
+            } else {
+              // ragged: element by element, walking the places of the line
+#pragma nounroll
+              for (int j = 0; j < 8; ++j) {
+                if (pi0 + j >= (uint32_t)p.npos) break;
+                const bool dead = p.mask && p.mask[place] == 0;
+                const uint32_t word = j < 2 ? v[0] : j < 4 ? v[1] : j < 6 ? v[2] : v[3];
+                const uint32_t bits = (word >> (16 * (j & 1))) & 0xffffu;
+                base[(int64_t)line * p.s_line + (int64_t)place * p.s_place] =
+                    dead ? T(0) : __builtin_bit_cast(T, (uint16_t)bits);
+                if (++place == (uint32_t)p.P) { place = 0; ++line; }
+              }
+            }
+          }
+          __builtin_amdgcn_wave_barrier();
+          cb += 1;
+          cbase += 16;
+          continue;
+        }
 #pragma unroll
         for (int pb = 0; pb < 2; ++pb) {
           if (!live[pb]) continue;
           const int c = cbase + 4 * g;
-          if constexpr (MUL) {
+          if constexpr (MUL && sizeof(T) != 2) {
             // element (line, place) of channel c+i
             const uint32_t line = pidx[pb] / (uint32_t)p.P, place = pidx[pb] - line * (uint32_t)p.P;
             const bool dead = p.mask && p.mask[place] == 0;
@@ -433,13 +490,15 @@ template <typename T>
 hipError_t launch_gemm(GemmParams& p, hipStream_t s) {
   // LDS per output column: its weight row and its constant
   const size_t row_bytes = (size_t)(p.K + PAD) * sizeof(T) + sizeof(float);
-  int per_pass = (int)(kLdsBudget / row_bytes) / 32 * 32;  // whole block pairs
+  // operand mode: the per-wave staging tiles (at most 16 waves)
+  const size_t stage = p.mode == 2 ? (size_t)16 * 32 * OS * sizeof(T) : 0;
+  int per_pass = (int)((kLdsBudget - stage) / row_bytes) / 32 * 32;  // whole block pairs
   const int ncols_pad = (p.ncols + 15) / 16 * 16;
   per_pass = std::min(per_pass, ncols_pad);
   for (int c0 = 0; c0 < p.ncols; c0 += per_pass) {
     p.col0 = c0;
     p.pass_cols = std::min(per_pass, ncols_pad - c0);
-    const size_t lds = (size_t)p.pass_cols * row_bytes;
+    const size_t lds = (size_t)p.pass_cols * row_bytes + stage;
     hipError_t e;
     switch (p.K / 32) {
       case 1: e = launch_pass<T, 1>(p, lds, s); break;
