@@ -410,7 +410,13 @@ attn_fwd_kernel(FwdParams p) {
         }
       }
       f32x4 s[ROWS][2][2];  // [rr][qb][kb]
+      // The products run at raised wave priority, so that a wave reaching
+      // them issues them ahead of the other waves' softmax arithmetic and
+      // the matrix core is fed sooner (0.540 -> 0.527 ms at N = 768; the
+      // same in the backward kernels measured 1% slower).
+      __builtin_amdgcn_s_setprio(1);
       EVO_FWD_QK(hf);
+      __builtin_amdgcn_s_setprio(0);
 
       // p = exp2(s*log2e - m), rounded to the operand type at once: P^T is
       // kept as matrix-core operands and the row sums are taken over
@@ -490,11 +496,13 @@ attn_fwd_kernel(FwdParams p) {
             vf[cb] = ld8(sV[buf][rr] + (cb * 16 + l16) * VST + hf * 32 + 8 * g);
           }
         }
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
           for (int cb = 0; cb < 2; ++cb)
             o[rr][qb][cb] = mma32(vf[cb], pf[rr][qb], o[rr][qb][cb]);
+        __builtin_amdgcn_s_setprio(0);
       }
     }
     // next tile's bias operands (the logit registers are free again); bf16
