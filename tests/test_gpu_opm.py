@@ -35,11 +35,12 @@ def oracle_args(d):
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("S,N,CM,C,CZ", [(37, 45, 64, 32, 64), (130, 9, 256, 32, 128),
                                          (1, 70, 32, 64, 32), (200, 130, 96, 32, 96),
-                                         (64, 260, 128, 32, 128)])
+                                         (64, 260, 128, 32, 128), (33, 20, 256, 128, 128)])
 def test_opm_parity(dtype, S, N, CM, C, CZ):
     """Ragged S (not a multiple of the 64-wide stage, and S = 1), ragged N
     (N*C spanning several 256-row product tiles and a tail; N above the 256
-    pairs of an output tile), every supported output width class."""
+    pairs of an output tile), every supported output width class, and the
+    widest supported channels (c_m = 256, c = 128, c_z = 128)."""
     log(f"case opm {dtype} S={S} N={N} CM={CM} C={C} CZ={CZ}")
     d = synth.rand_opm(S, N, CM, C, CZ, dtype, seed=S + N)
     got = gpu_opm(d)

@@ -25,10 +25,12 @@ def oracle_out(d, z=None):
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
-@pytest.mark.parametrize("N,CZ,HID", [(37, 64, 256), (5, 32, 64), (70, 128, 512), (16, 96, 192)])
+@pytest.mark.parametrize("N,CZ,HID", [(37, 64, 256), (5, 32, 64), (70, 128, 512), (16, 96, 192),
+                                      (9, 128, 4096)])
 def test_transition_parity(dtype, N, CZ, HID):
     """Ragged position counts (tails of the 256-position tiles), every
-    supported c_z, hidden widths of 1 to 8 chunks of 64."""
+    supported c_z, hidden widths of 1 to 8 chunks of 64, and the widest
+    supported hidden layer (4096)."""
     log(f"case transition {dtype} N={N} CZ={CZ} HID={HID}")
     d = synth.rand_transition(N, CZ, HID, dtype, seed=N + HID)
     compare("out", np64(gpu_transition(d)), oracle_out(d), dtype)
