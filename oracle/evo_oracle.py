@@ -47,7 +47,7 @@ __all__ = [
     "tri_module_forward", "tri_module_lines", "layer_norm_backward",
     "tri_out_project_backward", "tri_project_backward",
     "tri_module_backward", "tri_mul_forward", "tri_mul_entries",
-    "transition_forward", "outer_product_mean", "outer_product_mean_pairs",
+    "transition_forward", "outer_product_mean", "transition_backward", "outer_product_mean_pairs",
 ]
 
 
@@ -539,6 +539,35 @@ def transition_forward(z, ln_w, ln_b, eps, w_a, w_b, w_o):
     u = x @ w_a.T
     h = u * sigmoid(u) * (x @ w_b.T)
     return h @ w_o.T
+
+
+def transition_backward(z, ln_w, ln_b, eps, w_a, w_b, w_o, dout):
+    """Gradients of transition_forward (training, as EvoFusion's scope of
+    LayerNorm, projections and SwiGLU implies): the chain rule of
+        x = LN(z), u = x w_a^T, v = x w_b^T, h = silu(u) v, out = h w_o^T
+    with silu(u) = u sigmoid(u), silu'(u) = sigmoid(u) (1 + u (1 - sigmoid(u))):
+        dh = dout w_o,  du = dh v silu'(u),  dv = dh silu(u),
+        dx = du w_a + dv w_b,  dz = LayerNorm backward of dx,
+        dw_o = sum_p dout^T h,  dw_a = sum_p du^T x,  dw_b = sum_p dv^T x.
+    z, dout [..., CZ].  Returns a dict of dz (like z), dln_w, dln_b [CZ],
+    dw_a, dw_b [HID, CZ] and dw_o [CZ, HID]."""
+    z = np.asarray(z, np.float64)
+    dout = np.asarray(dout, np.float64)
+    CZ = z.shape[-1]
+    x = layer_norm(z, ln_w, ln_b, eps).reshape(-1, CZ)
+    dy = dout.reshape(-1, CZ)
+    u = x @ w_a.T
+    v = x @ w_b.T
+    sg = sigmoid(u)
+    silu = u * sg
+    h = silu * v
+    dh = dy @ w_o
+    dv = dh * silu
+    du = dh * v * sg * (1.0 + u * (1.0 - sg))
+    dx = du @ w_a + dv @ w_b
+    dz, dln_w, dln_b = layer_norm_backward(z.reshape(-1, CZ), ln_w, eps, dx)
+    return dict(dz=dz.reshape(z.shape), dln_w=dln_w, dln_b=dln_b,
+                dw_a=du.T @ x, dw_b=dv.T @ x, dw_o=dy.T @ h)
 
 
 # ----------------------------------------------------------------------------

@@ -832,6 +832,86 @@ def test_mutant_transition_relu_gate_is_caught(monkeypatch):
         test_transition_matches_torch()
 
 
+# ----------------------------------------------- transition backward
+
+def _transition_loss(d, dout):
+    return float((O.transition_forward(**d) * dout).sum())
+
+
+def test_transition_backward_matches_torch_autograd():
+    """torch.autograd (fp64) of F.layer_norm, F.linear and F.silu: every
+    gradient (input, LayerNorm weight and bias, the three weights)."""
+    d = transition_case(90, N=4, CZ=8, HID=12)
+    dout = np.random.default_rng(91).standard_normal((4, 4, 8))
+    t = {k: torch.tensor(v, requires_grad=True) for k, v in d.items() if isinstance(v, np.ndarray)}
+    x = F.layer_norm(t["z"], (8,), t["ln_w"], t["ln_b"], d["eps"])
+    out = F.linear(F.silu(F.linear(x, t["w_a"])) * F.linear(x, t["w_b"]), t["w_o"])
+    (out * torch.tensor(dout)).sum().backward()
+    got = O.transition_backward(dout=dout, **d)
+    for k_t, k_o in (("z", "dz"), ("ln_w", "dln_w"), ("ln_b", "dln_b"), ("w_a", "dw_a"),
+                     ("w_b", "dw_b"), ("w_o", "dw_o")):
+        np.testing.assert_allclose(got[k_o], t[k_t].grad.numpy(), rtol=1e-10, atol=1e-12,
+                                   err_msg=k_o)
+
+
+@pytest.mark.parametrize("which", ["z", "ln_w", "ln_b", "w_a", "w_b", "w_o"])
+def test_transition_backward_matches_central_finite_differences(which):
+    """The definition of the derivative: central differences of
+    sum(out * dout) on a tiny case, every element of the chosen input."""
+    d = transition_case(92, N=2, CZ=4, HID=6)
+    dout = np.random.default_rng(93).standard_normal((2, 2, 4))
+    got = O.transition_backward(dout=dout, **d)["d" + which]
+    h = 1e-6
+    fd = np.zeros_like(d[which])
+    for idx in np.ndindex(d[which].shape):
+        e = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in d.items()}
+        e[which][idx] += h
+        fp = _transition_loss(e, dout)
+        e[which][idx] -= 2 * h
+        fm = _transition_loss(e, dout)
+        fd[idx] = (fp - fm) / (2 * h)
+    np.testing.assert_allclose(got, fd, rtol=1e-6, atol=1e-8)
+
+
+def test_transition_backward_closed_forms():
+    """The LayerNorm ignores a shift of a position's channels, so dz sums to
+    zero over channels; with w_b = 0 the hidden layer is zero, so dw_o = 0
+    and dw_a = 0 (silu(u) * 0 has no gradient through u)."""
+    d = transition_case(94)
+    dout = np.random.default_rng(95).standard_normal((5, 5, 8))
+    g = O.transition_backward(dout=dout, **d)
+    np.testing.assert_allclose(g["dz"].sum(axis=-1), 0.0, atol=1e-12)
+    e = dict(d, w_b=np.zeros_like(d["w_b"]))
+    g0 = O.transition_backward(dout=dout, **e)
+    np.testing.assert_allclose(g0["dw_o"], 0.0, atol=1e-14)
+    np.testing.assert_allclose(g0["dw_a"], 0.0, atol=1e-14)
+    assert np.abs(g0["dw_b"]).max() > 1e-3
+
+
+def test_transition_backward_planted_mistake_fails():
+    """silu' taken as sigmoid(u) alone (the u sigmoid' term dropped), planted
+    in a copy of the oracle, must miss the finite differences."""
+    d = transition_case(96, N=2, CZ=4, HID=6)
+    dout = np.random.default_rng(97).standard_normal((2, 2, 4))
+    x = O.layer_norm(d["z"], d["ln_w"], d["ln_b"], d["eps"]).reshape(-1, 4)
+    u = x @ d["w_a"].T
+    v = x @ d["w_b"].T
+    dh = dout.reshape(-1, 4) @ d["w_o"]
+    du_wrong = dh * v * O.sigmoid(u)
+    dw_a_wrong = du_wrong.T @ x
+    h = 1e-6
+    fd = np.zeros_like(d["w_a"])
+    for idx in np.ndindex(d["w_a"].shape):
+        e = dict(d, w_a=d["w_a"].copy())
+        e["w_a"][idx] += h
+        fp = _transition_loss(e, dout)
+        e["w_a"][idx] -= 2 * h
+        fd[idx] = (fp - _transition_loss(e, dout)) / (2 * h)
+    assert np.abs(dw_a_wrong - fd).max() > 1e-3
+    np.testing.assert_allclose(O.transition_backward(dout=dout, **d)["dw_a"], fd, rtol=1e-6,
+                               atol=1e-8)
+
+
 # ------------------------------------------------------- outer product mean
 
 def opm_case(seed, S=4, N=5, CM=6, C=3, CZ=7):
