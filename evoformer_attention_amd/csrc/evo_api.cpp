@@ -793,4 +793,59 @@ evo_status_t outer_product_mean_fwd(evo_dtype_t dtype, int64_t S, int64_t N, int
   }
 }
 
+static evo_status_t check_transition_bwd_sizes(evo_dtype_t dtype, int64_t N, int64_t CZ,
+                                               int64_t HID) {
+  evo_status_t st = check_transition_sizes(dtype, N, CZ, HID);
+  if (st != EVO_OK) return st;
+  if (HID % 128 != 0)
+    return fail(EVO_ENOTSUP, "HID=%lld must be a multiple of 128 for the backward",
+                (long long)HID);
+  return EVO_OK;
+}
+
+size_t pair_transition_bwd_workspace_bytes(evo_dtype_t dtype, int64_t N, int64_t CZ,
+                                           int64_t HID) {
+  const std::string saved = g_last_error;
+  const evo_status_t st = check_transition_bwd_sizes(dtype, N, CZ, HID);
+  g_last_error = saved;
+  if (st != EVO_OK) return 0;
+  return evo::transition_bwd_workspace((int)dtype, N * N, CZ, HID);
+}
+
+evo_status_t pair_transition_bwd(evo_dtype_t dtype, int64_t N, int64_t CZ, int64_t HID,
+                                 const void* z, const void* ln_w, const void* ln_b,
+                                 float ln_eps, const void* w_a, const void* w_b,
+                                 const void* w_o, const void* dout, void* dz, float* dln_w,
+                                 float* dln_b, float* dw_a, float* dw_b, float* dw_o,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    evo_status_t st = check_transition_bwd_sizes(dtype, N, CZ, HID);
+    if (st != EVO_OK) return st;
+    if (!(ln_eps > 0.f)) return fail(EVO_EINVAL, "ln_eps must be > 0");
+    REQUIRE_PTR(z);
+    REQUIRE_PTR(ln_w);
+    REQUIRE_PTR(ln_b);
+    REQUIRE_PTR(w_a);
+    REQUIRE_PTR(w_b);
+    REQUIRE_PTR(w_o);
+    REQUIRE_PTR(dout);
+    REQUIRE_PTR(dz);
+    REQUIRE_PTR(dln_w);
+    REQUIRE_PTR(dln_b);
+    REQUIRE_PTR(dw_a);
+    REQUIRE_PTR(dw_b);
+    REQUIRE_PTR(dw_o);
+    st = check_workspace("pair_transition_bwd", workspace, workspace_bytes,
+                         evo::transition_bwd_workspace((int)dtype, N * N, CZ, HID));
+    if (st != EVO_OK) return st;
+    if (fault_injected())
+      return fail(EVO_EHIP, "pair_transition_bwd: injected launch failure");
+    evo::TransitionBwdArgs a{(int)dtype, N * N, CZ, HID, z, ln_w, ln_b, ln_eps, w_a, w_b,
+                             w_o, dout, dz, dln_w, dln_b, dw_a, dw_b, dw_o, workspace};
+    return from_hip(evo::launch_transition_bwd(a, (hipStream_t)stream), "pair_transition_bwd");
+  } catch (...) {
+    return fail(EVO_EINTERNAL, "pair_transition_bwd: internal error");
+  }
+}
+
 }  // extern "C"

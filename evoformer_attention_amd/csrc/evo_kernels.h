@@ -204,6 +204,52 @@ struct OpmArgs {
 };
 size_t opm_workspace(int dtype, int64_t S, int64_t N, int64_t C);
 hipError_t launch_opm(const OpmArgs& a, hipStream_t s);
+// Weight gradients against plain position rows: for the nseg (1 or 4)
+// segments A_s [npos][128] and B [npos][ncols] (LayerNorm-normalised from z
+// when b_ln),  M_s = A_s^T B  and the column sums of A_s, reduced in a fixed
+// order; dw_s [128][ncols] = M_s, or gamma * M_s + beta * colsum (b_ln), with
+// M and the column sums also kept in mred [nseg*128][ncols], cred
+// [nseg*128] (b_ln).
+struct SegWGradArgs {
+  int dtype;
+  int64_t npos;
+  int nseg;
+  const void* aseg[4];
+  const void* b;
+  int ncols, b_ln;
+  const void* ln_w;
+  const void* ln_b;
+  float eps;
+  float* dw[4];
+  float* mred;
+  float* cred;
+  void* workspace;  // seg_wgrad_workspace bytes
+};
+size_t seg_wgrad_workspace(int64_t npos, int64_t ncols);
+hipError_t launch_seg_wgrad(const SegWGradArgs& a, hipStream_t s);
+// Backward of the transition: dz [npos][CZ] (dtype); dln_w, dln_b [CZ],
+// dw_a, dw_b [HID][CZ], dw_o [CZ][HID] (fp32).  HID a multiple of 128.
+struct TransitionBwdArgs {
+  int dtype;
+  int64_t npos, CZ, HID;
+  const void* z;
+  const void* ln_w;
+  const void* ln_b;
+  float eps;
+  const void* w_a;
+  const void* w_b;
+  const void* w_o;
+  const void* dout;
+  void* dz;
+  float* dln_w;
+  float* dln_b;
+  float* dw_a;
+  float* dw_b;
+  float* dw_o;
+  void* workspace;  // transition_bwd_workspace bytes
+};
+size_t transition_bwd_workspace(int dtype, int64_t npos, int64_t CZ, int64_t HID);
+hipError_t launch_transition_bwd(const TransitionBwdArgs& a, hipStream_t s);
 size_t transition_workspace(int dtype, int64_t CZ, int64_t HID);
 hipError_t launch_transition(const TransitionArgs& a, hipStream_t s);
 hipError_t launch_out_project_bwd(const OutProjectBwdArgs& a, hipStream_t s);

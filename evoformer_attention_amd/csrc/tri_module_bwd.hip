@@ -469,10 +469,9 @@ constexpr size_t wgrad_lds() {
 // B = xhat); NSEG = 1: the output projection (A = dout, B = o).  Wave w owns
 // segment w / (8/NSEG) and the column blocks w % (8/NSEG) + (8/NSEG) i,
 // i < NSEG; with NSEG = 4 also the pair-bias rows of column block w.
-template <typename T, int NSEG>
+template <typename T, int NSEG, bool BIAS = NSEG == 4>
 __global__ void __launch_bounds__(512) wgrad_kernel(WGradParams p) {
   using Op = typename Tr<T>::Op;
-  constexpr bool BIAS = NSEG == 4;
   constexpr int WPS = 8 / NSEG;     // waves (and column groups) per segment
   constexpr int TPS = 512 / NSEG;   // staging threads per segment
   constexpr int NB = WL<T>::NBUF;
@@ -932,15 +931,20 @@ constexpr int kChunks = 256;
 template <typename T>
 hipError_t launch_wgrad(WGradParams& p, hipStream_t s) {
   const size_t lds = p.nseg == 4 ? wgrad_lds<T, 4>() : wgrad_lds<T, 1>();
-  const void* fn = p.nseg == 4 ? reinterpret_cast<const void*>(&wgrad_kernel<T, 4>)
-                               : reinterpret_cast<const void*>(&wgrad_kernel<T, 1>);
-  if ((p.nseg == 4) != (p.dbias != nullptr)) return hipErrorInvalidValue;
+  // four segments with or without the pair-bias rows; one segment without
+  const bool bias = p.dbias != nullptr;
+  if (bias && p.nseg != 4) return hipErrorInvalidValue;
+  const void* fn = p.nseg != 4 ? reinterpret_cast<const void*>(&wgrad_kernel<T, 1>)
+                   : bias      ? reinterpret_cast<const void*>(&wgrad_kernel<T, 4, true>)
+                               : reinterpret_cast<const void*>(&wgrad_kernel<T, 4, false>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  if (p.nseg == 4)
-    hipLaunchKernelGGL((wgrad_kernel<T, 4>), dim3(p.nchunks), dim3(512), lds, s, p);
-  else
+  if (p.nseg != 4)
     hipLaunchKernelGGL((wgrad_kernel<T, 1>), dim3(p.nchunks), dim3(512), lds, s, p);
+  else if (bias)
+    hipLaunchKernelGGL((wgrad_kernel<T, 4, true>), dim3(p.nchunks), dim3(512), lds, s, p);
+  else
+    hipLaunchKernelGGL((wgrad_kernel<T, 4, false>), dim3(p.nchunks), dim3(512), lds, s, p);
   return hipGetLastError();
 }
 
@@ -1075,7 +1079,58 @@ hipError_t project_bwd_t(const ProjectBwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+struct SegLayout {
+  size_t part, cpart, part2, cpart2, total;
+};
+SegLayout seg_layout(int64_t npos, int64_t ncols) {
+  int nc, cp;
+  chunking(npos, kChunks, nc, cp);
+  const int ng = (nc + kGroup - 1) / kGroup;
+  SegLayout L;
+  L.part = 0;
+  L.cpart = align256((size_t)nc * 512 * ncols * 4);
+  L.part2 = L.cpart + align256((size_t)nc * 512 * 4);
+  L.cpart2 = L.part2 + align256((size_t)ng * 512 * ncols * 4);
+  L.total = L.cpart2 + align256((size_t)ng * 512 * 4);
+  return L;
+}
+
+template <typename T>
+hipError_t seg_wgrad_t(const SegWGradArgs& a, hipStream_t s) {
+  const SegLayout L = seg_layout(a.npos, a.ncols);
+  char* ws = static_cast<char*>(a.workspace);
+  WGradParams w{};
+  w.N = 0; w.ending = 0; w.npos = (int)a.npos;  // plain rows: no z-row mapping
+  w.nseg = a.nseg; w.a_w = 128; w.a_zrow = 0;
+  for (int i = 0; i < a.nseg; ++i) w.aseg[i] = a.aseg[i];
+  w.dbias = nullptr; w.H = 0;
+  w.b_w = a.ncols; w.b_zrow = 0; w.b_ln = a.b_ln; w.b = a.b; w.eps = a.eps;
+  w.rows_pad = a.nseg * 128;
+  chunking(a.npos, kChunks, w.nchunks, w.chunk_pos);
+  w.part = reinterpret_cast<float*>(ws + L.part);
+  w.cpart = reinterpret_cast<float*>(ws + L.cpart);
+  hipError_t e = launch_wgrad<T>(w, s);
+  if (e != hipSuccess) return e;
+  FinishParams f{};
+  f.nchunks = w.nchunks; f.rows_pad = w.rows_pad; f.ncols = a.ncols;
+  f.nseg = a.nseg; f.a_w = 128; f.H = 0; f.has_bias = 0;
+  f.part = w.part; f.cpart = w.cpart;
+  f.ln = a.b_ln; f.ln_w = a.ln_w; f.ln_b = a.ln_b;
+  for (int i = 0; i < a.nseg; ++i) f.dw[i] = a.dw[i];
+  f.mred = a.mred; f.cred = a.cred;
+  return launch_finish<T>(f, reinterpret_cast<float*>(ws + L.part2),
+                          reinterpret_cast<float*>(ws + L.cpart2), s);
+}
+
 }  // namespace
+
+size_t seg_wgrad_workspace(int64_t npos, int64_t ncols) { return seg_layout(npos, ncols).total; }
+
+hipError_t launch_seg_wgrad(const SegWGradArgs& a, hipStream_t s) {
+  if ((a.nseg != 1 && a.nseg != 4) || a.ncols > 128 || a.ncols % 16 != 0)
+    return hipErrorInvalidValue;
+  return a.dtype == 1 ? seg_wgrad_t<bf16_t>(a, s) : seg_wgrad_t<float>(a, s);
+}
 
 size_t proj_bwd_workspace(int64_t N, int64_t CZ, int64_t H) {
   return part_layout(N, CZ, H).total;

@@ -22,6 +22,7 @@ __all__ = ["EvoAttnError", "lib", "evo_abi_version", "evo_attn_fwd",
            "tri_mul_workspace_bytes", "tri_mul_fwd", "pair_transition_fwd",
            "pair_transition_workspace_bytes",
            "outer_product_mean_workspace_bytes", "outer_product_mean_fwd",
+           "pair_transition_bwd_workspace_bytes", "pair_transition_bwd",
            "LIB_PATH", "EXPORTS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
@@ -78,6 +79,9 @@ EXPORTS = {
                                  _P, _P, _P, _SZ, _P]),
     "outer_product_mean_workspace_bytes": (_SZ, [_I, _I64, _I64, _I64, _I64,
                                                  _I64]),
+    "pair_transition_bwd_workspace_bytes": (_SZ, [_I, _I64, _I64, _I64]),
+    "pair_transition_bwd": (_I, [_I, _I64, _I64, _I64, _P, _P, _P, _F, _P, _P, _P,
+                                 _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "outer_product_mean_fwd": (_I, [_I, _I64, _I64, _I64, _I64, _I64, _P, _P,
                                     _P, _F, _P, _P, _P, _P, _P, _P, _SZ, _P]),
 }
@@ -489,3 +493,36 @@ def outer_product_mean_fwd(m, ln_w, ln_b, eps, w_a, w_b, w_o, b_o, out=None,
                                       workspace.numel(), _stream(m.device))
     _check("outer_product_mean_fwd", st)
     return out
+
+
+def pair_transition_bwd_workspace_bytes(dtype, N, CZ, HID):
+    code = EVO_BF16 if dtype == torch.bfloat16 else EVO_FP32
+    return lib().pair_transition_bwd_workspace_bytes(code, N, CZ, HID)
+
+
+def pair_transition_bwd(z, ln_w, ln_b, eps, w_a, w_b, w_o, dout, workspace=None):
+    """Backward of pair_transition_fwd -> dict of dz (dtype) and the fp32
+    parameter gradients dln_w, dln_b, dw_a, dw_b, dw_o."""
+    _dev_tensor("z", z)
+    N, _, CZ = z.shape
+    dt = z.dtype
+    for name, t in (("ln_w", ln_w), ("ln_b", ln_b), ("w_a", w_a), ("w_b", w_b),
+                    ("w_o", w_o)):
+        _dev_tensor(name, t, dt)
+    _dev_tensor("dout", dout, dt, (N, N, CZ))
+    HID = w_a.shape[0]
+    workspace = _workspace(pair_transition_bwd_workspace_bytes(dt, N, CZ, HID),
+                           z.device, workspace)
+    res = {"dz": torch.empty_like(z)}
+    for k, shape in (("dln_w", (CZ,)), ("dln_b", (CZ,)), ("dw_a", (HID, CZ)),
+                     ("dw_b", (HID, CZ)), ("dw_o", (CZ, HID))):
+        res[k] = torch.empty(shape, dtype=torch.float32, device=z.device)
+    st = lib().pair_transition_bwd(_dtype_code(z), N, CZ, HID, _ptr(z), _ptr(ln_w),
+                                   _ptr(ln_b), float(eps), _ptr(w_a), _ptr(w_b),
+                                   _ptr(w_o), _ptr(dout), _ptr(res["dz"]),
+                                   _ptr(res["dln_w"]), _ptr(res["dln_b"]),
+                                   _ptr(res["dw_a"]), _ptr(res["dw_b"]),
+                                   _ptr(res["dw_o"]), _ptr(workspace),
+                                   workspace.numel(), _stream(z.device))
+    _check("pair_transition_bwd", st)
+    return res

@@ -171,10 +171,11 @@ def trimul_inputs(name, seed=0):
     return rand_trimul(w["N"], w["CZ"], w["C"], w["dtype"], seed=seed, mask=w["mask"])
 
 
-def rand_transition(N, CZ, HID, dtype, seed=0):
+def rand_transition(N, CZ, HID, dtype, seed=0, dout=False):
     """Transition inputs: z ~ N(0,1) [N,N,CZ]; w_a, w_b [HID, CZ] ~ N(0,
     1/CZ); w_o [CZ, HID] ~ N(0, 1/HID); LayerNorm weight 1 + N(0, 0.2^2),
-    bias N(0, 0.2^2).  Draw order: z, w_a, w_b, w_o, ln_w, ln_b."""
+    bias N(0, 0.2^2); with dout, an upstream gradient ~ N(0,1) [N,N,CZ].
+    Draw order: z, w_a, w_b, w_o, ln_w, ln_b, dout."""
     gen = torch.Generator().manual_seed(seed)
 
     def draw(shape, std=1.0):
@@ -187,13 +188,15 @@ def rand_transition(N, CZ, HID, dtype, seed=0):
     d["ln_w"] = draw((CZ,), 0.2) + 1
     d["ln_b"] = draw((CZ,), 0.2)
     d["eps"] = 1e-5
+    if dout:
+        d["dout"] = draw((N, N, CZ))
     return d
 
 
-def transition_inputs(name, seed=0):
+def transition_inputs(name, seed=0, dout=False):
     w = WORKLOADS[name]
     assert w["kind"] == "transition"
-    return rand_transition(w["N"], w["CZ"], w["HID"], w["dtype"], seed=seed)
+    return rand_transition(w["N"], w["CZ"], w["HID"], w["dtype"], seed=seed, dout=dout)
 
 
 def rand_opm(S, N, CM, C, CZ, dtype, seed=0):

@@ -381,6 +381,42 @@ evo_status_t pair_transition_fwd(evo_dtype_t dtype, int64_t N, int64_t CZ,
                                  size_t workspace_bytes, void* stream);
 
 /*
+ * pair_transition_bwd -- gradients of pair_transition_fwd for training
+ * (EvoFusion targets the activation memory of LayerNorm, projections and
+ * SwiGLU: "MegaFold: Efficient Training of Next-Generation 3D Attention
+ * Protein Models on Cross-Platform GPUs", section "Methodologie", item 3).
+ * The chain rule of the forward, with silu'(u) = sigmoid(u) (1 + u (1 -
+ * sigmoid(u))):
+ *   dh = dout . w_o,  du = dh * v * silu'(u),  dv = dh * silu(u),
+ *   dz = LayerNorm backward of du . w_a + dv . w_b,
+ *   dw_a = sum over positions of du^T x, dw_b likewise with dv,
+ *   dw_o = sum of dout^T h,  dln_w, dln_b the LayerNorm parameter gradients.
+ * Activations are recomputed from z; sums over positions are deterministic
+ * (fixed order, no atomics).
+ *
+ *   z, ln_w, ln_b, ln_eps, w_a, w_b, w_o  as pair_transition_fwd; HID a
+ *              multiple of 128 (EVO_ENOTSUP otherwise).
+ *   dout       [N,N,CZ] dtype: the upstream gradient.
+ *   dz         [N,N,CZ] dtype (written).
+ *   dln_w, dln_b [CZ] fp32; dw_a, dw_b [HID, CZ] fp32; dw_o [CZ, HID] fp32
+ *              (written, not accumulated).
+ *   workspace  pair_transition_bwd_workspace_bytes(...) bytes, caller-owned:
+ *              the prepared weights, du, dv and h for the weight reductions
+ *              (3 N^2 HID elements of dtype) and the reduction partials.
+ * Pointers: device memory, 16-byte aligned.  Enqueued on `stream`.
+ */
+size_t pair_transition_bwd_workspace_bytes(evo_dtype_t dtype, int64_t N,
+                                           int64_t CZ, int64_t HID);
+evo_status_t pair_transition_bwd(evo_dtype_t dtype, int64_t N, int64_t CZ,
+                                 int64_t HID, const void* z, const void* ln_w,
+                                 const void* ln_b, float ln_eps,
+                                 const void* w_a, const void* w_b,
+                                 const void* w_o, const void* dout, void* dz,
+                                 float* dln_w, float* dln_b, float* dw_a,
+                                 float* dw_b, float* dw_o, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/*
  * outer_product_mean_fwd -- the MSA-to-pair bridge ("Evoformer: the memory
  * wall ZeRO cannot move", section "The three operations": the mean over all
  * sequences of the outer product of MSA columns i and j).  The pages give no

@@ -47,7 +47,7 @@ __all__ = [
     "tri_module_forward", "tri_module_lines", "layer_norm_backward",
     "tri_out_project_backward", "tri_project_backward",
     "tri_module_backward", "tri_mul_forward", "tri_mul_entries",
-    "transition_forward", "outer_product_mean", "transition_backward", "outer_product_mean_pairs",
+    "transition_forward", "outer_product_mean", "transition_backward", "transition_weight_grad_units", "outer_product_mean_pairs",
 ]
 
 
@@ -568,6 +568,28 @@ def transition_backward(z, ln_w, ln_b, eps, w_a, w_b, w_o, dout):
     dz, dln_w, dln_b = layer_norm_backward(z.reshape(-1, CZ), ln_w, eps, dx)
     return dict(dz=dz.reshape(z.shape), dln_w=dln_w, dln_b=dln_b,
                 dw_a=du.T @ x, dw_b=dv.T @ x, dw_o=dy.T @ h)
+
+
+def transition_weight_grad_units(z, ln_w, ln_b, eps, w_a, w_b, w_o, dout, units):
+    """Rows dw_a[k], dw_b[k] and columns dw_o[:, k] of transition_backward for
+    the hidden units k in `units` only, over every position: each unit's
+    u, v and dh are formed for that unit alone (the same chain rule).
+    Returns arrays [len(units), CZ] (dw_a, dw_b) and [CZ, len(units)]
+    (dw_o)."""
+    z = np.asarray(z, np.float64)
+    CZ = z.shape[-1]
+    x = layer_norm(z, ln_w, ln_b, eps).reshape(-1, CZ)
+    dy = np.asarray(dout, np.float64).reshape(-1, CZ)
+    ra, rb, ro = [], [], []
+    for k in units:
+        u = x @ w_a[k]
+        v = x @ w_b[k]
+        sg = sigmoid(u)
+        dh = dy @ w_o[:, k]
+        ra.append((dh * v * sg * (1.0 + u * (1.0 - sg))) @ x)
+        rb.append((dh * u * sg) @ x)
+        ro.append(dy.T @ (u * sg * v))
+    return np.stack(ra), np.stack(rb), np.stack(ro, axis=1)
 
 
 # ----------------------------------------------------------------------------

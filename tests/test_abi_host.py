@@ -285,3 +285,18 @@ def test_opm_fault_injection(monkeypatch):
             FAKE, FAKE, 1 << 30, None]
     assert L.outer_product_mean_fwd(*args) == ops.EVO_EHIP
     assert "injected" in err()
+
+
+def test_transition_bwd_validation():
+    assert L.pair_transition_bwd_workspace_bytes(1, 64, 128, 512) > 3 * 64 * 64 * 512 * 2
+    assert L.pair_transition_bwd_workspace_bytes(1, 64, 128, 192) == 0  # HID % 128
+    args = [1, 16, 64, 256, FAKE, FAKE, FAKE, 1e-5, FAKE, FAKE, FAKE, FAKE, FAKE,
+            FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 34, None]
+    args[12] = None
+    assert L.pair_transition_bwd(*args) == ops.EVO_EINVAL and "'dz' is NULL" in err()
+    args[12] = FAKE
+    args[19] = 128
+    assert L.pair_transition_bwd(*args) == ops.EVO_EWORKSPACE
+    args[19] = 1 << 34
+    args[3] = 192
+    assert L.pair_transition_bwd(*args) == ops.EVO_ENOTSUP and "HID=192" in err()

@@ -912,6 +912,17 @@ def test_transition_backward_planted_mistake_fails():
                                atol=1e-8)
 
 
+def test_transition_weight_grad_units_match_full_backward():
+    d = transition_case(98, N=4, CZ=8, HID=10)
+    dout = np.random.default_rng(99).standard_normal((4, 4, 8))
+    full = O.transition_backward(dout=dout, **d)
+    units = [0, 3, 9]
+    ga, gb, go = O.transition_weight_grad_units(dout=dout, units=units, **d)
+    np.testing.assert_allclose(ga, full["dw_a"][units], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(gb, full["dw_b"][units], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(go, full["dw_o"][:, units], rtol=1e-12, atol=1e-12)
+
+
 # ------------------------------------------------------- outer product mean
 
 def opm_case(seed, S=4, N=5, CM=6, C=3, CZ=7):
