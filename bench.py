@@ -18,7 +18,8 @@ Prints one JSON line.  Options: --steps K --warmup W --gpus 1
 the whole module instead: forward, then the backward with the LayerNorm,
 projection and output-projection gradients), --trimul (the triangular
 multiplicative update instead), --transition (the fused LayerNorm + SwiGLU
-transition instead) and --opm (the outer product mean instead).
+transition instead), --transition-bwd (its backward instead) and --opm (the
+outer product mean instead).
 """
 import argparse
 import hashlib
@@ -57,6 +58,9 @@ def parse():
     ap.add_argument("--transition", action="store_true",
                     help="time the fused LayerNorm + SwiGLU transition instead "
                          "(pair_transition_fwd, z [768,768,128], hidden 512)")
+    ap.add_argument("--transition-bwd", action="store_true",
+                    help="time the transition backward instead "
+                         "(pair_transition_bwd, z [768,768,128], hidden 512)")
     ap.add_argument("--opm", action="store_true",
                     help="time the outer product mean instead "
                          "(outer_product_mean_fwd, m [1024,768,256], 32 "
@@ -389,6 +393,55 @@ def transition_bench(a):
     print(json.dumps(res), flush=True)
 
 
+def transition_bwd_bench(a):
+    """The transition backward on transition_768 (dz and every parameter
+    gradient).  Prints one JSON line; the roofline entry is the whole call
+    against the dense bf16 matrix-core peak."""
+    import torch
+    from evoformer_attention_amd import metrics as M
+    from evoformer_attention_amd import ops, synth
+
+    w = dict(synth.WORKLOADS["transition_768"])
+    N, CZ, HID = w["N"], w["CZ"], w["HID"]
+    d = synth.transition_inputs("transition_768", dout=True)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    g = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    ws = torch.empty(ops.pair_transition_bwd_workspace_bytes(g["z"].dtype, N, CZ, HID),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        return ops.pair_transition_bwd(g["z"], g["ln_w"], g["ln_b"], g["eps"], g["w_a"],
+                                       g["w_b"], g["w_o"], g["dout"], workspace=ws)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(a.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / a.steps
+    tf = M.transition_bwd_flops(N, CZ, HID) / (ms * 1e-3) / 1e12
+    res = {
+        "metric": "LayerNorm + SwiGLU pair transition backward TFLOP/s (bf16), N_res=768",
+        "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "transition_768", "N_res": N, "c_z": CZ, "hidden": HID,
+                   "pass": "backward (dz, dln_w, dln_b, dw_a, dw_b, dw_o)"},
+        "roofline": {"bound": "mfma", "kernel": "pair_transition_bwd (call)",
+                     "achieved": round(tf, 2), "peak": M.MI355X_BF16_DENSE_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf / M.MI355X_BF16_DENSE_TFLOPS, 4),
+                     "traffic": None},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def opm_bench(a):
     """The outer product mean on opm_1024x768.  Prints one JSON line; the
     roofline entry is the whole call (projections, the product on the matrix
@@ -441,6 +494,12 @@ def opm_bench(a):
 
 def main():
     a = parse()
+    if a.transition_bwd:
+        if a.gpus != 1:
+            print("bench.py runs on one GPU only", file=sys.stderr)
+            sys.exit(2)
+        transition_bwd_bench(a)
+        return
     if a.opm:
         if a.gpus != 1:
             print("bench.py runs on one GPU only", file=sys.stderr)

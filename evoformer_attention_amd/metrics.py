@@ -101,6 +101,13 @@ def trimul_flops(N, CZ, C):
     return 2.0 * N * N * CZ * 2 * C + 2.0 * C * N ** 3 + 2.0 * N * N * C * CZ
 
 
+def transition_bwd_flops(N, CZ, HID):
+    """Counted flops of the transition backward per position: the recomputed
+    u, v (2 x 2 HID CZ), dh (2 HID CZ), dx (2 x 2 HID CZ) and the three
+    weight-gradient contractions (3 x 2 HID CZ): 16 HID CZ."""
+    return 16.0 * N * N * HID * CZ
+
+
 def opm_flops(S, N, CM, C, CZ):
     """Counted flops of one outer product mean: the a and b projections (2 x C
     outputs per sequence-residue position), the product of the [N*C, S] and
