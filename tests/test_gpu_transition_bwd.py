@@ -74,3 +74,24 @@ def test_transition_bwd_deterministic():
     b = gpu_bwd(d)
     for k in NAMES:
         assert torch.equal(a[k], b[k]), k
+
+
+def test_transition_bwd_768_parameter_gradients_in_chunks():
+    """Full size: every parameter gradient (dln_w, dln_b, dw_a, dw_b, dw_o)
+    is a sum over positions, so the oracle's gradients of position chunks add
+    up to the whole (fp64); compared in full against the GPU result."""
+    log("case transition_bwd_768 chunked")
+    d = synth.transition_inputs("transition_768", dout=True)
+    got = gpu_bwd(d)
+    a = oracle_args(d)
+    z = a["z"].reshape(-1, 1, a["z"].shape[-1])
+    dout = a["dout"].reshape(-1, 1, a["dout"].shape[-1])
+    tot = None
+    step = 32768
+    for p0 in range(0, z.shape[0], step):
+        e = dict(a, z=z[p0:p0 + step], dout=dout[p0:p0 + step])
+        g = O.transition_backward(**e)
+        g.pop("dz")
+        tot = g if tot is None else {k: tot[k] + g[k] for k in tot}
+    for k, v in tot.items():
+        compare(k, np64(got[k]), v, "bf16", scale="peak")
