@@ -468,6 +468,10 @@ bwd_dkdv_kernel(BwdParams p) {
     // S[qb][kb]: lane holds queries qb*16 + 4g + i for key kbase + kb*16 + l16.
     // dP starts from -D, so the accumulator ends at dP - D.
     f32x4 s[2][2], dp[2][2];
+    // products at raised wave priority (as in the forward): 677 -> 656 us
+    // here and 680 -> 656 us in dBias at N = 768; dQ measured slower (its
+    // registers spill), so it keeps the default
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const Op qa = *reinterpret_cast<const Op*>(sQ + (qb * 16 + l16) * RS + 8 * g);
@@ -479,6 +483,7 @@ bwd_dkdv_kernel(BwdParams p) {
         dp[qb][kb] = mma32(da, vf[kb], negd);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const f32x4 l2 = *reinterpret_cast<const f32x4*>(&sL[buf][0][qb * 16 + 4 * g]);
@@ -506,6 +511,7 @@ bwd_dkdv_kernel(BwdParams p) {
         dot = *reinterpret_cast<const Op*>(sT[buf][3] + (cb * 16 + l16) * RS + 8 * g);
         qtf = *reinterpret_cast<const Op*>(sT[buf][2] + (cb * 16 + l16) * RS + 8 * g);
       }
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const Op pf = pack8(s[0][kb], s[1][kb], (Op*)nullptr);
@@ -513,6 +519,8 @@ bwd_dkdv_kernel(BwdParams p) {
         dv[cb][kb] = mma32(dot, pf, dv[cb][kb]);
         dk[cb][kb] = mma32(qtf, sf, dk[cb][kb]);
       }
+      __builtin_amdgcn_s_setprio(0);
+
     }
   };
   StageRaw<T> ra, rb;
@@ -923,11 +931,14 @@ bwd_dbias_kernel(BwdParams p) {
         const Op kf = *reinterpret_cast<const Op*>(sK[buf] + (half * 32 + kb * 16 + l16) * KS + 8 * g);
         const Op vf = *reinterpret_cast<const Op*>(sV[buf] + (half * 32 + kb * 16 + l16) * KS + 8 * g);
         f32x4 s[2], dp[2];
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
           s[qb] = mma32(kf, qf[qb], cbias[half][qb][kb]);
           dp[qb] = mma32(vf, df[qb], negd[qb]);
         }
+        __builtin_amdgcn_s_setprio(0);
+
         bool dead[4] = {false, false, false, false};
         if constexpr (ROW_MASK) {
 #pragma unroll

@@ -412,8 +412,7 @@ attn_fwd_kernel(FwdParams p) {
       f32x4 s[ROWS][2][2];  // [rr][qb][kb]
       // The products run at raised wave priority, so that a wave reaching
       // them issues them ahead of the other waves' softmax arithmetic and
-      // the matrix core is fed sooner (0.540 -> 0.527 ms at N = 768; the
-      // same in the backward kernels measured 1% slower).
+      // the matrix core is fed sooner (0.540 -> 0.527 ms at N = 768).
       __builtin_amdgcn_s_setprio(1);
       EVO_FWD_QK(hf);
       __builtin_amdgcn_s_setprio(0);
