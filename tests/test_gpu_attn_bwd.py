@@ -6,7 +6,7 @@ import torch
 
 import oracle.evo_oracle as O
 from evoformer_attention_amd import ops, synth
-from helpers import compare, dev, log, np64, npu8
+from helpers import compare, dev, log, np64, npu8, round_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -24,6 +24,49 @@ def oracle_bwd(d):
     return O.attention_backward(np64(d["q"]), np64(d["k"]), np64(d["v"]),
                                 np64(d["gate"]), npu8(d["mask"]),
                                 np64(d["bias"]), np64(d["dout"]))
+
+
+U = 2.0 ** -8  # bf16 unit roundoff (relative size of one rounding)
+
+
+def dbias_rounding_bound(d):
+    """Worst-case (first-order) error of the bf16 dBias from the kernels'
+    own roundings, elementwise [B, H, N, N], summed over rows:
+      forward: every p is rounded to bf16 before the PV product and the
+        weights are renormalised by the sum of the rounded values, so each
+        weight moves by at most 2u relative: |dOut_pre| <= 2u sum_k P|V|;
+        the stored Out adds u|Out|;
+      D = sum_c dOut * Out (from the stored Out): |dD| <= sum_c |dOut| |dOut_err|;
+      dO * sigmoid(G) is rounded to bf16 before dP = dO V^T:
+        |d dP| <= u sum_c |dO V|;
+      P is recomputed from the log-sum-exp of the rounded p: |dP/P| <= u;
+      so |d dS| <= P (|d dP| + |dD|) + u |dS|, summed over the rows.
+    The pages fix no precision for these steps; this is the bf16 reading of
+    the standard backward (D from the stored forward output)."""
+    q, k, v = np64(d["q"]), np64(d["k"]), np64(d["v"])
+    g, bias, dout = np64(d["gate"]), np64(d["bias"]), np64(d["dout"])
+    mask = npu8(d["mask"])
+    B, R, N, H, C = q.shape
+    out = np.zeros((B, H, N, N))
+    for b in range(B):
+        for r in range(R):
+            keep = None if mask is None else mask[b, 0 if mask.shape[1] == 1 else r] != 0
+            P_all = O.attention_line_probs(q[b, r], k[b, r],
+                                           None if bias is None else bias[b], keep)
+            for h in range(H):
+                P = P_all[h]
+                V = v[b, r, :, h, :]
+                sg = np.ones((N, C)) if g is None else O.sigmoid(g[b, r, :, h, :])
+                do = dout[b, r, :, h, :]
+                o_pre = P @ V
+                err_out = 2 * U * sg * (P @ np.abs(V)) + U * np.abs(sg * o_pre)
+                dD = (np.abs(do) * err_out).sum(-1)                    # [N]
+                dop = do * sg
+                ddP = U * (np.abs(dop) @ np.abs(V).T)                  # [N, N]
+                dP = dop @ V.T
+                dS = P * (dP - (P * dP).sum(-1, keepdims=True))
+                out[b, h] += P * (ddP + dD[:, None]) + U * np.abs(dS)
+    return out
 
 
 SHAPES = [  # B, R, N, H
@@ -49,9 +92,14 @@ def test_bwd_parity_small(dtype, shape, opts):
         if r is None:
             assert gt is None
             continue
-        # dBias sums the R rows of dS: bound relative to its own peak.
-        scale = "peak" if name == "dbias" else 1.0
-        compare(name, np64(gt), r, dtype, scale=scale)
+        if name == "dbias":
+            # a sum over rows of dS: with few keys (large P) the rounding of
+            # the forward output through D alone can exceed 2e-2; the bf16
+            # bar is then the derived bound of the kernels' own roundings
+            bound = dbias_rounding_bound(d) if dtype == "bf16" else None
+            compare(name, np64(gt), r, dtype, stored="fp32", bound=bound)
+        else:
+            compare(name, np64(gt), r, dtype)
 
 
 def test_bwd_invariants_on_gpu_outputs():
@@ -80,8 +128,11 @@ def test_bwd_without_dbias_and_deterministic():
 def test_tri_start_512_fwd_bwd_sampled():
     """Projection + core forward + core backward at full size: starting
     node, z [512,512,128], H=4, upstream gradient ~ N(0,1).  The oracle
-    projects z itself (fp64) and its gradients are compared on sampled lines;
-    dBias (a sum over all 512 lines) on sampled query rows."""
+    projects z itself (fp64); the projections cross the boundary between
+    tri_attn_project and the attention calls as bf16 tensors, so the oracle's
+    are rounded to bf16 there (round to nearest even) before its attention
+    backward.  Gradients are compared on sampled lines, dBias (a sum over
+    all 512 lines) on sampled query rows, all under the plain bf16 bar."""
     log("case tri_start_512_bwd")
     w = synth.WORKLOADS["tri_start_512_bwd"]
     d = synth.module_inputs("tri_start_512_bwd")
@@ -100,6 +151,7 @@ def test_tri_start_512_fwd_bwd_sampled():
                                        np64(d["w_k"]), np64(d["w_v"]),
                                        np64(d["w_g"]), np64(d["b_g"]),
                                        np64(d["w_bias"]), H, C, False)
+    oq, ok, ov, og, ob = (round_bf16(t) for t in (oq, ok, ov, og, ob))
     dout = np64(d["dout"])
     for r in (0, 1, 255, 511):
         rq, rk, rv, rg_, _ = O.attention_line_backward(
@@ -111,4 +163,4 @@ def test_tri_start_512_fwd_bwd_sampled():
     picks = [(0, 0), (1, 100), (2, 311), (3, 511)]
     ref = O.dbias_query_rows(oq, ok, ov, og, None, ob, dout, 0, picks)
     got = np.stack([np64(db[0, h, qi]) for h, qi in picks])
-    compare("dbias rows", got, ref, "bf16", scale="peak")
+    compare("dbias rows", got, ref, "bf16", stored="fp32")

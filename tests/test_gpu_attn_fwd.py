@@ -30,7 +30,7 @@ def check(d, dtype, rows=None):
     if rows is None:
         ref, ref_lse = run_oracle(d)
         compare("out", np64(out), ref, dtype)
-        compare("lse", lse.numpy().astype(np.float64), ref_lse, dtype)
+        compare("lse", lse.numpy().astype(np.float64), ref_lse, dtype, stored="fp32")
         return
     mask = npu8(d["mask"])
     for (b, r) in rows:
@@ -44,7 +44,7 @@ def check(d, dtype, rows=None):
             keep)
         compare(f"out[{b},{r}]", np64(out[b, r]), ref, dtype)
         compare(f"lse[{b},{r}]", lse[b, r].numpy().astype(np.float64), ref_lse,
-                dtype)
+                dtype, stored="fp32")
 
 
 def test_core_fp32_small_workload():
@@ -178,3 +178,24 @@ def test_no_lse_and_stream_ordering():
     torch.cuda.synchronize()
     ref, _ = run_oracle(d)
     compare("out", np64(out.cpu()), ref, "bf16")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("profile", ["ramp", "step"])
+def test_logits_rising_along_keys(dtype, profile):
+    """Pair bias that rises along the keys, so that later key tiles hold
+    logits far above everything seen in the first one: the softmax
+    reference of the kernel has to be raised tile after tile (ramp: +0.1
+    per key, 32 nats over the line) or once by a large jump (step: +100
+    nats from key 200 on; e^100 exceeds the fp32 range, so a reference left
+    at the first tile's maximum would turn the sums into inf).  N = 320:
+    five 64-key tiles, the last one ragged only through the mask."""
+    log(f"case fwd rising logits {dtype} {profile}")
+    N = 320
+    d = synth.rand_core(1, 3, N, 2, 32, dtype, seed=77, mask="random")
+    kk = torch.arange(N, dtype=torch.float32)
+    add = 0.1 * kk if profile == "ramp" else 100.0 * (kk >= 200).float()
+    d["bias"] = synth.round_to(d["bias"].float() + add, dtype)
+    out, lse = run_gpu(d)
+    assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+    check(d, dtype)

@@ -1,8 +1,14 @@
 """GPU parity of the module backward entry points against the fp64 oracle:
 tri_attn_out_project_bwd, tri_attn_project_bwd and tri_attn_module_bwd,
-called through the C ABI.  Weight gradients are sums over every pair
-position, so they are compared in units of their largest entry (the "peak"
-scale of helpers.compare), as dBias is."""
+called through the C ABI.  d_o and the dz of the projection backward alone
+(per position, stored in the working dtype, from exact inputs) are held to
+the plain bar plus their storage rounding.  The dz of the whole-module
+backward passes through four bf16 roundings along each term (the attention
+output o, the gradient d_o, the attention gradient dq/dk/dv/dg, and the
+stored dz): plain bar plus 4 * 2^-8 |oracle| (helpers.compare, rounds=4).
+The weight and LayerNorm-parameter
+gradients (fp32 sums over every pair position) to the bar relative to their
+largest entry (helpers.compare, scale="peak")."""
 import numpy as np
 import pytest
 import torch
@@ -34,8 +40,8 @@ def test_out_project_bwd_parity(dtype, ending, N, CZ, H):
     torch.cuda.synchronize()
     r_do, r_dw, r_db = O.tri_out_project_backward(np64(o), np64(w_o), np64(dout), ending)
     compare("d_o", np64(d_o), r_do, dtype)
-    compare("dw_o", np64(dw_o), r_dw, "fp32" if dtype == "fp32" else "bf16", scale="peak")
-    compare("db_o", np64(db_o), r_db, dtype, scale="peak")
+    compare("dw_o", np64(dw_o), r_dw, dtype, scale="peak", stored="fp32")
+    compare("db_o", np64(db_o), r_db, dtype, scale="peak", stored="fp32")
 
 
 def _proj_case(N, CZ, H, dtype, seed):
@@ -67,7 +73,7 @@ def test_project_bwd_parity(dtype, ending, N, CZ, H):
         np64(d["dg"]), np64(d["dbias"]), ending)
     compare("dz", np64(got["dz"]), ref["dz"], dtype)
     for name in PARAM_NAMES:
-        compare(name, np64(got[name]), ref[name], dtype, scale="peak")
+        compare(name, np64(got[name]), ref[name], dtype, scale="peak", stored="fp32")
 
 
 def _module_case(N, CZ, H, dtype, seed, mask):
@@ -96,22 +102,10 @@ def _oracle_module_bwd(d, H, ending):
         np64(d["b_o"]), H, 32, ending, np64(d["dout"]))
 
 
-def _w_ext_gain(d):
-    """max over channels c of ||W_ext[:, c]||_2, W_ext = the Q, K, V, gate and
-    pair-bias weights stacked along their output rows.  In the whole-module
-    backward dz is formed from dX = [dq dk dv dg dbias] . W_ext, whose
-    inputs are themselves bf16 results of the attention backward (each within
-    the bf16 bar), so an error of the bar's size in every input reaches dX
-    multiplied by up to this factor (errors of independent sign add in
-    quadrature); the LayerNorm backward then scales it by rstd * gamma ~ 1."""
-    w = np.concatenate([np64(d[n]) for n in ("w_q", "w_k", "w_v", "w_g", "w_bias")])
-    return max(1.0, float(np.sqrt((w ** 2).sum(0)).max()))
-
-
 def _compare_module(got, ref, dtype, d):
-    compare("dz", np64(got["dz"]), ref["dz"], dtype, scale=_w_ext_gain(d))
+    compare("dz", np64(got["dz"]), ref["dz"], dtype, rounds=4 if dtype == "bf16" else 0)
     for name in PARAM_NAMES + ("dw_o", "db_o"):
-        compare(name, np64(got[name]), ref[name], dtype, scale="peak")
+        compare(name, np64(got[name]), ref[name], dtype, scale="peak", stored="fp32")
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
@@ -155,4 +149,55 @@ def test_module_bwd_tri_end_768_properties():
     s = dz.sum(-1).abs()
     bound = 2.0 ** -8 * dz.abs().sum(-1) + 1e-6
     assert bool((s <= bound).all()), float((s / bound).max())
-    compare("db_o", np64(g1["db_o"]), np64(d["dout"]).sum((0, 1)), "bf16", scale="peak")
+    compare("db_o", np64(g1["db_o"]), np64(d["dout"]).sum((0, 1)), "bf16", scale="peak", stored="fp32")
+
+
+def test_project_bwd_tri_end_768_parity():
+    """tri_attn_project_bwd at full size: z [768,768,128], ending node, 4
+    heads of 32, affine LayerNorm, bf16, incoming gradients dq, dk, dv, dg
+    ~ N(0,1) and dBias ~ N(0,16) (a sum over rows).  Every output against
+    the oracle's full backward (~20 s of fp64 on the host): dz at all
+    589824 positions and every parameter gradient summed over all of them."""
+    N, CZ, H = 768, 128, 4
+    log(f"case project_bwd bf16 N={N} CZ={CZ} H={H} ending (full size)")
+    d = synth.rand_module(N, CZ, H, 32, "bf16", seed=31, ln_affine=True,
+                          gate_bias=True)
+    gen = torch.Generator().manual_seed(1031)
+    for name in ("dq", "dk", "dv", "dg"):
+        d[name] = _draw(gen, (1, N, N, H, 32), "bf16")
+    d["dbias"] = torch.randn((1, H, N, N), generator=gen) * 4.0
+    got = ops.tri_attn_project_bwd(
+        dev(d["z"]), dev(d["ln_w"]), dev(d["ln_b"]), d["eps"], dev(d["w_q"]),
+        dev(d["w_k"]), dev(d["w_v"]), dev(d["w_g"]), dev(d["w_bias"]),
+        dev(d["dq"]), dev(d["dk"]), dev(d["dv"]), dev(d["dg"]), dev(d["dbias"]),
+        H, 32, True)
+    torch.cuda.synchronize()
+    got = {k: v.cpu() for k, v in got.items()}
+    log("  oracle ...")
+    ref = O.tri_project_backward(
+        np64(d["z"]), np64(d["ln_w"]), np64(d["ln_b"]), d["eps"],
+        np64(d["w_q"]), np64(d["w_k"]), np64(d["w_v"]), np64(d["w_g"]),
+        np64(d["w_bias"]), np64(d["dq"]), np64(d["dk"]), np64(d["dv"]),
+        np64(d["dg"]), np64(d["dbias"]), True)
+    compare("dz", np64(got["dz"]), ref["dz"], "bf16")
+    for name in PARAM_NAMES:
+        compare(name, np64(got[name]), ref[name], "bf16", scale="peak", stored="fp32")
+
+
+def test_out_project_bwd_tri_end_768_parity():
+    """tri_attn_out_project_bwd at full size: o [1,768,768,4,32], the
+    ending node's transposed write, c_z = 128, bf16: d_o at every position
+    (per position, plain bar) and dw_o, db_o summed over all
+    589824 positions, against the oracle in full."""
+    N, CZ, H = 768, 128, 4
+    log(f"case out_project_bwd bf16 N={N} CZ={CZ} H={H} ending (full size)")
+    gen = torch.Generator().manual_seed(768)
+    o = _draw(gen, (1, N, N, H, 32), "bf16")
+    w_o = _draw(gen, (CZ, H * 32), "bf16", (H * 32) ** -0.5)
+    dout = _draw(gen, (N, N, CZ), "bf16")
+    d_o, dw_o, db_o = ops.tri_attn_out_project_bwd(dev(o), dev(w_o), dev(dout), True)
+    torch.cuda.synchronize()
+    r_do, r_dw, r_db = O.tri_out_project_backward(np64(o), np64(w_o), np64(dout), True)
+    compare("d_o", np64(d_o), r_do, "bf16")
+    compare("dw_o", np64(dw_o), r_dw, "bf16", scale="peak", stored="fp32")
+    compare("db_o", np64(db_o), r_db, "bf16", scale="peak", stored="fp32")

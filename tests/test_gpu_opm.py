@@ -3,10 +3,12 @@ C ABI) against the fp64 oracle.
 
 Each output is a sum over C*C products o[i,j,c,d] * w_o, each o a mean over
 S sequences of a * b, with a, b and the product o stored in the working
-dtype in between; as for the multiplicative update, an entry's relative
-error stays that of one term while the entries' size varies with the sums,
-so the bf16 bar is applied in units of the output's largest entry
-(helpers.compare, scale="peak"); the relative L2 bar is unchanged."""
+dtype in between: six bf16 roundings along each term (the layer-normalised
+rows feeding a and b, a and b themselves, the product o, and the stored
+output), in sums that cancel, so an output's error scales with its terms
+rather than with itself.  The bar is the plain one relative to the output's
+largest entry (helpers.compare, scale="peak"); the relative L2 bar is
+unchanged.  The plain 2e-2 max-abs bar is not met (up to ~4e-2)."""
 import numpy as np
 import pytest
 import torch
@@ -71,4 +73,4 @@ def test_opm_deterministic_and_sequence_order():
     e = dict(d)
     e["m"] = d["m"].flip(0).contiguous()
     c = gpu_opm(e)
-    compare("reversed", np64(c), np64(a), "bf16", scale="peak")
+    compare("reversed", np64(c), np64(a), "bf16", rounds=2)

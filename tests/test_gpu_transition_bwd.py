@@ -3,10 +3,13 @@ ABI) against the fp64 oracle.
 
 dz is a LayerNorm backward of du . w_a + dv . w_b, sums over 2 * HID hidden
 units whose du, dv are rounded to the working dtype before the product (as
-the forward's hidden layer); the weight and LayerNorm-parameter gradients
-are sums over every position.  All are compared in units of their largest
-entry (helpers.compare, scale="peak"), as the module backward's weight
-gradients and dBias are; the relative L2 bar is unchanged."""
+the forward's hidden layer).  Along the path of a dz term the kernels round
+to bf16 four times (the hidden gradient dh, du or dv, the layer-normalised
+row of the recomputed forward, and the stored dz), so dz is held to the
+plain bar plus 4 * 2^-8 |oracle| (rounds=4); the weight and LayerNorm-parameter gradients
+are sums over every position.  dz (per position, stored in the working
+dtype) is held to the plain bar; the fp32 parameter gradients to the bar
+relative to their largest entry (helpers.compare, scale="peak")."""
 import numpy as np
 import pytest
 import torch
@@ -45,7 +48,10 @@ def test_transition_bwd_parity(dtype, N, CZ, HID):
     got = gpu_bwd(d)
     ref = O.transition_backward(**oracle_args(d))
     for k in NAMES:
-        compare(k, np64(got[k]), ref[k], dtype, scale="peak")
+        if k == "dz":
+            compare(k, np64(got[k]), ref[k], dtype, rounds=4 if dtype == "bf16" else 0)
+        else:
+            compare(k, np64(got[k]), ref[k], dtype, scale="peak", stored="fp32")
 
 
 def test_transition_bwd_768_sampled():
@@ -59,12 +65,12 @@ def test_transition_bwd_768_sampled():
     for r in (0, 383, 767):
         e = dict(a, z=a["z"][r:r + 1], dout=a["dout"][r:r + 1])
         ref = O.transition_backward(**e)
-        compare(f"dz[{r}]", np64(got["dz"][r:r + 1]), ref["dz"], "bf16", scale="peak")
+        compare(f"dz[{r}]", np64(got["dz"][r:r + 1]), ref["dz"], "bf16", rounds=4)
     units = [0, 77, 255, 256, 511]
     ga, gb, go = O.transition_weight_grad_units(units=units, **a)
-    compare("dw_a[units]", np64(got["dw_a"])[units], ga, "bf16", scale="peak")
-    compare("dw_b[units]", np64(got["dw_b"])[units], gb, "bf16", scale="peak")
-    compare("dw_o[:, units]", np64(got["dw_o"])[:, units], go, "bf16", scale="peak")
+    compare("dw_a[units]", np64(got["dw_a"])[units], ga, "bf16", scale="peak", stored="fp32")
+    compare("dw_b[units]", np64(got["dw_b"])[units], gb, "bf16", scale="peak", stored="fp32")
+    compare("dw_o[:, units]", np64(got["dw_o"])[:, units], go, "bf16", scale="peak", stored="fp32")
 
 
 def test_transition_bwd_deterministic():
@@ -94,4 +100,4 @@ def test_transition_bwd_768_parameter_gradients_in_chunks():
         g.pop("dz")
         tot = g if tot is None else {k: tot[k] + g[k] for k in tot}
     for k, v in tot.items():
-        compare(k, np64(got[k]), v, "bf16", scale="peak")
+        compare(k, np64(got[k]), v, "bf16", scale="peak", stored="fp32")
