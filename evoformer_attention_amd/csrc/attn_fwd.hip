@@ -48,6 +48,7 @@
 // exact up to rounding for any m, since O and l are scaled by the same
 // exp2(-m).
 #include <algorithm>
+#include <mutex>
 
 #include "evo_device.h"
 #include "evo_kernels.h"
@@ -566,6 +567,36 @@ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 size_t attn_fwd_workspace(int dtype, int64_t B, int64_t N, int64_t H) {
   return (size_t)(B * H * round_up(N, BQ) * round_up(N, BK) * (dtype == 1 ? 2 : 4));
+}
+
+// Scratch of the allocation-free forward entry point: a file-scope device
+// array (every GPU the library runs on holds its own copy until the process
+// ends).  In host code `scratch` names a host-side stand-in, not device
+// memory, so its device address is looked up with hipGetSymbolAddress once
+// per device, with that device current, and only that address is used.
+namespace {
+constexpr size_t kStaticScratchBytes = size_t(16) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t fwd_static_scratch(void** ptr, size_t* bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  *bytes = kStaticScratchBytes;
+  return hipSuccess;
 }
 
 hipError_t launch_attn_fwd(const AttnFwdArgs& a, hipStream_t s) {

@@ -149,6 +149,47 @@ evo_status_t evo_attn_fwd(evo_dtype_t dtype, int64_t B, int64_t R, int64_t N,
   }
 }
 
+evo_status_t evo_attn_fwd_noalloc(evo_dtype_t dtype, int64_t B, int64_t R,
+                                  int64_t N, int64_t H, int64_t C, const void* q,
+                                  const void* k, const void* v, const void* gate,
+                                  const uint8_t* key_mask, int64_t mask_rows,
+                                  const void* bias, void* out, float* lse,
+                                  void* stream) {
+  try {
+    evo_status_t st = check_core_sizes(dtype, B, R, N, H, C);
+    if (st != EVO_OK) return st;
+    REQUIRE_PTR(q);
+    REQUIRE_PTR(k);
+    REQUIRE_PTR(v);
+    REQUIRE_PTR(out);
+    OPTIONAL_PTR(gate);
+    OPTIONAL_PTR(bias);
+    OPTIONAL_PTR(lse);
+    OPTIONAL_PTR(key_mask);
+    if ((st = check_mask(key_mask, mask_rows, R)) != EVO_OK) return st;
+    void* scratch = nullptr;
+    if (bias || key_mask) {
+      const size_t need = evo::attn_fwd_workspace((int)dtype, B, N, H);
+      size_t cap = 0;
+      const hipError_t e = evo::fwd_static_scratch(&scratch, &cap);
+      if (e != hipSuccess) return from_hip(e, "evo_attn_fwd_noalloc: scratch lookup");
+      if (need > cap)
+        return fail(EVO_ENOTSUP,
+                    "evo_attn_fwd_noalloc: the prepared bias needs %zu bytes, more than "
+                    "the library's static scratch of %zu bytes (call evo_attn_fwd with "
+                    "a workspace instead)", need, cap);
+    }
+    if (fault_injected())
+      return fail(EVO_EHIP, "evo_attn_fwd_noalloc: injected launch failure");
+    evo::AttnFwdArgs a{(int)dtype, B, R, N, H, q, k, v, gate, key_mask,
+                       mask_rows, bias, out, lse, scratch};
+    return from_hip(evo::launch_attn_fwd(a, (hipStream_t)stream),
+                    "evo_attn_fwd_noalloc");
+  } catch (...) {
+    return fail(EVO_EINTERNAL, "evo_attn_fwd_noalloc: internal error");
+  }
+}
+
 size_t evo_attn_fwd_workspace_bytes(evo_dtype_t dtype, int64_t B, int64_t R,
                                     int64_t N, int64_t H, int64_t C) {
   const std::string saved = g_last_error;

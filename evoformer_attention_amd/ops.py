@@ -13,6 +13,7 @@ import os
 import torch
 
 __all__ = ["EvoAttnError", "lib", "evo_abi_version", "evo_attn_fwd",
+           "evo_attn_fwd_noalloc",
            "evo_attn_bwd", "evo_attn_bwd_workspace_bytes",
            "evo_attn_fwd_workspace_bytes", "tri_attn_project",
            "tri_attn_out_project", "tri_attn_module_fwd",
@@ -45,6 +46,8 @@ EXPORTS = {
     "evo_last_error": (ctypes.c_char_p, []),
     "evo_attn_fwd": (_I, [_I, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P,
                           _P, _I64, _P, _P, _P, _P, _SZ, _P]),
+    "evo_attn_fwd_noalloc": (_I, [_I, _I64, _I64, _I64, _I64, _I64, _P, _P, _P,
+                                  _P, _P, _I64, _P, _P, _P, _P]),
     "evo_attn_fwd_workspace_bytes": (_SZ, [_I, _I64, _I64, _I64, _I64, _I64]),
     "evo_attn_bwd_workspace_bytes": (_SZ, [_I, _I64, _I64, _I64, _I64, _I64]),
     "evo_attn_bwd": (_I, [_I, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P,
@@ -194,6 +197,38 @@ def evo_attn_fwd(q, k, v, gate=None, key_mask=None, bias=None, out=None,
                             ws_bytes, _stream(q.device))
     _check("evo_attn_fwd", st)
     return (out, lse) if want_lse else out
+
+
+def evo_attn_fwd_noalloc(q, k, v, gate=None, key_mask=None, bias=None, out=None,
+                         lse=None):
+    """evo_attn_fwd through the allocation-free entry point: the library uses
+    its static scratch instead of a workspace.  `out` (and `lse` [B,R,H,N]
+    fp32, optional) may be passed in; whatever is not given is allocated here
+    by torch, not by the library.  Returns out, or (out, lse) when lse is
+    given."""
+    _dev_tensor("q", q)
+    B, R, N, H, C = q.shape
+    dt = q.dtype
+    _dev_tensor("k", k, dt, q.shape)
+    _dev_tensor("v", v, dt, q.shape)
+    _dev_tensor("gate", gate, dt, q.shape)
+    _dev_tensor("bias", bias, dt, (B, H, N, N))
+    mask_rows = 0
+    if key_mask is not None:
+        _dev_tensor("key_mask", key_mask, torch.uint8)
+        if key_mask.dim() != 3 or key_mask.shape[0] != B or key_mask.shape[2] != N:
+            raise EvoAttnError("binding", EVO_EINVAL,
+                               f"key_mask has shape {tuple(key_mask.shape)}")
+        mask_rows = key_mask.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    _dev_tensor("out", out, dt, q.shape)
+    _dev_tensor("lse", lse, torch.float32, (B, R, H, N))
+    st = lib().evo_attn_fwd_noalloc(_dtype_code(q), B, R, N, H, C, _ptr(q), _ptr(k),
+                                    _ptr(v), _ptr(gate), _ptr(key_mask), mask_rows,
+                                    _ptr(bias), _ptr(out), _ptr(lse), _stream(q.device))
+    _check("evo_attn_fwd_noalloc", st)
+    return (out, lse) if lse is not None else out
 
 
 def evo_attn_bwd_workspace_bytes(dtype, B, R, N, H, C):

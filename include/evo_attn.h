@@ -21,7 +21,8 @@
  *
  * Conventions shared by every entry point:
  *  - Pointers are device memory owned by the caller (except where stated).
- *    The library never allocates, frees or keeps a pointer after returning.
+ *    The library never allocates, frees or keeps a pointer after returning;
+ *    the one exception is the fixed static scratch of evo_attn_fwd_noalloc.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *    the call returns at once.  Inputs must stay valid and unchanged, and
  *    outputs untouched, until the stream has passed the work.
@@ -96,6 +97,29 @@ evo_status_t evo_attn_fwd(evo_dtype_t dtype, int64_t B, int64_t R, int64_t N,
                           const void* bias, void* out, float* lse,
                           void* workspace, size_t workspace_bytes,
                           void* stream);
+
+/*
+ * evo_attn_fwd_noalloc -- evo_attn_fwd without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  Same arguments,
+ * results and errors as evo_attn_fwd, minus workspace/workspace_bytes.
+ *
+ * The prepared bias lives in a static scratch array of 16 MiB inside the
+ * library (one per GPU, held until the process ends; its device address is
+ * looked up once per device on the first call there).  A problem whose
+ * evo_attn_fwd_workspace_bytes(...) exceeds 16 MiB is rejected with
+ * EVO_ENOTSUP before anything is enqueued (e.g. bf16 with H * N^2 above
+ * 8 Mi elements: H = 4 up to N ~ 1448).  The call allocates nothing.  Every
+ * call on one GPU uses the same scratch: calls that may overlap on one GPU
+ * (different streams without ordering) race and must not be issued.  The
+ * scratch needs no clearing: each call writes every element it reads.
+ */
+evo_status_t evo_attn_fwd_noalloc(evo_dtype_t dtype, int64_t B, int64_t R,
+                                  int64_t N, int64_t H, int64_t C, const void* q,
+                                  const void* k, const void* v, const void* gate,
+                                  const uint8_t* key_mask, int64_t mask_rows,
+                                  const void* bias, void* out, float* lse,
+                                  void* stream);
 
 /* Bytes of device workspace evo_attn_fwd needs when a bias or mask is given
  * (O(B * H * N^2); 0 on a problem evo_attn_fwd would reject). */
