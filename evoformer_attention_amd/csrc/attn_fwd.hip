@@ -11,12 +11,12 @@
 // item 1).
 //
 // Kernels.
-//   bias_prep  writes the pair bias once per call, in the working dtype,
-//              with the shared key mask and the padding keys folded in as
-//              -inf, so the main loop needs no bounds or mask logic.  It is
-//              stored in the main kernel's fragment order (see the prep
-//              kernel): each wave's bias load is one contiguous 1 KB block,
-//              which each lane widens into matrix-core accumulator operands.
+//   bias_prep  writes the pair bias once per call (fp16 for bf16 inputs, fp32
+//              for fp32), with the shared key mask and the padding keys
+//              folded in as -inf, so the main loop needs no bounds or mask
+//              logic.  It is stored in the main kernel's fragment order (see
+//              the prep kernel): each wave's bias load is one contiguous 1 KB
+//              block, 8 consecutive keys of one query per lane.
 //   attn_fwd   a workgroup (4 waves) owns 128 queries of one head and one
 //              line (ROWS = 1; the kernel is written for ROWS lines sharing
 //              the bias tile); each wave owns 32 queries.  Keys stream in
@@ -24,11 +24,15 @@
 //              and bias being fetched into registers while the current one is
 //              computed (one barrier per tile); each tile is processed as two
 //              32-key halves (logits, softmax, PV), which keeps the kernel at
-//              ~120 registers per lane: four waves per SIMD.
+//              ~100 registers per lane: five waves per SIMD.
 //
 // Matrix-core mapping (v_mfma_f32_16x16x32_bf16, fp32 accumulate):
-//   S^T = K . (Q/sqrt(C))^T + bias^T   A = 16 keys x 32 dims (LDS), B = Q^T
-//                            held in registers for the whole line, C = bias.
+//   T^T = K . Q'^T - m       A = 16 keys x 32 dims (LDS), B = Q'^T = (Q
+//                            log2(e)/sqrt(C))^T held in registers for the
+//                            whole line, C = -m (the softmax reference of each
+//                            query, splat); then + bias * log2(e), one
+//                            v_fma_mix_f32 per logit straight from the fp16
+//                            bias, so T is the base-2 exponent itself.
 //   O^T += V^T . P^T         A = V^T from LDS, B = P^T taken straight from
 //                            the S^T accumulators (no LDS round trip).
 // In the accumulator layout a lane holds one query and 4 keys per 16-key
@@ -37,18 +41,19 @@
 // registers the lane holds, bias loads are 16-byte vectors and the V^T
 // operand is one 16-byte LDS read.
 //
-// Softmax with a lazy reference.  p = exp2(S*log2(e) - m) uses a per-query
-// reference m (base 2) that is only raised when needed: the first half-tile
-// (and any half while a query has seen no live key) computes the true
-// maximum; a later half is recomputed with a raised reference only if a
-// lane's sum of p over it exceeds 2^8.  So every p <= 2^8 (no overflow in
-// fp32 or bf16), m never exceeds the true maximum (no underflow of the
-// result), and the common half costs one FMA and one exp per logit plus a
-// dot2 per two for the row sum, with no cross-lane reduction.  The result is
-// exact up to rounding for any m, since O and l are scaled by the same
-// exp2(-m).
+// Softmax with a lazy reference.  p = exp2(T) uses a per-query reference m
+// (base 2, subtracted inside the products) that is only raised when needed:
+// the first half-tile (and any half while a query has seen no live key)
+// computes the true maximum; a later half is recomputed with a raised
+// reference only if a lane's sum of p over it exceeds 2^8.  So every
+// p <= 2^8 (no overflow in fp32 or bf16), m never exceeds the true maximum
+// (no underflow of the result), and the common half costs one fma and one
+// exp per logit plus a dot2 per two for the row sum, with no cross-lane
+// reduction and no conversion of the bias.  The result is exact up to
+// rounding for any m, since O and l are scaled by the same exp2(-m).
 #include <algorithm>
 #include <mutex>
+#include <type_traits>
 
 #include "evo_device.h"
 #include "evo_kernels.h"
@@ -62,6 +67,14 @@ constexpr int BQW = 32;           // queries per wave
 constexpr int WAVES = 4;
 constexpr int BQ = BQW * WAVES;   // queries per workgroup
 constexpr float kHeadroom = 256.f;  // 2^8: largest tile sum of p per lane
+
+// Prepared-bias element: bf16 inputs are stored as fp16, which holds every
+// bf16 value of magnitude 2^-14 .. 65504 exactly (8 significant bits fit in
+// 11) and lets v_fma_mix_f32 add bias * log2(e) to an fp32 logit in one
+// instruction; fp32 inputs stay fp32.
+template <typename T> struct PB;
+template <> struct PB<bf16_t> { using E = _Float16; };
+template <> struct PB<float> { using E = float; };
 
 template <typename T> struct FwdLds;
 // Row strides (elements) of the LDS K tile [64 keys][32 dims] and V tile;
@@ -78,13 +91,13 @@ struct FwdParams {
   const void* v;
   const void* gate;
   const uint8_t* mask;   // per-line masks only (shared masks are in biasp)
-  const void* biasp;     // [B, H, Nq, Nk] working dtype, or null (no bias, no mask)
+  const void* biasp;     // [B, H, Nq, Nk] fp16 (bf16 inputs) or fp32, or null (no bias, no mask)
   void* out;
   float* lse;
   int B, R, N, H, mask_rows;
   int Nq, Nk;            // padded bias dims
   int n_qt, n_rg, total;
-  float qscale;          // 1 / sqrt(C)
+  float qscale;          // log2(e) / sqrt(C): the products come out in base-2 units
 };
 
 // LDS row of physical key p (0..63) of a tile: A-operand lane m of block
@@ -198,7 +211,9 @@ __device__ __forceinline__ void st4f(float* p, const f32x4& v) {
 
 // Bias prep.  The prepared bias holds, for every (b, h, query q < Nq, key
 // k < Nk), the bias in natural units (0 without a bias), or -inf for keys
-// masked by a shared mask or beyond N.  It is stored in the order the main
+// masked by a shared mask or beyond N.  For bf16 inputs it is fp16: exact for
+// every bf16 value of magnitude 2^-14 .. 65504, within 2^-25 below that, and
+// finite values beyond +-65504 are clamped to it.  It is stored in the order the main
 // kernel reads it, so that each wave's bias load is one contiguous 1 KB
 // block: per (b, h) a grid of [Nq/128][Nk/64] tiles, each tile
 // [wave 4][qb 2][half 2][lane 64][8 keys], where lane (l16, g) of wave w
@@ -206,8 +221,9 @@ __device__ __forceinline__ void st4f(float* p, const f32x4& v) {
 // .. +7 (the accumulator-operand layout of the logit tile).
 template <typename T>
 __global__ void __launch_bounds__(256) fwd_bias_prep_kernel(
-    const T* bias, const uint8_t* mask, int shared_mask, T* biasp, int B,
+    const T* bias, const uint8_t* mask, int shared_mask, typename PB<T>::E* biasp, int B,
     int H, int N, int Nq, int Nk) {
+  using E = typename PB<T>::E;
   const int nqt = Nq / BQ, nkt = Nk / BK;
   const int64_t total = (int64_t)B * H * Nq * (Nk / 8);
   for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total;
@@ -223,7 +239,7 @@ __global__ void __launch_bounds__(256) fwd_bias_prep_kernel(
     const int b = (int)(bh / H);
     const int q = qt * BQ + wv * BQW + qb * 16 + (lane & 15);
     const int k0 = kt * BK + half * 32 + 8 * (lane >> 4);
-    f32x4 v[2];
+    E v[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int kk = k0 + j;
@@ -232,23 +248,42 @@ __global__ void __launch_bounds__(256) fwd_bias_prep_kernel(
         x = (bias && q < N) ? Tr<T>::to_f(bias[(bh * N + q) * N + kk]) : 0.f;
         if (shared_mask && mask[(int64_t)b * N + kk] == 0) x = -INFINITY;
       }
-      v[j >> 2][j & 3] = x;
+      // fp16: finite values beyond its range are clamped to +-65504
+      if (sizeof(E) == 2 && x == x && fabsf(x) != INFINITY) x = fminf(fmaxf(x, -65504.f), 65504.f);
+      v[j] = (E)x;
     }
-    // exact: every x is a value of type T, 0 or -inf
-    st4f(biasp + e * 8, v[0]);
-    st4f(biasp + e * 8 + 4, v[1]);
+    if constexpr (sizeof(E) == 2) {
+      *reinterpret_cast<u32x4*>(biasp + e * 8) = __builtin_bit_cast(u32x4, v);
+    } else {
+      *reinterpret_cast<u32x4*>(biasp + e * 8) = __builtin_bit_cast(u32x4, *reinterpret_cast<float(*)[4]>(v));
+      *reinterpret_cast<u32x4*>(biasp + e * 8 + 4) = __builtin_bit_cast(u32x4, *reinterpret_cast<float(*)[4]>(v + 4));
+    }
   }
 }
 
-// Logits of one 32-key half `hf_` of the tile, all lines of the group:
-// s[rr][qb][kb] = K . (Q/sqrt(C))^T + bias^T.
-#define EVO_FWD_QK(hf_)                                                          \
+// Exponents of one 32-key half `hf_` of the tile, base 2, all lines of the
+// group: t = K . (Q log2(e)/sqrt(C))^T - ref + bias * log2(e), where the
+// reference enters as the products' accumulator operand `ref_` ([qb] splats)
+// and the prepared bias (`braw`, 8 values per (qb, half)) is added by one
+// fma per logit (v_fma_mix_f32 for the fp16 bias).  Dead keys: -inf.
+#define EVO_FWD_T(hf_, ref_)                                                     \
   do {                                                                           \
     for (int rr = 0; rr < ROWS; ++rr)                                            \
       for (int kb = 0; kb < 2; ++kb) {                                           \
         const Op kf = ld8(sK[buf][rr] + ((hf_) * 32 + kb * 16 + l16) * KST + 8 * g); \
         for (int qb = 0; qb < 2; ++qb)                                           \
-          s[rr][qb][kb] = mma32(kf, qf[rr][qb], bt[qb][kb]);                     \
+          t[rr][qb][kb] = mma32(kf, qf[rr][qb], ref_[rr][qb]);                   \
+      }                                                                          \
+    for (int rr = 0; rr < ROWS; ++rr)                                            \
+      for (int qb = 0; qb < 2; ++qb) {                                           \
+        if constexpr (HAS_BIAS) {                                                \
+          add_bias8(t[rr][qb][0], t[rr][qb][1], braw[qb][hf_]);                   \
+        } else {                                                                 \
+          if (k0 + BK > N)                                                       \
+            for (int kb = 0; kb < 2; ++kb)                                       \
+              for (int i = 0; i < 4; ++i)                                        \
+                if (k0 + (hf_) * 32 + 8 * g + 4 * kb + i >= N) t[rr][qb][kb][i] = -INFINITY; \
+        }                                                                        \
       }                                                                          \
     if constexpr (ROW_MASK) {                                                    \
       for (int rr = 0; rr < ROWS; ++rr) {                                        \
@@ -256,13 +291,33 @@ __global__ void __launch_bounds__(256) fwd_bias_prep_kernel(
         for (int j = 0; j < 8; ++j) {                                            \
           const bool dead = kbase + j < N && mrow[rr][kbase + j] == 0;           \
           if (dead) {                                                            \
-            s[rr][0][j >> 2][j & 3] = -INFINITY;                                 \
-            s[rr][1][j >> 2][j & 3] = -INFINITY;                                 \
+            t[rr][0][j >> 2][j & 3] = -INFINITY;                                 \
+            t[rr][1][j >> 2][j & 3] = -INFINITY;                                 \
           }                                                                      \
         }                                                                        \
       }                                                                          \
     }                                                                            \
   } while (0)
+
+// x += bias * log2(e) for the 8 prepared values of a lane (keys 0..3 -> x,
+// 4..7 -> y): fp16 through v_fma_mix_f32 (no separate conversion), fp32
+// through a plain fma.
+__device__ __forceinline__ void add_bias8(f32x4& x, f32x4& y, const u32x4& raw) {
+  typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+  const f16x8 h = __builtin_bit_cast(f16x8, raw);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[i] = __builtin_fmaf((float)h[i], kLog2e, x[i]);
+    y[i] = __builtin_fmaf((float)h[4 + i], kLog2e, y[i]);
+  }
+}
+__device__ __forceinline__ void add_bias8(f32x4& x, f32x4& y, const Raw8<float>& raw) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[i] = __builtin_fmaf(__uint_as_float(raw.a[i]), kLog2e, x[i]);
+    y[i] = __builtin_fmaf(__uint_as_float(raw.b[i]), kLog2e, y[i]);
+  }
+}
 
 template <typename T, int ROWS, bool ROW_MASK, bool HAS_BIAS>
 __global__ void __launch_bounds__(256)
@@ -336,11 +391,12 @@ attn_fwd_kernel(FwdParams p) {
 
   // This lane's 8 bias values of (qb, half) in key tile `tile` sit at
   // bbase + tile * BQ*BK + (qb*2 + half) * 512 (prepared tile order).
-  const T* btile = HAS_BIAS ? static_cast<const T*>(p.biasp) +
+  using E = typename PB<T>::E;
+  const E* btile = HAS_BIAS ? static_cast<const E*>(p.biasp) +
                                   (((int64_t)b * H + h) * (p.Nq / BQ) + qt) *
                                       (p.Nk / BK) * (BQ * BK)
                             : nullptr;  // this workgroup's row of tiles
-  const T* bbase = HAS_BIAS ? btile + wave * 2048 + lane * 8 : nullptr;
+  const E* bbase = HAS_BIAS ? btile + wave * 2048 + lane * 8 : nullptr;
   const uint8_t* mrow[ROWS];
   if constexpr (ROW_MASK) {
 #pragma unroll
@@ -349,22 +405,23 @@ attn_fwd_kernel(FwdParams p) {
   }
 
   KVRaw<T> raw[ROWS];
-  // Bias operands of the next tile as loaded (raw), widened to fp32 only
-  // after the next barrier: the loads stay in flight across the K/V tile
-  // store instead of being waited for at the end of the tile.
-  Raw8<T> braw[2][2];  // [qb][half]
-  // (bf16: buffer loads from the workgroup's tile row with the lane's offset
-  // fixed, like the K/V tiles)
-  const uint32_t bvoff = (uint32_t)(wave * 2048 + lane * 8) * (uint32_t)sizeof(T);
-  const uint32_t bbytes = (uint32_t)(p.Nk / BK) * (BQ * BK) * (uint32_t)sizeof(T);  // the row
+  // Bias values of the next tile as loaded (raw); they stay in flight
+  // across the K/V tile store instead of being waited for at the end of the
+  // tile.  (bf16 inputs: 8 fp16 values per (qb, half) in one buffer load
+  // from the workgroup's tile row with the lane's offset fixed, like the K/V
+  // tiles.)
+  using BRaw = std::conditional_t<sizeof(T) == 2, u32x4, Raw8<float>>;
+  BRaw braw[2][2];  // [qb][half]
+  const uint32_t bvoff = (uint32_t)(wave * 2048 + lane * 8) * 2u;
+  const uint32_t bbytes = (uint32_t)(p.Nk / BK) * (BQ * BK) * 2u;  // the row
 #define EVO_FETCH_BIAS(k0_)                                                        \
   do {                                                                         \
     if constexpr (HAS_BIAS) {                                                  \
       for (int qb = 0; qb < 2; ++qb)                                           \
         for (int half = 0; half < 2; ++half) {                                 \
           if constexpr (sizeof(T) == 2)                                        \
-            braw[qb][half].a = buf_ld128(btile, bbytes, bvoff + (qb * 2 + half) * 1024u, \
-                                         (uint32_t)((k0_) / BK) * (BQ * BK * 2u)); \
+            braw[qb][half] = buf_ld128(btile, bbytes, bvoff + (qb * 2 + half) * 1024u, \
+                                       (uint32_t)((k0_) / BK) * (BQ * BK * 2u)); \
           else                                                                 \
             ld_raw8(braw[qb][half],                                            \
                     bbase + (int64_t)((k0_) / BK) * (BQ * BK) + (qb * 2 + half) * 512); \
@@ -374,6 +431,20 @@ attn_fwd_kernel(FwdParams p) {
 #pragma unroll
   for (int rr = 0; rr < ROWS; ++rr) fetch_kv<T>(raw[rr], kline[rr], vline[rr], 0, N, pos_stride);
   EVO_FETCH_BIAS(0);
+
+  // -m of each query as a splat accumulator operand of the logit products
+  // (+inf while a query has seen no live key: its exponents are then inf or
+  // NaN and force the exact path)
+  f32x4 negm[ROWS][2];
+#pragma unroll
+  for (int rr = 0; rr < ROWS; ++rr)
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) negm[rr][qb] = f32x4{INFINITY, INFINITY, INFINITY, INFINITY};
+  f32x4 zero[ROWS][2];
+#pragma unroll
+  for (int rr = 0; rr < ROWS; ++rr)
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) zero[rr][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int ntiles = (N + BK - 1) / BK;
   for (int tile = 0; tile < ntiles; ++tile) {
@@ -395,34 +466,19 @@ attn_fwd_kernel(FwdParams p) {
     // work of one line overlaps the softmax of the other.
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-      // this half's bias operands in accumulator layout: [qb][kb]
-      f32x4 bt[2][2];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        if constexpr (HAS_BIAS) {
-          widen8(braw[qb][hf], bt[qb][0], bt[qb][1]);
-        } else {
-          // no bias and no shared mask: 0, padding keys -inf
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              bt[qb][kb][i] = (k0 + hf * 32 + 8 * g + 4 * kb + i < N) ? 0.f : -INFINITY;
-        }
-      }
-      f32x4 s[ROWS][2][2];  // [rr][qb][kb]
+      f32x4 t[ROWS][2][2];  // [rr][qb][kb] exponents, base 2
       // The products run at raised wave priority, so that a wave reaching
       // them issues them ahead of the other waves' softmax arithmetic and
-      // the matrix core is fed sooner (0.540 -> 0.527 ms at N = 768).
+      // the matrix core is fed sooner.
       __builtin_amdgcn_s_setprio(1);
-      EVO_FWD_QK(hf);
+      EVO_FWD_T(hf, negm);
       __builtin_amdgcn_s_setprio(0);
 
-      // p = exp2(s*log2e - m), rounded to the operand type at once: P^T is
-      // kept as matrix-core operands and the row sums are taken over
-      // exactly the rounded values the PV product uses.  Fast path: the
-      // current reference; the first half of the first tile always takes
-      // the exact maximum.
+      // p = exp2(t), rounded to the operand type at once: P^T is kept as
+      // matrix-core operands and the row sums are taken over exactly the
+      // rounded values the PV product uses.  Fast path: the current
+      // reference; the first half of the first tile always takes the exact
+      // maximum.
       Op pf[ROWS][2];  // [rr][qb]
       float psum[ROWS][2];
       bool slow = tile == 0 && hf == 0;
@@ -432,23 +488,22 @@ attn_fwd_kernel(FwdParams p) {
         for (int rr = 0; rr < ROWS; ++rr)
 #pragma unroll
           for (int qb = 0; qb < 2; ++qb) {
-            const float nm = -m[rr][qb];
             f32x4 e[2];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-              for (int i = 0; i < 4; ++i)
-                e[kb][i] = exp2_fast(__builtin_fmaf(s[rr][qb][kb][i], kLog2e, nm));
+              for (int i = 0; i < 4; ++i) e[kb][i] = exp2_fast(t[rr][qb][kb][i]);
             pf[rr][qb] = pack8(e[0], e[1], (Op*)nullptr);
             psum[rr][qb] = sum8(pf[rr][qb], 0.f);
-            // not yet anchored (m = -inf gives inf or NaN), or too large
+            // not yet anchored (inf or NaN), or too large
             redo |= !(psum[rr][qb] <= kHeadroom);
           }
         slow = __builtin_amdgcn_ballot_w64(redo) != 0;
-        if (slow) EVO_FWD_QK(hf);  // the logits again, for the exact path
       }
       if (slow) {
-        // Raise the reference to the half's maximum where needed.
+        // The exponents again, relative to 0, and the reference raised to
+        // the half's maximum where needed.
+        EVO_FWD_T(hf, zero);
 #pragma unroll
         for (int rr = 0; rr < ROWS; ++rr)
 #pragma unroll
@@ -457,14 +512,16 @@ attn_fwd_kernel(FwdParams p) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-              for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[rr][qb][kb][i]);
+              for (int i = 0; i < 4; ++i) mx = fmaxf(mx, t[rr][qb][kb][i]);
             mx = fmaxf(mx, shfl_xor(mx, 16));
             mx = fmaxf(mx, shfl_xor(mx, 32));
             const float mold = m[rr][qb];
-            const float mnew = fmaxf(mold, mx * kLog2e);
+            const float mnew = fmaxf(mold, mx);
             const float muse = (mnew == -INFINITY) ? 0.f : mnew;
             const float alpha = (mold == -INFINITY) ? 0.f : exp2_fast(mold - muse);
             m[rr][qb] = (mnew == -INFINITY) ? -INFINITY : muse;
+            const float nm = -m[rr][qb];
+            negm[rr][qb] = f32x4{nm, nm, nm, nm};
             l[rr][qb] *= alpha;
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb) o[rr][qb][cb] *= alpha;
@@ -472,8 +529,7 @@ attn_fwd_kernel(FwdParams p) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-              for (int i = 0; i < 4; ++i)
-                e[kb][i] = exp2_fast(__builtin_fmaf(s[rr][qb][kb][i], kLog2e, -muse));
+              for (int i = 0; i < 4; ++i) e[kb][i] = exp2_fast(t[rr][qb][kb][i] - muse);
             pf[rr][qb] = pack8(e[0], e[1], (Op*)nullptr);
             psum[rr][qb] = sum8(pf[rr][qb], 0.f);
           }
@@ -605,7 +661,7 @@ hipError_t launch_attn_fwd(const AttnFwdArgs& a, hipStream_t s) {
   p.out = a.out; p.lse = a.lse;
   p.B = (int)a.B; p.R = (int)a.R; p.N = (int)a.N; p.H = (int)a.H;
   p.mask_rows = a.mask ? (int)a.mask_rows : 1;
-  p.qscale = 1.f / sqrtf((float)C);
+  p.qscale = kLog2e / sqrtf((float)C);
   p.Nq = (int)round_up(a.N, BQ);
   p.Nk = (int)round_up(a.N, BK);
   const bool row_mask = a.mask && a.mask_rows > 1;
@@ -619,7 +675,7 @@ hipError_t launch_attn_fwd(const AttnFwdArgs& a, hipStream_t s) {
     if (a.dtype == 1)
       hipLaunchKernelGGL(fwd_bias_prep_kernel<bf16_t>, dim3(grid), dim3(256), 0, s,
                          static_cast<const bf16_t*>(a.bias), a.mask, (int)shared_mask,
-                         static_cast<bf16_t*>(bp), p.B, p.H, p.N, p.Nq, p.Nk);
+                         static_cast<_Float16*>(bp), p.B, p.H, p.N, p.Nq, p.Nk);
     else
       hipLaunchKernelGGL(fwd_bias_prep_kernel<float>, dim3(grid), dim3(256), 0, s,
                          static_cast<const float*>(a.bias), a.mask, (int)shared_mask,

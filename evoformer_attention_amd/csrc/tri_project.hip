@@ -77,10 +77,10 @@ __device__ __forceinline__ uint32_t z_row(uint32_t pidx, uint32_t N, int ending)
 
 // Line-layout position of element j (0..31) of wave `wave` in tile `tile`
 // (WAVES*32 consecutive positions per tile); `live` is false past the end.
-template <int WAVES>
+template <int WAVES, int PWV = PW>
 __device__ __forceinline__ uint32_t tile_pos(const GemmParams& p, int tile, int wave, int j,
                                              bool& live) {
-  const uint32_t pi = ((uint32_t)tile * WAVES + wave) * PW + j;
+  const uint32_t pi = ((uint32_t)tile * WAVES + wave) * PWV + j;
   live = pi < (uint32_t)p.npos;
   return pi;
 }
@@ -158,9 +158,20 @@ __device__ __forceinline__ void store_pair<float>(float* row, const f32x4& a, co
 
 // MUL: the multiplicative-update operand mode (p.mode == 2), a separate
 // instantiation so that the other modes' code is unchanged by it.
-template <typename T, int KSTEPS, int WAVES = waves_for<KSTEPS>(), bool MUL = false>
+// SPLIT (bf16 projection, p.mode == 0): the LayerNorm output y = xhat * gamma
+// + beta is formed in fp32 and handed to the matrix cores as two bf16
+// operands, hi = bf16(y) and lo = bf16(y - hi) (16 significant bits), against
+// the unmodified bf16 weights: the projection is then exact up to fp32
+// accumulation before its one rounding to the output type, instead of
+// rounding y (and W * gamma) to bf16 first.  Twice the products and the
+// operand registers: eight waves per workgroup (two per SIMD); used up to
+// 160 input channels (wider inputs keep the single rounded operand).
+template <typename T, int KSTEPS, int WAVES = waves_for<KSTEPS>(), bool MUL = false,
+          bool SPLIT = false>
 __global__ void __launch_bounds__(WAVES * 64)
 rowgemm_kernel(GemmParams p) {
+  constexpr int PB = 2;               // 16-position blocks per wave
+  constexpr int PWV = 16 * PB;        // positions per wave
   using Op = typename Tr<T>::Op;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int K = KSTEPS * 32;
@@ -173,15 +184,17 @@ rowgemm_kernel(GemmParams p) {
   // operand mode (bf16): per wave, one 32-position x 16-channel block staged
   // row by position, read back channel by channel
   T* sO = reinterpret_cast<T*>(sC + p.pass_cols) + (MUL ? wave * 32 * OS : 0);
+  // SPLIT: gamma and beta of the K input channels, after the column constants
+  T* sG = reinterpret_cast<T*>(sC + p.pass_cols);
 
   const T* X = static_cast<const T*>(p.x);
   // Rows of position `pi` as loaded: channels 32s + 8g .. +7 in nx[s].
   // Positions past the end read row 0 (finite; never stored).
-  auto load_rows = [&](Op (&nx)[2][KSTEPS], int tile) {
+  auto load_rows = [&](Op (&nx)[PB][KSTEPS], int tile) {
 #pragma unroll
-    for (int pb = 0; pb < 2; ++pb) {
+    for (int pb = 0; pb < PB; ++pb) {
       bool live;
-      const uint32_t pi = tile_pos<WAVES>(p, tile, wave, pb * 16 + l16, live);
+      const uint32_t pi = tile_pos<WAVES, PWV>(p, tile, wave, pb * 16 + l16, live);
       uint32_t row = 0;
       if (live) {
         if constexpr (MUL) {
@@ -201,7 +214,7 @@ rowgemm_kernel(GemmParams p) {
   // tile's during the weight set-up (fp32 rows would not fit the register
   // budget and are loaded at the tile's start)
   constexpr bool PREFETCH = sizeof(T) == 2;
-  Op nx[2][KSTEPS];
+  Op nx[PB][KSTEPS];
   if (PREFETCH && blockIdx.x < p.ntiles) load_rows(nx, blockIdx.x);
 
   // ---- This pass's weights into LDS, with the LayerNorm affine folded in:
@@ -225,7 +238,7 @@ rowgemm_kernel(GemmParams p) {
         const T* src = e < total ? w_row<T>(p, p.col0 + cl) : nullptr;
         if (src) {
           ld_raw8(wr[u], src + k0);
-          if (p.mode != 1) ld_raw8(gr[u], lnw + k0);
+          if (p.mode != 1 && !SPLIT) ld_raw8(gr[u], lnw + k0);
         }
       }
 #pragma unroll
@@ -236,7 +249,7 @@ rowgemm_kernel(GemmParams p) {
         f32x4 w0 = {0.f, 0.f, 0.f, 0.f}, w1 = w0;
         if (w_row<T>(p, p.col0 + cl)) {
           widen8(wr[u], w0, w1);
-          if (p.mode != 1) {
+          if (p.mode != 1 && !SPLIT) {
             f32x4 g0, g1;
             widen8(gr[u], g0, g1);
             w0 *= g0;
@@ -257,7 +270,7 @@ rowgemm_kernel(GemmParams p) {
       const int c = p.col0 + cl;
       const T* src = w_row<T>(p, c);
       float acc = 0.f;
-      if (src && p.mode != 1) {
+      if (src && p.mode != 1 && !SPLIT) {
 #pragma unroll 4
         for (int k0 = 0; k0 < K; k0 += 8) {
           Raw8<T> wr, br;
@@ -279,6 +292,12 @@ rowgemm_kernel(GemmParams p) {
       }
       sC[cl] = acc;
     }
+    if constexpr (SPLIT) {
+      for (int c = tid; c < K; c += WAVES * 64) {
+        sG[c] = lnw[c];
+        sG[K + c] = lnb[c];
+      }
+    }
   }
   __syncthreads();
 
@@ -292,15 +311,17 @@ rowgemm_kernel(GemmParams p) {
   const int cbase0 = p.col0 - m0 * p.HC;
   for (int tile = blockIdx.x; tile < p.ntiles; tile += gridDim.x) {
     if (!PREFETCH) load_rows(nx, tile);
-    // ---- this wave's 32 rows, in B-operand layout: xf[pb][s] holds
-    // channels 32s + 8g .. +7 of position base + pb*16 + l16.
-    Op xf[2][KSTEPS];
+    // ---- this wave's 16 * PB rows, in B-operand layout: xf[pb][s] holds
+    // channels 32s + 8g .. +7 of position base + pb*16 + l16 (SPLIT: the hi
+    // part; xl the lo part).
+    Op xf[PB][KSTEPS];
+    Op xl[SPLIT ? PB : 1][SPLIT ? KSTEPS : 1];
     uint32_t pidx[2];
     int64_t orow[2];
-    bool live[2];
+    bool live[2] = {false, false};
 #pragma unroll
-    for (int pb = 0; pb < 2; ++pb) {
-      pidx[pb] = tile_pos<WAVES>(p, tile, wave, pb * 16 + l16, live[pb]);
+    for (int pb = 0; pb < PB; ++pb) {
+      pidx[pb] = tile_pos<WAVES, PWV>(p, tile, wave, pb * 16 + l16, live[pb]);
       // output row offset: line layout (project) or z layout (out projection)
       orow[pb] = p.mode == 0 ? (int64_t)pidx[pb] * p.HC
                              : (int64_t)(live[pb] ? z_row(pidx[pb], p.N, p.ending) : 0) * p.ncols;
@@ -309,7 +330,7 @@ rowgemm_kernel(GemmParams p) {
     }
     if (PREFETCH && tile + (int)gridDim.x < p.ntiles) load_rows(nx, tile + gridDim.x);
 #pragma unroll
-    for (int pb = 0; pb < 2; ++pb) {
+    for (int pb = 0; pb < PB; ++pb) {
       float v[1][KSTEPS][8];
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s)
@@ -341,15 +362,41 @@ rowgemm_kernel(GemmParams p) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) v[0][s][j] *= rstd;
       }
+      if constexpr (SPLIT) {
+        // y = xhat * gamma + beta in fp32, as hi + lo bf16 operands
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) {
-        Op f;
+        for (int s = 0; s < KSTEPS; ++s) {
+          Raw8<T> gr, br;
+          ld_raw8(gr, sG + 32 * s + 8 * g);
+          ld_raw8(br, sG + K + 32 * s + 8 * g);
+          f32x4 g0, g1, b0, b1;
+          widen8(gr, g0, g1);
+          widen8(br, b0, b1);
+          Op hi, lo;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          if constexpr (sizeof(T) == 2) f[j] = (__bf16)v[0][s][j];
-          else f[j] = v[0][s][j];
+          for (int j = 0; j < 8; ++j) {
+            const float y = __builtin_fmaf(v[0][s][j], j < 4 ? g0[j] : g1[j - 4], j < 4 ? b0[j] : b1[j - 4]);
+            const __bf16 h = (__bf16)y;
+            hi[j] = h;
+            lo[j] = (__bf16)(y - (float)h);
+          }
+          xf[pb][s] = hi;
+          xl[pb][s] = lo;
+          // keep the next step's gamma/beta loads here (hoisting them all
+          // ahead costs registers)
+          __builtin_amdgcn_sched_barrier(0);
         }
-        xf[pb][s] = f;
+      } else {
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) {
+          Op f;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            if constexpr (sizeof(T) == 2) f[j] = (__bf16)v[0][s][j];
+            else f[j] = v[0][s][j];
+          }
+          xf[pb][s] = f;
+        }
       }
     }
 
@@ -375,13 +422,20 @@ rowgemm_kernel(GemmParams p) {
 #pragma unroll
           for (int s = 0; s < KSTEPS; ++s) {
             const Op a = *reinterpret_cast<const Op*>(wr + 32 * s);
-            acc[j][0] = mma32(a, xf[0][s], acc[j][0]);
-            acc[j][1] = mma32(a, xf[1][s], acc[j][1]);
+            if constexpr (SPLIT) {
+              acc[j][0] = mma32(a, xl[0][s], acc[j][0]);
+              acc[j][0] = mma32(a, xf[0][s], acc[j][0]);
+              acc[j][1] = mma32(a, xl[1][s], acc[j][1]);
+              acc[j][1] = mma32(a, xf[1][s], acc[j][1]);
+            } else {
+              acc[j][0] = mma32(a, xf[0][s], acc[j][0]);
+              acc[j][1] = mma32(a, xf[1][s], acc[j][1]);
+            }
           }
         }
         if (pair) {
 #pragma unroll
-          for (int pb = 0; pb < 2; ++pb)
+          for (int pb = 0; pb < PB; ++pb)
             store_pair<T>(out + orow[pb] + cbase, acc[0][pb], acc[1][pb], g, live[pb]);
           cb += 2;
           cbase += 32;
@@ -437,7 +491,7 @@ rowgemm_kernel(GemmParams p) {
           continue;
         }
 #pragma unroll
-        for (int pb = 0; pb < 2; ++pb) {
+        for (int pb = 0; pb < PB; ++pb) {
           if (!live[pb]) continue;
           const int c = cbase + 4 * g;
           if constexpr (MUL && sizeof(T) != 2) {
@@ -464,34 +518,41 @@ rowgemm_kernel(GemmParams p) {
   }
 }
 
-template <typename T, int KSTEPS, bool MUL>
+template <typename T, int KSTEPS, bool MUL, bool SPLIT = false>
 hipError_t launch_pass_m(GemmParams& p, size_t lds, hipStream_t s) {
-  constexpr int WAVES = waves_for<KSTEPS>();
-  const int64_t tiles = (p.npos + PW * WAVES - 1) / (PW * WAVES);
+  constexpr int WAVES = SPLIT ? 8 : waves_for<KSTEPS>();
+  constexpr int PWV = PW;
+  const int64_t tiles = (p.npos + PWV * WAVES - 1) / (PWV * WAVES);
   if (tiles > (int64_t)INT32_MAX) return hipErrorInvalidValue;
   p.ntiles = (int)tiles;
   const int grid = (int)std::min<int64_t>(tiles, 256);  // persistent: one per CU
   hipError_t e = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&rowgemm_kernel<T, KSTEPS, WAVES, MUL>),
+      reinterpret_cast<const void*>(&rowgemm_kernel<T, KSTEPS, WAVES, MUL, SPLIT>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((rowgemm_kernel<T, KSTEPS, WAVES, MUL>), dim3(grid), dim3(WAVES * 64), lds,
+  hipLaunchKernelGGL((rowgemm_kernel<T, KSTEPS, WAVES, MUL, SPLIT>), dim3(grid), dim3(WAVES * 64), lds,
                      s, p);
   return hipGetLastError();
 }
 
 template <typename T, int KSTEPS>
 hipError_t launch_pass(GemmParams& p, size_t lds, hipStream_t s) {
-  return p.mode == 2 ? launch_pass_m<T, KSTEPS, true>(p, lds, s)
-                     : launch_pass_m<T, KSTEPS, false>(p, lds, s);
+  if (p.mode == 2) return launch_pass_m<T, KSTEPS, true>(p, lds, s);
+  // split operands up to 160 input channels (beyond, their registers spill)
+  if (p.mode == 0 && sizeof(T) == 2 && KSTEPS <= 5)
+    return launch_pass_m<T, KSTEPS, false, true>(p, lds, s);
+  return launch_pass_m<T, KSTEPS, false>(p, lds, s);
 }
 
 template <typename T>
 hipError_t launch_gemm(GemmParams& p, hipStream_t s) {
   // LDS per output column: its weight row and its constant
   const size_t row_bytes = (size_t)(p.K + PAD) * sizeof(T) + sizeof(float);
-  // operand mode: the per-wave staging tiles (at most 16 waves)
-  const size_t stage = p.mode == 2 ? (size_t)16 * 32 * OS * sizeof(T) : 0;
+  // operand mode: the per-wave staging tiles (at most 16 waves); bf16
+  // projection: gamma and beta
+  const size_t stage = p.mode == 2 ? (size_t)16 * 32 * OS * sizeof(T)
+                       : (p.mode == 0 && sizeof(T) == 2 && p.K <= 160) ? (size_t)2 * p.K * sizeof(T)
+                                                                      : 0;
   int per_pass = (int)((kLdsBudget - stage) / row_bytes) / 32 * 32;  // whole block pairs
   const int ncols_pad = (p.ncols + 15) / 16 * 16;
   per_pass = std::min(per_pass, ncols_pad);

@@ -85,8 +85,12 @@ const char* evo_last_error(void);
  *             (needed by evo_attn_bwd); NULL = not written.
  *   workspace device scratch of evo_attn_fwd_workspace_bytes(...) bytes,
  *             16-byte aligned, owned by the caller; required when bias or
- *             key_mask is given (it holds the bias as fp32 with the mask
- *             folded in), ignored otherwise.  Contents on entry are ignored.
+ *             key_mask is given, ignored otherwise.  It holds the bias in the
+ *             kernel's tile order with the shared mask and the tile padding
+ *             folded in as -inf: fp32 for EVO_FP32, fp16 for EVO_BF16 (which
+ *             holds every bf16 value of magnitude 2^-14 .. 65504 exactly;
+ *             finite bias values beyond +-65504 are clamped to it).  Contents
+ *             on entry are ignored.
  *
  * A query whose keys are all masked gets Out = 0 and lse = -inf.
  */
@@ -222,7 +226,7 @@ size_t tri_attn_workspace_bytes(evo_dtype_t dtype, int64_t N, int64_t CZ,
  *   out           [N,N,CZ] dtype, the module's update (no residual add).
  *   workspace     caller-owned device scratch of tri_attn_workspace_bytes(...)
  *                 bytes (holds the projected Q, K, V, gate, bias, the
- *                 attention output and the forward's fp32 bias;
+ *                 attention output and the forward's prepared bias;
  *                 O(N^2 * H * C)).
  * Other arguments as in tri_attn_project / tri_attn_out_project.
  */
