@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libevoattn.so")
 SOURCES = ["evo_api.cpp", "attn_fwd.hip", "attn_bwd.hip", "tri_project.hip",
            "tri_module_bwd.hip", "tri_mul.hip", "transition.hip", "opm.hip",
-           "transition_bwd.hip"]
+           "transition_bwd.hip", "measure.hip"]
 ARCH = "gfx950"
 
 

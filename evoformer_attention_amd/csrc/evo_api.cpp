@@ -190,6 +190,21 @@ evo_status_t evo_attn_fwd_noalloc(evo_dtype_t dtype, int64_t B, int64_t R,
   }
 }
 
+evo_status_t evo_probe_issue_rate(int kind, int waves_per_simd, int iters, float* out,
+                                  void* stream) {
+  try {
+    if (kind < 0 || kind > 2) return fail(EVO_EINVAL, "evo_probe_issue_rate: kind %d", kind);
+    if (waves_per_simd < 1 || waves_per_simd > 8 || iters < 1)
+      return fail(EVO_EINVAL, "evo_probe_issue_rate: waves_per_simd %d, iters %d",
+                  waves_per_simd, iters);
+    REQUIRE_PTR(out);
+    return from_hip(evo::launch_probe(kind, waves_per_simd, iters, out, (hipStream_t)stream),
+                    "evo_probe_issue_rate");
+  } catch (...) {
+    return fail(EVO_EINTERNAL, "evo_probe_issue_rate: internal error");
+  }
+}
+
 size_t evo_attn_fwd_workspace_bytes(evo_dtype_t dtype, int64_t B, int64_t R,
                                     int64_t N, int64_t H, int64_t C) {
   const std::string saved = g_last_error;

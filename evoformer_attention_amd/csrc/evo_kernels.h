@@ -176,6 +176,7 @@ hipError_t launch_attn_fwd(const AttnFwdArgs& a, hipStream_t s);
 // The library's static forward scratch on the current device (its address,
 // looked up once per device) and its size in bytes.
 hipError_t fwd_static_scratch(void** ptr, size_t* bytes);
+hipError_t launch_probe(int kind, int waves_per_simd, int iters, float* out, hipStream_t s);
 size_t attn_bwd_workspace(int dtype, int64_t B, int64_t R, int64_t N,
                           int64_t H);
 hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t s);

@@ -13,7 +13,7 @@ import os
 import torch
 
 __all__ = ["EvoAttnError", "lib", "evo_abi_version", "evo_attn_fwd",
-           "evo_attn_fwd_noalloc",
+           "evo_attn_fwd_noalloc", "evo_probe_issue_rate",
            "evo_attn_bwd", "evo_attn_bwd_workspace_bytes",
            "evo_attn_fwd_workspace_bytes", "tri_attn_project",
            "tri_attn_out_project", "tri_attn_module_fwd",
@@ -49,6 +49,7 @@ EXPORTS = {
     "evo_attn_fwd_noalloc": (_I, [_I, _I64, _I64, _I64, _I64, _I64, _P, _P, _P,
                                   _P, _P, _I64, _P, _P, _P, _P]),
     "evo_attn_fwd_workspace_bytes": (_SZ, [_I, _I64, _I64, _I64, _I64, _I64]),
+    "evo_probe_issue_rate": (_I, [_I, _I, _I, _P, _P]),
     "evo_attn_bwd_workspace_bytes": (_SZ, [_I, _I64, _I64, _I64, _I64, _I64]),
     "evo_attn_bwd": (_I, [_I, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P,
                           _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
@@ -138,20 +139,52 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _dev_tensor(name, t, dtype=None, shape=None):
+def _check_meta(name, t, dtype=None, shape=None):
     if t is None:
-        return None
-    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        return
+    if not isinstance(t, torch.Tensor):
         raise EvoAttnError("binding", EVO_EINVAL, f"{name} must be a GPU tensor")
-    if not t.is_contiguous():
-        raise EvoAttnError("binding", EVO_EINVAL, f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
         raise EvoAttnError("binding", EVO_EINVAL,
                            f"{name} has dtype {t.dtype}, expected {dtype}")
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise EvoAttnError("binding", EVO_EINVAL,
                            f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _check_dev(name, t):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise EvoAttnError("binding", EVO_EINVAL, f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise EvoAttnError("binding", EVO_EINVAL, f"{name} must be contiguous")
+
+
+def _dev_tensor(name, t, dtype=None, shape=None):
+    """Check one tensor argument: dtype and shape, then device and layout."""
+    _check_meta(name, t, dtype, shape)
+    _check_dev(name, t)
     return t
+
+
+def _dev_tensors(specs):
+    """Check (name, tensor, dtype, shape) arguments: every dtype and shape
+    first, so that a mismatch is reported as such whatever the devices, then
+    every device and layout."""
+    for name, t, dtype, shape in specs:
+        _check_meta(name, t, dtype, shape)
+    for name, t, _, _ in specs:
+        _check_dev(name, t)
+
+
+def _pair_rep(name, z):
+    """z [N, N, CZ] -> (N, CZ)."""
+    if not isinstance(z, torch.Tensor) or z.dim() != 3 or z.shape[0] != z.shape[1]:
+        raise EvoAttnError("binding", EVO_EINVAL,
+                           f"{name} must be [N, N, c] (got "
+                           f"{tuple(z.shape) if isinstance(z, torch.Tensor) else type(z)})")
+    return z.shape[0], z.shape[2]
 
 
 def evo_abi_version():
@@ -231,6 +264,18 @@ def evo_attn_fwd_noalloc(q, k, v, gate=None, key_mask=None, bias=None, out=None,
     return (out, lse) if lse is not None else out
 
 
+def evo_probe_issue_rate(kind, waves_per_simd, iters, out):
+    """Launch the library's issue-rate probe (kind 0 exp, 1 fma, 2 bf16
+    MFMA) on torch's current stream; `out` is a float32 device tensor of at
+    least 65536 * waves_per_simd elements."""
+    _dev_tensor("out", out, torch.float32)
+    if out.numel() < 65536 * waves_per_simd:
+        raise EvoAttnError("binding", EVO_EINVAL, "out too small")
+    st = lib().evo_probe_issue_rate(int(kind), int(waves_per_simd), int(iters), _ptr(out),
+                                    _stream(out.device))
+    _check("evo_probe_issue_rate", st)
+
+
 def evo_attn_bwd_workspace_bytes(dtype, B, R, N, H, C):
     code = EVO_BF16 if dtype == torch.bfloat16 else EVO_FP32
     return lib().evo_attn_bwd_workspace_bytes(code, B, R, N, H, C)
@@ -252,6 +297,9 @@ def evo_attn_bwd(q, k, v, gate, key_mask, bias, out, lse, dout,
     mask_rows = 0
     if key_mask is not None:
         _dev_tensor("key_mask", key_mask, torch.uint8)
+        if key_mask.dim() != 3 or key_mask.shape[0] != B or key_mask.shape[2] != N:
+            raise EvoAttnError("binding", EVO_EINVAL,
+                               f"key_mask has shape {tuple(key_mask.shape)}")
         mask_rows = key_mask.shape[1]
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
     dg = torch.empty_like(q) if gate is not None else None
@@ -274,12 +322,18 @@ def tri_attn_project(z, ln_w, ln_b, eps, w_q, w_k, w_v, w_g, b_g, w_bias, H,
                      C, ending):
     """LayerNorm + projections.  Returns q, k, v, g [1,N,N,H,C] and bias
     [1,H,N,N] in line layout."""
-    _dev_tensor("z", z)
-    N, _, CZ = z.shape
+    N, CZ = _pair_rep("z", z)
     dt = z.dtype
-    for name, t in (("ln_w", ln_w), ("ln_b", ln_b), ("w_q", w_q), ("w_k", w_k),
-                    ("w_v", w_v), ("w_g", w_g), ("w_bias", w_bias), ("b_g", b_g)):
-        _dev_tensor(name, t, dt)
+    HC = H * C
+    _dev_tensors([("z", z, None, None),
+                  ("ln_w", ln_w, dt, (CZ,)),
+                  ("ln_b", ln_b, dt, (CZ,)),
+                  ("w_q", w_q, dt, (HC, CZ)),
+                  ("w_k", w_k, dt, (HC, CZ)),
+                  ("w_v", w_v, dt, (HC, CZ)),
+                  ("w_g", w_g, dt, (HC, CZ)),
+                  ("w_bias", w_bias, dt, (H, CZ)),
+                  ("b_g", b_g, dt, (HC,))])
     q = torch.empty((1, N, N, H, C), dtype=dt, device=z.device)
     k, v, g = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
     bias = torch.empty((1, H, N, N), dtype=dt, device=z.device)
@@ -295,9 +349,11 @@ def tri_attn_project(z, ln_w, ln_b, eps, w_q, w_k, w_v, w_g, b_g, w_bias, H,
 def tri_attn_out_project(o, w_o, b_o, CZ, ending):
     """Output projection of o [1,N,N,H,C] (line layout) -> [N,N,CZ]."""
     _dev_tensor("o", o)
+    if o.dim() != 5 or o.shape[0] != 1 or o.shape[1] != o.shape[2]:
+        raise EvoAttnError("binding", EVO_EINVAL, f"o must be [1, N, N, H, C] (got {tuple(o.shape)})")
     _, N, _, H, C = o.shape
-    _dev_tensor("w_o", w_o, o.dtype)
-    _dev_tensor("b_o", b_o, o.dtype)
+    _dev_tensor("w_o", w_o, o.dtype, (CZ, H * C))
+    _dev_tensor("b_o", b_o, o.dtype, (CZ,))
     out = torch.empty((N, N, CZ), dtype=o.dtype, device=o.device)
     st = lib().tri_attn_out_project(_dtype_code(o), N, CZ, H, C, int(ending),
                                     _ptr(o), _ptr(w_o), _ptr(b_o), _ptr(out),
@@ -315,14 +371,21 @@ def tri_attn_module_fwd(z, residue_mask, ln_w, ln_b, eps, w_q, w_k, w_v, w_g,
                         b_g, w_bias, w_o, b_o, H, C, ending, workspace=None,
                         out=None):
     """Whole triangle-attention module forward -> [N,N,CZ] update."""
-    _dev_tensor("z", z)
-    N, _, CZ = z.shape
+    N, CZ = _pair_rep("z", z)
     dt = z.dtype
-    for name, t in (("ln_w", ln_w), ("ln_b", ln_b), ("w_q", w_q), ("w_k", w_k),
-                    ("w_v", w_v), ("w_g", w_g), ("w_bias", w_bias),
-                    ("w_o", w_o), ("b_g", b_g), ("b_o", b_o)):
-        _dev_tensor(name, t, dt)
-    _dev_tensor("residue_mask", residue_mask, torch.uint8)
+    HC = H * C
+    _dev_tensors([("z", z, None, None),
+                  ("ln_w", ln_w, dt, (CZ,)),
+                  ("ln_b", ln_b, dt, (CZ,)),
+                  ("w_q", w_q, dt, (HC, CZ)),
+                  ("w_k", w_k, dt, (HC, CZ)),
+                  ("w_v", w_v, dt, (HC, CZ)),
+                  ("w_g", w_g, dt, (HC, CZ)),
+                  ("w_bias", w_bias, dt, (H, CZ)),
+                  ("w_o", w_o, dt, (CZ, HC)),
+                  ("b_g", b_g, dt, (HC,)),
+                  ("b_o", b_o, dt, (CZ,)),
+                  ("residue_mask", residue_mask, torch.uint8, (N,))])
     need = tri_attn_workspace_bytes(dt, N, CZ, H, C)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=z.device)
@@ -362,11 +425,15 @@ def _workspace(need, device, workspace):
 def tri_attn_out_project_bwd(o, w_o, dout, ending, workspace=None):
     """Backward of tri_attn_out_project -> (d_o, dw_o fp32, db_o fp32)."""
     _dev_tensor("o", o)
+    if o.dim() != 5 or o.shape[0] != 1 or o.shape[1] != o.shape[2]:
+        raise EvoAttnError("binding", EVO_EINVAL, f"o must be [1, N, N, H, C] (got {tuple(o.shape)})")
     _, N, _, H, C = o.shape
     dt = o.dtype
-    _dev_tensor("w_o", w_o, dt)
-    _dev_tensor("dout", dout, dt)
+    if not isinstance(w_o, torch.Tensor) or w_o.dim() != 2:
+        raise EvoAttnError("binding", EVO_EINVAL, "w_o must be [CZ, H*C]")
     CZ = w_o.shape[0]
+    _dev_tensor("w_o", w_o, dt, (CZ, H * C))
+    _dev_tensor("dout", dout, dt, (N, N, CZ))
     workspace = _workspace(tri_attn_proj_bwd_workspace_bytes(dt, N, CZ, H, C),
                            o.device, workspace)
     d_o = torch.empty_like(o)
@@ -395,14 +462,22 @@ def tri_attn_project_bwd(z, ln_w, ln_b, eps, w_q, w_k, w_v, w_g, w_bias, dq,
                          dk, dv, dg, dbias, H, C, ending, workspace=None):
     """Backward of tri_attn_project -> dict with dz and the fp32 parameter
     gradients (dln_w, dln_b, dw_q, dw_k, dw_v, dw_g, db_g, dw_bias)."""
-    _dev_tensor("z", z)
-    N, _, CZ = z.shape
+    N, CZ = _pair_rep("z", z)
     dt = z.dtype
-    for name, t in (("ln_w", ln_w), ("ln_b", ln_b), ("w_q", w_q), ("w_k", w_k),
-                    ("w_v", w_v), ("w_g", w_g), ("w_bias", w_bias), ("dq", dq),
-                    ("dk", dk), ("dv", dv), ("dg", dg)):
-        _dev_tensor(name, t, dt)
-    _dev_tensor("dbias", dbias, torch.float32)
+    HC = H * C
+    _dev_tensors([("z", z, None, None),
+                  ("ln_w", ln_w, dt, (CZ,)),
+                  ("ln_b", ln_b, dt, (CZ,)),
+                  ("w_q", w_q, dt, (HC, CZ)),
+                  ("w_k", w_k, dt, (HC, CZ)),
+                  ("w_v", w_v, dt, (HC, CZ)),
+                  ("w_g", w_g, dt, (HC, CZ)),
+                  ("w_bias", w_bias, dt, (H, CZ)),
+                  ("dq", dq, dt, (1, N, N, H, C)),
+                  ("dk", dk, dt, (1, N, N, H, C)),
+                  ("dv", dv, dt, (1, N, N, H, C)),
+                  ("dg", dg, dt, (1, N, N, H, C)),
+                  ("dbias", dbias, torch.float32, (1, H, N, N))])
     workspace = _workspace(tri_attn_proj_bwd_workspace_bytes(dt, N, CZ, H, C),
                            z.device, workspace)
     res = _param_grads(CZ, H, C, z.device)
@@ -421,14 +496,21 @@ def tri_attn_module_bwd(z, residue_mask, ln_w, ln_b, eps, w_q, w_k, w_v, w_g,
                         b_g, w_bias, w_o, dout, H, C, ending, workspace=None):
     """Gradients of the module forward -> dict with dz and the fp32
     parameter gradients (those of tri_attn_project_bwd plus dw_o, db_o)."""
-    _dev_tensor("z", z)
-    N, _, CZ = z.shape
+    N, CZ = _pair_rep("z", z)
     dt = z.dtype
-    for name, t in (("ln_w", ln_w), ("ln_b", ln_b), ("w_q", w_q), ("w_k", w_k),
-                    ("w_v", w_v), ("w_g", w_g), ("b_g", b_g),
-                    ("w_bias", w_bias), ("w_o", w_o), ("dout", dout)):
-        _dev_tensor(name, t, dt)
-    _dev_tensor("residue_mask", residue_mask, torch.uint8)
+    HC = H * C
+    _dev_tensors([("z", z, None, None),
+                  ("ln_w", ln_w, dt, (CZ,)),
+                  ("ln_b", ln_b, dt, (CZ,)),
+                  ("w_q", w_q, dt, (HC, CZ)),
+                  ("w_k", w_k, dt, (HC, CZ)),
+                  ("w_v", w_v, dt, (HC, CZ)),
+                  ("w_g", w_g, dt, (HC, CZ)),
+                  ("b_g", b_g, dt, (HC,)),
+                  ("w_bias", w_bias, dt, (H, CZ)),
+                  ("w_o", w_o, dt, (CZ, HC)),
+                  ("dout", dout, dt, (N, N, CZ)),
+                  ("residue_mask", residue_mask, torch.uint8, (N,))])
     workspace = _workspace(tri_attn_bwd_workspace_bytes(dt, N, CZ, H, C),
                            z.device, workspace)
     res = _param_grads(CZ, H, C, z.device)
@@ -454,14 +536,19 @@ def tri_mul_workspace_bytes(dtype, N, CZ, C):
 def tri_mul_fwd(z, residue_mask, ln_w, ln_b, eps, w_a, w_b, w_o, b_o,
                 outgoing=True, workspace=None, out=None):
     """Triangular multiplicative update -> [N,N,CZ] update."""
-    _dev_tensor("z", z)
-    N, _, CZ = z.shape
+    N, CZ = _pair_rep("z", z)
     dt = z.dtype
-    for name, t in (("ln_w", ln_w), ("ln_b", ln_b), ("w_a", w_a), ("w_b", w_b),
-                    ("w_o", w_o), ("b_o", b_o)):
-        _dev_tensor(name, t, dt)
-    _dev_tensor("residue_mask", residue_mask, torch.uint8)
+    if not isinstance(w_a, torch.Tensor) or w_a.dim() != 2:
+        raise EvoAttnError("binding", EVO_EINVAL, "w_a must be [C, CZ]")
     C = w_a.shape[0]
+    _dev_tensors([("z", z, None, None),
+                  ("ln_w", ln_w, dt, (CZ,)),
+                  ("ln_b", ln_b, dt, (CZ,)),
+                  ("w_a", w_a, dt, (C, CZ)),
+                  ("w_b", w_b, dt, (C, CZ)),
+                  ("w_o", w_o, dt, (CZ, C)),
+                  ("b_o", b_o, dt, (CZ,)),
+                  ("residue_mask", residue_mask, torch.uint8, (N,))])
     workspace = _workspace(tri_mul_workspace_bytes(dt, N, CZ, C), z.device, workspace)
     if out is None:
         out = torch.empty((N, N, CZ), dtype=dt, device=z.device)
@@ -482,13 +569,17 @@ def pair_transition_workspace_bytes(dtype, N, CZ, HID):
 def pair_transition_fwd(z, ln_w, ln_b, eps, w_a, w_b, w_o, out=None,
                         workspace=None):
     """LayerNorm + SwiGLU transition of the pair representation -> [N,N,CZ]."""
-    _dev_tensor("z", z)
-    N, _, CZ = z.shape
+    N, CZ = _pair_rep("z", z)
     dt = z.dtype
-    for name, t in (("ln_w", ln_w), ("ln_b", ln_b), ("w_a", w_a), ("w_b", w_b),
-                    ("w_o", w_o)):
-        _dev_tensor(name, t, dt)
+    if not isinstance(w_a, torch.Tensor) or w_a.dim() != 2:
+        raise EvoAttnError("binding", EVO_EINVAL, "w_a must be [HID, CZ]")
     HID = w_a.shape[0]
+    _dev_tensors([("z", z, None, None),
+                  ("ln_w", ln_w, dt, (CZ,)),
+                  ("ln_b", ln_b, dt, (CZ,)),
+                  ("w_a", w_a, dt, (HID, CZ)),
+                  ("w_b", w_b, dt, (HID, CZ)),
+                  ("w_o", w_o, dt, (CZ, HID))])
     workspace = _workspace(pair_transition_workspace_bytes(dt, N, CZ, HID),
                            z.device, workspace)
     if out is None:
@@ -510,13 +601,21 @@ def outer_product_mean_workspace_bytes(dtype, S, N, CM, C, CZ):
 def outer_product_mean_fwd(m, ln_w, ln_b, eps, w_a, w_b, w_o, b_o, out=None,
                            workspace=None):
     """Outer product mean of the MSA representation m [S,N,CM] -> [N,N,CZ]."""
-    _dev_tensor("m", m)
+    if not isinstance(m, torch.Tensor) or m.dim() != 3:
+        raise EvoAttnError("binding", EVO_EINVAL, "m must be [S, N, CM]")
     S, N, CM = m.shape
     dt = m.dtype
-    for name, t in (("ln_w", ln_w), ("ln_b", ln_b), ("w_a", w_a), ("w_b", w_b),
-                    ("w_o", w_o), ("b_o", b_o)):
-        _dev_tensor(name, t, dt)
+    for name, t in (("w_a", w_a), ("w_o", w_o)):
+        if not isinstance(t, torch.Tensor) or t.dim() != 2:
+            raise EvoAttnError("binding", EVO_EINVAL, f"{name} must be a matrix")
     C, CZ = w_a.shape[0], w_o.shape[0]
+    _dev_tensors([("m", m, None, None),
+                  ("ln_w", ln_w, dt, (CM,)),
+                  ("ln_b", ln_b, dt, (CM,)),
+                  ("w_a", w_a, dt, (C, CM)),
+                  ("w_b", w_b, dt, (C, CM)),
+                  ("w_o", w_o, dt, (CZ, C * C)),
+                  ("b_o", b_o, dt, (CZ,))])
     workspace = _workspace(outer_product_mean_workspace_bytes(dt, S, N, CM, C, CZ),
                            m.device, workspace)
     if out is None:
@@ -538,14 +637,18 @@ def pair_transition_bwd_workspace_bytes(dtype, N, CZ, HID):
 def pair_transition_bwd(z, ln_w, ln_b, eps, w_a, w_b, w_o, dout, workspace=None):
     """Backward of pair_transition_fwd -> dict of dz (dtype) and the fp32
     parameter gradients dln_w, dln_b, dw_a, dw_b, dw_o."""
-    _dev_tensor("z", z)
-    N, _, CZ = z.shape
+    N, CZ = _pair_rep("z", z)
     dt = z.dtype
-    for name, t in (("ln_w", ln_w), ("ln_b", ln_b), ("w_a", w_a), ("w_b", w_b),
-                    ("w_o", w_o)):
-        _dev_tensor(name, t, dt)
-    _dev_tensor("dout", dout, dt, (N, N, CZ))
+    if not isinstance(w_a, torch.Tensor) or w_a.dim() != 2:
+        raise EvoAttnError("binding", EVO_EINVAL, "w_a must be [HID, CZ]")
     HID = w_a.shape[0]
+    _dev_tensors([("z", z, None, None),
+                  ("ln_w", ln_w, dt, (CZ,)),
+                  ("ln_b", ln_b, dt, (CZ,)),
+                  ("w_a", w_a, dt, (HID, CZ)),
+                  ("w_b", w_b, dt, (HID, CZ)),
+                  ("w_o", w_o, dt, (CZ, HID)),
+                  ("dout", dout, dt, (N, N, CZ))])
     workspace = _workspace(pair_transition_bwd_workspace_bytes(dt, N, CZ, HID),
                            z.device, workspace)
     res = {"dz": torch.empty_like(z)}

@@ -125,6 +125,19 @@ evo_status_t evo_attn_fwd_noalloc(evo_dtype_t dtype, int64_t B, int64_t R,
                                   const void* bias, void* out, float* lse,
                                   void* stream);
 
+/*
+ * evo_probe_issue_rate -- a measurement helper, not part of the attention
+ * path: launches 256 * waves_per_simd workgroups of 256 threads that each
+ * run `iters` iterations of 8 independent instructions of one kind (0:
+ * v_exp_f32, 1: v_fma_f32, 2: v_mfma_f32_16x16x32_bf16) and write one
+ * float per thread to `out` (device, 256 * 256 * waves_per_simd floats,
+ * caller-owned).  Timing the launch gives that instruction's issue interval
+ * per SIMD, from which the benchmark derives the softmax's ceiling on the
+ * matrix-core fraction.  waves_per_simd in 1..8, iters >= 1.
+ */
+evo_status_t evo_probe_issue_rate(int kind, int waves_per_simd, int iters, float* out,
+                                  void* stream);
+
 /* Bytes of device workspace evo_attn_fwd needs when a bias or mask is given
  * (O(B * H * N^2); 0 on a problem evo_attn_fwd would reject). */
 size_t evo_attn_fwd_workspace_bytes(evo_dtype_t dtype, int64_t B, int64_t R,

@@ -300,3 +300,82 @@ def test_transition_bwd_validation():
     args[19] = 1 << 34
     args[3] = 192
     assert L.pair_transition_bwd(*args) == ops.EVO_ENOTSUP and "HID=192" in err()
+
+
+def _bf(*shape):
+    return torch.zeros(shape, dtype=torch.bfloat16)
+
+
+def _module_args(N=8, CZ=32, H=2, C=32):
+    HC = H * C
+    return dict(z=_bf(N, N, CZ), ln_w=_bf(CZ), ln_b=_bf(CZ), eps=1e-5, w_q=_bf(HC, CZ),
+                w_k=_bf(HC, CZ), w_v=_bf(HC, CZ), w_g=_bf(HC, CZ), b_g=_bf(HC),
+                w_bias=_bf(H, CZ), w_o=_bf(CZ, HC), b_o=_bf(CZ))
+
+
+@pytest.mark.parametrize("call,bad,needle", [
+    # tri_attn_project: every weight and LayerNorm vector, and z itself
+    ("project", dict(z=_bf(8, 7, 32)), "z must be [N, N, c]"),
+    ("project", dict(ln_w=_bf(31)), "ln_w has shape"),
+    ("project", dict(ln_b=_bf(33)), "ln_b has shape"),
+    ("project", dict(w_q=_bf(64, 31)), "w_q has shape"),
+    ("project", dict(w_k=_bf(63, 32)), "w_k has shape"),
+    ("project", dict(w_v=_bf(64, 33)), "w_v has shape"),
+    ("project", dict(w_g=_bf(32, 32)), "w_g has shape"),
+    ("project", dict(b_g=_bf(63)), "b_g has shape"),
+    ("project", dict(w_bias=_bf(3, 32)), "w_bias has shape"),
+    ("module", dict(w_o=_bf(32, 63)), "w_o has shape"),
+    ("module", dict(b_o=_bf(31)), "b_o has shape"),
+    ("module", dict(residue_mask=torch.ones(7, dtype=torch.uint8)), "residue_mask has shape"),
+])
+def test_module_bindings_check_shapes(call, bad, needle):
+    """A mismatched weight, vector or mask is rejected by the binding with
+    EVO_EINVAL before any pointer reaches the library (tensors here are
+    host tensors: the shape check comes first)."""
+    a = _module_args()
+    mask = bad.pop("residue_mask", None)
+    a.update(bad)
+    with pytest.raises(ops.EvoAttnError) as ei:
+        if call == "project":
+            ops.tri_attn_project(a["z"], a["ln_w"], a["ln_b"], a["eps"], a["w_q"], a["w_k"],
+                                 a["w_v"], a["w_g"], a["b_g"], a["w_bias"], 2, 32, False)
+        else:
+            ops.tri_attn_module_fwd(a["z"], mask, a["ln_w"], a["ln_b"], a["eps"], a["w_q"],
+                                    a["w_k"], a["w_v"], a["w_g"], a["b_g"], a["w_bias"],
+                                    a["w_o"], a["b_o"], 2, 32, False)
+    assert ei.value.status == ops.EVO_EINVAL
+    assert needle in str(ei.value), str(ei.value)
+
+
+@pytest.mark.parametrize("fn,args,needle", [
+    ("tri_mul_fwd", lambda: (_bf(8, 8, 32), None, _bf(32), _bf(32), 1e-5, _bf(16, 32),
+                             _bf(16, 31), _bf(32, 16), _bf(32)), "w_b has shape"),
+    ("tri_mul_fwd", lambda: (_bf(8, 8, 32), None, _bf(32), _bf(32), 1e-5, _bf(16, 32),
+                             _bf(16, 32), _bf(32, 15), _bf(32)), "w_o has shape"),
+    ("tri_mul_fwd", lambda: (_bf(8, 8, 32), torch.ones(9, dtype=torch.uint8), _bf(32),
+                             _bf(32), 1e-5, _bf(16, 32), _bf(16, 32), _bf(32, 16), _bf(32)),
+     "residue_mask has shape"),
+    ("pair_transition_fwd", lambda: (_bf(8, 8, 32), _bf(32), _bf(32), 1e-5, _bf(64, 32),
+                                     _bf(64, 32), _bf(32, 63)), "w_o has shape"),
+    ("pair_transition_fwd", lambda: (_bf(8, 8, 32), _bf(31), _bf(32), 1e-5, _bf(64, 32),
+                                     _bf(64, 32), _bf(32, 64)), "ln_w has shape"),
+    ("pair_transition_bwd", lambda: (_bf(8, 8, 32), _bf(32), _bf(32), 1e-5, _bf(64, 32),
+                                     _bf(65, 32), _bf(32, 64), _bf(8, 8, 32)), "w_b has shape"),
+    ("pair_transition_bwd", lambda: (_bf(8, 8, 32), _bf(32), _bf(32), 1e-5, _bf(64, 32),
+                                     _bf(64, 32), _bf(32, 64), _bf(8, 7, 32)), "dout has shape"),
+    ("outer_product_mean_fwd", lambda: (_bf(4, 8, 16), _bf(16), _bf(16), 1e-5, _bf(8, 16),
+                                        _bf(8, 16), _bf(32, 63), _bf(32)), "w_o has shape"),
+    ("outer_product_mean_fwd", lambda: (_bf(4, 8, 16), _bf(15), _bf(16), 1e-5, _bf(8, 16),
+                                        _bf(8, 16), _bf(32, 64), _bf(32)), "ln_w has shape"),
+])
+def test_pair_op_bindings_check_shapes(fn, args, needle):
+    with pytest.raises(ops.EvoAttnError) as ei:
+        getattr(ops, fn)(*args())
+    assert ei.value.status == ops.EVO_EINVAL
+    assert needle in str(ei.value), str(ei.value)
+
+
+def test_probe_validation():
+    assert L.evo_probe_issue_rate(3, 1, 1, FAKE, None) == ops.EVO_EINVAL
+    assert L.evo_probe_issue_rate(0, 9, 1, FAKE, None) == ops.EVO_EINVAL
+    assert L.evo_probe_issue_rate(0, 1, 1, None, None) == ops.EVO_EINVAL
