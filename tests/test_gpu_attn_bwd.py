@@ -164,3 +164,36 @@ def test_tri_start_512_fwd_bwd_sampled():
     ref = O.dbias_query_rows(oq, ok, ov, og, None, ob, dout, 0, picks)
     got = np.stack([np64(db[0, h, qi]) for h, qi in picks])
     compare("dbias rows", got, ref, "bf16", stored="fp32")
+
+
+def nan_tail(t, pad=1 << 18):
+    """`t` on the GPU at the start of a larger allocation whose remaining
+    elements are NaN, so that a read past the tensor's end shows up."""
+    if t is None:
+        return None
+    buf = torch.full((t.numel() + pad,), float("nan"), dtype=t.dtype, device="cuda")
+    view = buf[: t.numel()].view(t.shape)
+    view.copy_(t.to("cuda"))
+    return view
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_bwd_padding_reads_nothing_past_the_tensors(dtype):
+    """Query and key rows past N in the last tiles of the last line read
+    zeros, not the memory after the inputs (here NaN): N = 100."""
+    log(f"case bwd nan tail {dtype}")
+    d = synth.rand_core(1, 3, 100, 2, 32, dtype, seed=23, dout=True, mask="random")
+    q, k, v, g, b, do = (nan_tail(d[n]) for n in ("q", "k", "v", "gate", "bias", "dout"))
+    m = dev(d["mask"])
+    out, lse = ops.evo_attn_fwd(q, k, v, g, m, b, want_lse=True)
+    out, lse = nan_tail(out), nan_tail(lse)
+    grads = ops.evo_attn_bwd(q, k, v, g, m, b, out, lse, do)
+    torch.cuda.synchronize()
+    ref = oracle_bwd(d)
+    for name, gt, r in zip(("dq", "dk", "dv", "dgate", "dbias"), grads, ref):
+        assert torch.isfinite(gt).all(), name
+        if name == "dbias":
+            bound = dbias_rounding_bound(d) if dtype == "bf16" else None
+            compare(name, np64(gt), r, dtype, stored="fp32", bound=bound)
+        else:
+            compare(name, np64(gt), r, dtype)

@@ -199,3 +199,30 @@ def test_logits_rising_along_keys(dtype, profile):
     out, lse = run_gpu(d)
     assert torch.isfinite(out).all() and torch.isfinite(lse).all()
     check(d, dtype)
+
+
+def nan_tail(t, pad=1 << 18):
+    """`t` on the GPU at the start of a larger allocation whose remaining
+    elements are NaN, so that a read past the tensor's end shows up."""
+    if t is None:
+        return None
+    buf = torch.full((t.numel() + pad,), float("nan"), dtype=t.dtype, device="cuda")
+    view = buf[: t.numel()].view(t.shape)
+    view.copy_(t.to("cuda"))
+    return view
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_padding_keys_read_nothing_past_the_tensors(dtype):
+    """Keys past N in the last key tile of the last line read zeros, not the
+    memory after K and V (here NaN): N = 100 leaves 28 padding keys."""
+    log(f"case fwd nan tail {dtype}")
+    d = synth.rand_core(1, 3, 100, 2, 32, dtype, seed=21, mask="random")
+    q, k, v, g = (nan_tail(d[n]) for n in ("q", "k", "v", "gate"))
+    out, lse = ops.evo_attn_fwd(q, k, v, g, dev(d["mask"]), nan_tail(d["bias"]),
+                                want_lse=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    ref, ref_lse = run_oracle(d)
+    compare("out", np64(out), ref, dtype)
+    compare("lse", lse.cpu().numpy().astype(np.float64), ref_lse, dtype, stored="fp32")
