@@ -896,11 +896,13 @@ def attention_bench(a, name, ceiling):
                 mark()
                 return out, grads
 
-            torch.cuda.reset_peak_memory_stats()
             ms, warm, cold = time_steps(step, a.steps, a.warmup, stream, dev)
             # per-call breakdown in a second pass, events between the calls
+            # (the peak memory of these steps: the cold-cache write is freed)
             evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
                    for _ in range(a.steps)]
+            torch.cuda.synchronize()
+            torch.cuda.reset_peak_memory_stats()
             for e in evs:
                 step(e)
             torch.cuda.synchronize()
