@@ -29,7 +29,7 @@ def oracle_bwd(d):
 U = 2.0 ** -8  # bf16 unit roundoff (relative size of one rounding)
 
 
-def dbias_rounding_bound(d):
+def dbias_rounding_bound(d, lam=None):
     """Worst-case (first-order) error of the bf16 dBias from the kernels'
     own roundings, elementwise [B, H, N, N], summed over rows:
       forward: every p is rounded to bf16 before the PV product and the
@@ -42,12 +42,19 @@ def dbias_rounding_bound(d):
       P is recomputed from the log-sum-exp of the rounded p: |dP/P| <= u;
       so |d dS| <= P (|d dP| + |dD|) + u |dS|, summed over the rows.
     The pages fix no precision for these steps; this is the bf16 reading of
-    the standard backward (D from the stored forward output)."""
+    the standard backward (D from the stored forward output).
+    With `lam`, the bound of the sum over rows is also taken in its
+    probabilistic form: the rows' errors are independent (each row has its
+    own inputs and roundings) and each lies within its own bound b_r, so by
+    Hoeffding's inequality |sum_r e_r| <= lam * sqrt(sum_r b_r^2) except with
+    probability 2 exp(-lam^2 / 2); the smaller of the two bounds is
+    returned."""
     q, k, v = np64(d["q"]), np64(d["k"]), np64(d["v"])
     g, bias, dout = np64(d["gate"]), np64(d["bias"]), np64(d["dout"])
     mask = npu8(d["mask"])
     B, R, N, H, C = q.shape
     out = np.zeros((B, H, N, N))
+    sq = np.zeros((B, H, N, N))
     for b in range(B):
         for r in range(R):
             keep = None if mask is None else mask[b, 0 if mask.shape[1] == 1 else r] != 0
@@ -65,7 +72,11 @@ def dbias_rounding_bound(d):
                 ddP = U * (np.abs(dop) @ np.abs(V).T)                  # [N, N]
                 dP = dop @ V.T
                 dS = P * (dP - (P * dP).sum(-1, keepdims=True))
-                out[b, h] += P * (ddP + dD[:, None]) + U * np.abs(dS)
+                br = P * (ddP + dD[:, None]) + U * np.abs(dS)
+                out[b, h] += br
+                sq[b, h] += br * br
+    if lam is not None:
+        out = np.minimum(out, lam * np.sqrt(sq))
     return out
 
 
@@ -197,3 +208,35 @@ def test_bwd_padding_reads_nothing_past_the_tensors(dtype):
             compare(name, np64(gt), r, dtype, stored="fp32", bound=bound)
         else:
             compare(name, np64(gt), r, dtype)
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 2500, 2), (2, 1024, 40, 1)])
+def test_fwd_bwd_long_lines_and_many_rows(shape):
+    """Extremes of the two loops: one line of 2500 keys (39 full key tiles
+    and a ragged one; every index past 2^21 elements of the bias) and 2048
+    lines of 40 keys (a grid of thousands of line workgroups, dBias summed
+    over 1024 rows in several row groups).  bf16, bias, shared random mask,
+    gate; every output against the oracle."""
+    B, R, N, H = shape
+    log(f"case fwd+bwd extreme B={B} R={R} N={N} H={H}")
+    d = synth.rand_core(B, R, N, H, 32, "bf16", seed=N + R, dout=True, mask="random")
+    q, k, v = dev(d["q"]), dev(d["k"]), dev(d["v"])
+    g, m, b, do = dev(d["gate"]), dev(d["mask"]), dev(d["bias"]), dev(d["dout"])
+    out, lse = ops.evo_attn_fwd(q, k, v, g, m, b, want_lse=True)
+    grads = ops.evo_attn_bwd(q, k, v, g, m, b, out, lse, do)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = O.attention_forward(np64(d["q"]), np64(d["k"]), np64(d["v"]),
+                                           np64(d["gate"]), npu8(d["mask"]), np64(d["bias"]))
+    compare("out", np64(out), ref_out, "bf16")
+    compare("lse", lse.cpu().numpy().astype(np.float64), ref_lse, "bf16", stored="fp32")
+    ref = oracle_bwd(d)
+    for name, gt, r in zip(("dq", "dk", "dv", "dgate", "dbias"), grads, ref):
+        if name == "dbias":
+            # a sum over up to 1024 rows of short lines (large P): the
+            # derived bound of the kernels' own roundings where it exceeds
+            # the plain bar, in its probabilistic form over the rows
+            # (lam = 6: failure probability 3e-8 per element)
+            compare(name, np64(gt), r, "bf16", stored="fp32",
+                    bound=dbias_rounding_bound(d, lam=6.0))
+        else:
+            compare(name, np64(gt), r, "bf16")
