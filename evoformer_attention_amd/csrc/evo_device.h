@@ -191,6 +191,15 @@ __device__ __forceinline__ u32x4 buf_ld128(const void* base, uint32_t nbytes, ui
 #endif
 }
 
+// Offset of element (row r, column k) of a row-major M x kp matrix stored
+// in the order of MFMA A-operand fragments of 16 rows x 32 columns: per
+// (16-row block, 32-column block) 64 lanes x 8 elements, lane l holding row
+// l % 16 and columns 8 (l / 16) .. +7 of the block.  kp is a multiple of 32.
+// A wave reads one block as one contiguous 1 KB load.
+__device__ __forceinline__ int64_t frag_off(int64_t r, int k, int kp) {
+  return ((r >> 4) * (kp >> 5) + (k >> 5)) * 512 + ((r & 15) + 16 * ((k >> 3) & 3)) * 8 + (k & 7);
+}
+
 // Workgroups are dispatched round-robin over the XCDs (workgroup i runs on
 // XCD i % 8).  Remap so that XCD x receives the contiguous work range
 // [x * per, (x + 1) * per): neighbouring work items, which share inputs,

@@ -136,6 +136,10 @@ struct ChannelProjectArgs {
   void* a;
   void* b;
   int64_t s_ch, s_line, s_place;
+  // > 0: a is written in MFMA fragment order (frag_off) as a matrix of rows
+  // (c * s_ch + line * s_line) / a_frag_kp and columns `place` (s_place = 1);
+  // 0: a and b both at the strides above
+  int64_t a_frag_kp = 0;
 };
 
 struct TriMulArgs {
@@ -190,7 +194,7 @@ hipError_t launch_trimul(const TriMulArgs& a, hipStream_t s);
 // T [C][M][M]; M <= Np, Np a multiple of pair_gemm_row_tile().
 int pair_gemm_row_tile();
 hipError_t launch_pair_gemm(int dtype, int C, int M, int K, int Np, int Kp, void* a, void* b,
-                            void* t, hipStream_t s);
+                            void* t, bool a_frag, hipStream_t s);
 // Outer product mean: m [S][N][CM] -> out [N][N][CZ].
 struct OpmArgs {
   int dtype;

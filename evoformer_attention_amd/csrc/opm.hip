@@ -205,11 +205,14 @@ hipError_t opm_t(const OpmArgs& a, hipStream_t s) {
   T* Pm = reinterpret_cast<T*>(ws + L.p);
   // lines = residues, places = sequences: m row s*N + i is read for position
   // i*S + s, and a[s, i, c] lands at A[(i*C + c)][s]
+  // bf16: A in fragment order for the product kernel (rows i*C + c, columns s)
   ChannelProjectArgs pa{a.dtype, a.N, a.S, a.CM, a.C, 1, a.m, nullptr, a.ln_w, a.ln_b,
-                        a.eps, a.w_a, a.w_b, A, B, L.Kp, a.C * L.Kp, 1};
+                        a.eps, a.w_a, a.w_b, A, B, L.Kp, a.C * L.Kp, 1,
+                        a.dtype == 1 ? L.Kp : 0};
   hipError_t e = launch_channel_project(pa, s);
   if (e != hipSuccess) return e;
-  e = launch_pair_gemm(a.dtype, 1, (int)L.M, (int)a.S, (int)L.Np, (int)L.Kp, A, B, Pm, s);
+  e = launch_pair_gemm(a.dtype, 1, (int)L.M, (int)a.S, (int)L.Np, (int)L.Kp, A, B, Pm,
+                       a.dtype == 1, s);
   if (e != hipSuccess) return e;
   OpmOutParams o{};
   o.N = (int)a.N;

@@ -39,9 +39,11 @@ template <typename T> struct MulCfg;
 template <> struct MulCfg<bf16_t> { static constexpr int BK = 64, RS = 72; };
 template <> struct MulCfg<float> { static constexpr int BK = 32, RS = 36; };
 
-// Columns [K, Kp) of rows [0, M) of the C matrices [Np][Kp] of a and b: zero.
+// Columns [K, Kp) of rows [0, M) of the C matrices [Np][Kp] of a and b: zero
+// (a_frag: a in fragment order, frag_off).
 template <typename T>
-__global__ void __launch_bounds__(256) pad_cols_kernel(T* a, T* b, int C, int M, int K, int Np, int Kp) {
+__global__ void __launch_bounds__(256) pad_cols_kernel(T* a, T* b, int C, int M, int K, int Np,
+                                                       int Kp, int a_frag) {
   const int padw = Kp - K;
   const int64_t total = (int64_t)C * M * padw;
   for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total;
@@ -50,7 +52,7 @@ __global__ void __launch_bounds__(256) pad_cols_kernel(T* a, T* b, int C, int M,
     const int64_t r = e / padw;  // matrix * M + row
     const int c = (int)(r / M), row = (int)(r - (int64_t)c * M);
     const int64_t off = ((int64_t)c * Np + row) * Kp + col;
-    a[off] = T(0);
+    a[a_frag ? (int64_t)c * Np * Kp + frag_off(row, col, Kp) : off] = T(0);
     b[off] = T(0);
   }
 }
@@ -186,9 +188,12 @@ __global__ void __launch_bounds__(256) trimul_gemm_kernel(MulGemmParams p) {
 // bf16 products: a workgroup of 4*WJ waves owns a 256 x 128*WJ tile (rows i
 // of A, rows j of B); wave (wi, wj) owns rows wi*64 .. +63 and columns
 // wj*128 .. +127 as 4 x 8 accumulator blocks.  Each wave's A rows are its
-// own, so its A operands come straight from global memory into registers
-// (16 rows x 64 contiguous bytes per load), one 64-wide stage ahead; only B
-// goes through double-buffered LDS.  Per 32-wide K step a wave issues 32
+// own, so its A operands come straight from global memory into registers,
+// one 64-wide stage ahead: A is stored in fragment order (frag_off), so
+// each operand is one contiguous 1 KB load (in row-major order the same
+// load touches 16 rows x 64 bytes, four times slower through the load
+// path: 2.02 vs 1.81 ms per outer product mean); only B goes through
+// double-buffered LDS.  Per 32-wide K step a wave issues 32
 // products against 8 LDS operand reads (a 64 x 64 wave tile with both
 // operands in LDS needs 8 reads for 16), and per 64-wide stage the
 // workgroup moves (256 + 128*WJ) x 128 bytes from L2.
@@ -220,8 +225,10 @@ __global__ void __launch_bounds__(256 * WJ) pair_gemm_bf16_kernel(MulGemmParams 
   const int l16 = lane & 15, g = lane >> 4;
   const int wi = wave & 3, wj = wave >> 2;
   const int64_t cs = (int64_t)p.Np * p.Kp;
+  // this wave's first 16-row block of A (fragment order), this lane's slot
+  const int kblk = p.Kp >> 5;  // 32-column blocks per row block
   const T* A = static_cast<const T*>(p.a) + c * cs +
-               ((int64_t)ti * kBigI + wi * 64 + l16) * p.Kp + 8 * g;
+               ((int64_t)(ti * kBigI + wi * 64) >> 4) * kblk * 512 + lane * 8;
   const T* B = static_cast<const T*>(p.b) + c * cs + (int64_t)tj * BROWS * p.Kp;
 
   u32x4 rb[CPT];
@@ -246,7 +253,7 @@ __global__ void __launch_bounds__(256 * WJ) pair_gemm_bf16_kernel(MulGemmParams 
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int bi = 0; bi < 4; ++bi)
-        v[ks][bi] = *reinterpret_cast<const Op*>(A + (int64_t)bi * 16 * p.Kp + k0 + ks * 32);
+        v[ks][bi] = *reinterpret_cast<const Op*>(A + ((int64_t)bi * kblk + (k0 >> 5) + ks) * 512);
   };
 
   f32x4 acc[8][4];  // [column block bj][row block bi]
@@ -489,12 +496,14 @@ MulLayout mul_layout(int dtype, int64_t N, int64_t C) {
 }
 
 template <typename T>
-hipError_t pair_gemm_t(int C, int M, int K, int Np, int Kp, T* A, T* B, T* Tm, hipStream_t s) {
+hipError_t pair_gemm_t(int C, int M, int K, int Np, int Kp, T* A, T* B, T* Tm, bool a_frag,
+                       hipStream_t s) {
   hipError_t e;
   if (Kp > K) {
     const int64_t total = (int64_t)C * M * (Kp - K);
     const int grid = (int)std::min<int64_t>((total + 255) / 256, 4096);
-    hipLaunchKernelGGL(pad_cols_kernel<T>, dim3(grid), dim3(256), 0, s, A, B, C, M, K, Np, Kp);
+    hipLaunchKernelGGL(pad_cols_kernel<T>, dim3(grid), dim3(256), 0, s, A, B, C, M, K, Np, Kp,
+                       (int)a_frag);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   MulGemmParams g{};
@@ -504,13 +513,14 @@ hipError_t pair_gemm_t(int C, int M, int K, int Np, int Kp, T* A, T* B, T* Tm, h
   // bf16: the 256 x 128 kernel for one large product (24576^2 by K = 1024:
   // 1.78 vs 1.93 ms), the 128 x 128 one for many small ones (128 products of
   // 768^2 by 768: 206 vs 218 us)
-  if (sizeof(T) == 2 && C == 1) {
+  if (sizeof(T) == 2 && C == 1 && a_frag) {
     constexpr int WJ = 1;  // 256 x 256 tiles with 8 waves (WJ = 2) measured slower
     const int total = C * (Np / kBigI) * (Np / (kBigJ * WJ));
     const int grid = (total + kNumXcd - 1) / kNumXcd * kNumXcd;
     if constexpr (sizeof(T) == 2)
       hipLaunchKernelGGL(pair_gemm_bf16_kernel<WJ>, dim3(grid), dim3(256 * WJ), 0, s, g);
   } else {
+    if (a_frag) return hipErrorInvalidValue;  // the 128 x 128 kernel reads row-major A
     const int total = C * g.ntile * g.ntile;
     const int grid = (total + kNumXcd - 1) / kNumXcd * kNumXcd;
     hipLaunchKernelGGL(trimul_gemm_kernel<T>, dim3(grid), dim3(256), 0, s, g);
@@ -532,7 +542,8 @@ hipError_t trimul_t(const TriMulArgs& a, hipStream_t s) {
                         L.Np * L.Kp, L.Kp, 1};
   hipError_t e = launch_channel_project(pa, s);
   if (e != hipSuccess) return e;
-  if ((e = pair_gemm_t<T>(C, N, N, (int)L.Np, (int)L.Kp, A, B, Tm, s)) != hipSuccess) return e;
+  if ((e = pair_gemm_t<T>(C, N, N, (int)L.Np, (int)L.Kp, A, B, Tm, false, s)) != hipSuccess)
+    return e;
   MulOutParams o{};
   o.C = C; o.CZ = (int)a.CZ; o.npos = N * N;
   o.ntiles = (o.npos + kOutP - 1) / kOutP;
@@ -559,14 +570,15 @@ hipError_t launch_trimul(const TriMulArgs& a, hipStream_t s) {
 int pair_gemm_row_tile() { return kRowPad; }
 
 hipError_t launch_pair_gemm(int dtype, int C, int M, int K, int Np, int Kp, void* a, void* b,
-                            void* t, hipStream_t s) {
+                            void* t, bool a_frag, hipStream_t s) {
   if (Np % kRowPad != 0 || M > Np || K > Kp || Kp % MulCfg<float>::BK != 0 ||
-      Kp % MulCfg<bf16_t>::BK != 0)
+      Kp % MulCfg<bf16_t>::BK != 0 || (a_frag && (dtype != 1 || C != 1)))
     return hipErrorInvalidValue;
   return dtype == 1 ? pair_gemm_t<bf16_t>(C, M, K, Np, Kp, static_cast<bf16_t*>(a),
-                                          static_cast<bf16_t*>(b), static_cast<bf16_t*>(t), s)
+                                          static_cast<bf16_t*>(b), static_cast<bf16_t*>(t),
+                                          a_frag, s)
                     : pair_gemm_t<float>(C, M, K, Np, Kp, static_cast<float*>(a),
-                                         static_cast<float*>(b), static_cast<float*>(t), s);
+                                         static_cast<float*>(b), static_cast<float*>(t), false, s);
 }
 
 }  // namespace evo

@@ -65,6 +65,7 @@ struct GemmParams {
   const uint8_t* mask;  // operands: keep flags per place, or null
   int P, L;             // operands: places per line, lines (npos = P * L)
   int64_t s_ch, s_line, s_place;
+  int64_t frag_kp;      // operands: > 0, a in fragment order (frag_off)
 };
 
 // z row (or output row) of line-layout position pidx (N*N < 2^31, so 32-bit
@@ -461,6 +462,8 @@ rowgemm_kernel(GemmParams p) {
           if (c < p.HC && pi0 < (uint32_t)p.npos) {
             uint32_t line = pi0 / (uint32_t)p.P, place = pi0 - line * (uint32_t)p.P;
             T* base = out + (int64_t)c * p.s_ch;
+            // a in fragment order: row (c s_ch + line s_line) / frag_kp
+            const bool frag = m == 0 && p.frag_kp > 0;
             if (vec_ok && pi0 + 8 <= (uint32_t)p.npos) {
               if (p.mask) {  // 8 keep flags, 8-byte aligned: zero the dead places
                 const uint2 mb = *reinterpret_cast<const uint2*>(p.mask + place);
@@ -470,7 +473,12 @@ rowgemm_kernel(GemmParams p) {
                   v[i] &= ((w & 0xffu) ? 0xffffu : 0u) | ((w & 0xff00u) ? 0xffff0000u : 0u);
                 }
               }
-              *reinterpret_cast<u32x4*>(base + (int64_t)line * p.s_line + place) = v;
+              if (frag)
+                *reinterpret_cast<u32x4*>(
+                    out + frag_off(((int64_t)c * p.s_ch + (int64_t)line * p.s_line) / p.frag_kp,
+                                   (int)place, (int)p.frag_kp)) = v;
+              else
+                *reinterpret_cast<u32x4*>(base + (int64_t)line * p.s_line + place) = v;
             } else {
               // ragged: element by element, walking the places of the line
 #pragma nounroll
@@ -479,8 +487,12 @@ rowgemm_kernel(GemmParams p) {
                 const bool dead = p.mask && p.mask[place] == 0;
                 const uint32_t word = j < 2 ? v[0] : j < 4 ? v[1] : j < 6 ? v[2] : v[3];
                 const uint32_t bits = (word >> (16 * (j & 1))) & 0xffffu;
-                base[(int64_t)line * p.s_line + (int64_t)place * p.s_place] =
-                    dead ? T(0) : __builtin_bit_cast(T, (uint16_t)bits);
+                const T val = dead ? T(0) : __builtin_bit_cast(T, (uint16_t)bits);
+                if (frag)
+                  out[frag_off(((int64_t)c * p.s_ch + (int64_t)line * p.s_line) / p.frag_kp,
+                               (int)place, (int)p.frag_kp)] = val;
+                else
+                  base[(int64_t)line * p.s_line + (int64_t)place * p.s_place] = val;
                 if (++place == (uint32_t)p.P) { place = 0; ++line; }
               }
             }
@@ -629,6 +641,9 @@ hipError_t launch_channel_project(const ChannelProjectArgs& a, hipStream_t s) {
   p.s_ch = a.s_ch;
   p.s_line = a.s_line;
   p.s_place = a.s_place;
+  p.frag_kp = a.a_frag_kp;
+  if (p.frag_kp > 0 && (a.dtype != 1 || a.s_place != 1 || p.frag_kp % 32 != 0))
+    return hipErrorInvalidValue;
   return dispatch(a.dtype, p, s);
 }
 
