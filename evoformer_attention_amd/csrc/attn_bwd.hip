@@ -18,8 +18,12 @@
 // Kernels:
 //   prep      an elementwise pass: dO, dG, -D and the base-2 LSE.
 //   bias      the mask-folded pair bias, in the fragment orders of the dQ /
-//             dBias kernels and (transposed) of the dK/dV kernel (working
-//             dtype; the exp argument s*log2(e) - LSE*log2(e) is one FMA).
+//             dBias kernels and (transposed) of the dK/dV kernel (fp16 for
+//             bf16 inputs, as in the forward, fp32 for fp32).  The dK/dV and
+//             dQ kernels prescale their resident Q or K operand by
+//             log2(e)/sqrt(C) and start the logit product from -LSE (base 2),
+//             so the exponent is the product plus bias*log2(e): one
+//             mixed-precision FMA per logit straight from the fp16 bias.
 //   dkdv      one line, one head, 128 keys per workgroup (32 per wave);
 //             loops over 32-query steps staged through double-buffered LDS
 //             (next step prefetched into registers).  Lane = key in the
@@ -139,6 +143,7 @@ struct BwdParams {
   void* bp; void* bpt;  // pair bias, natural units, masked, working dtype
   int B, R, N, H, Np, mask_rows, n_rg, rows_per_group, row_mask;
   float qscale;  // 1 / sqrt(C)
+  float lscale;  // log2(e) / sqrt(C), the forward's scale of Q
 };
 
 // ----------------------------------------------------------------- prep
@@ -231,9 +236,12 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdParams p) {
   }
 }
 
-// Pair bias (natural units, working dtype) with the shared key mask and the
-// padding folded in: -inf for masked keys and keys >= N, 0 without a bias,
-// any finite value for queries >= N.  Every stored value is exact.  Two
+// Pair bias (natural units) with the shared key mask and the padding folded
+// in: -inf for masked keys and keys >= N, 0 without a bias, any finite value
+// for queries >= N.  bf16 inputs store it in fp16, exactly as the forward
+// prepares its own: every bf16 value of magnitude 2^-14 .. 65504 is exact,
+// smaller ones are within 2^-25, finite values beyond +-65504 are clamped
+// to it (so the backward recomputes the logits the forward normalised).  Two
 // copies, each in the order one kernel reads it, so that every bias load is
 // a contiguous block per wave:
 //   bp  (dQ and dBias kernels; the forward's order): per (b, h) a grid of
@@ -241,9 +249,10 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdParams p) {
 //       lane (l16, g) of wave w holds query 128*qt + 32*w + 16*qb + l16,
 //       keys 64*kt + 32*half + 8*g .. +7.
 //   bpt (dK/dV kernel): per (b, h) a grid of [Nk128/128][Np/32] blocks (key
-//       tile, 32-query step), each [wave 4][lane 64][qb 2][kb 2][i 4]: lane
+//       tile, 32-query step), each [wave 4][qb 2][lane 64][kb 2][i 4]: lane
 //       (l16, g) of wave w holds key 128*kt + 32*w + 16*kb + l16 and
-//       queries 32*st + 16*qb + 4*g + i.
+//       queries 32*st + 16*qb + 4*g + i (a wave reads each qb half as one
+//       contiguous 1 KB load).
 template <typename T>
 __device__ __forceinline__ float bias_value(const BwdParams& p, int bh, int q, int k) {
   if (k >= p.N) return -INFINITY;
@@ -251,6 +260,32 @@ __device__ __forceinline__ float bias_value(const BwdParams& p, int bh, int q, i
   if (p.mask && !p.row_mask && p.mask[(int64_t)b * p.mask_rows * p.N + k] == 0) return -INFINITY;
   const T* Bias = static_cast<const T*>(p.bias);
   return (Bias && q < p.N) ? Tr<T>::to_f(Bias[((int64_t)bh * p.N + q) * p.N + k]) : 0.f;
+}
+
+// Four prepared-bias values: bf16 inputs store fp16 bits in the 16-bit
+// slots (finite values clamped to +-65504, as in the forward), fp32 inputs
+// fp32.
+__device__ __forceinline__ void st4pb(bf16_t* p, const f32x4& v) {
+  typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+  f16x4 h;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float x = v[i];
+    if (x == x && fabsf(x) != INFINITY) x = fminf(fmaxf(x, -65504.f), 65504.f);
+    h[i] = (_Float16)x;
+  }
+  *reinterpret_cast<f16x4*>(p) = h;
+}
+__device__ __forceinline__ void st4pb(float* p, const f32x4& v) { st4e(p, v); }
+
+// Element j (0..7) of a lane's raw 8-value prepared-bias chunk, in fp32
+// (fp16 widens inside the consuming FMA: v_fma_mix_f32).
+__device__ __forceinline__ float pb_elem(const Raw8<bf16_t>& r, int j) {
+  typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+  return (float)__builtin_bit_cast(f16x8, r.a)[j];
+}
+__device__ __forceinline__ float pb_elem(const Raw8<float>& r, int j) {
+  return __uint_as_float(j < 4 ? r.a[j] : r.b[j - 4]);
 }
 
 template <typename T>
@@ -274,12 +309,12 @@ __global__ void __launch_bounds__(256) bwd_bias_kernel(BwdParams p) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) v[j >> 2][j & 3] = bias_value<T>(p, bh, q, k0 + j);
       T* dst = static_cast<T*>(p.bp) + e * 8;
-      st4e(dst, v[0]);
-      st4e(dst + 4, v[1]);
-    } else {  // bpt chunk: (qb) half of a lane's 16 values, 4 queries x 2 keys
+      st4pb(dst, v[0]);
+      st4pb(dst + 4, v[1]);
+    } else {  // bpt chunk: the qb half of a lane's 16 values, 4 queries x 2 keys
       const int64_t f = e - chunks;
-      const int qb = (int)(f & 1);
-      const int lane = (int)((f >> 1) & 63);
+      const int lane = (int)(f & 63);
+      const int qb = (int)((f >> 6) & 1);
       int64_t t = f >> 7;
       const int wv = (int)(t & 3); t >>= 2;
       const int st = (int)(t % nst); t /= nst;
@@ -293,8 +328,8 @@ __global__ void __launch_bounds__(256) bwd_bias_kernel(BwdParams p) {
           v[kb][i] = bias_value<T>(p, bh, st * 32 + qb * 16 + 4 * (lane >> 4) + i, k);
       }
       T* dst = static_cast<T*>(p.bpt) + f * 8;
-      st4e(dst, v[0]);
-      st4e(dst + 4, v[1]);
+      st4pb(dst, v[0]);
+      st4pb(dst + 4, v[1]);
     }
   }
 }
@@ -317,7 +352,7 @@ bwd_dkdv_kernel(BwdParams p) {
   // [buf][Q, dO, Q^T, dO^T]; bf16 reads the transposed operands straight
   // from the row-major tiles (lds_read_tr16), so only fp32 stores Q^T, dO^T
   __shared__ __attribute__((aligned(32))) T sT[2][sizeof(T) == 2 ? 2 : 4][32 * RS];
-  __shared__ float sL[2][2][32];                                 // [buf][lse2, D]
+  __shared__ float sL[2][2][32];                                 // [buf][-lse2, -D]
 
   // Work order (fastest first): key tile, head within a head pair, line,
   // head pair.  The key tiles of one line read the same query-side data and
@@ -346,21 +381,23 @@ bwd_dkdv_kernel(BwdParams p) {
   const T* V = static_cast<const T*>(p.v);
   const T* Q = static_cast<const T*>(p.q);
   const T* DO = static_cast<const T*>(p.dopre);
-  // This lane's bias^T operands of step st: 16 values at BPT + st * 4096
-  // (prepared block order: [qb][kb][i]).
+  // This lane's bias^T operands of step st: 8 values [kb][i] per qb at
+  // BPT + st * 4096 + qb * 512 (prepared block order).
   const T* BPT = static_cast<const T*>(p.bpt) +
-                 ((int64_t)(b * H + h) * nkt + kt) * (Np / 32) * 4096 + wave * 1024 + lane * 16;
+                 ((int64_t)(b * H + h) * nkt + kt) * (Np / 32) * 4096 + wave * 1024 + lane * 8;
   const uint8_t* mrow = ROW_MASK ? p.mask + ((int64_t)b * p.mask_rows + r) * N : nullptr;
 
-  // This wave's keys: kbase + kb*16 + l16 (kb = 0, 1).
+  // This wave's keys: kbase + kb*16 + l16 (kb = 0, 1).  K is held scaled by
+  // log2(e)/sqrt(C), so the logit product is already in base 2.
   const int kbase = kt * 128 + wave * 32;
+  const float ksc = p.lscale;
   Op kf[2], vf[2];
   bool kdead[2];  // keys of a per-line mask (padding and shared masks are in the bias)
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     const int key = kbase + kb * 16 + l16;
     if (key < N) {
-      kf[kb] = scale8(ldop<T>(K + lbase + (int64_t)key * pos_stride + 8 * g), p.qscale);
+      kf[kb] = scale8(ldop<T>(K + lbase + (int64_t)key * pos_stride + 8 * g), ksc);
       vf[kb] = ldop<T>(V + lbase + (int64_t)key * pos_stride + 8 * g);
     } else {
       kf[kb] = Op{};
@@ -422,8 +459,9 @@ bwd_dkdv_kernel(BwdParams p) {
         d32[(4 + j) * RS] = raw.b[j];
       }
     }
-    // every wave writes the same values (no branch, see the LSE load)
-    sL[buf][lane >> 5][lane & 31] = raw.l;
+    // every wave writes the same values (no branch, see the LSE load);
+    // -LSE starts the logit product, -D the dP product
+    sL[buf][lane >> 5][lane & 31] = (lane & 32) ? raw.l : -raw.l;
   };
   (void)E16;
   // A step's bias^T operands (bf16: buffer loads; past this workgroup's
@@ -435,12 +473,12 @@ bwd_dkdv_kernel(BwdParams p) {
   auto fetch_bias = [&](Raw8<T> (&bn)[2], int st) {
     if constexpr (sizeof(T) == 2) {
       const uint32_t so = (uint32_t)st * 4096u * 2u;
-      bn[0].a = buf_ld128(bpt_w, b_nbytes, (uint32_t)lane * 32u, so);
-      bn[1].a = buf_ld128(bpt_w, b_nbytes, (uint32_t)lane * 32u + 16u, so);
+      bn[0].a = buf_ld128(bpt_w, b_nbytes, (uint32_t)lane * 16u, so);
+      bn[1].a = buf_ld128(bpt_w, b_nbytes, (uint32_t)lane * 16u + 1024u, so);
     } else {
       const T* src = BPT + (int64_t)min(st, nsteps - 1) * 4096;
       ld_raw8(bn[0], src);
-      ld_raw8(bn[1], src + 8);
+      ld_raw8(bn[1], src + 512);
     }
   };
 
@@ -456,17 +494,15 @@ bwd_dkdv_kernel(BwdParams p) {
     __builtin_amdgcn_sched_barrier(0);
     store(cur, buf);
     __syncthreads();
-    f32x4 cbias[2][2];  // [qb][kb]
-    widen8(bc[0], cbias[0][0], cbias[0][1]);
-    widen8(bc[1], cbias[1][0], cbias[1][1]);
     fetch(nxt, q0 + 32);
     fetch_bias(bx, st + 1);
     __builtin_amdgcn_sched_barrier(0);  // issue the prefetch here, not later
     const T* sQ = sT[buf][0];
     const T* sDO = sT[buf][1];
 
-    // S[qb][kb]: lane holds queries qb*16 + 4g + i for key kbase + kb*16 + l16.
-    // dP starts from -D, so the accumulator ends at dP - D.
+    // S[qb][kb]: lane holds queries qb*16 + 4g + i for key kbase + kb*16 + l16,
+    // base 2, starting from -LSE (the bias is added below).  dP starts from
+    // -D, so the accumulator ends at dP - D.
     f32x4 s[2][2], dp[2][2];
     // products at raised wave priority (as in the forward): 677 -> 656 us
     // here and 680 -> 656 us in dBias at N = 768; dQ measured slower (its
@@ -476,22 +512,22 @@ bwd_dkdv_kernel(BwdParams p) {
     for (int qb = 0; qb < 2; ++qb) {
       const Op qa = *reinterpret_cast<const Op*>(sQ + (qb * 16 + l16) * RS + 8 * g);
       const Op da = *reinterpret_cast<const Op*>(sDO + (qb * 16 + l16) * RS + 8 * g);
+      const f32x4 negl = *reinterpret_cast<const f32x4*>(&sL[buf][0][qb * 16 + 4 * g]);
       const f32x4 negd = *reinterpret_cast<const f32x4*>(&sL[buf][1][qb * 16 + 4 * g]);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        s[qb][kb] = mma32(qa, kf[kb], cbias[qb][kb]);
+        s[qb][kb] = mma32(qa, kf[kb], negl);
         dp[qb][kb] = mma32(da, vf[kb], negd);
       }
     }
     __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      const f32x4 l2 = *reinterpret_cast<const f32x4*>(&sL[buf][0][qb * 16 + 4 * g]);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float pv = exp2_fast(__builtin_fmaf(s[qb][kb][i], kLog2e, -l2[i]));
+          float pv = exp2_fast(__builtin_fmaf(pb_elem(bc[qb], kb * 4 + i), kLog2e, s[qb][kb][i]));
           if constexpr (ROW_MASK) pv = kdead[kb] ? 0.f : pv;
           s[qb][kb][i] = pv;
           dp[qb][kb][i] = pv * dp[qb][kb][i];
@@ -635,14 +671,17 @@ bwd_dq_kernel(BwdParams p) {
   const T* V = static_cast<const T*>(p.v) + lbase;
   const uint8_t* mrow = ROW_MASK ? p.mask + ((int64_t)b * p.mask_rows + r) * N : nullptr;
 
+  // Q is held scaled by log2(e)/sqrt(C) and the logit product starts from
+  // -LSE (base 2), so the exponent is the product plus bias*log2(e).
   Op qf[2], df[2];
   float l2[2], dd[2];  // dd = -D
+  const float qsc = p.lscale;
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int q = qw0 + qb * 16 + l16;
     const int qc = min(q, N - 1);
     qf[qb] = scale8(ldop<T>(static_cast<const T*>(p.q) + lbase + (int64_t)qc * pos_stride + 8 * g),
-                    p.qscale);
+                    qsc);
     df[qb] = ldop<T>(static_cast<const T*>(p.dopre) + lbase + (int64_t)qc * pos_stride + 8 * g);
     l2[qb] = q < N ? p.lse2[lh * Np + q] : INFINITY;
     dd[qb] = q < N ? p.dd[lh * Np + q] : 0.f;
@@ -651,7 +690,6 @@ bwd_dq_kernel(BwdParams p) {
   // BP + tile * 8192 + (qb*2 + half) * 512 (prepared tile order).
   const T* BP = static_cast<const T*>(p.bp) +
                 (((int64_t)(b * H + h) * nqt + qt) * (Np / 64)) * 8192 + wave * 2048 + lane * 8;
-  Raw8<T> bn[2][2];  // next tile's bias operands [qb][half], raw
   f32x4 dq[2][2];  // [qb][cb]
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb)
@@ -670,7 +708,8 @@ bwd_dq_kernel(BwdParams p) {
   const T* BPw = static_cast<const T*>(p.bp) +
                  (((int64_t)(b * H + h) * nqt + qt) * (Np / 64)) * 8192 + wave * 2048;
   const uint32_t b_nbytes = (uint32_t)((Np / 64) * 8192 - wave * 2048) * 2u;
-  auto fetch_tile = [&](int tile) {
+  // A tile's K and V into rk/rv, its bias operands [qb][half] (raw) into bn.
+  auto fetch_tile = [&](int tile, Raw8<T> (&bn)[2][2]) {
     if constexpr (sizeof(T) == 2) {
       const uint32_t so = (uint32_t)(tile * 64 * pos_stride) * 2u;
       rk0 = buf_ld128(K, kv_nbytes, kv_voff, so);
@@ -691,20 +730,23 @@ bwd_dq_kernel(BwdParams p) {
           ld_raw8(bn[qb][half], BP + (int64_t)nt * 8192 + (qb * 2 + half) * 512);
     }
   };
-  fetch_tile(0);
+  const f32x4 negl[2] = {f32x4{-l2[0], -l2[0], -l2[0], -l2[0]},
+                         f32x4{-l2[1], -l2[1], -l2[1], -l2[1]}};
+  Raw8<T> bn[2][2];  // the next tile's bias operands [qb][half], raw
+  fetch_tile(0, bn);
   const int ntiles = (N + 63) / 64;
   for (int tile = 0; tile < ntiles; ++tile) {
     const int k0 = tile * 64, buf = tile & 1;
     EVO_STORE_K(T, sK[buf], sV[buf], sKt[buf], KS, TS);
     __syncthreads();
-    f32x4 cb_[2][2][2];  // this tile's bias operands [qb][half][kb]
+    Raw8<T> bc[2][2];  // this tile's
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int half = 0; half < 2; ++half) widen8(bn[qb][half], cb_[qb][half][0], cb_[qb][half][1]);
+      for (int half = 0; half < 2; ++half) bc[qb][half] = bn[qb][half];
     // next tile (after the last: zeros for bf16, the last tile again for
     // fp32; unused)
-    fetch_tile(tile + 1);
+    fetch_tile(tile + 1, bn);
     // issue that prefetch here: left to itself, the scheduler sinks it to
     // the end of the tile, next to the store that waits for it
     __builtin_amdgcn_sched_barrier(0);
@@ -723,7 +765,7 @@ bwd_dq_kernel(BwdParams p) {
         const Op kf = *reinterpret_cast<const Op*>(sK[buf] + (half * 32 + kb * 16 + l16) * KS + 8 * g);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
-          s[qb][kb] = mma32(kf, qf[qb], cb_[qb][half][kb]);
+          s[qb][kb] = mma32(kf, qf[qb], negl[qb]);
       }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -740,7 +782,9 @@ bwd_dq_kernel(BwdParams p) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const float pv =
-                dead[i] ? 0.f : exp2_fast(__builtin_fmaf(s[qb][kb][i], kLog2e, -l2[qb]));
+                dead[i] ? 0.f
+                        : exp2_fast(__builtin_fmaf(pb_elem(bc[qb][half], kb * 4 + i), kLog2e,
+                                                   s[qb][kb][i]));
             dp[qb][kb][i] = pv * dp[qb][kb][i];
           }
       }
@@ -821,11 +865,10 @@ bwd_dbias_kernel(BwdParams p) {
       for (int half = 0; half < 2; ++half) {
         Raw8<T> r;
         ld_raw8(r, bt + (qb * 2 + half) * 512);
-        widen8(r, cbias[half][qb][0], cbias[half][qb][1]);
         // the logit accumulators hold <Q,K> + bias*sqrt(C) (unscaled Q);
         // 1/sqrt(C) is applied in the exponent
-        cbias[half][qb][0] *= kSqrtC;
-        cbias[half][qb][1] *= kSqrtC;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) cbias[half][qb][j >> 2][j & 3] = pb_elem(r, j) * kSqrtC;
         db[half][qb][0] = f32x4{0.f, 0.f, 0.f, 0.f};
         db[half][qb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
@@ -845,6 +888,8 @@ bwd_dbias_kernel(BwdParams p) {
   const int64_t lstride = (int64_t)N * pos_stride;       // one line of [.., N, H, C]
   const int64_t l0 = ((int64_t)b * R + r_begin) * lstride + h * C;
   const int qa = qw0 + l16, qbq = qw0 + 16 + l16;
+  // LSE / -D reads clamped into the padded rows (queries >= N are never stored)
+  const int qac = min(qa, Np - 1), qbc = min(qbq, Np - 1);
   const T* kp = static_cast<const T*>(p.k) + l0 + (int64_t)kk * pos_stride + ch * 8;
   const T* vp = static_cast<const T*>(p.v) + l0 + (int64_t)kk * pos_stride + ch * 8;
   // Q and dO rows.  bf16 loads them with four consecutive lanes covering one
@@ -878,10 +923,10 @@ bwd_dbias_kernel(BwdParams p) {
     qn1 = ldop<T>(qp1 + lo_);                                                  \
     dn0 = ldop<T>(op0 + lo_);                                                  \
     dn1 = ldop<T>(op1 + lo_);                                                  \
-    l2n0 = qa < N ? lp[ho_ + qa] : INFINITY;                                   \
-    l2n1 = qbq < N ? lp[ho_ + qbq] : INFINITY;                                 \
-    ddn0 = qa < N ? dq_[ho_ + qa] : 0.f;                                       \
-    ddn1 = qbq < N ? dq_[ho_ + qbq] : 0.f;                                     \
+    l2n0 = lp[ho_ + qac];                                                      \
+    l2n1 = lp[ho_ + qbc];                                                      \
+    ddn0 = dq_[ho_ + qac];                                                     \
+    ddn1 = dq_[ho_ + qbc];                                                     \
   } while (0)
   if (r_begin < r_end) EVO_FETCH_ROW(r_begin);
   for (int r = r_begin; r < r_end; ++r) {
@@ -1078,6 +1123,7 @@ hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t s) {
   p.n_rg = (int)L.n_rg;
   p.rows_per_group = (int)L.rows_per_group;
   p.qscale = 1.f / sqrtf((float)C);
+  p.lscale = kLog2e / sqrtf((float)C);
   return a.dtype == 1 ? launch_t<bf16_t>(p, s) : launch_t<float>(p, s);
 }
 
