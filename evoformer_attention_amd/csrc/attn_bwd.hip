@@ -563,12 +563,16 @@ bwd_dkdv_kernel(BwdParams p) {
   Raw8<T> ba[2], bb[2];
   fetch(ra, 0);
   fetch_bias(ba, 0);
-  int st = 0;
-  for (; st + 1 < nsteps; st += 2) {
+  // An even number of steps, so that no tail copy of the step follows the
+  // loop (its address registers would otherwise stay live across the loop
+  // and spill).  An odd count gains one step of padded queries: the padding
+  // is Np = pad64(N) >= 32 * (nsteps + 1), whose base-2 LSE is +inf, so its
+  // P and dS are exactly 0.
+  const int nsteps2 = (nsteps + 1) & ~1;
+  for (int st = 0; st < nsteps2; st += 2) {
     step(st, ra, rb, ba, bb);
     step(st + 1, rb, ra, bb, ba);
   }
-  if (st < nsteps) step(st, ra, rb, ba, bb);
 
   // Store: lane holds dims cb*16 + 4g + i of key kbase + kb*16 + l16.
   T* DK = static_cast<T*>(p.dk);
