@@ -102,12 +102,18 @@ TRAFFIC_KERNELS = {"attn_fwd": "attn_fwd_kernel", "bwd_dkdv": "bwd_dkdv_kernel",
 COPY_KERNEL = "neg_kernel"    # torch.neg(out=): a plain streaming copy
 
 
+# The sources that define and launch the kernels whose counters are stored
+# (attention forward and backward, the projection row-GEMM, their shared
+# device helpers).
+DIGEST_SOURCES = ("attn_fwd.hip", "attn_bwd.hip", "tri_project.hip", "evo_device.h")
+
+
 def kernel_sources_digest():
-    """Digest of the HIP sources; stored traffic counters are reported only
-    while it matches the digest they were taken with."""
+    """Digest of the measured kernels' sources; stored traffic counters are
+    reported only while it matches the digest they were taken with."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "evoformer_attention_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in DIGEST_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())
