@@ -47,6 +47,7 @@ __all__ = [
     "tri_module_forward", "tri_module_lines", "layer_norm_backward",
     "tri_out_project_backward", "tri_project_backward",
     "tri_module_backward", "tri_mul_forward", "tri_mul_entries",
+    "tri_mul_backward", "tri_mul_backward_entries",
     "transition_forward", "outer_product_mean", "transition_backward", "transition_weight_grad_units", "outer_product_mean_pairs",
 ]
 
@@ -518,6 +519,80 @@ def tri_mul_entries(z, residue_mask, ln_w, ln_b, eps, w_a, w_b, w_o, b_o,
         b = layer_norm(ej, ln_w, ln_b, eps) @ w_b.T
         t = (keep[:, None] * a * b).sum(axis=0)
         res.append(t @ w_o.T + b_o)
+    return np.stack(res)
+
+
+def tri_mul_backward(z, residue_mask, ln_w, ln_b, eps, w_a, w_b, w_o, b_o,
+                     dout, outgoing=True):
+    """Gradients of tri_mul_forward for training.  The pages print no backward
+    (the update is part of the trained trunk, [COURSE] "The three
+    operations"); this is the chain rule of the forward above, nothing else.
+    With A_c[i, k] = a[i, k, c] (outgoing; a[k, i, c] incoming), B_c
+    likewise, keep the residue mask and dT_c[i, j] = (dout . w_o)[i, j, c]:
+        dA_c = (dT_c . B_c) * keep[k],   dB_c = (dT_c^T . A_c) * keep[k],
+        dx   = da . w_a + db . w_b,      dz   = LayerNorm backward of dx,
+        dw_a = sum_p da[p]^T x[p],  dw_b likewise,
+        dw_o = sum_p dout[p]^T t[p],  db_o = sum_p dout[p].
+    Returns dict(dz, dln_w, dln_b, dw_a, dw_b, dw_o, db_o)."""
+    z = np.asarray(z, np.float64)
+    N, _, CZ = z.shape
+    dout = np.asarray(dout, np.float64)
+    x = layer_norm(z, ln_w, ln_b, eps)
+    a = x @ w_a.T
+    b = x @ w_b.T
+    C = a.shape[-1]
+    keep = (np.ones(N) if residue_mask is None
+            else (np.asarray(residue_mask) != 0).astype(np.float64))
+    dt = dout @ w_o                       # [N, N, C]
+    t = np.empty((N, N, C))
+    da = np.empty((N, N, C))
+    db = np.empty((N, N, C))
+    for c in range(C):
+        A = a[:, :, c] if outgoing else a[:, :, c].T      # A[i, k]
+        Bm = b[:, :, c] if outgoing else b[:, :, c].T     # Bm[j, k]
+        t[:, :, c] = (A * keep) @ Bm.T
+        dA = (dt[:, :, c] @ Bm) * keep                    # dA[i, k]
+        dB = (dt[:, :, c].T @ A) * keep                   # dB[j, k]
+        da[:, :, c] = dA if outgoing else dA.T
+        db[:, :, c] = dB if outgoing else dB.T
+    dx = da @ w_a + db @ w_b
+    dz, dln_w, dln_b = layer_norm_backward(z, ln_w, eps, dx)
+    flat = lambda v: v.reshape(-1, v.shape[-1])
+    return dict(dz=dz, dln_w=dln_w, dln_b=dln_b,
+                dw_a=flat(da).T @ flat(x), dw_b=flat(db).T @ flat(x),
+                dw_o=flat(dout).T @ flat(t), db_o=flat(dout).sum(axis=0))
+
+
+def tri_mul_backward_entries(z, residue_mask, ln_w, ln_b, eps, w_a, w_b, w_o,
+                             dout, picks, outgoing=True):
+    """dz[p] of tri_mul_backward at the z positions p = (i, k) in `picks`
+    only: the same chain rule with da[p] and db[p] formed for those
+    positions alone.  For outgoing, da[i, k] needs dT[i, :] (row i of dout)
+    and b on the edges (j, k) for all j; db[i, k] (as B's edge (j=i, k))
+    needs dT[:, i] and a on the edges (j, k) ... of every j.  Incoming swaps
+    the edge indices.  Returns [len(picks), CZ]."""
+    z = np.asarray(z, np.float64)
+    N = z.shape[0]
+    dout = np.asarray(dout, np.float64)
+    keep = (np.ones(N) if residue_mask is None
+            else (np.asarray(residue_mask) != 0).astype(np.float64))
+    res = []
+    for p0, p1 in picks:
+        # the edge's (row, third residue) in the A/B matrices
+        r, k = (p0, p1) if outgoing else (p1, p0)
+        # edges (j, k) for every j: z[j, k] (outgoing) or z[k, j] (incoming)
+        ek = z[:, k] if outgoing else z[k, :]
+        xk = layer_norm(ek, ln_w, ln_b, eps)              # [N(j), CZ]
+        a_k = xk @ w_a.T                                  # A_c[j, k] over j
+        b_k = xk @ w_b.T                                  # B_c[j, k] over j
+        dT_row = dout[r, :, :] @ w_o                      # dT_c[r, j] over j
+        dT_col = dout[:, r, :] @ w_o                      # dT_c[i, r] over i
+        da = keep[k] * (dT_row * b_k).sum(axis=0)         # dA_c[r, k]
+        db = keep[k] * (dT_col * a_k).sum(axis=0)         # dB_c[r, k]
+        dx = da @ w_a + db @ w_b
+        zp = z[p0, p1]
+        dzp, _, _ = layer_norm_backward(zp[None], ln_w, eps, dx[None])
+        res.append(dzp[0])
     return np.stack(res)
 
 

@@ -759,6 +759,106 @@ def test_trimul_entries_match_full_forward(outgoing):
         np.testing.assert_allclose(got[t], full[i, j], rtol=1e-12, atol=1e-12)
 
 
+TRIMUL_GRADS = (("z", "dz"), ("ln_w", "dln_w"), ("ln_b", "dln_b"), ("w_a", "dw_a"),
+                ("w_b", "dw_b"), ("w_o", "dw_o"), ("b_o", "db_o"))
+
+
+def _trimul_loss(d, dout, outgoing):
+    return float((O.tri_mul_forward(outgoing=outgoing, **d) * dout).sum())
+
+
+@pytest.mark.parametrize("outgoing", [True, False])
+def test_trimul_backward_matches_torch_autograd(outgoing):
+    """torch.autograd (fp64) of the update written with F.layer_norm,
+    F.linear and torch.einsum: every gradient, with a residue mask."""
+    d = trimul_case(70, N=6, CZ=8, C=5)
+    dout = np.random.default_rng(71).standard_normal((6, 6, 8))
+    t = {k: torch.tensor(v, requires_grad=True) for k, v in d.items()
+         if isinstance(v, np.ndarray) and k != "residue_mask"}
+    keep = torch.tensor(d["residue_mask"] != 0, dtype=torch.float64)
+    x = F.layer_norm(t["z"], (8,), t["ln_w"], t["ln_b"], d["eps"])
+    a, b = F.linear(x, t["w_a"]), F.linear(x, t["w_b"])
+    eq = "ikc,jkc,k->ijc" if outgoing else "kic,kjc,k->ijc"
+    out = F.linear(torch.einsum(eq, a, b, keep), t["w_o"], t["b_o"])
+    (out * torch.tensor(dout)).sum().backward()
+    got = O.tri_mul_backward(dout=dout, outgoing=outgoing, **d)
+    for k_t, k_o in TRIMUL_GRADS:
+        np.testing.assert_allclose(got[k_o], t[k_t].grad.numpy(), rtol=1e-10, atol=1e-12,
+                                   err_msg=k_o)
+
+
+@pytest.mark.parametrize("outgoing", [True, False])
+@pytest.mark.parametrize("which", ["z", "ln_w", "w_a", "w_b", "w_o", "b_o"])
+def test_trimul_backward_matches_central_finite_differences(which, outgoing):
+    """The definition of the derivative: central differences of
+    sum(out * dout) on a tiny masked case, every element of the input."""
+    d = trimul_case(72, N=4, CZ=4, C=3)
+    dout = np.random.default_rng(73).standard_normal((4, 4, 4))
+    got = O.tri_mul_backward(dout=dout, outgoing=outgoing, **d)["d" + which]
+    h = 1e-6
+    fd = np.zeros_like(d[which])
+    for idx in np.ndindex(d[which].shape):
+        e = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in d.items()}
+        e[which][idx] += h
+        fp = _trimul_loss(e, dout, outgoing)
+        e[which][idx] -= 2 * h
+        fd[idx] = (fp - _trimul_loss(e, dout, outgoing)) / (2 * h)
+    np.testing.assert_allclose(got, fd, rtol=1e-6, atol=1e-8)
+
+
+def test_trimul_backward_closed_forms():
+    """dz sums to zero over a position's channels (LayerNorm ignores a
+    shift); db_o is the sum of dout; a masked third residue k receives no
+    gradient through a or b on the edges (., k) / (k, .), so with w_o = 0
+    (dT = 0) every gradient but dw_o and db_o vanishes."""
+    d = trimul_case(74, N=6)
+    dout = np.random.default_rng(75).standard_normal((6, 6, 8))
+    for outgoing in (True, False):
+        g = O.tri_mul_backward(dout=dout, outgoing=outgoing, **d)
+        np.testing.assert_allclose(g["dz"].sum(-1), 0.0, atol=1e-12)
+        np.testing.assert_allclose(g["db_o"], dout.sum((0, 1)), rtol=1e-12)
+        g0 = O.tri_mul_backward(dout=dout, outgoing=outgoing, **dict(d, w_o=0 * d["w_o"]))
+        for k in ("dz", "dw_a", "dw_b", "dln_w", "dln_b"):
+            np.testing.assert_allclose(g0[k], 0.0, atol=1e-14, err_msg=k)
+        assert np.abs(g0["dw_o"]).max() > 1e-3
+
+
+def test_trimul_backward_planted_mistake_fails():
+    """dB taken as dT . A (the transpose of dT dropped), planted in a copy of
+    the chain rule, must miss the finite differences of w_b."""
+    d = trimul_case(76, N=4, CZ=4, C=3)
+    dout = np.random.default_rng(77).standard_normal((4, 4, 4))
+    x = O.layer_norm(d["z"], d["ln_w"], d["ln_b"], d["eps"])
+    a = x @ d["w_a"].T
+    keep = (d["residue_mask"] != 0).astype(float)
+    dt = dout @ d["w_o"]
+    db_wrong = np.stack([(dt[:, :, c] @ a[:, :, c]) * keep for c in range(3)], -1)
+    dw_b_wrong = db_wrong.reshape(-1, 3).T @ x.reshape(-1, 4)
+    h = 1e-6
+    fd = np.zeros_like(d["w_b"])
+    for idx in np.ndindex(d["w_b"].shape):
+        e = dict(d, w_b=d["w_b"].copy())
+        e["w_b"][idx] += h
+        fp = _trimul_loss(e, dout, True)
+        e["w_b"][idx] -= 2 * h
+        fd[idx] = (fp - _trimul_loss(e, dout, True)) / (2 * h)
+    assert np.abs(dw_b_wrong - fd).max() > 1e-3
+    np.testing.assert_allclose(O.tri_mul_backward(dout=dout, **d)["dw_b"], fd, rtol=1e-6,
+                               atol=1e-8)
+
+
+@pytest.mark.parametrize("outgoing", [True, False])
+def test_trimul_backward_entries_match_full_backward(outgoing):
+    d = trimul_case(78, N=7)
+    dout = np.random.default_rng(79).standard_normal((7, 7, 8))
+    full = O.tri_mul_backward(dout=dout, outgoing=outgoing, **d)
+    picks = [(0, 0), (2, 5), (6, 1), (3, 3)]
+    e = {k: v for k, v in d.items() if k != "b_o"}
+    got = O.tri_mul_backward_entries(dout=dout, picks=picks, outgoing=outgoing, **e)
+    for t, (i, j) in enumerate(picks):
+        np.testing.assert_allclose(got[t], full["dz"][i, j], rtol=1e-12, atol=1e-12)
+
+
 # -------------------------------------------- LayerNorm + SwiGLU transition
 
 def transition_case(seed, N=5, CZ=8, HID=12):
