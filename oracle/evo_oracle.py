@@ -491,13 +491,21 @@ def tri_mul_forward(z, residue_mask, ln_w, ln_b, eps, w_a, w_b, w_o, b_o,
     keep = (np.ones(N) if residue_mask is None
             else (np.asarray(residue_mask) != 0).astype(np.float64))
     C = a.shape[-1]
+    Ac, Bc = _channel_matrices(a, b, outgoing)
     t = np.empty((N, N, C))
     for c in range(C):
-        # edges (i, k) / (j, k) for outgoing, (k, i) / (k, j) for incoming
-        A = a[:, :, c] if outgoing else a[:, :, c].T     # A[i, k]
-        Bm = b[:, :, c] if outgoing else b[:, :, c].T    # Bm[j, k]
-        t[:, :, c] = (A * keep) @ Bm.T
+        t[:, :, c] = (Ac[c] * keep) @ Bc[c].T
     return t @ w_o.T + b_o
+
+
+def _channel_matrices(a, b, outgoing):
+    """Per channel c the matrices A_c[i, k] and B_c[j, k] of the update:
+    a[i, k, c] and b[j, k, c] (edges (i, k), (j, k)) for outgoing, a[k, i, c]
+    and b[k, j, c] for incoming; each channel's matrix is a contiguous copy,
+    so that the library matrix product serves it."""
+    perm = (2, 0, 1) if outgoing else (2, 1, 0)
+    return (np.ascontiguousarray(a.transpose(perm)),
+            np.ascontiguousarray(b.transpose(perm)))
 
 
 def tri_mul_entries(z, residue_mask, ln_w, ln_b, eps, w_a, w_b, w_o, b_o,
@@ -544,15 +552,15 @@ def tri_mul_backward(z, residue_mask, ln_w, ln_b, eps, w_a, w_b, w_o, b_o,
     keep = (np.ones(N) if residue_mask is None
             else (np.asarray(residue_mask) != 0).astype(np.float64))
     dt = dout @ w_o                       # [N, N, C]
+    dtc = np.ascontiguousarray(dt.transpose(2, 0, 1))     # dT_c[i, j]
+    Ac, Bc = _channel_matrices(a, b, outgoing)            # A_c[i, k], B_c[j, k]
     t = np.empty((N, N, C))
     da = np.empty((N, N, C))
     db = np.empty((N, N, C))
     for c in range(C):
-        A = a[:, :, c] if outgoing else a[:, :, c].T      # A[i, k]
-        Bm = b[:, :, c] if outgoing else b[:, :, c].T     # Bm[j, k]
-        t[:, :, c] = (A * keep) @ Bm.T
-        dA = (dt[:, :, c] @ Bm) * keep                    # dA[i, k]
-        dB = (dt[:, :, c].T @ A) * keep                   # dB[j, k]
+        t[:, :, c] = (Ac[c] * keep) @ Bc[c].T
+        dA = (dtc[c] @ Bc[c]) * keep                      # dA[i, k]
+        dB = (dtc[c].T @ Ac[c]) * keep                    # dB[j, k]
         da[:, :, c] = dA if outgoing else dA.T
         db[:, :, c] = dB if outgoing else dB.T
     dx = da @ w_a + db @ w_b
