@@ -32,7 +32,8 @@ Prints one JSON line per workload.  Options: --steps K --warmup W --gpus 1
 --workload NAME --all --no-cpu-baseline --cpu-lines L --calibrate-copy
 --write-traffic FETCH_CSV WRITE_CSV, --write-counters CSV..., and
 --module-train (a training step of the whole module instead), --trimul
-(the triangular multiplicative update), --transition (the fused LayerNorm +
+(the triangular multiplicative update), --trimul-bwd (its backward),
+--transition (the fused LayerNorm +
 SwiGLU transition), --transition-bwd (its backward) and --opm (the outer
 product mean).
 """
@@ -78,6 +79,9 @@ def parse():
                     help="time the triangular multiplicative update instead "
                          "(tri_mul_fwd, outgoing edges, z [768,768,128], 128 "
                          "channels, 38 residues masked)")
+    ap.add_argument("--trimul-bwd", action="store_true",
+                    help="time the multiplicative update's backward instead "
+                         "(tri_mul_bwd, the same workload, every gradient)")
     ap.add_argument("--transition", action="store_true",
                     help="time the fused LayerNorm + SwiGLU transition instead "
                          "(pair_transition_fwd, z [768,768,128], hidden 512)")
@@ -587,6 +591,57 @@ def trimul_bench(a):
     print(json.dumps(res), flush=True)
 
 
+def trimul_bwd_bench(a):
+    """The multiplicative update's backward on trimul_out_768 (dz and every
+    parameter gradient).  Prints one JSON line; the roofline entry is the
+    whole call against the dense bf16 matrix-core peak, with the gradient
+    flops counted (the recomputed forward is not)."""
+    import torch
+    from evoformer_attention_amd import metrics as M
+    from evoformer_attention_amd import ops, synth
+
+    w = dict(synth.WORKLOADS["trimul_out_768"])
+    N, CZ, C = w["N"], w["CZ"], w["C"]
+    d = synth.trimul_inputs("trimul_out_768", dout=True)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    g = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    ws = torch.empty(ops.tri_mul_bwd_workspace_bytes(g["z"].dtype, N, CZ, C),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        return ops.tri_mul_bwd(g["z"], g["mask"], g["ln_w"], g["ln_b"], g["eps"], g["w_a"],
+                               g["w_b"], g["w_o"], g["dout"], w["outgoing"], workspace=ws)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(a.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / a.steps
+    tf = M.trimul_bwd_flops(N, CZ, C) / (ms * 1e-3) / 1e12
+    res = {
+        "metric": "Triangular multiplicative update (outgoing) backward TFLOP/s (bf16), "
+                  "N_res=768, c=128",
+        "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "trimul_out_768", "N_res": N, "c_z": CZ, "channels": C,
+                   "edges": "outgoing", "masked_residues": int((d["mask"] == 0).sum()),
+                   "pass": "backward (dz, dln_w, dln_b, dw_a, dw_b, dw_o, db_o)"},
+        "roofline": {"bound": "mfma", "kernel": "tri_mul_bwd (call)", "achieved": round(tf, 2),
+                     "peak": M.MI355X_BF16_DENSE_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / M.MI355X_BF16_DENSE_TFLOPS, 4), "traffic": None},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def transition_bench(a):
     """The fused transition on transition_768.  Prints one JSON line; the
     roofline entry is the call (a weight-preparation kernel of ~1% plus the
@@ -983,7 +1038,8 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     for flag, fn in (("transition_bwd", transition_bwd_bench), ("opm", opm_bench),
-                     ("transition", transition_bench), ("trimul", trimul_bench),
+                     ("transition", transition_bench), ("trimul_bwd", trimul_bwd_bench),
+                     ("trimul", trimul_bench),
                      ("module_train", module_train)):
         if getattr(a, flag):
             fn(a)

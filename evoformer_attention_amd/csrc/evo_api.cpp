@@ -749,6 +749,57 @@ evo_status_t tri_mul_fwd(evo_dtype_t dtype, int64_t N, int64_t CZ, int64_t C,
   }
 }
 
+size_t tri_mul_bwd_workspace_bytes(evo_dtype_t dtype, int64_t N, int64_t CZ,
+                                   int64_t C) {
+  const std::string saved = g_last_error;
+  const evo_status_t st = check_trimul_sizes(dtype, N, CZ, C);
+  g_last_error = saved;
+  if (st != EVO_OK) return 0;
+  return evo::trimul_bwd_workspace((int)dtype, N, CZ, C);
+}
+
+evo_status_t tri_mul_bwd(evo_dtype_t dtype, int64_t N, int64_t CZ, int64_t C,
+                         int outgoing, const void* z,
+                         const uint8_t* residue_mask, const void* ln_w,
+                         const void* ln_b, float ln_eps, const void* w_a,
+                         const void* w_b, const void* w_o, const void* dout,
+                         void* dz, float* dln_w, float* dln_b, float* dw_a,
+                         float* dw_b, float* dw_o, float* db_o, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  try {
+    evo_status_t st = check_trimul_sizes(dtype, N, CZ, C);
+    if (st != EVO_OK) return st;
+    if (outgoing != 0 && outgoing != 1)
+      return fail(EVO_EINVAL, "outgoing=%d must be 0 or 1", outgoing);
+    if (!(ln_eps > 0.f)) return fail(EVO_EINVAL, "ln_eps must be > 0");
+    REQUIRE_PTR(z);
+    REQUIRE_PTR(ln_w);
+    REQUIRE_PTR(ln_b);
+    REQUIRE_PTR(w_a);
+    REQUIRE_PTR(w_b);
+    REQUIRE_PTR(w_o);
+    REQUIRE_PTR(dout);
+    REQUIRE_PTR(dz);
+    REQUIRE_PTR(dln_w);
+    REQUIRE_PTR(dln_b);
+    REQUIRE_PTR(dw_a);
+    REQUIRE_PTR(dw_b);
+    REQUIRE_PTR(dw_o);
+    REQUIRE_PTR(db_o);
+    OPTIONAL_PTR(residue_mask);
+    st = check_workspace("tri_mul_bwd", workspace, workspace_bytes,
+                         evo::trimul_bwd_workspace((int)dtype, N, CZ, C));
+    if (st != EVO_OK) return st;
+    if (fault_injected()) return fail(EVO_EHIP, "tri_mul_bwd: injected launch failure");
+    evo::TriMulBwdArgs a{(int)dtype, N, CZ, C, outgoing, z, residue_mask, ln_w, ln_b,
+                         ln_eps, w_a, w_b, w_o, dout, dz, dln_w, dln_b, dw_a, dw_b,
+                         dw_o, db_o, workspace};
+    return from_hip(evo::launch_trimul_bwd(a, (hipStream_t)stream), "tri_mul_bwd");
+  } catch (...) {
+    return fail(EVO_EINTERNAL, "tri_mul_bwd: internal error");
+  }
+}
+
 // ---------------------------------------------- LayerNorm + SwiGLU transition
 
 static evo_status_t check_transition_sizes(evo_dtype_t dtype, int64_t N,

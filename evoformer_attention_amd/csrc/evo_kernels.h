@@ -190,6 +190,32 @@ size_t proj_bwd_workspace(int64_t N, int64_t CZ, int64_t H);
 hipError_t launch_channel_project(const ChannelProjectArgs& a, hipStream_t s);
 size_t trimul_workspace(int dtype, int64_t N, int64_t C);
 hipError_t launch_trimul(const TriMulArgs& a, hipStream_t s);
+// Backward of the multiplicative update: dz (dtype); dln_w, dln_b [CZ],
+// dw_a, dw_b [C][CZ], dw_o [CZ][C], db_o [CZ] (fp32).
+struct TriMulBwdArgs {
+  int dtype;
+  int64_t N, CZ, C;
+  int outgoing;
+  const void* z;
+  const uint8_t* mask;
+  const void* ln_w;
+  const void* ln_b;
+  float eps;
+  const void* w_a;
+  const void* w_b;
+  const void* w_o;
+  const void* dout;
+  void* dz;
+  float* dln_w;
+  float* dln_b;
+  float* dw_a;
+  float* dw_b;
+  float* dw_o;
+  float* db_o;
+  void* workspace;  // trimul_bwd_workspace bytes
+};
+size_t trimul_bwd_workspace(int dtype, int64_t N, int64_t CZ, int64_t C);
+hipError_t launch_trimul_bwd(const TriMulBwdArgs& a, hipStream_t s);
 // T_c = A_c . B_c^T for c < C: A, B [C][Np][Kp] (columns >= K zeroed here),
 // T [C][M][M]; M <= Np, Np a multiple of pair_gemm_row_tile().
 int pair_gemm_row_tile();
@@ -260,6 +286,31 @@ size_t transition_bwd_workspace(int dtype, int64_t npos, int64_t CZ, int64_t HID
 hipError_t launch_transition_bwd(const TransitionBwdArgs& a, hipStream_t s);
 size_t transition_workspace(int dtype, int64_t CZ, int64_t HID);
 hipError_t launch_transition(const TransitionArgs& a, hipStream_t s);
+// Backward of a LayerNorm followed by nseg (2) bias-free projections of z
+// [N*N][CZ] (rows in z order): with dY_s [N*N][seg_w] the projections'
+// gradients and W_s [seg_w][CZ] their weights,
+//   dz = LayerNorm backward of sum_s dY_s . W_s       (dtype, z layout),
+//   dW_s = sum over positions of dY_s^T LN(z)         (fp32, [seg_w][CZ]),
+//   dln_w, dln_b                                      (fp32, [CZ]),
+// all reduced in a fixed order.  seg_w and CZ multiples of 32, at most 128.
+struct LnProjBwdArgs {
+  int dtype;
+  int64_t N, CZ;
+  int nseg, seg_w;
+  const void* dy[2];
+  const void* w[2];
+  const void* z;
+  const void* ln_w;
+  const void* ln_b;
+  float eps;
+  void* dz;
+  float* dw[2];
+  float* dln_w;
+  float* dln_b;
+  void* workspace;  // ln_proj_bwd_workspace bytes
+};
+size_t ln_proj_bwd_workspace(int64_t N, int64_t CZ, int seg_w);
+hipError_t launch_ln_proj_bwd(const LnProjBwdArgs& a, hipStream_t s);
 hipError_t launch_out_project_bwd(const OutProjectBwdArgs& a, hipStream_t s);
 hipError_t launch_project_bwd(const ProjectBwdArgs& a, hipStream_t s);
 

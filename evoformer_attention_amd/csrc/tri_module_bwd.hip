@@ -142,13 +142,15 @@ __device__ __forceinline__ int wrow_of(int c) {
 }
 
 // NSEG = 4 (the module: q, k, v, gate segments, then the pair-bias block,
-// LayerNorm backward) or 1 (the output projection: one z-layout segment, dX
-// written).  Eight waves, 32 positions per wave per tile.
+// LayerNorm backward), 2 (two segments and the LayerNorm backward, no
+// pair-bias block: the multiplicative update's a and b) or 1 (the output
+// projection: one z-layout segment, dX written).  Eight waves, 32 positions
+// per wave per tile.
 template <typename T, int CB, int NSEG>
 __global__ void __launch_bounds__(512) rowgrad_kernel(RowGradParams p) {
   using Op = typename Tr<T>::Op;
   constexpr int WAVES = 8;
-  constexpr bool LN = NSEG == 4;  // the module: pair-bias block and LayerNorm
+  constexpr bool LN = NSEG != 1;  // LayerNorm backward (and with NSEG 4 the pair-bias block)
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   T* sW = reinterpret_cast<T*>(smem);  // [cout][kc + PADE]
   const int KCS = p.kc + PADE;
@@ -399,8 +401,8 @@ __global__ void __launch_bounds__(512) rowgrad_kernel(RowGradParams p) {
         float bx[2][8];
         load_bias(bx, cur);
         comp_bias(bx);
-        load_z(zr, cur);
       }
+      if constexpr (LN) load_z(zr, cur);
     } else if constexpr (NSEG == 4) {
       float bx[2][8];
       load_seg(xb, 1, cur);
@@ -414,6 +416,12 @@ __global__ void __launch_bounds__(512) rowgrad_kernel(RowGradParams p) {
       load_seg(xa, 0, nxt);  // the next tile's first segment
       comp_seg(xb, 3);
       comp_bias(bx);
+    } else if constexpr (NSEG == 2) {
+      load_seg(xb, 1, cur);
+      load_z(zr, cur);
+      comp_seg(xa, 0);
+      load_seg(xa, 0, nxt);  // the next tile's first segment
+      comp_seg(xb, 1);
     } else {
       load_seg(xb, 0, nxt);
       comp_seg(xa, 0);
@@ -466,7 +474,8 @@ constexpr size_t wgrad_lds() {
 // One workgroup (eight waves) per chunk of positions computes every row of
 // M = A^T B for that chunk, so each B row (and its LayerNorm) is formed once.
 // NSEG = 4: the module (A = q, k, v, gate gradients + the pair-bias rows,
-// B = xhat); NSEG = 1: the output projection (A = dout, B = o).  Wave w owns
+// B = xhat); NSEG = 2: the multiplicative update (A = its a and b
+// gradients, B = xhat); NSEG = 1: the output projection (A = dout, B = o).  Wave w owns
 // segment w / (8/NSEG) and the column blocks w % (8/NSEG) + (8/NSEG) i,
 // i < NSEG; with NSEG = 4 also the pair-bias rows of column block w.
 template <typename T, int NSEG, bool BIAS = NSEG == 4>
@@ -902,16 +911,26 @@ hipError_t launch_rowgrad_cb(RowGradParams& p, hipStream_t s) {
 }
 
 // nseg 4 with the pair-bias block and the LayerNorm backward (the module),
-// or 1 without either (the output projection).
+// 2 with the LayerNorm backward only (the multiplicative update), or 1
+// without either (the output projection).
+template <typename T, int CB>
+hipError_t launch_rowgrad_n(RowGradParams& p, hipStream_t s) {
+  switch (p.nseg) {
+    case 4: return launch_rowgrad_cb<T, CB, 4>(p, s);
+    case 2: return launch_rowgrad_cb<T, CB, 2>(p, s);
+    default: return launch_rowgrad_cb<T, CB, 1>(p, s);
+  }
+}
 template <typename T>
 hipError_t launch_rowgrad(RowGradParams& p, hipStream_t s) {
-  const bool module = p.nseg == 4;
-  if (module != (p.dbias != nullptr) || module != (p.ln != 0)) return hipErrorInvalidValue;
+  if (p.nseg != 1 && p.nseg != 2 && p.nseg != 4) return hipErrorInvalidValue;
+  if ((p.nseg == 4) != (p.dbias != nullptr) || (p.nseg != 1) != (p.ln != 0))
+    return hipErrorInvalidValue;
   switch (p.cout / 16) {
-    case 2: return module ? launch_rowgrad_cb<T, 2, 4>(p, s) : launch_rowgrad_cb<T, 2, 1>(p, s);
-    case 4: return module ? launch_rowgrad_cb<T, 4, 4>(p, s) : launch_rowgrad_cb<T, 4, 1>(p, s);
-    case 6: return module ? launch_rowgrad_cb<T, 6, 4>(p, s) : launch_rowgrad_cb<T, 6, 1>(p, s);
-    case 8: return module ? launch_rowgrad_cb<T, 8, 4>(p, s) : launch_rowgrad_cb<T, 8, 1>(p, s);
+    case 2: return launch_rowgrad_n<T, 2>(p, s);
+    case 4: return launch_rowgrad_n<T, 4>(p, s);
+    case 6: return launch_rowgrad_n<T, 6>(p, s);
+    case 8: return launch_rowgrad_n<T, 8>(p, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -928,24 +947,27 @@ void chunking(int64_t npos, int target, int& nchunks, int& chunk_pos) {
 // KB of LDS), each over one chunk of positions.
 constexpr int kChunks = 256;
 
+template <typename T, int NSEG, bool BIAS>
+hipError_t launch_wgrad_k(WGradParams& p, hipStream_t s) {
+  const size_t lds = wgrad_lds<T, NSEG>();
+  hipError_t e =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&wgrad_kernel<T, NSEG, BIAS>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((wgrad_kernel<T, NSEG, BIAS>), dim3(p.nchunks), dim3(512), lds, s, p);
+  return hipGetLastError();
+}
+// four segments with or without the pair-bias rows; two or one without
 template <typename T>
 hipError_t launch_wgrad(WGradParams& p, hipStream_t s) {
-  const size_t lds = p.nseg == 4 ? wgrad_lds<T, 4>() : wgrad_lds<T, 1>();
-  // four segments with or without the pair-bias rows; one segment without
   const bool bias = p.dbias != nullptr;
   if (bias && p.nseg != 4) return hipErrorInvalidValue;
-  const void* fn = p.nseg != 4 ? reinterpret_cast<const void*>(&wgrad_kernel<T, 1>)
-                   : bias      ? reinterpret_cast<const void*>(&wgrad_kernel<T, 4, true>)
-                               : reinterpret_cast<const void*>(&wgrad_kernel<T, 4, false>);
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
-  if (p.nseg != 4)
-    hipLaunchKernelGGL((wgrad_kernel<T, 1>), dim3(p.nchunks), dim3(512), lds, s, p);
-  else if (bias)
-    hipLaunchKernelGGL((wgrad_kernel<T, 4, true>), dim3(p.nchunks), dim3(512), lds, s, p);
-  else
-    hipLaunchKernelGGL((wgrad_kernel<T, 4, false>), dim3(p.nchunks), dim3(512), lds, s, p);
-  return hipGetLastError();
+  switch (p.nseg) {
+    case 4: return bias ? launch_wgrad_k<T, 4, true>(p, s) : launch_wgrad_k<T, 4, false>(p, s);
+    case 2: return launch_wgrad_k<T, 2, false>(p, s);
+    case 1: return launch_wgrad_k<T, 1, false>(p, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 // Sums the chunk partials in two fixed-order stages (groups of kGroup chunks
@@ -1079,6 +1101,54 @@ hipError_t project_bwd_t(const ProjectBwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// LayerNorm + nseg projections of z, backward from the projections'
+// gradients (the multiplicative update's a and b): dz, dW_s, dgamma, dbeta.
+template <typename T>
+hipError_t ln_proj_bwd_t(const LnProjBwdArgs& a, hipStream_t s) {
+  const int N = (int)a.N, CZ = (int)a.CZ, W = a.seg_w;
+  const int npos = N * N;
+  const PartLayout L = part_layout(a.N, a.CZ, W / kHeadDim);
+  char* ws = static_cast<char*>(a.workspace);
+  RowGradParams r{};
+  r.N = N; r.ending = 0; r.npos = npos;
+  r.nseg = a.nseg; r.seg_w = W; r.in_zrow = 0;
+  for (int i = 0; i < a.nseg; ++i) { r.seg[i] = a.dy[i]; r.wseg[i] = a.w[i]; }
+  r.dbias = nullptr; r.H = 0; r.Kext = a.nseg * W;
+  r.wbias = nullptr; r.cout = CZ;
+  r.ln = 1; r.z = a.z; r.ln_w = a.ln_w; r.eps = a.eps; r.y = a.dz;
+  hipError_t e = launch_rowgrad<T>(r, s);
+  if (e != hipSuccess) return e;
+  WGradParams w{};
+  w.N = N; w.ending = 0; w.npos = npos;
+  w.nseg = a.nseg; w.a_w = W; w.a_zrow = 0;
+  for (int i = 0; i < a.nseg; ++i) w.aseg[i] = a.dy[i];
+  w.dbias = nullptr; w.H = 0;
+  w.b_w = CZ; w.b_zrow = 1; w.b_ln = 1; w.b = a.z; w.eps = a.eps;
+  w.rows_pad = a.nseg * 128;
+  chunking(npos, kChunks, w.nchunks, w.chunk_pos);
+  w.part = reinterpret_cast<float*>(ws + L.part);
+  w.cpart = reinterpret_cast<float*>(ws + L.cpart);
+  if ((e = launch_wgrad<T>(w, s)) != hipSuccess) return e;
+  FinishParams f{};
+  f.nchunks = w.nchunks; f.rows_pad = w.rows_pad; f.ncols = CZ;
+  f.nseg = a.nseg; f.a_w = W; f.H = 0; f.has_bias = 0;
+  f.part = w.part; f.cpart = w.cpart;
+  f.ln = 1; f.ln_w = a.ln_w; f.ln_b = a.ln_b;
+  for (int i = 0; i < a.nseg; ++i) f.dw[i] = a.dw[i];
+  f.mred = reinterpret_cast<float*>(ws + L.mred);
+  f.cred = reinterpret_cast<float*>(ws + L.cred);
+  if ((e = launch_finish<T>(f, reinterpret_cast<float*>(ws + L.part2),
+                           reinterpret_cast<float*>(ws + L.cpart2), s)) != hipSuccess)
+    return e;
+  LnParamParams l{};
+  l.nseg = a.nseg; l.a_w = W; l.H = 0; l.ncols = CZ;
+  for (int i = 0; i < a.nseg; ++i) l.wseg[i] = a.w[i];
+  l.wbias = nullptr; l.mred = f.mred; l.cred = f.cred;
+  l.dln_w = a.dln_w; l.dln_b = a.dln_b;
+  hipLaunchKernelGGL(lnparam_kernel<T>, dim3(CZ), dim3(256), 0, s, l);
+  return hipGetLastError();
+}
+
 struct SegLayout {
   size_t part, cpart, part2, cpart2, total;
 };
@@ -1142,6 +1212,16 @@ hipError_t launch_out_project_bwd(const OutProjectBwdArgs& a, hipStream_t s) {
 
 hipError_t launch_project_bwd(const ProjectBwdArgs& a, hipStream_t s) {
   return a.dtype == 1 ? project_bwd_t<bf16_t>(a, s) : project_bwd_t<float>(a, s);
+}
+
+size_t ln_proj_bwd_workspace(int64_t N, int64_t CZ, int seg_w) {
+  return part_layout(N, CZ, seg_w / kHeadDim).total;
+}
+
+hipError_t launch_ln_proj_bwd(const LnProjBwdArgs& a, hipStream_t s) {
+  if (a.nseg != 2 || a.seg_w % 32 != 0 || a.seg_w > 128 || a.CZ % 32 != 0 || a.CZ > 128)
+    return hipErrorInvalidValue;
+  return a.dtype == 1 ? ln_proj_bwd_t<bf16_t>(a, s) : ln_proj_bwd_t<float>(a, s);
 }
 
 }  // namespace evo

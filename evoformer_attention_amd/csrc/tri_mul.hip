@@ -557,6 +557,212 @@ hipError_t trimul_t(const TriMulArgs& a, hipStream_t s) {
   }
 }
 
+// ---------------------------------------------------------------- backward
+// Channel-major <-> position-major permutes for the backward, through LDS:
+// a workgroup takes 64 columns q of one matrix row r for every channel, so
+// it reads or writes C runs of 64 contiguous elements on the channel-major
+// side and 64 rows of C contiguous elements on the position-major side.
+constexpr int kPermQ = 64;
+constexpr int kMaxC = 128;
+
+template <typename T>
+__device__ __forceinline__ void ld16e(const T* p, T (&v)[16 / sizeof(T)]) {
+  const u32x4 u = *reinterpret_cast<const u32x4*>(p);
+  __builtin_memcpy(v, &u, 16);
+}
+template <typename T>
+__device__ __forceinline__ void st16e(T* p, const T (&v)[16 / sizeof(T)]) {
+  u32x4 u;
+  __builtin_memcpy(&u, v, 16);
+  *reinterpret_cast<u32x4*>(p) = u;
+}
+
+// Matrices [C] of (row r < rows, column q < ncols) at c*cs + r*ld + q to
+// rows dst[pos][C], pos = r*N + q (q*N + r when trans); zero where keep is
+// given and keep[q] == 0.  vec: cs and ld are multiples of 16 bytes.
+template <typename T>
+__global__ void __launch_bounds__(256) cm_to_pm_kernel(const T* src, T* dst, int C, int ncols,
+                                                       int64_t ld, int64_t cs, int N, int trans,
+                                                       const uint8_t* keep, int vec) {
+  constexpr int E = 16 / sizeof(T), TS = kMaxC + 16 / (int)sizeof(T);
+  __shared__ __attribute__((aligned(16))) T tile[kPermQ * TS];  // [q][c]
+  const int r = blockIdx.y, q0 = blockIdx.x * kPermQ, tid = threadIdx.x;
+  constexpr int CPS = kPermQ / E;  // 16-byte chunks per channel run
+  for (int e = tid; e < C * CPS; e += 256) {
+    const int c = e / CPS, ql = (e % CPS) * E, q = q0 + ql;
+    const T* sp = src + (int64_t)c * cs + (int64_t)r * ld + q;
+    T v[E];
+    if (vec && q + E <= ncols) {
+      ld16e(sp, v);
+    } else {
+#pragma unroll
+      for (int j = 0; j < E; ++j) v[j] = q + j < ncols ? sp[j] : T(0);
+    }
+#pragma unroll
+    for (int j = 0; j < E; ++j) tile[(ql + j) * TS + c] = v[j];
+  }
+  __syncthreads();
+  const int CPP = C / E;  // chunks per position
+  for (int e = tid; e < kPermQ * CPP; e += 256) {
+    const int ql = e / CPP, c0 = (e % CPP) * E, q = q0 + ql;
+    if (q >= ncols) continue;
+    const int64_t pos = trans ? (int64_t)q * N + r : (int64_t)r * N + q;
+    const bool dead = keep && keep[q] == 0;
+    T v[E];
+#pragma unroll
+    for (int j = 0; j < E; ++j) v[j] = dead ? T(0) : tile[ql * TS + c0 + j];
+    st16e(dst + pos * C + c0, v);
+  }
+}
+
+// Rows src[pos][C] to matrices [C][Np][Kp] (row r, column q) at c*cs + r*Kp
+// + q: src[pos][c] with pos = r*N + q (q*N + r when trans), zero for r >= N
+// or q >= N.  Grid: (Kp / 64, Np).
+template <typename T>
+__global__ void __launch_bounds__(256) pm_to_cm_kernel(const T* src, T* dst, int C, int N,
+                                                       int64_t Kp, int64_t cs, int trans) {
+  constexpr int E = 16 / sizeof(T), TS = kPermQ + 16 / (int)sizeof(T);
+  __shared__ __attribute__((aligned(16))) T tile[kMaxC * TS];  // [c][q]
+  const int r = blockIdx.y, q0 = blockIdx.x * kPermQ, tid = threadIdx.x;
+  const int CPP = C / E;
+  for (int e = tid; e < kPermQ * CPP; e += 256) {
+    const int ql = e / CPP, c0 = (e % CPP) * E, q = q0 + ql;
+    T v[E];
+    if (r < N && q < N) {
+      const int64_t pos = trans ? (int64_t)q * N + r : (int64_t)r * N + q;
+      ld16e(src + pos * C + c0, v);
+    } else {
+#pragma unroll
+      for (int j = 0; j < E; ++j) v[j] = T(0);
+    }
+#pragma unroll
+    for (int j = 0; j < E; ++j) tile[(c0 + j) * TS + ql] = v[j];
+  }
+  __syncthreads();
+  constexpr int CPS = kPermQ / E;
+  for (int e = tid; e < C * CPS; e += 256) {
+    const int c = e / CPS, ql = (e % CPS) * E;
+    T v[E];
+#pragma unroll
+    for (int j = 0; j < E; ++j) v[j] = tile[c * TS + ql + j];
+    st16e(dst + (int64_t)c * cs + (int64_t)r * Kp + q0 + ql, v);
+  }
+}
+
+template <typename T>
+hipError_t cm_to_pm(const T* src, T* dst, int C, int rows, int ncols, int64_t ld, int64_t cs,
+                    int N, int trans, const uint8_t* keep, hipStream_t s) {
+  constexpr int E = 16 / sizeof(T);
+  const int vec = (ld % E == 0 && cs % E == 0) ? 1 : 0;
+  hipLaunchKernelGGL(cm_to_pm_kernel<T>, dim3((ncols + kPermQ - 1) / kPermQ, rows), dim3(256), 0,
+                     s, src, dst, C, ncols, ld, cs, N, trans, keep, vec);
+  return hipGetLastError();
+}
+template <typename T>
+hipError_t pm_to_cm(const T* src, T* dst, int C, int N, int64_t Np, int64_t Kp, int trans,
+                    hipStream_t s) {
+  hipLaunchKernelGGL(pm_to_cm_kernel<T>, dim3((unsigned)(Kp / kPermQ), (unsigned)Np), dim3(256),
+                     0, s, src, dst, C, N, Kp, Np * Kp, trans);
+  return hipGetLastError();
+}
+
+struct MulBwdLayout {
+  int64_t Np, Kp;
+  size_t s1, s2, a, b, at, bt, dtc, dtt, tm, tpm, dtpm, part, total;
+};
+MulBwdLayout mul_bwd_layout(int dtype, int64_t N, int64_t CZ, int64_t C) {
+  const size_t es = dtype == 1 ? 2 : 4;
+  auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
+  MulBwdLayout L;
+  L.Np = round_up(N, kRowPad);
+  L.Kp = round_up(N, 64);
+  L.s1 = al((size_t)C * L.Np * L.Kp * es);
+  L.s2 = al((size_t)C * N * N * es);
+  L.a = 0;
+  L.b = L.s1;
+  L.at = 2 * L.s1;
+  L.bt = 3 * L.s1;
+  L.dtc = 4 * L.s1;
+  L.dtt = 5 * L.s1;
+  L.tm = 6 * L.s1;
+  L.tpm = L.tm + L.s2;
+  L.dtpm = L.tpm + L.s2;
+  L.part = L.dtpm + L.s2;
+  L.total = L.part + al(std::max(proj_bwd_workspace(N, CZ, C / kHeadDim),
+                                 ln_proj_bwd_workspace(N, CZ, (int)C)));
+  return L;
+}
+
+// Backward of the update: the chain rule of the forward, in matrix form per
+// channel (A_c, B_c as in the forward, keep the residue mask):
+//   dT = dout . W_o (position rows),  dW_o = sum dout^T t,  db_o = sum dout,
+//   dA_c = dT_c . B_c * keep[k],  dB_c = dT_c^T . A_c * keep[k],
+//   dz, dW_a, dW_b, dgamma, dbeta from the LayerNorm + projection backward.
+// Steps: the forward's operands A_c, B_c (masked) and, from the same
+// projection with the orientation flipped and no mask, their transposes
+// A_c^T, B_c^T; T_c = A_c . B_c^T recomputed (for dW_o); the output
+// projection's backward on T in position rows; dT_c and dT_c^T; the two
+// products dA_c = dT_c . (B_c^T)^T and dB_c = dT_c^T . (A_c^T)^T (masked
+// rows of A^T and B^T are not zero, so the mask is applied when dA and dB
+// return to position rows); then the LayerNorm + projection backward.
+template <typename T>
+hipError_t trimul_bwd_t(const TriMulBwdArgs& a, hipStream_t s) {
+  const MulBwdLayout L = mul_bwd_layout(a.dtype, a.N, a.CZ, a.C);
+  char* ws = static_cast<char*>(a.workspace);
+  auto at = [&](size_t off) { return reinterpret_cast<T*>(ws + off); };
+  const int N = (int)a.N, C = (int)a.C;
+  const int Np = (int)L.Np, Kp = (int)L.Kp;
+  const int64_t cs = L.Np * L.Kp;
+  ChannelProjectArgs pa{a.dtype, a.N, a.N, a.CZ, a.C, a.outgoing ? 0 : 1, a.z, a.mask,
+                        a.ln_w, a.ln_b, a.eps, a.w_a, a.w_b, at(L.a), at(L.b),
+                        cs, L.Kp, 1};
+  hipError_t e = launch_channel_project(pa, s);
+  if (e != hipSuccess) return e;
+  ChannelProjectArgs pt = pa;
+  pt.transposed = a.outgoing ? 1 : 0;
+  pt.mask = nullptr;
+  pt.a = at(L.at);
+  pt.b = at(L.bt);
+  if ((e = launch_channel_project(pt, s)) != hipSuccess) return e;
+  // T_c (channel-major [C][N][N]) -> position rows
+  if ((e = pair_gemm_t<T>(C, N, N, Np, Kp, at(L.a), at(L.b), at(L.tm), false, s)) != hipSuccess)
+    return e;
+  if ((e = cm_to_pm<T>(at(L.tm), at(L.tpm), C, N, N, N, (int64_t)N * N, N, 0, nullptr, s)) !=
+      hipSuccess)
+    return e;
+  // dT = dout . W_o, dW_o, db_o: the output projection's backward
+  OutProjectBwdArgs ob{};
+  ob.dtype = a.dtype; ob.N = a.N; ob.CZ = a.CZ; ob.H = a.C / kHeadDim; ob.ending = 0;
+  ob.o = at(L.tpm); ob.w_o = a.w_o; ob.dout = a.dout; ob.d_o = at(L.dtpm);
+  ob.dw_o = a.dw_o; ob.db_o = a.db_o; ob.workspace = ws + L.part;
+  if ((e = launch_out_project_bwd(ob, s)) != hipSuccess) return e;
+  if ((e = pm_to_cm<T>(at(L.dtpm), at(L.dtc), C, N, L.Np, L.Kp, 0, s)) != hipSuccess) return e;
+  if ((e = pm_to_cm<T>(at(L.dtpm), at(L.dtt), C, N, L.Np, L.Kp, 1, s)) != hipSuccess) return e;
+  // dA_c[i][k] = sum_j dT_c[i][j] B_c[j][k]; dB_c[j][k] = sum_i dT_c[i][j] A_c[i][k]
+  T* dA = at(L.tm);
+  T* dB = at(L.tpm);
+  if ((e = pair_gemm_t<T>(C, N, N, Np, Kp, at(L.dtc), at(L.bt), dA, false, s)) != hipSuccess)
+    return e;
+  if ((e = pair_gemm_t<T>(C, N, N, Np, Kp, at(L.dtt), at(L.at), dB, false, s)) != hipSuccess)
+    return e;
+  // back to position rows (z order), masked third residues zeroed: A_c[i][k]
+  // is the edge (i, k) outgoing, (k, i) incoming
+  T* da = at(L.a);
+  T* db = at(L.b);
+  const int tr = a.outgoing ? 0 : 1;
+  if ((e = cm_to_pm<T>(dA, da, C, N, N, N, (int64_t)N * N, N, tr, a.mask, s)) != hipSuccess)
+    return e;
+  if ((e = cm_to_pm<T>(dB, db, C, N, N, N, (int64_t)N * N, N, tr, a.mask, s)) != hipSuccess)
+    return e;
+  LnProjBwdArgs lb{};
+  lb.dtype = a.dtype; lb.N = a.N; lb.CZ = a.CZ; lb.nseg = 2; lb.seg_w = C;
+  lb.dy[0] = da; lb.dy[1] = db; lb.w[0] = a.w_a; lb.w[1] = a.w_b;
+  lb.z = a.z; lb.ln_w = a.ln_w; lb.ln_b = a.ln_b; lb.eps = a.eps;
+  lb.dz = a.dz; lb.dw[0] = a.dw_a; lb.dw[1] = a.dw_b; lb.dln_w = a.dln_w; lb.dln_b = a.dln_b;
+  lb.workspace = ws + L.part;
+  return launch_ln_proj_bwd(lb, s);
+}
+
 }  // namespace
 
 size_t trimul_workspace(int dtype, int64_t N, int64_t C) {
@@ -565,6 +771,14 @@ size_t trimul_workspace(int dtype, int64_t N, int64_t C) {
 
 hipError_t launch_trimul(const TriMulArgs& a, hipStream_t s) {
   return a.dtype == 1 ? trimul_t<bf16_t>(a, s) : trimul_t<float>(a, s);
+}
+
+size_t trimul_bwd_workspace(int dtype, int64_t N, int64_t CZ, int64_t C) {
+  return mul_bwd_layout(dtype, N, CZ, C).total;
+}
+
+hipError_t launch_trimul_bwd(const TriMulBwdArgs& a, hipStream_t s) {
+  return a.dtype == 1 ? trimul_bwd_t<bf16_t>(a, s) : trimul_bwd_t<float>(a, s);
 }
 
 int pair_gemm_row_tile() { return kRowPad; }

@@ -101,6 +101,14 @@ def trimul_flops(N, CZ, C):
     return 2.0 * N * N * CZ * 2 * C + 2.0 * C * N ** 3 + 2.0 * N * N * C * CZ
 
 
+def trimul_bwd_flops(N, CZ, C):
+    """Counted flops of the multiplicative update's backward: dT = dout . W_o
+    and dW_o = dout^T t (2 x 2 N^2 CZ C), the two per-channel products dA and
+    dB (2 x 2 C N^3), dx = da . W_a + db . W_b and dW_a, dW_b (4 x 2 N^2 C
+    CZ).  The recomputed forward (a, b and t) is not counted."""
+    return 4.0 * C * N ** 3 + 12.0 * N * N * C * CZ
+
+
 def transition_bwd_flops(N, CZ, HID):
     """Counted flops of the transition backward per position: the recomputed
     u, v (2 x 2 HID CZ), dh (2 HID CZ), dx (2 x 2 HID CZ) and the three

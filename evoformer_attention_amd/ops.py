@@ -24,6 +24,7 @@ __all__ = ["EvoAttnError", "lib", "evo_abi_version", "evo_attn_fwd",
            "pair_transition_workspace_bytes",
            "outer_product_mean_workspace_bytes", "outer_product_mean_fwd",
            "pair_transition_bwd_workspace_bytes", "pair_transition_bwd",
+           "tri_mul_bwd_workspace_bytes", "tri_mul_bwd",
            "LIB_PATH", "EXPORTS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
@@ -88,6 +89,9 @@ EXPORTS = {
                                  _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "outer_product_mean_fwd": (_I, [_I, _I64, _I64, _I64, _I64, _I64, _P, _P,
                                     _P, _F, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "tri_mul_bwd_workspace_bytes": (_SZ, [_I, _I64, _I64, _I64]),
+    "tri_mul_bwd": (_I, [_I, _I64, _I64, _I64, _I, _P, _P, _P, _P, _F, _P, _P,
+                         _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
 }
 
 
@@ -663,4 +667,41 @@ def pair_transition_bwd(z, ln_w, ln_b, eps, w_a, w_b, w_o, dout, workspace=None)
                                    _ptr(res["dw_o"]), _ptr(workspace),
                                    workspace.numel(), _stream(z.device))
     _check("pair_transition_bwd", st)
+    return res
+
+
+def tri_mul_bwd_workspace_bytes(dtype, N, CZ, C):
+    code = EVO_BF16 if dtype == torch.bfloat16 else EVO_FP32
+    return lib().tri_mul_bwd_workspace_bytes(code, N, CZ, C)
+
+
+def tri_mul_bwd(z, residue_mask, ln_w, ln_b, eps, w_a, w_b, w_o, dout,
+                outgoing=True, workspace=None):
+    """Backward of tri_mul_fwd -> dict of dz (dtype) and the fp32 parameter
+    gradients dln_w, dln_b, dw_a, dw_b, dw_o, db_o."""
+    N, CZ = _pair_rep("z", z)
+    dt = z.dtype
+    if not isinstance(w_a, torch.Tensor) or w_a.dim() != 2:
+        raise EvoAttnError("binding", EVO_EINVAL, "w_a must be [C, CZ]")
+    C = w_a.shape[0]
+    _dev_tensors([("z", z, None, None),
+                  ("ln_w", ln_w, dt, (CZ,)),
+                  ("ln_b", ln_b, dt, (CZ,)),
+                  ("w_a", w_a, dt, (C, CZ)),
+                  ("w_b", w_b, dt, (C, CZ)),
+                  ("w_o", w_o, dt, (CZ, C)),
+                  ("dout", dout, dt, (N, N, CZ)),
+                  ("residue_mask", residue_mask, torch.uint8, (N,))])
+    workspace = _workspace(tri_mul_bwd_workspace_bytes(dt, N, CZ, C), z.device, workspace)
+    res = {"dz": torch.empty_like(z)}
+    for k, shape in (("dln_w", (CZ,)), ("dln_b", (CZ,)), ("dw_a", (C, CZ)),
+                     ("dw_b", (C, CZ)), ("dw_o", (CZ, C)), ("db_o", (CZ,))):
+        res[k] = torch.empty(shape, dtype=torch.float32, device=z.device)
+    st = lib().tri_mul_bwd(_dtype_code(z), N, CZ, C, int(bool(outgoing)), _ptr(z),
+                           _ptr(residue_mask), _ptr(ln_w), _ptr(ln_b), float(eps),
+                           _ptr(w_a), _ptr(w_b), _ptr(w_o), _ptr(dout), _ptr(res["dz"]),
+                           _ptr(res["dln_w"]), _ptr(res["dln_b"]), _ptr(res["dw_a"]),
+                           _ptr(res["dw_b"]), _ptr(res["dw_o"]), _ptr(res["db_o"]),
+                           _ptr(workspace), workspace.numel(), _stream(z.device))
+    _check("tri_mul_bwd", st)
     return res

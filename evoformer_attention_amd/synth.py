@@ -143,11 +143,12 @@ def module_inputs(name, seed=0):
                        mask=w["mask"], dout=(w["kind"] == "module_bwd"))
 
 
-def rand_trimul(N, CZ, C, dtype, seed=0, mask=None):
+def rand_trimul(N, CZ, C, dtype, seed=0, mask=None, dout=False):
     """Multiplicative-update inputs: z ~ N(0,1) [N,N,CZ]; w_a, w_b [C, CZ]
     ~ N(0, 1/CZ); w_o [CZ, C] ~ N(0, 1/C) / sqrt(N) (the update sums N
     products); LayerNorm weight 1 + N(0, 0.2^2), bias N(0, 0.2^2); b_o
-    N(0, 0.5^2).  Draw order: z, w_a, w_b, w_o, mask, ln_w, ln_b, b_o."""
+    N(0, 0.5^2); with dout, an upstream gradient ~ N(0,1) [N,N,CZ].  Draw
+    order: z, w_a, w_b, w_o, mask, ln_w, ln_b, b_o, dout."""
     gen = torch.Generator().manual_seed(seed)
 
     def draw(shape, std=1.0):
@@ -162,13 +163,16 @@ def rand_trimul(N, CZ, C, dtype, seed=0, mask=None):
     d["ln_b"] = draw((CZ,), 0.2)
     d["b_o"] = draw((CZ,), 0.5)
     d["eps"] = 1e-5
+    if dout:
+        d["dout"] = draw((N, N, CZ))
     return d
 
 
-def trimul_inputs(name, seed=0):
+def trimul_inputs(name, seed=0, dout=False):
     w = WORKLOADS[name]
     assert w["kind"] == "trimul"
-    return rand_trimul(w["N"], w["CZ"], w["C"], w["dtype"], seed=seed, mask=w["mask"])
+    return rand_trimul(w["N"], w["CZ"], w["C"], w["dtype"], seed=seed, mask=w["mask"],
+                       dout=dout)
 
 
 def rand_transition(N, CZ, HID, dtype, seed=0, dout=False):

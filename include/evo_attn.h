@@ -392,6 +392,46 @@ evo_status_t tri_mul_fwd(evo_dtype_t dtype, int64_t N, int64_t CZ, int64_t C,
                          void* stream);
 
 /*
+ * tri_mul_bwd -- gradients of tri_mul_fwd for training.  The pages print no
+ * backward for the update (it is part of the trained trunk, "Evoformer: the
+ * memory wall ZeRO cannot move", section "The three operations"); this is
+ * the chain rule of the forward.  Per channel, with A_c[i,k] = a[i,k,c]
+ * (outgoing; a[k,i,c] incoming), B_c likewise and dT = dout . w_o:
+ *   dA_c = (dT_c . B_c) * keep[k],   dB_c = (dT_c^T . A_c) * keep[k],
+ *   dz   = LayerNorm backward of (da . w_a + db . w_b),
+ *   dw_a = sum over positions of da^T LN(z), dw_b likewise,
+ *   dw_o = sum over positions of dout^T t,   db_o = sum of dout,
+ *   dln_w, dln_b the LayerNorm parameter gradients.
+ * The activations (a, b, t) are recomputed from z; the two products per
+ * channel run on the matrix cores; sums over positions are deterministic
+ * (fixed order, no atomics).
+ *
+ *   N, CZ, C, outgoing, z, residue_mask, ln_w, ln_b, ln_eps, w_a, w_b, w_o
+ *              as tri_mul_fwd (b_o is not needed).
+ *   dout       [N,N,CZ] dtype: the upstream gradient.
+ *   dz         [N,N,CZ] dtype (written).
+ *   dln_w, dln_b [CZ] fp32; dw_a, dw_b [C, CZ] fp32; dw_o [CZ, C] fp32;
+ *              db_o [CZ] fp32 (written, not accumulated).
+ *   workspace  tri_mul_bwd_workspace_bytes(...) bytes, caller-owned: the
+ *              operands and their transposes, t, dT and the products, and
+ *              the reduction partials (about 6 C N^2 + 3 C N^2 elements of
+ *              dtype; 1.4 GB in bf16 at N = 768, C = 128).
+ * Sizes outside tri_mul_fwd's limits: EVO_ENOTSUP; null required pointers
+ * or a short workspace: EVO_EINVAL.  Pointers: device memory, 16-byte
+ * aligned.  Enqueued on `stream`.
+ */
+size_t tri_mul_bwd_workspace_bytes(evo_dtype_t dtype, int64_t N, int64_t CZ,
+                                   int64_t C);
+evo_status_t tri_mul_bwd(evo_dtype_t dtype, int64_t N, int64_t CZ, int64_t C,
+                         int outgoing, const void* z,
+                         const uint8_t* residue_mask, const void* ln_w,
+                         const void* ln_b, float ln_eps, const void* w_a,
+                         const void* w_b, const void* w_o, const void* dout,
+                         void* dz, float* dln_w, float* dln_b, float* dw_a,
+                         float* dw_b, float* dw_o, float* db_o, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/*
  * pair_transition_fwd -- LayerNorm + linear + SwiGLU transition of the pair
  * representation, fused (EvoFusion, "MegaFold: Efficient Training of
  * Next-Generation 3D Attention Protein Models on Cross-Platform GPUs",
