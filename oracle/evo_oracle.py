@@ -49,6 +49,7 @@ __all__ = [
     "tri_module_backward", "tri_mul_forward", "tri_mul_entries",
     "tri_mul_backward", "tri_mul_backward_entries",
     "transition_forward", "outer_product_mean", "transition_backward", "transition_weight_grad_units", "outer_product_mean_pairs",
+    "outer_product_mean_backward", "outer_product_mean_backward_sampled",
 ]
 
 
@@ -704,6 +705,95 @@ def outer_product_mean(m, ln_w, ln_b, eps, w_a, w_b, w_o, b_o):
         o_i = np.einsum("sc,sjd->jcd", a[:, i, :], b) / S   # [N, C, C]
         out[i] = o_i.reshape(N, C * C) @ w_o.T + b_o
     return out
+
+
+def outer_product_mean_backward(m, ln_w, ln_b, eps, w_a, w_b, w_o, b_o, dout):
+    """Gradients of outer_product_mean for training.  The pages print no
+    backward (the bridge is part of the trained trunk, [COURSE] "The three
+    operations"); this is the chain rule of the forward above, nothing else.
+    With P[i, j, c, d] = sum_s a[s, i, c] b[s, j, d] and
+    dO[i, j, c, d] = (dout[i, j] . w_o)[c*C + d] / S:
+        da[s, i, c] = sum_{j, d} dO[i, j, c, d] b[s, j, d],
+        db[s, j, d] = sum_{i, c} dO[i, j, c, d] a[s, i, c],
+        dx = da . w_a + db . w_b,  dm = LayerNorm backward of dx,
+        dw_a = sum_{s, i} da^T x,  dw_b likewise,
+        dw_o = sum_{i, j} dout[i, j]^T flatten(P[i, j]) / S,  db_o = sum dout.
+    Returns dict(dm, dln_w, dln_b, dw_a, dw_b, dw_o, db_o)."""
+    m = np.asarray(m, np.float64)
+    S, N, CM = m.shape
+    dout = np.asarray(dout, np.float64)
+    x = layer_norm(m, ln_w, ln_b, eps)
+    a = x @ w_a.T                                   # [S, N, C]
+    b = x @ w_b.T
+    C = a.shape[-1]
+    CZ = w_o.shape[0]
+    dO = (dout @ w_o).reshape(N, N, C, C) / S       # [i, j, c, d]
+    # the [N*C, S] operand matrices of the forward: rows (i, c), columns s
+    A = a.transpose(1, 2, 0).reshape(N * C, S)
+    B = b.transpose(1, 2, 0).reshape(N * C, S)
+    dP = dO.transpose(0, 2, 1, 3).reshape(N * C, N * C)   # rows (i, c), cols (j, d)
+    dA = dP @ B                                     # [(i, c), s]
+    dB = dP.T @ A                                   # [(j, d), s]
+    da = dA.reshape(N, C, S).transpose(2, 0, 1)     # [s, i, c]
+    db = dB.reshape(N, C, S).transpose(2, 0, 1)
+    dx = da @ w_a + db @ w_b
+    dm, dln_w, dln_b = layer_norm_backward(m, ln_w, eps, dx)
+    P = (A @ B.T).reshape(N, C, N, C).transpose(0, 2, 1, 3)   # [i, j, c, d]
+    flat = lambda v: v.reshape(-1, v.shape[-1])
+    dw_o = flat(dout).T @ P.reshape(N * N, C * C) / S
+    return dict(dm=dm, dln_w=dln_w, dln_b=dln_b,
+                dw_a=flat(da).T @ flat(x), dw_b=flat(db).T @ flat(x),
+                dw_o=dw_o, db_o=flat(dout).sum(axis=0))
+
+
+def outer_product_mean_backward_sampled(m, ln_w, ln_b, eps, w_a, w_b, w_o, dout,
+                                        dm_picks, wa_rows, wb_rows, wo_cols):
+    """Parts of outer_product_mean_backward that a few channels or
+    positions determine, each formed from the same chain rule for those
+    alone (so that a large problem stays cheap):
+      dm[s, i] for (s, i) in dm_picks (da[s, i] needs dO[i, :] and b[s, :],
+               db[s, i] needs dO[:, i] and a[s, :]),
+      dw_a[c] for c in wa_rows (da[:, :, c] over every (s, i)),
+      dw_b[d] for d in wb_rows,
+      dw_o[:, c*C + d] for (c, d) in wo_cols (P[:, :, c, d] alone).
+    Returns (dm [len(dm_picks), CM], dw_a rows, dw_b rows, dw_o columns
+    [CZ, len(wo_cols)])."""
+    m = np.asarray(m, np.float64)
+    S, N, CM = m.shape
+    dout = np.asarray(dout, np.float64)
+    x = layer_norm(m, ln_w, ln_b, eps)
+    a = x @ w_a.T                                   # [S, N, C]
+    b = x @ w_b.T
+    C = a.shape[-1]
+    wo4 = w_o.reshape(-1, C, C)                     # [CZ, c, d]
+    dm = []
+    for s_, i in dm_picks:
+        dO_row = np.einsum("jz,zcd->jcd", dout[i], wo4) / S     # dO[i, j, c, d]
+        dO_col = np.einsum("jz,zcd->jcd", dout[:, i], wo4) / S  # dO[j, i, c, d]
+        da = np.einsum("jcd,jd->c", dO_row, b[s_])
+        db = np.einsum("jcd,jc->d", dO_col, a[s_])
+        dx = da @ w_a + db @ w_b
+        g, _, _ = layer_norm_backward(m[s_, i][None], ln_w, eps, dx[None])
+        dm.append(g[0])
+    xf = x.reshape(-1, CM)
+    bf = b.reshape(S, N * C)                        # b[s, (j, d)]
+    ra = []
+    for c in wa_rows:
+        dO_c = (dout @ wo4[:, c, :]) / S            # dO[i, j, c, d] over (i, j, d)
+        da_c = bf @ dO_c.reshape(N, N * C).T        # da[s, i, c]: sum over (j, d)
+        ra.append(da_c.reshape(-1) @ xf)
+    af = a.reshape(S, N * C)                        # a[s, (i, c)]
+    rb = []
+    for d_ in wb_rows:
+        dO_d = (dout @ wo4[:, :, d_]) / S           # dO[i, j, c, d] over (i, j, c)
+        dO_t = dO_d.transpose(1, 0, 2).reshape(N, N * C)    # [j, (i, c)]
+        db_d = af @ dO_t.T                          # db[s, j, d]: sum over (i, c)
+        rb.append(db_d.reshape(-1) @ xf)
+    ro = []
+    for c, d_ in wo_cols:
+        P_cd = a[:, :, c].T @ b[:, :, d_]           # P[i, j, c, d]
+        ro.append(dout.reshape(N * N, -1).T @ P_cd.reshape(-1) / S)
+    return np.stack(dm), np.stack(ra), np.stack(rb), np.stack(ro, axis=1)
 
 
 def outer_product_mean_pairs(m, ln_w, ln_b, eps, w_a, w_b, w_o, b_o, picks):

@@ -1111,3 +1111,108 @@ def test_mutant_opm_sum_instead_of_mean_is_caught(monkeypatch):
     monkeypatch.setattr(O, "outer_product_mean", summed)
     with pytest.raises(AssertionError):
         test_opm_matches_torch_einsum()
+
+
+OPM_GRADS = (("m", "dm"), ("ln_w", "dln_w"), ("ln_b", "dln_b"), ("w_a", "dw_a"),
+             ("w_b", "dw_b"), ("w_o", "dw_o"), ("b_o", "db_o"))
+
+
+def test_opm_backward_matches_torch_autograd():
+    """torch.autograd (fp64) of the bridge written with F.layer_norm,
+    F.linear and torch.einsum: every gradient."""
+    d = opm_case(85, S=6, N=5, CM=10, C=4, CZ=9)
+    dout = np.random.default_rng(86).standard_normal((5, 5, 9))
+    t = {k: torch.tensor(v, requires_grad=True) for k, v in d.items()
+         if isinstance(v, np.ndarray)}
+    x = F.layer_norm(t["m"], (10,), t["ln_w"], t["ln_b"], d["eps"])
+    a, b = F.linear(x, t["w_a"]), F.linear(x, t["w_b"])
+    o = torch.einsum("sic,sjd->ijcd", a, b) / 6
+    out = F.linear(o.reshape(5, 5, 16), t["w_o"], t["b_o"])
+    (out * torch.tensor(dout)).sum().backward()
+    got = O.outer_product_mean_backward(dout=dout, **d)
+    for k_t, k_o in OPM_GRADS:
+        np.testing.assert_allclose(got[k_o], t[k_t].grad.numpy(), rtol=1e-10, atol=1e-12,
+                                   err_msg=k_o)
+
+
+def _opm_loss(d, dout):
+    return float((O.outer_product_mean(**d) * dout).sum())
+
+
+@pytest.mark.parametrize("which", ["m", "ln_w", "ln_b", "w_a", "w_b", "w_o", "b_o"])
+def test_opm_backward_matches_central_finite_differences(which):
+    """The definition of the derivative: central differences of
+    sum(out * dout) on a tiny case, every element of the chosen input."""
+    d = opm_case(87, S=3, N=3, CM=4, C=2, CZ=3)
+    dout = np.random.default_rng(88).standard_normal((3, 3, 3))
+    got = O.outer_product_mean_backward(dout=dout, **d)["d" + which]
+    h = 1e-6
+    fd = np.zeros_like(d[which])
+    for idx in np.ndindex(d[which].shape):
+        e = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in d.items()}
+        e[which][idx] += h
+        fp = _opm_loss(e, dout)
+        e[which][idx] -= 2 * h
+        fd[idx] = (fp - _opm_loss(e, dout)) / (2 * h)
+    np.testing.assert_allclose(got, fd, rtol=1e-6, atol=1e-8)
+
+
+def test_opm_backward_closed_forms():
+    """dm sums to zero over each (sequence, residue)'s channels (LayerNorm
+    ignores a shift); db_o is the sum of dout; with w_o = 0 only dw_o and
+    db_o survive; permuting the sequences permutes dm alike and leaves every
+    parameter gradient unchanged."""
+    d = opm_case(89, S=5, N=4)
+    dout = np.random.default_rng(90).standard_normal((4, 4, 7))
+    g = O.outer_product_mean_backward(dout=dout, **d)
+    np.testing.assert_allclose(g["dm"].sum(-1), 0.0, atol=1e-12)
+    np.testing.assert_allclose(g["db_o"], dout.sum((0, 1)), rtol=1e-12)
+    g0 = O.outer_product_mean_backward(dout=dout, **dict(d, w_o=0 * d["w_o"]))
+    for k in ("dm", "dw_a", "dw_b", "dln_w", "dln_b"):
+        np.testing.assert_allclose(g0[k], 0.0, atol=1e-14, err_msg=k)
+    assert np.abs(g0["dw_o"]).max() > 1e-3
+    perm = np.random.default_rng(3).permutation(5)
+    gp = O.outer_product_mean_backward(dout=dout, **dict(d, m=d["m"][perm]))
+    np.testing.assert_allclose(gp["dm"], g["dm"][perm], rtol=1e-12, atol=1e-12)
+    for k in ("dw_a", "dw_b", "dw_o", "dln_w", "dln_b"):
+        np.testing.assert_allclose(gp[k], g[k], rtol=1e-11, atol=1e-12, err_msg=k)
+
+
+def test_opm_backward_planted_mistake_fails():
+    """The mean's 1/S dropped from dO (the gradient of a sum instead of a
+    mean), planted in a copy of the chain rule, must miss the finite
+    differences of w_a."""
+    d = opm_case(91, S=3, N=3, CM=4, C=2, CZ=3)
+    dout = np.random.default_rng(92).standard_normal((3, 3, 3))
+    S, N, CM = d["m"].shape
+    C = d["w_a"].shape[0]
+    x = O.layer_norm(d["m"], d["ln_w"], d["ln_b"], d["eps"])
+    b = x @ d["w_b"].T
+    dO = (dout @ d["w_o"]).reshape(N, N, C, C)             # no 1/S
+    da = np.einsum("ijcd,sjd->sic", dO, b)
+    dw_a_wrong = da.reshape(-1, C).T @ x.reshape(-1, CM)
+    h = 1e-6
+    fd = np.zeros_like(d["w_a"])
+    for idx in np.ndindex(d["w_a"].shape):
+        e = dict(d, w_a=d["w_a"].copy())
+        e["w_a"][idx] += h
+        fp = _opm_loss(e, dout)
+        e["w_a"][idx] -= 2 * h
+        fd[idx] = (fp - _opm_loss(e, dout)) / (2 * h)
+    assert np.abs(dw_a_wrong - fd).max() > 1e-3
+    np.testing.assert_allclose(O.outer_product_mean_backward(dout=dout, **d)["dw_a"], fd,
+                               rtol=1e-6, atol=1e-8)
+
+
+def test_opm_backward_sampled_matches_full_backward():
+    d = opm_case(93, S=5, N=6, CM=8, C=3, CZ=7)
+    dout = np.random.default_rng(94).standard_normal((6, 6, 7))
+    full = O.outer_product_mean_backward(dout=dout, **d)
+    e = {k: v for k, v in d.items() if k != "b_o"}
+    dm, ra, rb, ro = O.outer_product_mean_backward_sampled(
+        dout=dout, dm_picks=[(0, 0), (4, 5), (2, 3)], wa_rows=[0, 2], wb_rows=[1],
+        wo_cols=[(0, 0), (2, 1)], **e)
+    np.testing.assert_allclose(dm, full["dm"][[0, 4, 2], [0, 5, 3]], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(ra, full["dw_a"][[0, 2]], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(rb, full["dw_b"][[1]], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(ro, full["dw_o"][:, [0, 2 * 3 + 1]], rtol=1e-12, atol=1e-12)
