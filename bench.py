@@ -34,8 +34,8 @@ Prints one JSON line per workload.  Options: --steps K --warmup W --gpus 1
 --module-train (a training step of the whole module instead), --trimul
 (the triangular multiplicative update), --trimul-bwd (its backward),
 --transition (the fused LayerNorm +
-SwiGLU transition), --transition-bwd (its backward) and --opm (the outer
-product mean).
+SwiGLU transition), --transition-bwd (its backward), --opm (the outer
+product mean) and --opm-bwd (its backward).
 """
 import argparse
 import hashlib
@@ -92,6 +92,9 @@ def parse():
                     help="time the outer product mean instead "
                          "(outer_product_mean_fwd, m [1024,768,256], 32 "
                          "channels, out [768,768,128])")
+    ap.add_argument("--opm-bwd", action="store_true",
+                    help="time the outer product mean's backward instead "
+                         "(outer_product_mean_bwd, the same workload, every gradient)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU work: turn two rocprofv3 --pmc counter files "
                          "(FETCH_SIZE run, WRITE_SIZE run) of a --calibrate-copy "
@@ -740,6 +743,57 @@ def transition_bwd_bench(a):
     print(json.dumps(res), flush=True)
 
 
+def opm_bwd_bench(a):
+    """The outer product mean's backward on opm_1024x768 (dm and every
+    parameter gradient).  Prints one JSON line; the roofline entry is the
+    whole call against the dense bf16 matrix-core peak, with the gradient
+    flops counted (the recomputed forward is not)."""
+    import torch
+    from evoformer_attention_amd import metrics as M
+    from evoformer_attention_amd import ops, synth
+
+    w = dict(synth.WORKLOADS["opm_1024x768"])
+    S, N, CM, C, CZ = w["S"], w["N"], w["CM"], w["C"], w["CZ"]
+    d = synth.opm_inputs("opm_1024x768", dout=True)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    g = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    ws = torch.empty(ops.outer_product_mean_bwd_workspace_bytes(g["m"].dtype, S, N, CM, C, CZ),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        return ops.outer_product_mean_bwd(g["m"], g["ln_w"], g["ln_b"], g["eps"], g["w_a"],
+                                          g["w_b"], g["w_o"], g["dout"], workspace=ws)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(a.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / a.steps
+    tf = M.opm_bwd_flops(S, N, CM, C, CZ) / (ms * 1e-3) / 1e12
+    res = {
+        "metric": "Outer product mean backward TFLOP/s (bf16), N_seq=1024, N_res=768",
+        "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "opm_1024x768", "N_seq": S, "N_res": N, "c_m": CM,
+                   "channels": C, "c_z": CZ,
+                   "pass": "backward (dm, dln_w, dln_b, dw_a, dw_b, dw_o, db_o)"},
+        "roofline": {"bound": "mfma", "kernel": "outer_product_mean_bwd (call)",
+                     "achieved": round(tf, 2), "peak": M.MI355X_BF16_DENSE_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf / M.MI355X_BF16_DENSE_TFLOPS, 4),
+                     "traffic": None},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def opm_bench(a):
     """The outer product mean on opm_1024x768.  Prints one JSON line; the
     roofline entry is the whole call (projections, the product on the matrix
@@ -1037,7 +1091,8 @@ def main():
               "library has no multi-GPU path (no sharding, no collectives).",
               file=sys.stderr)
         sys.exit(2)
-    for flag, fn in (("transition_bwd", transition_bwd_bench), ("opm", opm_bench),
+    for flag, fn in (("transition_bwd", transition_bwd_bench), ("opm_bwd", opm_bwd_bench),
+                     ("opm", opm_bench),
                      ("transition", transition_bench), ("trimul_bwd", trimul_bwd_bench),
                      ("trimul", trimul_bench),
                      ("module_train", module_train)):

@@ -900,6 +900,57 @@ evo_status_t outer_product_mean_fwd(evo_dtype_t dtype, int64_t S, int64_t N, int
   }
 }
 
+size_t outer_product_mean_bwd_workspace_bytes(evo_dtype_t dtype, int64_t S, int64_t N,
+                                              int64_t CM, int64_t C, int64_t CZ) {
+  const std::string saved = g_last_error;
+  evo_status_t st = check_opm_sizes(dtype, S, N, CM, C, CZ);
+  if (st == EVO_OK && CM > 128 && CM != 256) st = EVO_ENOTSUP;
+  g_last_error = saved;
+  if (st != EVO_OK) return 0;
+  return evo::opm_bwd_workspace((int)dtype, S, N, CM, C, CZ);
+}
+
+evo_status_t outer_product_mean_bwd(evo_dtype_t dtype, int64_t S, int64_t N, int64_t CM,
+                                    int64_t C, int64_t CZ, const void* m, const void* ln_w,
+                                    const void* ln_b, float ln_eps, const void* w_a,
+                                    const void* w_b, const void* w_o, const void* dout,
+                                    void* dm, float* dln_w, float* dln_b, float* dw_a,
+                                    float* dw_b, float* dw_o, float* db_o, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  try {
+    evo_status_t st = check_opm_sizes(dtype, S, N, CM, C, CZ);
+    if (st != EVO_OK) return st;
+    if (CM > 128 && CM != 256)
+      return fail(EVO_ENOTSUP, "outer_product_mean_bwd: CM=%lld must be at most 128, or 256",
+                  (long long)CM);
+    if (!(ln_eps > 0.f)) return fail(EVO_EINVAL, "ln_eps must be > 0");
+    REQUIRE_PTR(m);
+    REQUIRE_PTR(ln_w);
+    REQUIRE_PTR(ln_b);
+    REQUIRE_PTR(w_a);
+    REQUIRE_PTR(w_b);
+    REQUIRE_PTR(w_o);
+    REQUIRE_PTR(dout);
+    REQUIRE_PTR(dm);
+    REQUIRE_PTR(dln_w);
+    REQUIRE_PTR(dln_b);
+    REQUIRE_PTR(dw_a);
+    REQUIRE_PTR(dw_b);
+    REQUIRE_PTR(dw_o);
+    REQUIRE_PTR(db_o);
+    st = check_workspace("outer_product_mean_bwd", workspace, workspace_bytes,
+                         evo::opm_bwd_workspace((int)dtype, S, N, CM, C, CZ));
+    if (st != EVO_OK) return st;
+    if (fault_injected())
+      return fail(EVO_EHIP, "outer_product_mean_bwd: injected launch failure");
+    evo::OpmBwdArgs a{(int)dtype, S, N, CM, C, CZ, m, ln_w, ln_b, ln_eps, w_a, w_b, w_o,
+                      dout, dm, dln_w, dln_b, dw_a, dw_b, dw_o, db_o, workspace};
+    return from_hip(evo::launch_opm_bwd(a, (hipStream_t)stream), "outer_product_mean_bwd");
+  } catch (...) {
+    return fail(EVO_EINTERNAL, "outer_product_mean_bwd: internal error");
+  }
+}
+
 static evo_status_t check_transition_bwd_sizes(evo_dtype_t dtype, int64_t N, int64_t CZ,
                                                int64_t HID) {
   evo_status_t st = check_transition_sizes(dtype, N, CZ, HID);

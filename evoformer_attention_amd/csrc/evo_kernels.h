@@ -221,6 +221,16 @@ hipError_t launch_trimul_bwd(const TriMulBwdArgs& a, hipStream_t s);
 int pair_gemm_row_tile();
 hipError_t launch_pair_gemm(int dtype, int C, int M, int K, int Np, int Kp, void* a, void* b,
                             void* t, bool a_frag, hipStream_t s);
+// The same with M rows from a and M2 from b: A [C][Np][Kp], B [C][Np2][Kp],
+// T [C][M][M2]; Np and Np2 multiples of pair_gemm_row_tile().
+hipError_t launch_pair_gemm_rect(int dtype, int C, int M, int M2, int K, int Np, int Np2, int Kp,
+                                 void* a, void* b, void* t, bool a_frag, hipStream_t s);
+// Channel-major matrices [C] of (row r < rows, column q < ncols) at c*cs +
+// r*ld + q to position rows dst[pos][C], pos = r*N + q (q*N + r when trans),
+// zero where keep is given and keep[q] == 0.  C a multiple of 32, at most 128.
+hipError_t launch_cm_to_pm(int dtype, const void* src, void* dst, int C, int rows, int ncols,
+                           int64_t ld, int64_t cs, int N, int trans, const uint8_t* keep,
+                           hipStream_t s);
 // Outer product mean: m [S][N][CM] -> out [N][N][CZ].
 struct OpmArgs {
   int dtype;
@@ -238,6 +248,30 @@ struct OpmArgs {
 };
 size_t opm_workspace(int dtype, int64_t S, int64_t N, int64_t C);
 hipError_t launch_opm(const OpmArgs& a, hipStream_t s);
+// Backward of the outer product mean: dm (dtype); dln_w, dln_b [CM], dw_a,
+// dw_b [C][CM], dw_o [CZ][C * C], db_o [CZ] (fp32).  CM at most 128, or 256.
+struct OpmBwdArgs {
+  int dtype;
+  int64_t S, N, CM, C, CZ;
+  const void* m;
+  const void* ln_w;
+  const void* ln_b;
+  float eps;
+  const void* w_a;
+  const void* w_b;
+  const void* w_o;
+  const void* dout;
+  void* dm;
+  float* dln_w;
+  float* dln_b;
+  float* dw_a;
+  float* dw_b;
+  float* dw_o;
+  float* db_o;
+  void* workspace;  // opm_bwd_workspace bytes
+};
+size_t opm_bwd_workspace(int dtype, int64_t S, int64_t N, int64_t CM, int64_t C, int64_t CZ);
+hipError_t launch_opm_bwd(const OpmBwdArgs& a, hipStream_t s);
 // Weight gradients against plain position rows: for the nseg (1 or 4)
 // segments A_s [npos][128] and B [npos][ncols] (LayerNorm-normalised from z
 // when b_ln),  M_s = A_s^T B  and the column sums of A_s, reduced in a fixed
@@ -286,16 +320,17 @@ size_t transition_bwd_workspace(int dtype, int64_t npos, int64_t CZ, int64_t HID
 hipError_t launch_transition_bwd(const TransitionBwdArgs& a, hipStream_t s);
 size_t transition_workspace(int dtype, int64_t CZ, int64_t HID);
 hipError_t launch_transition(const TransitionArgs& a, hipStream_t s);
-// Backward of a LayerNorm followed by nseg (2) bias-free projections of z
-// [N*N][CZ] (rows in z order): with dY_s [N*N][seg_w] the projections'
-// gradients and W_s [seg_w][CZ] their weights,
-//   dz = LayerNorm backward of sum_s dY_s . W_s       (dtype, z layout),
+// Backward of a LayerNorm followed by nseg (2) bias-free projections of the
+// rows z [npos][CZ]: with dY_s [npos][seg_w] the projections' gradients and
+// W_s [seg_w][CZ] their weights,
+//   dz = LayerNorm backward of sum_s dY_s . W_s       (dtype, [npos][CZ]),
 //   dW_s = sum over positions of dY_s^T LN(z)         (fp32, [seg_w][CZ]),
 //   dln_w, dln_b                                      (fp32, [CZ]),
-// all reduced in a fixed order.  seg_w and CZ multiples of 32, at most 128.
+// all reduced in a fixed order.  seg_w a multiple of 32, at most 128; CZ a
+// multiple of 32, at most 128, or 256.
 struct LnProjBwdArgs {
   int dtype;
-  int64_t N, CZ;
+  int64_t npos, CZ;
   int nseg, seg_w;
   const void* dy[2];
   const void* w[2];
@@ -309,7 +344,26 @@ struct LnProjBwdArgs {
   float* dln_b;
   void* workspace;  // ln_proj_bwd_workspace bytes
 };
-size_t ln_proj_bwd_workspace(int64_t N, int64_t CZ, int seg_w);
+size_t ln_proj_bwd_workspace(int64_t npos, int64_t CZ, int seg_w);
+// M = A^T B over npos plain rows: A [npos][a_w] (a_w a multiple of 32, at
+// most 128), B [npos][b_w] at row stride b_ld (b_w a multiple of 16, at most
+// 256); dw[r * dw_ld + c] = M[r][c] (fp32), dcol[r] = sum of A's column r
+// (if dcol is given); fixed-order reduction.
+struct ColWGradArgs {
+  int dtype;
+  int64_t npos;
+  const void* a;
+  int a_w;
+  const void* b;
+  int b_w;
+  int64_t b_ld;
+  float* dw;
+  int64_t dw_ld;
+  float* dcol;
+  void* workspace;  // col_wgrad_workspace bytes
+};
+size_t col_wgrad_workspace(int64_t npos, int b_w);
+hipError_t launch_col_wgrad(const ColWGradArgs& a, hipStream_t s);
 hipError_t launch_ln_proj_bwd(const LnProjBwdArgs& a, hipStream_t s);
 hipError_t launch_out_project_bwd(const OutProjectBwdArgs& a, hipStream_t s);
 hipError_t launch_project_bwd(const ProjectBwdArgs& a, hipStream_t s);

@@ -445,6 +445,7 @@ struct WGradParams {
   int H;
   int b_w, b_zrow, b_ln;        // B [npos][b_w]; LayerNorm-normalised (no affine)
   const void* b;
+  int64_t b_ld;                 // row stride of B (0: b_w)
   float eps;
   int rows_pad;                 // nseg*128 (+16 pair-bias rows): partial rows
   int nchunks, chunk_pos;       // one workgroup per chunk of positions
@@ -456,18 +457,24 @@ struct WGradParams {
 // read with transposing reads (a 288-byte row stride spreads a read's four
 // rows over distinct banks), double-buffered; fp32: transposed
 // [cols][32 positions], single-buffered.
+// A B tile of up to 256 columns (WIDE) is [32][272] (bf16) or [256][36]
+// (fp32).
 template <typename T> struct WL;
 template <> struct WL<bf16_t> {
   static constexpr int RS = 144, BRS = 24;  // row strides: 128- and 16-column tiles
   static constexpr int TILE = 32 * RS, BTILE = 32 * BRS, NBUF = 2;
+  static constexpr int RSW = 272, TILEW = 32 * RSW;
 };
 template <> struct WL<float> {
   static constexpr int PS = 36;             // position stride of a transposed tile
   static constexpr int TILE = 128 * PS, BTILE = 16 * PS, NBUF = 1;
+  static constexpr int TILEW = 256 * PS;
 };
-template <typename T, int NSEG>
+template <typename T, int NSEG, bool WIDE = false>
 constexpr size_t wgrad_lds() {
-  return (size_t)WL<T>::NBUF * ((NSEG + 1) * WL<T>::TILE + WL<T>::BTILE) * sizeof(T) +
+  return (size_t)WL<T>::NBUF *
+             (NSEG * WL<T>::TILE + (WIDE ? WL<T>::TILEW : WL<T>::TILE) + WL<T>::BTILE) *
+             sizeof(T) +
          8 * 144 * sizeof(float);
 }
 
@@ -477,17 +484,22 @@ constexpr size_t wgrad_lds() {
 // B = xhat); NSEG = 2: the multiplicative update (A = its a and b
 // gradients, B = xhat); NSEG = 1: the output projection (A = dout, B = o).  Wave w owns
 // segment w / (8/NSEG) and the column blocks w % (8/NSEG) + (8/NSEG) i,
-// i < NSEG; with NSEG = 4 also the pair-bias rows of column block w.
-template <typename T, int NSEG, bool BIAS = NSEG == 4>
+// i < NSEG (i < 2 NSEG when WIDE: B up to 256 columns); with NSEG = 4 also
+// the pair-bias rows of column block w.
+template <typename T, int NSEG, bool BIAS = NSEG == 4, bool WIDE = false>
 __global__ void __launch_bounds__(512) wgrad_kernel(WGradParams p) {
   using Op = typename Tr<T>::Op;
   constexpr int WPS = 8 / NSEG;     // waves (and column groups) per segment
   constexpr int TPS = 512 / NSEG;   // staging threads per segment
   constexpr int NB = WL<T>::NBUF;
+  constexpr int NCG = WIDE ? 2 * NSEG : NSEG;   // column blocks per wave
+  constexpr int NBC = WIDE ? 2 : 1;             // 128-column B chunks per thread
+  constexpr int BT = WIDE ? WL<T>::TILEW : WL<T>::TILE;
+  static_assert(!(WIDE && BIAS), "the pair-bias rows go with 128-column B tiles");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   T* sA = reinterpret_cast<T*>(smem);                   // [NB][NSEG][TILE]
-  T* sB = sA + NB * NSEG * WL<T>::TILE;                  // [NB][TILE]
-  T* sBi = sB + NB * WL<T>::TILE;                        // [NB][BTILE]
+  T* sB = sA + NB * NSEG * WL<T>::TILE;                  // [NB][BT]
+  T* sBi = sB + NB * BT;                                 // [NB][BTILE]
   float (*sred)[144] = reinterpret_cast<float (*)[144]>(sBi + NB * WL<T>::BTILE);
 
   const int chunk = blockIdx.x;
@@ -506,6 +518,7 @@ __global__ void __launch_bounds__(512) wgrad_kernel(WGradParams p) {
   const int a_seg = tid / TPS, a_c8 = (tid & 15) * 8, a_pos0 = (tid % TPS) >> 4;
   const T* Aseg = static_cast<const T*>(p.aseg[a_seg]);
   const T* Bsrc = static_cast<const T*>(p.b);
+  const int64_t bld = p.b_ld ? p.b_ld : p.b_w;
   const int b_pos = tid >> 4, b_c8 = (tid & 15) * 8, bi_row = tid & 15;
   float csum[8], csum_b = 0.f;
 #pragma unroll
@@ -513,7 +526,7 @@ __global__ void __launch_bounds__(512) wgrad_kernel(WGradParams p) {
 
   struct Raw {
     Raw8<T> a[NSEG];
-    Raw8<T> b;
+    Raw8<T> b[NBC];
     float bi;
   };
   auto zero8 = [](Raw8<T>& r) {
@@ -532,13 +545,14 @@ __global__ void __launch_bounds__(512) wgrad_kernel(WGradParams p) {
         zero8(r.a[u]);
       }
     }
-    {
-      const int pidx = p0 + b_pos;
-      if (pidx < pend && b_c8 < p.b_w) {
+#pragma unroll
+    for (int q = 0; q < NBC; ++q) {
+      const int pidx = p0 + b_pos, c8 = b_c8 + 128 * q;
+      if (pidx < pend && c8 < p.b_w) {
         const uint32_t row = p.b_zrow ? zrow_of(pidx, p.N, p.ending) : (uint32_t)pidx;
-        ld_raw8(r.b, Bsrc + (int64_t)row * p.b_w + b_c8);
+        ld_raw8(r.b[q], Bsrc + (int64_t)row * bld + c8);
       } else {
-        zero8(r.b);
+        zero8(r.b[q]);
       }
     }
     if constexpr (BIAS) {
@@ -547,10 +561,11 @@ __global__ void __launch_bounds__(512) wgrad_kernel(WGradParams p) {
                  ? p.dbias[(int64_t)(bi_row % p.H) * p.npos + pidx] : 0.f;
     }
   };
-  // Store 8 values (channels c8 .. c8+7 of position pos) into a tile.
-  auto put8 = [&](T* tile, int pos, int c8, const float (&v)[8]) {
+  // Store 8 values (channels c8 .. c8+7 of position pos) into a tile with
+  // row stride rs (bf16).
+  auto put8 = [&](T* tile, int pos, int c8, const float (&v)[8], int rs) {
     if constexpr (sizeof(T) == 2) {
-      st8f(tile + pos * WL<T>::RS + c8, v);
+      st8f(tile + pos * rs + c8, v);
     } else {
 #pragma unroll
       for (int j = 0; j < 8; ++j) tile[(c8 + j) * WL<T>::PS + pos] = v[j];
@@ -570,23 +585,28 @@ __global__ void __launch_bounds__(512) wgrad_kernel(WGradParams p) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) csum[j] += v[j];
       if (a_c8 < p.a_w)
-        put8(sA + (buf * NSEG + a_seg) * WL<T>::TILE, a_pos0 + (TPS / 16) * u, a_c8, v);
+        put8(sA + (buf * NSEG + a_seg) * WL<T>::TILE, a_pos0 + (TPS / 16) * u, a_c8, v,
+             sizeof(T) == 2 ? WL<bf16_t>::RS : 0);
     }
     {
-      float v[8];
-      f32x4 lo, hi;
-      widen8(r.b, lo, hi);
+      float v[NBC][8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[i] = lo[i];
-        v[4 + i] = hi[i];
+      for (int q = 0; q < NBC; ++q) {
+        f32x4 lo, hi;
+        widen8(r.b[q], lo, hi);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[q][i] = lo[i];
+          v[q][4 + i] = hi[i];
+        }
       }
       if (p.b_ln) {
-        // statistics over the 16 lanes of this position
-        const bool in = b_c8 < p.b_w;
+        // statistics over the 16 lanes of this position (NBC chunks each)
         float sm = 0.f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) sm += v[j];
+        for (int q = 0; q < NBC; ++q)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) sm += v[q][j];
         sm += __shfl_xor(sm, 1, 64);
         sm += __shfl_xor(sm, 2, 64);
         sm += __shfl_xor(sm, 4, 64);
@@ -595,9 +615,13 @@ __global__ void __launch_bounds__(512) wgrad_kernel(WGradParams p) {
         const float mu = sm * inv_n;
         float var = 0.f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          v[j] = in ? v[j] - mu : 0.f;
-          var = __builtin_fmaf(v[j], v[j], var);
+        for (int q = 0; q < NBC; ++q) {
+          const bool in = b_c8 + 128 * q < p.b_w;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            v[q][j] = in ? v[q][j] - mu : 0.f;
+            var = __builtin_fmaf(v[q][j], v[q][j], var);
+          }
         }
         var += __shfl_xor(var, 1, 64);
         var += __shfl_xor(var, 2, 64);
@@ -605,9 +629,15 @@ __global__ void __launch_bounds__(512) wgrad_kernel(WGradParams p) {
         var += __shfl_xor(var, 8, 64);
         const float rstd = rsqrtf(var * inv_n + p.eps);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] *= rstd;
+        for (int q = 0; q < NBC; ++q)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[q][j] *= rstd;
       }
-      if (b_c8 < p.b_w) put8(sB + buf * WL<T>::TILE, b_pos, b_c8, v);
+#pragma unroll
+      for (int q = 0; q < NBC; ++q)
+        if (b_c8 + 128 * q < p.b_w)
+          put8(sB + buf * BT, b_pos, b_c8 + 128 * q, v[q],
+               sizeof(T) == 2 ? (WIDE ? WL<bf16_t>::RSW : WL<bf16_t>::RS) : 0);
     }
     if constexpr (BIAS) {
       const float d = r.bi;
@@ -632,12 +662,13 @@ __global__ void __launch_bounds__(512) wgrad_kernel(WGradParams p) {
     }
   };
 
-  f32x4 acc[8][NSEG], accb = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[8][NCG], accb = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int rb = 0; rb < 8; ++rb)
 #pragma unroll
-    for (int i = 0; i < NSEG; ++i) acc[rb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int rsA = sizeof(T) == 2 ? WL<bf16_t>::RS : 0, rsB = rsA;
+    for (int i = 0; i < NCG; ++i) acc[rb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int rsA = sizeof(T) == 2 ? WL<bf16_t>::RS : 0;
+  const int rsB = sizeof(T) == 2 ? (WIDE ? WL<bf16_t>::RSW : WL<bf16_t>::RS) : 0;
   const int rsBi = sizeof(T) == 2 ? WL<bf16_t>::BRS : 0;
 
   Raw raw;
@@ -649,24 +680,24 @@ __global__ void __launch_bounds__(512) wgrad_kernel(WGradParams p) {
     __syncthreads();
     if (st + 1 < nst) fetch(st + 1, raw);
     const T* tA = sA + (buf * NSEG + wseg) * WL<T>::TILE;
-    const T* tB = sB + buf * WL<T>::TILE;
+    const T* tB = sB + buf * BT;
     if constexpr (sizeof(T) == 2) {
-      Op bf[NSEG];
+      Op bf[NCG];
 #pragma unroll
-      for (int i = 0; i < NSEG; ++i)
+      for (int i = 0; i < NCG; ++i)
         if (cw + WPS * i < CBn) bf[i] = frag(tB, (cw + WPS * i) * 16, rsB);
 #pragma unroll
       for (int rb = 0; rb < 8; ++rb) {
         if (rb >= RB) break;
         const Op af = frag(tA, rb * 16, rsA);
 #pragma unroll
-        for (int i = 0; i < NSEG; ++i)
+        for (int i = 0; i < NCG; ++i)
           if (cw + WPS * i < CBn) acc[rb][i] = mma32(af, bf[i], acc[rb][i]);
       }
     } else {
       // fp32 fragments are twice the registers: one column block at a time
 #pragma unroll
-      for (int i = 0; i < NSEG; ++i) {
+      for (int i = 0; i < NCG; ++i) {
         if (cw + WPS * i >= CBn) continue;
         const Op bfi = frag(tB, (cw + WPS * i) * 16, rsB);
 #pragma unroll
@@ -688,7 +719,7 @@ __global__ void __launch_bounds__(512) wgrad_kernel(WGradParams p) {
   // Partials: lane (l16, g) holds M[rb*16 + 4g + i][cb*16 + l16].
   float* dst = p.part + (int64_t)chunk * p.rows_pad * p.b_w;
 #pragma unroll
-  for (int i = 0; i < NSEG; ++i) {
+  for (int i = 0; i < NCG; ++i) {
     const int cb = cw + WPS * i;
     if (cb >= CBn) continue;
 #pragma unroll
@@ -779,6 +810,7 @@ struct FinishParams {
   float* dcol[kMaxSeg];     // column sums of segment s ([a_w]) or null
   float* mred;              // [nseg*a_w + H][ncols] (ln)
   float* cred;              // [nseg*a_w + H] (ln)
+  int64_t ldw;              // row stride of dw (0: ncols)
 };
 
 // Sum of 16 lanes' partials (lanes 16a .. 16a+15), complete in the first
@@ -836,7 +868,7 @@ __global__ void __launch_bounds__(256) wgrad_finish_kernel(FinishParams p) {
       if (c == 0) p.cred[k] = s;
     }
     if (seg >= 0) {
-      p.dw[seg][(int64_t)r * p.ncols + c] = out;
+      p.dw[seg][(int64_t)r * (p.ldw ? p.ldw : p.ncols) + c] = out;
       if (c == 0 && p.dcol[seg]) p.dcol[seg][r] = s;
     } else {
       p.dw_bias[(int64_t)r * p.ncols + c] = out;
@@ -947,21 +979,27 @@ void chunking(int64_t npos, int target, int& nchunks, int& chunk_pos) {
 // KB of LDS), each over one chunk of positions.
 constexpr int kChunks = 256;
 
-template <typename T, int NSEG, bool BIAS>
+template <typename T, int NSEG, bool BIAS, bool WIDE = false>
 hipError_t launch_wgrad_k(WGradParams& p, hipStream_t s) {
-  const size_t lds = wgrad_lds<T, NSEG>();
+  const size_t lds = wgrad_lds<T, NSEG, WIDE>();
   hipError_t e =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&wgrad_kernel<T, NSEG, BIAS>),
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&wgrad_kernel<T, NSEG, BIAS, WIDE>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((wgrad_kernel<T, NSEG, BIAS>), dim3(p.nchunks), dim3(512), lds, s, p);
+  hipLaunchKernelGGL((wgrad_kernel<T, NSEG, BIAS, WIDE>), dim3(p.nchunks), dim3(512), lds, s,
+                     p);
   return hipGetLastError();
 }
-// four segments with or without the pair-bias rows; two or one without
+// four segments with or without the pair-bias rows; two or one without; B
+// wider than 128 columns (up to 256) with two segments only
 template <typename T>
 hipError_t launch_wgrad(WGradParams& p, hipStream_t s) {
   const bool bias = p.dbias != nullptr;
   if (bias && p.nseg != 4) return hipErrorInvalidValue;
+  if (p.b_w > 256 || (p.b_w > 128 && p.nseg != 2 && p.nseg != 1)) return hipErrorInvalidValue;
+  if (p.b_w > 128)
+    return p.nseg == 2 ? launch_wgrad_k<T, 2, false, true>(p, s)
+                       : launch_wgrad_k<T, 1, false, true>(p, s);
   switch (p.nseg) {
     case 4: return bias ? launch_wgrad_k<T, 4, true>(p, s) : launch_wgrad_k<T, 4, false>(p, s);
     case 2: return launch_wgrad_k<T, 2, false>(p, s);
@@ -1101,29 +1139,223 @@ hipError_t project_bwd_t(const ProjectBwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ------------------------------------------- LayerNorm backward, 256 wide
+// dz = LayerNorm backward of dX = sum_s dY_s . W_s for rows of 256 channels
+// (too wide for rowgrad_kernel's registers).  Four waves, 16 positions per
+// wave per tile: dX^T = W_ext^T . dY^T on the matrix cores with W_ext^T
+// ([256][K], K = nseg * seg_w) in LDS (resident when it fits, else in
+// column chunks of kc per tile), so lane (l16, g) ends with
+// channels 16 cb + 4 g .. +3 of position l16 for cb < 16; then the
+// LayerNorm backward in registers (statistics recomputed from z in fp32,
+// two-pass, sums over the four lane groups).
+struct LnWideParams {
+  int npos, seg_w, K, kc, ntiles;
+  const void* dy[2];
+  const void* w[2];   // [seg_w][256]
+  const void* z;      // [npos][256]
+  const void* ln_w;
+  float eps;
+  void* dz;           // [npos][256]
+};
+constexpr int kWideC = 256;
+
+template <typename T>
+__device__ __forceinline__ void ld4f(const T* p, float (&v)[4]) {
+  if constexpr (sizeof(T) == 2) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    v[0] = __uint_as_float(u.x << 16);
+    v[1] = __uint_as_float(u.x & 0xffff0000u);
+    v[2] = __uint_as_float(u.y << 16);
+    v[3] = __uint_as_float(u.y & 0xffff0000u);
+  } else {
+    const float4 f = *reinterpret_cast<const float4*>(p);
+    v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+  }
+}
+template <typename T>
+__device__ __forceinline__ void st4f(T* p, const float (&v)[4]) {
+  if constexpr (sizeof(T) == 2) {
+    uint2 u;
+    u.x = uint32_t(Tr<bf16_t>::from_f(v[0])) | (uint32_t(Tr<bf16_t>::from_f(v[1])) << 16);
+    u.y = uint32_t(Tr<bf16_t>::from_f(v[2])) | (uint32_t(Tr<bf16_t>::from_f(v[3])) << 16);
+    *reinterpret_cast<uint2*>(p) = u;
+  } else {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) ln_bwd_wide_kernel(LnWideParams p) {
+  using Op = typename Tr<T>::Op;
+  constexpr int CB = kWideC / 16;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int KS = p.kc + PADE;
+  T* sW = reinterpret_cast<T*>(smem);                                  // [256][kc + PADE]
+  float* sG = reinterpret_cast<float*>(smem + (size_t)kWideC * KS * sizeof(T));  // [256]
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, g = lane >> 4;
+  // W_ext^T columns [k0, k0 + kc) into LDS
+  auto load_w = [&](int k0) {
+    for (int e = tid; e < kWideC * p.kc; e += 256) {
+      const int o = e / p.kc, k = k0 + (e - o * p.kc);
+      const int sg = k / p.seg_w;
+      sW[o * KS + (k - k0)] =
+          static_cast<const T*>(p.w[sg])[(int64_t)(k - sg * p.seg_w) * kWideC + o];
+    }
+  };
+  const bool resident = p.kc == p.K;
+  if (resident) load_w(0);
+  for (int c = tid; c < kWideC; c += 256) sG[c] = Tr<T>::to_f(static_cast<const T*>(p.ln_w)[c]);
+  __syncthreads();
+  const int ksteps = p.kc / 32;
+  const float inv_n = 1.f / (float)kWideC;
+  for (int tile = blockIdx.x; tile < p.ntiles; tile += gridDim.x) {
+    const int pos = (tile * 4 + wave) * 16 + l16;
+    const bool live = pos < p.npos;
+    const int pc = live ? pos : p.npos - 1;
+    f32x4 acc[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < p.K; k0 += p.kc) {
+      if (!resident) {
+        __syncthreads();  // every wave is done with the previous chunk
+        load_w(k0);
+        __syncthreads();
+      }
+      for (int u = 0; u < ksteps; ++u) {
+        const int k = k0 + 32 * u + 8 * g, sg = k / p.seg_w;
+        const Op x = ld_op<T>(static_cast<const T*>(p.dy[sg]) + (int64_t)pc * p.seg_w +
+                              (k - sg * p.seg_w));
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          const Op a = ld_op<T>(sW + (cb * 16 + l16) * KS + 32 * u + 8 * g);
+          acc[cb] = mma32(a, x, acc[cb]);
+        }
+      }
+    }
+    // lane (l16, g): dX[pos][16 cb + 4 g + i] in acc[cb][i]
+    const T* zr = static_cast<const T*>(p.z) + (int64_t)pc * kWideC + 4 * g;
+    float xv[CB][4];
+    float sum = 0.f;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      ld4f<T>(zr + 16 * cb, xv[cb]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sum += xv[cb][i];
+    }
+    sum += shfl_xor(sum, 16);
+    sum += shfl_xor(sum, 32);
+    const float mu = sum * inv_n;
+    float var = 0.f;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xv[cb][i] -= mu;
+        var = __builtin_fmaf(xv[cb][i], xv[cb][i], var);
+      }
+    var += shfl_xor(var, 16);
+    var += shfl_xor(var, 32);
+    const float rstd = rsqrtf(var * inv_n + p.eps);
+    float a = 0.f, b = 0.f;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xv[cb][i] *= rstd;  // xhat
+        const float d = acc[cb][i] * sG[16 * cb + 4 * g + i];
+        acc[cb][i] = d;     // dxhat
+        a += d;
+        b = __builtin_fmaf(d, xv[cb][i], b);
+      }
+    a += shfl_xor(a, 16);
+    a += shfl_xor(a, 32);
+    b += shfl_xor(b, 16);
+    b += shfl_xor(b, 32);
+    a *= inv_n;
+    b *= inv_n;
+    if (live) {
+      T* dst = static_cast<T*>(p.dz) + (int64_t)pos * kWideC + 4 * g;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = rstd * (acc[cb][i] - a - xv[cb][i] * b);
+        st4f<T>(dst + 16 * cb, v);
+      }
+    }
+  }
+}
+
+template <typename T>
+hipError_t launch_ln_bwd_wide(LnWideParams& p, hipStream_t s) {
+  // all of W_ext^T when it fits the LDS budget, else 128-column chunks (fp32
+  // with K = 256)
+  p.kc = (size_t)kWideC * (p.K + PADE) * sizeof(T) <= kLdsBudget ? p.K : 128;
+  const size_t lds = (size_t)kWideC * (p.kc + PADE) * sizeof(T) + kWideC * sizeof(float);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&ln_bwd_wide_kernel<T>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  p.ntiles = (p.npos + 63) / 64;
+  const int grid = std::min(p.ntiles, 2048);
+  hipLaunchKernelGGL(ln_bwd_wide_kernel<T>, dim3(grid), dim3(256), lds, s, p);
+  return hipGetLastError();
+}
+
+// Workspace of the two-segment LayerNorm + projection backward: chunk
+// partials (256 rows: 128 per segment), their group sums, M and s.
+struct LnProjLayout {
+  size_t part, cpart, part2, cpart2, mred, cred, total;
+};
+LnProjLayout ln_proj_layout(int64_t npos, int64_t CZ, int seg_w) {
+  int nc, cp;
+  chunking(npos, kChunks, nc, cp);
+  const int ng = (nc + kGroup - 1) / kGroup;
+  LnProjLayout L;
+  L.part = 0;
+  L.cpart = align256((size_t)nc * 256 * CZ * 4);
+  L.part2 = L.cpart + align256((size_t)nc * 256 * 4);
+  L.cpart2 = L.part2 + align256((size_t)ng * 256 * CZ * 4);
+  L.mred = L.cpart2 + align256((size_t)ng * 256 * 4);
+  L.cred = L.mred + align256((size_t)2 * seg_w * CZ * 4);
+  L.total = L.cred + align256((size_t)2 * seg_w * 4);
+  return L;
+}
+
 // LayerNorm + nseg projections of z, backward from the projections'
-// gradients (the multiplicative update's a and b): dz, dW_s, dgamma, dbeta.
+// gradients (the multiplicative update's a and b, the outer product mean's
+// a and b): dz, dW_s, dgamma, dbeta.
 template <typename T>
 hipError_t ln_proj_bwd_t(const LnProjBwdArgs& a, hipStream_t s) {
-  const int N = (int)a.N, CZ = (int)a.CZ, W = a.seg_w;
-  const int npos = N * N;
-  const PartLayout L = part_layout(a.N, a.CZ, W / kHeadDim);
+  const int CZ = (int)a.CZ, W = a.seg_w;
+  const int npos = (int)a.npos;
+  const LnProjLayout L = ln_proj_layout(a.npos, a.CZ, W);
   char* ws = static_cast<char*>(a.workspace);
-  RowGradParams r{};
-  r.N = N; r.ending = 0; r.npos = npos;
-  r.nseg = a.nseg; r.seg_w = W; r.in_zrow = 0;
-  for (int i = 0; i < a.nseg; ++i) { r.seg[i] = a.dy[i]; r.wseg[i] = a.w[i]; }
-  r.dbias = nullptr; r.H = 0; r.Kext = a.nseg * W;
-  r.wbias = nullptr; r.cout = CZ;
-  r.ln = 1; r.z = a.z; r.ln_w = a.ln_w; r.eps = a.eps; r.y = a.dz;
-  hipError_t e = launch_rowgrad<T>(r, s);
+  hipError_t e;
+  if (CZ == kWideC) {
+    LnWideParams q{};
+    q.npos = npos; q.seg_w = W; q.K = a.nseg * W;
+    for (int i = 0; i < a.nseg; ++i) { q.dy[i] = a.dy[i]; q.w[i] = a.w[i]; }
+    q.z = a.z; q.ln_w = a.ln_w; q.eps = a.eps; q.dz = a.dz;
+    e = launch_ln_bwd_wide<T>(q, s);
+  } else {
+    RowGradParams r{};
+    r.N = 0; r.ending = 0; r.npos = npos;  // plain rows: no z-row mapping
+    r.nseg = a.nseg; r.seg_w = W; r.in_zrow = 0;
+    for (int i = 0; i < a.nseg; ++i) { r.seg[i] = a.dy[i]; r.wseg[i] = a.w[i]; }
+    r.dbias = nullptr; r.H = 0; r.Kext = a.nseg * W;
+    r.wbias = nullptr; r.cout = CZ;
+    r.ln = 1; r.z = a.z; r.ln_w = a.ln_w; r.eps = a.eps; r.y = a.dz;
+    e = launch_rowgrad<T>(r, s);
+  }
   if (e != hipSuccess) return e;
   WGradParams w{};
-  w.N = N; w.ending = 0; w.npos = npos;
+  w.N = 0; w.ending = 0; w.npos = npos;
   w.nseg = a.nseg; w.a_w = W; w.a_zrow = 0;
   for (int i = 0; i < a.nseg; ++i) w.aseg[i] = a.dy[i];
   w.dbias = nullptr; w.H = 0;
-  w.b_w = CZ; w.b_zrow = 1; w.b_ln = 1; w.b = a.z; w.eps = a.eps;
+  w.b_w = CZ; w.b_zrow = 0; w.b_ln = 1; w.b = a.z; w.eps = a.eps;
   w.rows_pad = a.nseg * 128;
   chunking(npos, kChunks, w.nchunks, w.chunk_pos);
   w.part = reinterpret_cast<float*>(ws + L.part);
@@ -1163,6 +1395,34 @@ SegLayout seg_layout(int64_t npos, int64_t ncols) {
   L.cpart2 = L.part2 + align256((size_t)ng * 512 * ncols * 4);
   L.total = L.cpart2 + align256((size_t)ng * 512 * 4);
   return L;
+}
+
+// M = A^T B over plain position rows, A [npos][a_w] (a_w <= 128), B
+// [npos][b_w] at row stride b_ld (b_w <= 256): dw[r * dw_ld + c] = M[r][c],
+// dcol[r] = the column sums of A (if given); fixed-order reduction.
+template <typename T>
+hipError_t col_wgrad_t(const ColWGradArgs& a, hipStream_t s) {
+  const SegLayout L = seg_layout(a.npos, a.b_w);
+  char* ws = static_cast<char*>(a.workspace);
+  WGradParams w{};
+  w.N = 0; w.ending = 0; w.npos = (int)a.npos;
+  w.nseg = 1; w.a_w = a.a_w; w.a_zrow = 0; w.aseg[0] = a.a;
+  w.dbias = nullptr; w.H = 0;
+  w.b_w = a.b_w; w.b_zrow = 0; w.b_ln = 0; w.b = a.b; w.b_ld = a.b_ld; w.eps = 0.f;
+  w.rows_pad = 128;
+  chunking(a.npos, kChunks, w.nchunks, w.chunk_pos);
+  w.part = reinterpret_cast<float*>(ws + L.part);
+  w.cpart = reinterpret_cast<float*>(ws + L.cpart);
+  hipError_t e = launch_wgrad<T>(w, s);
+  if (e != hipSuccess) return e;
+  FinishParams f{};
+  f.nchunks = w.nchunks; f.rows_pad = w.rows_pad; f.ncols = a.b_w;
+  f.nseg = 1; f.a_w = a.a_w; f.H = 0; f.has_bias = 0;
+  f.part = w.part; f.cpart = w.cpart;
+  f.ln = 0;
+  f.dw[0] = a.dw; f.dcol[0] = a.dcol; f.ldw = a.dw_ld;
+  return launch_finish<T>(f, reinterpret_cast<float*>(ws + L.part2),
+                          reinterpret_cast<float*>(ws + L.cpart2), s);
 }
 
 template <typename T>
@@ -1214,12 +1474,22 @@ hipError_t launch_project_bwd(const ProjectBwdArgs& a, hipStream_t s) {
   return a.dtype == 1 ? project_bwd_t<bf16_t>(a, s) : project_bwd_t<float>(a, s);
 }
 
-size_t ln_proj_bwd_workspace(int64_t N, int64_t CZ, int seg_w) {
-  return part_layout(N, CZ, seg_w / kHeadDim).total;
+size_t ln_proj_bwd_workspace(int64_t npos, int64_t CZ, int seg_w) {
+  return ln_proj_layout(npos, CZ, seg_w).total;
+}
+
+size_t col_wgrad_workspace(int64_t npos, int b_w) { return seg_layout(npos, b_w).total; }
+
+hipError_t launch_col_wgrad(const ColWGradArgs& a, hipStream_t s) {
+  if (a.a_w % 32 != 0 || a.a_w > 128 || a.b_w % 16 != 0 || a.b_w > 256 || a.npos <= 0 ||
+      a.npos > INT32_MAX)
+    return hipErrorInvalidValue;
+  return a.dtype == 1 ? col_wgrad_t<bf16_t>(a, s) : col_wgrad_t<float>(a, s);
 }
 
 hipError_t launch_ln_proj_bwd(const LnProjBwdArgs& a, hipStream_t s) {
-  if (a.nseg != 2 || a.seg_w % 32 != 0 || a.seg_w > 128 || a.CZ % 32 != 0 || a.CZ > 128)
+  if (a.nseg != 2 || a.seg_w % 32 != 0 || a.seg_w > 128 || a.CZ % 32 != 0 || a.CZ > 256 ||
+      (a.CZ > 128 && a.CZ != 256) || a.npos <= 0 || a.npos > INT32_MAX)
     return hipErrorInvalidValue;
   return a.dtype == 1 ? ln_proj_bwd_t<bf16_t>(a, s) : ln_proj_bwd_t<float>(a, s);
 }

@@ -39,31 +39,34 @@ template <typename T> struct MulCfg;
 template <> struct MulCfg<bf16_t> { static constexpr int BK = 64, RS = 72; };
 template <> struct MulCfg<float> { static constexpr int BK = 32, RS = 36; };
 
-// Columns [K, Kp) of rows [0, M) of the C matrices [Np][Kp] of a and b: zero
-// (a_frag: a in fragment order, frag_off).
+// Columns [K, Kp) of rows [0, M) of the C matrices [Np][Kp] of a and of
+// rows [0, M2) of the C matrices [Np2][Kp] of b: zero (a_frag: a in
+// fragment order, frag_off).
 template <typename T>
-__global__ void __launch_bounds__(256) pad_cols_kernel(T* a, T* b, int C, int M, int K, int Np,
-                                                       int Kp, int a_frag) {
-  const int padw = Kp - K;
-  const int64_t total = (int64_t)C * M * padw;
+__global__ void __launch_bounds__(256) pad_cols_kernel(T* a, T* b, int C, int M, int M2, int K,
+                                                       int Np, int Np2, int Kp, int a_frag) {
+  const int padw = Kp - K, Mm = M > M2 ? M : M2;
+  const int64_t total = (int64_t)C * Mm * padw;
   for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total;
        e += (int64_t)gridDim.x * 256) {
     const int col = K + (int)(e % padw);
-    const int64_t r = e / padw;  // matrix * M + row
-    const int c = (int)(r / M), row = (int)(r - (int64_t)c * M);
-    const int64_t off = ((int64_t)c * Np + row) * Kp + col;
-    a[a_frag ? (int64_t)c * Np * Kp + frag_off(row, col, Kp) : off] = T(0);
-    b[off] = T(0);
+    const int64_t r = e / padw;  // matrix * Mm + row
+    const int c = (int)(r / Mm), row = (int)(r - (int64_t)c * Mm);
+    if (row < M)
+      a[a_frag ? (int64_t)c * Np * Kp + frag_off(row, col, Kp)
+               : ((int64_t)c * Np + row) * Kp + col] = T(0);
+    if (row < M2) b[((int64_t)c * Np2 + row) * Kp + col] = T(0);
   }
 }
 
 // ----------------------------------------------------------------- GEMM
 struct MulGemmParams {
   int C, N, Np, Kp;  // N: rows of each product (at most Np)
+  int N2, Np2;       // columns of each product (rows of b, at most Np2)
   const void* a;  // [C][Np][Kp]
-  const void* b;  // [C][Np][Kp]
-  void* t;        // [C][N][N]
-  int ntile;      // Np / kTile
+  const void* b;  // [C][Np2][Kp]
+  void* t;        // [C][N][N2]
+  int ntile, ntile2;  // Np / kTile, Np2 / kTile
 };
 
 // Row tiles per group of the work order.
@@ -101,21 +104,21 @@ __global__ void __launch_bounds__(256) trimul_gemm_kernel(MulGemmParams p) {
   __shared__ __attribute__((aligned(16))) T sA[2][kTile * RS];
   __shared__ __attribute__((aligned(16))) T sB[2][kTile * RS];
 
-  const int w = xcd_work_index(p.C * p.ntile * p.ntile);
+  const int w = xcd_work_index(p.C * p.ntile * p.ntile2);
   if (w < 0) return;
-  const int per_c = p.ntile * p.ntile;
+  const int per_c = p.ntile * p.ntile2;
   const int c = w / per_c, r0 = w - c * per_c;
-  const int first = r0 / (kGroup * p.ntile) * kGroup;
+  const int first = r0 / (kGroup * p.ntile2) * kGroup;
   const int h = min(kGroup, p.ntile - first);
-  const int r = r0 - first * p.ntile;
+  const int r = r0 - first * p.ntile2;
   const int ti = first + r % h, tj = r / h;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
   const int wi = wave >> 1, wj = wave & 1;
-  const int64_t cs = (int64_t)p.Np * p.Kp;
+  const int64_t cs = (int64_t)p.Np * p.Kp, cs2 = (int64_t)p.Np2 * p.Kp;
   const T* A = static_cast<const T*>(p.a) + c * cs + (int64_t)ti * kTile * p.Kp;
-  const T* B = static_cast<const T*>(p.b) + c * cs + (int64_t)tj * kTile * p.Kp;
+  const T* B = static_cast<const T*>(p.b) + c * cs2 + (int64_t)tj * kTile * p.Kp;
 
   // staging: chunk e = tid + 256 u: tile row e / CPR, elements (e % CPR) * E16
   u32x4 ra[CPT], rb[CPT];
@@ -165,7 +168,7 @@ __global__ void __launch_bounds__(256) trimul_gemm_kernel(MulGemmParams p) {
   }
 
   // lane (l16, g) holds T[i = .. + bi*16 + l16][j = .. + bj*16 + 4g + r]
-  T* Tc = static_cast<T*>(p.t) + (int64_t)c * p.N * p.N;
+  T* Tc = static_cast<T*>(p.t) + (int64_t)c * p.N * p.N2;
 #pragma unroll
   for (int bi = 0; bi < 4; ++bi) {
     const int i = ti * kTile + wi * 64 + bi * 16 + l16;
@@ -173,13 +176,13 @@ __global__ void __launch_bounds__(256) trimul_gemm_kernel(MulGemmParams p) {
 #pragma unroll
     for (int bj = 0; bj < 4; ++bj) {
       const int j0 = tj * kTile + wj * 64 + bj * 16 + 4 * g;
-      T* dst = Tc + (int64_t)i * p.N + j0;
-      if (j0 + 3 < p.N && (p.N & 3) == 0) {
+      T* dst = Tc + (int64_t)i * p.N2 + j0;
+      if (j0 + 3 < p.N2 && (p.N2 & 3) == 0) {
         st4t<T>(dst, acc[bj][bi]);
       } else {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          if (j0 + r < p.N) dst[r] = Tr<T>::from_f(acc[bj][bi][r]);
+          if (j0 + r < p.N2) dst[r] = Tr<T>::from_f(acc[bj][bi][r]);
       }
     }
   }
@@ -209,7 +212,7 @@ __global__ void __launch_bounds__(256 * WJ) pair_gemm_bf16_kernel(MulGemmParams 
   constexpr int CPT = BROWS * (BK / 8) / NT;   // 16-byte B chunks per thread per stage
   __shared__ __attribute__((aligned(16))) T sB[2][BROWS * RS];
 
-  const int nti = p.Np / kBigI, ntj = p.Np / BROWS;
+  const int nti = p.Np / kBigI, ntj = p.Np2 / BROWS;
   const int w = xcd_work_index(p.C * nti * ntj);
   if (w < 0) return;
   const int per_c = nti * ntj;
@@ -224,12 +227,12 @@ __global__ void __launch_bounds__(256 * WJ) pair_gemm_bf16_kernel(MulGemmParams 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
   const int wi = wave & 3, wj = wave >> 2;
-  const int64_t cs = (int64_t)p.Np * p.Kp;
+  const int64_t cs = (int64_t)p.Np * p.Kp, cs2 = (int64_t)p.Np2 * p.Kp;
   // this wave's first 16-row block of A (fragment order), this lane's slot
   const int kblk = p.Kp >> 5;  // 32-column blocks per row block
   const T* A = static_cast<const T*>(p.a) + c * cs +
                ((int64_t)(ti * kBigI + wi * 64) >> 4) * kblk * 512 + lane * 8;
-  const T* B = static_cast<const T*>(p.b) + c * cs + (int64_t)tj * BROWS * p.Kp;
+  const T* B = static_cast<const T*>(p.b) + c * cs2 + (int64_t)tj * BROWS * p.Kp;
 
   u32x4 rb[CPT];
   auto fetch_b = [&](int k0) {
@@ -296,7 +299,7 @@ __global__ void __launch_bounds__(256 * WJ) pair_gemm_bf16_kernel(MulGemmParams 
   }
 
   // lane (l16, g) holds T[i = .. + bi*16 + l16][j = .. + bj*16 + 4g + r]
-  T* Tc = static_cast<T*>(p.t) + (int64_t)c * p.N * p.N;
+  T* Tc = static_cast<T*>(p.t) + (int64_t)c * p.N * p.N2;
 #pragma unroll
   for (int bi = 0; bi < 4; ++bi) {
     const int i = ti * kBigI + wi * 64 + bi * 16 + l16;
@@ -304,13 +307,13 @@ __global__ void __launch_bounds__(256 * WJ) pair_gemm_bf16_kernel(MulGemmParams 
 #pragma unroll
     for (int bj = 0; bj < 8; ++bj) {
       const int j0 = tj * BROWS + wj * kBigJ + bj * 16 + 4 * g;
-      T* dst = Tc + (int64_t)i * p.N + j0;
-      if (j0 + 3 < p.N && (p.N & 3) == 0) {
+      T* dst = Tc + (int64_t)i * p.N2 + j0;
+      if (j0 + 3 < p.N2 && (p.N2 & 3) == 0) {
         st4t<T>(dst, acc[bj][bi]);
       } else {
 #pragma unroll
         for (int r2 = 0; r2 < 4; ++r2)
-          if (j0 + r2 < p.N) dst[r2] = Tr<T>::from_f(acc[bj][bi][r2]);
+          if (j0 + r2 < p.N2) dst[r2] = Tr<T>::from_f(acc[bj][bi][r2]);
       }
     }
   }
@@ -495,33 +498,37 @@ MulLayout mul_layout(int dtype, int64_t N, int64_t C) {
   return L;
 }
 
+// T_c = A_c . B_c^T: A [C][Np][Kp] (M rows), B [C][Np2][Kp] (M2 rows), T
+// [C][M][M2].
 template <typename T>
-hipError_t pair_gemm_t(int C, int M, int K, int Np, int Kp, T* A, T* B, T* Tm, bool a_frag,
-                       hipStream_t s) {
+hipError_t pair_gemm_t(int C, int M, int M2, int K, int Np, int Np2, int Kp, T* A, T* B, T* Tm,
+                       bool a_frag, hipStream_t s) {
   hipError_t e;
   if (Kp > K) {
-    const int64_t total = (int64_t)C * M * (Kp - K);
+    const int64_t total = (int64_t)C * std::max(M, M2) * (Kp - K);
     const int grid = (int)std::min<int64_t>((total + 255) / 256, 4096);
-    hipLaunchKernelGGL(pad_cols_kernel<T>, dim3(grid), dim3(256), 0, s, A, B, C, M, K, Np, Kp,
-                       (int)a_frag);
+    hipLaunchKernelGGL(pad_cols_kernel<T>, dim3(grid), dim3(256), 0, s, A, B, C, M, M2, K, Np,
+                       Np2, Kp, (int)a_frag);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   MulGemmParams g{};
   g.C = C; g.N = M; g.Np = Np; g.Kp = Kp;
+  g.N2 = M2; g.Np2 = Np2;
   g.a = A; g.b = B; g.t = Tm;
   g.ntile = Np / kTile;
+  g.ntile2 = Np2 / kTile;
   // bf16: the 256 x 128 kernel for one large product (24576^2 by K = 1024:
   // 1.78 vs 1.93 ms), the 128 x 128 one for many small ones (128 products of
   // 768^2 by 768: 206 vs 218 us)
   if (sizeof(T) == 2 && C == 1 && a_frag) {
     constexpr int WJ = 1;  // 256 x 256 tiles with 8 waves (WJ = 2) measured slower
-    const int total = C * (Np / kBigI) * (Np / (kBigJ * WJ));
+    const int total = C * (Np / kBigI) * (Np2 / (kBigJ * WJ));
     const int grid = (total + kNumXcd - 1) / kNumXcd * kNumXcd;
     if constexpr (sizeof(T) == 2)
       hipLaunchKernelGGL(pair_gemm_bf16_kernel<WJ>, dim3(grid), dim3(256 * WJ), 0, s, g);
   } else {
     if (a_frag) return hipErrorInvalidValue;  // the 128 x 128 kernel reads row-major A
-    const int total = C * g.ntile * g.ntile;
+    const int total = C * g.ntile * g.ntile2;
     const int grid = (total + kNumXcd - 1) / kNumXcd * kNumXcd;
     hipLaunchKernelGGL(trimul_gemm_kernel<T>, dim3(grid), dim3(256), 0, s, g);
   }
@@ -542,7 +549,7 @@ hipError_t trimul_t(const TriMulArgs& a, hipStream_t s) {
                         L.Np * L.Kp, L.Kp, 1};
   hipError_t e = launch_channel_project(pa, s);
   if (e != hipSuccess) return e;
-  if ((e = pair_gemm_t<T>(C, N, N, (int)L.Np, (int)L.Kp, A, B, Tm, false, s)) != hipSuccess)
+  if ((e = pair_gemm_t<T>(C, N, N, N, (int)L.Np, (int)L.Np, (int)L.Kp, A, B, Tm, false, s)) != hipSuccess)
     return e;
   MulOutParams o{};
   o.C = C; o.CZ = (int)a.CZ; o.npos = N * N;
@@ -689,7 +696,7 @@ MulBwdLayout mul_bwd_layout(int dtype, int64_t N, int64_t CZ, int64_t C) {
   L.dtpm = L.tpm + L.s2;
   L.part = L.dtpm + L.s2;
   L.total = L.part + al(std::max(proj_bwd_workspace(N, CZ, C / kHeadDim),
-                                 ln_proj_bwd_workspace(N, CZ, (int)C)));
+                                 ln_proj_bwd_workspace(N * N, CZ, (int)C)));
   return L;
 }
 
@@ -725,7 +732,7 @@ hipError_t trimul_bwd_t(const TriMulBwdArgs& a, hipStream_t s) {
   pt.b = at(L.bt);
   if ((e = launch_channel_project(pt, s)) != hipSuccess) return e;
   // T_c (channel-major [C][N][N]) -> position rows
-  if ((e = pair_gemm_t<T>(C, N, N, Np, Kp, at(L.a), at(L.b), at(L.tm), false, s)) != hipSuccess)
+  if ((e = pair_gemm_t<T>(C, N, N, N, Np, Np, Kp, at(L.a), at(L.b), at(L.tm), false, s)) != hipSuccess)
     return e;
   if ((e = cm_to_pm<T>(at(L.tm), at(L.tpm), C, N, N, N, (int64_t)N * N, N, 0, nullptr, s)) !=
       hipSuccess)
@@ -741,9 +748,9 @@ hipError_t trimul_bwd_t(const TriMulBwdArgs& a, hipStream_t s) {
   // dA_c[i][k] = sum_j dT_c[i][j] B_c[j][k]; dB_c[j][k] = sum_i dT_c[i][j] A_c[i][k]
   T* dA = at(L.tm);
   T* dB = at(L.tpm);
-  if ((e = pair_gemm_t<T>(C, N, N, Np, Kp, at(L.dtc), at(L.bt), dA, false, s)) != hipSuccess)
+  if ((e = pair_gemm_t<T>(C, N, N, N, Np, Np, Kp, at(L.dtc), at(L.bt), dA, false, s)) != hipSuccess)
     return e;
-  if ((e = pair_gemm_t<T>(C, N, N, Np, Kp, at(L.dtt), at(L.at), dB, false, s)) != hipSuccess)
+  if ((e = pair_gemm_t<T>(C, N, N, N, Np, Np, Kp, at(L.dtt), at(L.at), dB, false, s)) != hipSuccess)
     return e;
   // back to position rows (z order), masked third residues zeroed: A_c[i][k]
   // is the edge (i, k) outgoing, (k, i) incoming
@@ -755,7 +762,7 @@ hipError_t trimul_bwd_t(const TriMulBwdArgs& a, hipStream_t s) {
   if ((e = cm_to_pm<T>(dB, db, C, N, N, N, (int64_t)N * N, N, tr, a.mask, s)) != hipSuccess)
     return e;
   LnProjBwdArgs lb{};
-  lb.dtype = a.dtype; lb.N = a.N; lb.CZ = a.CZ; lb.nseg = 2; lb.seg_w = C;
+  lb.dtype = a.dtype; lb.npos = a.N * a.N; lb.CZ = a.CZ; lb.nseg = 2; lb.seg_w = C;
   lb.dy[0] = da; lb.dy[1] = db; lb.w[0] = a.w_a; lb.w[1] = a.w_b;
   lb.z = a.z; lb.ln_w = a.ln_w; lb.ln_b = a.ln_b; lb.eps = a.eps;
   lb.dz = a.dz; lb.dw[0] = a.dw_a; lb.dw[1] = a.dw_b; lb.dln_w = a.dln_w; lb.dln_b = a.dln_b;
@@ -785,14 +792,31 @@ int pair_gemm_row_tile() { return kRowPad; }
 
 hipError_t launch_pair_gemm(int dtype, int C, int M, int K, int Np, int Kp, void* a, void* b,
                             void* t, bool a_frag, hipStream_t s) {
-  if (Np % kRowPad != 0 || M > Np || K > Kp || Kp % MulCfg<float>::BK != 0 ||
-      Kp % MulCfg<bf16_t>::BK != 0 || (a_frag && (dtype != 1 || C != 1)))
+  return launch_pair_gemm_rect(dtype, C, M, M, K, Np, Np, Kp, a, b, t, a_frag, s);
+}
+
+hipError_t launch_pair_gemm_rect(int dtype, int C, int M, int M2, int K, int Np, int Np2, int Kp,
+                                 void* a, void* b, void* t, bool a_frag, hipStream_t s) {
+  if (Np % kRowPad != 0 || Np2 % kRowPad != 0 || M > Np || M2 > Np2 || K > Kp ||
+      Kp % MulCfg<float>::BK != 0 || Kp % MulCfg<bf16_t>::BK != 0 ||
+      (a_frag && (dtype != 1 || C != 1)))
     return hipErrorInvalidValue;
-  return dtype == 1 ? pair_gemm_t<bf16_t>(C, M, K, Np, Kp, static_cast<bf16_t*>(a),
+  return dtype == 1 ? pair_gemm_t<bf16_t>(C, M, M2, K, Np, Np2, Kp, static_cast<bf16_t*>(a),
                                           static_cast<bf16_t*>(b), static_cast<bf16_t*>(t),
                                           a_frag, s)
-                    : pair_gemm_t<float>(C, M, K, Np, Kp, static_cast<float*>(a),
-                                         static_cast<float*>(b), static_cast<float*>(t), false, s);
+                    : pair_gemm_t<float>(C, M, M2, K, Np, Np2, Kp, static_cast<float*>(a),
+                                         static_cast<float*>(b), static_cast<float*>(t), false,
+                                         s);
+}
+
+hipError_t launch_cm_to_pm(int dtype, const void* src, void* dst, int C, int rows, int ncols,
+                           int64_t ld, int64_t cs, int N, int trans, const uint8_t* keep,
+                           hipStream_t s) {
+  if (C % 32 != 0 || C > kMaxC) return hipErrorInvalidValue;
+  return dtype == 1 ? cm_to_pm<bf16_t>(static_cast<const bf16_t*>(src), static_cast<bf16_t*>(dst),
+                                       C, rows, ncols, ld, cs, N, trans, keep, s)
+                    : cm_to_pm<float>(static_cast<const float*>(src), static_cast<float*>(dst),
+                                      C, rows, ncols, ld, cs, N, trans, keep, s);
 }
 
 }  // namespace evo

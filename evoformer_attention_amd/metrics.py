@@ -116,6 +116,15 @@ def transition_bwd_flops(N, CZ, HID):
     return 16.0 * N * N * HID * CZ
 
 
+def opm_bwd_flops(S, N, CM, C, CZ):
+    """Counted flops of the outer product mean's backward: dP = dout . W_o and
+    dW_o = dout^T P (2 x 2 N^2 CZ C^2), the two products dA = dP . B and
+    dB = dP^T . A (2 x 2 (N C)^2 S), dx = da . W_a + db . W_b and dW_a, dW_b
+    (4 x 2 S N C CM).  The recomputed forward (a, b and P) is not counted."""
+    return (4.0 * N * N * CZ * C * C + 4.0 * (N * C) ** 2 * S
+            + 8.0 * S * N * C * CM)
+
+
 def opm_flops(S, N, CM, C, CZ):
     """Counted flops of one outer product mean: the a and b projections (2 x C
     outputs per sequence-residue position), the product of the [N*C, S] and

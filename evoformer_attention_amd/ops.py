@@ -25,6 +25,7 @@ __all__ = ["EvoAttnError", "lib", "evo_abi_version", "evo_attn_fwd",
            "outer_product_mean_workspace_bytes", "outer_product_mean_fwd",
            "pair_transition_bwd_workspace_bytes", "pair_transition_bwd",
            "tri_mul_bwd_workspace_bytes", "tri_mul_bwd",
+           "outer_product_mean_bwd_workspace_bytes", "outer_product_mean_bwd",
            "LIB_PATH", "EXPORTS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
@@ -90,6 +91,9 @@ EXPORTS = {
     "outer_product_mean_fwd": (_I, [_I, _I64, _I64, _I64, _I64, _I64, _P, _P,
                                     _P, _F, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "tri_mul_bwd_workspace_bytes": (_SZ, [_I, _I64, _I64, _I64]),
+    "outer_product_mean_bwd_workspace_bytes": (_SZ, [_I, _I64, _I64, _I64, _I64, _I64]),
+    "outer_product_mean_bwd": (_I, [_I, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _F, _P,
+                                    _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "tri_mul_bwd": (_I, [_I, _I64, _I64, _I64, _I, _P, _P, _P, _P, _F, _P, _P,
                          _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
 }
@@ -704,4 +708,44 @@ def tri_mul_bwd(z, residue_mask, ln_w, ln_b, eps, w_a, w_b, w_o, dout,
                            _ptr(res["dw_b"]), _ptr(res["dw_o"]), _ptr(res["db_o"]),
                            _ptr(workspace), workspace.numel(), _stream(z.device))
     _check("tri_mul_bwd", st)
+    return res
+
+
+def outer_product_mean_bwd_workspace_bytes(dtype, S, N, CM, C, CZ):
+    code = EVO_BF16 if dtype == torch.bfloat16 else EVO_FP32
+    return lib().outer_product_mean_bwd_workspace_bytes(code, S, N, CM, C, CZ)
+
+
+def outer_product_mean_bwd(m, ln_w, ln_b, eps, w_a, w_b, w_o, dout, workspace=None):
+    """Backward of outer_product_mean_fwd -> dict of dm (dtype) and the fp32
+    parameter gradients dln_w, dln_b, dw_a, dw_b, dw_o, db_o."""
+    if not isinstance(m, torch.Tensor) or m.dim() != 3:
+        raise EvoAttnError("binding", EVO_EINVAL, "m must be [S, N, CM]")
+    S, N, CM = m.shape
+    dt = m.dtype
+    for name, t in (("w_a", w_a), ("w_o", w_o)):
+        if not isinstance(t, torch.Tensor) or t.dim() != 2:
+            raise EvoAttnError("binding", EVO_EINVAL, f"{name} must be a matrix")
+    C, CZ = w_a.shape[0], w_o.shape[0]
+    _dev_tensors([("m", m, None, None),
+                  ("ln_w", ln_w, dt, (CM,)),
+                  ("ln_b", ln_b, dt, (CM,)),
+                  ("w_a", w_a, dt, (C, CM)),
+                  ("w_b", w_b, dt, (C, CM)),
+                  ("w_o", w_o, dt, (CZ, C * C)),
+                  ("dout", dout, dt, (N, N, CZ))])
+    workspace = _workspace(outer_product_mean_bwd_workspace_bytes(dt, S, N, CM, C, CZ),
+                           m.device, workspace)
+    res = {"dm": torch.empty_like(m)}
+    for k, shape in (("dln_w", (CM,)), ("dln_b", (CM,)), ("dw_a", (C, CM)),
+                     ("dw_b", (C, CM)), ("dw_o", (CZ, C * C)), ("db_o", (CZ,))):
+        res[k] = torch.empty(shape, dtype=torch.float32, device=m.device)
+    st = lib().outer_product_mean_bwd(_dtype_code(m), S, N, CM, C, CZ, _ptr(m), _ptr(ln_w),
+                                      _ptr(ln_b), float(eps), _ptr(w_a), _ptr(w_b),
+                                      _ptr(w_o), _ptr(dout), _ptr(res["dm"]),
+                                      _ptr(res["dln_w"]), _ptr(res["dln_b"]),
+                                      _ptr(res["dw_a"]), _ptr(res["dw_b"]),
+                                      _ptr(res["dw_o"]), _ptr(res["db_o"]), _ptr(workspace),
+                                      workspace.numel(), _stream(m.device))
+    _check("outer_product_mean_bwd", st)
     return res

@@ -203,13 +203,13 @@ def transition_inputs(name, seed=0, dout=False):
     return rand_transition(w["N"], w["CZ"], w["HID"], w["dtype"], seed=seed, dout=dout)
 
 
-def rand_opm(S, N, CM, C, CZ, dtype, seed=0):
+def rand_opm(S, N, CM, C, CZ, dtype, seed=0, dout=False):
     """Outer-product-mean inputs: m ~ N(0,1) [S,N,CM]; w_a, w_b [C, CM] ~
     N(0, 1/CM); w_o [CZ, C*C] ~ N(0, S/C^2) (a mean of S products of
     independent unit terms has size 1/sqrt(S), so the projected update is of
     unit size, like b_o); LayerNorm weight 1 + N(0, 0.2^2), bias N(0,
-    0.2^2); b_o N(0, 0.5^2).  Draw order: m, w_a, w_b, w_o, ln_w, ln_b,
-    b_o."""
+    0.2^2); b_o N(0, 0.5^2); with dout, an upstream gradient ~ N(0,1)
+    [N,N,CZ].  Draw order: m, w_a, w_b, w_o, ln_w, ln_b, b_o, dout."""
     gen = torch.Generator().manual_seed(seed)
 
     def draw(shape, std=1.0):
@@ -223,10 +223,13 @@ def rand_opm(S, N, CM, C, CZ, dtype, seed=0):
     d["ln_b"] = draw((CM,), 0.2)
     d["b_o"] = draw((CZ,), 0.5)
     d["eps"] = 1e-5
+    if dout:
+        d["dout"] = draw((N, N, CZ))
     return d
 
 
-def opm_inputs(name, seed=0):
+def opm_inputs(name, seed=0, dout=False):
     w = WORKLOADS[name]
     assert w["kind"] == "opm"
-    return rand_opm(w["S"], w["N"], w["CM"], w["C"], w["CZ"], w["dtype"], seed=seed)
+    return rand_opm(w["S"], w["N"], w["CM"], w["C"], w["CZ"], w["dtype"], seed=seed,
+                    dout=dout)

@@ -534,6 +534,52 @@ evo_status_t outer_product_mean_fwd(evo_dtype_t dtype, int64_t S, int64_t N,
                                     void* out, void* workspace,
                                     size_t workspace_bytes, void* stream);
 
+/*
+ * outer_product_mean_bwd -- gradients of outer_product_mean_fwd for
+ * training.  The pages print no backward (the bridge is part of the trained
+ * trunk, "Evoformer: the memory wall ZeRO cannot move", section "The three
+ * operations"); this is the chain rule of the forward.  With
+ * P[i,j,c,d] = sum_s a[s,i,c] b[s,j,d] and dO = (dout . w_o) / S per pair:
+ *   da[s,i,c] = sum_{j,d} dO[i,j,c,d] b[s,j,d],
+ *   db[s,j,d] = sum_{i,c} dO[i,j,c,d] a[s,i,c],
+ *   dm   = LayerNorm backward of (da . w_a + db . w_b),
+ *   dw_a = sum over (s, i) of da^T LN(m), dw_b likewise,
+ *   dw_o = sum over pairs of dout^T flatten(P) / S,  db_o = sum of dout,
+ *   dln_w, dln_b the LayerNorm parameter gradients.
+ * a, b and P are recomputed from m; the three large contractions run on the
+ * matrix cores; sums over positions are deterministic (fixed order, no
+ * atomics).
+ *
+ *   S, N, CM, C, CZ, m, ln_w, ln_b, ln_eps, w_a, w_b, w_o  as
+ *              outer_product_mean_fwd (b_o is not needed); CM at most 128,
+ *              or 256 (EVO_ENOTSUP otherwise).
+ *   dout       [N,N,CZ] dtype: the upstream gradient.
+ *   dm         [S,N,CM] dtype (written).
+ *   dln_w, dln_b [CM] fp32; dw_a, dw_b [C, CM] fp32; dw_o [CZ, C*C] fp32;
+ *              db_o [CZ] fp32 (written, not accumulated).
+ *   workspace  outer_product_mean_bwd_workspace_bytes(...) bytes,
+ *              caller-owned: the operands in both orientations, P (then
+ *              dP), P by pair rows (then dP transposed), dA, dB in both
+ *              layouts and the reduction partials (about 2 (N C)^2 elements
+ *              of dtype; 2.5 GB in bf16 at N = 768, C = 32).
+ * Sizes outside these limits: EVO_ENOTSUP; null required pointers or a
+ * short workspace: EVO_EINVAL.  Pointers: device memory, 16-byte aligned.
+ * Enqueued on `stream`.
+ */
+size_t outer_product_mean_bwd_workspace_bytes(evo_dtype_t dtype, int64_t S,
+                                              int64_t N, int64_t CM, int64_t C,
+                                              int64_t CZ);
+evo_status_t outer_product_mean_bwd(evo_dtype_t dtype, int64_t S, int64_t N,
+                                    int64_t CM, int64_t C, int64_t CZ,
+                                    const void* m, const void* ln_w,
+                                    const void* ln_b, float ln_eps,
+                                    const void* w_a, const void* w_b,
+                                    const void* w_o, const void* dout, void* dm,
+                                    float* dln_w, float* dln_b, float* dw_a,
+                                    float* dw_b, float* dw_o, float* db_o,
+                                    void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
 #ifdef __cplusplus
 }
 #endif
