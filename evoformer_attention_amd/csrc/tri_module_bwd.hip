@@ -146,7 +146,8 @@ __device__ __forceinline__ int wrow_of(int c) {
 // pair-bias block: the multiplicative update's a and b) or 1 (the output
 // projection: one z-layout segment, dX written).  Eight waves, 32 positions
 // per wave per tile.
-template <typename T, int CB, int NSEG>
+// FULL: segments 128 wide (four 32-wide steps, folded at compile time).
+template <typename T, int CB, int NSEG, bool FULL = false>
 __global__ void __launch_bounds__(512) rowgrad_kernel(RowGradParams p) {
   using Op = typename Tr<T>::Op;
   constexpr int WAVES = 8;
@@ -159,7 +160,7 @@ __global__ void __launch_bounds__(512) rowgrad_kernel(RowGradParams p) {
   const int l16 = lane & 15, g = lane >> 4;
   const int cout = p.cout;  // 16 * CB
   const int segK = NSEG * p.seg_w;
-  const int seg_steps = p.seg_w / 32;  // 1..4
+  const int seg_steps = FULL ? 4 : p.seg_w / 32;  // 1..4
 
   // W_ext columns [k0, k0 + kn) into LDS (channel-permuted rows).
   auto load_w = [&](int k0, int kn) {
@@ -486,7 +487,9 @@ constexpr size_t wgrad_lds() {
 // segment w / (8/NSEG) and the column blocks w % (8/NSEG) + (8/NSEG) i,
 // i < NSEG (i < 2 NSEG when WIDE: B up to 256 columns); with NSEG = 4 also
 // the pair-bias rows of column block w.
-template <typename T, int NSEG, bool BIAS = NSEG == 4, bool WIDE = false>
+// FULL: every segment 128 wide and B 128 (WIDE: 256) columns, so the
+// per-block guards fold away and the products are straight-line code.
+template <typename T, int NSEG, bool BIAS = NSEG == 4, bool WIDE = false, bool FULL = false>
 __global__ void __launch_bounds__(512) wgrad_kernel(WGradParams p) {
   using Op = typename Tr<T>::Op;
   constexpr int WPS = 8 / NSEG;     // waves (and column groups) per segment
@@ -508,7 +511,7 @@ __global__ void __launch_bounds__(512) wgrad_kernel(WGradParams p) {
   const int l16 = lane & 15, g = lane >> 4;
   const int pbeg = chunk * p.chunk_pos, pend = min(p.npos, pbeg + p.chunk_pos);
   const int nst = (pend - pbeg + PW - 1) / PW;
-  const int RB = p.a_w / 16, CBn = p.b_w / 16;
+  const int RB = FULL ? 8 : p.a_w / 16, CBn = FULL ? (WIDE ? 16 : 8) : p.b_w / 16;
   const int wseg = wave / WPS, cw = wave % WPS;
 
   // Staging roles.  A: segment tid / TPS, channels 8*(tid%16) .. +7 of
@@ -925,7 +928,7 @@ __global__ void __launch_bounds__(256) lnparam_kernel(LnParamParams p) {
 }
 
 // ----------------------------------------------------------------- launches
-template <typename T, int CB, int NSEG>
+template <typename T, int CB, int NSEG, bool FULL = false>
 hipError_t launch_rowgrad_cb(RowGradParams& p, hipStream_t s) {
   constexpr int WAVES = 8;
   const size_t wbytes = (size_t)p.cout * (p.Kext + PADE) * sizeof(T);
@@ -935,10 +938,12 @@ hipError_t launch_rowgrad_cb(RowGradParams& p, hipStream_t s) {
   const int64_t tiles = ((int64_t)p.npos + PW * WAVES - 1) / (PW * WAVES);
   p.ntiles = (int)tiles;
   const int grid = (int)std::min<int64_t>(tiles, 256);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&rowgrad_kernel<T, CB, NSEG>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipError_t e =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&rowgrad_kernel<T, CB, NSEG, FULL>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((rowgrad_kernel<T, CB, NSEG>), dim3(grid), dim3(WAVES * 64), lds, s, p);
+  hipLaunchKernelGGL((rowgrad_kernel<T, CB, NSEG, FULL>), dim3(grid), dim3(WAVES * 64), lds, s,
+                     p);
   return hipGetLastError();
 }
 
@@ -948,7 +953,10 @@ hipError_t launch_rowgrad_cb(RowGradParams& p, hipStream_t s) {
 template <typename T, int CB>
 hipError_t launch_rowgrad_n(RowGradParams& p, hipStream_t s) {
   switch (p.nseg) {
-    case 4: return launch_rowgrad_cb<T, CB, 4>(p, s);
+    case 4:
+      // the module at H*C = 128, c_z = 128
+      if (CB == 8 && p.seg_w == 128) return launch_rowgrad_cb<T, CB, 4, true>(p, s);
+      return launch_rowgrad_cb<T, CB, 4>(p, s);
     case 2: return launch_rowgrad_cb<T, CB, 2>(p, s);
     default: return launch_rowgrad_cb<T, CB, 1>(p, s);
   }
@@ -979,15 +987,15 @@ void chunking(int64_t npos, int target, int& nchunks, int& chunk_pos) {
 // KB of LDS), each over one chunk of positions.
 constexpr int kChunks = 256;
 
-template <typename T, int NSEG, bool BIAS, bool WIDE = false>
+template <typename T, int NSEG, bool BIAS, bool WIDE = false, bool FULL = false>
 hipError_t launch_wgrad_k(WGradParams& p, hipStream_t s) {
   const size_t lds = wgrad_lds<T, NSEG, WIDE>();
-  hipError_t e =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&wgrad_kernel<T, NSEG, BIAS, WIDE>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipError_t e = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&wgrad_kernel<T, NSEG, BIAS, WIDE, FULL>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((wgrad_kernel<T, NSEG, BIAS, WIDE>), dim3(p.nchunks), dim3(512), lds, s,
-                     p);
+  hipLaunchKernelGGL((wgrad_kernel<T, NSEG, BIAS, WIDE, FULL>), dim3(p.nchunks), dim3(512), lds,
+                     s, p);
   return hipGetLastError();
 }
 // four segments with or without the pair-bias rows; two or one without; B
@@ -1000,10 +1008,15 @@ hipError_t launch_wgrad(WGradParams& p, hipStream_t s) {
   if (p.b_w > 128)
     return p.nseg == 2 ? launch_wgrad_k<T, 2, false, true>(p, s)
                        : launch_wgrad_k<T, 1, false, true>(p, s);
+  const bool full = p.a_w == 128 && p.b_w == 128;
   switch (p.nseg) {
-    case 4: return bias ? launch_wgrad_k<T, 4, true>(p, s) : launch_wgrad_k<T, 4, false>(p, s);
+    case 4:
+      if (bias && full) return launch_wgrad_k<T, 4, true, false, true>(p, s);
+      return bias ? launch_wgrad_k<T, 4, true>(p, s) : launch_wgrad_k<T, 4, false>(p, s);
     case 2: return launch_wgrad_k<T, 2, false>(p, s);
-    case 1: return launch_wgrad_k<T, 1, false>(p, s);
+    case 1:
+      return full ? launch_wgrad_k<T, 1, false, false, true>(p, s)
+                  : launch_wgrad_k<T, 1, false>(p, s);
     default: return hipErrorInvalidValue;
   }
 }
