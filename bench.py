@@ -344,10 +344,11 @@ def softmax_ceiling(dev):
     """Issue intervals of v_exp_f32 and v_fma_f32 relative to the bf16 MFMA
     (16 clocks per v_mfma_f32_16x16x32_bf16 and SIMD at the dense peak), from
     the library's probe, and the fraction of the matrix-core peak they leave
-    the forward: per 256 logits the forward issues 2 MFMAs (32 clocks at
-    peak), 4 exp wave-instructions and 8 other VALU ones (the bias fma, the
-    bf16 packing and the row sums).  exp_only assumes the exps overlap the
-    MFMAs fully, fwd_valu the whole VALU mix, fwd_serial none of it."""
+    the forward: per 256 logits the forward issues 2 counted MFMAs (32 clocks
+    at peak) plus half a row-sum MFMA (8 clocks), 4 exp wave-instructions and
+    6 other VALU ones (the bias fma and the bf16 packing).  exp_only assumes
+    the exps overlap the MFMAs fully, fwd_valu the whole VALU mix, fwd_serial
+    none of it; each is the counted MFMA time over the busier unit's."""
     import torch
     from evoformer_attention_amd import ops
     waves, iters = 8, 4096
@@ -365,12 +366,13 @@ def softmax_ceiling(dev):
         t[kind] = e0.elapsed_time(e1) / (waves * iters * 8)
     c_exp = 16.0 * t[0] / t[2]
     c_fma = 16.0 * t[1] / t[2]
-    valu = 4 * c_exp + 8 * c_fma
+    valu = 4 * c_exp + 6 * c_fma
+    mfma = 32.0 + 8.0
     return {"exp_clocks": round(c_exp, 2), "fma_clocks": round(c_fma, 2),
             "mfma_clocks": 16.0,
-            "exp_only": round(min(1.0, 32.0 / (4 * c_exp)), 3),
-            "fwd_valu": round(min(1.0, 32.0 / valu), 3),
-            "fwd_serial": round(32.0 / (32.0 + valu), 3),
+            "exp_only": round(32.0 / max(mfma, 4 * c_exp), 3),
+            "fwd_valu": round(32.0 / max(mfma, valu), 3),
+            "fwd_serial": round(32.0 / (mfma + valu), 3),
             "method": "evo_probe_issue_rate, 8 waves per SIMD; clocks relative to "
                       "the MFMA interval (16 at the dense peak)"}
 

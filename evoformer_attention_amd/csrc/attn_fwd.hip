@@ -67,6 +67,7 @@ constexpr int BQW = 32;           // queries per wave
 constexpr int WAVES = 4;
 constexpr int BQ = BQW * WAVES;   // queries per workgroup
 constexpr float kHeadroom = 256.f;  // 2^8: largest tile sum of p per lane
+constexpr float kHeadroomRow = 1024.f;  // 2^10: largest half-tile row sum
 
 // Prepared-bias element: bf16 inputs are stored as fp16, which holds every
 // bf16 value of magnitude 2^-14 .. 65504 exactly (8 significant bits fit in
@@ -264,7 +265,7 @@ __global__ void __launch_bounds__(256) fwd_bias_prep_kernel(
 // Exponents of one 32-key half `hf_` of the tile, base 2, all lines of the
 // group: t = K . (Q log2(e)/sqrt(C))^T - ref + bias * log2(e), where the
 // reference enters as the products' accumulator operand `ref_` ([qb] splats)
-// and the prepared bias (`braw`, 8 values per (qb, half)) is added by one
+// and the prepared bias of the half (`braw`, 8 values per qb) is added by one
 // fma per logit (v_fma_mix_f32 for the fp16 bias).  Dead keys: -inf.
 #define EVO_FWD_T(hf_, ref_)                                                     \
   do {                                                                           \
@@ -277,7 +278,7 @@ __global__ void __launch_bounds__(256) fwd_bias_prep_kernel(
     for (int rr = 0; rr < ROWS; ++rr)                                            \
       for (int qb = 0; qb < 2; ++qb) {                                           \
         if constexpr (HAS_BIAS) {                                                \
-          add_bias8(t[rr][qb][0], t[rr][qb][1], braw[qb][hf_]);                   \
+          add_bias8(t[rr][qb][0], t[rr][qb][1], braw[qb]);                        \
         } else {                                                                 \
           if (k0 + BK > N)                                                       \
             for (int kb = 0; kb < 2; ++kb)                                       \
@@ -411,26 +412,24 @@ attn_fwd_kernel(FwdParams p) {
   // from the workgroup's tile row with the lane's offset fixed, like the K/V
   // tiles.)
   using BRaw = std::conditional_t<sizeof(T) == 2, u32x4, Raw8<float>>;
-  BRaw braw[2][2];  // [qb][half]
+  BRaw braw[2];  // [qb], one half tile ahead
   const uint32_t bvoff = (uint32_t)(wave * 2048 + lane * 8) * 2u;
   const uint32_t bbytes = (uint32_t)(p.Nk / BK) * (BQ * BK) * 2u;  // the row
-#define EVO_FETCH_BIAS(k0_)                                                        \
+#define EVO_FETCH_BIAS(k0_, half_)                                                 \
   do {                                                                         \
     if constexpr (HAS_BIAS) {                                                  \
-      for (int qb = 0; qb < 2; ++qb)                                           \
-        for (int half = 0; half < 2; ++half) {                                 \
-          if constexpr (sizeof(T) == 2)                                        \
-            braw[qb][half] = buf_ld128(btile, bbytes, bvoff + (qb * 2 + half) * 1024u, \
-                                       (uint32_t)((k0_) / BK) * (BQ * BK * 2u)); \
-          else                                                                 \
-            ld_raw8(braw[qb][half],                                            \
-                    bbase + (int64_t)((k0_) / BK) * (BQ * BK) + (qb * 2 + half) * 512); \
-        }                                                                      \
+      for (int qb = 0; qb < 2; ++qb) {                                         \
+        if constexpr (sizeof(T) == 2)                                          \
+          braw[qb] = buf_ld128(btile, bbytes, bvoff + (qb * 2 + (half_)) * 1024u, \
+                               (uint32_t)((k0_) / BK) * (BQ * BK * 2u));       \
+        else                                                                   \
+          ld_raw8(braw[qb], bbase + (int64_t)((k0_) / BK) * (BQ * BK) + (qb * 2 + (half_)) * 512); \
+      }                                                                        \
     }                                                                          \
   } while (0)
 #pragma unroll
   for (int rr = 0; rr < ROWS; ++rr) fetch_kv<T>(raw[rr], kline[rr], vline[rr], 0, N, pos_stride);
-  EVO_FETCH_BIAS(0);
+  EVO_FETCH_BIAS(0, 0);
 
   // -m of each query as a splat accumulator operand of the logit products
   // (+inf while a query has seen no live key: its exponents are then inf or
@@ -445,6 +444,21 @@ attn_fwd_kernel(FwdParams p) {
   for (int rr = 0; rr < ROWS; ++rr)
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) zero[rr][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Sum of p over a half tile for each query.  bf16: on the matrix core
+  // (A = ones), so every lane holds its query's whole sum; fp32: the lane's
+  // 8 values, summed across lanes in the epilogue.
+  constexpr bool kRowSum = sizeof(T) == 2;
+  auto half_sum = [&](const Op& pv) -> float {
+    if constexpr (kRowSum) {
+      Op ones;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ones[j] = (__bf16)1.0f;
+      return mma32(ones, pv, f32x4{0.f, 0.f, 0.f, 0.f})[0];
+    } else {
+      return sum8(pv, 0.f);
+    }
+  };
 
   const int ntiles = (N + BK - 1) / BK;
   for (int tile = 0; tile < ntiles; ++tile) {
@@ -494,9 +508,9 @@ attn_fwd_kernel(FwdParams p) {
 #pragma unroll
               for (int i = 0; i < 4; ++i) e[kb][i] = exp2_fast(t[rr][qb][kb][i]);
             pf[rr][qb] = pack8(e[0], e[1], (Op*)nullptr);
-            psum[rr][qb] = sum8(pf[rr][qb], 0.f);
+            psum[rr][qb] = half_sum(pf[rr][qb]);
             // not yet anchored (inf or NaN), or too large
-            redo |= !(psum[rr][qb] <= kHeadroom);
+            redo |= !(psum[rr][qb] <= (kRowSum ? kHeadroomRow : kHeadroom));
           }
         slow = __builtin_amdgcn_ballot_w64(redo) != 0;
       }
@@ -531,9 +545,15 @@ attn_fwd_kernel(FwdParams p) {
 #pragma unroll
               for (int i = 0; i < 4; ++i) e[kb][i] = exp2_fast(t[rr][qb][kb][i] - muse);
             pf[rr][qb] = pack8(e[0], e[1], (Op*)nullptr);
-            psum[rr][qb] = sum8(pf[rr][qb], 0.f);
+            psum[rr][qb] = half_sum(pf[rr][qb]);
           }
       }
+      // the bias of the next half (bf16 reads past the workgroup's row of
+      // tiles as zeros, so it needs no test and its waits stay exact)
+      if (hf == 0)
+        EVO_FETCH_BIAS(k0, 1);
+      else if (sizeof(T) == 2 || tile + 1 < ntiles)
+        EVO_FETCH_BIAS(k0 + BK, 0);
 #pragma unroll
       for (int rr = 0; rr < ROWS; ++rr)
 #pragma unroll
@@ -564,7 +584,6 @@ attn_fwd_kernel(FwdParams p) {
     // next tile's bias operands (the logit registers are free again); bf16
     // reads past the workgroup's row of tiles as zeros, so it needs no test
     // and its waits stay exact
-    if (sizeof(T) == 2 || tile + 1 < ntiles) EVO_FETCH_BIAS(k0 + BK);
   }
 
   // Epilogue: normalise, gate, store; LSE in natural log.
@@ -578,8 +597,10 @@ attn_fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       float lt = l[rr][qb];
-      lt += shfl_xor(lt, 16);
-      lt += shfl_xor(lt, 32);
+      if constexpr (!kRowSum) {
+        lt += shfl_xor(lt, 16);
+        lt += shfl_xor(lt, 32);
+      }
       const int q = qw0 + qb * 16 + l16;
       if (q >= N) continue;
       const float inv = lt > 0.f ? rcp_fast(lt) : 0.f;
