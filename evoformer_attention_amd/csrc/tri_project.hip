@@ -165,13 +165,15 @@ __device__ __forceinline__ void store_pair<float>(float* row, const f32x4& a, co
 // the unmodified bf16 weights: the projection is then exact up to fp32
 // accumulation before its one rounding to the output type, instead of
 // rounding y (and W * gamma) to bf16 first.  Twice the products and the
-// operand registers: eight waves per workgroup (two per SIMD); used up to
-// 160 input channels (wider inputs keep the single rounded operand).
+// operand registers: up to 128 input channels, 16 positions per wave and
+// 16 waves per workgroup (four per SIMD); up to 160, 32 positions and eight
+// waves (wider inputs keep the single rounded operand).
 template <typename T, int KSTEPS, int WAVES = waves_for<KSTEPS>(), bool MUL = false,
-          bool SPLIT = false>
+          bool SPLIT = false, int PB = 2>
 __global__ void __launch_bounds__(WAVES * 64)
 rowgemm_kernel(GemmParams p) {
-  constexpr int PB = 2;               // 16-position blocks per wave
+  // PB: 16-position blocks per wave (1 only for the split operands)
+  static_assert(PB == 2 || (SPLIT && PB == 1), "one block per wave only with split operands");
   constexpr int PWV = 16 * PB;        // positions per wave
   using Op = typename Tr<T>::Op;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -317,9 +319,9 @@ rowgemm_kernel(GemmParams p) {
     // part; xl the lo part).
     Op xf[PB][KSTEPS];
     Op xl[SPLIT ? PB : 1][SPLIT ? KSTEPS : 1];
-    uint32_t pidx[2];
-    int64_t orow[2];
-    bool live[2] = {false, false};
+    uint32_t pidx[PB];
+    int64_t orow[PB];
+    bool live[PB];
 #pragma unroll
     for (int pb = 0; pb < PB; ++pb) {
       pidx[pb] = tile_pos<WAVES, PWV>(p, tile, wave, pb * 16 + l16, live[pb]);
@@ -412,22 +414,23 @@ rowgemm_kernel(GemmParams p) {
       T* out = static_cast<T*>(p.y[p.mode == 1 ? 0 : m]);  // mode 2: a, then b
       while (cb < nblk && cbase < width) {
         const bool pair = !MUL && !bias_out && cb + 1 < nblk && cbase + 32 <= width;
-        f32x4 acc[2][2];  // [block][pb]
+        f32x4 acc[2][PB];  // [block][pb]
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           if (j == 1 && !pair) break;
           const f32x4 cc4 = *reinterpret_cast<const f32x4*>(sC + (cb + j) * 16 + 4 * g);
-          acc[j][0] = cc4;
-          acc[j][1] = cc4;
+#pragma unroll
+          for (int pb = 0; pb < PB; ++pb) acc[j][pb] = cc4;
           const T* wr = sW + ((cb + j) * 16 + l16) * KS + 8 * g;
 #pragma unroll
           for (int s = 0; s < KSTEPS; ++s) {
             const Op a = *reinterpret_cast<const Op*>(wr + 32 * s);
             if constexpr (SPLIT) {
-              acc[j][0] = mma32(a, xl[0][s], acc[j][0]);
-              acc[j][0] = mma32(a, xf[0][s], acc[j][0]);
-              acc[j][1] = mma32(a, xl[1][s], acc[j][1]);
-              acc[j][1] = mma32(a, xf[1][s], acc[j][1]);
+#pragma unroll
+              for (int pb = 0; pb < PB; ++pb) {
+                acc[j][pb] = mma32(a, xl[pb][s], acc[j][pb]);
+                acc[j][pb] = mma32(a, xf[pb][s], acc[j][pb]);
+              }
             } else {
               acc[j][0] = mma32(a, xf[0][s], acc[j][0]);
               acc[j][1] = mma32(a, xf[1][s], acc[j][1]);
@@ -532,17 +535,20 @@ rowgemm_kernel(GemmParams p) {
 
 template <typename T, int KSTEPS, bool MUL, bool SPLIT = false>
 hipError_t launch_pass_m(GemmParams& p, size_t lds, hipStream_t s) {
-  constexpr int WAVES = SPLIT ? 8 : waves_for<KSTEPS>();
-  constexpr int PWV = PW;
+  // split operands: 16 positions per wave up to 128 input channels (16
+  // waves), 32 positions and 8 waves above
+  constexpr int PB = SPLIT && KSTEPS <= 4 ? 1 : 2;
+  constexpr int WAVES = SPLIT ? (PB == 1 ? 16 : 8) : waves_for<KSTEPS>();
+  constexpr int PWV = 16 * PB;
   const int64_t tiles = (p.npos + PWV * WAVES - 1) / (PWV * WAVES);
   if (tiles > (int64_t)INT32_MAX) return hipErrorInvalidValue;
   p.ntiles = (int)tiles;
   const int grid = (int)std::min<int64_t>(tiles, 256);  // persistent: one per CU
   hipError_t e = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&rowgemm_kernel<T, KSTEPS, WAVES, MUL, SPLIT>),
+      reinterpret_cast<const void*>(&rowgemm_kernel<T, KSTEPS, WAVES, MUL, SPLIT, PB>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((rowgemm_kernel<T, KSTEPS, WAVES, MUL, SPLIT>), dim3(grid), dim3(WAVES * 64), lds,
+  hipLaunchKernelGGL((rowgemm_kernel<T, KSTEPS, WAVES, MUL, SPLIT, PB>), dim3(grid), dim3(WAVES * 64), lds,
                      s, p);
   return hipGetLastError();
 }
