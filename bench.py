@@ -248,18 +248,32 @@ def cpu_baseline(name, w, d, n_lines):
         mask = None if d["mask"] is None else d["mask"].numpy()
         bias = None if d["bias"] is None else np64(d["bias"][0])
         keep = None if mask is None else mask[0, 0] != 0
-        reps = 0
-        while True:     # a workload this small is repeated for a stable time
-            for r in rows:
-                O.attention_line_forward(np64(d["q"][0, r]), np64(d["k"][0, r]),
-                                         np64(d["v"][0, r]), np64(d["gate"][0, r]), bias, keep)
-            reps += 1
-            if time.perf_counter() - t0 > 2.0:
-                break
+
+        def run_lines(seconds):
+            """Repeat the sampled lines for at least `seconds` (a workload
+            this small is repeated for a stable time); (reps, elapsed s)."""
+            reps, ts = 0, time.perf_counter()
+            while True:
+                for r in rows:
+                    O.attention_line_forward(np64(d["q"][0, r]), np64(d["k"][0, r]),
+                                             np64(d["v"][0, r]), np64(d["gate"][0, r]),
+                                             bias, keep)
+                reps += 1
+                if time.perf_counter() - ts > seconds:
+                    return reps, time.perf_counter() - ts
+        reps, _ = run_lines(2.0)
         t1 = t2 = time.perf_counter()
         flops = reps * len(rows) * 4.0 * H * N * N * C
         what = (f"{len(rows)} of {R} attention lines of {name}: forward"
                 + (f", {reps} times" if reps > 1 else ""))
+        # the same lines with the BLAS pool held to one thread: a per-core figure
+        try:
+            from threadpoolctl import threadpool_limits
+            with threadpool_limits(limits=1):
+                reps1, dt1 = run_lines(1.0)
+            single = reps1 * len(rows) * 4.0 * H * N * N * C / dt1 / 1e12
+        except Exception:  # noqa: BLE001
+            single = None
     else:
         ending = w.get("ending", False)
         args = dict(z=np64(d["z"]),
@@ -287,10 +301,13 @@ def cpu_baseline(name, w, d, n_lines):
         what = (f"{len(lines)} of {N} attention lines of {name}: line-wise module forward"
                 + (" + core backward" if backward else "")
                 + f" ({t1 - t0:.1f} s forward including the pair bias of the whole z)")
-    return {"value": flops / (t2 - t0) / 1e12, "unit": "TFLOP/s",
-            "cores": int(blas), "kind": "oracle",
-            "sample": f"{what}; {t2 - t0:.1f} s wall",
-            "host_cpus": int(nproc), "cpu_model": model}
+    out = {"value": flops / (t2 - t0) / 1e12, "unit": "TFLOP/s",
+           "cores": int(blas), "kind": "oracle",
+           "sample": f"{what}; {t2 - t0:.1f} s wall",
+           "host_cpus": int(nproc), "cpu_model": model}
+    if w["kind"] == "core" and single is not None:
+        out["single_thread_value"] = single
+    return out
 
 
 def stats(ms):
