@@ -225,6 +225,11 @@ hipError_t launch_pair_gemm(int dtype, int C, int M, int K, int Np, int Kp, void
 // T [C][M][M2]; Np and Np2 multiples of pair_gemm_row_tile().
 hipError_t launch_pair_gemm_rect(int dtype, int C, int M, int M2, int K, int Np, int Np2, int Kp,
                                  void* a, void* b, void* t, bool a_frag, hipStream_t s);
+// bf16, one product with A in fragment order, M = N*C rows (i, c) and columns
+// (j, d), C a multiple of 32: P written as pair rows pf[(i*N + j)*C + c][d] =
+// scale * P[(i, c)][(j, d)], rounded once.
+hipError_t launch_pair_gemm_pairs(int M, int K, int Np, int Kp, void* a, void* b, void* pf,
+                                  int N, int C, float scale, hipStream_t s);
 // Channel-major matrices [C] of (row r < rows, column q < ncols) at c*cs +
 // r*ld + q to position rows dst[pos][C], pos = r*N + q (q*N + r when trans),
 // zero where keep is given and keep[q] == 0.  C a multiple of 32, at most 128.

@@ -422,8 +422,9 @@ OpmBwdLayout opm_bwd_layout(int dtype, int64_t S, int64_t N, int64_t CM, int64_t
 //   dP = dout . W_o / S (per pair, the C x C block),  dW_o = sum dout^T P / S,
 //   dA = dP . B  (rows (i, c), columns s),  dB = dP^T . A,
 //   then the LayerNorm + projection backward of m from da, db.
-// Steps: the forward's operands A, B and the product P recomputed; P to pair
-// rows (scaled by 1/S) for dW_o, db_o (column weight-gradient reduction, 256
+// Steps: the forward's operands A, B and the product P recomputed as pair
+// rows scaled by 1/S (bf16: written so by the product's epilogue; fp32: a
+// separate pass) for dW_o, db_o (column weight-gradient reduction, 256
 // columns of W_o at a time); the same projections written with sequences as
 // rows (Y_a[s][(i, c)] = a[s, i, c], likewise Y_b) as the second operands;
 // dP and dP^T (opm_dp_kernel); the two products dA = dP . Y_b^T and
@@ -442,10 +443,15 @@ hipError_t opm_bwd_t(const OpmBwdArgs& a, hipStream_t s) {
                         bf ? L.Kp : 0};
   hipError_t e = launch_channel_project(pa, s);
   if (e != hipSuccess) return e;
-  if ((e = launch_pair_gemm(a.dtype, 1, M, S, (int)L.Np, (int)L.Kp, at(L.a), at(L.b), at(L.p),
-                            bf, s)) != hipSuccess)
-    return e;
-  {
+  if (bf) {
+    // bf16: the product's epilogue writes the pair rows directly
+    if ((e = launch_pair_gemm_pairs(M, S, (int)L.Np, (int)L.Kp, at(L.a), at(L.b), at(L.pf), N, C,
+                                    1.f / (float)S, s)) != hipSuccess)
+      return e;
+  } else {
+    if ((e = launch_pair_gemm(a.dtype, 1, M, S, (int)L.Np, (int)L.Kp, at(L.a), at(L.b), at(L.p),
+                              false, s)) != hipSuccess)
+      return e;
     const int64_t total = (int64_t)M * M / 8;
     const int grid = (int)std::min<int64_t>((total + 255) / 256, 16384);
     hipLaunchKernelGGL(opm_pair_rows_kernel<T>, dim3(grid), dim3(256), 0, s, at(L.p), at(L.pf),

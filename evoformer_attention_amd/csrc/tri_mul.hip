@@ -67,6 +67,11 @@ struct MulGemmParams {
   const void* b;  // [C][Np2][Kp]
   void* t;        // [C][N][N2]
   int ntile, ntile2;  // Np / kTile, Np2 / kTile
+  // pair_c > 0 (bf16 256 x 128 kernel, one product): T[(i, c)][(j, d)] is
+  // written as pair rows t[(i * pair_n + j) * pair_c + c][d] times pair_scale
+  // (rows and columns of T are residue * pair_c + channel)
+  int pair_n, pair_c;
+  float pair_scale;
 };
 
 // Row tiles per group of the work order.
@@ -299,6 +304,26 @@ __global__ void __launch_bounds__(256 * WJ) pair_gemm_bf16_kernel(MulGemmParams 
   }
 
   // lane (l16, g) holds T[i = .. + bi*16 + l16][j = .. + bj*16 + 4g + r]
+  if (p.pair_c > 0) {
+    // pair rows: the 4 consecutive j of a lane share one residue (pair_c is a
+    // multiple of 32), so each stays one 8-byte store
+    const int PC = p.pair_c;
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi) {
+      const int i = ti * kBigI + wi * 64 + bi * 16 + l16;
+      if (i >= p.N) continue;
+      const int ir = i / PC, ci = i - ir * PC;
+#pragma unroll
+      for (int bj = 0; bj < 8; ++bj) {
+        const int j0 = tj * BROWS + wj * kBigJ + bj * 16 + 4 * g;
+        if (j0 >= p.N2) continue;
+        const int jr = j0 / PC, dj = j0 - jr * PC;
+        st4t<T>(static_cast<T*>(p.t) + ((int64_t)(ir * p.pair_n + jr) * PC + ci) * PC + dj,
+                acc[bj][bi] * p.pair_scale);
+      }
+    }
+    return;
+  }
   T* Tc = static_cast<T*>(p.t) + (int64_t)c * p.N * p.N2;
 #pragma unroll
   for (int bi = 0; bi < 4; ++bi) {
@@ -502,7 +527,8 @@ MulLayout mul_layout(int dtype, int64_t N, int64_t C) {
 // [C][M][M2].
 template <typename T>
 hipError_t pair_gemm_t(int C, int M, int M2, int K, int Np, int Np2, int Kp, T* A, T* B, T* Tm,
-                       bool a_frag, hipStream_t s) {
+                       bool a_frag, hipStream_t s, int pair_n = 0, int pair_c = 0,
+                       float pair_scale = 1.f) {
   hipError_t e;
   if (Kp > K) {
     const int64_t total = (int64_t)C * std::max(M, M2) * (Kp - K);
@@ -517,6 +543,9 @@ hipError_t pair_gemm_t(int C, int M, int M2, int K, int Np, int Np2, int Kp, T* 
   g.a = A; g.b = B; g.t = Tm;
   g.ntile = Np / kTile;
   g.ntile2 = Np2 / kTile;
+  g.pair_n = pair_n;
+  g.pair_c = pair_c;
+  g.pair_scale = pair_scale;
   // bf16: the 256 x 128 kernel for one large product (24576^2 by K = 1024:
   // 1.78 vs 1.93 ms), the 128 x 128 one for many small ones (128 products of
   // 768^2 by 768: 206 vs 218 us)
@@ -527,7 +556,8 @@ hipError_t pair_gemm_t(int C, int M, int M2, int K, int Np, int Np2, int Kp, T* 
     if constexpr (sizeof(T) == 2)
       hipLaunchKernelGGL(pair_gemm_bf16_kernel<WJ>, dim3(grid), dim3(256 * WJ), 0, s, g);
   } else {
-    if (a_frag) return hipErrorInvalidValue;  // the 128 x 128 kernel reads row-major A
+    // the 128 x 128 kernel reads row-major A and writes T in plain rows
+    if (a_frag || pair_c > 0) return hipErrorInvalidValue;
     const int total = C * g.ntile * g.ntile2;
     const int grid = (total + kNumXcd - 1) / kNumXcd * kNumXcd;
     hipLaunchKernelGGL(trimul_gemm_kernel<T>, dim3(grid), dim3(256), 0, s, g);
@@ -793,6 +823,16 @@ int pair_gemm_row_tile() { return kRowPad; }
 hipError_t launch_pair_gemm(int dtype, int C, int M, int K, int Np, int Kp, void* a, void* b,
                             void* t, bool a_frag, hipStream_t s) {
   return launch_pair_gemm_rect(dtype, C, M, M, K, Np, Np, Kp, a, b, t, a_frag, s);
+}
+
+hipError_t launch_pair_gemm_pairs(int M, int K, int Np, int Kp, void* a, void* b, void* pf,
+                                  int N, int C, float scale, hipStream_t s) {
+  if (Np % kRowPad != 0 || M > Np || K > Kp || Kp % MulCfg<bf16_t>::BK != 0 || C <= 0 ||
+      C % 32 != 0 || (int64_t)N * C != M)
+    return hipErrorInvalidValue;
+  return pair_gemm_t<bf16_t>(1, M, M, K, Np, Np, Kp, static_cast<bf16_t*>(a),
+                             static_cast<bf16_t*>(b), static_cast<bf16_t*>(pf), true, s, N, C,
+                             scale);
 }
 
 hipError_t launch_pair_gemm_rect(int dtype, int C, int M, int M2, int K, int Np, int Np2, int Kp,
