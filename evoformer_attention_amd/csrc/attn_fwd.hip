@@ -20,11 +20,12 @@
 //   attn_fwd   a workgroup (4 waves) owns 128 queries of one head and one
 //              line (ROWS = 1; the kernel is written for ROWS lines sharing
 //              the bias tile); each wave owns 32 queries.  Keys stream in
-//              tiles of 64 through double-buffered LDS, the next tile's K, V
-//              and bias being fetched into registers while the current one is
+//              tiles of 64 through double-buffered LDS, the next tile's K and
+//              V being fetched into registers while the current one is
 //              computed (one barrier per tile); each tile is processed as two
-//              32-key halves (logits, softmax, PV), which keeps the kernel at
-//              ~100 registers per lane: five waves per SIMD.
+//              32-key halves (logits, softmax, PV), the bias one half ahead,
+//              which keeps the kernel under 96 registers per lane: five
+//              waves per SIMD.
 //
 // Matrix-core mapping (v_mfma_f32_16x16x32_bf16, fp32 accumulate):
 //   T^T = K . Q'^T - m       A = 16 keys x 32 dims (LDS), B = Q'^T = (Q
@@ -35,6 +36,9 @@
 //                            bias, so T is the base-2 exponent itself.
 //   O^T += V^T . P^T         A = V^T from LDS, B = P^T taken straight from
 //                            the S^T accumulators (no LDS round trip).
+//   l += ones . P^T          (bf16) the row sums of P over each half, on the
+//                            matrix core: every lane receives its query's
+//                            whole sum, no cross-lane reduction.
 // In the accumulator layout a lane holds one query and 4 keys per 16-key
 // block; the key order inside a tile is permuted so that each lane's 8 keys
 // of a 32-key half are consecutive: the P^T operand is then exactly the
@@ -45,10 +49,11 @@
 // (base 2, subtracted inside the products) that is only raised when needed:
 // the first half-tile (and any half while a query has seen no live key)
 // computes the true maximum; a later half is recomputed with a raised
-// reference only if a lane's sum of p over it exceeds 2^8.  So every
-// p <= 2^8 (no overflow in fp32 or bf16), m never exceeds the true maximum
-// (no underflow of the result), and the common half costs one fma and one
-// exp per logit plus a dot2 per two for the row sum, with no cross-lane
+// reference only if a query's sum of p over it exceeds 2^10 (bf16, the
+// matrix-core row sum; fp32: a lane's 8 values, 2^8).  So every p <= 2^10
+// (no overflow in fp32 or bf16), m never exceeds the true maximum (no
+// underflow of the result), and the common half costs one fma and one exp
+// per logit plus half a pack and the row-sum product, with no cross-lane
 // reduction and no conversion of the bias.  The result is exact up to
 // rounding for any m, since O and l are scaled by the same exp2(-m).
 #include <algorithm>
@@ -66,7 +71,7 @@ constexpr int BK = 64;            // keys per tile
 constexpr int BQW = 32;           // queries per wave
 constexpr int WAVES = 4;
 constexpr int BQ = BQW * WAVES;   // queries per workgroup
-constexpr float kHeadroom = 256.f;  // 2^8: largest tile sum of p per lane
+constexpr float kHeadroom = 256.f;  // 2^8: largest half-tile sum of p per lane (fp32)
 constexpr float kHeadroomRow = 1024.f;  // 2^10: largest half-tile row sum
 
 // Prepared-bias element: bf16 inputs are stored as fp16, which holds every
@@ -406,11 +411,10 @@ attn_fwd_kernel(FwdParams p) {
   }
 
   KVRaw<T> raw[ROWS];
-  // Bias values of the next tile as loaded (raw); they stay in flight
-  // across the K/V tile store instead of being waited for at the end of the
-  // tile.  (bf16 inputs: 8 fp16 values per (qb, half) in one buffer load
-  // from the workgroup's tile row with the lane's offset fixed, like the K/V
-  // tiles.)
+  // Bias values of the next half tile as loaded (raw), fetched into the
+  // registers the current half has just used.  (bf16 inputs: 8 fp16 values
+  // per (qb, half) in one buffer load from the workgroup's tile row with the
+  // lane's offset fixed, like the K/V tiles.)
   using BRaw = std::conditional_t<sizeof(T) == 2, u32x4, Raw8<float>>;
   BRaw braw[2];  // [qb], one half tile ahead
   const uint32_t bvoff = (uint32_t)(wave * 2048 + lane * 8) * 2u;
@@ -581,9 +585,6 @@ attn_fwd_kernel(FwdParams p) {
         __builtin_amdgcn_s_setprio(0);
       }
     }
-    // next tile's bias operands (the logit registers are free again); bf16
-    // reads past the workgroup's row of tiles as zeros, so it needs no test
-    // and its waits stay exact
   }
 
   // Epilogue: normalise, gate, store; LSE in natural log.
