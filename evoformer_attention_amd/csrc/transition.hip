@@ -135,26 +135,51 @@ __global__ void __launch_bounds__(WAVES * 64) transition_kernel(TransParams p) {
   const int l16 = lane & 15, g = lane >> 4;
   const int nchunks = p.HID / HC;
 
-  // The chunk's prepared weights into buffer `buf`: 16-byte copies of the
-  // contiguous prepared blocks into the padded LDS rows.
-  auto load_chunk = [&](int q, int buf) {
+  // The chunk's prepared weights: 16-byte loads of the contiguous prepared
+  // blocks into registers at the start of a chunk (fetch_chunk), copied into
+  // the padded LDS rows of the other buffer at its end (store_chunk), so the
+  // loads are in flight while the chunk is computed.
+  constexpr int E16 = 16 / sizeof(T);
+  constexpr int NWAB = 2 * HC * CZ / E16, NWO = CZ * HC / E16;
+  constexpr int PER = (NWAB + NWO + WAVES * 64 - 1) / (WAVES * 64);
+  u32x4 wreg[PER];
+  float creg = 0.f;
+  // buffer loads: the prepared arrays' bases and sizes uniform, each lane's
+  // offset fixed, the chunk's offset added per chunk
+  const uint32_t wab_bytes = (uint32_t)((int64_t)nchunks * 2 * HC * CZ * sizeof(T));
+  const uint32_t wo_bytes = (uint32_t)((int64_t)nchunks * CZ * HC * sizeof(T));
+  auto fetch_chunk = [&](int q) {
+    const uint32_t qab = (uint32_t)(q * 2 * HC * CZ * sizeof(T));
+    const uint32_t qo = (uint32_t)(q * CZ * HC * sizeof(T));
+    // each prepared array is contiguous: its 16-byte block e sits at byte
+    // 16 e of the chunk
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = tid + u * WAVES * 64;
+      if (e < NWAB)
+        wreg[u] = buf_ld128(p.wab, wab_bytes, (uint32_t)e * 16u, qab);
+      else if (e < NWAB + NWO)
+        wreg[u] = buf_ld128(p.wo, wo_bytes, (uint32_t)(e - NWAB) * 16u, qo);
+    }
+    if (tid < 2 * HC) creg = p.cst[(int64_t)q * 2 * HC + tid];
+  };
+  auto store_chunk = [&](int buf) {
     T* sw = sbuf + buf * BUF;
     T* so = sw + 2 * HC * WRS;
-    constexpr int E16 = 16 / sizeof(T);
-    const T* gw = static_cast<const T*>(p.wab) + (int64_t)q * 2 * HC * CZ;
-    const T* go = static_cast<const T*>(p.wo) + (int64_t)q * CZ * HC;
-    for (int e = tid; e < 2 * HC * CZ / E16; e += WAVES * 64) {
-      const int row = e / (CZ / E16), col = (e - row * (CZ / E16)) * E16;
-      *reinterpret_cast<u32x4*>(sw + row * WRS + col) =
-          *reinterpret_cast<const u32x4*>(gw + (int64_t)row * CZ + col);
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = tid + u * WAVES * 64;
+      if (e < NWAB) {
+        const int row = e / (CZ / E16), col = (e - row * (CZ / E16)) * E16;
+        *reinterpret_cast<u32x4*>(sw + row * WRS + col) = wreg[u];
+      } else if (e < NWAB + NWO) {
+        const int e2 = e - NWAB, row = e2 / (HC / E16), col = (e2 - row * (HC / E16)) * E16;
+        *reinterpret_cast<u32x4*>(so + row * ORS + col) = wreg[u];
+      }
     }
-    for (int e = tid; e < CZ * HC / E16; e += WAVES * 64) {
-      const int row = e / (HC / E16), col = (e - row * (HC / E16)) * E16;
-      *reinterpret_cast<u32x4*>(so + row * ORS + col) =
-          *reinterpret_cast<const u32x4*>(go + (int64_t)row * HC + col);
-    }
-    for (int e = tid; e < 2 * HC; e += WAVES * 64) sC[buf * 2 * HC + e] = p.cst[(int64_t)q * 2 * HC + e];
+    if (tid < 2 * HC) sC[buf * 2 * HC + tid] = creg;
   };
+  static_assert(2 * HC <= WAVES * 64, "one constant per thread");
 
   const T* Z = static_cast<const T*>(p.z);
   for (int tile = blockIdx.x; tile < p.ntiles; tile += gridDim.x) {
@@ -215,11 +240,12 @@ __global__ void __launch_bounds__(WAVES * 64) transition_kernel(TransParams p) {
     for (int cb = 0; cb < CB; ++cb) acc[cb][0] = acc[cb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     __syncthreads();  // the previous tile's last chunk is no longer read
-    load_chunk(0, 0);
+    fetch_chunk(0);
+    store_chunk(0);
     for (int q = 0; q < nchunks; ++q) {
       const int buf = q & 1;
       __syncthreads();  // chunk q is in LDS; chunk q-1's buffer is free
-      if (q + 1 < nchunks) load_chunk(q + 1, buf ^ 1);
+      if (q + 1 < nchunks) fetch_chunk(q + 1);
       const T* sw = sbuf + buf * BUF;
       const T* so = sw + 2 * HC * WRS;
       const float* sc = sC + buf * 2 * HC;
@@ -271,6 +297,7 @@ __global__ void __launch_bounds__(WAVES * 64) transition_kernel(TransParams p) {
           acc[cb][1] = mma32(wo, hf[1], acc[cb][1]);
         }
       }
+      if (q + 1 < nchunks) store_chunk(buf ^ 1);
     }
     // lane (l16, g) holds out[position pb*16 + l16][cb*16 + 4g + i]
 #pragma unroll

@@ -168,6 +168,44 @@ __global__ void __launch_bounds__(WAVES * 64) transition_bwd_kernel(TransBwdPara
     for (int e = tid; e < 2 * HC; e += WAVES * 64) sC[buf * 2 * HC + e] = p.cst[(int64_t)q * 2 * HC + e];
   };
 
+  // bf16 (two buffers): the next chunk's 16-byte blocks are loaded into
+  // registers at the start of a chunk (buffer loads: uniform bases, each
+  // lane's offset fixed) and copied into the other buffer at its end, so the
+  // loads are in flight while the chunk is computed.
+  constexpr int NW3 = 3 * HC * CZ / E16, NTT = 2 * CZ * HC / E16;
+  constexpr int PER = (NW3 + NTT + WAVES * 64 - 1) / (WAVES * 64);
+  u32x4 wreg[NB == 2 ? PER : 1];
+  float creg = 0.f;
+  const uint32_t wts_bytes = (uint32_t)((int64_t)nchunks * 5 * HC * CZ * sizeof(T));
+  auto fetch_chunk = [&](int q) {
+    const uint32_t qo = (uint32_t)(q * 5 * HC * CZ * sizeof(T));
+    // the chunk's prepared blocks are contiguous: 16-byte block e sits at
+    // byte 16 e of the chunk
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = tid + u * WAVES * 64;
+      if (e < NW3 + NTT) wreg[u] = buf_ld128(p.wts, wts_bytes, (uint32_t)e * 16u, qo);
+    }
+    if (tid < 2 * HC) creg = p.cst[(int64_t)q * 2 * HC + tid];
+  };
+  auto store_chunk = [&](int buf) {
+    T* sw = sbuf + buf * BUF;
+    T* st = sw + 3 * HC * WRS;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = tid + u * WAVES * 64;
+      if (e < NW3) {
+        const int row = e / (CZ / E16), col = (e - row * (CZ / E16)) * E16;
+        *reinterpret_cast<u32x4*>(sw + row * WRS + col) = wreg[u];
+      } else if (e < NW3 + NTT) {
+        const int e2 = e - NW3, row = e2 / (HC / E16), col = (e2 - row * (HC / E16)) * E16;
+        *reinterpret_cast<u32x4*>(st + row * TRS + col) = wreg[u];
+      }
+    }
+    if (tid < 2 * HC) sC[buf * 2 * HC + tid] = creg;
+  };
+  static_assert(2 * HC <= WAVES * 64, "one constant per thread");
+
   const T* Z = static_cast<const T*>(p.z);
   const T* D = static_cast<const T*>(p.dout);
   for (int tile = blockIdx.x; tile < p.ntiles; tile += gridDim.x) {
@@ -235,13 +273,18 @@ __global__ void __launch_bounds__(WAVES * 64) transition_bwd_kernel(TransBwdPara
     for (int cb = 0; cb < CB; ++cb) dx[cb][0] = dx[cb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     __syncthreads();  // the previous tile's last chunk is no longer read
-    load_chunk(0, 0);
+    if constexpr (NB == 2) {
+      fetch_chunk(0);
+      store_chunk(0);
+    } else {
+      load_chunk(0, 0);
+    }
     for (int q = 0; q < nchunks; ++q) {
       int buf = 0;
       if constexpr (NB == 2) {
         buf = q & 1;
         __syncthreads();  // chunk q is in LDS; chunk q-1's buffer is free
-        if (q + 1 < nchunks) load_chunk(q + 1, buf ^ 1);
+        if (q + 1 < nchunks) fetch_chunk(q + 1);
       } else {
         if (q > 0) {
           __syncthreads();  // chunk q-1 no longer read
@@ -306,6 +349,8 @@ __global__ void __launch_bounds__(WAVES * 64) transition_bwd_kernel(TransBwdPara
           dx[cb][pb] = mma32(tb, fv, dx[cb][pb]);
         }
       }
+      if constexpr (NB == 2)
+        if (q + 1 < nchunks) store_chunk(buf ^ 1);
     }
 
     // LayerNorm backward: lane (l16, g) holds dx[pos pb*16 + l16][cb*16 + 4g + i]

@@ -1011,9 +1011,13 @@ hipError_t launch_wgrad(WGradParams& p, hipStream_t s) {
   const bool full = p.a_w == 128 && p.b_w == 128;
   switch (p.nseg) {
     case 4:
-      if (bias && full) return launch_wgrad_k<T, 4, true, false, true>(p, s);
+      if (full)
+        return bias ? launch_wgrad_k<T, 4, true, false, true>(p, s)
+                    : launch_wgrad_k<T, 4, false, false, true>(p, s);
       return bias ? launch_wgrad_k<T, 4, true>(p, s) : launch_wgrad_k<T, 4, false>(p, s);
-    case 2: return launch_wgrad_k<T, 2, false>(p, s);
+    case 2:
+      return full ? launch_wgrad_k<T, 2, false, false, true>(p, s)
+                  : launch_wgrad_k<T, 2, false>(p, s);
     case 1:
       return full ? launch_wgrad_k<T, 1, false, false, true>(p, s)
                   : launch_wgrad_k<T, 1, false>(p, s);
