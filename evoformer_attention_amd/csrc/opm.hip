@@ -277,7 +277,7 @@ __device__ __forceinline__ int64_t dp_off(int64_t r, int64_t k, int64_t kp) {
   else return r * kp + k;
 }
 
-template <typename T>
+template <typename T, int KS>  // KS = c_z / 32
 __global__ void __launch_bounds__(256) opm_dp_kernel(OpmDpParams p) {
   using Op = typename Tr<T>::Op;
   constexpr int CS = DpCfg<T>::CS, ROWS = 32 * CS, RPW = ROWS / 4, RB = RPW / 16;
@@ -303,26 +303,40 @@ __global__ void __launch_bounds__(256) opm_dp_kernel(OpmDpParams p) {
   const T* D = static_cast<const T*>(p.dout);
   T* dP = static_cast<T*>(p.dp);
   T* dPt = static_cast<T*>(p.dpt);
-  const int ksteps = p.CZ / 32;
+  // A tile's dout operands: 4 blocks of 16 pairs, c_z in 32-wide steps.
+  // The next tile's are loaded while the current one is computed, staged
+  // and stored (after the last tile: the last tile again, in bounds).
+  auto load_b = [&](Op (&b)[KS][4], int tile) {
+    const int p0 = tile * kDpPairs;
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb) {
+      const int pr = min(p0 + pb * 16 + l16, p.npairs - 1);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) b[ks][pb] = ld_op8<T>(D + (int64_t)pr * (32 * KS) + 32 * ks + 8 * g);
+    }
+  };
+  Op bn[KS][4];
+  load_b(bn, min((int)blockIdx.x, p.ntiles - 1));
   for (int tile = blockIdx.x; tile < p.ntiles; tile += gridDim.x) {
     const int p0 = tile * kDpPairs;
+    Op bc[KS][4];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int pb = 0; pb < 4; ++pb) bc[ks][pb] = bn[ks][pb];
+    load_b(bn, min(tile + (int)gridDim.x, p.ntiles - 1));
     f32x4 acc[RB][4];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int pb = 0; pb < 4; ++pb) acc[rb][pb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int ks = 0; ks < ksteps; ++ks) {
-      Op b[4];
 #pragma unroll
-      for (int pb = 0; pb < 4; ++pb) {
-        const int pr = min(p0 + pb * 16 + l16, p.npairs - 1);
-        b[pb] = ld_op8<T>(D + (int64_t)pr * p.CZ + 32 * ks + 8 * g);
-      }
+    for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         const Op a = ld_op8<T>(sW + (wave * RPW + rb * 16 + l16) * WS + 32 * ks + 8 * g);
 #pragma unroll
-        for (int pb = 0; pb < 4; ++pb) acc[rb][pb] = mma32(a, b[pb], acc[rb][pb]);
+        for (int pb = 0; pb < 4; ++pb) acc[rb][pb] = mma32(a, bc[ks][pb], acc[rb][pb]);
       }
     }
     __syncthreads();  // the previous tile's stores have read sO
@@ -482,13 +496,23 @@ hipError_t opm_bwd_t(const OpmBwdArgs& a, hipStream_t s) {
     constexpr int ROWS = 32 * DpCfg<T>::CS;
     const size_t lds = ((size_t)ROWS * (CZ + 16 / sizeof(T)) +
                         (size_t)kDpPairs * (ROWS + 16 / sizeof(T))) * sizeof(T);
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&opm_dp_kernel<T>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
     const int slices = (C / DpCfg<T>::CS) * (C / 32);
     const int gx = std::max(1, std::min(d.ntiles, 1024 / slices));
-    hipLaunchKernelGGL(opm_dp_kernel<T>, dim3(gx, slices), dim3(256), lds, s, d);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    auto launch_dp = [&](auto kernel) {
+      hipError_t e2 = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e2 != hipSuccess) return e2;
+      hipLaunchKernelGGL(kernel, dim3(gx, slices), dim3(256), lds, s, d);
+      return hipGetLastError();
+    };
+    switch (CZ / 32) {
+      case 1: e = launch_dp(&opm_dp_kernel<T, 1>); break;
+      case 2: e = launch_dp(&opm_dp_kernel<T, 2>); break;
+      case 3: e = launch_dp(&opm_dp_kernel<T, 3>); break;
+      case 4: e = launch_dp(&opm_dp_kernel<T, 4>); break;
+      default: return hipErrorInvalidValue;
+    }
+    if (e != hipSuccess) return e;
   }
   // dA[(i, c)][s] = sum_(j, d) dP[(i, c)][(j, d)] Y_b[s][(j, d)]; dB likewise
   if ((e = launch_pair_gemm_rect(a.dtype, 1, M, S, M, (int)L.Np, (int)L.Np2, (int)L.Kp2, at(L.p),
