@@ -23,6 +23,7 @@
 //   3. trimul_out: out[p] = W_o . T[:, p] + b_o with T read channel-major,
 //      staged through LDS and read with transposing LDS reads.
 #include <algorithm>
+#include <type_traits>
 
 #include "evo_device.h"
 #include "evo_kernels.h"
@@ -617,26 +618,45 @@ __device__ __forceinline__ void st16e(T* p, const T (&v)[16 / sizeof(T)]) {
 // Matrices [C] of (row r < rows, column q < ncols) at c*cs + r*ld + q to
 // rows dst[pos][C], pos = r*N + q (q*N + r when trans); zero where keep is
 // given and keep[q] == 0.  vec: cs and ld are multiples of 16 bytes.
+// A thread loads the same 16-byte run of positions from 4 consecutive
+// channels and writes each position's 4 channels as one LDS store; the
+// 4-channel group g of position q sits in slot g ^ perm_swz(q) of its LDS
+// row, which spreads the stores of a wave over all banks and keeps the two
+// groups of an aligned 8-channel read adjacent and in order.
+template <typename T>
+__device__ __forceinline__ int perm_swz(int q) {
+  return sizeof(T) == 2 ? 2 * ((q >> 3) & 7) : ((q >> 2) & 7);
+}
 template <typename T>
 __global__ void __launch_bounds__(256) cm_to_pm_kernel(const T* src, T* dst, int C, int ncols,
                                                        int64_t ld, int64_t cs, int N, int trans,
                                                        const uint8_t* keep, int vec) {
-  constexpr int E = 16 / sizeof(T), TS = kMaxC + 16 / (int)sizeof(T);
-  __shared__ __attribute__((aligned(16))) T tile[kPermQ * TS];  // [q][c]
+  constexpr int E = 16 / sizeof(T), TS = kMaxC;
+  using T4 = typename std::conditional<sizeof(T) == 2, uint2, u32x4>::type;
+  __shared__ __attribute__((aligned(16))) T tile[kPermQ * TS];  // [q][c], swizzled groups
   const int r = blockIdx.y, q0 = blockIdx.x * kPermQ, tid = threadIdx.x;
   constexpr int CPS = kPermQ / E;  // 16-byte chunks per channel run
-  for (int e = tid; e < C * CPS; e += 256) {
-    const int c = e / CPS, ql = (e % CPS) * E, q = q0 + ql;
-    const T* sp = src + (int64_t)c * cs + (int64_t)r * ld + q;
-    T v[E];
-    if (vec && q + E <= ncols) {
-      ld16e(sp, v);
-    } else {
+  for (int e = tid; e < C / 4 * CPS; e += 256) {
+    const int cg = e / CPS, ql = (e % CPS) * E, q = q0 + ql;
+    T v[4][E];
 #pragma unroll
-      for (int j = 0; j < E; ++j) v[j] = q + j < ncols ? sp[j] : T(0);
+    for (int u = 0; u < 4; ++u) {
+      const T* sp = src + (int64_t)(4 * cg + u) * cs + (int64_t)r * ld + q;
+      if (vec && q + E <= ncols) {
+        ld16e(sp, v[u]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < E; ++j) v[u][j] = q + j < ncols ? sp[j] : T(0);
+      }
     }
 #pragma unroll
-    for (int j = 0; j < E; ++j) tile[(ql + j) * TS + c] = v[j];
+    for (int j = 0; j < E; ++j) {
+      T w[4] = {v[0][j], v[1][j], v[2][j], v[3][j]};
+      T4 x;
+      __builtin_memcpy(&x, w, sizeof(x));
+      const int slot = cg ^ perm_swz<T>(ql + j);
+      *reinterpret_cast<T4*>(tile + (ql + j) * TS + 4 * slot) = x;
+    }
   }
   __syncthreads();
   const int CPP = C / E;  // chunks per position
@@ -645,43 +665,63 @@ __global__ void __launch_bounds__(256) cm_to_pm_kernel(const T* src, T* dst, int
     if (q >= ncols) continue;
     const int64_t pos = trans ? (int64_t)q * N + r : (int64_t)r * N + q;
     const bool dead = keep && keep[q] == 0;
+    const int slot = (c0 >> 2) ^ perm_swz<T>(ql);
     T v[E];
+    ld16e(tile + ql * TS + 4 * slot, v);
 #pragma unroll
-    for (int j = 0; j < E; ++j) v[j] = dead ? T(0) : tile[ql * TS + c0 + j];
+    for (int j = 0; j < E; ++j) v[j] = dead ? T(0) : v[j];
     st16e(dst + pos * C + c0, v);
   }
 }
 
 // Rows src[pos][C] to matrices [C][Np][Kp] (row r, column q) at c*cs + r*Kp
 // + q: src[pos][c] with pos = r*N + q (q*N + r when trans), zero for r >= N
-// or q >= N.  Grid: (Kp / 64, Np).
+// or q >= N.  Grid: (Kp / 64, Np).  A thread loads one 16-byte run of
+// channels from 4 consecutive positions and writes each channel's 4
+// positions as one LDS store, in slot pg ^ ((c / E) & 15) of the channel's
+// row (pg: the group of 4 positions).
 template <typename T>
 __global__ void __launch_bounds__(256) pm_to_cm_kernel(const T* src, T* dst, int C, int N,
                                                        int64_t Kp, int64_t cs, int trans) {
-  constexpr int E = 16 / sizeof(T), TS = kPermQ + 16 / (int)sizeof(T);
-  __shared__ __attribute__((aligned(16))) T tile[kMaxC * TS];  // [c][q]
+  constexpr int E = 16 / sizeof(T), TS = kPermQ;
+  using T4 = typename std::conditional<sizeof(T) == 2, uint2, u32x4>::type;
+  __shared__ __attribute__((aligned(16))) T tile[kMaxC * TS];  // [c][q], swizzled groups
   const int r = blockIdx.y, q0 = blockIdx.x * kPermQ, tid = threadIdx.x;
   const int CPP = C / E;
-  for (int e = tid; e < kPermQ * CPP; e += 256) {
-    const int ql = e / CPP, c0 = (e % CPP) * E, q = q0 + ql;
-    T v[E];
-    if (r < N && q < N) {
-      const int64_t pos = trans ? (int64_t)q * N + r : (int64_t)r * N + q;
-      ld16e(src + pos * C + c0, v);
-    } else {
+  for (int e = tid; e < kPermQ / 4 * CPP; e += 256) {
+    const int pg = e / CPP, cc = e % CPP, c0 = cc * E;
+    T v[4][E];
 #pragma unroll
-      for (int j = 0; j < E; ++j) v[j] = T(0);
+    for (int u = 0; u < 4; ++u) {
+      const int q = q0 + 4 * pg + u;
+      if (r < N && q < N) {
+        const int64_t pos = trans ? (int64_t)q * N + r : (int64_t)r * N + q;
+        ld16e(src + pos * C + c0, v[u]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < E; ++j) v[u][j] = T(0);
+      }
     }
+    const int slot = pg ^ (cc & 15);
 #pragma unroll
-    for (int j = 0; j < E; ++j) tile[(c0 + j) * TS + ql] = v[j];
+    for (int j = 0; j < E; ++j) {
+      T w[4] = {v[0][j], v[1][j], v[2][j], v[3][j]};
+      T4 x;
+      __builtin_memcpy(&x, w, sizeof(x));
+      *reinterpret_cast<T4*>(tile + (c0 + j) * TS + 4 * slot) = x;
+    }
   }
   __syncthreads();
   constexpr int CPS = kPermQ / E;
   for (int e = tid; e < C * CPS; e += 256) {
     const int c = e / CPS, ql = (e % CPS) * E;
+    const int sw = (c / E) & 15;
     T v[E];
 #pragma unroll
-    for (int j = 0; j < E; ++j) v[j] = tile[c * TS + ql + j];
+    for (int h = 0; h < E / 4; ++h) {
+      const T4 x = *reinterpret_cast<const T4*>(tile + c * TS + 4 * ((ql / 4 + h) ^ sw));
+      __builtin_memcpy(&v[4 * h], &x, sizeof(x));
+    }
     st16e(dst + (int64_t)c * cs + (int64_t)r * Kp + q0 + ql, v);
   }
 }
